@@ -1,0 +1,224 @@
+/*
+ * rkv.h -- C ABI of librkv: flash attention over a KV cache split into position
+ * segments, for AMD Instinct MI355X (gfx950).
+ *
+ * The cache is split in one of two ways:
+ *   - a device-resident window of cells [0, wc) plus a tail [wc, n_kv) that may sit in
+ *     pinned host memory and is lifted to the GPU tile by tile
+ *     (opencoti-llamafile patch 0070-rolling-kv, commit message "position-windowed KV
+ *     residency" and fattn.cu ggml_cuda_streaming_flash_attn; patch
+ *     0102-fattn-bulk-h2d-scratch-ring, bulk raw-quant lift and persistent scratch ring);
+ *   - an arbitrary per-sequence list of rows into a shared cell pool
+ *     (llama.cpp PR #29510 "flash_attn_ext_rows", API comment in ggml.h).
+ * Every segment yields a partial (M, S, VKQ) per output row and a log-sum-exp merge
+ * combines the partials (patch 0070, fattn.cu header comment and streaming_combine_kernel).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Tensors are described ggml-style: ne[0] is the fastest dimension, nb[] are byte
+ * strides, nb[0] is the element (or quant block) size.  Rows of head_dim values must be
+ * contiguous (nb[0] == type size).  Supported: head_dim == dv == 128; Q in F16;
+ * K in F16 or Q8_0; V in F16 or Q4_0.  Q8_0 is a 34-byte block (binary16 scale d, 32
+ * int8 codes q; value d*q).  Q4_0 is an 18-byte block (binary16 scale d, 16 bytes; byte
+ * j holds element j in its low nibble and element j+16 in its high nibble; value
+ * d*(n-8)).  K/V data pointers and their nb[1], nb[2] must be multiples of 8 bytes; Q
+ * pointers and strides multiples of 4 bytes.
+ *
+ *   score s_j = scale * <q, k_j> + mask[j]   (mask additive binary16, -inf hides;
+ *                                             column j is the GLOBAL key position)
+ *   grouped-query map: query head h reads KV head h / (n_head / n_head_kv).
+ *   O = softmax-weighted sum of v_j over visible keys; LSE = ln sum_j exp(s_j).
+ *   A row with no visible key gets O = 0 and LSE = -inf.
+ *
+ * Output layouts: O is float32 [dv, n_head, n_q(, n_seq)] contiguous; LSE is float32
+ * [n_head, n_q(, n_seq)] contiguous; output row index r = h + n_head*(i + n_q*b).
+ * Partials are float32 [n_seg][n_rows][2 + dv] holding (M, S, VKQ[dv]) with
+ * M = max_j s_j (natural-log units), S = sum_j exp(s_j - M), VKQ = sum_j exp(s_j - M) v_j;
+ * an empty segment is (-inf, 0, 0...).
+ *
+ * Every call returns an rkv_status.  Arguments are validated on the host before any
+ * device work; nothing aborts across the ABI.  Work is enqueued on the caller's stream
+ * (a hipStream_t passed as void*; NULL = the legacy default stream) and the call returns
+ * without waiting.  Device faults surface as RKV_ERR_HIP on a later call.
+ * rkv_last_error() gives a human-readable reason for the last non-OK status on the
+ * calling thread.
+ *
+ * Ownership: the caller owns every input and output buffer.  An rkv_ctx owns its copy
+ * stream, its pre-created events, its persistent grow-only scratch ring and its partials
+ * workspace.  One context serves one stream at a time and is not re-entrant.
+ */
+#ifndef RKV_H
+#define RKV_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct rkv_ctx rkv_ctx;
+
+enum rkv_type { RKV_TYPE_F32 = 0, RKV_TYPE_F16 = 1, RKV_TYPE_Q4_0 = 2, RKV_TYPE_Q8_0 = 8 };
+
+enum rkv_status {
+    RKV_OK = 0,
+    RKV_ERR_ARG = -1,          /* malformed argument (shape, stride, pointer kind)        */
+    RKV_ERR_UNSUPPORTED = -2,  /* well-formed but outside what the kernels implement      */
+    RKV_ERR_HIP = -3,          /* a HIP runtime call failed                                */
+    RKV_ERR_NOMEM = -4,        /* device allocation failed                                 */
+    RKV_ERR_CAPTURE = -5       /* workspace growth needed while the stream is capturing    */
+};
+
+enum rkv_lift_mode {
+    RKV_LIFT_BULK = 0,  /* hipMemcpyAsync DMA of the raw bytes into the scratch ring         */
+    RKV_LIFT_UVA = 1    /* contrast only: a kernel reads the pinned host bytes word by word  */
+};
+
+typedef struct rkv_tensor {
+    const void *data;
+    int32_t type;   /* enum rkv_type */
+    int64_t ne[4];
+    int64_t nb[4];
+} rkv_tensor;
+
+/* Statistics of the last attention call on a context (host-side planning facts). */
+typedef struct rkv_stats {
+    int32_t n_segments;       /* device segments launched (window, tail tiles, ...)      */
+    int32_t n_partials;       /* partial slots merged                                    */
+    int32_t n_tail_tiles;     /* tail tiles lifted                                       */
+    int32_t lift_mode;        /* enum rkv_lift_mode used for the tail                    */
+    int64_t lift_bytes;       /* raw bytes lifted host -> device                         */
+    int32_t splits_window;    /* split-K factor used on the window segment               */
+    int32_t kernel_variant;   /* 0 = vector decode kernel, 1 = MFMA prefill kernel        */
+} rkv_stats;
+
+/* ---- context ---------------------------------------------------------------------- */
+
+/* Create a context on `device`: a non-blocking copy stream at default priority and a
+ * pool of pre-created events (never created during graph capture, as patch 0070's
+ * copy/compute double buffer requires).  Returns RKV_ERR_HIP if the device is absent. */
+int rkv_create(int device, rkv_ctx **out);
+
+/* Grow (never shrink) the persistent scratch ring and partials workspace so that later
+ * calls allocate nothing; call it before capturing a stream into a graph.  Each of the
+ * n_slots (1..4) ring slots holds max_tile_bytes_k of K and max_tile_bytes_v of V
+ * (patch 0102: worst-case tile capacity, persistent per-slot scratch).  max_partial_floats
+ * sizes the partials workspace.  Zero arguments leave that part unchanged. */
+int rkv_reserve(rkv_ctx *ctx, int64_t max_tile_bytes_k, int64_t max_tile_bytes_v,
+                int n_slots, int64_t max_partial_floats);
+
+/* Free everything the context owns (synchronises its device first). NULL is a no-op. */
+void rkv_destroy(rkv_ctx *ctx);
+
+const char *rkv_strerror(int status);
+const char *rkv_last_error(void);
+int rkv_get_stats(const rkv_ctx *ctx, rkv_stats *out);
+
+/* Choose how tail tiles are lifted by later calls on this context (enum rkv_lift_mode).
+ * RKV_LIFT_UVA exists only to measure the word-granularity host read of patch 0102's
+ * commit message against the bulk DMA; it is never the default. */
+int rkv_set_lift_mode(rkv_ctx *ctx, int mode);
+
+/* Override the split-K factor of window/pool segments (0 = automatic). */
+int rkv_set_splits(rkv_ctx *ctx, int splits);
+
+/* Measurement aid: when on, later calls record timing events around each tail-tile lift on
+ * the copy stream (up to 64 per call). */
+int rkv_set_lift_timing(rkv_ctx *ctx, int on);
+
+/* Waits for the last call's timed lifts and reports the sum of their durations, the span
+ * from the first lift's start to the last lift's end, and how many were timed. */
+int rkv_lift_timing_ms(rkv_ctx *ctx, float *total_ms, float *span_ms, int *n_lifts);
+
+/* ---- attention -------------------------------------------------------------------- */
+
+/* Decode attention over a window + tail split (patch 0070, ggml_streaming_flash_attn_window:
+ * window K/V in one pair of sources, tail K/V in another, a NULL tail meaning one region;
+ * tiles never straddle wc; the mask is sliced at the global position).
+ *   q       F16 [128, n_q, n_head, 1], device.  n_q * (n_head/n_head_kv) <= 8.
+ *   k_win   [128, >= wc, n_head_kv, 1] device (cells [0, wc) are used); NULL iff wc == 0.
+ *   v_win   as k_win with V's type.
+ *   k_tail  [128, n_tail, n_head_kv, 1] or NULL.  Pinned host memory (lifted in tiles of
+ *           tile_kv cells through the context's scratch ring on its copy stream,
+ *           double-buffered against compute) or device memory (read in place).
+ *           A pinned host tail must be cell-major-contiguous per tile
+ *           (nb[1] >= n_head_kv*row and heads inside a cell) or head-major; pageable host
+ *           memory is RKV_ERR_ARG.
+ *   mask    F16 [>= n_kv, >= n_q, 1, 1] additive, device, or NULL (all keys visible).
+ *   n_kv    = wc + n_tail.  tile_kv > 0.
+ *   o       float32 [128, n_head, n_q] device; lse float32 [n_head, n_q] device or NULL.
+ * Stream-ordered on `stream`; returns once enqueued. */
+int rkv_attn_decode(rkv_ctx *ctx, const rkv_tensor *q,
+                    const rkv_tensor *k_win, const rkv_tensor *v_win,
+                    const rkv_tensor *k_tail, const rkv_tensor *v_tail,
+                    const rkv_tensor *mask, int64_t wc, int64_t tile_kv, float scale,
+                    float *o, float *lse, void *stream);
+
+/* Prefill attention: the same arguments as rkv_attn_decode for any n_q, computed with
+ * MFMA f16 tiles (K and V are dequantised to binary16 in LDS).  q_pos0 >= 0 makes it
+ * causal: query i sits at absolute position q_pos0 + i and sees keys at positions
+ * <= q_pos0 + i (in addition to the mask); q_pos0 == -1 uses the mask alone. */
+int rkv_attn_prefill(rkv_ctx *ctx, const rkv_tensor *q,
+                     const rkv_tensor *k_win, const rkv_tensor *v_win,
+                     const rkv_tensor *k_tail, const rkv_tensor *v_tail,
+                     const rkv_tensor *mask, int64_t wc, int64_t tile_kv, float scale,
+                     int64_t q_pos0, float *o, float *lse, void *stream);
+
+/* Unified-pool attention (llama.cpp PR #29510, ggml_flash_attn_ext_rows): each sequence
+ * b attends to its own list of pool rows.
+ *   q       F16 [128, n_q, n_head, n_seq] device, n_q * (n_head/n_head_kv) <= 8.
+ *   k_pool  [128, n_pool, n_head_kv, 1] device, shared by all sequences; v_pool likewise.
+ *   kv_rows int32 [n_kv, n_seq] device, contiguous: key j of sequence b is pool row
+ *           kv_rows[j + n_kv*b].  A negative row is padding: it contributes nothing and is
+ *           never dereferenced.  Rows >= n_pool are a contract violation (not checked on
+ *           the device).
+ *   mask    F16 [>= n_kv, >= n_q, 1, n_seq] additive, device, or NULL.
+ *   o       float32 [128, n_head, n_q, n_seq]; lse float32 [n_head, n_q, n_seq] or NULL. */
+int rkv_attn_rows(rkv_ctx *ctx, const rkv_tensor *q, const rkv_tensor *k_pool,
+                  const rkv_tensor *v_pool, const int32_t *kv_rows, int64_t n_kv,
+                  const rkv_tensor *mask, float scale, float *o, float *lse, void *stream);
+
+/* One segment's partial over device-resident K/V (the per-segment step of the method):
+ * writes (M, S, VKQ) for every output row into `partial` float32 [n_rows][2 + 128].
+ * kv_pos0 is the global position of the segment's first cell (mask column offset and
+ * causal position); q_pos0 as in rkv_attn_prefill (-1 = mask only).  Chooses the vector
+ * kernel when n_q * gqa <= 8, the MFMA kernel otherwise. */
+int rkv_attn_partial(rkv_ctx *ctx, const rkv_tensor *q, const rkv_tensor *k,
+                     const rkv_tensor *v, const rkv_tensor *mask, int64_t kv_pos0,
+                     int64_t q_pos0, float scale, float *partial, void *stream);
+
+/* Log-sum-exp merge (patch 0070 streaming_combine_kernel; the tail-partial rule of
+ * tail_partial_to_tile_kernel): partials float32 [n_seg][n_rows][2 + dv] on the device
+ * -> o float32 [dv, n_rows] and lse float32 [n_rows] (lse may be NULL).  Rows whose
+ * segments are all empty get O = 0 and LSE = -inf.  dv must be 128.  No context needed. */
+int rkv_lse_merge(const float *partials, int n_seg, int64_t n_rows, int dv,
+                  float *o, float *lse, void *stream);
+
+/* Lift nbytes raw bytes (binary16 or quant blocks, copied as they are) from pinned host
+ * memory into ring slot `slot` of the context (patch 0102: bulk H2D of the raw quant
+ * tail into a persistent per-slot scratch ring; K uses the slot's first buffer).
+ * *dev_dst receives the slot's device address.  mode RKV_LIFT_BULK issues one
+ * hipMemcpyAsync on copy_stream; RKV_LIFT_UVA launches the word-granularity reader
+ * kernel instead (contrast measurement).  The slot's copy-done event is recorded on
+ * copy_stream.  copy_stream NULL means the context's own copy stream.  The ring grows on
+ * demand outside graph capture (RKV_ERR_CAPTURE inside it). */
+int rkv_tail_lift(rkv_ctx *ctx, const void *host_src, int64_t nbytes, int slot, int mode,
+                  void **dev_dst, void *copy_stream);
+
+/* ---- testing aid ------------------------------------------------------------------ */
+
+/* Dequantise n_rows rows of 128 values (type F16, Q8_0 or Q4_0; row r at byte offset
+ * r*row_stride from src, device memory) into float32 dst [n_rows][128] with the same
+ * device routines the attention kernels use.  q8_0 gives d*q and q4_0 d*(n-8), both
+ * exact in float32; binary16 subnormal scales are kept. */
+int rkv_dequant_rows(const void *src, int type, int64_t n_rows, int64_t row_stride,
+                     float *dst, void *stream);
+
+/* Library version as "major.minor.patch". */
+const char *rkv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RKV_H */

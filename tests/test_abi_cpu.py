@@ -1,0 +1,101 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports every symbol
+include/rkv.h declares (and the Python binding declares the same set), and argument
+errors are reported as status codes before any device work."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rkv.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rkv_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from tiered_kv_cache_split_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("librkv.so is not built (run __graft_entry__.build())")
+    return _lib.load()
+
+
+def test_header_declares_the_boundary():
+    names = header_functions()
+    for required in ("rkv_attn_decode", "rkv_attn_prefill", "rkv_attn_rows", "rkv_lse_merge",
+                     "rkv_tail_lift"):
+        assert required in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in header_functions():
+        assert hasattr(lib, name), name
+
+
+def test_binding_matches_header():
+    from tiered_kv_cache_split_amd import _lib
+    assert sorted(_lib.SIGNATURES) == header_functions()
+
+
+def test_version_and_strerror(lib):
+    assert re.match(r"^\d+\.\d+\.\d+$", lib.rkv_version().decode())
+    for st in (0, -1, -2, -3, -4, -5):
+        assert lib.rkv_strerror(st).decode() not in ("", "unknown status")
+    assert lib.rkv_strerror(42).decode() == "unknown status"
+
+
+def test_null_context_is_an_argument_error(lib):
+    from tiered_kv_cache_split_amd import _lib
+    assert lib.rkv_attn_decode(None, None, None, None, None, None, None, 0, 1, 1.0, None, None, None) == _lib.RKV_ERR_ARG
+    assert lib.rkv_attn_rows(None, None, None, None, None, 0, None, 1.0, None, None, None) == _lib.RKV_ERR_ARG
+    assert lib.rkv_attn_prefill(None, None, None, None, None, None, None, 0, 1, 1.0, -1, None, None, None) == _lib.RKV_ERR_ARG
+    assert lib.rkv_reserve(None, 0, 0, 2, 0) == _lib.RKV_ERR_ARG
+    assert b"ctx" in lib.rkv_last_error()
+    d = ctypes.c_void_p()
+    assert lib.rkv_tail_lift(None, None, 0, 0, 0, ctypes.byref(d), None) == _lib.RKV_ERR_ARG
+    lib.rkv_destroy(None)  # no-op
+
+
+def test_merge_rejects_bad_sizes_before_device_work(lib):
+    from tiered_kv_cache_split_amd import _lib
+    assert lib.rkv_lse_merge(None, 2, 4, 64, None, None, None) == _lib.RKV_ERR_UNSUPPORTED
+    assert lib.rkv_lse_merge(None, 0, 4, 128, None, None, None) == _lib.RKV_ERR_ARG
+    assert lib.rkv_lse_merge(None, 1, 0, 128, None, None, None) == _lib.RKV_OK  # nothing to do
+
+
+def test_dequant_rejects_unknown_type(lib):
+    from tiered_kv_cache_split_amd import _lib
+    assert lib.rkv_dequant_rows(None, 3, 4, 256, None, None) == _lib.RKV_ERR_UNSUPPORTED
+    assert lib.rkv_dequant_rows(None, 8, 4, 100, None, None) == _lib.RKV_ERR_ARG
+
+
+def test_descriptor_layouts():
+    """The binding's descriptors follow the ggml convention (ne[0] fastest, byte strides)."""
+    torch = pytest.importorskip("torch")
+    import tiered_kv_cache_split_amd as rkv
+    q = torch.zeros(40, 3, 128, dtype=torch.float16)
+    d = rkv.q_desc(q)
+    assert list(d.ne) == [128, 3, 40, 1] and list(d.nb)[:3] == [2, 256, 3 * 256]
+    k = torch.zeros(100, 8, 136, dtype=torch.uint8)
+    d = rkv.kv_desc(k, rkv.RKV_TYPE_Q8_0, "cell")
+    assert list(d.ne) == [128, 100, 8, 1] and list(d.nb)[:3] == [34, 8 * 136, 136]
+    kh = torch.zeros(8, 100, 72, dtype=torch.uint8)
+    d = rkv.kv_desc(kh, rkv.RKV_TYPE_Q4_0, "head")
+    assert list(d.ne) == [128, 100, 8, 1] and list(d.nb)[:3] == [18, 72, 100 * 72]
+    m = torch.zeros(3, 500, dtype=torch.float16)
+    d = rkv.mask_desc(m)
+    assert list(d.ne) == [500, 3, 1, 1] and list(d.nb)[:2] == [2, 1000]
+
+
+def test_no_device_is_reported(lib):
+    torch = pytest.importorskip("torch")
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    from tiered_kv_cache_split_amd import _lib
+    h = ctypes.c_void_p()
+    assert lib.rkv_create(0, ctypes.byref(h)) == _lib.RKV_ERR_HIP

@@ -1,0 +1,209 @@
+"""GPU parity of rkv_attn_decode / rkv_lse_merge / rkv_attn_partial against the fp64 oracle."""
+import numpy as np
+import pytest
+
+import oracle
+import rkv_inputs as gen
+from rkv_testutil import LSE_TOL, O_TOL, Runner, assert_close, dev, oracle_decode, step
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def run():
+    return Runner()
+
+
+def small(num, n_kv, wc, tile, **over):
+    """Workload `num` at an oracle-sized length (several chunks, ragged ends)."""
+    w = gen.make_workload(num, **over)
+    if w["n_kv"] != n_kv:
+        base = gen.WORKLOADS[num]
+        sd = max(1, base["n_kv"] // n_kv)
+        w = gen.make_workload(num, scale_down=sd, **over)
+    w["wc"], w["tile_kv"] = min(wc, w["n_kv"]), tile
+    return w
+
+
+def test_f16_window_only_config1_shape(run):
+    w = gen.make_workload(1)
+    step("decode f16 n_kv=4096 window only")
+    O, L = run.decode(w, wc=w["n_kv"], tail=None)
+    Oref, Lref = oracle_decode(w)
+    assert_close(O, L, Oref, Lref, what="window only")
+
+
+@pytest.mark.parametrize("tail", ["device", "host"])
+def test_f16_window_plus_tail_config1(run, tail):
+    w = gen.make_workload(1)
+    step(f"decode f16 config1 wc=2048 tail={tail} tile=1024")
+    O, L = run.decode(w, tail=tail)
+    Oref, Lref = oracle_decode(w)
+    assert_close(O, L, Oref, Lref, what=f"tail {tail}")
+    st = run.ctx.stats()
+    if tail == "host":
+        assert st["n_tail_tiles"] == 2 and st["lift_bytes"] == 2048 * 2 * 2 * 256
+
+
+@pytest.mark.parametrize("tile", [31, 256, 512, 768, 1024, 32768])
+def test_tile_sweep_wc_not_multiple_of_256(run, tile):
+    w = gen.make_workload(1)
+    step(f"decode f16 wc=1333 tile={tile}")
+    O, L = run.decode(w, wc=1333, tile_kv=tile, tail="host")
+    Oref, Lref = oracle_decode(w)
+    assert_close(O, L, Oref, Lref, what=f"tile {tile}")
+
+
+@pytest.mark.parametrize("kt,vt", [(gen.TYPE_Q8_0, gen.TYPE_Q4_0), (gen.TYPE_Q8_0, gen.TYPE_F16),
+                                   (gen.TYPE_F16, gen.TYPE_Q4_0)])
+def test_quant_decode_ragged(run, kt, vt):
+    w = gen.make_workload(2, scale_down=32, k_type=kt, v_type=vt)  # n_kv 4096
+    step(f"decode k={kt} v={vt} n_kv=4096 wc=2333 tile=700")
+    O, L = run.decode(w, wc=2333, tile_kv=700, tail="host")
+    Oref, Lref = oracle_decode(w)
+    assert_close(O, L, Oref, Lref, what="quant")
+
+
+@pytest.mark.parametrize("layout", ["cell", "head"])
+def test_quant_layouts_and_device_tail(run, layout):
+    w = gen.make_workload(3, scale_down=64)  # n_kv 4096, wc 2048, tile 512
+    step(f"decode q8q4 layout={layout} device tail")
+    O, L = run.decode(w, tail="device", layout=layout)
+    Oref, Lref = oracle_decode(w)
+    assert_close(O, L, Oref, Lref, what=layout)
+    step(f"decode q8q4 layout={layout} host tail")
+    O2, L2 = run.decode(w, tail="host", layout=layout)
+    assert_close(O2, L2, Oref, Lref, what=layout + " host")
+
+
+@pytest.mark.parametrize("n_head,n_head_kv,n_q", [(8, 8, 1), (8, 4, 1), (16, 2, 1), (8, 2, 2), (6, 2, 1),
+                                                  (7, 1, 1)])
+def test_group_shapes(run, n_head, n_head_kv, n_q):
+    w = gen.make_workload(1, n_head=n_head, n_head_kv=n_head_kv, n_q=n_q)
+    step(f"decode gqa shape {n_head}/{n_head_kv} n_q={n_q}")
+    O, L = run.decode(w, wc=1500, tile_kv=1000, tail="host")
+    Oref, Lref = oracle_decode(w)
+    assert_close(O, L, Oref, Lref, what="gqa")
+
+
+def test_mask_with_hidden_keys_and_empty_row(run):
+    w = gen.make_workload(1, n_q=2, n_head=8, n_head_kv=2)
+    rng = np.random.default_rng(3)
+    mask = gen.random_mask_f16(rng, 2, w["n_kv"], p_hidden=0.4)
+    mask[1, :] = -np.inf  # query 1 sees nothing
+    step("decode masked, one empty row")
+    O, L = run.decode(w, wc=2048, tile_kv=1024, tail="host", mask=mask)
+    Oref, Lref = oracle_decode(w, mask=mask)
+    assert_close(O, L, Oref, Lref, what="mask")
+    assert np.all(O[1] == 0) and np.all(L[1] == -np.inf)
+
+
+def test_mask_sliced_at_global_position(run):
+    """Hiding exactly the tail columns must give the window-only result (mask column = global key)."""
+    w = gen.make_workload(1)
+    mask = np.zeros((1, w["n_kv"]), np.float16)
+    mask[0, 2048:] = -np.inf
+    step("decode mask hides tail")
+    O, L = run.decode(w, wc=2048, tile_kv=512, tail="host", mask=mask)
+    w2 = dict(w)
+    w2["k"], w2["v"], w2["n_kv"] = w["k"][:2048], w["v"][:2048], 2048
+    Oref, Lref = oracle_decode(w2)
+    assert_close(O, L, Oref, Lref, what="global mask")
+
+
+def test_outlier_keys(run):
+    rng = gen.rng_for(99)
+    q, k, v = gen.draw_qkv(rng, 8, 1, 2, 3000, k_type=gen.TYPE_Q8_0, v_type=gen.TYPE_Q4_0, outlier_every=17)
+    w = dict(n_head=8, n_head_kv=2, q=q, k=k, v=v, k_type=gen.TYPE_Q8_0, v_type=gen.TYPE_Q4_0,
+             scale=1 / np.sqrt(128), n_kv=3000, wc=1800, tile_kv=600)
+    step("decode outlier keys x30 every 17th")
+    O, L = run.decode(w, tail="host")
+    Oref, Lref = oracle_decode(w)
+    assert_close(O, L, Oref, Lref, what="outliers")
+
+
+def test_empty_tail_equals_single_resident(run):
+    w = gen.make_workload(1)
+    step("decode empty tail vs window only")
+    O1, L1 = run.decode(w, wc=4096, tail=None)
+    w2 = dict(w)
+    O2, L2 = run.decode(w2, wc=4096, tail="host")  # zero-length tail slice
+    assert np.array_equal(O1, O2) and np.array_equal(L1, L2)
+
+
+def test_back_to_back_calls_reuse_slots(run):
+    """Several calls with 4 tail tiles through a 2-slot ring, queued without syncing between them,
+    each against other work on the stream (the reused-slot race classes)."""
+    import torch
+    ws = [gen.make_workload(3, scale_down=64) for _ in range(1)]
+    w = ws[0]
+    Oref, Lref = oracle_decode(w)
+    keep = []
+    outs = []
+    step("decode back-to-back 5 calls, 4 tiles, 2 slots")
+    rkv = run.rkv
+    q = dev(w["q"])
+    kw, vw = dev(w["k"][:2048]), dev(w["v"][:2048])
+    from rkv_testutil import pinned
+    kt, vt = pinned(w["k"][2048:]), pinned(w["v"][2048:])
+    junk = torch.randn(4096, 4096, device="cuda")
+    for it in range(5):
+        o = torch.empty((1, w["n_head"], 128), dtype=torch.float32, device="cuda")
+        lse = torch.empty((1, w["n_head"]), dtype=torch.float32, device="cuda")
+        junk = junk @ junk.T * 1e-3  # unrelated compute on the same stream
+        run.ctx.attn_decode(rkv.q_desc(q), rkv.kv_desc(kw, w["k_type"]), rkv.kv_desc(vw, w["v_type"]),
+                            rkv.kv_desc(kt, w["k_type"]), rkv.kv_desc(vt, w["v_type"]), None, 2048, 512,
+                            w["scale"], o, lse)
+        outs.append((o, lse))
+    torch.cuda.synchronize()
+    for o, lse in outs:
+        assert_close(o.cpu().numpy(), lse.cpu().numpy(), Oref, Lref, what="back-to-back")
+
+
+def test_lse_merge_of_oracle_partials(run):
+    rng = np.random.default_rng(5)
+    q = rng.standard_normal((8, 3, 128))
+    k = rng.standard_normal((2, 900, 128))
+    v = rng.standard_normal((2, 900, 128))
+    bounds = [0, 100, 100, 555, 900]
+    parts = [oracle.partial(q, k[:, a:b], v[:, a:b], 0.09, None) for a, b in zip(bounds[:-1], bounds[1:])]
+    n_rows = 3 * 8
+    P = np.zeros((len(parts), n_rows, 130), np.float32)
+    for s, (M, S, VKQ) in enumerate(parts):
+        P[s, :, 0] = M.reshape(-1)
+        P[s, :, 1] = S.reshape(-1)
+        P[s, :, 2:] = VKQ.reshape(n_rows, 128)
+    import torch
+    import tiered_kv_cache_split_amd as rkv
+    Pd = dev(P)
+    o = torch.empty((n_rows, 128), dtype=torch.float32, device="cuda")
+    lse = torch.empty((n_rows,), dtype=torch.float32, device="cuda")
+    step("lse merge of oracle partials")
+    rkv.lse_merge(Pd, len(parts), n_rows, o, lse)
+    torch.cuda.synchronize()
+    Oref, Lref = oracle.merge(parts)
+    assert_close(o.cpu().numpy(), lse.cpu().numpy(), Oref.reshape(n_rows, 128), Lref.reshape(-1), what="merge")
+
+
+def test_attn_partial_matches_oracle_partial(run):
+    import torch
+    import tiered_kv_cache_split_amd as rkv
+    w = gen.make_workload(2, scale_down=64)  # 2048 cells q8q4
+    step("attn_partial q8q4 segment at kv_pos0=5000")
+    seg = slice(300, 1700)
+    mask = gen.random_mask_f16(np.random.default_rng(8), 1, 5000 + 1400, p_hidden=0.2)
+    q = dev(w["q"])
+    kd, vd = dev(w["k"][seg]), dev(w["v"][seg])
+    md = dev(mask)
+    part = torch.empty((w["n_head"], 130), dtype=torch.float32, device="cuda")
+    run.ctx.attn_partial(rkv.q_desc(q), rkv.kv_desc(kd, w["k_type"]), rkv.kv_desc(vd, w["v_type"]),
+                         rkv.mask_desc(md), 5000, -1, w["scale"], part)
+    torch.cuda.synchronize()
+    P = part.cpu().numpy().astype(np.float64)
+    qv = oracle.q_values(w["q"])
+    kv = oracle.kv_values(w["k_type"], w["k"][seg])
+    vv = oracle.kv_values(w["v_type"], w["v"][seg])
+    M, S, VKQ = oracle.partial(qv, kv, vv, w["scale"], mask[:, 5000:].astype(np.float64))
+    # compare the normalised forms (a partial is defined up to the common factor e^M)
+    assert np.allclose(P[:, 0] + np.log(P[:, 1]), (M + np.log(S))[0], atol=LSE_TOL)
+    assert np.abs(P[:, 2:] / P[:, 1:2] - (VKQ / S[..., None])[0]).max() <= O_TOL

@@ -1,0 +1,92 @@
+"""Bit-exact checks: the GPU dequantiser against the oracle's reading of the same bytes, and
+the tail lift (bulk DMA and the word-granularity contrast) as a byte copy."""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import rkv_inputs as gen
+from rkv_testutil import dev, pinned, step
+
+pytestmark = pytest.mark.gpu
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def gpu_dequant(rows_bytes: np.ndarray, t: int) -> np.ndarray:
+    import torch
+    import tiered_kv_cache_split_amd as rkv
+    src = dev(rows_bytes)
+    dst = torch.empty((rows_bytes.shape[0], 128), dtype=torch.float32, device="cuda")
+    rkv.dequant_rows(src, t, rows_bytes.shape[0], rows_bytes.shape[1], dst)
+    torch.cuda.synchronize()
+    return dst.cpu().numpy()
+
+
+def golden_rows(name, block):
+    raw = []
+    for line in open(os.path.join(GOLDEN, name)):
+        if line.startswith("bytes "):
+            raw.append(bytes.fromhex(line.split()[1]))
+    blocks = [np.frombuffer(b, np.uint8) for b in raw]
+    while len(blocks) % 4:
+        blocks.append(blocks[len(blocks) % len(raw)])
+    return np.concatenate(blocks).reshape(-1, 4 * block)
+
+
+@pytest.mark.parametrize("t", [gen.TYPE_Q8_0, gen.TYPE_Q4_0, gen.TYPE_F16])
+def test_dequant_bit_exact_random(t):
+    rng = np.random.default_rng(21)
+    x = rng.standard_normal((4096, 128)).astype(np.float32)
+    x[::7] *= 1e-6   # tiny blocks: binary16 subnormal scales
+    x[1::97] = 0.0   # all-zero blocks: d = 0
+    raw = gen.pack(t, x)
+    step(f"dequant type {t}")
+    got = gpu_dequant(raw, t)
+    want = oracle.decode(t, raw).astype(np.float32)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+@pytest.mark.parametrize("name,t,blk", [("q8_0_blocks.txt", gen.TYPE_Q8_0, 34), ("q4_0_blocks.txt", gen.TYPE_Q4_0, 18)])
+def test_dequant_golden_blocks(name, t, blk):
+    raw = golden_rows(name, blk)
+    step(f"dequant golden {name}")
+    got = gpu_dequant(raw, t)
+    want = oracle.decode(t, raw).astype(np.float32)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+@pytest.mark.parametrize("nbytes", [1, 4, 4099, 3 * 1024 * 1024 + 5])
+def test_tail_lift_is_a_byte_copy(mode, nbytes):
+    import torch
+    import tiered_kv_cache_split_amd as rkv
+    rng = np.random.default_rng(nbytes)
+    host = pinned(rng.integers(0, 256, size=nbytes, dtype=np.uint8))
+    ctx = rkv.Context(0)
+    step(f"tail lift mode {mode} nbytes {nbytes}")
+    ptr = ctx.tail_lift(host, nbytes, 1, mode)
+    torch.cuda.synchronize()
+    out = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    import ctypes
+    hip = ctypes.CDLL("libamdhip64.so")
+    assert hip.hipMemcpy(ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(ptr), ctypes.c_size_t(nbytes), 3) == 0
+    assert torch.equal(out.cpu(), host)
+    ctx.close()
+
+
+def test_pageable_tail_is_rejected():
+    import torch
+    import tiered_kv_cache_split_amd as rkv
+    w = gen.make_workload(1)
+    ctx = rkv.Context(0)
+    q = dev(w["q"])
+    kw, vw = dev(w["k"][:2048]), dev(w["v"][:2048])
+    kt = torch.from_numpy(np.ascontiguousarray(w["k"][2048:]))  # pageable
+    vt = torch.from_numpy(np.ascontiguousarray(w["v"][2048:]))
+    o = torch.empty((1, 8, 128), dtype=torch.float32, device="cuda")
+    with pytest.raises(rkv.RkvError) as e:
+        ctx.attn_decode(rkv.q_desc(q), rkv.kv_desc(kw, 1), rkv.kv_desc(vw, 1), rkv.kv_desc(kt, 1),
+                        rkv.kv_desc(vt, 1), None, 2048, 1024, 0.088, o)
+    assert e.value.status == -1
+    ctx.close()

@@ -1,0 +1,188 @@
+"""rkv: split-KV (device window + pinned-host tail, or row-list pool) flash attention for
+AMD Instinct MI355X.  Python binding of librkv.so; torch supplies device memory, pinned
+host memory and streams, every step of the attention runs in the library's HIP kernels.
+
+Tensor conventions (numpy/torch C order, last axis fastest; ggml shapes in brackets):
+  * q       float16 (n_head, n_q, 128)            [128, n_q, n_head]
+            rows variant: (n_seq, n_head, n_q, 128) [128, n_q, n_head, n_seq]
+  * K / V   uint8 cell-major cache (n_cells, n_head_kv, row_bytes) or head-major
+            (n_head_kv, n_cells, row_bytes); row_bytes 256 (f16), 136 (q8_0), 72 (q4_0)
+  * mask    float16 (n_q, n_kv) additive; rows variant (n_seq, 1, n_q, n_kv)
+  * o       float32 (n_q, n_head, 128); lse float32 (n_q, n_head)
+"""
+from __future__ import annotations
+
+import ctypes
+
+from ._lib import (RKV_LIFT_BULK, RKV_LIFT_UVA, RKV_TYPE_F16, RKV_TYPE_F32, RKV_TYPE_Q4_0,  # noqa: F401
+                   RKV_TYPE_Q8_0, RkvError, RkvStats, RkvTensor, check, load)
+
+BLOCK_BYTES = {RKV_TYPE_F16: 2, RKV_TYPE_F32: 4, RKV_TYPE_Q8_0: 34, RKV_TYPE_Q4_0: 18}
+ROW_BYTES = {RKV_TYPE_F16: 256, RKV_TYPE_Q8_0: 136, RKV_TYPE_Q4_0: 72}
+
+
+def _ptr(t) -> int:
+    return 0 if t is None else int(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        import torch
+        stream = torch.cuda.current_stream()
+    if hasattr(stream, "cuda_stream"):
+        stream = stream.cuda_stream
+    return ctypes.c_void_p(int(stream))
+
+
+def tensor(data_ptr: int, type_id: int, ne, nb) -> RkvTensor:
+    t = RkvTensor()
+    t.data = ctypes.c_void_p(int(data_ptr))
+    t.type = int(type_id)
+    for i in range(4):
+        t.ne[i] = int(ne[i]) if i < len(ne) else 1
+        t.nb[i] = int(nb[i]) if i < len(nb) else int(t.nb[i - 1] * t.ne[i - 1])
+    return t
+
+
+def q_desc(q) -> RkvTensor:
+    """float16 q (n_head, n_q, 128) or (n_seq, n_head, n_q, 128)."""
+    es = q.element_size()
+    if q.dim() == 3:
+        h, n, d = q.shape
+        return tensor(q.data_ptr(), RKV_TYPE_F16, [d, n, h, 1],
+                      [es, q.stride(1) * es, q.stride(0) * es, q.stride(0) * es * h])
+    s, h, n, d = q.shape
+    return tensor(q.data_ptr(), RKV_TYPE_F16, [d, n, h, s],
+                  [es, q.stride(2) * es, q.stride(1) * es, q.stride(0) * es])
+
+
+def kv_desc(cache, type_id: int, layout: str = "cell") -> RkvTensor:
+    """uint8 cache: cell-major (n_cells, n_head_kv, row_bytes) or head-major
+    (n_head_kv, n_cells, row_bytes) -> [128, n_cells, n_head_kv, 1]."""
+    rb = ROW_BYTES[type_id]
+    if layout == "cell":
+        n_cells, n_head_kv, row = cache.shape
+        nb1, nb2 = cache.stride(0), cache.stride(1)
+    else:
+        n_head_kv, n_cells, row = cache.shape
+        nb1, nb2 = cache.stride(1), cache.stride(0)
+    assert row == rb and cache.stride(2) == 1, "rows must be contiguous bytes"
+    return tensor(cache.data_ptr(), type_id, [128, n_cells, n_head_kv, 1],
+                  [BLOCK_BYTES[type_id], nb1, nb2, nb2 * n_head_kv])
+
+
+def mask_desc(mask) -> RkvTensor | None:
+    """float16 mask (n_q, n_kv) or (n_seq, 1, n_q, n_kv)."""
+    if mask is None:
+        return None
+    es = mask.element_size()
+    if mask.dim() == 2:
+        n_q, n_kv = mask.shape
+        return tensor(mask.data_ptr(), RKV_TYPE_F16, [n_kv, n_q, 1, 1],
+                      [es, mask.stride(0) * es, mask.stride(0) * es * n_q, mask.stride(0) * es * n_q])
+    s, one, n_q, n_kv = mask.shape
+    return tensor(mask.data_ptr(), RKV_TYPE_F16, [n_kv, n_q, one, s],
+                  [es, mask.stride(2) * es, mask.stride(1) * es, mask.stride(0) * es])
+
+
+def _ref(t):
+    return None if t is None else ctypes.byref(t)
+
+
+class Context:
+    """Owns an rkv_ctx (copy stream, events, scratch ring, partials workspace)."""
+
+    def __init__(self, device: int = 0):
+        self.lib = load()
+        h = ctypes.c_void_p()
+        check(self.lib.rkv_create(int(device), ctypes.byref(h)), "rkv_create")
+        self.h = h
+
+    def close(self):
+        if getattr(self, "h", None):
+            self.lib.rkv_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *a):
+        self.close()
+
+    # -- configuration
+    def reserve(self, max_tile_bytes_k=0, max_tile_bytes_v=0, n_slots=0, max_partial_floats=0):
+        check(self.lib.rkv_reserve(self.h, int(max_tile_bytes_k), int(max_tile_bytes_v), int(n_slots),
+                                   int(max_partial_floats)), "rkv_reserve")
+
+    def set_lift_mode(self, mode: int):
+        check(self.lib.rkv_set_lift_mode(self.h, int(mode)), "rkv_set_lift_mode")
+
+    def set_splits(self, splits: int):
+        check(self.lib.rkv_set_splits(self.h, int(splits)), "rkv_set_splits")
+
+    def set_lift_timing(self, on: bool):
+        check(self.lib.rkv_set_lift_timing(self.h, int(bool(on))), "rkv_set_lift_timing")
+
+    def lift_timing_ms(self):
+        tot, span, n = ctypes.c_float(), ctypes.c_float(), ctypes.c_int()
+        check(self.lib.rkv_lift_timing_ms(self.h, ctypes.byref(tot), ctypes.byref(span), ctypes.byref(n)),
+              "rkv_lift_timing_ms")
+        return tot.value, span.value, n.value
+
+    def stats(self) -> dict:
+        s = RkvStats()
+        check(self.lib.rkv_get_stats(self.h, ctypes.byref(s)), "rkv_get_stats")
+        return {f: getattr(s, f) for f, _ in RkvStats._fields_}
+
+    # -- attention
+    def attn_decode(self, q, k_win, v_win, k_tail, v_tail, mask, wc, tile_kv, scale, o, lse=None,
+                    stream=None):
+        """Tensors are rkv_tensor descriptors (see q_desc / kv_desc / mask_desc) or None."""
+        check(self.lib.rkv_attn_decode(self.h, _ref(q), _ref(k_win), _ref(v_win), _ref(k_tail), _ref(v_tail),
+                                       _ref(mask), int(wc), int(tile_kv), float(scale), _ptr(o), _ptr(lse),
+                                       _stream(stream)), "rkv_attn_decode")
+
+    def attn_prefill(self, q, k_win, v_win, k_tail, v_tail, mask, wc, tile_kv, scale, q_pos0, o, lse=None,
+                     stream=None):
+        check(self.lib.rkv_attn_prefill(self.h, _ref(q), _ref(k_win), _ref(v_win), _ref(k_tail), _ref(v_tail),
+                                        _ref(mask), int(wc), int(tile_kv), float(scale), int(q_pos0), _ptr(o),
+                                        _ptr(lse), _stream(stream)), "rkv_attn_prefill")
+
+    def attn_rows(self, q, k_pool, v_pool, kv_rows, n_kv, mask, scale, o, lse=None, stream=None):
+        check(self.lib.rkv_attn_rows(self.h, _ref(q), _ref(k_pool), _ref(v_pool), _ptr(kv_rows), int(n_kv),
+                                     _ref(mask), float(scale), _ptr(o), _ptr(lse), _stream(stream)),
+              "rkv_attn_rows")
+
+    def attn_partial(self, q, k, v, mask, kv_pos0, q_pos0, scale, partial, stream=None):
+        check(self.lib.rkv_attn_partial(self.h, _ref(q), _ref(k), _ref(v), _ref(mask), int(kv_pos0),
+                                        int(q_pos0), float(scale), _ptr(partial), _stream(stream)),
+              "rkv_attn_partial")
+
+    def tail_lift(self, host_src, nbytes: int, slot: int, mode: int = RKV_LIFT_BULK, copy_stream=None) -> int:
+        dst = ctypes.c_void_p()
+        cs = ctypes.c_void_p(0) if copy_stream is None else _stream(copy_stream)
+        check(self.lib.rkv_tail_lift(self.h, _ptr(host_src), int(nbytes), int(slot), int(mode),
+                                     ctypes.byref(dst), cs), "rkv_tail_lift")
+        return int(dst.value or 0)
+
+
+def lse_merge(partials, n_seg: int, n_rows: int, o, lse=None, stream=None):
+    lib = load()
+    check(lib.rkv_lse_merge(_ptr(partials), int(n_seg), int(n_rows), 128, _ptr(o), _ptr(lse), _stream(stream)),
+          "rkv_lse_merge")
+
+
+def dequant_rows(src, type_id: int, n_rows: int, row_stride: int, dst, stream=None):
+    lib = load()
+    check(lib.rkv_dequant_rows(_ptr(src), int(type_id), int(n_rows), int(row_stride), _ptr(dst),
+                               _stream(stream)), "rkv_dequant_rows")
+
+
+def version() -> str:
+    return load().rkv_version().decode()

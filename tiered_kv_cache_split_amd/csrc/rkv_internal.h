@@ -1,0 +1,57 @@
+// Internal interface between the host runtime (rkv_runtime.cpp) and the gfx950 kernels
+// (rkv_kernels.hip).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rkv {
+
+constexpr int kHeadDim = 128;          // d == dv for every kernel here
+constexpr int kPartialStride = 2 + kHeadDim;
+constexpr int kMaxRowsVec = 8;         // vector kernel: n_q * gqa rows per KV head
+constexpr int kChunk = 64;             // cells per wave iteration in the vector kernel
+
+enum { T_F32 = 0, T_F16 = 1, T_Q4_0 = 2, T_Q8_0 = 8 };
+
+// One device-resident key segment processed by one kernel launch.
+struct SegParams {
+    // queries: element strides of query i, head h and sequence b
+    const _Float16 *q;
+    int64_t q_s1, q_s2, q_s3;
+    // keys/values of the segment: byte strides per cell and per KV head
+    const uint8_t *k, *v;
+    int64_t k_s1, k_s2, v_s1, v_s2;
+    // optional row list (unified pool): key j of sequence b is cell rows[j + rows_s*b]
+    const int32_t *rows;
+    int64_t rows_s;
+    // optional additive binary16 mask: element strides of query i and sequence b;
+    // column = pos0 + j (global key position)
+    const _Float16 *mask;
+    int64_t m_s1, m_s3;
+    int64_t n_cells;   // keys in the segment
+    int64_t pos0;      // global position of key 0
+    int64_t q_pos0;    // >= 0: causal, query i at q_pos0 + i; -1: none
+    int cells_per_split, n_splits;
+    int n_head, n_head_kv, n_q, n_seq, gqa;
+    float scale_log2;  // scale * log2(e)
+    float *partials;   // [slot][n_rows][2 + 128]
+    int slot0;         // first partial slot used by this segment
+    int64_t n_rows;    // n_head * n_q * n_seq
+};
+
+// Launches; every function returns a hipError_t and checks nothing the host has not.
+hipError_t launch_decode_segment(const SegParams &p, int k_type, int v_type, hipStream_t s);
+hipError_t launch_prefill_segment(const SegParams &p, int k_type, int v_type, hipStream_t s);
+// Blocks the prefill kernel uses per (q tile, KV head) along the key axis.
+int prefill_rows_per_block();
+int prefill_keys_per_iter();
+hipError_t launch_merge(const float *partials, int n_seg, int64_t n_rows, float *o,
+                        float *lse, float *partial_out, hipStream_t s);
+// Writes (M=-inf, S=0, VKQ=0) for n_rows rows into partial slot 0.
+hipError_t launch_empty_partials(float *partials, int64_t n_rows, hipStream_t s);
+hipError_t launch_uva_read(const void *host_src, void *dst, int64_t nbytes, hipStream_t s);
+hipError_t launch_dequant_rows(const void *src, int type, int64_t n_rows, int64_t row_stride,
+                               float *dst, hipStream_t s);
+
+}  // namespace rkv

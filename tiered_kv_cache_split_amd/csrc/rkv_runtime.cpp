@@ -1,0 +1,820 @@
+// Host runtime of librkv: the C ABI declared in include/rkv.h.
+//
+// Responsibilities: argument validation (before any device work), the segment planner
+// (device window split-K, tail tiles that never straddle wc, global mask offsets), the
+// tail lift pipeline (persistent grow-only scratch ring, context-owned copy stream,
+// pre-created events, double buffer) and the partials workspace.
+//
+// Sources: opencoti-llamafile patch 0070-rolling-kv (fattn.cu ggml_cuda_streaming_flash_attn:
+// window and tail tiled separately, mask sliced at the global offset, copy stream with
+// copy_done/compute_done events created outside graph capture, an entry event that orders
+// the copy stream after earlier compute -- bug-255) and patch
+// 0102-fattn-bulk-h2d-scratch-ring (bulk raw-byte lift of a host tail into a persistent
+// per-slot scratch ring sized for the worst-case tile, never allocated inside capture).
+#include "rkv.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "rkv_internal.h"
+
+using namespace rkv;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int status, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return status;
+}
+
+int hip_fail(hipError_t e, const char *what) {
+    return fail(RKV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define RKV_HIP(call)                                              \
+    do {                                                           \
+        hipError_t e_ = (call);                                    \
+        if (e_ != hipSuccess) return hip_fail(e_, #call);          \
+    } while (0)
+
+constexpr int kMaxSlots = 4;
+constexpr int kMaxLiftTiming = 64;
+
+int64_t type_block_bytes(int t) {
+    switch (t) {
+        case RKV_TYPE_F16: return 2;
+        case RKV_TYPE_F32: return 4;
+        case RKV_TYPE_Q8_0: return 34;
+        case RKV_TYPE_Q4_0: return 18;
+        default: return 0;
+    }
+}
+int64_t row_bytes(int t) {
+    switch (t) {
+        case RKV_TYPE_F16: return 256;
+        case RKV_TYPE_Q8_0: return 136;
+        case RKV_TYPE_Q4_0: return 72;
+        default: return 0;
+    }
+}
+
+enum class Mem { Device, PinnedHost, Other };
+
+Mem pointer_kind(const void *p) {
+    hipPointerAttribute_t a;
+    std::memset(&a, 0, sizeof a);
+    hipError_t e = hipPointerGetAttributes(&a, p);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();  // clear the sticky error of probing an unknown pointer
+        return Mem::Other;
+    }
+    if (a.type == hipMemoryTypeDevice || a.type == hipMemoryTypeManaged) return Mem::Device;
+    if (a.type == hipMemoryTypeHost) return Mem::PinnedHost;
+    return Mem::Other;
+}
+
+int check_device_ptr(const void *p, const char *name) {
+    if (!p) return fail(RKV_ERR_ARG, "%s is NULL", name);
+    if (pointer_kind(p) != Mem::Device) return fail(RKV_ERR_ARG, "%s is not device memory", name);
+    return RKV_OK;
+}
+
+// K/V tensor [128, n_cells, n_head_kv, 1] with contiguous rows.
+int check_kv(const rkv_tensor *t, const char *name, bool is_k) {
+    if (!t) return fail(RKV_ERR_ARG, "%s is NULL", name);
+    const bool ok_type = is_k ? (t->type == RKV_TYPE_F16 || t->type == RKV_TYPE_Q8_0)
+                              : (t->type == RKV_TYPE_F16 || t->type == RKV_TYPE_Q4_0);
+    if (!ok_type) return fail(RKV_ERR_UNSUPPORTED, "%s: type %d not supported", name, t->type);
+    if (t->ne[0] != kHeadDim) return fail(RKV_ERR_UNSUPPORTED, "%s: head dim %lld != 128", name, (long long)t->ne[0]);
+    if (t->ne[1] < 0 || t->ne[2] <= 0 || t->ne[3] != 1)
+        return fail(RKV_ERR_ARG, "%s: bad shape [%lld,%lld,%lld,%lld]", name, (long long)t->ne[0],
+                    (long long)t->ne[1], (long long)t->ne[2], (long long)t->ne[3]);
+    if (t->ne[1] >= (int64_t)1 << 31) return fail(RKV_ERR_UNSUPPORTED, "%s: more than 2^31 cells", name);
+    if (t->nb[0] != type_block_bytes(t->type)) return fail(RKV_ERR_ARG, "%s: rows must be contiguous (nb[0])", name);
+    const int64_t rb = row_bytes(t->type);
+    if (t->ne[1] > 1 && t->nb[1] < rb) return fail(RKV_ERR_ARG, "%s: nb[1] smaller than a row", name);
+    if (t->ne[2] > 1 && t->nb[2] < rb) return fail(RKV_ERR_ARG, "%s: nb[2] smaller than a row", name);
+    if ((t->nb[1] | t->nb[2]) % 8 != 0 || ((uintptr_t)t->data) % 8 != 0)
+        return fail(RKV_ERR_UNSUPPORTED, "%s: data and nb[1], nb[2] must be multiples of 8 bytes", name);
+    if (t->nb[1] >= ((int64_t)1 << 25) || t->nb[1] < 0 || t->nb[2] < 0)
+        return fail(RKV_ERR_UNSUPPORTED, "%s: cell stride beyond 32 MiB", name);
+    if (t->ne[1] > 0 && !t->data) return fail(RKV_ERR_ARG, "%s: data is NULL", name);
+    return RKV_OK;
+}
+
+int check_q(const rkv_tensor *q, bool allow_seq) {
+    if (!q || !q->data) return fail(RKV_ERR_ARG, "q is NULL");
+    if (q->type != RKV_TYPE_F16) return fail(RKV_ERR_UNSUPPORTED, "q must be F16");
+    if (q->ne[0] != kHeadDim) return fail(RKV_ERR_UNSUPPORTED, "q head dim must be 128");
+    if (q->ne[1] <= 0 || q->ne[2] <= 0 || q->ne[3] <= 0) return fail(RKV_ERR_ARG, "q: bad shape");
+    if (!allow_seq && q->ne[3] != 1) return fail(RKV_ERR_ARG, "q: ne[3] must be 1");
+    if (q->nb[0] != 2) return fail(RKV_ERR_ARG, "q rows must be contiguous");
+    if ((q->nb[1] | q->nb[2] | q->nb[3]) % 4 != 0 || ((uintptr_t)q->data) % 4 != 0)
+        return fail(RKV_ERR_UNSUPPORTED, "q data and strides must be multiples of 4 bytes");
+    return check_device_ptr(q->data, "q");
+}
+
+int check_mask(const rkv_tensor *m, int64_t n_kv, int64_t n_q, int64_t n_seq) {
+    if (!m) return RKV_OK;
+    if (!m->data) return fail(RKV_ERR_ARG, "mask data is NULL");
+    if (m->type != RKV_TYPE_F16) return fail(RKV_ERR_UNSUPPORTED, "mask must be F16");
+    if (m->nb[0] != 2) return fail(RKV_ERR_ARG, "mask columns must be contiguous");
+    if (m->ne[0] < n_kv || m->ne[1] < n_q)
+        return fail(RKV_ERR_ARG, "mask [%lld,%lld] smaller than [n_kv=%lld, n_q=%lld]", (long long)m->ne[0],
+                    (long long)m->ne[1], (long long)n_kv, (long long)n_q);
+    if (m->ne[3] != 1 && m->ne[3] != n_seq) return fail(RKV_ERR_ARG, "mask ne[3] must be 1 or n_seq");
+    if ((m->nb[1] | m->nb[3]) % 2 != 0) return fail(RKV_ERR_ARG, "mask strides must be even");
+    return check_device_ptr(m->data, "mask");
+}
+
+int same_kv_shape(const rkv_tensor *a, const rkv_tensor *b, const char *what) {
+    if (a->type != b->type || a->ne[2] != b->ne[2])
+        return fail(RKV_ERR_ARG, "%s: window and tail disagree in type or n_head_kv", what);
+    return RKV_OK;
+}
+
+}  // namespace
+
+struct rkv_ctx {
+    int device = 0;
+    int n_cu = 256;
+    hipStream_t copy_stream = nullptr;
+    hipEvent_t copy_done[kMaxSlots] = {};
+    hipEvent_t compute_done[kMaxSlots] = {};
+    hipEvent_t entry = nullptr;
+    hipEvent_t lift_t0[kMaxLiftTiming] = {}, lift_t1[kMaxLiftTiming] = {};
+    bool lift_timing = false;
+    int n_lift_timed = 0;
+    void *scr_k[kMaxSlots] = {};
+    void *scr_v[kMaxSlots] = {};
+    size_t cap_k[kMaxSlots] = {};
+    size_t cap_v[kMaxSlots] = {};
+    int n_slots = 2;
+    float *partials = nullptr;
+    size_t partials_cap = 0;  // floats
+    int lift_mode = RKV_LIFT_BULK;
+    int splits_override = 0;
+    rkv_stats stats = {};
+};
+
+namespace {
+
+bool stream_capturing(hipStream_t s) {
+    hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &st) != hipSuccess) {
+        (void)hipGetLastError();
+        return false;
+    }
+    return st == hipStreamCaptureStatusActive;
+}
+
+int ensure_device(rkv_ctx *ctx) {
+    int cur = -1;
+    RKV_HIP(hipGetDevice(&cur));
+    if (cur != ctx->device) RKV_HIP(hipSetDevice(ctx->device));
+    return RKV_OK;
+}
+
+int grow(void **buf, size_t *cap, size_t need, hipStream_t s) {
+    if (*cap >= need) return RKV_OK;
+    if (stream_capturing(s))
+        return fail(RKV_ERR_CAPTURE, "workspace must grow to %zu bytes while the stream is capturing; call rkv_reserve first", need);
+    if (*buf) {
+        RKV_HIP(hipDeviceSynchronize());  // earlier work may still read the old buffer
+        RKV_HIP(hipFree(*buf));
+        *buf = nullptr;
+        *cap = 0;
+    }
+    hipError_t e = hipMalloc(buf, need);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        *buf = nullptr;
+        return fail(RKV_ERR_NOMEM, "hipMalloc(%zu) failed", need);
+    }
+    *cap = need;
+    return RKV_OK;
+}
+
+int ensure_partials(rkv_ctx *ctx, int64_t floats, hipStream_t s) {
+    void *p = ctx->partials;
+    size_t cap = ctx->partials_cap * sizeof(float);
+    int st = grow(&p, &cap, (size_t)floats * sizeof(float), s);
+    ctx->partials = static_cast<float *>(p);
+    ctx->partials_cap = cap / sizeof(float);
+    return st;
+}
+
+// Split-K factor of a device segment for the vector kernel: enough workgroups to fill the
+// chip (about eight waves per CU) while keeping at least 256 cells per split.
+int vec_splits(const rkv_ctx *ctx, int64_t n_cells, int64_t n_groups) {
+    if (ctx->splits_override > 0) return (int)std::max<int64_t>(1, std::min<int64_t>(ctx->splits_override, (n_cells + kChunk - 1) / kChunk));
+    if (n_cells <= 0) return 1;
+    const int64_t target_blocks = 8LL * ctx->n_cu;
+    int64_t want = (target_blocks + n_groups - 1) / std::max<int64_t>(1, n_groups);
+    const int64_t max_by_len = std::max<int64_t>(1, n_cells / 256);
+    want = std::max<int64_t>(1, std::min(want, max_by_len));
+    return (int)want;
+}
+
+struct Seg {
+    const uint8_t *k, *v;
+    int64_t k_s1, k_s2, v_s1, v_s2;
+    int64_t n_cells, pos0;
+};
+
+void fill_q(SegParams &p, const rkv_tensor *q) {
+    p.q = static_cast<const _Float16 *>(q->data);
+    p.q_s1 = q->nb[1] / 2;
+    p.q_s2 = q->nb[2] / 2;
+    p.q_s3 = q->nb[3] / 2;
+}
+
+void fill_mask(SegParams &p, const rkv_tensor *m) {
+    p.mask = m ? static_cast<const _Float16 *>(m->data) : nullptr;
+    p.m_s1 = m ? m->nb[1] / 2 : 0;
+    p.m_s3 = (m && m->ne[3] > 1) ? m->nb[3] / 2 : 0;
+}
+
+// Split-K plan of one device segment: cells per split and number of splits.  The vector
+// kernel walks 64-cell chunks; the MFMA kernel walks key tiles of prefill_keys_per_iter().
+void seg_plan(const rkv_ctx *ctx, int64_t n_cells, const SegParams &p, bool mfma, int64_t &cps, int &n_splits) {
+    if (mfma) {
+        const int kpi = prefill_keys_per_iter();
+        const int64_t q_tiles = ((int64_t)p.gqa * p.n_q + prefill_rows_per_block() - 1) / prefill_rows_per_block();
+        const int64_t groups = q_tiles * p.n_head_kv * p.n_seq;
+        int64_t want = ctx->splits_override > 0 ? ctx->splits_override
+                                                : std::max<int64_t>(1, (2LL * ctx->n_cu + groups - 1) / groups);
+        want = std::min<int64_t>(want, std::max<int64_t>(1, (n_cells + kpi - 1) / kpi));
+        cps = (n_cells + want - 1) / want;
+        cps = std::max<int64_t>(kpi, (cps + kpi - 1) / kpi * kpi);
+    } else {
+        const int splits = vec_splits(ctx, n_cells, (int64_t)p.n_head_kv * p.n_seq);
+        cps = (n_cells + splits - 1) / splits;
+        cps = std::max<int64_t>(kChunk, (cps + kChunk - 1) / kChunk * kChunk);
+    }
+    n_splits = (int)std::max<int64_t>(1, (n_cells + cps - 1) / cps);
+}
+
+int planned_slots(const rkv_ctx *ctx, int64_t n_cells, const SegParams &p, bool mfma) {
+    int64_t cps;
+    int n;
+    seg_plan(ctx, n_cells, p, mfma, cps, n);
+    return n;
+}
+
+// Launch one device segment; `slot` advances by the splits it used.
+int run_segment(rkv_ctx *ctx, SegParams base, const Seg &sg, bool mfma, int k_type, int v_type,
+                int &slot, hipStream_t s) {
+    SegParams p = base;
+    p.k = sg.k;
+    p.v = sg.v;
+    p.k_s1 = sg.k_s1;
+    p.k_s2 = sg.k_s2;
+    p.v_s1 = sg.v_s1;
+    p.v_s2 = sg.v_s2;
+    p.n_cells = sg.n_cells;
+    p.pos0 = sg.pos0;
+    p.slot0 = slot;
+    int64_t cps;
+    seg_plan(ctx, sg.n_cells, p, mfma, cps, p.n_splits);
+    p.cells_per_split = (int)cps;
+    const hipError_t e = mfma ? launch_prefill_segment(p, k_type, v_type, s) : launch_decode_segment(p, k_type, v_type, s);
+    if (e != hipSuccess) return hip_fail(e, mfma ? "prefill segment launch" : "decode segment launch");
+    slot += p.n_splits;
+    ctx->stats.n_segments += 1;
+    return RKV_OK;
+}
+
+// Geometry of a host tail for tile lifting: each tile of `cells` cells is one contiguous
+// span (cell-major: all heads inside a cell) or n_head_kv spans (head-major).
+struct TailGeom {
+    bool cell_major;
+    int64_t nb1, nb2, n_head_kv;
+    int64_t tile_bytes(int64_t cells) const { return cell_major ? cells * nb1 : n_head_kv * cells * nb1; }
+};
+
+int tail_geom(const rkv_tensor *t, TailGeom &g) {
+    const int64_t rb = row_bytes(t->type);
+    g.nb1 = t->nb[1];
+    g.nb2 = t->nb[2];
+    g.n_head_kv = t->ne[2];
+    if (t->ne[2] == 1 || (t->nb[2] * (t->ne[2] - 1) + rb <= t->nb[1])) {
+        g.cell_major = true;
+        return RKV_OK;
+    }
+    if (t->nb[1] == rb && t->nb[2] >= t->ne[1] * rb) {
+        g.cell_major = false;
+        return RKV_OK;
+    }
+    return fail(RKV_ERR_UNSUPPORTED, "host tail must be cell-major (heads inside a cell) or head-major contiguous");
+}
+
+// Enqueue the lift of cells [loc, loc+cells) of a host tail tensor into ring slot `slot`.
+int lift_tile(rkv_ctx *ctx, const rkv_tensor *t, const TailGeom &g, int64_t loc, int64_t cells,
+              int64_t tile_cap_cells, void *dst, hipStream_t cs) {
+    const uint8_t *src = static_cast<const uint8_t *>(t->data) + loc * g.nb1;
+    if (g.cell_major) {
+        const int64_t bytes = cells * g.nb1;
+        if (ctx->lift_mode == RKV_LIFT_UVA) {
+            hipError_t e = launch_uva_read(src, dst, bytes, cs);
+            if (e != hipSuccess) return hip_fail(e, "uva lift");
+        } else {
+            RKV_HIP(hipMemcpyAsync(dst, src, bytes, hipMemcpyHostToDevice, cs));
+        }
+        ctx->stats.lift_bytes += bytes;
+    } else {
+        const int64_t width = cells * g.nb1;
+        if (ctx->lift_mode == RKV_LIFT_UVA) {
+            for (int64_t h = 0; h < g.n_head_kv; ++h) {
+                hipError_t e = launch_uva_read(src + h * g.nb2, static_cast<uint8_t *>(dst) + h * tile_cap_cells * g.nb1, width, cs);
+                if (e != hipSuccess) return hip_fail(e, "uva lift");
+            }
+        } else {
+            RKV_HIP(hipMemcpy2DAsync(dst, (size_t)(tile_cap_cells * g.nb1), src, (size_t)g.nb2, (size_t)width,
+                                     (size_t)g.n_head_kv, hipMemcpyHostToDevice, cs));
+        }
+        ctx->stats.lift_bytes += width * g.n_head_kv;
+    }
+    return RKV_OK;
+}
+
+// Common body of decode and prefill.
+int attn_window_tail(rkv_ctx *ctx, const rkv_tensor *q, const rkv_tensor *k_win,
+                     const rkv_tensor *v_win, const rkv_tensor *k_tail, const rkv_tensor *v_tail,
+                     const rkv_tensor *mask, int64_t wc, int64_t tile_kv, float scale,
+                     int64_t q_pos0, bool mfma, float *o, float *lse, hipStream_t stream) {
+    if (!ctx) return fail(RKV_ERR_ARG, "ctx is NULL");
+    int st = check_q(q, false);
+    if (st) return st;
+    if (wc < 0) return fail(RKV_ERR_ARG, "wc < 0");
+    if (tile_kv <= 0) return fail(RKV_ERR_ARG, "tile_kv must be > 0");
+    if (!std::isfinite(scale)) return fail(RKV_ERR_ARG, "scale is not finite");
+    if (!o) return fail(RKV_ERR_ARG, "o is NULL");
+    if (q_pos0 < -1) return fail(RKV_ERR_ARG, "q_pos0 must be >= -1");
+    if ((k_tail == nullptr) != (v_tail == nullptr)) return fail(RKV_ERR_ARG, "k_tail and v_tail must both be given or both NULL");
+    if (wc > 0 && (!k_win || !v_win)) return fail(RKV_ERR_ARG, "window tensors missing while wc > 0");
+    const rkv_tensor *kref = k_win ? k_win : k_tail;
+    const rkv_tensor *vref = v_win ? v_win : v_tail;
+    if (!kref) return fail(RKV_ERR_ARG, "no K/V given");
+    if (k_win) {
+        if ((st = check_kv(k_win, "k_win", true)) || (st = check_kv(v_win, "v_win", false))) return st;
+        if (k_win->ne[1] < wc || v_win->ne[1] < wc) return fail(RKV_ERR_ARG, "window tensors hold fewer than wc cells");
+        if (k_win->ne[2] != v_win->ne[2]) return fail(RKV_ERR_ARG, "k_win and v_win disagree in n_head_kv");
+    }
+    int64_t n_tail = 0;
+    Mem tail_kind = Mem::Device;
+    if (k_tail) {
+        if ((st = check_kv(k_tail, "k_tail", true)) || (st = check_kv(v_tail, "v_tail", false))) return st;
+        if (k_tail->ne[1] != v_tail->ne[1] || k_tail->ne[2] != v_tail->ne[2])
+            return fail(RKV_ERR_ARG, "k_tail and v_tail disagree in shape");
+        if (k_win && ((st = same_kv_shape(k_win, k_tail, "K")) || (st = same_kv_shape(v_win, v_tail, "V")))) return st;
+        n_tail = k_tail->ne[1];
+        if (n_tail > 0) {
+            const Mem a = pointer_kind(k_tail->data), b = pointer_kind(v_tail->data);
+            if (a != b) return fail(RKV_ERR_ARG, "k_tail and v_tail live in different memory kinds");
+            if (a == Mem::Other) return fail(RKV_ERR_ARG, "tail is neither device nor pinned host memory (pageable memory cannot be lifted)");
+            tail_kind = a;
+        }
+    }
+    const int64_t n_head = q->ne[2], n_q = q->ne[1];
+    const int64_t n_head_kv = kref->ne[2];
+    if (n_head % n_head_kv != 0) return fail(RKV_ERR_ARG, "n_head %% n_head_kv != 0");
+    const int64_t gqa = n_head / n_head_kv;
+    if (!mfma && gqa * n_q > kMaxRowsVec)
+        return fail(RKV_ERR_UNSUPPORTED, "decode handles n_q*gqa <= %d rows per KV head (got %lld); use rkv_attn_prefill",
+                    kMaxRowsVec, (long long)(gqa * n_q));
+    const int64_t n_kv = wc + n_tail;
+    if ((st = check_mask(mask, n_kv, n_q, 1))) return st;
+    if ((st = check_device_ptr(o, "o"))) return st;
+    if (lse && (st = check_device_ptr(lse, "lse"))) return st;
+    if (k_win && wc > 0 && ((st = check_device_ptr(k_win->data, "k_win")) || (st = check_device_ptr(v_win->data, "v_win")))) return st;
+    if ((st = ensure_device(ctx))) return st;
+
+    const int k_type = kref->type, v_type = vref->type;
+    SegParams base{};
+    fill_q(base, q);
+    fill_mask(base, mask);
+    base.rows = nullptr;
+    base.q_pos0 = q_pos0;
+    base.n_head = (int)n_head;
+    base.n_head_kv = (int)n_head_kv;
+    base.n_q = (int)n_q;
+    base.n_seq = 1;
+    base.gqa = (int)gqa;
+    base.scale_log2 = scale * 1.4426950408889634f;
+    base.n_rows = n_head * n_q;
+
+    // ---- plan: window segment, then tail (in place or lifted tiles)
+    const bool lifted = n_tail > 0 && tail_kind == Mem::PinnedHost;
+    const int64_t n_tiles = lifted ? (n_tail + tile_kv - 1) / tile_kv : 0;
+    int64_t total_slots = 0;
+    if (wc > 0) total_slots += planned_slots(ctx, wc, base, mfma);
+    if (n_tail > 0 && !lifted) total_slots += planned_slots(ctx, n_tail, base, mfma);
+    for (int64_t t = 0; t < n_tiles; ++t)
+        total_slots += planned_slots(ctx, std::min(tile_kv, n_tail - t * tile_kv), base, mfma);
+    if (total_slots == 0) total_slots = 1;  // n_kv == 0: one empty partial
+    if ((st = ensure_partials(ctx, total_slots * base.n_rows * kPartialStride, stream))) return st;
+    base.partials = ctx->partials;
+
+    ctx->stats = rkv_stats{};
+    ctx->stats.kernel_variant = mfma ? 1 : 0;
+    ctx->stats.lift_mode = ctx->lift_mode;
+    int slot = 0;
+
+    TailGeom gk{}, gv{};
+    int n_slots = 0;
+    if (lifted) {
+        if ((st = tail_geom(k_tail, gk)) || (st = tail_geom(v_tail, gv))) return st;
+        n_slots = (int)std::min<int64_t>(ctx->n_slots, n_tiles);
+        const int64_t cap_cells = std::min(tile_kv, n_tail);
+        for (int sl = 0; sl < n_slots; ++sl) {
+            if ((st = grow(&ctx->scr_k[sl], &ctx->cap_k[sl], (size_t)gk.tile_bytes(cap_cells), stream))) return st;
+            if ((st = grow(&ctx->scr_v[sl], &ctx->cap_v[sl], (size_t)gv.tile_bytes(cap_cells), stream))) return st;
+        }
+        // the copy stream starts after all earlier work on the compute stream, so a slot
+        // still read by an earlier call is never overwritten
+        RKV_HIP(hipEventRecord(ctx->entry, stream));
+        RKV_HIP(hipStreamWaitEvent(ctx->copy_stream, ctx->entry, 0));
+    }
+    const int64_t cap_cells = lifted ? std::min(tile_kv, n_tail) : 0;
+    auto lift = [&](int64_t t) -> int {
+        const int sl = (int)(t % n_slots);
+        const int64_t loc = t * tile_kv, cells = std::min(tile_kv, n_tail - loc);
+        const bool timed = ctx->lift_timing && ctx->n_lift_timed < kMaxLiftTiming;
+        if (timed) RKV_HIP(hipEventRecord(ctx->lift_t0[ctx->n_lift_timed], ctx->copy_stream));
+        int r = lift_tile(ctx, k_tail, gk, loc, cells, cap_cells, ctx->scr_k[sl], ctx->copy_stream);
+        if (!r) r = lift_tile(ctx, v_tail, gv, loc, cells, cap_cells, ctx->scr_v[sl], ctx->copy_stream);
+        if (r) return r;
+        if (timed) RKV_HIP(hipEventRecord(ctx->lift_t1[ctx->n_lift_timed++], ctx->copy_stream));
+        RKV_HIP(hipEventRecord(ctx->copy_done[sl], ctx->copy_stream));
+        ctx->stats.n_tail_tiles += 1;
+        return RKV_OK;
+    };
+    if (lifted) {
+        ctx->n_lift_timed = 0;
+        if ((st = lift(0))) return st;
+    }
+
+    if (wc > 0) {
+        const Seg w{static_cast<const uint8_t *>(k_win->data), static_cast<const uint8_t *>(v_win->data),
+                    k_win->nb[1], k_win->nb[2], v_win->nb[1], v_win->nb[2], wc, 0};
+        const int before = slot;
+        if ((st = run_segment(ctx, base, w, mfma, k_type, v_type, slot, stream))) return st;
+        ctx->stats.splits_window = slot - before;
+    }
+    if (n_tail > 0 && !lifted) {
+        const Seg t{static_cast<const uint8_t *>(k_tail->data), static_cast<const uint8_t *>(v_tail->data),
+                    k_tail->nb[1], k_tail->nb[2], v_tail->nb[1], v_tail->nb[2], n_tail, wc};
+        if ((st = run_segment(ctx, base, t, mfma, k_type, v_type, slot, stream))) return st;
+    }
+    for (int64_t t = 0; t < n_tiles; ++t) {
+        const int sl = (int)(t % n_slots);
+        if (t + 1 < n_tiles) {
+            const int ns = (int)((t + 1) % n_slots);
+            if (t + 1 >= n_slots) RKV_HIP(hipStreamWaitEvent(ctx->copy_stream, ctx->compute_done[ns], 0));
+            if ((st = lift(t + 1))) return st;
+        }
+        RKV_HIP(hipStreamWaitEvent(stream, ctx->copy_done[sl], 0));
+        const int64_t loc = t * tile_kv, cells = std::min(tile_kv, n_tail - loc);
+        Seg tile{static_cast<const uint8_t *>(ctx->scr_k[sl]), static_cast<const uint8_t *>(ctx->scr_v[sl]),
+                 gk.nb1, gk.cell_major ? gk.nb2 : cap_cells * gk.nb1,
+                 gv.nb1, gv.cell_major ? gv.nb2 : cap_cells * gv.nb1, cells, wc + loc};
+        if ((st = run_segment(ctx, base, tile, mfma, k_type, v_type, slot, stream))) return st;
+        RKV_HIP(hipEventRecord(ctx->compute_done[sl], stream));
+    }
+    if (slot == 0) {
+        // n_kv == 0: a single empty partial, so every row gets O = 0 and LSE = -inf
+        hipError_t e0 = launch_empty_partials(ctx->partials, base.n_rows, stream);
+        if (e0 != hipSuccess) return hip_fail(e0, "empty partial");
+        slot = 1;
+    }
+    ctx->stats.n_partials = slot;
+    hipError_t e = launch_merge(ctx->partials, slot, base.n_rows, o, lse, nullptr, stream);
+    if (e != hipSuccess) return hip_fail(e, "merge launch");
+    return RKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *rkv_version(void) { return "0.1.0"; }
+
+const char *rkv_strerror(int status) {
+    switch (status) {
+        case RKV_OK: return "ok";
+        case RKV_ERR_ARG: return "invalid argument";
+        case RKV_ERR_UNSUPPORTED: return "unsupported";
+        case RKV_ERR_HIP: return "HIP runtime error";
+        case RKV_ERR_NOMEM: return "out of device memory";
+        case RKV_ERR_CAPTURE: return "allocation needed during stream capture";
+        default: return "unknown status";
+    }
+}
+
+const char *rkv_last_error(void) { return g_err.c_str(); }
+
+int rkv_create(int device, rkv_ctx **out) {
+    if (!out) return fail(RKV_ERR_ARG, "out is NULL");
+    *out = nullptr;
+    int n = 0;
+    hipError_t e = hipGetDeviceCount(&n);
+    if (e != hipSuccess || device < 0 || device >= n) {
+        (void)hipGetLastError();
+        return fail(RKV_ERR_HIP, "device %d not available (%d devices)", device, n);
+    }
+    RKV_HIP(hipSetDevice(device));
+    rkv_ctx *c = new rkv_ctx();
+    c->device = device;
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, device) == hipSuccess && prop.multiProcessorCount > 0)
+        c->n_cu = prop.multiProcessorCount;
+    auto bail = [&](hipError_t err, const char *what) {
+        rkv_destroy(c);
+        return hip_fail(err, what);
+    };
+    if ((e = hipStreamCreateWithFlags(&c->copy_stream, hipStreamNonBlocking)) != hipSuccess) return bail(e, "copy stream");
+    for (int i = 0; i < kMaxSlots; ++i) {
+        if ((e = hipEventCreateWithFlags(&c->copy_done[i], hipEventDisableTiming)) != hipSuccess) return bail(e, "event");
+        if ((e = hipEventCreateWithFlags(&c->compute_done[i], hipEventDisableTiming)) != hipSuccess) return bail(e, "event");
+    }
+    if ((e = hipEventCreateWithFlags(&c->entry, hipEventDisableTiming)) != hipSuccess) return bail(e, "event");
+    for (int i = 0; i < kMaxLiftTiming; ++i) {
+        if ((e = hipEventCreate(&c->lift_t0[i])) != hipSuccess) return bail(e, "timing event");
+        if ((e = hipEventCreate(&c->lift_t1[i])) != hipSuccess) return bail(e, "timing event");
+    }
+    *out = c;
+    return RKV_OK;
+}
+
+void rkv_destroy(rkv_ctx *c) {
+    if (!c) return;
+    int cur = -1;
+    if (hipGetDevice(&cur) == hipSuccess && cur != c->device) (void)hipSetDevice(c->device);
+    (void)hipDeviceSynchronize();
+    for (int i = 0; i < kMaxSlots; ++i) {
+        if (c->scr_k[i]) (void)hipFree(c->scr_k[i]);
+        if (c->scr_v[i]) (void)hipFree(c->scr_v[i]);
+        if (c->copy_done[i]) (void)hipEventDestroy(c->copy_done[i]);
+        if (c->compute_done[i]) (void)hipEventDestroy(c->compute_done[i]);
+    }
+    for (int i = 0; i < kMaxLiftTiming; ++i) {
+        if (c->lift_t0[i]) (void)hipEventDestroy(c->lift_t0[i]);
+        if (c->lift_t1[i]) (void)hipEventDestroy(c->lift_t1[i]);
+    }
+    if (c->entry) (void)hipEventDestroy(c->entry);
+    if (c->partials) (void)hipFree(c->partials);
+    if (c->copy_stream) (void)hipStreamDestroy(c->copy_stream);
+    (void)hipGetLastError();
+    delete c;
+}
+
+int rkv_reserve(rkv_ctx *ctx, int64_t max_tile_bytes_k, int64_t max_tile_bytes_v, int n_slots,
+                int64_t max_partial_floats) {
+    if (!ctx) return fail(RKV_ERR_ARG, "ctx is NULL");
+    if (n_slots < 0 || n_slots > kMaxSlots) return fail(RKV_ERR_ARG, "n_slots must be in [0, %d]", kMaxSlots);
+    if (max_tile_bytes_k < 0 || max_tile_bytes_v < 0 || max_partial_floats < 0) return fail(RKV_ERR_ARG, "negative size");
+    int st = ensure_device(ctx);
+    if (st) return st;
+    if (n_slots > 0) ctx->n_slots = n_slots;
+    for (int sl = 0; sl < ctx->n_slots; ++sl) {
+        if (max_tile_bytes_k > 0 && (st = grow(&ctx->scr_k[sl], &ctx->cap_k[sl], (size_t)max_tile_bytes_k, nullptr))) return st;
+        if (max_tile_bytes_v > 0 && (st = grow(&ctx->scr_v[sl], &ctx->cap_v[sl], (size_t)max_tile_bytes_v, nullptr))) return st;
+    }
+    if (max_partial_floats > 0 && (st = ensure_partials(ctx, max_partial_floats, nullptr))) return st;
+    return RKV_OK;
+}
+
+int rkv_get_stats(const rkv_ctx *ctx, rkv_stats *out) {
+    if (!ctx || !out) return fail(RKV_ERR_ARG, "NULL argument");
+    *out = ctx->stats;
+    return RKV_OK;
+}
+
+int rkv_set_lift_mode(rkv_ctx *ctx, int mode) {
+    if (!ctx) return fail(RKV_ERR_ARG, "ctx is NULL");
+    if (mode != RKV_LIFT_BULK && mode != RKV_LIFT_UVA) return fail(RKV_ERR_ARG, "unknown lift mode %d", mode);
+    ctx->lift_mode = mode;
+    return RKV_OK;
+}
+
+int rkv_set_splits(rkv_ctx *ctx, int splits) {
+    if (!ctx) return fail(RKV_ERR_ARG, "ctx is NULL");
+    if (splits < 0) return fail(RKV_ERR_ARG, "splits < 0");
+    ctx->splits_override = splits;
+    return RKV_OK;
+}
+
+int rkv_set_lift_timing(rkv_ctx *ctx, int on) {
+    if (!ctx) return fail(RKV_ERR_ARG, "ctx is NULL");
+    ctx->lift_timing = on != 0;
+    ctx->n_lift_timed = 0;
+    return RKV_OK;
+}
+
+int rkv_lift_timing_ms(rkv_ctx *ctx, float *total_ms, float *span_ms, int *n_lifts) {
+    if (!ctx || !total_ms) return fail(RKV_ERR_ARG, "NULL argument");
+    float tot = 0.f;
+    for (int i = 0; i < ctx->n_lift_timed; ++i) {
+        RKV_HIP(hipEventSynchronize(ctx->lift_t1[i]));
+        float ms = 0.f;
+        RKV_HIP(hipEventElapsedTime(&ms, ctx->lift_t0[i], ctx->lift_t1[i]));
+        tot += ms;
+    }
+    *total_ms = tot;
+    if (span_ms) {
+        float sp = 0.f;
+        if (ctx->n_lift_timed > 0) RKV_HIP(hipEventElapsedTime(&sp, ctx->lift_t0[0], ctx->lift_t1[ctx->n_lift_timed - 1]));
+        *span_ms = sp;
+    }
+    if (n_lifts) *n_lifts = ctx->n_lift_timed;
+    return RKV_OK;
+}
+
+int rkv_attn_decode(rkv_ctx *ctx, const rkv_tensor *q, const rkv_tensor *k_win, const rkv_tensor *v_win,
+                    const rkv_tensor *k_tail, const rkv_tensor *v_tail, const rkv_tensor *mask, int64_t wc,
+                    int64_t tile_kv, float scale, float *o, float *lse, void *stream) {
+    return attn_window_tail(ctx, q, k_win, v_win, k_tail, v_tail, mask, wc, tile_kv, scale, -1, false, o, lse,
+                            static_cast<hipStream_t>(stream));
+}
+
+int rkv_attn_prefill(rkv_ctx *ctx, const rkv_tensor *q, const rkv_tensor *k_win, const rkv_tensor *v_win,
+                     const rkv_tensor *k_tail, const rkv_tensor *v_tail, const rkv_tensor *mask, int64_t wc,
+                     int64_t tile_kv, float scale, int64_t q_pos0, float *o, float *lse, void *stream) {
+    return attn_window_tail(ctx, q, k_win, v_win, k_tail, v_tail, mask, wc, tile_kv, scale, q_pos0, true, o, lse,
+                            static_cast<hipStream_t>(stream));
+}
+
+int rkv_attn_rows(rkv_ctx *ctx, const rkv_tensor *q, const rkv_tensor *k_pool, const rkv_tensor *v_pool,
+                  const int32_t *kv_rows, int64_t n_kv, const rkv_tensor *mask, float scale, float *o, float *lse,
+                  void *stream_) {
+    hipStream_t stream = static_cast<hipStream_t>(stream_);
+    if (!ctx) return fail(RKV_ERR_ARG, "ctx is NULL");
+    int st = check_q(q, true);
+    if (st) return st;
+    if ((st = check_kv(k_pool, "k_pool", true)) || (st = check_kv(v_pool, "v_pool", false))) return st;
+    if (k_pool->ne[1] != v_pool->ne[1] || k_pool->ne[2] != v_pool->ne[2]) return fail(RKV_ERR_ARG, "k_pool and v_pool disagree in shape");
+    if (n_kv < 0 || n_kv >= ((int64_t)1 << 31)) return fail(RKV_ERR_ARG, "bad n_kv");
+    if (!std::isfinite(scale)) return fail(RKV_ERR_ARG, "scale is not finite");
+    if (!o) return fail(RKV_ERR_ARG, "o is NULL");
+    const int64_t n_head = q->ne[2], n_q = q->ne[1], n_seq = q->ne[3];
+    const int64_t n_head_kv = k_pool->ne[2];
+    if (n_head % n_head_kv != 0) return fail(RKV_ERR_ARG, "n_head %% n_head_kv != 0");
+    const int64_t gqa = n_head / n_head_kv;
+    if (gqa * n_q > kMaxRowsVec) return fail(RKV_ERR_UNSUPPORTED, "rows attention handles n_q*gqa <= %d", kMaxRowsVec);
+    if ((st = check_mask(mask, n_kv, n_q, n_seq))) return st;
+    if (n_kv > 0 && (st = check_device_ptr(kv_rows, "kv_rows"))) return st;
+    if (k_pool->ne[1] > 0 && ((st = check_device_ptr(k_pool->data, "k_pool")) || (st = check_device_ptr(v_pool->data, "v_pool")))) return st;
+    if ((st = check_device_ptr(o, "o"))) return st;
+    if (lse && (st = check_device_ptr(lse, "lse"))) return st;
+    if ((st = ensure_device(ctx))) return st;
+
+    SegParams p{};
+    fill_q(p, q);
+    fill_mask(p, mask);
+    p.rows = kv_rows;
+    p.rows_s = n_kv;
+    p.q_pos0 = -1;
+    p.n_head = (int)n_head;
+    p.n_head_kv = (int)n_head_kv;
+    p.n_q = (int)n_q;
+    p.n_seq = (int)n_seq;
+    p.gqa = (int)gqa;
+    p.scale_log2 = scale * 1.4426950408889634f;
+    p.n_rows = n_head * n_q * n_seq;
+    const int slots = planned_slots(ctx, n_kv, p, false);
+    if ((st = ensure_partials(ctx, (int64_t)slots * p.n_rows * kPartialStride, stream))) return st;
+    p.partials = ctx->partials;
+    ctx->stats = rkv_stats{};
+    int slot = 0;
+    const Seg pool{static_cast<const uint8_t *>(k_pool->data), static_cast<const uint8_t *>(v_pool->data),
+                   k_pool->nb[1], k_pool->nb[2], v_pool->nb[1], v_pool->nb[2], n_kv, 0};
+    if (n_kv > 0) {
+        if ((st = run_segment(ctx, p, pool, false, k_pool->type, v_pool->type, slot, stream))) return st;
+    } else {
+        hipError_t e0 = launch_empty_partials(ctx->partials, p.n_rows, stream);
+        if (e0 != hipSuccess) return hip_fail(e0, "empty partial");
+        slot = 1;
+    }
+    ctx->stats.splits_window = slot;
+    ctx->stats.n_partials = slot;
+    hipError_t e = launch_merge(ctx->partials, slot, p.n_rows, o, lse, nullptr, stream);
+    if (e != hipSuccess) return hip_fail(e, "merge launch");
+    return RKV_OK;
+}
+
+int rkv_attn_partial(rkv_ctx *ctx, const rkv_tensor *q, const rkv_tensor *k, const rkv_tensor *v,
+                     const rkv_tensor *mask, int64_t kv_pos0, int64_t q_pos0, float scale, float *partial,
+                     void *stream_) {
+    hipStream_t stream = static_cast<hipStream_t>(stream_);
+    if (!ctx) return fail(RKV_ERR_ARG, "ctx is NULL");
+    int st = check_q(q, false);
+    if (st) return st;
+    if ((st = check_kv(k, "k", true)) || (st = check_kv(v, "v", false))) return st;
+    if (k->ne[1] != v->ne[1] || k->ne[2] != v->ne[2]) return fail(RKV_ERR_ARG, "k and v disagree in shape");
+    if (kv_pos0 < 0 || q_pos0 < -1) return fail(RKV_ERR_ARG, "bad positions");
+    if (!std::isfinite(scale)) return fail(RKV_ERR_ARG, "scale is not finite");
+    const int64_t n_head = q->ne[2], n_q = q->ne[1], n_head_kv = k->ne[2];
+    if (n_head % n_head_kv != 0) return fail(RKV_ERR_ARG, "n_head %% n_head_kv != 0");
+    const int64_t gqa = n_head / n_head_kv;
+    const bool mfma = gqa * n_q > kMaxRowsVec;
+    if ((st = check_mask(mask, kv_pos0 + k->ne[1], n_q, 1))) return st;
+    if (k->ne[1] > 0 && ((st = check_device_ptr(k->data, "k")) || (st = check_device_ptr(v->data, "v")))) return st;
+    if ((st = check_device_ptr(partial, "partial"))) return st;
+    if ((st = ensure_device(ctx))) return st;
+    SegParams p{};
+    fill_q(p, q);
+    fill_mask(p, mask);
+    p.q_pos0 = q_pos0;
+    p.n_head = (int)n_head;
+    p.n_head_kv = (int)n_head_kv;
+    p.n_q = (int)n_q;
+    p.n_seq = 1;
+    p.gqa = (int)gqa;
+    p.scale_log2 = scale * 1.4426950408889634f;
+    p.n_rows = n_head * n_q;
+    const int slots = planned_slots(ctx, k->ne[1], p, mfma);
+    if ((st = ensure_partials(ctx, (int64_t)slots * p.n_rows * kPartialStride, stream))) return st;
+    p.partials = ctx->partials;
+    ctx->stats = rkv_stats{};
+    ctx->stats.kernel_variant = mfma ? 1 : 0;
+    int slot = 0;
+    const Seg sg{static_cast<const uint8_t *>(k->data), static_cast<const uint8_t *>(v->data), k->nb[1], k->nb[2],
+                 v->nb[1], v->nb[2], k->ne[1], kv_pos0};
+    if (k->ne[1] > 0) {
+        if ((st = run_segment(ctx, p, sg, mfma, k->type, v->type, slot, stream))) return st;
+    } else {
+        hipError_t e0 = launch_empty_partials(ctx->partials, p.n_rows, stream);
+        if (e0 != hipSuccess) return hip_fail(e0, "empty partial");
+        slot = 1;
+    }
+    ctx->stats.n_partials = slot;
+    hipError_t e = launch_merge(ctx->partials, slot, p.n_rows, nullptr, nullptr, partial, stream);
+    if (e != hipSuccess) return hip_fail(e, "merge launch");
+    return RKV_OK;
+}
+
+int rkv_lse_merge(const float *partials, int n_seg, int64_t n_rows, int dv, float *o, float *lse, void *stream) {
+    if (dv != kHeadDim) return fail(RKV_ERR_UNSUPPORTED, "dv must be 128");
+    if (n_seg <= 0 || n_rows < 0) return fail(RKV_ERR_ARG, "n_seg must be > 0 and n_rows >= 0");
+    if (n_rows == 0) return RKV_OK;
+    int st = check_device_ptr(partials, "partials");
+    if (st) return st;
+    if ((st = check_device_ptr(o, "o"))) return st;
+    if (lse && (st = check_device_ptr(lse, "lse"))) return st;
+    hipError_t e = launch_merge(partials, n_seg, n_rows, o, lse, nullptr, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "merge launch");
+    return RKV_OK;
+}
+
+int rkv_tail_lift(rkv_ctx *ctx, const void *host_src, int64_t nbytes, int slot, int mode, void **dev_dst,
+                  void *copy_stream_) {
+    if (!ctx || !host_src || !dev_dst) return fail(RKV_ERR_ARG, "NULL argument");
+    if (slot < 0 || slot >= kMaxSlots) return fail(RKV_ERR_ARG, "slot out of range");
+    if (nbytes < 0) return fail(RKV_ERR_ARG, "nbytes < 0");
+    if (mode != RKV_LIFT_BULK && mode != RKV_LIFT_UVA) return fail(RKV_ERR_ARG, "unknown lift mode");
+    if (pointer_kind(host_src) != Mem::PinnedHost) return fail(RKV_ERR_ARG, "host_src is not pinned host memory");
+    int st = ensure_device(ctx);
+    if (st) return st;
+    hipStream_t cs = copy_stream_ ? static_cast<hipStream_t>(copy_stream_) : ctx->copy_stream;
+    if ((st = grow(&ctx->scr_k[slot], &ctx->cap_k[slot], (size_t)std::max<int64_t>(nbytes, 1), cs))) return st;
+    if (mode == RKV_LIFT_UVA) {
+        hipError_t e = launch_uva_read(host_src, ctx->scr_k[slot], nbytes, cs);
+        if (e != hipSuccess) return hip_fail(e, "uva lift");
+    } else if (nbytes > 0) {
+        RKV_HIP(hipMemcpyAsync(ctx->scr_k[slot], host_src, (size_t)nbytes, hipMemcpyHostToDevice, cs));
+    }
+    RKV_HIP(hipEventRecord(ctx->copy_done[slot], cs));
+    *dev_dst = ctx->scr_k[slot];
+    return RKV_OK;
+}
+
+int rkv_dequant_rows(const void *src, int type, int64_t n_rows, int64_t row_stride, float *dst, void *stream) {
+    if (type != RKV_TYPE_F16 && type != RKV_TYPE_Q8_0 && type != RKV_TYPE_Q4_0)
+        return fail(RKV_ERR_UNSUPPORTED, "type %d", type);
+    if (n_rows < 0 || row_stride < row_bytes(type)) return fail(RKV_ERR_ARG, "bad n_rows or row_stride");
+    if (n_rows == 0) return RKV_OK;
+    if (row_stride % 2 != 0 || ((uintptr_t)src) % 2 != 0) return fail(RKV_ERR_UNSUPPORTED, "rows must be 2-byte aligned");
+    int st = check_device_ptr(src, "src");
+    if (st) return st;
+    if ((st = check_device_ptr(dst, "dst"))) return st;
+    hipError_t e = launch_dequant_rows(src, type, n_rows, row_stride, dst, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "dequant launch");
+    return RKV_OK;
+}
+
+}  // extern "C"
