@@ -1,0 +1,367 @@
+#!/usr/bin/env python3
+"""Benchmark of the split-KV attention path on one MI355X.
+
+Default (the headline line): decode, 1 query, 40 query heads / 8 KV heads, head_dim 128,
+n_kv = 131072 cells fully device-resident, K q8_0 / V q4_0, Q f16 -- one rkv_attn_decode
+call per step (window split-K segment kernel + LSE merge).  Inputs are seeded synthetic
+draws (rkv_inputs); the KV cache is rotated over several independent device copies so the
+256 MB last-level cache cannot serve repeats.
+
+Other workloads (--workload 1..5) print a line of the same form for the small decode
+split, the rolling window + pinned-host tail decode, the unified-pool rows decode and the
+prefill chunk.
+
+The JSON line carries:
+  value       whole-call effective KV GB/s (algorithmic KV bytes / ms_per_step)
+  roofline    the dominant segment kernel: algorithmic bytes (or flops) per launch over
+              its average launch time, timed with HIP events on its own stream inside the
+              timed region, against the MI355X peak
+  cpu_baseline the fp64 oracle on the host cores over a bounded sample, scaled to the
+              same unit
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense f16 MFMA, vendor figure
+PROFILES = os.path.join(ROOT, "profiles")
+
+METRIC = "decode attn effective KV GB/s (% HBM peak) + tok/s/layer at n_kv=128K"
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("rkv_decode.hip", "rkv_prefill.hip", "rkv_quant.h", "rkv_internal.h"):
+        p = os.path.join(ROOT, "tiered_kv_cache_split_amd", "csrc", f)
+        if os.path.exists(p):
+            h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(name: str):
+    """HBM bytes per launch from the committed PMC summary, if it was taken on this kernel."""
+    p = os.path.join(PROFILES, f"{name}_traffic.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        d = json.load(open(p))
+    except Exception:
+        return None
+    if d.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas"]
+        if n:
+            return int(max(n))
+    except Exception:
+        pass
+    return os.cpu_count() or 1
+
+
+# ------------------------------------------------------------------ workloads on device
+def setup(num: int, sets: int):
+    import numpy as np
+    import torch
+
+    import rkv_inputs as gen
+    import tiered_kv_cache_split_amd as rkv
+
+    w = gen.make_workload(num)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    def pinned(a):
+        src = torch.from_numpy(np.ascontiguousarray(a))
+        t = torch.empty(src.shape, dtype=src.dtype, pin_memory=True)
+        t.copy_(src)
+        return t
+
+    st = {"w": w, "q": dev(w["q"])}
+    if w["kind"] == "rows":
+        k0, v0 = dev(w["k"]), dev(w["v"])
+        st["sets"] = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(sets - 1)]
+        st["rows"] = dev(w["kv_rows"].astype(np.int32))
+        st["mask"] = dev(w["mask"])
+        n_seq, n_head, n_q, _ = w["q"].shape
+        st["o"] = torch.empty((n_seq, n_q, n_head, 128), dtype=torch.float32, device="cuda")
+        st["lse"] = torch.empty((n_seq, n_q, n_head), dtype=torch.float32, device="cuda")
+        kv_bytes = int((w["kv_rows"] >= 0).sum()) * w["n_head_kv"] * (
+            rkv.ROW_BYTES[w["k_type"]] + rkv.ROW_BYTES[w["v_type"]])
+        st["kv_bytes"] = kv_bytes
+        st["tail_bytes"] = 0
+        return st
+    wc = w["wc"]
+    kw, vw = dev(w["k"][:wc]), dev(w["v"][:wc])
+    st["sets"] = [(kw, vw)] + [(kw.clone(), vw.clone()) for _ in range(sets - 1)]
+    st["tail"] = None
+    if w["n_kv"] > wc:
+        st["tail"] = (pinned(w["k"][wc:]), pinned(w["v"][wc:]))
+    n_head, n_q = w["n_head"], w["q"].shape[1]
+    st["o"] = torch.empty((n_q, n_head, 128), dtype=torch.float32, device="cuda")
+    st["lse"] = torch.empty((n_q, n_head), dtype=torch.float32, device="cuda")
+    per_cell = w["n_head_kv"] * (rkv.ROW_BYTES[w["k_type"]] + rkv.ROW_BYTES[w["v_type"]])
+    st["kv_bytes"] = w["n_kv"] * per_cell
+    st["tail_bytes"] = (w["n_kv"] - wc) * per_cell
+    st["window_bytes"] = wc * per_cell
+    return st
+
+
+def call(ctx, st, i):
+    import tiered_kv_cache_split_amd as rkv
+    w = st["w"]
+    k, v = st["sets"][i % len(st["sets"])]
+    if w["kind"] == "rows":
+        ctx.attn_rows(rkv.q_desc(st["q"]), rkv.kv_desc(k, w["k_type"]), rkv.kv_desc(v, w["v_type"]), st["rows"],
+                      w["n_kv"], rkv.mask_desc(st["mask"]), w["scale"], st["o"], st["lse"])
+        return
+    kt = vt = None
+    if st["tail"] is not None:
+        kt = rkv.kv_desc(st["tail"][0], w["k_type"])
+        vt = rkv.kv_desc(st["tail"][1], w["v_type"])
+    args = (rkv.q_desc(st["q"]), rkv.kv_desc(k, w["k_type"]), rkv.kv_desc(v, w["v_type"]), kt, vt, None,
+            w["wc"], w["tile_kv"], w["scale"])
+    if w["kind"] == "prefill":
+        ctx.attn_prefill(*args, w["q_pos0"], st["o"], st["lse"])
+    else:
+        ctx.attn_decode(*args, st["o"], st["lse"])
+
+
+def prefill_flops(w) -> float:
+    """QK^T and PV flops over the visible (query, key) pairs of a causal chunk at the end."""
+    n_q, n_kv, q0 = w["q"].shape[1], w["n_kv"], w["q_pos0"]
+    pairs = sum(min(n_kv, q0 + i + 1) for i in range(n_q))
+    return 4.0 * 128 * pairs * w["n_head"]
+
+
+def measured_h2d_gbs(nbytes=256 << 20, reps=10) -> float:
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    dst = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    ts = []
+    for _ in range(reps + 2):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src, non_blocking=True)
+        e1.record()
+        e1.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    ts = sorted(ts[2:])
+    return nbytes / (ts[len(ts) // 2] * 1e-3) / 1e9
+
+
+def measured_copy_gbs(nbytes=1 << 30, reps=10) -> float:
+    """Device-to-device copy kernel, counting read + write bytes."""
+    import torch
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    ts = []
+    for _ in range(reps + 2):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        b.copy_(a)
+        e1.record()
+        e1.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    ts = sorted(ts[2:])
+    return 2 * nbytes / (ts[len(ts) // 2] * 1e-3) / 1e9
+
+
+# ------------------------------------------------------------------ CPU baseline (oracle)
+def cpu_baseline(num: int, budget_s: float = 12.0, w=None):
+    """Time the fp64 oracle on a bounded sample of the same workload and scale to GB/s of
+    the full workload's algorithmic KV bytes."""
+    import numpy as np
+
+    import oracle
+    import rkv_inputs as gen
+
+    w = gen.make_workload(num) if w is None else w
+    n_kv = w["n_kv"]
+    per_cell = None
+    if w["kind"] == "rows":
+        per_cell = w["n_head_kv"] * (256 + 256)
+        total_cells = int((w["kv_rows"] >= 0).sum())
+        q = np.stack([oracle.q_values(w["q"][b]) for b in range(w["q"].shape[0])])
+        cells = 1024
+        while True:
+            t0 = time.perf_counter()
+            rows = np.where(w["kv_rows"][:, :cells] >= 0, w["kv_rows"][:, :cells], -1)
+            k = oracle.kv_values(w["k_type"], w["k"])
+            v = oracle.kv_values(w["v_type"], w["v"])
+            oracle.attention_rows(q, k, v, rows, w["scale"], None)
+            dt = time.perf_counter() - t0
+            done = int((rows >= 0).sum())
+            if dt >= budget_s / 2 or cells >= w["n_kv"]:
+                break
+            cells = min(w["n_kv"], cells * 4)
+        full_s = dt * total_cells / max(1, done)
+        sample = f"row lists cut to their first {cells} entries ({done} pool rows of {total_cells}); time scaled linearly"
+        gbs = total_cells * per_cell / full_s / 1e9
+        return {"value": round(gbs, 4), "unit": "GB/s", "cores": blas_threads(), "kind": "oracle",
+                "sample": sample, "oracle_s_full_extrapolated": round(full_s, 2)}
+    rb = {gen.TYPE_F16: 256, gen.TYPE_Q8_0: 136, gen.TYPE_Q4_0: 72}
+    per_cell = w["n_head_kv"] * (rb[w["k_type"]] + rb[w["v_type"]])
+    q = oracle.q_values(w["q"])
+    n_q = w["q"].shape[1]
+    if w["kind"] == "prefill":
+        q = q[:, -min(n_q, 64):]
+    cells = 4096
+    while True:
+        t0 = time.perf_counter()
+        k = oracle.kv_values(w["k_type"], w["k"][:cells])
+        v = oracle.kv_values(w["v_type"], w["v"][:cells])
+        oracle.attention(q, k, v, w["scale"], None)
+        dt = time.perf_counter() - t0
+        if dt >= budget_s / 2 or cells >= n_kv:
+            break
+        cells = min(n_kv, cells * 4)
+    scale_q = (n_q / q.shape[1]) if w["kind"] == "prefill" else 1.0
+    full_s = dt * (n_kv / cells) * scale_q
+    sample = f"first {cells} of {n_kv} cells"
+    if w["kind"] == "prefill":
+        sample += f", last {q.shape[1]} of {n_q} queries (unmasked)"
+    sample += "; time scaled linearly to the full workload"
+    gbs = n_kv * per_cell / full_s / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": blas_threads(), "kind": "oracle", "sample": sample,
+            "oracle_s_full_extrapolated": round(full_s, 2)}
+
+
+# ------------------------------------------------------------------ main
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--sets", type=int, default=4, help="independent device copies of the KV cache")
+    ap.add_argument("--splits", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--lift-mode", type=int, default=0, help="0 bulk DMA, 1 word-granularity UVA read")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (--gpus must be 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import rkv_inputs as gen
+    import tiered_kv_cache_split_amd as rkv
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    print(f"[bench] workload {args.workload}: {gen.WORKLOADS[args.workload]['name']} setup", file=sys.stderr,
+          flush=True)
+    st = setup(args.workload, args.sets)
+    w = st["w"]
+    ctx = rkv.Context(0)
+    if args.splits:
+        ctx.set_splits(args.splits)
+    if args.lift_mode:
+        ctx.set_lift_mode(args.lift_mode)
+    for i in range(args.warmup):
+        call(ctx, st, i)
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done, timing {args.steps} steps", file=sys.stderr, flush=True)
+
+    # timed region: whole calls, with the segment kernels bracketed by events on their stream
+    ctx.set_kernel_timing(True)
+    lift_totals = []
+    if st.get("tail_bytes"):
+        ctx.set_lift_timing(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        call(ctx, st, i)
+        if st.get("tail_bytes"):
+            tot, span, n = ctx.lift_timing_ms()  # waits for this call's lifts
+            lift_totals.append((tot, span, n))
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    k_ms, k_n = ctx.kernel_timing_ms()
+    ctx.set_kernel_timing(False)
+    ctx.set_lift_timing(False)
+    stats = ctx.stats()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    assert torch.isfinite(st["o"]).all()
+
+    launches_per_step = max(1, k_n // args.steps)
+    kern_ms = k_ms / max(1, k_n)  # average segment-kernel launch
+    kv_bytes = st["kv_bytes"]
+    out = {
+        "metric": METRIC,
+        "value": round(kv_bytes / (ms_per_step * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w["name"], "n_head": w["n_head"], "n_head_kv": w["n_head_kv"], "head_dim": 128,
+                   "n_q": int(w["q"].shape[-2]), "n_kv": int(w["n_kv"]),
+                   "k_type": gen.TYPE_NAMES[w["k_type"]], "v_type": gen.TYPE_NAMES[w["v_type"]],
+                   "kv_sets_rotated": args.sets, "parallelism": "single GPU"},
+        "tok_per_s_per_layer": round(1e3 / ms_per_step, 1),
+        "pct_hbm_peak_whole_call": round(100 * kv_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+        "segment_launches_per_step": launches_per_step,
+        "stats": stats,
+    }
+    if w["kind"] == "prefill":
+        flops = prefill_flops(w)
+        kern_total_ms = k_ms / args.steps
+        achieved = flops / (kern_total_ms * 1e-3) / 1e12
+        out["roofline"] = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_F16_PEAK_TFLOPS,
+                           "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4),
+                           "traffic": traffic_from_profiles("prefill_seg_q8q4_nq512_nkv106496"),
+                           "kernel": "prefill_seg_kernel (all segments of a step)",
+                           "kernel_ms_per_step": round(kern_total_ms, 4)}
+    else:
+        name = {2: "decode_seg_q8q4_nkv131072", 4: "decode_seg_rows_f16_pool65536"}.get(args.workload, "")
+        if launches_per_step == 1:
+            # one segment launch per step (resident window or pool): bytes of one launch / its time
+            achieved = kv_bytes / (kern_ms * 1e-3) / 1e9
+            label = "decode_seg_kernel"
+        else:
+            # window plus tail tiles: all KV bytes over the step's total segment-kernel time
+            achieved = kv_bytes / ((k_ms / args.steps) * 1e-3) / 1e9
+            label = "decode_seg_kernel (all segments of a step)"
+        out["roofline"] = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                           "frac": round(achieved / HBM_PEAK_GBS, 4),
+                           "traffic": traffic_from_profiles(name) if name else None,
+                           "kernel": label, "kernel_avg_ms": round(kern_ms, 5)}
+    if lift_totals:
+        tot = sum(t[0] for t in lift_totals) / len(lift_totals)
+        span = sum(t[1] for t in lift_totals) / len(lift_totals)
+        h2d = measured_h2d_gbs()
+        lift_gbs = st["tail_bytes"] / (tot * 1e-3) / 1e9 if tot > 0 else None
+        out["lift"] = {"mode": "bulk" if args.lift_mode == 0 else "uva", "tail_bytes": st["tail_bytes"],
+                       "lift_ms_sum": round(tot, 4), "lift_span_ms": round(span, 4),
+                       "lift_GBps_overlapped": round(lift_gbs, 2) if lift_gbs else None,
+                       "measured_h2d_GBps": round(h2d, 2),
+                       "frac_of_measured_h2d": round(lift_gbs / h2d, 4) if lift_gbs else None}
+    out["measured_copy_GBps"] = round(measured_copy_gbs(), 1)
+    if not args.no_cpu_baseline:
+        print("[bench] timing the oracle on the host cores", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(args.workload, w=w)
+    ctx.close()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -130,6 +130,14 @@ int rkv_set_lift_timing(rkv_ctx *ctx, int on);
  * from the first lift's start to the last lift's end, and how many were timed. */
 int rkv_lift_timing_ms(rkv_ctx *ctx, float *total_ms, float *span_ms, int *n_lifts);
 
+/* Measurement aid: when on, every later segment-kernel launch (the per-segment decode, rows
+ * or prefill kernel, not the merge) is bracketed by timing events on the stream it is
+ * launched on, up to 4096 launches; turning it on resets the record. */
+int rkv_set_kernel_timing(rkv_ctx *ctx, int on);
+
+/* Waits for the recorded launches and reports the sum of their durations and their count. */
+int rkv_kernel_timing_ms(rkv_ctx *ctx, float *total_ms, int *n_launches);
+
 /* ---- attention -------------------------------------------------------------------- */
 
 /* Decode attention over a window + tail split (patch 0070, ggml_streaming_flash_attn_window:

@@ -135,6 +135,14 @@ class Context:
               "rkv_lift_timing_ms")
         return tot.value, span.value, n.value
 
+    def set_kernel_timing(self, on: bool):
+        check(self.lib.rkv_set_kernel_timing(self.h, int(bool(on))), "rkv_set_kernel_timing")
+
+    def kernel_timing_ms(self):
+        tot, n = ctypes.c_float(), ctypes.c_int()
+        check(self.lib.rkv_kernel_timing_ms(self.h, ctypes.byref(tot), ctypes.byref(n)), "rkv_kernel_timing_ms")
+        return tot.value, n.value
+
     def stats(self) -> dict:
         s = RkvStats()
         check(self.lib.rkv_get_stats(self.h, ctypes.byref(s)), "rkv_get_stats")

@@ -42,6 +42,8 @@ SIGNATURES = {
     "rkv_set_lift_timing": (ctypes.c_int, [vp, ctypes.c_int]),
     "rkv_lift_timing_ms": (ctypes.c_int, [vp, ctypes.POINTER(ctypes.c_float),
                                           ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_int)]),
+    "rkv_set_kernel_timing": (ctypes.c_int, [vp, ctypes.c_int]),
+    "rkv_kernel_timing_ms": (ctypes.c_int, [vp, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_int)]),
     "rkv_attn_decode": (ctypes.c_int, [vp, TP, TP, TP, TP, TP, TP, i64, i64, ctypes.c_float, vp, vp, vp]),
     "rkv_attn_prefill": (ctypes.c_int, [vp, TP, TP, TP, TP, TP, TP, i64, i64, ctypes.c_float, i64, vp, vp, vp]),
     "rkv_attn_rows": (ctypes.c_int, [vp, TP, TP, TP, vp, i64, TP, ctypes.c_float, vp, vp, vp]),

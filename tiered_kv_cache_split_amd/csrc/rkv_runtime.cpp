@@ -53,6 +53,7 @@ int hip_fail(hipError_t e, const char *what) {
 
 constexpr int kMaxSlots = 4;
 constexpr int kMaxLiftTiming = 64;
+constexpr int kMaxKernelTiming = 4096;
 
 int64_t type_block_bytes(int t) {
     switch (t) {
@@ -159,6 +160,10 @@ struct rkv_ctx {
     hipEvent_t lift_t0[kMaxLiftTiming] = {}, lift_t1[kMaxLiftTiming] = {};
     bool lift_timing = false;
     int n_lift_timed = 0;
+    // opt-in timing of segment-kernel launches (events on the launching stream)
+    std::vector<hipEvent_t> kt0, kt1;
+    bool kernel_timing = false;
+    int n_kernel_timed = 0;
     void *scr_k[kMaxSlots] = {};
     void *scr_v[kMaxSlots] = {};
     size_t cap_k[kMaxSlots] = {};
@@ -292,8 +297,11 @@ int run_segment(rkv_ctx *ctx, SegParams base, const Seg &sg, bool mfma, int k_ty
     int64_t cps;
     seg_plan(ctx, sg.n_cells, p, mfma, cps, p.n_splits);
     p.cells_per_split = (int)cps;
+    const bool timed = ctx->kernel_timing && ctx->n_kernel_timed < (int)ctx->kt0.size();
+    if (timed) RKV_HIP(hipEventRecord(ctx->kt0[ctx->n_kernel_timed], s));
     const hipError_t e = mfma ? launch_prefill_segment(p, k_type, v_type, s) : launch_decode_segment(p, k_type, v_type, s);
     if (e != hipSuccess) return hip_fail(e, mfma ? "prefill segment launch" : "decode segment launch");
+    if (timed) RKV_HIP(hipEventRecord(ctx->kt1[ctx->n_kernel_timed++], s));
     slot += p.n_splits;
     ctx->stats.n_segments += 1;
     return RKV_OK;
@@ -576,6 +584,10 @@ void rkv_destroy(rkv_ctx *c) {
         if (c->lift_t0[i]) (void)hipEventDestroy(c->lift_t0[i]);
         if (c->lift_t1[i]) (void)hipEventDestroy(c->lift_t1[i]);
     }
+    for (size_t i = 0; i < c->kt0.size(); ++i) {
+        (void)hipEventDestroy(c->kt0[i]);
+        (void)hipEventDestroy(c->kt1[i]);
+    }
     if (c->entry) (void)hipEventDestroy(c->entry);
     if (c->partials) (void)hipFree(c->partials);
     if (c->copy_stream) (void)hipStreamDestroy(c->copy_stream);
@@ -623,6 +635,37 @@ int rkv_set_lift_timing(rkv_ctx *ctx, int on) {
     if (!ctx) return fail(RKV_ERR_ARG, "ctx is NULL");
     ctx->lift_timing = on != 0;
     ctx->n_lift_timed = 0;
+    return RKV_OK;
+}
+
+int rkv_set_kernel_timing(rkv_ctx *ctx, int on) {
+    if (!ctx) return fail(RKV_ERR_ARG, "ctx is NULL");
+    int st = ensure_device(ctx);
+    if (st) return st;
+    if (on && ctx->kt0.empty()) {
+        ctx->kt0.resize(kMaxKernelTiming);
+        ctx->kt1.resize(kMaxKernelTiming);
+        for (int i = 0; i < kMaxKernelTiming; ++i) {
+            RKV_HIP(hipEventCreate(&ctx->kt0[i]));
+            RKV_HIP(hipEventCreate(&ctx->kt1[i]));
+        }
+    }
+    ctx->kernel_timing = on != 0;
+    ctx->n_kernel_timed = 0;
+    return RKV_OK;
+}
+
+int rkv_kernel_timing_ms(rkv_ctx *ctx, float *total_ms, int *n_launches) {
+    if (!ctx || !total_ms) return fail(RKV_ERR_ARG, "NULL argument");
+    float tot = 0.f;
+    for (int i = 0; i < ctx->n_kernel_timed; ++i) {
+        RKV_HIP(hipEventSynchronize(ctx->kt1[i]));
+        float ms = 0.f;
+        RKV_HIP(hipEventElapsedTime(&ms, ctx->kt0[i], ctx->kt1[i]));
+        tot += ms;
+    }
+    *total_ms = tot;
+    if (n_launches) *n_launches = ctx->n_kernel_timed;
     return RKV_OK;
 }
 
