@@ -207,3 +207,17 @@ def test_attn_partial_matches_oracle_partial(run):
     # compare the normalised forms (a partial is defined up to the common factor e^M)
     assert np.allclose(P[:, 0] + np.log(P[:, 1]), (M + np.log(S))[0], atol=LSE_TOL)
     assert np.abs(P[:, 2:] / P[:, 1:2] - (VKQ / S[..., None])[0]).max() <= O_TOL
+
+
+@pytest.mark.parametrize("kt,vt", [(gen.TYPE_Q8_0, gen.TYPE_Q4_0), (gen.TYPE_F16, gen.TYPE_F16)])
+def test_large_logits_need_the_true_running_max(run, kt, vt):
+    """Unscaled outlier scores (hundreds): exp overflows unless every chunk's wave max is the
+    true maximum, so a wrong cross-lane reduction shows up as inf/NaN or a large error."""
+    rng = gen.rng_for(98)
+    q, k, v = gen.draw_qkv(rng, 8, 1, 2, 2500, k_type=kt, v_type=vt, outlier_every=17, outlier_scale=30.0)
+    w = dict(n_head=8, n_head_kv=2, q=q, k=k, v=v, k_type=kt, v_type=vt, scale=1.0, n_kv=2500, wc=1700,
+             tile_kv=500)
+    step(f"decode large logits k={kt} v={vt}")
+    O, L = run.decode(w, tail="host")
+    Oref, Lref = oracle_decode(w)
+    assert_close(O, L, Oref, Lref, what="large logits")

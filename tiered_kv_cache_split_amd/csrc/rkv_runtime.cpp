@@ -223,12 +223,14 @@ int ensure_partials(rkv_ctx *ctx, int64_t floats, hipStream_t s) {
     return st;
 }
 
-// Split-K factor of a device segment for the vector kernel: enough workgroups to fill the
-// chip (about eight waves per CU) while keeping at least 256 cells per split.
+// Split-K factor of a device segment for the vector kernel (4-wave workgroups): about two
+// workgroups per CU, i.e. one full round of resident workgroups, with at least 256 cells
+// (one chunk per wave) per split.
 int vec_splits(const rkv_ctx *ctx, int64_t n_cells, int64_t n_groups) {
-    if (ctx->splits_override > 0) return (int)std::max<int64_t>(1, std::min<int64_t>(ctx->splits_override, (n_cells + kChunk - 1) / kChunk));
+    if (ctx->splits_override > 0)
+        return (int)std::max<int64_t>(1, std::min<int64_t>(ctx->splits_override, (n_cells + kChunk - 1) / kChunk));
     if (n_cells <= 0) return 1;
-    const int64_t target_blocks = 8LL * ctx->n_cu;
+    const int64_t target_blocks = 2LL * ctx->n_cu;
     int64_t want = (target_blocks + n_groups - 1) / std::max<int64_t>(1, n_groups);
     const int64_t max_by_len = std::max<int64_t>(1, n_cells / 256);
     want = std::max<int64_t>(1, std::min(want, max_by_len));
