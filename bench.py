@@ -250,6 +250,8 @@ def main():
     ap.add_argument("--splits", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--lift-mode", type=int, default=0, help="0 bulk DMA, 1 word-granularity UVA read")
+    ap.add_argument("--copy-only", action="store_true",
+                    help="only run a plain 1 GiB device copy (calibrates HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -262,6 +264,10 @@ def main():
     import tiered_kv_cache_split_amd as rkv
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_only:
+        gbs = measured_copy_gbs(1 << 30, reps=5)
+        print(json.dumps({"copy_bytes_read": 1 << 30, "copy_bytes_written": 1 << 30, "copy_GBps": round(gbs, 1)}))
+        return
     print(f"[bench] workload {args.workload}: {gen.WORKLOADS[args.workload]['name']} setup", file=sys.stderr,
           flush=True)
     st = setup(args.workload, args.sets)
