@@ -237,11 +237,6 @@ int vec_splits(const rkv_ctx *ctx, int64_t n_cells, int64_t n_groups) {
     return (int)want;
 }
 
-struct Seg {
-    const uint8_t *k, *v;
-    int64_t k_s1, k_s2, v_s1, v_s2;
-    int64_t n_cells, pos0;
-};
 
 void fill_q(SegParams &p, const rkv_tensor *q) {
     p.q = static_cast<const _Float16 *>(q->data);
@@ -256,6 +251,25 @@ void fill_mask(SegParams &p, const rkv_tensor *m) {
     p.m_s3 = (m && m->ne[3] > 1) ? m->nb[3] / 2 : 0;
 }
 
+struct Seg {
+    const uint8_t *k, *v;
+    int64_t k_s1, k_s2, v_s1, v_s2;
+    int64_t n_cells, pos0;
+};
+
+// The cell-major kernel applies when every cell holds all KV heads packed (head stride ==
+// row size), cell strides and bases are 16-byte aligned, and the head count and types have an
+// instantiation.
+bool use_cell_kernel(const Seg &sg, const SegParams &p, int k_type, int v_type) {
+    const int64_t rk = row_bytes(k_type), rv = row_bytes(v_type);
+    if (!cell_kernel_ok(k_type, v_type, p.n_head_kv, p.gqa * p.n_q)) return false;
+    if (p.n_head_kv > 1 && (sg.k_s2 != rk || sg.v_s2 != rv)) return false;
+    if (sg.k_s1 < p.n_head_kv * rk || sg.v_s1 < p.n_head_kv * rv) return false;
+    if ((sg.k_s1 | sg.v_s1) % 16 != 0) return false;
+    if (((uintptr_t)sg.k | (uintptr_t)sg.v) % 16 != 0) return false;
+    return true;
+}
+
 // Split-K plan of one device segment: cells per split and number of splits.  The vector
 // kernel walks 64-cell chunks; the MFMA kernel walks key tiles of prefill_keys_per_iter().
 void seg_plan(const rkv_ctx *ctx, int64_t n_cells, const SegParams &p, bool mfma, int64_t &cps, int &n_splits) {
@@ -268,6 +282,14 @@ void seg_plan(const rkv_ctx *ctx, int64_t n_cells, const SegParams &p, bool mfma
         want = std::min<int64_t>(want, std::max<int64_t>(1, (n_cells + kpi - 1) / kpi));
         cps = (n_cells + want - 1) / want;
         cps = std::max<int64_t>(kpi, (cps + kpi - 1) / kpi * kpi);
+    } else if (p.cell_hw > 0) {
+        // cell-major kernel: one workgroup (n_head_kv waves) per split and per CU (its LDS
+        // footprint allows one resident workgroup per CU), at least 256 cells each
+        int64_t want = ctx->splits_override > 0 ? ctx->splits_override
+                                                : std::max<int64_t>(1, (ctx->n_cu + p.n_seq - 1) / p.n_seq);
+        want = std::max<int64_t>(1, std::min(want, std::max<int64_t>(1, n_cells / 256)));
+        cps = (n_cells + want - 1) / want;
+        cps = std::max<int64_t>(kChunk, (cps + kChunk - 1) / kChunk * kChunk);
     } else {
         const int splits = vec_splits(ctx, n_cells, (int64_t)p.n_head_kv * p.n_seq);
         cps = (n_cells + splits - 1) / splits;
@@ -276,11 +298,18 @@ void seg_plan(const rkv_ctx *ctx, int64_t n_cells, const SegParams &p, bool mfma
     n_splits = (int)std::max<int64_t>(1, (n_cells + cps - 1) / cps);
 }
 
-int planned_slots(const rkv_ctx *ctx, int64_t n_cells, const SegParams &p, bool mfma) {
+struct SegPlan {
+    int cell_hw;
     int64_t cps;
-    int n;
-    seg_plan(ctx, n_cells, p, mfma, cps, n);
-    return n;
+    int n_splits;
+};
+
+SegPlan plan_segment(const rkv_ctx *ctx, const SegParams &base, const Seg &sg, bool mfma, int k_type, int v_type) {
+    SegParams p = base;
+    p.cell_hw = (!mfma && !p.rows && use_cell_kernel(sg, p, k_type, v_type)) ? p.n_head_kv : 0;
+    SegPlan pl{p.cell_hw, 0, 0};
+    seg_plan(ctx, sg.n_cells, p, mfma, pl.cps, pl.n_splits);
+    return pl;
 }
 
 // Launch one device segment; `slot` advances by the splits it used.
@@ -296,9 +325,10 @@ int run_segment(rkv_ctx *ctx, SegParams base, const Seg &sg, bool mfma, int k_ty
     p.n_cells = sg.n_cells;
     p.pos0 = sg.pos0;
     p.slot0 = slot;
-    int64_t cps;
-    seg_plan(ctx, sg.n_cells, p, mfma, cps, p.n_splits);
-    p.cells_per_split = (int)cps;
+    const SegPlan pl = plan_segment(ctx, base, sg, mfma, k_type, v_type);
+    p.cell_hw = pl.cell_hw;
+    p.n_splits = pl.n_splits;
+    p.cells_per_split = (int)pl.cps;
     const bool timed = ctx->kernel_timing && ctx->n_kernel_timed < (int)ctx->kt0.size();
     if (timed) RKV_HIP(hipEventRecord(ctx->kt0[ctx->n_kernel_timed], s));
     const hipError_t e = mfma ? launch_prefill_segment(p, k_type, v_type, s) : launch_decode_segment(p, k_type, v_type, s);
@@ -428,14 +458,40 @@ int attn_window_tail(rkv_ctx *ctx, const rkv_tensor *q, const rkv_tensor *k_win,
     base.scale_log2 = scale * 1.4426950408889634f;
     base.n_rows = n_head * n_q;
 
-    // ---- plan: window segment, then tail (in place or lifted tiles)
+    // ---- plan: window segment, then tail (in place, or lifted tiles through the ring)
     const bool lifted = n_tail > 0 && tail_kind == Mem::PinnedHost;
     const int64_t n_tiles = lifted ? (n_tail + tile_kv - 1) / tile_kv : 0;
+    TailGeom gk{}, gv{};
+    int n_slots = 0;
+    const int64_t cap_cells = lifted ? std::min(tile_kv, n_tail) : 0;
+    if (lifted) {
+        if ((st = tail_geom(k_tail, gk)) || (st = tail_geom(v_tail, gv))) return st;
+        n_slots = (int)std::min<int64_t>(ctx->n_slots, n_tiles);
+        for (int sl = 0; sl < n_slots; ++sl) {
+            if ((st = grow(&ctx->scr_k[sl], &ctx->cap_k[sl], (size_t)gk.tile_bytes(cap_cells), stream))) return st;
+            if ((st = grow(&ctx->scr_v[sl], &ctx->cap_v[sl], (size_t)gv.tile_bytes(cap_cells), stream))) return st;
+        }
+    }
+    Seg win{}, dtail{};
+    if (wc > 0)
+        win = Seg{static_cast<const uint8_t *>(k_win->data), static_cast<const uint8_t *>(v_win->data),
+                  k_win->nb[1], k_win->nb[2], v_win->nb[1], v_win->nb[2], wc, 0};
+    if (n_tail > 0 && !lifted)
+        dtail = Seg{static_cast<const uint8_t *>(k_tail->data), static_cast<const uint8_t *>(v_tail->data),
+                    k_tail->nb[1], k_tail->nb[2], v_tail->nb[1], v_tail->nb[2], n_tail, wc};
+    // tile t of the lifted tail, read from ring slot t % n_slots (the ring keeps the tail's
+    // cell layout; a head-major tail gets head planes of cap_cells cells)
+    auto tile_seg = [&](int64_t t) {
+        const int sl = (int)(t % n_slots);
+        const int64_t loc = t * tile_kv, cells = std::min(tile_kv, n_tail - loc);
+        return Seg{static_cast<const uint8_t *>(ctx->scr_k[sl]), static_cast<const uint8_t *>(ctx->scr_v[sl]),
+                   gk.nb1, gk.cell_major ? gk.nb2 : cap_cells * gk.nb1,
+                   gv.nb1, gv.cell_major ? gv.nb2 : cap_cells * gv.nb1, cells, wc + loc};
+    };
     int64_t total_slots = 0;
-    if (wc > 0) total_slots += planned_slots(ctx, wc, base, mfma);
-    if (n_tail > 0 && !lifted) total_slots += planned_slots(ctx, n_tail, base, mfma);
-    for (int64_t t = 0; t < n_tiles; ++t)
-        total_slots += planned_slots(ctx, std::min(tile_kv, n_tail - t * tile_kv), base, mfma);
+    if (wc > 0) total_slots += plan_segment(ctx, base, win, mfma, k_type, v_type).n_splits;
+    if (n_tail > 0 && !lifted) total_slots += plan_segment(ctx, base, dtail, mfma, k_type, v_type).n_splits;
+    for (int64_t t = 0; t < n_tiles; ++t) total_slots += plan_segment(ctx, base, tile_seg(t), mfma, k_type, v_type).n_splits;
     if (total_slots == 0) total_slots = 1;  // n_kv == 0: one empty partial
     if ((st = ensure_partials(ctx, total_slots * base.n_rows * kPartialStride, stream))) return st;
     base.partials = ctx->partials;
@@ -445,22 +501,12 @@ int attn_window_tail(rkv_ctx *ctx, const rkv_tensor *q, const rkv_tensor *k_win,
     ctx->stats.lift_mode = ctx->lift_mode;
     int slot = 0;
 
-    TailGeom gk{}, gv{};
-    int n_slots = 0;
     if (lifted) {
-        if ((st = tail_geom(k_tail, gk)) || (st = tail_geom(v_tail, gv))) return st;
-        n_slots = (int)std::min<int64_t>(ctx->n_slots, n_tiles);
-        const int64_t cap_cells = std::min(tile_kv, n_tail);
-        for (int sl = 0; sl < n_slots; ++sl) {
-            if ((st = grow(&ctx->scr_k[sl], &ctx->cap_k[sl], (size_t)gk.tile_bytes(cap_cells), stream))) return st;
-            if ((st = grow(&ctx->scr_v[sl], &ctx->cap_v[sl], (size_t)gv.tile_bytes(cap_cells), stream))) return st;
-        }
         // the copy stream starts after all earlier work on the compute stream, so a slot
         // still read by an earlier call is never overwritten
         RKV_HIP(hipEventRecord(ctx->entry, stream));
         RKV_HIP(hipStreamWaitEvent(ctx->copy_stream, ctx->entry, 0));
     }
-    const int64_t cap_cells = lifted ? std::min(tile_kv, n_tail) : 0;
     auto lift = [&](int64_t t) -> int {
         const int sl = (int)(t % n_slots);
         const int64_t loc = t * tile_kv, cells = std::min(tile_kv, n_tail - loc);
@@ -480,16 +526,12 @@ int attn_window_tail(rkv_ctx *ctx, const rkv_tensor *q, const rkv_tensor *k_win,
     }
 
     if (wc > 0) {
-        const Seg w{static_cast<const uint8_t *>(k_win->data), static_cast<const uint8_t *>(v_win->data),
-                    k_win->nb[1], k_win->nb[2], v_win->nb[1], v_win->nb[2], wc, 0};
         const int before = slot;
-        if ((st = run_segment(ctx, base, w, mfma, k_type, v_type, slot, stream))) return st;
+        if ((st = run_segment(ctx, base, win, mfma, k_type, v_type, slot, stream))) return st;
         ctx->stats.splits_window = slot - before;
     }
     if (n_tail > 0 && !lifted) {
-        const Seg t{static_cast<const uint8_t *>(k_tail->data), static_cast<const uint8_t *>(v_tail->data),
-                    k_tail->nb[1], k_tail->nb[2], v_tail->nb[1], v_tail->nb[2], n_tail, wc};
-        if ((st = run_segment(ctx, base, t, mfma, k_type, v_type, slot, stream))) return st;
+        if ((st = run_segment(ctx, base, dtail, mfma, k_type, v_type, slot, stream))) return st;
     }
     for (int64_t t = 0; t < n_tiles; ++t) {
         const int sl = (int)(t % n_slots);
@@ -499,11 +541,7 @@ int attn_window_tail(rkv_ctx *ctx, const rkv_tensor *q, const rkv_tensor *k_win,
             if ((st = lift(t + 1))) return st;
         }
         RKV_HIP(hipStreamWaitEvent(stream, ctx->copy_done[sl], 0));
-        const int64_t loc = t * tile_kv, cells = std::min(tile_kv, n_tail - loc);
-        Seg tile{static_cast<const uint8_t *>(ctx->scr_k[sl]), static_cast<const uint8_t *>(ctx->scr_v[sl]),
-                 gk.nb1, gk.cell_major ? gk.nb2 : cap_cells * gk.nb1,
-                 gv.nb1, gv.cell_major ? gv.nb2 : cap_cells * gv.nb1, cells, wc + loc};
-        if ((st = run_segment(ctx, base, tile, mfma, k_type, v_type, slot, stream))) return st;
+        if ((st = run_segment(ctx, base, tile_seg(t), mfma, k_type, v_type, slot, stream))) return st;
         RKV_HIP(hipEventRecord(ctx->compute_done[sl], stream));
     }
     if (slot == 0) {
@@ -741,13 +779,13 @@ int rkv_attn_rows(rkv_ctx *ctx, const rkv_tensor *q, const rkv_tensor *k_pool, c
     p.gqa = (int)gqa;
     p.scale_log2 = scale * 1.4426950408889634f;
     p.n_rows = n_head * n_q * n_seq;
-    const int slots = planned_slots(ctx, n_kv, p, false);
+    const Seg pool{static_cast<const uint8_t *>(k_pool->data), static_cast<const uint8_t *>(v_pool->data),
+                   k_pool->nb[1], k_pool->nb[2], v_pool->nb[1], v_pool->nb[2], n_kv, 0};
+    const int slots = plan_segment(ctx, p, pool, false, k_pool->type, v_pool->type).n_splits;
     if ((st = ensure_partials(ctx, (int64_t)slots * p.n_rows * kPartialStride, stream))) return st;
     p.partials = ctx->partials;
     ctx->stats = rkv_stats{};
     int slot = 0;
-    const Seg pool{static_cast<const uint8_t *>(k_pool->data), static_cast<const uint8_t *>(v_pool->data),
-                   k_pool->nb[1], k_pool->nb[2], v_pool->nb[1], v_pool->nb[2], n_kv, 0};
     if (n_kv > 0) {
         if ((st = run_segment(ctx, p, pool, false, k_pool->type, v_pool->type, slot, stream))) return st;
     } else {
@@ -792,14 +830,14 @@ int rkv_attn_partial(rkv_ctx *ctx, const rkv_tensor *q, const rkv_tensor *k, con
     p.gqa = (int)gqa;
     p.scale_log2 = scale * 1.4426950408889634f;
     p.n_rows = n_head * n_q;
-    const int slots = planned_slots(ctx, k->ne[1], p, mfma);
+    const Seg sg{static_cast<const uint8_t *>(k->data), static_cast<const uint8_t *>(v->data), k->nb[1], k->nb[2],
+                 v->nb[1], v->nb[2], k->ne[1], kv_pos0};
+    const int slots = plan_segment(ctx, p, sg, mfma, k->type, v->type).n_splits;
     if ((st = ensure_partials(ctx, (int64_t)slots * p.n_rows * kPartialStride, stream))) return st;
     p.partials = ctx->partials;
     ctx->stats = rkv_stats{};
     ctx->stats.kernel_variant = mfma ? 1 : 0;
     int slot = 0;
-    const Seg sg{static_cast<const uint8_t *>(k->data), static_cast<const uint8_t *>(v->data), k->nb[1], k->nb[2],
-                 v->nb[1], v->nb[2], k->ne[1], kv_pos0};
     if (k->ne[1] > 0) {
         if ((st = run_segment(ctx, p, sg, mfma, k->type, v->type, slot, stream))) return st;
     } else {
