@@ -51,6 +51,7 @@ hipError_t launch_prefill_segment(const SegParams &p, int k_type, int v_type, hi
 // Blocks the prefill kernel uses per (q tile, KV head) along the key axis.
 int prefill_rows_per_block();
 int prefill_keys_per_iter();
+int prefill_blocks_per_cu();  // workgroups of the prefill kernel resident per CU (LDS bound)
 hipError_t launch_merge(const float *partials, int n_seg, int64_t n_rows, float *o,
                         float *lse, float *partial_out, hipStream_t s);
 // Writes (M=-inf, S=0, VKQ=0) for n_rows rows into partial slot 0.

@@ -7,12 +7,13 @@
 // s_j = scale*<q, k_j> + mask_j, keys at positions after the query's own (causal) or with a
 // -inf mask contributing nothing.
 //
-// Workgroup = 4 waves = 128 query rows of one KV head (row rho = i*gqa + r: query i, head
+// Workgroup = 8 waves = 256 query rows of one KV head (row rho = i*gqa + r: query i, head
 // g*gqa + r) over one split of the segment's keys, 64 keys per iteration:
-//   1. the tile's raw K/V bytes (binary16 or q8_0/q4_0 blocks) are fetched one tile ahead
-//      into registers and staged in LDS;
-//   2. they are decoded once per workgroup into binary16 MFMA operands in LDS: K as rows
-//      [key][d]; q8_0 K exactly, as a rounded binary16 part plus the binary16 residual
+//   1. the tile's raw K/V bytes (binary16 or q8_0/q4_0 blocks) are fetched three tiles ahead
+//      into registers and staged in LDS (two staging and two operand buffers, one barrier
+//      per tile);
+//   2. they are decoded once per workgroup, a tile ahead of use, into binary16 MFMA
+//      operands in LDS: K as rows [key][d]; q8_0 K exactly, as a rounded binary16 part plus the binary16 residual
 //      (d*q has up to 18 significant bits; the two parts carry all of them), so that a large
 //      key is not perturbed by rounding; V transposed to [d][key] (q4_0 values d*(n-8)
 //      rounded once to binary16, the same rounding P gets);
@@ -34,7 +35,7 @@ typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float f16x_t __attribute__((ext_vector_type(16)));
 
-constexpr int kWavesP = 4;
+constexpr int kWavesP = 8;
 constexpr int kThreadsP = 64 * kWavesP;
 constexpr int kBM = 32 * kWavesP;  // query rows per workgroup
 constexpr int kBN = 64;            // keys per iteration
@@ -54,21 +55,22 @@ template <int T> struct Tile {
     static constexpr int kPer = (kTotal + kThreadsP - 1) / kThreadsP;
 };
 
-// LDS layout (bytes).
+// LDS layout (bytes): two operand sets (binary16 K rows, for q8_0 K also the residual rows,
+// and V^T) and two raw staging buffers, so one barrier per tile separates every producer from
+// its consumers.
 template <int KT, int VT> struct Lds {
-    static constexpr int kKhi = 0;
-    static constexpr int kKlo = kKhi + kBN * kKStride;                       // q8_0 K only
+    static constexpr int kKlo = kBN * kKStride;                                // q8_0 K only
     static constexpr int kVt = kKlo + (KT == T_Q8_0 ? kBN * kKStride : 0);
-    static constexpr int kSk = kVt + kHeadDim * kVtStride;                    // raw K tile
-    static constexpr int kSv = kSk + Tile<KT>::kTotal * 8;                     // raw V tile
-    static constexpr int kSize = kSv + Tile<VT>::kTotal * 8 + 16;             // +16: slack of block-window reads
+    static constexpr int kOp = kVt + kHeadDim * kVtStride;                     // one operand set
+    static constexpr int kSv = Tile<KT>::kTotal * 8;                            // raw V after raw K
+    static constexpr int kSt = kSv + Tile<VT>::kTotal * 8 + 16;                 // +16: block-window slack
+    static constexpr int kSize = 2 * kOp + 2 * kSt;
 };
 
 __device__ __forceinline__ half2_t as_h2(uint32_t x) { return __builtin_bit_cast(half2_t, x); }
 __device__ __forceinline__ uint32_t as_u(half2_t x) { return __builtin_bit_cast(uint32_t, x); }
 
-// Word-aligned view of the bytes of a block that starts (after its 2-byte scale) at LDS byte
-// offset o (o even): out[j] = bytes o+4j .. o+4j+3.
+// Word-aligned view of LDS bytes starting at an even offset o: out[j] = bytes o+4j .. o+4j+3.
 template <int NW>
 __device__ __forceinline__ void block_words(const uint8_t *lds, int o, uint32_t (&out)[NW]) {
     const uint32_t *w = reinterpret_cast<const uint32_t *>(lds + (o & ~3));
@@ -116,28 +118,31 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint8_t *base,
     return __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, (int)((nv - 1) * s1 + rb), 0x00020000);
 }
 
-// ---- decode of the staged raw tile into binary16 MFMA operands (one pass per workgroup)
+// ---- decode of a staged raw tile into binary16 MFMA operands (once per workgroup)
 
-// K rows: binary16 copy, or q8_0 as hi = rn(d*q) and lo = rn(d*q - hi) (exact).
+// K rows: binary16 copy, or q8_0 as hi = rn(d*q) and lo = rn(d*q - hi) (exact).  A thread
+// takes 16 values of one key.
 template <int KT>
 __device__ __forceinline__ void decode_k(const uint8_t *sk, uint8_t *khi, uint8_t *klo, int tid) {
-    const int key = tid & 63, part = tid >> 6;  // part: q8_0 block, or 64-byte quarter of a binary16 row
+    const int key = tid & 63;
     if constexpr (KT == T_F16) {
-        const uint4 *src = reinterpret_cast<const uint4 *>(sk + key * 256 + 64 * part);
-        uint4 *dst = reinterpret_cast<uint4 *>(khi + key * kKStride + 64 * part);
-#pragma unroll
-        for (int m = 0; m < 4; ++m) dst[m] = src[m];
+        const int part = tid >> 6;  // 32-byte eighth of the row
+        const uint4 *src = reinterpret_cast<const uint4 *>(sk + key * 256 + 32 * part);
+        uint4 *dst = reinterpret_cast<uint4 *>(khi + key * kKStride + 32 * part);
+        dst[0] = src[0];
+        dst[1] = src[1];
     } else {
+        const int blk = (tid >> 6) & 3, hf = tid >> 8;
         const uint8_t *row = sk + key * 136;
-        const int o = 34 * part;
+        const int o = 34 * blk;
         const uint32_t dbits = *reinterpret_cast<const uint16_t *>(row + o);
         const half2_t dd = as_h2(dbits | (dbits << 16));
-        uint32_t qw[8];
-        block_words<8>(row, o + 2, qw);
+        uint32_t qw[4];
+        block_words<4>(row, o + 2 + 16 * hf, qw);
         const half2_t bias = {(_Float16)-1152.0f, (_Float16)-1152.0f};
-        uint32_t hi[16], lo[16];
+        uint32_t hi[8], lo[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < 4; ++j) {
             // q + 128 as the low byte of binary16 0x64xx = 1024 + (q + 128): exact integers
             const uint32_t x = qw[j] ^ 0x80808080u;
             const half2_t q01 = as_h2(__builtin_amdgcn_perm(0x64646464u, x, 0x04010400u)) + bias;
@@ -148,50 +153,49 @@ __device__ __forceinline__ void decode_k(const uint8_t *sk, uint8_t *khi, uint8_
             lo[2 * j] = as_u(__builtin_elementwise_fma(q01, dd, -h01));
             lo[2 * j + 1] = as_u(__builtin_elementwise_fma(q23, dd, -h23));
         }
-        uint4 *dh = reinterpret_cast<uint4 *>(khi + key * kKStride + 64 * part);
-        uint4 *dl = reinterpret_cast<uint4 *>(klo + key * kKStride + 64 * part);
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            dh[m] = make_uint4(hi[4 * m], hi[4 * m + 1], hi[4 * m + 2], hi[4 * m + 3]);
-            dl[m] = make_uint4(lo[4 * m], lo[4 * m + 1], lo[4 * m + 2], lo[4 * m + 3]);
-        }
+        uint4 *dh = reinterpret_cast<uint4 *>(khi + key * kKStride + 64 * blk + 32 * hf);
+        uint4 *dl = reinterpret_cast<uint4 *>(klo + key * kKStride + 64 * blk + 32 * hf);
+        dh[0] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+        dh[1] = make_uint4(hi[4], hi[5], hi[6], hi[7]);
+        dl[0] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+        dl[1] = make_uint4(lo[4], lo[5], lo[6], lo[7]);
     }
 }
 
-// V^T rows [d][key position]: a thread takes two adjacent keys (one 32-bit LDS word per d).
+// V^T rows [d][key position]: a thread takes two adjacent keys (one 32-bit LDS word per d)
+// and 8 values of head_dim.
 template <int VT>
 __device__ __forceinline__ void decode_v(const uint8_t *sv, uint8_t *vt, int tid) {
     const int kp = tid & 31;
     const int ka = 2 * kp;
     const int col = vt_pos(ka) * 2;  // byte offset of the key pair in a V^T row
     if constexpr (VT == T_F16) {
-        const int dq = tid >> 5;  // 16 values of head_dim
-        const uint4 *pa = reinterpret_cast<const uint4 *>(sv + ka * 256 + 32 * dq);
-        const uint4 *pb = reinterpret_cast<const uint4 *>(sv + (ka + 1) * 256 + 32 * dq);
-        const uint4 a0 = pa[0], a1 = pa[1], b0 = pb[0], b1 = pb[1];
-        const uint32_t aw[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-        const uint32_t bw[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
-        uint8_t *dst = vt + 16 * dq * kVtStride + col;
+        const int dq = tid >> 5;  // 8 values of head_dim
+        const uint4 a = *reinterpret_cast<const uint4 *>(sv + ka * 256 + 16 * dq);
+        const uint4 b = *reinterpret_cast<const uint4 *>(sv + (ka + 1) * 256 + 16 * dq);
+        const uint32_t aw[4] = {a.x, a.y, a.z, a.w};
+        const uint32_t bw[4] = {b.x, b.y, b.z, b.w};
+        uint8_t *dst = vt + 8 * dq * kVtStride + col;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < 4; ++j) {
             *reinterpret_cast<uint32_t *>(dst + (2 * j) * kVtStride) = __builtin_amdgcn_perm(bw[j], aw[j], 0x05040100u);
             *reinterpret_cast<uint32_t *>(dst + (2 * j + 1) * kVtStride) = __builtin_amdgcn_perm(bw[j], aw[j], 0x07060302u);
         }
     } else {
-        const int blk = (tid >> 5) & 3, half = tid >> 7;
+        const int blk = (tid >> 5) & 3, half = (tid >> 7) & 1, qq = tid >> 8;
         const int o = 18 * blk;
         const uint8_t *ra = sv + ka * 72, *rb = sv + (ka + 1) * 72;
         const uint32_t da = *reinterpret_cast<const uint16_t *>(ra + o);
         const uint32_t db = *reinterpret_cast<const uint16_t *>(rb + o);
         const half2_t dd = as_h2(da | (db << 16));
-        uint32_t wa[4], wb[4];
-        block_words<4>(ra, o + 2, wa);
-        block_words<4>(rb, o + 2, wb);
+        uint32_t wa[2], wb[2];
+        block_words<2>(ra, o + 2 + 8 * qq, wa);
+        block_words<2>(rb, o + 2 + 8 * qq, wb);
         const half2_t bias = {(_Float16)-1032.0f, (_Float16)-1032.0f};
-        uint8_t *dst = vt + (32 * blk + 16 * half) * kVtStride + col;
+        uint8_t *dst = vt + (32 * blk + 16 * half + 8 * qq) * kVtStride + col;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            // nibble of element 4j+e (low nibbles: elements 0..15, high nibbles: 16..31)
+        for (int j = 0; j < 2; ++j) {
+            // nibbles of elements (low nibbles: 0..15 of the block, high nibbles: 16..31)
             const uint32_t na = (wa[j] >> (4 * half)) & 0x0F0F0F0Fu;
             const uint32_t nb = (wb[j] >> (4 * half)) & 0x0F0F0F0Fu;
 #pragma unroll
@@ -248,6 +252,7 @@ prefill_seg_kernel(const SegParams p, int q_tiles, int n_tasks) {
         const int64_t lim = p.q_pos0 + i_last - p.pos0 + 1;
         if (lim < c_end) c_end = lim;
     }
+    const int n_it = c_end > c_begin ? (int)((c_end - c_begin + kBN - 1) / kBN) : 0;
 
     const int rl = lane & 31, hh = lane >> 5;
     const int rho = row0 + 32 * wave + rl;
@@ -269,12 +274,8 @@ prefill_seg_kernel(const SegParams p, int q_tiles, int n_tasks) {
             qf[ks] = __builtin_bit_cast(half8_t, v);
         }
     }
-
-    uint8_t *khi = smem + L::kKhi;
-    uint8_t *klo = smem + L::kKlo;
-    uint8_t *vt = smem + L::kVt;
-    uint8_t *sk = smem + L::kSk;
-    uint8_t *sv = smem + L::kSv;
+    // Q is complete before any tile load is issued, so no wait inside the loop covers it
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 
     const uint8_t *kbase = p.k + (int64_t)g * p.k_s2;
     const uint8_t *vbase = p.v + (int64_t)g * p.v_s2;
@@ -282,11 +283,23 @@ prefill_seg_kernel(const SegParams p, int q_tiles, int n_tasks) {
     tile_offsets<KT>(koff, (int)p.k_s1, tid);
     tile_offsets<VT>(voff, (int)p.v_s1, tid);
     uint2 kraw[Tile<KT>::kPer], vraw[Tile<VT>::kPer];
-    auto fetch = [&](int64_t c0) {
+    auto fetch = [&](int it) {
+        const int64_t c0 = c_begin + (int64_t)kBN * it;
         const int64_t rem = p.n_cells - c0;
         const int64_t nv = rem < kBN ? rem : (int64_t)kBN;
         fetch_tile<KT>(kraw, tile_rsrc(kbase + c0 * p.k_s1, p.k_s1, nv, row_bytes_of<KT>()), koff, tid);
         fetch_tile<VT>(vraw, tile_rsrc(vbase + c0 * p.v_s1, p.v_s1, nv, row_bytes_of<VT>()), voff, tid);
+    };
+    auto stash = [&](int s) {
+        uint8_t *st = smem + 2 * L::kOp + s * L::kSt;
+        stash_tile<KT>(kraw, st, tid);
+        stash_tile<VT>(vraw, st + L::kSv, tid);
+    };
+    auto decode = [&](int s) {
+        const uint8_t *st = smem + 2 * L::kOp + s * L::kSt;
+        uint8_t *op = smem + s * L::kOp;
+        decode_k<KT>(st, op, op + L::kKlo, tid);
+        decode_v<VT>(st + L::kSv, op + L::kVt, tid);
     };
 
     const float c = p.scale_log2;
@@ -295,22 +308,29 @@ prefill_seg_kernel(const SegParams p, int q_tiles, int n_tasks) {
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) oacc[dt] = f16x_t{};
 
-    if (c_begin < c_end) {
-        fetch(c_begin);
-        stash_tile<KT>(kraw, sk, tid);
-        stash_tile<VT>(vraw, sv, tid);
-        if (c_begin + kBN < c_end) fetch(c_begin + kBN);
+    // pipeline: tile it+3 in flight to registers, it+2 staged raw, it+1 being decoded while it
+    // is computed; one barrier per tile
+    if (n_it > 0) {
+        fetch(0);
+        stash(0);
     }
-    for (int64_t c0 = c_begin; c0 < c_end; c0 += kBN) {
-        __syncthreads();  // stage holds tile c0; every wave is done with the previous operands
-        decode_k<KT>(sk, khi, klo, tid);
-        decode_v<VT>(sv, vt, tid);
-        __syncthreads();  // operands ready; stage free
-        if (c0 + kBN < c_end) {
-            stash_tile<KT>(kraw, sk, tid);
-            stash_tile<VT>(vraw, sv, tid);
-            if (c0 + 2 * kBN < c_end) fetch(c0 + 2 * kBN);
-        }
+    if (n_it > 1) fetch(1);
+    __syncthreads();
+    if (n_it > 0) decode(0);
+    if (n_it > 1) stash(1);
+    if (n_it > 2) fetch(2);
+
+    for (int it = 0; it < n_it; ++it) {
+        const int cur = it & 1;
+        __syncthreads();
+        if (it + 1 < n_it) decode(cur ^ 1);
+        if (it + 2 < n_it) stash(cur);
+        if (it + 3 < n_it) fetch(it + 3);
+
+        const int64_t c0 = c_begin + (int64_t)kBN * it;
+        const uint8_t *khi = smem + cur * L::kOp;
+        const uint8_t *klo = khi + L::kKlo;
+        const uint8_t *vt = khi + L::kVt;
 
         // ---- S^T = K.Q^T: two 32-key tiles, lane holds key 32kt + 8(i/4) + 4hh + i%4 of row rl
         f16x_t sacc[2] = {f16x_t{}, f16x_t{}};
@@ -352,15 +372,13 @@ prefill_seg_kernel(const SegParams p, int q_tiles, int n_tasks) {
         }
 
         // ---- online softmax (exp2 domain) for the lane's row; the lane pair (l, l^32) holds it
-        float mx;
+        float mx = -INFINITY;
         if (cc >= 0.f) {
-            mx = -INFINITY;
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kt][i]);
         } else {
-            mx = -INFINITY;
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -444,6 +462,7 @@ hipError_t launch_t(const SegParams &p, hipStream_t s) {
 
 int prefill_rows_per_block() { return kBM; }
 int prefill_keys_per_iter() { return kBN; }
+int prefill_blocks_per_cu() { return 1; }
 
 hipError_t launch_prefill_segment(const SegParams &p, int k_type, int v_type, hipStream_t s) {
     if (p.rows) return hipErrorNotSupported;

@@ -276,11 +276,11 @@ void seg_plan(const rkv_ctx *ctx, int64_t n_cells, const SegParams &p, bool mfma
     if (mfma) {
         const int kpi = prefill_keys_per_iter();
         const int64_t q_tiles = ((int64_t)p.gqa * p.n_q + prefill_rows_per_block() - 1) / prefill_rows_per_block();
-        // two workgroups fit on a CU (LDS); take as many splits as keep every launch within one
-        // wave of workgroups, so all blocks of a segment run concurrently and finish together
+        // as many splits as keep every launch within one wave of resident workgroups, so all
+        // blocks of a segment run concurrently and finish together
         const int64_t groups = q_tiles * p.n_head_kv * p.n_seq;
-        int64_t want = ctx->splits_override > 0 ? ctx->splits_override
-                                                : std::max<int64_t>(1, (2LL * ctx->n_cu) / groups);
+        const int64_t slots = (int64_t)prefill_blocks_per_cu() * ctx->n_cu;
+        int64_t want = ctx->splits_override > 0 ? ctx->splits_override : std::max<int64_t>(1, slots / groups);
         want = std::min<int64_t>(want, std::max<int64_t>(1, (n_cells + kpi - 1) / kpi));
         cps = (n_cells + want - 1) / want;
         cps = std::max<int64_t>(kpi, (cps + kpi - 1) / kpi * kpi);
