@@ -38,16 +38,23 @@ PROFILES = os.path.join(ROOT, "profiles")
 METRIC = "decode attn effective KV GB/s (% HBM peak) + tok/s/layer at n_kv=128K"
 
 
-def kernel_source_hash() -> str:
+KERNEL_SOURCES = {
+    # sources whose change invalidates a committed traffic measurement of that kernel
+    "decode": ("rkv_decode.hip", "rkv_quant.h", "rkv_internal.h", "rkv_runtime.cpp"),
+    "prefill": ("rkv_prefill.hip", "rkv_internal.h", "rkv_runtime.cpp"),
+}
+
+
+def kernel_source_hash(kind: str) -> str:
     h = hashlib.sha256()
-    for f in ("rkv_decode.hip", "rkv_prefill.hip", "rkv_quant.h", "rkv_internal.h"):
+    for f in KERNEL_SOURCES[kind]:
         p = os.path.join(ROOT, "tiered_kv_cache_split_amd", "csrc", f)
         if os.path.exists(p):
             h.update(open(p, "rb").read())
     return h.hexdigest()[:16]
 
 
-def traffic_from_profiles(name: str):
+def traffic_from_profiles(name: str, kind: str):
     """HBM bytes per launch from the committed PMC summary, if it was taken on this kernel."""
     p = os.path.join(PROFILES, f"{name}_traffic.json")
     if not os.path.exists(p):
@@ -56,7 +63,7 @@ def traffic_from_profiles(name: str):
         d = json.load(open(p))
     except Exception:
         return None
-    if d.get("kernel_source_hash") != kernel_source_hash():
+    if d.get("kernel_source_hash") != kernel_source_hash(kind):
         return None
     return d.get("hbm_bytes_per_launch")
 
@@ -334,7 +341,7 @@ def main():
         achieved = flops / (kern_total_ms * 1e-3) / 1e12
         out["roofline"] = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_F16_PEAK_TFLOPS,
                            "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4),
-                           "traffic": traffic_from_profiles("prefill_seg_q8q4_nq512_nkv106496"),
+                           "traffic": traffic_from_profiles("prefill_seg_q8q4_nq512_nkv106496", "prefill"),
                            "kernel": "prefill_seg_kernel (all segments of a step)",
                            "kernel_ms_per_step": round(kern_total_ms, 4)}
     else:
@@ -349,7 +356,7 @@ def main():
             label = "decode_seg_kernel (all segments of a step)"
         out["roofline"] = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": round(achieved / HBM_PEAK_GBS, 4),
-                           "traffic": traffic_from_profiles(name) if name else None,
+                           "traffic": traffic_from_profiles(name, "decode") if name else None,
                            "kernel": label, "kernel_avg_ms": round(kern_ms, 5)}
     if lift_totals:
         tot = sum(t[0] for t in lift_totals) / len(lift_totals)

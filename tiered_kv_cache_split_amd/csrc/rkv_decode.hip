@@ -802,6 +802,59 @@ __global__ void __launch_bounds__(kMergeThreads) merge_kernel(const float *__res
     if (lse && d == 0) lse[row] = ok ? M + logf(S) : -INFINITY;
 }
 
+// The same merge for many rows over few segments (prefill: thousands of rows, a handful of
+// segments): one wave per output row, lane l holding head_dim l and l+64; segment weights
+// are computed by the lane of that segment and read back with readlane.
+constexpr int kMergeRowsPerBlock = 4;
+
+__global__ void __launch_bounds__(64 * kMergeRowsPerBlock) merge_rows_kernel(const float *__restrict__ part, int n_seg,
+                                                                           int64_t n_rows, float *__restrict__ o,
+                                                                           float *__restrict__ lse,
+                                                                           float *__restrict__ pout) {
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * kMergeRowsPerBlock + (threadIdx.x >> 6);
+    if (row >= n_rows) return;
+    const int64_t step = n_rows * kPartialStride;
+    const float *base = part + row * kPartialStride;
+    float M = -INFINITY;
+    for (int s = lane; s < n_seg; s += 64) M = fmaxf(M, base[(int64_t)s * step]);
+    M = wave_max(M);
+    float S = 0.f, a0 = 0.f, a1 = 0.f;
+    if (M != -INFINITY) {
+        for (int s0 = 0; s0 < n_seg; s0 += 64) {
+            const int s = s0 + lane;
+            float w = 0.f;
+            if (s < n_seg) {
+                const float Ms = base[(int64_t)s * step];
+                w = (Ms == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((Ms - M) * kLog2e);
+                S = fmaf(base[(int64_t)s * step + 1], w, S);
+            }
+            const int nt = min(64, n_seg - s0);
+            for (int j = 0; j < nt; ++j) {
+                const float wj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), j));
+                const float *v = base + (int64_t)(s0 + j) * step + 2 + lane;
+                a0 = fmaf(v[0], wj, a0);
+                a1 = fmaf(v[64], wj, a1);
+            }
+        }
+    }
+    S = wave_sum(S);
+    if (pout) {
+        float *q = pout + row * kPartialStride;
+        if (lane == 0) {
+            q[0] = M;
+            q[1] = S;
+        }
+        q[2 + lane] = a0;
+        q[66 + lane] = a1;
+        return;
+    }
+    const bool ok = (M != -INFINITY) && (S > 0.f);
+    o[row * kHeadDim + lane] = ok ? a0 / S : 0.f;
+    o[row * kHeadDim + 64 + lane] = ok ? a1 / S : 0.f;
+    if (lse && lane == 0) lse[row] = ok ? M + logf(S) : -INFINITY;
+}
+
 // Contrast path: the GPU reads pinned host memory through its device mapping four bytes
 // per lane (the word-granularity read patch 0102's commit message measures against the
 // bulk DMA).
@@ -898,8 +951,14 @@ hipError_t launch_decode_segment(const SegParams &p, int k_type, int v_type, hip
 hipError_t launch_merge(const float *partials, int n_seg, int64_t n_rows, float *o, float *lse,
                         float *partial_out, hipStream_t s) {
     if (n_rows <= 0) return hipSuccess;
-    hipLaunchKernelGGL(merge_kernel, dim3((unsigned)n_rows), dim3(kMergeThreads), 0, s, partials, n_seg, n_rows, o,
-                       lse, partial_out);
+    if (n_rows >= 1024 || n_seg <= 16) {
+        // enough rows to fill the chip one wave each (or too few segments to share a row)
+        hipLaunchKernelGGL(merge_rows_kernel, dim3((unsigned)((n_rows + kMergeRowsPerBlock - 1) / kMergeRowsPerBlock)),
+                           dim3(64 * kMergeRowsPerBlock), 0, s, partials, n_seg, n_rows, o, lse, partial_out);
+    } else {
+        hipLaunchKernelGGL(merge_kernel, dim3((unsigned)n_rows), dim3(kMergeThreads), 0, s, partials, n_seg, n_rows,
+                           o, lse, partial_out);
+    }
     return hipGetLastError();
 }
 
