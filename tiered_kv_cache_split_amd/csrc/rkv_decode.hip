@@ -1,6 +1,4 @@
-// Vector (VALU) segment kernel for decode and unified-pool attention on gfx950,
-// plus the log-sum-exp merge, the dequantiser used by tests, and the word-granularity
-// host reader kept as a measured contrast to the bulk DMA lift.
+// Vector (VALU) segment kernel for decode and unified-pool attention on gfx950.
 //
 // What a segment computes (opencoti-llamafile patch 0070-rolling-kv, fattn.cu
 // streaming_lse_kernel and the tail-partial op): for every output row, over the keys of
@@ -23,6 +21,7 @@
 // range and reads every chunk as one contiguous span (the cache layout of the pages).
 #include "rkv_internal.h"
 #include "rkv_quant.h"
+#include "rkv_wave.h"
 
 #include <math.h>
 
@@ -32,57 +31,7 @@ namespace rkv {
 
 namespace {
 
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
-
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
-
-// ---- wave64 reductions.  Floats are maxed as order-preserving integer keys so the max is a
-// plain integer op on DPP operands; rows of 16 lanes are reduced with DPP, then row pairs and
-// wave halves with the gfx950 permlane swaps.
-__device__ __forceinline__ int f2key(float x) {
-    const int b = __builtin_bit_cast(int, x);
-    return b ^ ((b >> 31) & 0x7FFFFFFF);
-}
-__device__ __forceinline__ float key2f(int k) { return __builtin_bit_cast(float, k ^ ((k >> 31) & 0x7FFFFFFF)); }
-
-template <int CTRL>
-__device__ __forceinline__ int dpp_i(int x) { return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xF, 0xF, false); }
-template <int CTRL>
-__device__ __forceinline__ float dpp_f(float x) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
-}
-constexpr int kQuadSwap1 = 0xB1, kQuadSwap2 = 0x4E, kRowRor4 = 0x124, kRowRor8 = 0x128;
-
-// Value of lane k summed over the four 16-lane rows, in every row.
-__device__ __forceinline__ float fold_rows(float x) {
-    const int xi = __builtin_bit_cast(int, x);
-    const auto r16 = __builtin_amdgcn_permlane16_swap(xi, xi, false, false);
-    x = __builtin_bit_cast(float, (int)r16[0]) + __builtin_bit_cast(float, (int)r16[1]);
-    const int yi = __builtin_bit_cast(int, x);
-    const auto r32 = __builtin_amdgcn_permlane32_swap(yi, yi, false, false);
-    return __builtin_bit_cast(float, (int)r32[0]) + __builtin_bit_cast(float, (int)r32[1]);
-}
-
-__device__ __forceinline__ float wave_max(float x) {
-    int k = f2key(x);
-    k = max(k, dpp_i<kQuadSwap1>(k));
-    k = max(k, dpp_i<kQuadSwap2>(k));
-    k = max(k, dpp_i<kRowRor4>(k));
-    k = max(k, dpp_i<kRowRor8>(k));
-    const auto r16 = __builtin_amdgcn_permlane16_swap(k, k, false, false);
-    k = max((int)r16[0], (int)r16[1]);
-    const auto r32 = __builtin_amdgcn_permlane32_swap(k, k, false, false);
-    k = max((int)r32[0], (int)r32[1]);
-    return key2f(k);
-}
-__device__ __forceinline__ float wave_sum(float x) {
-    x += dpp_f<kQuadSwap1>(x);
-    x += dpp_f<kQuadSwap2>(x);
-    x += dpp_f<kRowRor4>(x);
-    x += dpp_f<kRowRor8>(x);
-    return fold_rows(x);
-}
 
 // Orders this wave's LDS accesses (each wave owns its LDS region; no workgroup barrier).
 __device__ __forceinline__ void wave_sync() {
@@ -728,165 +677,6 @@ decode_cell_kernel(const SegParams p) {
     }
 }
 
-// Log-sum-exp merge of partials (patch 0070 streaming_combine_kernel, applied to the
-// un-normalised (M, S, VKQ) form).  One workgroup per output row: the segment weights
-// e^(M_s - M*) are computed once into LDS, then 8 groups of 128 lanes accumulate the
-// values of interleaved segments and fold through LDS.
-constexpr int kMergeGroups = 8;
-constexpr int kMergeThreads = kMergeGroups * kHeadDim;
-constexpr int kMergeTile = 2048;  // segment weights held in LDS per pass
-
-__global__ void __launch_bounds__(kMergeThreads) merge_kernel(const float *__restrict__ part, int n_seg,
-                                                              int64_t n_rows, float *__restrict__ o,
-                                                              float *__restrict__ lse,
-                                                              float *__restrict__ pout) {
-    __shared__ float s_wt[kMergeTile];
-    __shared__ float s_red[kMergeThreads / 64];
-    __shared__ float s_acc[kMergeGroups][kHeadDim];
-    const int64_t row = blockIdx.x;
-    const int tid = threadIdx.x, d = tid & (kHeadDim - 1), grp = tid / kHeadDim;
-    const int64_t step = n_rows * kPartialStride;
-    const float *base = part + row * kPartialStride;
-
-    // M* = max over segments
-    float M = -INFINITY;
-    for (int s = tid; s < n_seg; s += kMergeThreads) M = fmaxf(M, base[(int64_t)s * step]);
-    M = wave_max(M);
-    if ((tid & 63) == 0) s_red[tid >> 6] = M;
-    __syncthreads();
-    M = -INFINITY;
-#pragma unroll
-    for (int j = 0; j < kMergeThreads / 64; ++j) M = fmaxf(M, s_red[j]);
-    __syncthreads();
-
-    float S = 0.f, acc = 0.f;
-    if (M != -INFINITY) {
-        for (int t0 = 0; t0 < n_seg; t0 += kMergeTile) {
-            const int nt = min(kMergeTile, n_seg - t0);
-            for (int j = tid; j < nt; j += kMergeThreads) {
-                const float *pp = base + (int64_t)(t0 + j) * step;
-                const float Ms = pp[0];
-                const float w = (Ms == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((Ms - M) * kLog2e);
-                s_wt[j] = w;
-                S = fmaf(pp[1], w, S);  // each segment's S counted once, by the lane that weighed it
-            }
-            __syncthreads();
-#pragma unroll 4
-            for (int j = grp; j < nt; j += kMergeGroups) acc = fmaf(base[(int64_t)(t0 + j) * step + 2 + d], s_wt[j], acc);
-            __syncthreads();
-        }
-    }
-    // fold S over the block and acc over the groups
-    S = wave_sum(S);
-    if ((tid & 63) == 0) s_red[tid >> 6] = S;
-    s_acc[grp][d] = acc;
-    __syncthreads();
-    if (grp != 0) return;
-    S = 0.f;
-#pragma unroll
-    for (int j = 0; j < kMergeThreads / 64; ++j) S += s_red[j];
-    acc = 0.f;
-#pragma unroll
-    for (int j = 0; j < kMergeGroups; ++j) acc += s_acc[j][d];
-    if (pout) {
-        float *q = pout + row * kPartialStride;
-        if (d == 0) {
-            q[0] = M;
-            q[1] = S;
-        }
-        q[2 + d] = acc;
-        return;
-    }
-    const bool ok = (M != -INFINITY) && (S > 0.f);
-    o[row * kHeadDim + d] = ok ? acc / S : 0.f;
-    if (lse && d == 0) lse[row] = ok ? M + logf(S) : -INFINITY;
-}
-
-// The same merge for many rows over few segments (prefill: thousands of rows, a handful of
-// segments): one wave per output row, lane l holding head_dim l and l+64; segment weights
-// are computed by the lane of that segment and read back with readlane.
-constexpr int kMergeRowsPerBlock = 4;
-
-__global__ void __launch_bounds__(64 * kMergeRowsPerBlock) merge_rows_kernel(const float *__restrict__ part, int n_seg,
-                                                                           int64_t n_rows, float *__restrict__ o,
-                                                                           float *__restrict__ lse,
-                                                                           float *__restrict__ pout) {
-    const int lane = threadIdx.x & 63;
-    const int64_t row = (int64_t)blockIdx.x * kMergeRowsPerBlock + (threadIdx.x >> 6);
-    if (row >= n_rows) return;
-    const int64_t step = n_rows * kPartialStride;
-    const float *base = part + row * kPartialStride;
-    float M = -INFINITY;
-    for (int s = lane; s < n_seg; s += 64) M = fmaxf(M, base[(int64_t)s * step]);
-    M = wave_max(M);
-    float S = 0.f, a0 = 0.f, a1 = 0.f;
-    if (M != -INFINITY) {
-        for (int s0 = 0; s0 < n_seg; s0 += 64) {
-            const int s = s0 + lane;
-            float w = 0.f;
-            if (s < n_seg) {
-                const float Ms = base[(int64_t)s * step];
-                w = (Ms == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((Ms - M) * kLog2e);
-                S = fmaf(base[(int64_t)s * step + 1], w, S);
-            }
-            const int nt = min(64, n_seg - s0);
-            for (int j = 0; j < nt; ++j) {
-                const float wj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), j));
-                const float *v = base + (int64_t)(s0 + j) * step + 2 + lane;
-                a0 = fmaf(v[0], wj, a0);
-                a1 = fmaf(v[64], wj, a1);
-            }
-        }
-    }
-    S = wave_sum(S);
-    if (pout) {
-        float *q = pout + row * kPartialStride;
-        if (lane == 0) {
-            q[0] = M;
-            q[1] = S;
-        }
-        q[2 + lane] = a0;
-        q[66 + lane] = a1;
-        return;
-    }
-    const bool ok = (M != -INFINITY) && (S > 0.f);
-    o[row * kHeadDim + lane] = ok ? a0 / S : 0.f;
-    o[row * kHeadDim + 64 + lane] = ok ? a1 / S : 0.f;
-    if (lse && lane == 0) lse[row] = ok ? M + logf(S) : -INFINITY;
-}
-
-// Contrast path: the GPU reads pinned host memory through its device mapping four bytes
-// per lane (the word-granularity read patch 0102's commit message measures against the
-// bulk DMA).
-__global__ void __launch_bounds__(256) uva_read_kernel(const uint32_t *__restrict__ src,
-                                                       uint32_t *__restrict__ dst,
-                                                       int64_t n_words) {
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_words; i += stride)
-        dst[i] = src[i];
-}
-__global__ void uva_tail_kernel(const uint8_t *src, uint8_t *dst, int64_t n) {
-    const int64_t i = threadIdx.x;
-    if (i < n) dst[i] = src[i];
-}
-
-__global__ void __launch_bounds__(128) empty_partials_kernel(float *__restrict__ part) {
-    float *q = part + (int64_t)blockIdx.x * kPartialStride;
-    q[2 + threadIdx.x] = 0.f;
-    if (threadIdx.x == 0) {
-        q[0] = -INFINITY;
-        q[1] = 0.f;
-    }
-}
-
-__global__ void __launch_bounds__(128) dequant_kernel(const uint8_t *__restrict__ src, int type,
-                                                      int64_t row_stride,
-                                                      float *__restrict__ dst) {
-    const int64_t row = blockIdx.x;
-    const int e = threadIdx.x;
-    dst[row * kHeadDim + e] = row_value(src + row * row_stride, type, e);
-}
-
 template <int KT, int VT, int R, int HW>
 hipError_t launch_cell(const SegParams &p, hipStream_t s) {
     hipLaunchKernelGGL((decode_cell_kernel<KT, VT, R, HW>), dim3((unsigned)(p.n_splits * p.n_seq)), dim3(64 * HW), 0,
@@ -946,52 +736,6 @@ hipError_t launch_decode_segment(const SegParams &p, int k_type, int v_type, hip
     if (k_type == T_Q8_0 && v_type == T_F16) return launch_decode_t<T_Q8_0, T_F16>(p, R, s);
     if (k_type == T_F16 && v_type == T_Q4_0) return launch_decode_t<T_F16, T_Q4_0>(p, R, s);
     return hipErrorInvalidValue;
-}
-
-hipError_t launch_merge(const float *partials, int n_seg, int64_t n_rows, float *o, float *lse,
-                        float *partial_out, hipStream_t s) {
-    if (n_rows <= 0) return hipSuccess;
-    if (n_rows >= 1024 || n_seg <= 16) {
-        // enough rows to fill the chip one wave each (or too few segments to share a row)
-        hipLaunchKernelGGL(merge_rows_kernel, dim3((unsigned)((n_rows + kMergeRowsPerBlock - 1) / kMergeRowsPerBlock)),
-                           dim3(64 * kMergeRowsPerBlock), 0, s, partials, n_seg, n_rows, o, lse, partial_out);
-    } else {
-        hipLaunchKernelGGL(merge_kernel, dim3((unsigned)n_rows), dim3(kMergeThreads), 0, s, partials, n_seg, n_rows,
-                           o, lse, partial_out);
-    }
-    return hipGetLastError();
-}
-
-hipError_t launch_empty_partials(float *partials, int64_t n_rows, hipStream_t s) {
-    if (n_rows <= 0) return hipSuccess;
-    hipLaunchKernelGGL(empty_partials_kernel, dim3((unsigned)n_rows), dim3(kHeadDim), 0, s, partials);
-    return hipGetLastError();
-}
-
-hipError_t launch_uva_read(const void *host_src, void *dst, int64_t nbytes, hipStream_t s) {
-    void *dev_view = nullptr;
-    hipError_t e = hipHostGetDevicePointer(&dev_view, const_cast<void *>(host_src), 0);
-    if (e != hipSuccess) return e;
-    const int64_t n_words = nbytes / 4;
-    if (n_words > 0) {
-        const int64_t blocks = std::min<int64_t>((n_words + 255) / 256, 4096);
-        hipLaunchKernelGGL(uva_read_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
-                           static_cast<const uint32_t *>(dev_view), static_cast<uint32_t *>(dst), n_words);
-    }
-    const int64_t rem = nbytes - 4 * n_words;
-    if (rem > 0)
-        hipLaunchKernelGGL(uva_tail_kernel, dim3(1), dim3(4), 0, s,
-                           static_cast<const uint8_t *>(dev_view) + 4 * n_words,
-                           static_cast<uint8_t *>(dst) + 4 * n_words, rem);
-    return hipGetLastError();
-}
-
-hipError_t launch_dequant_rows(const void *src, int type, int64_t n_rows, int64_t row_stride,
-                               float *dst, hipStream_t s) {
-    if (n_rows <= 0) return hipSuccess;
-    hipLaunchKernelGGL(dequant_kernel, dim3((unsigned)n_rows), dim3(kHeadDim), 0, s,
-                       static_cast<const uint8_t *>(src), type, row_stride, dst);
-    return hipGetLastError();
 }
 
 }  // namespace rkv

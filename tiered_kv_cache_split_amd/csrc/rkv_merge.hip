@@ -1,0 +1,170 @@
+// Log-sum-exp merge of segment partials on gfx950, and the empty partial written for a
+// segment with no keys.
+#include "rkv_internal.h"
+#include "rkv_wave.h"
+
+#include <math.h>
+
+namespace rkv {
+
+namespace {
+
+// Log-sum-exp merge of partials (patch 0070 streaming_combine_kernel, applied to the
+// un-normalised (M, S, VKQ) form).  One workgroup per output row: the segment weights
+// e^(M_s - M*) are computed once into LDS, then 8 groups of 128 lanes accumulate the
+// values of interleaved segments and fold through LDS.
+constexpr int kMergeGroups = 8;
+constexpr int kMergeThreads = kMergeGroups * kHeadDim;
+constexpr int kMergeTile = 2048;  // segment weights held in LDS per pass
+
+__global__ void __launch_bounds__(kMergeThreads) merge_kernel(const float *__restrict__ part, int n_seg,
+                                                              int64_t n_rows, float *__restrict__ o,
+                                                              float *__restrict__ lse,
+                                                              float *__restrict__ pout) {
+    __shared__ float s_wt[kMergeTile];
+    __shared__ float s_red[kMergeThreads / 64];
+    __shared__ float s_acc[kMergeGroups][kHeadDim];
+    const int64_t row = blockIdx.x;
+    const int tid = threadIdx.x, d = tid & (kHeadDim - 1), grp = tid / kHeadDim;
+    const int64_t step = n_rows * kPartialStride;
+    const float *base = part + row * kPartialStride;
+
+    // M* = max over segments
+    float M = -INFINITY;
+    for (int s = tid; s < n_seg; s += kMergeThreads) M = fmaxf(M, base[(int64_t)s * step]);
+    M = wave_max(M);
+    if ((tid & 63) == 0) s_red[tid >> 6] = M;
+    __syncthreads();
+    M = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < kMergeThreads / 64; ++j) M = fmaxf(M, s_red[j]);
+    __syncthreads();
+
+    float S = 0.f, acc = 0.f;
+    if (M != -INFINITY) {
+        for (int t0 = 0; t0 < n_seg; t0 += kMergeTile) {
+            const int nt = min(kMergeTile, n_seg - t0);
+            for (int j = tid; j < nt; j += kMergeThreads) {
+                const float *pp = base + (int64_t)(t0 + j) * step;
+                const float Ms = pp[0];
+                const float w = (Ms == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((Ms - M) * kLog2e);
+                s_wt[j] = w;
+                S = fmaf(pp[1], w, S);  // each segment's S counted once, by the lane that weighed it
+            }
+            __syncthreads();
+#pragma unroll 4
+            for (int j = grp; j < nt; j += kMergeGroups) acc = fmaf(base[(int64_t)(t0 + j) * step + 2 + d], s_wt[j], acc);
+            __syncthreads();
+        }
+    }
+    // fold S over the block and acc over the groups
+    S = wave_sum(S);
+    if ((tid & 63) == 0) s_red[tid >> 6] = S;
+    s_acc[grp][d] = acc;
+    __syncthreads();
+    if (grp != 0) return;
+    S = 0.f;
+#pragma unroll
+    for (int j = 0; j < kMergeThreads / 64; ++j) S += s_red[j];
+    acc = 0.f;
+#pragma unroll
+    for (int j = 0; j < kMergeGroups; ++j) acc += s_acc[j][d];
+    if (pout) {
+        float *q = pout + row * kPartialStride;
+        if (d == 0) {
+            q[0] = M;
+            q[1] = S;
+        }
+        q[2 + d] = acc;
+        return;
+    }
+    const bool ok = (M != -INFINITY) && (S > 0.f);
+    o[row * kHeadDim + d] = ok ? acc / S : 0.f;
+    if (lse && d == 0) lse[row] = ok ? M + logf(S) : -INFINITY;
+}
+
+// The same merge for many rows over few segments (prefill: thousands of rows, a handful of
+// segments): one wave per output row, lane l holding head_dim l and l+64; segment weights
+// are computed by the lane of that segment and read back with readlane.
+constexpr int kMergeRowsPerBlock = 4;
+
+__global__ void __launch_bounds__(64 * kMergeRowsPerBlock) merge_rows_kernel(const float *__restrict__ part, int n_seg,
+                                                                           int64_t n_rows, float *__restrict__ o,
+                                                                           float *__restrict__ lse,
+                                                                           float *__restrict__ pout) {
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * kMergeRowsPerBlock + (threadIdx.x >> 6);
+    if (row >= n_rows) return;
+    const int64_t step = n_rows * kPartialStride;
+    const float *base = part + row * kPartialStride;
+    float M = -INFINITY;
+    for (int s = lane; s < n_seg; s += 64) M = fmaxf(M, base[(int64_t)s * step]);
+    M = wave_max(M);
+    float S = 0.f, a0 = 0.f, a1 = 0.f;
+    if (M != -INFINITY) {
+        for (int s0 = 0; s0 < n_seg; s0 += 64) {
+            const int s = s0 + lane;
+            float w = 0.f;
+            if (s < n_seg) {
+                const float Ms = base[(int64_t)s * step];
+                w = (Ms == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((Ms - M) * kLog2e);
+                S = fmaf(base[(int64_t)s * step + 1], w, S);
+            }
+            const int nt = min(64, n_seg - s0);
+            for (int j = 0; j < nt; ++j) {
+                const float wj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), j));
+                const float *v = base + (int64_t)(s0 + j) * step + 2 + lane;
+                a0 = fmaf(v[0], wj, a0);
+                a1 = fmaf(v[64], wj, a1);
+            }
+        }
+    }
+    S = wave_sum(S);
+    if (pout) {
+        float *q = pout + row * kPartialStride;
+        if (lane == 0) {
+            q[0] = M;
+            q[1] = S;
+        }
+        q[2 + lane] = a0;
+        q[66 + lane] = a1;
+        return;
+    }
+    const bool ok = (M != -INFINITY) && (S > 0.f);
+    o[row * kHeadDim + lane] = ok ? a0 / S : 0.f;
+    o[row * kHeadDim + 64 + lane] = ok ? a1 / S : 0.f;
+    if (lse && lane == 0) lse[row] = ok ? M + logf(S) : -INFINITY;
+}
+
+__global__ void __launch_bounds__(128) empty_partials_kernel(float *__restrict__ part) {
+    float *q = part + (int64_t)blockIdx.x * kPartialStride;
+    q[2 + threadIdx.x] = 0.f;
+    if (threadIdx.x == 0) {
+        q[0] = -INFINITY;
+        q[1] = 0.f;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_merge(const float *partials, int n_seg, int64_t n_rows, float *o, float *lse,
+                        float *partial_out, hipStream_t s) {
+    if (n_rows <= 0) return hipSuccess;
+    if (n_rows >= 1024 || n_seg <= 16) {
+        // enough rows to fill the chip one wave each (or too few segments to share a row)
+        hipLaunchKernelGGL(merge_rows_kernel, dim3((unsigned)((n_rows + kMergeRowsPerBlock - 1) / kMergeRowsPerBlock)),
+                           dim3(64 * kMergeRowsPerBlock), 0, s, partials, n_seg, n_rows, o, lse, partial_out);
+    } else {
+        hipLaunchKernelGGL(merge_kernel, dim3((unsigned)n_rows), dim3(kMergeThreads), 0, s, partials, n_seg, n_rows,
+                           o, lse, partial_out);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_empty_partials(float *partials, int64_t n_rows, hipStream_t s) {
+    if (n_rows <= 0) return hipSuccess;
+    hipLaunchKernelGGL(empty_partials_kernel, dim3((unsigned)n_rows), dim3(kHeadDim), 0, s, partials);
+    return hipGetLastError();
+}
+
+}  // namespace rkv

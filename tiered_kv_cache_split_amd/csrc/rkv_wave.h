@@ -1,0 +1,59 @@
+// Wave64 reductions shared by the gfx950 kernels of librkv.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rkv {
+
+inline constexpr float kLog2e = 1.4426950408889634f;
+inline constexpr float kLn2 = 0.6931471805599453f;
+
+// ---- wave64 reductions.  Floats are maxed as order-preserving integer keys so the max is a
+// plain integer op on DPP operands; rows of 16 lanes are reduced with DPP, then row pairs and
+// wave halves with the gfx950 permlane swaps.
+__device__ __forceinline__ int f2key(float x) {
+    const int b = __builtin_bit_cast(int, x);
+    return b ^ ((b >> 31) & 0x7FFFFFFF);
+}
+__device__ __forceinline__ float key2f(int k) { return __builtin_bit_cast(float, k ^ ((k >> 31) & 0x7FFFFFFF)); }
+
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int x) { return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xF, 0xF, false); }
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+inline constexpr int kQuadSwap1 = 0xB1, kQuadSwap2 = 0x4E, kRowRor4 = 0x124, kRowRor8 = 0x128;
+
+// Value of lane k summed over the four 16-lane rows, in every row.
+__device__ __forceinline__ float fold_rows(float x) {
+    const int xi = __builtin_bit_cast(int, x);
+    const auto r16 = __builtin_amdgcn_permlane16_swap(xi, xi, false, false);
+    x = __builtin_bit_cast(float, (int)r16[0]) + __builtin_bit_cast(float, (int)r16[1]);
+    const int yi = __builtin_bit_cast(int, x);
+    const auto r32 = __builtin_amdgcn_permlane32_swap(yi, yi, false, false);
+    return __builtin_bit_cast(float, (int)r32[0]) + __builtin_bit_cast(float, (int)r32[1]);
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+    int k = f2key(x);
+    k = max(k, dpp_i<kQuadSwap1>(k));
+    k = max(k, dpp_i<kQuadSwap2>(k));
+    k = max(k, dpp_i<kRowRor4>(k));
+    k = max(k, dpp_i<kRowRor8>(k));
+    const auto r16 = __builtin_amdgcn_permlane16_swap(k, k, false, false);
+    k = max((int)r16[0], (int)r16[1]);
+    const auto r32 = __builtin_amdgcn_permlane32_swap(k, k, false, false);
+    k = max((int)r32[0], (int)r32[1]);
+    return key2f(k);
+}
+__device__ __forceinline__ float wave_sum(float x) {
+    x += dpp_f<kQuadSwap1>(x);
+    x += dpp_f<kQuadSwap2>(x);
+    x += dpp_f<kRowRor4>(x);
+    x += dpp_f<kRowRor8>(x);
+    return fold_rows(x);
+}
+
+}  // namespace rkv
