@@ -71,3 +71,54 @@ def test_rows_gqa8_two_queries(run):
     O, L = run.rows(w)
     Oref, Lref = oracle_rows(w)
     assert_close(O, L, Oref, Lref, what="rows n_q 2")
+
+
+def test_rows_padding_scattered_inside_lists(run):
+    """-1 entries in the middle of a list (not only as trailing padding), f16 cell-major pool."""
+    rng = np.random.default_rng(17)
+    w = gen.make_workload(4, scale_down=16)
+    rows = w["kv_rows"].copy()
+    hole = rng.random(rows.shape) < 0.3
+    rows[hole] = -1
+    rows[1, 64:192] = -1  # two whole 64-entry chunks of padding in the middle
+    step("rows f16 scattered padding, no mask")
+    O, L = run.rows(w, rows=rows, mask=None)
+    Oref, Lref = oracle_rows(w, rows=rows, mask=None)
+    assert_close(O, L, Oref, Lref, what="rows scattered padding")
+
+
+@pytest.mark.parametrize("n_head,n_head_kv", [(4, 4), (6, 3), (10, 5)])
+def test_rows_head_shapes_without_cell_instantiation(run, n_head, n_head_kv):
+    """One row per KV head, or an odd KV head count: the per-head kernel serves these."""
+    rng = gen.rng_for(42)
+    n_pool = 2500
+    q = gen.draw_normal(rng, (3, n_head, 1, 128)).astype(np.float16)
+    k = gen.pack_f16(gen.draw_normal(rng, (n_pool, n_head_kv, 128)))
+    v = gen.pack_f16(gen.draw_normal(rng, (n_pool, n_head_kv, 128)))
+    rows = gen.rows_lists(rng, n_pool, (900, 400, 1300), 1300)
+    mask = np.where(rows[:, None, None, :] >= 0, 0.0, -np.inf).astype(np.float16)
+    w = dict(q=q, k=k, v=v, kv_rows=rows, mask=mask, k_type=gen.TYPE_F16, v_type=gen.TYPE_F16,
+             scale=1 / np.sqrt(128))
+    step(f"rows f16 heads {n_head}/{n_head_kv}")
+    O, L = run.rows(w)
+    Oref, Lref = oracle_rows(w)
+    assert_close(O, L, Oref, Lref, what="rows head shapes")
+
+
+def test_rows_full_size_config4_sampled_heads(run):
+    """Full pool (65536 cells x 8 KV heads f16) and lists 8192/12288/20480/30720, in the launch
+    configuration the benchmark times; the oracle checks every query head of KV heads 0 and 5."""
+    import oracle
+    w = gen.make_workload(4)
+    step("rows full size config 4")
+    O, L = run.rows(w)
+    assert np.all(np.isfinite(O)) and np.all(np.isfinite(L))
+    gqa = w["n_head"] // w["n_head_kv"]
+    mm = np.asarray(w["mask"], dtype=np.float64)[:, 0]
+    for g in (0, 5):
+        k = oracle.kv_values(w["k_type"], w["k"][:, g:g + 1])
+        v = oracle.kv_values(w["v_type"], w["v"][:, g:g + 1])
+        q = np.stack([oracle.q_values(w["q"][b, g * gqa:(g + 1) * gqa]) for b in range(w["q"].shape[0])])
+        Oref, Lref = oracle.attention_rows(q, k, v, w["kv_rows"], w["scale"], mm)
+        assert_close(O[:, :, g * gqa:(g + 1) * gqa], L[:, :, g * gqa:(g + 1) * gqa], Oref, Lref,
+                     what=f"rows full size head group {g}")

@@ -473,8 +473,11 @@ decode_seg_kernel(const SegParams p) {
     uint8_t *lk = s_k[wave];
     uint8_t *lv = s_v[wave];
     const int64_t n_ch = (c_end > c_beg) ? (c_end - c_beg + kChunk - 1) / kChunk : 0;
+    // K rows are fetched one chunk ahead, except when both K and V are binary16: V then sits in
+    // registers during Q.K, and holding the next chunk's K as well would spill
+    constexpr bool kPrefetchK = kVq || KT != T_F16;
     int myrow = -1;
-    if (wave < n_ch) {
+    if (kPrefetchK && wave < n_ch) {
         const int64_t c0 = c_beg + (int64_t)wave * kChunk;
         myrow = row_of(c0);
         fetch_rows<KT, ROWS>(kb, kbase, p.k_s1, c0, nvalid(c0), myrow, lane);
@@ -483,24 +486,36 @@ decode_seg_kernel(const SegParams p) {
 
     for (int64_t ch = wave; ch < n_ch; ch += kWaves) {
         const int64_t c0 = c_beg + ch * kChunk;
+        if constexpr (!kPrefetchK) {
+            myrow = row_of(c0);
+            fetch_rows<KT, ROWS>(kb, kbase, p.k_s1, c0, nvalid(c0), myrow, lane);
+        }
+        const int cur_row = myrow;
+        // a chunk of gathered rows that is all padding contributes nothing (uniform per wave)
+        const bool any = !ROWS || __builtin_amdgcn_ballot_w64(cur_row >= 0) != 0;
+        // binary16 V without K prefetch: this chunk's rows into registers, in flight during Q.K
+        if constexpr (!kVq && !kPrefetchK) {
+            if (any) fetch_rows<VT, ROWS>(vb, vbase, p.v_s1, c0, nvalid(c0), cur_row, lane);
+        }
         stash_rows<KT>(kb, lk, kKs, lane);
         if constexpr (kVq) stash_rows<VT>(vb, lv, kVs, lane);
-        const int cur_row = myrow;
         float xadd[R];
         score_terms<R>(p, qi, b, c0 + lane, cur_row >= 0, xadd);
         wave_sync();
-        // next chunk of this wave (past c_end every row is -1 / out of range: nothing is read)
-        {
+        if constexpr (kPrefetchK) {
+            // next chunk of this wave (past c_end every row is -1 / out of range: nothing is read)
             const int64_t cn = c0 + kWaves * kChunk;
             myrow = row_of(cn);
             fetch_rows<KT, ROWS>(kb, kbase, p.k_s1, cn, nvalid(cn), myrow, lane);
             if constexpr (kVq) fetch_rows<VT, ROWS>(vb, vbase, p.v_s1, cn, nvalid(cn), myrow, lane);
+            // binary16 V: this chunk's rows straight into registers, in flight during Q.K
+            if constexpr (!kVq) {
+                if (any) fetch_rows<VT, ROWS>(vb, vbase, p.v_s1, c0, nvalid(c0), cur_row, lane);
+            }
         }
-        // binary16 V: this chunk's rows straight into registers, in flight during Q.K
-        if constexpr (!kVq) fetch_rows<VT, ROWS>(vb, vbase, p.v_s1, c0, nvalid(c0), cur_row, lane);
-
-        process_chunk<KT, VT, R, kVq>(lk + lane * kKs, lv, kVs, vb, qw, s_qsum, s_w[wave], xadd, p.scale_log2,
-                                      lane, m, l, acc, sw);
+        if (any)
+            process_chunk<KT, VT, R, kVq>(lk + lane * kKs, lv, kVs, vb, qw, s_qsum, s_w[wave], xadd, p.scale_log2,
+                                          lane, m, l, acc, sw);
         wave_sync();
     }
     finish_wave<VT, R>(lane, l, acc, sw);
@@ -550,12 +565,13 @@ decode_seg_kernel(const SegParams p) {
 }
 
 // ============================================================================ cell-major kernel
-// K/V stored cell-major with all HW KV heads packed inside each cell (row stride nb[2] equal
-// to the row size): the heads of one cell are one contiguous segment.  Workgroup = HW waves
-// for one (split, sequence); wave w is KV head w.  Every 64-cell chunk is fetched by the
-// whole workgroup as one contiguous span with 16-byte loads (one chunk ahead, in registers)
-// and stored to LDS with a small pad per cell so that the one-row-per-lane K reads stay
-// bank-conflict free; each wave then runs the Q.K / softmax / P.V of its head.
+// K/V stored cell-major with the KV heads packed inside each cell (row stride nb[2] equal to
+// the row size): the HW heads of a head group in one cell are one contiguous segment.
+// Workgroup = HW waves for one (split, head group, sequence); wave w is KV head g0 + w.  Every
+// 64-cell chunk is fetched by the whole workgroup as one contiguous span with 16-byte loads
+// (one chunk ahead, in registers) and stored to LDS with a small pad per cell so that the
+// one-row-per-lane K reads stay bank-conflict free; each wave then runs the Q.K / softmax /
+// P.V of its head.
 template <int T> constexpr int cell_pad() { return T == T_F16 ? 16 : 8; }
 
 template <int KT, int VT, int R, int HW>
@@ -563,7 +579,7 @@ __global__ void __launch_bounds__(64 * HW) __attribute__((amdgpu_waves_per_eu(2)
 decode_cell_kernel(const SegParams p) {
     constexpr int kNB = n_wblocks<VT>();
     constexpr int kRk = RowFmt<KT>::kRow, kRv = RowFmt<VT>::kRow;  // bytes of one head row
-    constexpr int kCk = HW * kRk, kCv = HW * kRv;                  // bytes of one cell (all heads)
+    constexpr int kCk = HW * kRk, kCv = HW * kRv;                  // bytes of one cell (head group)
     constexpr int kSk = kCk + cell_pad<KT>(), kSv = kCv + cell_pad<VT>();  // LDS cell strides
     constexpr int kNT = 64 * HW;
     constexpr int kUk = kChunk * kCk / 16, kUv = kChunk * kCv / 16;         // 16-byte units per chunk
@@ -575,16 +591,23 @@ decode_cell_kernel(const SegParams p) {
     __shared__ float s_qsum[HW][R * 4];
 
     const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-    const int split = blockIdx.x % p.n_splits;
-    const int b = blockIdx.x / p.n_splits;
+    const int n_hgrp = p.n_head_kv / HW;
+    int bid = blockIdx.x;
+    const int split = bid % p.n_splits;
+    bid /= p.n_splits;
+    const int hgrp = bid % n_hgrp;
+    const int b = bid / n_hgrp;
+    const int g = hgrp * HW + wave;  // this wave's KV head
     const int64_t c_beg = (int64_t)split * p.cells_per_split;
     const int64_t c_end = min(p.n_cells, c_beg + (int64_t)p.cells_per_split);
+    const uint8_t *kbase = p.k + (int64_t)(hgrp * HW) * p.k_s2;
+    const uint8_t *vbase = p.v + (int64_t)(hgrp * HW) * p.v_s2;
 
     const uint32_t *qw[R];
     int qi[R];
-    q_rows<R>(p, wave, b, qw, qi);
+    q_rows<R>(p, g, b, qw, qi);
     if constexpr (KT == T_Q8_0) {
-        if (lane < R * 4) q_block_sums<R>(p, wave, b, s_qsum[wave], lane);
+        if (lane < R * 4) q_block_sums<R>(p, g, b, s_qsum[wave], lane);
     }
     wave_sync();
 
@@ -599,7 +622,7 @@ decode_cell_kernel(const SegParams p) {
         for (int j = 0; j < kNB; ++j) sw[rho][j] = 0.f;
     }
 
-    // per-thread 16-byte units: chunk offsets (global, by cell stride) and LDS offsets (padded)
+    // per-thread 16-byte units: chunk-relative global offsets (by cell stride) and LDS offsets (padded)
     int gk[kLk], lk[kLk], gv[kLv], lv[kLv];
 #pragma unroll
     for (int i = 0; i < kLk; ++i) {
@@ -617,9 +640,9 @@ decode_cell_kernel(const SegParams p) {
     auto fetch = [&](int64_t c0) {
         const int64_t nv = max((int64_t)0, min((int64_t)kChunk, c_end - c0));
         const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(p.k + c0 * p.k_s1), (short)0, (int)(nv * p.k_s1), 0x00020000);
+            (void *)(kbase + c0 * p.k_s1), (short)0, (int)(nv * p.k_s1), 0x00020000);
         const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(p.v + c0 * p.v_s1), (short)0, (int)(nv * p.v_s1), 0x00020000);
+            (void *)(vbase + c0 * p.v_s1), (short)0, (int)(nv * p.v_s1), 0x00020000);
 #pragma unroll
         for (int i = 0; i < kLk; ++i) kb[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, gk[i], 0, 0));
 #pragma unroll
@@ -660,7 +683,7 @@ decode_cell_kernel(const SegParams p) {
     finish_wave<VT, R>(lane, l, acc, sw);
 
     // ---- each wave writes the partial of its KV head
-    const int g = wave, slot = p.slot0 + split;
+    const int slot = p.slot0 + split;
 #pragma unroll
     for (int rho = 0; rho < R; ++rho) {
         const int r = rho % p.gqa, i = rho / p.gqa;
@@ -678,25 +701,28 @@ decode_cell_kernel(const SegParams p) {
 }
 
 template <int KT, int VT, int R, int HW>
-hipError_t launch_cell(const SegParams &p, hipStream_t s) {
-    hipLaunchKernelGGL((decode_cell_kernel<KT, VT, R, HW>), dim3((unsigned)(p.n_splits * p.n_seq)), dim3(64 * HW), 0,
-                       s, p);
+hipError_t launch_cell(const SegParams &p, hipStream_t s, int *occupancy) {
+    if (occupancy)
+        return hipOccupancyMaxActiveBlocksPerMultiprocessor(occupancy, decode_cell_kernel<KT, VT, R, HW>, 64 * HW, 0);
+    hipLaunchKernelGGL((decode_cell_kernel<KT, VT, R, HW>), dim3((unsigned)(p.n_splits * (p.n_head_kv / HW) * p.n_seq)),
+                       dim3(64 * HW), 0, s, p);
     return hipGetLastError();
 }
 
 template <int KT, int VT, int R>
-hipError_t launch_decode_r(const SegParams &p, hipStream_t s) {
+hipError_t launch_decode_r(const SegParams &p, hipStream_t s, int *occupancy) {
     if (p.cell_hw > 0) {
         if constexpr (KT == T_Q8_0 && VT == T_Q4_0) {
-            if (p.cell_hw == 8) return launch_cell<KT, VT, R, 8>(p, s);
-            if (p.cell_hw == 4) return launch_cell<KT, VT, R, 4>(p, s);
-            if (p.cell_hw == 2) return launch_cell<KT, VT, R, 2>(p, s);
+            if (p.cell_hw == 8) return launch_cell<KT, VT, R, 8>(p, s, occupancy);
+            if (p.cell_hw == 4) return launch_cell<KT, VT, R, 4>(p, s, occupancy);
+            if (p.cell_hw == 2) return launch_cell<KT, VT, R, 2>(p, s, occupancy);
         }
         if constexpr (KT == T_F16 && VT == T_F16) {
-            if (p.cell_hw == 2) return launch_cell<KT, VT, R, 2>(p, s);
+            if (p.cell_hw == 2) return launch_cell<KT, VT, R, 2>(p, s, occupancy);
         }
         return hipErrorInvalidValue;
     }
+    if (occupancy) return hipErrorInvalidValue;
     const int64_t blocks = (int64_t)p.n_splits * p.n_head_kv * p.n_seq;
     if (p.rows)
         hipLaunchKernelGGL((decode_seg_kernel<KT, VT, R, true>), dim3((unsigned)blocks), dim3(64 * kWaves), 0, s, p);
@@ -706,36 +732,50 @@ hipError_t launch_decode_r(const SegParams &p, hipStream_t s) {
 }
 
 template <int KT, int VT>
-hipError_t launch_decode_t(const SegParams &p, int R, hipStream_t s) {
+hipError_t launch_decode_t(const SegParams &p, int R, hipStream_t s, int *occupancy) {
     switch (R) {
-        case 1: return launch_decode_r<KT, VT, 1>(p, s);
-        case 2: return launch_decode_r<KT, VT, 2>(p, s);
-        case 3: return launch_decode_r<KT, VT, 3>(p, s);
-        case 4: return launch_decode_r<KT, VT, 4>(p, s);
-        case 5: return launch_decode_r<KT, VT, 5>(p, s);
-        case 6: return launch_decode_r<KT, VT, 6>(p, s);
-        case 7: return launch_decode_r<KT, VT, 7>(p, s);
-        case 8: return launch_decode_r<KT, VT, 8>(p, s);
+        case 1: return launch_decode_r<KT, VT, 1>(p, s, occupancy);
+        case 2: return launch_decode_r<KT, VT, 2>(p, s, occupancy);
+        case 3: return launch_decode_r<KT, VT, 3>(p, s, occupancy);
+        case 4: return launch_decode_r<KT, VT, 4>(p, s, occupancy);
+        case 5: return launch_decode_r<KT, VT, 5>(p, s, occupancy);
+        case 6: return launch_decode_r<KT, VT, 6>(p, s, occupancy);
+        case 7: return launch_decode_r<KT, VT, 7>(p, s, occupancy);
+        case 8: return launch_decode_r<KT, VT, 8>(p, s, occupancy);
         default: return hipErrorInvalidValue;
     }
 }
 
+hipError_t dispatch_decode(const SegParams &p, int k_type, int v_type, hipStream_t s, int *occupancy) {
+    const int R = p.gqa * p.n_q;
+    if (k_type == T_Q8_0 && v_type == T_Q4_0) return launch_decode_t<T_Q8_0, T_Q4_0>(p, R, s, occupancy);
+    if (k_type == T_F16 && v_type == T_F16) return launch_decode_t<T_F16, T_F16>(p, R, s, occupancy);
+    if (k_type == T_Q8_0 && v_type == T_F16) return launch_decode_t<T_Q8_0, T_F16>(p, R, s, occupancy);
+    if (k_type == T_F16 && v_type == T_Q4_0) return launch_decode_t<T_F16, T_Q4_0>(p, R, s, occupancy);
+    return hipErrorInvalidValue;
+}
+
 }  // namespace
 
-bool cell_kernel_ok(int k_type, int v_type, int n_head_kv, int R) {
-    if (R < 1 || R > kMaxRowsVec) return false;
-    if (k_type == T_Q8_0 && v_type == T_Q4_0) return n_head_kv == 2 || n_head_kv == 4 || n_head_kv == 8;
-    if (k_type == T_F16 && v_type == T_F16) return n_head_kv == 2;
-    return false;
+int cell_heads(int k_type, int v_type, int n_head_kv, int R, bool rows) {
+    if (R < 1 || R > kMaxRowsVec || rows) return 0;  // gathered rows: per-head kernel
+    if (k_type == T_Q8_0 && v_type == T_Q4_0) {
+        for (int hw : {8, 4, 2})
+            if (n_head_kv % hw == 0) return hw;
+        return 0;
+    }
+    if (k_type == T_F16 && v_type == T_F16) return n_head_kv % 2 == 0 ? 2 : 0;
+    return 0;
+}
+
+int cell_blocks_per_cu(const SegParams &p, int k_type, int v_type) {
+    int n = 0;
+    if (p.cell_hw <= 0 || dispatch_decode(p, k_type, v_type, nullptr, &n) != hipSuccess || n < 1) return 1;
+    return n;
 }
 
 hipError_t launch_decode_segment(const SegParams &p, int k_type, int v_type, hipStream_t s) {
-    const int R = p.gqa * p.n_q;
-    if (k_type == T_Q8_0 && v_type == T_Q4_0) return launch_decode_t<T_Q8_0, T_Q4_0>(p, R, s);
-    if (k_type == T_F16 && v_type == T_F16) return launch_decode_t<T_F16, T_F16>(p, R, s);
-    if (k_type == T_Q8_0 && v_type == T_F16) return launch_decode_t<T_Q8_0, T_F16>(p, R, s);
-    if (k_type == T_F16 && v_type == T_Q4_0) return launch_decode_t<T_F16, T_Q4_0>(p, R, s);
-    return hipErrorInvalidValue;
+    return dispatch_decode(p, k_type, v_type, s, nullptr);
 }
 
 }  // namespace rkv

@@ -38,12 +38,14 @@ struct SegParams {
     float *partials;   // [slot][n_rows][2 + 128]
     int slot0;         // first partial slot used by this segment
     int64_t n_rows;    // n_head * n_q * n_seq
-    int cell_hw;       // > 0: K/V are cell-major with all cell_hw KV heads packed per cell
+    int cell_hw;       // > 0: cell-major kernel, cell_hw KV heads (packed per cell) per workgroup
 };
 
-// Whether the vector kernel can read this segment as whole cells (all KV heads packed inside
-// each cell, 16-byte aligned): then one workgroup owns all heads of a cell range.
-bool cell_kernel_ok(int k_type, int v_type, int n_head_kv, int R);
+// KV heads per workgroup of the cell-major vector kernel for these types (0: no instantiation):
+// a workgroup owns that many heads, packed inside each cell, over a cell range.
+int cell_heads(int k_type, int v_type, int n_head_kv, int R, bool rows);
+// Resident workgroups per CU of the cell-major kernel selected by p.cell_hw (at least 1).
+int cell_blocks_per_cu(const SegParams &p, int k_type, int v_type);
 
 // Launches; every function returns a hipError_t and checks nothing the host has not.
 hipError_t launch_decode_segment(const SegParams &p, int k_type, int v_type, hipStream_t s);

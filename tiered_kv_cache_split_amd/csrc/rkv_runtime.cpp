@@ -257,22 +257,24 @@ struct Seg {
     int64_t n_cells, pos0;
 };
 
-// The cell-major kernel applies when every cell holds all KV heads packed (head stride ==
-// row size), cell strides and bases are 16-byte aligned, and the head count and types have an
-// instantiation.
-bool use_cell_kernel(const Seg &sg, const SegParams &p, int k_type, int v_type) {
+// KV heads per workgroup of the cell-major kernel for this segment, or 0 when it does not
+// apply: every cell must hold the KV heads packed (head stride == row size), cell strides and
+// bases must be 16-byte aligned, and the types and head count must have an instantiation.
+int use_cell_kernel(const Seg &sg, const SegParams &p, int k_type, int v_type) {
     const int64_t rk = row_bytes(k_type), rv = row_bytes(v_type);
-    if (!cell_kernel_ok(k_type, v_type, p.n_head_kv, p.gqa * p.n_q)) return false;
-    if (p.n_head_kv > 1 && (sg.k_s2 != rk || sg.v_s2 != rv)) return false;
-    if (sg.k_s1 < p.n_head_kv * rk || sg.v_s1 < p.n_head_kv * rv) return false;
-    if ((sg.k_s1 | sg.v_s1) % 16 != 0) return false;
-    if (((uintptr_t)sg.k | (uintptr_t)sg.v) % 16 != 0) return false;
-    return true;
+    const int hw = cell_heads(k_type, v_type, p.n_head_kv, p.gqa * p.n_q, p.rows != nullptr);
+    if (hw == 0) return 0;
+    if (p.n_head_kv > 1 && (sg.k_s2 != rk || sg.v_s2 != rv)) return 0;
+    if (sg.k_s1 < p.n_head_kv * rk || sg.v_s1 < p.n_head_kv * rv) return 0;
+    if ((sg.k_s1 | sg.v_s1) % 16 != 0) return 0;
+    if (((uintptr_t)sg.k | (uintptr_t)sg.v) % 16 != 0) return 0;
+    return hw;
 }
 
 // Split-K plan of one device segment: cells per split and number of splits.  The vector
 // kernel walks 64-cell chunks; the MFMA kernel walks key tiles of prefill_keys_per_iter().
-void seg_plan(const rkv_ctx *ctx, int64_t n_cells, const SegParams &p, bool mfma, int64_t &cps, int &n_splits) {
+void seg_plan(const rkv_ctx *ctx, int64_t n_cells, const SegParams &p, bool mfma, int cell_occupancy, int64_t &cps,
+              int &n_splits) {
     if (mfma) {
         const int kpi = prefill_keys_per_iter();
         const int64_t q_tiles = ((int64_t)p.gqa * p.n_q + prefill_rows_per_block() - 1) / prefill_rows_per_block();
@@ -285,10 +287,11 @@ void seg_plan(const rkv_ctx *ctx, int64_t n_cells, const SegParams &p, bool mfma
         cps = (n_cells + want - 1) / want;
         cps = std::max<int64_t>(kpi, (cps + kpi - 1) / kpi * kpi);
     } else if (p.cell_hw > 0) {
-        // cell-major kernel: one workgroup (n_head_kv waves) per split and per CU (its LDS
-        // footprint allows one resident workgroup per CU), at least 256 cells each
-        int64_t want = ctx->splits_override > 0 ? ctx->splits_override
-                                                : std::max<int64_t>(1, (ctx->n_cu + p.n_seq - 1) / p.n_seq);
+        // cell-major kernel: one wave of resident workgroups over (split, head group, sequence),
+        // at least 256 cells per split
+        const int64_t groups = (int64_t)p.n_seq * (p.n_head_kv / p.cell_hw);
+        const int64_t slots = (int64_t)std::max(1, cell_occupancy) * ctx->n_cu;
+        int64_t want = ctx->splits_override > 0 ? ctx->splits_override : std::max<int64_t>(1, slots / groups);
         want = std::max<int64_t>(1, std::min(want, std::max<int64_t>(1, n_cells / 256)));
         cps = (n_cells + want - 1) / want;
         cps = std::max<int64_t>(kChunk, (cps + kChunk - 1) / kChunk * kChunk);
@@ -308,9 +311,10 @@ struct SegPlan {
 
 SegPlan plan_segment(const rkv_ctx *ctx, const SegParams &base, const Seg &sg, bool mfma, int k_type, int v_type) {
     SegParams p = base;
-    p.cell_hw = (!mfma && !p.rows && use_cell_kernel(sg, p, k_type, v_type)) ? p.n_head_kv : 0;
+    p.cell_hw = mfma ? 0 : use_cell_kernel(sg, p, k_type, v_type);
     SegPlan pl{p.cell_hw, 0, 0};
-    seg_plan(ctx, sg.n_cells, p, mfma, pl.cps, pl.n_splits);
+    const int occ = p.cell_hw > 0 ? cell_blocks_per_cu(p, k_type, v_type) : 1;
+    seg_plan(ctx, sg.n_cells, p, mfma, occ, pl.cps, pl.n_splits);
     return pl;
 }
 
