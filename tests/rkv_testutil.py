@@ -58,15 +58,17 @@ def oracle_decode(w, mask=None, heads=None):
     """fp64 oracle of a window/tail workload dict from rkv_inputs.make_workload.
     heads: optional list of KV heads to restrict to (full-size sampling)."""
     q = oracle.q_values(w["q"])
-    k = oracle.kv_values(w["k_type"], w["k"])
-    v = oracle.kv_values(w["v_type"], w["v"])
     gqa = w["n_head"] // w["n_head_kv"]
     m = None if mask is None else np.asarray(mask, dtype=np.float64)
     if heads is None:
+        k = oracle.kv_values(w["k_type"], w["k"])
+        v = oracle.kv_values(w["v_type"], w["v"])
         return oracle.attention(q, k, v, w["scale"], m)
     outs = {}
     for g in heads:
-        O, L = oracle.attention(q[g * gqa:(g + 1) * gqa], k[g:g + 1], v[g:g + 1], w["scale"], m)
+        k = oracle.kv_values(w["k_type"], w["k"][:, g:g + 1])
+        v = oracle.kv_values(w["v_type"], w["v"][:, g:g + 1])
+        O, L = oracle.attention(q[g * gqa:(g + 1) * gqa], k, v, w["scale"], m)
         outs[g] = (O, L)
     return outs
 

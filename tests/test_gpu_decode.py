@@ -221,3 +221,74 @@ def test_large_logits_need_the_true_running_max(run, kt, vt):
     O, L = run.decode(w, tail="host")
     Oref, Lref = oracle_decode(w)
     assert_close(O, L, Oref, Lref, what="large logits")
+
+
+# ---- matrix-core decode kernel (cell-major q8_0 K / q4_0 V, eight KV heads per workgroup)
+
+@pytest.mark.parametrize("n_head,n_q", [(8, 1), (16, 1), (24, 1), (32, 1), (40, 1), (48, 1), (56, 1), (64, 1),
+                                        (32, 2), (16, 3)])
+def test_mma_decode_row_counts(run, n_head, n_q):
+    w = gen.make_workload(2, scale_down=32, n_head=n_head, n_q=n_q)  # n_kv 4096, 8 KV heads
+    step(f"decode q8q4 8 kv heads n_head={n_head} n_q={n_q} wc=2500 tile=900")
+    O, L = run.decode(w, wc=2500, tile_kv=900, tail="host")
+    Oref, Lref = oracle_decode(w)
+    assert_close(O, L, Oref, Lref, what=f"mma rows {n_head}x{n_q}")
+
+
+def test_mma_decode_mask_empty_row_ragged(run):
+    w = gen.make_workload(2, scale_down=32, n_q=1)
+    w = dict(w)
+    n_kv = 3001
+    w["k"], w["v"], w["n_kv"] = w["k"][:n_kv], w["v"][:n_kv], n_kv
+    rng = np.random.default_rng(21)
+    mask = gen.random_mask_f16(rng, 1, n_kv, p_hidden=0.3)
+    step("decode q8q4 8 kv heads, mask, n_kv=3001 window only")
+    O, L = run.decode(w, wc=n_kv, tail=None, mask=mask)
+    Oref, Lref = oracle_decode(w, mask=mask)
+    assert_close(O, L, Oref, Lref, what="mma mask")
+    mask2 = np.full((1, n_kv), -np.inf, np.float16)
+    step("decode q8q4 8 kv heads, everything masked")
+    O2, L2 = run.decode(w, wc=n_kv, tail=None, mask=mask2)
+    assert np.all(O2 == 0) and np.all(L2 == -np.inf)
+
+
+def test_mma_decode_outlier_keys(run):
+    rng = gen.rng_for(97)
+    q, k, v = gen.draw_qkv(rng, 40, 1, 8, 3000, k_type=gen.TYPE_Q8_0, v_type=gen.TYPE_Q4_0, outlier_every=17)
+    w = dict(n_head=40, n_head_kv=8, q=q, k=k, v=v, k_type=gen.TYPE_Q8_0, v_type=gen.TYPE_Q4_0,
+             scale=1 / np.sqrt(128), n_kv=3000, wc=1800, tile_kv=600)
+    step("decode q8q4 8 kv heads outlier keys")
+    O, L = run.decode(w, tail="host")
+    Oref, Lref = oracle_decode(w)
+    assert_close(O, L, Oref, Lref, what="mma outliers")
+
+
+def test_mma_decode_two_head_groups(run):
+    w = gen.make_workload(2, scale_down=32, n_head=32, n_head_kv=16)
+    step("decode q8q4 16 kv heads (two groups of 8)")
+    O, L = run.decode(w, wc=3000, tile_kv=1096, tail="device")
+    Oref, Lref = oracle_decode(w)
+    assert_close(O, L, Oref, Lref, what="mma head groups")
+
+
+def test_full_size_config2_sampled_heads(run):
+    """n_kv = 131072 fully resident, 40/8 heads q8_0/q4_0, in the benchmark's launch configuration;
+    the oracle checks every query head of KV heads 0, 3 and 7 over all keys."""
+    w = gen.make_workload(2)
+    step("decode full size config 2")
+    O, L = run.decode(w, wc=w["n_kv"], tail=None)
+    gqa = w["n_head"] // w["n_head_kv"]
+    for g, (Oref, Lref) in oracle_decode(w, heads=[0, 3, 7]).items():
+        assert_close(O[:, g * gqa:(g + 1) * gqa], L[:, g * gqa:(g + 1) * gqa], Oref, Lref, what=f"config 2 head {g}")
+
+
+def test_full_size_config3_sampled_heads(run):
+    """Window 131072 + pinned tail 131072 in 32768-cell tiles (four lifts through the 2-slot ring)."""
+    w = gen.make_workload(3)
+    step("decode full size config 3")
+    O, L = run.decode(w, tail="host")
+    st = run.ctx.stats()
+    assert st["n_tail_tiles"] == 4 and st["lift_bytes"] == 131072 * 8 * (136 + 72)
+    gqa = w["n_head"] // w["n_head_kv"]
+    for g, (Oref, Lref) in oracle_decode(w, heads=[1, 6]).items():
+        assert_close(O[:, g * gqa:(g + 1) * gqa], L[:, g * gqa:(g + 1) * gqa], Oref, Lref, what=f"config 3 head {g}")

@@ -49,6 +49,11 @@ int cell_blocks_per_cu(const SegParams &p, int k_type, int v_type);
 
 // Launches; every function returns a hipError_t and checks nothing the host has not.
 hipError_t launch_decode_segment(const SegParams &p, int k_type, int v_type, hipStream_t s);
+// Matrix-core decode kernel for cell-major q8_0 K / q4_0 V with 8 KV heads per workgroup
+// (decode_mma_ok); with `occupancy` set it reports resident workgroups per CU instead of
+// launching.
+bool decode_mma_ok(const SegParams &p);
+hipError_t launch_decode_mma(const SegParams &p, hipStream_t s, int *occupancy);
 hipError_t launch_prefill_segment(const SegParams &p, int k_type, int v_type, hipStream_t s);
 // Blocks the prefill kernel uses per (q tile, KV head) along the key axis.
 int prefill_rows_per_block();
