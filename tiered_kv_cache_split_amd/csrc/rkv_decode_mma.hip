@@ -92,32 +92,6 @@ decode_mma_kernel(const SegParams p) {
     const uint8_t *kbase = p.k + (int64_t)(hgrp * HW) * p.k_s2;
     const uint8_t *vbase = p.v + (int64_t)(hgrp * HW) * p.v_s2;
 
-    // ---- Q as the A operand of Q.K: lane holds row `col`, head_dim 32*blk + 8*grp + 0..7
-    half8_t qa[4];
-    float4_t cneg[4];  // accumulator inputs: -1152 * block sum of Q for the rows 4*grp + i
-    {
-        const bool ok = col < R;
-        const int r = ok ? col : 0;
-        const _Float16 *qrow = p.q + (int64_t)(r / p.gqa) * p.q_s1 + (int64_t)(g * p.gqa + r % p.gqa) * p.q_s2 +
-                               (int64_t)b * p.q_s3;
-        float qs[4];
-#pragma unroll
-        for (int blk = 0; blk < 4; ++blk) {
-            const uint32_t *src = reinterpret_cast<const uint32_t *>(qrow + 32 * blk + 8 * grp);
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (ok) v = make_uint4(src[0], src[1], src[2], src[3]);
-            qa[blk] = __builtin_bit_cast(half8_t, v);
-            float sum = 0.f;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) sum += (float)qa[blk][j];
-            qs[blk] = fold_rows(sum);  // block sum of row `col`, in every lane of the column
-        }
-#pragma unroll
-        for (int blk = 0; blk < 4; ++blk)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) cneg[blk][i] = -kMagicK * __shfl(qs[blk], 4 * grp + i, 64);
-    }
-
     // ---- chunk fetch (registers, one chunk ahead) and staging (LDS, padded cells).  Thread t
     // moves 16-byte units sub, sub + 8, ... of cell t / 8 (sub = t % 8): eight threads cover
     // 128 contiguous bytes of a cell per instruction, and every offset is a per-thread base plus
@@ -183,6 +157,10 @@ decode_mma_kernel(const SegParams p) {
         lrow[i] = 0.f;
     }
     const half2_t ones = {(_Float16)1.0f, (_Float16)1.0f};
+    // kept in a register so that mask-and-insert compiles to one v_and_or_b32 (two literals
+    // cannot share an instruction)
+    uint32_t vmagic = 0x64006400u;
+    asm volatile("" : "+v"(vmagic));
     const float c = p.scale_log2;
     const uint8_t *kw = s_k + wave * kQ8Row;  // this head's K row of cell j at kw + j*kSk
     const uint8_t *vw = s_v + wave * kQ4Row;
@@ -190,7 +168,34 @@ decode_mma_kernel(const SegParams p) {
     _Float16 *dvw = s_dv[wave];
 
     const int64_t n_ch = (c_end > c_beg) ? (c_end - c_beg + kCh - 1) / kCh : 0;
-    if (n_ch > 0) fetch(c_beg);
+    if (n_ch > 0) fetch(c_beg);  // the first chunk is in flight while Q is prepared
+
+    // ---- Q as the A operand of Q.K: lane holds row `col`, head_dim 32*blk + 8*grp + 0..7
+    half8_t qa[4];
+    float4_t cneg[4];  // accumulator inputs: -1152 * block sum of Q for the rows 4*grp + i
+    {
+        const bool ok = col < R;
+        const int r = ok ? col : 0;
+        const _Float16 *qrow = p.q + (int64_t)(r / p.gqa) * p.q_s1 + (int64_t)(g * p.gqa + r % p.gqa) * p.q_s2 +
+                               (int64_t)b * p.q_s3;
+        float qs[4];
+#pragma unroll
+        for (int blk = 0; blk < 4; ++blk) {
+            const uint32_t *src = reinterpret_cast<const uint32_t *>(qrow + 32 * blk + 8 * grp);
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (ok) v = make_uint4(src[0], src[1], src[2], src[3]);
+            qa[blk] = __builtin_bit_cast(half8_t, v);
+            float sum = 0.f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) sum += (float)qa[blk][j];
+            qs[blk] = fold_rows(sum);  // block sum of row `col`, in every lane of the column
+        }
+#pragma unroll
+        for (int blk = 0; blk < 4; ++blk)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) cneg[blk][i] = -kMagicK * __shfl(qs[blk], 4 * grp + i, 64);
+    }
+
     for (int64_t ch = 0; ch < n_ch; ++ch) {
         const int64_t c0 = c_beg + ch * kCh;
         __syncthreads();  // every wave is done with the previous chunk's LDS
@@ -327,8 +332,8 @@ decode_mma_kernel(const SegParams p) {
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) {
                     const uint32_t y = __builtin_amdgcn_perm(bt[2 * jj + 1], bt[2 * jj], 0x0C040C00u);  // b0, 0, b1, 0
-                    lo[jj] = (y & 0x000F000Fu) | 0x64006400u;
-                    hi[jj] = ((y >> 4) & 0x000F000Fu) | 0x64006400u;
+                    lo[jj] = (y & 0x000F000Fu) | vmagic;
+                    hi[jj] = ((y >> 4) & 0x000F000Fu) | vmagic;
                 }
                 oacc[2 * blk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
                     __builtin_bit_cast(half8_t, make_uint4(lo[0], lo[1], lo[2], lo[3])), wf, oacc[2 * blk], 0, 0, 0);

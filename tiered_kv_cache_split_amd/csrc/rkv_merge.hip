@@ -11,10 +11,11 @@ namespace {
 
 // Log-sum-exp merge of partials (patch 0070 streaming_combine_kernel, applied to the
 // un-normalised (M, S, VKQ) form).  One workgroup per output row: the segment weights
-// e^(M_s - M*) are computed once into LDS, then 8 groups of 128 lanes accumulate the
-// values of interleaved segments and fold through LDS.
-constexpr int kMergeGroups = 8;
-constexpr int kMergeThreads = kMergeGroups * kHeadDim;
+// e^(M_s - M*) are computed once into LDS, then 32 groups of 32 lanes (four head_dim values
+// per lane) accumulate the values of interleaved segments -- many independent loads in
+// flight per lane -- and fold through LDS.
+constexpr int kMergeThreads = 1024;
+constexpr int kMergeGroups = kMergeThreads / 32;
 constexpr int kMergeTile = 2048;  // segment weights held in LDS per pass
 
 __global__ void __launch_bounds__(kMergeThreads) merge_kernel(const float *__restrict__ part, int n_seg,
@@ -25,7 +26,7 @@ __global__ void __launch_bounds__(kMergeThreads) merge_kernel(const float *__res
     __shared__ float s_red[kMergeThreads / 64];
     __shared__ float s_acc[kMergeGroups][kHeadDim];
     const int64_t row = blockIdx.x;
-    const int tid = threadIdx.x, d = tid & (kHeadDim - 1), grp = tid / kHeadDim;
+    const int tid = threadIdx.x, q = tid & 31, grp = tid >> 5;  // lane q holds head_dim q + 32m
     const int64_t step = n_rows * kPartialStride;
     const float *base = part + row * kPartialStride;
 
@@ -40,7 +41,7 @@ __global__ void __launch_bounds__(kMergeThreads) merge_kernel(const float *__res
     for (int j = 0; j < kMergeThreads / 64; ++j) M = fmaxf(M, s_red[j]);
     __syncthreads();
 
-    float S = 0.f, acc = 0.f;
+    float S = 0.f, acc[4] = {0.f, 0.f, 0.f, 0.f};
     if (M != -INFINITY) {
         for (int t0 = 0; t0 < n_seg; t0 += kMergeTile) {
             const int nt = min(kMergeTile, n_seg - t0);
@@ -53,33 +54,40 @@ __global__ void __launch_bounds__(kMergeThreads) merge_kernel(const float *__res
             }
             __syncthreads();
 #pragma unroll 4
-            for (int j = grp; j < nt; j += kMergeGroups) acc = fmaf(base[(int64_t)(t0 + j) * step + 2 + d], s_wt[j], acc);
+            for (int j = grp; j < nt; j += kMergeGroups) {
+                const float *v = base + (int64_t)(t0 + j) * step + 2 + q;
+                const float wj = s_wt[j];
+#pragma unroll
+                for (int m = 0; m < 4; ++m) acc[m] = fmaf(v[32 * m], wj, acc[m]);
+            }
             __syncthreads();
         }
     }
     // fold S over the block and acc over the groups
     S = wave_sum(S);
     if ((tid & 63) == 0) s_red[tid >> 6] = S;
-    s_acc[grp][d] = acc;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) s_acc[grp][q + 32 * m] = acc[m];
     __syncthreads();
-    if (grp != 0) return;
+    if (tid >= kHeadDim) return;
+    const int d = tid;
     S = 0.f;
 #pragma unroll
     for (int j = 0; j < kMergeThreads / 64; ++j) S += s_red[j];
-    acc = 0.f;
+    float a = 0.f;
 #pragma unroll
-    for (int j = 0; j < kMergeGroups; ++j) acc += s_acc[j][d];
+    for (int j = 0; j < kMergeGroups; ++j) a += s_acc[j][d];
     if (pout) {
-        float *q = pout + row * kPartialStride;
+        float *dst = pout + row * kPartialStride;
         if (d == 0) {
-            q[0] = M;
-            q[1] = S;
+            dst[0] = M;
+            dst[1] = S;
         }
-        q[2 + d] = acc;
+        dst[2 + d] = a;
         return;
     }
     const bool ok = (M != -INFINITY) && (S > 0.f);
-    o[row * kHeadDim + d] = ok ? acc / S : 0.f;
+    o[row * kHeadDim + d] = ok ? a / S : 0.f;
     if (lse && d == 0) lse[row] = ok ? M + logf(S) : -INFINITY;
 }
 
