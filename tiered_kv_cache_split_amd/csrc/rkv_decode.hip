@@ -704,8 +704,8 @@ template <int KT, int VT, int R, int HW>
 hipError_t launch_cell(const SegParams &p, hipStream_t s, int *occupancy) {
     if (occupancy)
         return hipOccupancyMaxActiveBlocksPerMultiprocessor(occupancy, decode_cell_kernel<KT, VT, R, HW>, 64 * HW, 0);
-    hipLaunchKernelGGL((decode_cell_kernel<KT, VT, R, HW>), dim3((unsigned)(p.n_splits * (p.n_head_kv / HW) * p.n_seq)),
-                       dim3(64 * HW), 0, s, p);
+    launch_seg(decode_cell_kernel<KT, VT, R, HW>, dim3((unsigned)(p.n_splits * (p.n_head_kv / HW) * p.n_seq)),
+               dim3(64 * HW), s, p);
     return hipGetLastError();
 }
 
@@ -728,9 +728,9 @@ hipError_t launch_decode_r(const SegParams &p, hipStream_t s, int *occupancy) {
     if (occupancy) return hipErrorInvalidValue;
     const int64_t blocks = (int64_t)p.n_splits * p.n_head_kv * p.n_seq;
     if (p.rows)
-        hipLaunchKernelGGL((decode_seg_kernel<KT, VT, R, true>), dim3((unsigned)blocks), dim3(64 * kWaves), 0, s, p);
+        launch_seg(decode_seg_kernel<KT, VT, R, true>, dim3((unsigned)blocks), dim3(64 * kWaves), s, p);
     else
-        hipLaunchKernelGGL((decode_seg_kernel<KT, VT, R, false>), dim3((unsigned)blocks), dim3(64 * kWaves), 0, s, p);
+        launch_seg(decode_seg_kernel<KT, VT, R, false>, dim3((unsigned)blocks), dim3(64 * kWaves), s, p);
     return hipGetLastError();
 }
 

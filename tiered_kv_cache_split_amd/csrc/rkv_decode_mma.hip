@@ -376,8 +376,8 @@ template <int R, int HW>
 hipError_t launch_mma(const SegParams &p, hipStream_t s, int *occupancy) {
     if (occupancy)
         return hipOccupancyMaxActiveBlocksPerMultiprocessor(occupancy, decode_mma_kernel<R, HW>, 64 * HW, 0);
-    hipLaunchKernelGGL((decode_mma_kernel<R, HW>), dim3((unsigned)(p.n_splits * (p.n_head_kv / HW) * p.n_seq)),
-                       dim3(64 * HW), 0, s, p);
+    launch_seg(decode_mma_kernel<R, HW>, dim3((unsigned)(p.n_splits * (p.n_head_kv / HW) * p.n_seq)), dim3(64 * HW),
+               s, p);
     return hipGetLastError();
 }
 

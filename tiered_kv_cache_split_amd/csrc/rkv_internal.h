@@ -2,6 +2,7 @@
 // (rkv_kernels.hip).  Not part of the public ABI.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -39,7 +40,19 @@ struct SegParams {
     int slot0;         // first partial slot used by this segment
     int64_t n_rows;    // n_head * n_q * n_seq
     int cell_hw;       // > 0: cell-major kernel, cell_hw KV heads (packed per cell) per workgroup
+    // optional: events the segment kernel's own dispatch records at its start and end
+    hipEvent_t ev_start, ev_stop;
 };
+
+// Launch a segment kernel; with timing events set, the dispatch itself records them, so the
+// interval covers the kernel alone.
+template <typename F, typename... Args>
+inline void launch_seg(F kernel, dim3 grid, dim3 block, hipStream_t s, const SegParams &p, Args... args) {
+    if (p.ev_start)
+        hipExtLaunchKernelGGL(kernel, grid, block, 0, s, p.ev_start, p.ev_stop, 0, p, args...);
+    else
+        hipLaunchKernelGGL(kernel, grid, block, 0, s, p, args...);
+}
 
 // KV heads per workgroup of the cell-major vector kernel for these types (0: no instantiation):
 // a workgroup owns that many heads, packed inside each cell, over a cell range.

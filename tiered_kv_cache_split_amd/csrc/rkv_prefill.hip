@@ -453,8 +453,7 @@ hipError_t launch_t(const SegParams &p, hipStream_t s) {
     if (n_tasks <= 0) return hipSuccess;
     if (n_tasks > ((int64_t)1 << 30)) return hipErrorInvalidValue;
     const int64_t per = (n_tasks + 7) / 8;
-    hipLaunchKernelGGL((prefill_seg_kernel<KT, VT>), dim3((unsigned)(8 * per)), dim3(kThreadsP), 0, s, p, q_tiles,
-                       (int)n_tasks);
+    launch_seg(prefill_seg_kernel<KT, VT>, dim3((unsigned)(8 * per)), dim3(kThreadsP), s, p, q_tiles, (int)n_tasks);
     return hipGetLastError();
 }
 

@@ -336,10 +336,11 @@ int run_segment(rkv_ctx *ctx, SegParams base, const Seg &sg, bool mfma, int k_ty
     p.n_splits = pl.n_splits;
     p.cells_per_split = (int)pl.cps;
     const bool timed = ctx->kernel_timing && ctx->n_kernel_timed < (int)ctx->kt0.size();
-    if (timed) RKV_HIP(hipEventRecord(ctx->kt0[ctx->n_kernel_timed], s));
+    p.ev_start = timed ? ctx->kt0[ctx->n_kernel_timed] : nullptr;
+    p.ev_stop = timed ? ctx->kt1[ctx->n_kernel_timed] : nullptr;
     const hipError_t e = mfma ? launch_prefill_segment(p, k_type, v_type, s) : launch_decode_segment(p, k_type, v_type, s);
     if (e != hipSuccess) return hip_fail(e, mfma ? "prefill segment launch" : "decode segment launch");
-    if (timed) RKV_HIP(hipEventRecord(ctx->kt1[ctx->n_kernel_timed++], s));
+    if (timed) ctx->n_kernel_timed++;
     slot += p.n_splits;
     ctx->stats.n_segments += 1;
     return RKV_OK;
