@@ -126,6 +126,10 @@ def setup(num: int, sets: int):
     return st
 
 
+# kernel families reported in the context's stats (enum rkv_kernel_variant)
+DECODE_KERNELS = {0: "decode_seg_kernel", 2: "decode_cell_kernel", 3: "decode_mma_kernel"}
+
+
 def call(ctx, st, i):
     import tiered_kv_cache_split_amd as rkv
     w = st["w"]
@@ -346,14 +350,14 @@ def main():
                            "kernel_ms_per_step": round(kern_total_ms, 4)}
     else:
         name = {2: "decode_seg_q8q4_nkv131072", 4: "decode_seg_rows_f16_pool65536"}.get(args.workload, "")
+        label = DECODE_KERNELS.get(stats.get("kernel_variant"), "decode segment kernel")
         if launches_per_step == 1:
             # one segment launch per step (resident window or pool): bytes of one launch / its time
             achieved = kv_bytes / (kern_ms * 1e-3) / 1e9
-            label = "decode_seg_kernel"
         else:
             # window plus tail tiles: all KV bytes over the step's total segment-kernel time
             achieved = kv_bytes / ((k_ms / args.steps) * 1e-3) / 1e9
-            label = "decode_seg_kernel (all segments of a step)"
+            label += " (all segments of a step)"
         out["roofline"] = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": round(achieved / HBM_PEAK_GBS, 4),
                            "traffic": traffic_from_profiles(name, "decode") if name else None,

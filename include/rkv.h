@@ -89,8 +89,16 @@ typedef struct rkv_stats {
     int32_t lift_mode;        /* enum rkv_lift_mode used for the tail                    */
     int64_t lift_bytes;       /* raw bytes lifted host -> device                         */
     int32_t splits_window;    /* split-K factor used on the window segment               */
-    int32_t kernel_variant;   /* 0 = vector decode kernel, 1 = MFMA prefill kernel        */
+    int32_t kernel_variant;   /* enum rkv_kernel_variant of the last segment launched    */
 } rkv_stats;
+
+/* Segment kernel families (rkv_stats.kernel_variant). */
+enum rkv_kernel_variant {
+    RKV_KERNEL_DECODE_HEAD = 0,       /* vector decode, one KV head per workgroup (any layout, rows) */
+    RKV_KERNEL_PREFILL_MFMA = 1,      /* matrix-core prefill over 256-row query tiles                */
+    RKV_KERNEL_DECODE_CELL = 2,       /* vector decode over cell-major groups of KV heads           */
+    RKV_KERNEL_DECODE_CELL_MFMA = 3   /* matrix-core decode over eight cell-major KV heads          */
+};
 
 /* ---- context ---------------------------------------------------------------------- */
 

@@ -231,6 +231,7 @@ def test_mma_decode_row_counts(run, n_head, n_q):
     w = gen.make_workload(2, scale_down=32, n_head=n_head, n_q=n_q)  # n_kv 4096, 8 KV heads
     step(f"decode q8q4 8 kv heads n_head={n_head} n_q={n_q} wc=2500 tile=900")
     O, L = run.decode(w, wc=2500, tile_kv=900, tail="host")
+    assert run.ctx.stats()["kernel_variant"] == 3  # every row count here is at most 8 per KV head
     Oref, Lref = oracle_decode(w)
     assert_close(O, L, Oref, Lref, what=f"mma rows {n_head}x{n_q}")
 
@@ -277,6 +278,7 @@ def test_full_size_config2_sampled_heads(run):
     w = gen.make_workload(2)
     step("decode full size config 2")
     O, L = run.decode(w, wc=w["n_kv"], tail=None)
+    assert run.ctx.stats()["kernel_variant"] == 3  # the matrix-core cell-major kernel
     gqa = w["n_head"] // w["n_head_kv"]
     for g, (Oref, Lref) in oracle_decode(w, heads=[0, 3, 7]).items():
         assert_close(O[:, g * gqa:(g + 1) * gqa], L[:, g * gqa:(g + 1) * gqa], Oref, Lref, what=f"config 2 head {g}")

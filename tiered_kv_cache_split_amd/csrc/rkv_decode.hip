@@ -19,6 +19,7 @@
 // Two kernels share this per-wave routine: a per-head kernel for any layout and for
 // gathered rows, and a cell-major kernel in which a workgroup owns all KV heads of a cell
 // range and reads every chunk as one contiguous span (the cache layout of the pages).
+#include "rkv.h"
 #include "rkv_internal.h"
 #include "rkv_quant.h"
 #include "rkv_wave.h"
@@ -775,6 +776,14 @@ int cell_blocks_per_cu(const SegParams &p, int k_type, int v_type) {
     int n = 0;
     if (p.cell_hw <= 0 || dispatch_decode(p, k_type, v_type, nullptr, &n) != hipSuccess || n < 1) return 1;
     return n;
+}
+
+int decode_kernel_variant(const SegParams &p, int k_type, int v_type) {
+    if (p.cell_hw <= 0) return RKV_KERNEL_DECODE_HEAD;
+#ifndef RKV_DECODE_VALU_CELL
+    if (k_type == T_Q8_0 && v_type == T_Q4_0 && decode_mma_ok(p)) return RKV_KERNEL_DECODE_CELL_MFMA;
+#endif
+    return RKV_KERNEL_DECODE_CELL;
 }
 
 hipError_t launch_decode_segment(const SegParams &p, int k_type, int v_type, hipStream_t s) {

@@ -18,9 +18,11 @@
 //        the value, 1024 for the encoding) at the end.
 //
 // Workgroup = HW (8) waves for one (split, head group, sequence), wave w = KV head g0 + w, as in
-// the vector cell-major kernel: every 64-cell chunk is one contiguous span fetched with 16-byte
-// buffer loads one chunk ahead and staged in LDS; the online softmax is exact (the running max
-// is raised whenever a tile exceeds it) so the binary16 weights stay within range.
+// the vector cell-major kernel.  A 32-cell chunk is one contiguous span of each cache, moved
+// with 16-byte buffer loads into registers and from there into one of two LDS stages; two
+// chunks are always in flight in registers, so one barrier per chunk separates the stage being
+// computed from the one being filled and the loads never pause.  The online softmax is exact
+// (the running max is raised whenever a chunk exceeds it) so the binary16 weights stay in range.
 #include "rkv_internal.h"
 #include "rkv_quant.h"
 #include "rkv_wave.h"
@@ -35,7 +37,7 @@ typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kCh = 64;              // cells per chunk
+constexpr int kCh = 32;              // cells per chunk
 constexpr float kMagicK = 1152.0f;   // q8_0 code q as binary16 1024 + (q + 128)
 constexpr float kMagicV = 1032.0f;   // q4_0 nibble n (value n - 8) as binary16 1024 + n
 
@@ -59,24 +61,45 @@ __device__ __forceinline__ float row16_sum(float x) {
     return x;
 }
 
+// Max of lane k over the four 16-lane rows, in every row.
+__device__ __forceinline__ float fold_rows_max(float x) {
+    const int xi = __builtin_bit_cast(int, x);
+    const auto r16 = __builtin_amdgcn_permlane16_swap(xi, xi, false, false);
+    x = fmaxf(__builtin_bit_cast(float, (int)r16[0]), __builtin_bit_cast(float, (int)r16[1]));
+    const int yi = __builtin_bit_cast(int, x);
+    const auto r32 = __builtin_amdgcn_permlane32_swap(yi, yi, false, false);
+    return fmaxf(__builtin_bit_cast(float, (int)r32[0]), __builtin_bit_cast(float, (int)r32[1]));
+}
+
 __device__ __forceinline__ void lds_order() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+template <int HW>
+struct Stage {
+    static constexpr int kNT = 64 * HW;
+    static constexpr int kTpc = kNT / kCh;                    // threads per cell
+    static constexpr int kUk = HW * kQ8Row / 16, kUv = HW * kQ4Row / 16;  // 16-byte units per cell
+    static constexpr int kMk = (kUk + kTpc - 1) / kTpc, kMv = (kUv + kTpc - 1) / kTpc;
+    uint4 k[kMk], v[kMv];
+};
+
 template <int R, int HW>
 __global__ void __launch_bounds__(64 * HW) __attribute__((amdgpu_waves_per_eu(2)))
 decode_mma_kernel(const SegParams p) {
+    using St = Stage<HW>;
     constexpr int kCk = HW * kQ8Row, kCv = HW * kQ4Row;     // bytes of one cell (head group)
     constexpr int kSk = kCk + 8, kSv = kCv + 8;               // LDS cell strides
-    constexpr int kNT = 64 * HW;
-    static_assert(kCk % 16 == 0 && kCv % 16 == 0, "cell segments must be whole 16-byte units");
-    __shared__ __attribute__((aligned(16))) uint8_t s_k[kCh * kSk];
-    __shared__ __attribute__((aligned(16))) uint8_t s_v[kCh * kSv];
-    __shared__ __attribute__((aligned(16))) _Float16 s_p[HW][16 * kCh];  // P[row][key] per wave
-    __shared__ __attribute__((aligned(16))) _Float16 s_dv[HW][4 * kCh];  // d_V[block][key] per wave
-    __shared__ float s_ml[HW][2][16];                                     // per-row exchange
+    constexpr int kBk = kCh * kSk, kBv = kCh * kSv;           // bytes of one LDS stage
+    constexpr int kTpc = St::kTpc;
+    static_assert(St::kNT % kCh == 0 && kCk % 16 == 0 && kCv % 16 == 0, "thread mapping");
+    static_assert(kCh == 32, "the key permutation of P.V assumes 32-key chunks");
+    __shared__ __attribute__((aligned(16))) uint8_t s_k[2 * kBk];
+    __shared__ __attribute__((aligned(16))) uint8_t s_v[2 * kBv];
+    __shared__ __attribute__((aligned(16))) _Float16 s_dk[HW][4 * kCh];  // d_K[block][key] per wave
+    __shared__ __attribute__((aligned(16))) _Float16 s_dv[HW][4 * kCh];  // d_V[block][slot(key)] per wave
 
     const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int col = lane & 15, grp = lane >> 4;
@@ -92,129 +115,118 @@ decode_mma_kernel(const SegParams p) {
     const uint8_t *kbase = p.k + (int64_t)(hgrp * HW) * p.k_s2;
     const uint8_t *vbase = p.v + (int64_t)(hgrp * HW) * p.v_s2;
 
-    // ---- chunk fetch (registers, one chunk ahead) and staging (LDS, padded cells).  Thread t
-    // moves 16-byte units sub, sub + 8, ... of cell t / 8 (sub = t % 8): eight threads cover
-    // 128 contiguous bytes of a cell per instruction, and every offset is a per-thread base plus
-    // an immediate.
-    static_assert(kNT == 8 * kCh || kNT < 8 * kCh, "thread mapping");
-    constexpr int kCells = kNT / 8;                       // cells per pass
-    constexpr int kPass = kCh / kCells;                   // passes per chunk
-    constexpr int kUkc = kCk / 16, kUvc = kCv / 16;       // units per cell
-    constexpr int kMk = (kUkc + 7) / 8, kMv = (kUvc + 7) / 8;
-    const int fcell = tid >> 3, fsub = tid & 7;
+    // ---- chunk fetch (registers) and staging (LDS, padded cells).  Thread t moves the 16-byte
+    // units sub, sub + kTpc, ... of cell t / kTpc (sub = t % kTpc), so consecutive threads cover
+    // contiguous bytes of a cell and every offset is a per-thread base plus an immediate.  Cells
+    // past the segment end lie outside the buffer resource's range and read as zero.
+    const int fcell = tid / kTpc, fsub = tid % kTpc;
     const int gkb = fcell * (int)p.k_s1 + 16 * fsub, gvb = fcell * (int)p.v_s1 + 16 * fsub;
     const int lkb = fcell * kSk + 16 * fsub, lvb = fcell * kSv + 16 * fsub;
-    uint4 kb[kPass][kMk], vb[kPass][kMv];
-    auto fetch = [&](int64_t c0) {
+    auto fetch = [&](St &st, int64_t c0) __attribute__((always_inline)) {
         const int64_t nv = max((int64_t)0, min((int64_t)kCh, c_end - c0));
         const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
             (void *)(kbase + c0 * p.k_s1), (short)0, (int)(nv * p.k_s1), 0x00020000);
         const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
             (void *)(vbase + c0 * p.v_s1), (short)0, (int)(nv * p.v_s1), 0x00020000);
 #pragma unroll
-        for (int ps = 0; ps < kPass; ++ps) {
-            const int so_k = ps * kCells * (int)p.k_s1, so_v = ps * kCells * (int)p.v_s1;
+        for (int m = 0; m < St::kMk; ++m)
+            if (kTpc * (m + 1) <= St::kUk || fsub + kTpc * m < St::kUk)
+                st.k[m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, gkb + 16 * kTpc * m, 0, 0));
 #pragma unroll
-            for (int m = 0; m < kMk; ++m)
-                if (8 * m + 8 <= kUkc || fsub + 8 * m < kUkc)
-                    kb[ps][m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, gkb + 128 * m, so_k, 0));
-#pragma unroll
-            for (int m = 0; m < kMv; ++m)
-                if (8 * m + 8 <= kUvc || fsub + 8 * m < kUvc)
-                    vb[ps][m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, gvb + 128 * m, so_v, 0));
-        }
+        for (int m = 0; m < St::kMv; ++m)
+            if (kTpc * (m + 1) <= St::kUv || fsub + kTpc * m < St::kUv)
+                st.v[m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, gvb + 16 * kTpc * m, 0, 0));
     };
-    auto stash = [&]() {
+    auto stash = [&](const St &st, int buf) __attribute__((always_inline)) {
 #pragma unroll
-        for (int ps = 0; ps < kPass; ++ps) {
+        for (int m = 0; m < St::kMk; ++m)
+            if (kTpc * (m + 1) <= St::kUk || fsub + kTpc * m < St::kUk) {
+                uint2 *d = reinterpret_cast<uint2 *>(s_k + buf * kBk + lkb + 16 * kTpc * m);
+                d[0] = make_uint2(st.k[m].x, st.k[m].y);
+                d[1] = make_uint2(st.k[m].z, st.k[m].w);
+            }
 #pragma unroll
-            for (int m = 0; m < kMk; ++m)
-                if (8 * m + 8 <= kUkc || fsub + 8 * m < kUkc) {
-                    uint2 *d = reinterpret_cast<uint2 *>(s_k + lkb + ps * kCells * kSk + 128 * m);
-                    d[0] = make_uint2(kb[ps][m].x, kb[ps][m].y);
-                    d[1] = make_uint2(kb[ps][m].z, kb[ps][m].w);
-                }
-#pragma unroll
-            for (int m = 0; m < kMv; ++m)
-                if (8 * m + 8 <= kUvc || fsub + 8 * m < kUvc) {
-                    uint2 *d = reinterpret_cast<uint2 *>(s_v + lvb + ps * kCells * kSv + 128 * m);
-                    d[0] = make_uint2(vb[ps][m].x, vb[ps][m].y);
-                    d[1] = make_uint2(vb[ps][m].z, vb[ps][m].w);
-                }
-        }
+        for (int m = 0; m < St::kMv; ++m)
+            if (kTpc * (m + 1) <= St::kUv || fsub + kTpc * m < St::kUv) {
+                uint2 *d = reinterpret_cast<uint2 *>(s_v + buf * kBv + lvb + 16 * kTpc * m);
+                d[0] = make_uint2(st.v[m].x, st.v[m].y);
+                d[1] = make_uint2(st.v[m].z, st.v[m].w);
+            }
     };
 
-    float4_t oacc[8];   // O^T: head_dim 16*dt + 4*grp + i of row `col`
-    float swacc[4];     // this lane's part (its 8 keys per step) of the weight sum of V block blk, row `col`
-    float mrow[4], lrow[4];  // softmax layout: rows 4*grp + i
+    // Lane (col, grp) owns query row `col` (rows >= R are padding and never written) and, within
+    // a chunk, the keys 16*kt + 4*grp + ii (kt, ii < 2, 4): the Q.K output layout.  Its P.V
+    // accumulators hold O^T[d][col] for d = 16*dt + 4*grp + e, so the softmax state of a row lives
+    // in the four lanes col, col + 16, col + 32, col + 48 and never crosses LDS.
+    float4_t oacc[8];
+    float swacc[4];        // sum of the weights W of this lane's keys, per V block
+    float mrow = -INFINITY, lrow = 0.f;  // running max (log2 domain) and this lane's part of the sum
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) oacc[dt] = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int blk = 0; blk < 4; ++blk) swacc[blk] = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        mrow[i] = -INFINITY;
-        lrow[i] = 0.f;
-    }
     const half2_t ones = {(_Float16)1.0f, (_Float16)1.0f};
     // kept in a register so that mask-and-insert compiles to one v_and_or_b32 (two literals
     // cannot share an instruction)
     uint32_t vmagic = 0x64006400u;
     asm volatile("" : "+v"(vmagic));
     const float c = p.scale_log2;
-    const uint8_t *kw = s_k + wave * kQ8Row;  // this head's K row of cell j at kw + j*kSk
-    const uint8_t *vw = s_v + wave * kQ4Row;
-    _Float16 *pw = s_p[wave];
+    _Float16 *dkw = s_dk[wave];
     _Float16 *dvw = s_dv[wave];
-
     const int64_t n_ch = (c_end > c_beg) ? (c_end - c_beg + kCh - 1) / kCh : 0;
-    if (n_ch > 0) fetch(c_beg);  // the first chunk is in flight while Q is prepared
+    const int qi_row = min(col, R - 1) / p.gqa;  // query position of this lane's row
 
-    // ---- Q as the A operand of Q.K: lane holds row `col`, head_dim 32*blk + 8*grp + 0..7
-    half8_t qa[4];
-    float4_t cneg[4];  // accumulator inputs: -1152 * block sum of Q for the rows 4*grp + i
+    // ---- Q^T as the B operand of Q.K: lane holds row `col`, head_dim 32*blk + 8*grp + 0..7.  Its
+    // loads are issued before the first two chunks' so that waiting for them waits for Q only.
+    half8_t qb[4];
+    float4_t cneg[4];  // accumulator inputs: -1152 * block sum of row `col` of Q
+    St sa, sb;         // chunks 2i (sa) and 2i + 1 (sb) of the split
     {
         const bool ok = col < R;
         const int r = ok ? col : 0;
         const _Float16 *qrow = p.q + (int64_t)(r / p.gqa) * p.q_s1 + (int64_t)(g * p.gqa + r % p.gqa) * p.q_s2 +
                                (int64_t)b * p.q_s3;
-        float qs[4];
+        uint4 qv[4];
+#pragma unroll
+        for (int blk = 0; blk < 4; ++blk) qv[blk] = *reinterpret_cast<const uint4 *>(qrow + 32 * blk + 8 * grp);
+        fetch(sa, c_beg);
+        fetch(sb, c_beg + kCh);
 #pragma unroll
         for (int blk = 0; blk < 4; ++blk) {
-            const uint32_t *src = reinterpret_cast<const uint32_t *>(qrow + 32 * blk + 8 * grp);
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (ok) v = make_uint4(src[0], src[1], src[2], src[3]);
-            qa[blk] = __builtin_bit_cast(half8_t, v);
+            qb[blk] = __builtin_bit_cast(half8_t, ok ? qv[blk] : make_uint4(0, 0, 0, 0));
             float sum = 0.f;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) sum += (float)qa[blk][j];
-            qs[blk] = fold_rows(sum);  // block sum of row `col`, in every lane of the column
+            for (int j = 0; j < 8; ++j) sum += (float)qb[blk][j];
+            const float cb = -kMagicK * fold_rows(sum);  // block sum of row `col`, in every lane of the column
+            cneg[blk] = float4_t{cb, cb, cb, cb};
         }
-#pragma unroll
-        for (int blk = 0; blk < 4; ++blk)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) cneg[blk][i] = -kMagicK * __shfl(qs[blk], 4 * grp + i, 64);
     }
 
-    for (int64_t ch = 0; ch < n_ch; ++ch) {
-        const int64_t c0 = c_beg + ch * kCh;
-        __syncthreads();  // every wave is done with the previous chunk's LDS
-        stash();
-        __syncthreads();
-        fetch(c0 + kCh);  // past c_end nothing is read
+    // ---- one chunk from LDS stage `buf`
+    auto compute = [&](int buf, int64_t c0) __attribute__((always_inline)) {
+        const uint8_t *kw = s_k + buf * kBk + wave * kQ8Row;  // this head's K row of cell j at kw + j*kSk
+        const uint8_t *vw = s_v + buf * kBv + wave * kQ4Row;
 
-        // V block scales of the chunk, [block][key], lane = key
+        // block scales of the chunk: d_K as [block][key], d_V as [block][slot] with the key of P.V
+        // slot 8*gg + jj being 4*gg + jj (jj < 4) or 16 + 4*gg + jj - 4; lane = key (lane % 32),
+        // blocks 2 (lane / 32) + 0, 1
+        {
+            const int key = lane & (kCh - 1), bb = 2 * (lane / kCh);
+            const int slot = 8 * ((key >> 2) & 3) + 4 * (key >> 4) + (key & 3);
 #pragma unroll
-        for (int blk = 0; blk < 4; ++blk)
-            dvw[blk * kCh + lane] = __builtin_bit_cast(_Float16, (uint16_t)ld_u16(vw + lane * kSv + kQ4Block * blk));
+            for (int u = 0; u < 2; ++u) {
+                dkw[(bb + u) * kCh + key] = __builtin_bit_cast(_Float16, (uint16_t)ld_u16(kw + key * kSk + kQ8Block * (bb + u)));
+                dvw[(bb + u) * kCh + slot] = __builtin_bit_cast(_Float16, (uint16_t)ld_u16(vw + key * kSv + kQ4Block * (bb + u)));
+            }
+        }
 
-        // ---- Q.K: s[kt][i] = score of key 16*kt + col for row 4*grp + i
-        float s[4][4];
+        // ---- Q.K on the matrix cores: A = K (16 keys x 32 head_dim of one q8_0 block, codes as
+        // binary16 1024 + (q + 128)), B = Q^T; d[ii] = score of key 16*kt + 4*grp + ii for row col
+        // before the block scale
+        float4_t dq[2][4];
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
+        for (int kt = 0; kt < 2; ++kt) {
             const uint8_t *kr = kw + (16 * kt + col) * kSk;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) s[kt][i] = 0.f;
 #pragma unroll
             for (int blk = 0; blk < 4; ++blk) {
                 const int o = kQ8Block * blk + 2 + 8 * grp;  // codes 8*grp .. 8*grp+7 of the block
@@ -231,15 +243,30 @@ decode_mma_kernel(const SegParams p) {
                 }
                 w0 ^= 0x80808080u;  // q + 128 per byte
                 w1 ^= 0x80808080u;
-                const uint4 bk = make_uint4(__builtin_amdgcn_perm(0x64646464u, w0, 0x05010400u),
+                const uint4 ak = make_uint4(__builtin_amdgcn_perm(0x64646464u, w0, 0x05010400u),
                                             __builtin_amdgcn_perm(0x64646464u, w0, 0x05030402u),
                                             __builtin_amdgcn_perm(0x64646464u, w1, 0x05010400u),
                                             __builtin_amdgcn_perm(0x64646464u, w1, 0x05030402u));
-                const float4_t d = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[blk], __builtin_bit_cast(half8_t, bk),
-                                                                          cneg[blk], 0, 0, 0);
-                const float dk = h2f(ld_u16(kr + kQ8Block * blk));
+                dq[kt][blk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, ak), qb[blk],
+                                                                     cneg[blk], 0, 0, 0);
+            }
+        }
+        lds_order();  // the block scales are in place
+
+        // scores s[kt][ii] = sum over blocks of d_K * d
+        float s[2][4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) s[kt][i] = fmaf(dk, d[i], s[kt][i]);
+        for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) s[kt][ii] = 0.f;
+#pragma unroll
+            for (int blk = 0; blk < 4; ++blk) {
+                const uint2 dk2 = *reinterpret_cast<const uint2 *>(dkw + blk * kCh + 16 * kt + 4 * grp);
+                const half2_t d01 = h2v(dk2.x), d23 = h2v(dk2.y);
+                s[kt][0] = fmaf((float)d01[0], dq[kt][blk][0], s[kt][0]);
+                s[kt][1] = fmaf((float)d01[1], dq[kt][blk][1], s[kt][1]);
+                s[kt][2] = fmaf((float)d23[0], dq[kt][blk][2], s[kt][2]);
+                s[kt][3] = fmaf((float)d23[1], dq[kt][blk][3], s[kt][3]);
             }
         }
 
@@ -247,122 +274,115 @@ decode_mma_kernel(const SegParams p) {
         const bool full = (c0 + kCh <= c_end) && !p.mask && (p.q_pos0 < 0 || p.pos0 + c0 + kCh - 1 <= p.q_pos0);
         float cc = c;
         if (!full) {
+            // in chunk-relative 32-bit terms: keys below n_in exist, keys up to lim are not after
+            // the query (causal rule); mask reads clamp to the segment's last key
+            const int n_in = (int)min((int64_t)kCh, c_end - c0);
+            const int lim = p.q_pos0 < 0 ? kCh
+                                         : (int)max((int64_t)-1, min((int64_t)kCh, p.q_pos0 + qi_row - p.pos0 - c0));
+            const _Float16 *mr = p.mask ? p.mask + p.pos0 + (int64_t)b * p.m_s3 + (int64_t)qi_row * p.m_s1 : nullptr;
 #pragma unroll
-            for (int kt = 0; kt < 4; ++kt) {
+            for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = min(4 * grp + i, R - 1);
-                    const int qi = r / p.gqa;
-                    const int64_t key = c0 + 16 * kt + col;
-                    bool vis = key < c_end;
-                    if (p.q_pos0 >= 0 && p.pos0 + key > p.q_pos0 + qi) vis = false;
-                    float x = s[kt][i] * c;
-                    if (vis && p.mask)
-                        x = fmaf((float)p.mask[p.pos0 + key + (int64_t)qi * p.m_s1 + (int64_t)b * p.m_s3], kLog2e, x);
-                    s[kt][i] = vis ? x : -INFINITY;
+                for (int ii = 0; ii < 4; ++ii) {
+                    const int kr = 16 * kt + 4 * grp + ii;
+                    const bool vis = kr < n_in && kr <= lim;
+                    float x = s[kt][ii] * c;
+                    if (mr) x = fmaf((float)mr[min(c0 + kr, c_end - 1)], kLog2e, x);
+                    s[kt][ii] = vis ? x : -INFINITY;
                 }
             }
             cc = 1.0f;
         }
 
-        // ---- online softmax per row (exact: the max is raised whenever a chunk exceeds it)
-        float mt[4];
-        bool need = false;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float mx;
-            if (cc >= 0.f)
-                mx = fmaxf(fmaxf(s[0][i], s[1][i]), fmaxf(s[2][i], s[3][i]));
-            else
-                mx = fmaxf(fmaxf(-s[0][i], -s[1][i]), fmaxf(-s[2][i], -s[3][i]));
-            mt[i] = row16_max(mx) * (cc >= 0.f ? cc : -cc);
-            need = need || (mt[i] > mrow[i]);
-        }
-        if (__builtin_amdgcn_ballot_w64(need)) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const bool up = mt[i] > mrow[i];
-                const float mnew = up ? mt[i] : mrow[i];
-                const float alpha = up ? __builtin_amdgcn_exp2f(mrow[i] - mnew) : 1.0f;
-                lrow[i] *= alpha;
-                mrow[i] = mnew;
-                if (col == 0) s_ml[wave][0][4 * grp + i] = alpha;
-            }
-            lds_order();
-            // the P.V accumulators of this lane belong to row `col`
-            const float a = s_ml[wave][0][col];
+        // ---- online softmax of row `col` (exact: the max is raised whenever a chunk exceeds it)
+        float mx;
+        if (cc >= 0.f)
+            mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                       fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+        else
+            mx = -fminf(fminf(fminf(s[0][0], s[0][1]), fminf(s[0][2], s[0][3])),
+                        fminf(fminf(s[1][0], s[1][1]), fminf(s[1][2], s[1][3])));
+        const float mt = fold_rows_max(mx) * (cc >= 0.f ? cc : -cc);
+        if (__builtin_amdgcn_ballot_w64(mt > mrow)) {
+            const float mnew = fmaxf(mt, mrow);
+            const float a = (mnew > mrow) ? __builtin_amdgcn_exp2f(mrow - mnew) : 1.0f;
+            mrow = mnew;
+            lrow *= a;
 #pragma unroll
             for (int dt = 0; dt < 8; ++dt) oacc[dt] *= a;
 #pragma unroll
             for (int blk = 0; blk < 4; ++blk) swacc[blk] *= a;
         }
+        const float msub = mrow == -INFINITY ? 0.f : mrow;
+        half2_t pk[4];  // P of P.V slots 8*grp + 2u, 2u + 1 (keys 16*(u/2) + 4*grp + 2*(u%2) + 0, 1)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float msub = mrow[i] == -INFINITY ? 0.f : mrow[i];
-#pragma unroll
-            for (int kt = 0; kt < 4; ++kt) {
-                const float pv = __builtin_amdgcn_exp2f(fmaf(s[kt][i], cc, -msub));
-                lrow[i] += pv;
-                pw[(4 * grp + i) * kCh + 16 * kt + col] = (_Float16)pv;
-            }
+        for (int u = 0; u < 4; ++u) {
+            const float p0 = __builtin_amdgcn_exp2f(fmaf(s[u >> 1][2 * (u & 1)], cc, -msub));
+            const float p1 = __builtin_amdgcn_exp2f(fmaf(s[u >> 1][2 * (u & 1) + 1], cc, -msub));
+            lrow += p0 + p1;
+            pk[u] = half2_t{(_Float16)p0, (_Float16)p1};
         }
-        lds_order();
 
-        // ---- P.V: per 32-key step and V block, weights W = p * d_V, then the two nibble tiles
+        // ---- P.V over the chunk's 32 keys, per V block: B = W^T with W = p * d_V in the slot
+        // order above, A = V^T gathered from the staged raw bytes in the same order (byte `col`
+        // of the block: element col as the low nibble, element col + 16 as the high one)
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const uint4 pf = *reinterpret_cast<const uint4 *>(pw + col * kCh + 32 * ks + 8 * grp);
+        for (int blk = 0; blk < 4; ++blk) {
+            const uint4 dv = *reinterpret_cast<const uint4 *>(dvw + blk * kCh + 8 * grp);
+            const uint4 wu = make_uint4(u32v(pk[0] * h2v(dv.x)), u32v(pk[1] * h2v(dv.y)),
+                                        u32v(pk[2] * h2v(dv.z)), u32v(pk[3] * h2v(dv.w)));
+            const half8_t wf = __builtin_bit_cast(half8_t, wu);
+            swacc[blk] = __builtin_amdgcn_fdot2(h2v(wu.x), ones, swacc[blk], false);
+            swacc[blk] = __builtin_amdgcn_fdot2(h2v(wu.y), ones, swacc[blk], false);
+            swacc[blk] = __builtin_amdgcn_fdot2(h2v(wu.z), ones, swacc[blk], false);
+            swacc[blk] = __builtin_amdgcn_fdot2(h2v(wu.w), ones, swacc[blk], false);
+            const uint8_t *vb0 = vw + (4 * grp) * kSv + kQ4Block * blk + 2 + col;
+            uint32_t bt[8];
 #pragma unroll
-            for (int blk = 0; blk < 4; ++blk) {
-                const uint4 dv = *reinterpret_cast<const uint4 *>(dvw + blk * kCh + 32 * ks + 8 * grp);
-                const uint4 wu = make_uint4(u32v(h2v(pf.x) * h2v(dv.x)), u32v(h2v(pf.y) * h2v(dv.y)),
-                                            u32v(h2v(pf.z) * h2v(dv.z)), u32v(h2v(pf.w) * h2v(dv.w)));
-                const half8_t wf = __builtin_bit_cast(half8_t, wu);
-                swacc[blk] = __builtin_amdgcn_fdot2(h2v(wu.x), ones, swacc[blk], false);
-                swacc[blk] = __builtin_amdgcn_fdot2(h2v(wu.y), ones, swacc[blk], false);
-                swacc[blk] = __builtin_amdgcn_fdot2(h2v(wu.z), ones, swacc[blk], false);
-                swacc[blk] = __builtin_amdgcn_fdot2(h2v(wu.w), ones, swacc[blk], false);
-                // byte `col` of block blk for keys 32*ks + 8*grp + j: element col (low nibble)
-                // and element col + 16 (high nibble)
-                const uint8_t *vb0 = vw + (32 * ks + 8 * grp) * kSv + kQ4Block * blk + 2 + col;
-                uint32_t bt[8];
+            for (int j = 0; j < 8; ++j) bt[j] = vb0[((j & 3) + 16 * (j >> 2)) * kSv];
+            uint32_t lo[4], hi[4];
 #pragma unroll
-                for (int j = 0; j < 8; ++j) bt[j] = vb0[j * kSv];
-                uint32_t lo[4], hi[4];
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    const uint32_t y = __builtin_amdgcn_perm(bt[2 * jj + 1], bt[2 * jj], 0x0C040C00u);  // b0, 0, b1, 0
-                    lo[jj] = (y & 0x000F000Fu) | vmagic;
-                    hi[jj] = ((y >> 4) & 0x000F000Fu) | vmagic;
-                }
-                oacc[2 * blk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                    __builtin_bit_cast(half8_t, make_uint4(lo[0], lo[1], lo[2], lo[3])), wf, oacc[2 * blk], 0, 0, 0);
-                oacc[2 * blk + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                    __builtin_bit_cast(half8_t, make_uint4(hi[0], hi[1], hi[2], hi[3])), wf, oacc[2 * blk + 1], 0, 0, 0);
+            for (int jj = 0; jj < 4; ++jj) {
+                const uint32_t y = __builtin_amdgcn_perm(bt[2 * jj + 1], bt[2 * jj], 0x0C040C00u);  // b0, 0, b1, 0
+                lo[jj] = (y & 0x000F000Fu) | vmagic;
+                hi[jj] = ((y >> 4) & 0x000F000Fu) | vmagic;
             }
+            oacc[2 * blk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                __builtin_bit_cast(half8_t, make_uint4(lo[0], lo[1], lo[2], lo[3])), wf, oacc[2 * blk], 0, 0, 0);
+            oacc[2 * blk + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                __builtin_bit_cast(half8_t, make_uint4(hi[0], hi[1], hi[2], hi[3])), wf, oacc[2 * blk + 1], 0, 0, 0);
         }
+    };
+
+    // ---- pipeline: chunk ch is computed from stage ch % 2 while chunks ch + 2 and ch + 3 are
+    // in flight in registers; the barrier before a stash orders it after every wave's reads of
+    // that stage (two chunks earlier) and the previous stash before this chunk's reads.  Loads
+    // past the segment end read nothing.  Chunks go in pairs with no exit in between (a chunk
+    // past the end has no visible key and adds nothing), so that every path into the loop
+    // head has the same loads in flight and the waits before a stash cover one chunk only.
+    stash(sa, 0);
+    fetch(sa, c_beg + 2 * kCh);
+    for (int64_t ch = 0; ch < n_ch; ch += 2) {
+        __syncthreads();
+        stash(sb, 1);
+        fetch(sb, c_beg + (ch + 3) * kCh);
+        compute(0, c_beg + ch * kCh);
+        __syncthreads();
+        stash(sa, 0);
+        fetch(sa, c_beg + (ch + 4) * kCh);
+        compute(1, c_beg + (ch + 1) * kCh);
     }
 
-    // ---- partial of row `col`: gather its max and sum from the softmax layout; the weight sums
-    // are folded over the four lane groups (each holds 8 of every 32 keys)
+    // ---- partial of row `col`: the sums are folded over the four lanes of the row
+    const float S = fold_rows(lrow);
 #pragma unroll
     for (int blk = 0; blk < 4; ++blk) swacc[blk] = fold_rows(swacc[blk]);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        lrow[i] = row16_sum(lrow[i]);
-        if (col == 0) {
-            s_ml[wave][0][4 * grp + i] = mrow[i];
-            s_ml[wave][1][4 * grp + i] = lrow[i];
-        }
-    }
-    lds_order();
     if (col < R) {
-        const float M = s_ml[wave][0][col], S = s_ml[wave][1][col];
         const int r = col % p.gqa, i = col / p.gqa;
         const int64_t row = (g * p.gqa + r) + (int64_t)p.n_head * (i + (int64_t)p.n_q * b);
         float *out = p.partials + ((int64_t)(p.slot0 + split) * p.n_rows + row) * kPartialStride;
         if (grp == 0) {
-            out[0] = (M == -INFINITY) ? -INFINITY : M * kLn2;
+            out[0] = (mrow == -INFINITY) ? -INFINITY : mrow * kLn2;
             out[1] = S;
         }
 #pragma unroll

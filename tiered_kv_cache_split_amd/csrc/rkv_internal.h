@@ -61,6 +61,8 @@ int cell_heads(int k_type, int v_type, int n_head_kv, int R, bool rows);
 int cell_blocks_per_cu(const SegParams &p, int k_type, int v_type);
 
 // Launches; every function returns a hipError_t and checks nothing the host has not.
+// Which decode kernel launch_decode_segment will run for p (enum rkv_kernel_variant).
+int decode_kernel_variant(const SegParams &p, int k_type, int v_type);
 hipError_t launch_decode_segment(const SegParams &p, int k_type, int v_type, hipStream_t s);
 // Matrix-core decode kernel for cell-major q8_0 K / q4_0 V with 8 KV heads per workgroup
 // (decode_mma_ok); with `occupancy` set it reports resident workgroups per CU instead of

@@ -341,6 +341,7 @@ int run_segment(rkv_ctx *ctx, SegParams base, const Seg &sg, bool mfma, int k_ty
     const hipError_t e = mfma ? launch_prefill_segment(p, k_type, v_type, s) : launch_decode_segment(p, k_type, v_type, s);
     if (e != hipSuccess) return hip_fail(e, mfma ? "prefill segment launch" : "decode segment launch");
     if (timed) ctx->n_kernel_timed++;
+    ctx->stats.kernel_variant = mfma ? RKV_KERNEL_PREFILL_MFMA : decode_kernel_variant(p, k_type, v_type);
     slot += p.n_splits;
     ctx->stats.n_segments += 1;
     return RKV_OK;
@@ -504,7 +505,7 @@ int attn_window_tail(rkv_ctx *ctx, const rkv_tensor *q, const rkv_tensor *k_win,
     base.partials = ctx->partials;
 
     ctx->stats = rkv_stats{};
-    ctx->stats.kernel_variant = mfma ? 1 : 0;
+    ctx->stats.kernel_variant = mfma ? RKV_KERNEL_PREFILL_MFMA : RKV_KERNEL_DECODE_HEAD;
     ctx->stats.lift_mode = ctx->lift_mode;
     int slot = 0;
 
@@ -843,7 +844,7 @@ int rkv_attn_partial(rkv_ctx *ctx, const rkv_tensor *q, const rkv_tensor *k, con
     if ((st = ensure_partials(ctx, (int64_t)slots * p.n_rows * kPartialStride, stream))) return st;
     p.partials = ctx->partials;
     ctx->stats = rkv_stats{};
-    ctx->stats.kernel_variant = mfma ? 1 : 0;
+    ctx->stats.kernel_variant = mfma ? RKV_KERNEL_PREFILL_MFMA : RKV_KERNEL_DECODE_HEAD;
     int slot = 0;
     if (k->ne[1] > 0) {
         if ((st = run_segment(ctx, p, sg, mfma, k->type, v->type, slot, stream))) return st;
