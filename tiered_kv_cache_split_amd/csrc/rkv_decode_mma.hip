@@ -6,16 +6,18 @@
 // few query rows (gqa x n_q <= 8) run on v_mfma_f32_16x16x32_f16, which frees the vector
 // units for the dequantisation and the softmax:
 //
-//   Q.K  D[row][key] = Q (A: 16 rows x 32 head_dim, rows >= R zero) times K^T (B: one q8_0
-//        block of 16 keys).  The codes q enter B as exact binary16 integers 1024 + (q + 128)
-//        built by one byte permute; the accumulator input -1152 * (block sum of Q) removes
-//        that offset inside the MFMA, and the block scale d_K is applied per key afterwards.
+//   Q.K  D[key][row] = K (A: 16 keys x 32 head_dim of one q8_0 block) times Q^T (B, rows >= R
+//        zero).  The codes q enter A as exact binary16 integers 1024 + (q + 128) built by one
+//        byte permute; the accumulator input -1152 * (block sum of Q) removes that offset
+//        inside the MFMA, and the block scale d_K is applied per key afterwards.  In this
+//        output layout a lane holds one query row for four keys, so the softmax of a row needs
+//        no LDS round trip and its probabilities are already the B operand of P.V.
 //   P.V  O^T[d][row] = V^T (A: 16 head_dim x 32 keys) times W^T (B: weights of 32 keys) where
 //        W = p * d_V folds the per-key block scale of V into the binary16 weights.  V^T is
 //        gathered from the staged raw bytes: a lane takes one byte position of eight keys,
-//        whose low and high nibbles are the elements e and e + 16 of the block; they enter
-//        as exact 1024 + n, and sum W (kept per V block) removes the offset 1032 (n - 8 for
-//        the value, 1024 for the encoding) at the end.
+//        whose low and high nibbles are the elements e and e + 16 of the block.  The low
+//        nibble enters as exact 1024 + n, the high one in place as 1024 + 16 n; sum W (kept
+//        per V block) removes the offsets 1032 and 1152 at the end (n - 8 is the value).
 //
 // Workgroup = HW (8) waves for one (split, head group, sequence), wave w = KV head g0 + w, as in
 // the vector cell-major kernel.  A 32-cell chunk is one contiguous span of each cache, moved
@@ -39,7 +41,8 @@ typedef float float4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kCh = 32;              // cells per chunk
 constexpr float kMagicK = 1152.0f;   // q8_0 code q as binary16 1024 + (q + 128)
-constexpr float kMagicV = 1032.0f;   // q4_0 nibble n (value n - 8) as binary16 1024 + n
+constexpr float kMagicV = 1032.0f;   // q4_0 low nibble n (value n - 8) as binary16 1024 + n
+constexpr float kMagicVHi = 1152.0f; // q4_0 high nibble n kept in place: binary16 1024 + 16 n = 16 (n - 8) + 1152
 
 __device__ __forceinline__ half2_t h2v(uint32_t x) { return __builtin_bit_cast(half2_t, x); }
 __device__ __forceinline__ uint32_t u32v(half2_t x) { return __builtin_bit_cast(uint32_t, x); }
@@ -344,8 +347,8 @@ decode_mma_kernel(const SegParams p) {
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
                 const uint32_t y = __builtin_amdgcn_perm(bt[2 * jj + 1], bt[2 * jj], 0x0C040C00u);  // b0, 0, b1, 0
-                lo[jj] = (y & 0x000F000Fu) | vmagic;
-                hi[jj] = ((y >> 4) & 0x000F000Fu) | vmagic;
+                lo[jj] = (y & 0x000F000Fu) | vmagic;  // 1024 + n
+                hi[jj] = (y & 0x00F000F0u) | vmagic;  // 1024 + 16 n: no shift needed
             }
             oacc[2 * blk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
                 __builtin_bit_cast(half8_t, make_uint4(lo[0], lo[1], lo[2], lo[3])), wf, oacc[2 * blk], 0, 0, 0);
@@ -385,10 +388,13 @@ decode_mma_kernel(const SegParams p) {
             out[0] = (mrow == -INFINITY) ? -INFINITY : mrow * kLn2;
             out[1] = S;
         }
+        // low nibbles: O = acc - 1032 sum W; high nibbles: O = (acc - 1152 sum W) / 16
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) out[2 + 16 * dt + 4 * grp + e] = fmaf(-kMagicV, swacc[dt >> 1], oacc[dt][e]);
+            for (int e = 0; e < 4; ++e)
+                out[2 + 16 * dt + 4 * grp + e] = (dt & 1) ? fmaf(-kMagicVHi, swacc[dt >> 1], oacc[dt][e]) * 0.0625f
+                                                          : fmaf(-kMagicV, swacc[dt >> 1], oacc[dt][e]);
     }
 }
 
