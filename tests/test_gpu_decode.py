@@ -294,3 +294,43 @@ def test_full_size_config3_sampled_heads(run):
     gqa = w["n_head"] // w["n_head_kv"]
     for g, (Oref, Lref) in oracle_decode(w, heads=[1, 6]).items():
         assert_close(O[:, g * gqa:(g + 1) * gqa], L[:, g * gqa:(g + 1) * gqa], Oref, Lref, what=f"config 3 head {g}")
+
+
+# ---- binary16 matrix-core decode kernel (eight cell-major KV heads per workgroup)
+
+@pytest.mark.parametrize("tail", ["device", "host"])
+def test_f16_matrix_core_window_and_tail(run, tail):
+    w = gen.make_workload(1, n_head=32, n_head_kv=8)  # n_kv 4096, window 2048, tiles 1024
+    rng = np.random.default_rng(31)
+    mask = gen.random_mask_f16(rng, 1, w["n_kv"], p_hidden=0.2)
+    step(f"decode f16 32/8 heads window 2048 + {tail} tail, mask")
+    O, L = run.decode(w, wc=2000, tile_kv=700, tail=tail, mask=mask)
+    assert run.ctx.stats()["kernel_variant"] == 3
+    Oref, Lref = oracle_decode(w, mask=mask)
+    assert_close(O, L, Oref, Lref, what=f"f16 mfma {tail}")
+
+
+def test_f16_matrix_core_partial_causal(run):
+    """attn_partial with the causal rule and gqa 4 x n_q 2 = 8 rows per KV head."""
+    import torch
+    import tiered_kv_cache_split_amd as rkv
+    w = gen.make_workload(1, n_head=32, n_head_kv=8, n_q=2)
+    seg = slice(100, 3000)
+    q_pos0 = 2500
+    step("attn_partial f16 32/8 heads n_q=2 kv_pos0=100 q_pos0=2500")
+    qd = dev(w["q"])
+    kd, vd = dev(w["k"][seg]), dev(w["v"][seg])
+    part = torch.empty((2 * w["n_head"], 130), dtype=torch.float32, device="cuda")
+    run.ctx.attn_partial(rkv.q_desc(qd), rkv.kv_desc(kd, w["k_type"]), rkv.kv_desc(vd, w["v_type"]), None, 100,
+                         q_pos0, w["scale"], part)
+    torch.cuda.synchronize()
+    assert run.ctx.stats()["kernel_variant"] == 3
+    P = part.cpu().numpy().astype(np.float64)
+    qv = oracle.q_values(w["q"])
+    kv = oracle.kv_values(w["k_type"], w["k"][seg])
+    vv = oracle.kv_values(w["v_type"], w["v"][seg])
+    m = oracle.causal_mask(2, 3000, q_pos0)[:, 100:3000]
+    M, S, VKQ = oracle.partial(qv, kv, vv, w["scale"], m)
+    Og, Lg = P[:, 2:] / P[:, 1:2], P[:, 0] + np.log(P[:, 1])
+    Or, Lr = (VKQ / S[..., None]).reshape(-1, 128), (M + np.log(S)).reshape(-1)
+    assert_close(Og, Lg, Or, Lr, what="f16 mfma partial causal")

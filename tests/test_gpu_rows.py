@@ -17,8 +17,48 @@ def test_rows_config4_scaled(run):
     w = gen.make_workload(4, scale_down=16)  # pool 4096, lists 512/768/1280/1920 padded to 1920
     step("rows f16 pool=4096 4 seqs padded, mask given")
     O, L = run.rows(w)
+    assert run.ctx.stats()["kernel_variant"] == 3  # binary16 matrix-core cell-major kernel
     Oref, Lref = oracle_rows(w)
     assert_close(O, L, Oref, Lref, what="rows")
+
+
+@pytest.mark.parametrize("n_head,n_head_kv,n_q", [(64, 8, 1), (32, 8, 2), (8, 8, 1), (48, 16, 1), (16, 8, 3)])
+def test_rows_f16_matrix_core_shapes(run, n_head, n_head_kv, n_q):
+    """Row counts 1..8 per KV head, two head groups, ragged list lengths (not multiples of the
+    16-cell chunk), a random mask with hidden keys, lists overlapping across sequences."""
+    rng = gen.rng_for(43)
+    n_pool = 2000
+    lengths = (300, 1000, 777)
+    q = gen.draw_normal(rng, (3, n_head, n_q, 128)).astype(np.float16)
+    k = gen.pack_f16(gen.draw_normal(rng, (n_pool, n_head_kv, 128)))
+    v = gen.pack_f16(gen.draw_normal(rng, (n_pool, n_head_kv, 128)))
+    rows = gen.rows_lists(rng, n_pool, lengths, 1000, shuffle=True)
+    mask = np.stack([gen.random_mask_f16(rng, n_q, 1000, p_hidden=0.25) for _ in range(3)])[:, None]
+    w = dict(q=q, k=k, v=v, kv_rows=rows, mask=mask, k_type=gen.TYPE_F16, v_type=gen.TYPE_F16,
+             scale=1 / np.sqrt(128))
+    step(f"rows f16 heads {n_head}/{n_head_kv} n_q={n_q} lists {lengths}")
+    O, L = run.rows(w)
+    assert run.ctx.stats()["kernel_variant"] == 3
+    Oref, Lref = oracle_rows(w)
+    assert_close(O, L, Oref, Lref, what="rows f16 mfma")
+
+
+def test_rows_f16_matrix_core_padding_chunks_and_no_mask(run):
+    """Whole 16-entry chunks of padding, padding holes, a list shorter than one chunk."""
+    rng = gen.rng_for(44)
+    n_pool = 1500
+    q = gen.draw_normal(rng, (2, 32, 1, 128)).astype(np.float16)
+    k = gen.pack_f16(gen.draw_normal(rng, (n_pool, 8, 128)))
+    v = gen.pack_f16(gen.draw_normal(rng, (n_pool, 8, 128)))
+    rows = gen.rows_lists(rng, n_pool, (900, 11), 900)
+    rows[0, 32:80] = -1
+    rows[0, rng.random(900) < 0.2] = -1
+    w = dict(q=q, k=k, v=v, kv_rows=rows, mask=None, k_type=gen.TYPE_F16, v_type=gen.TYPE_F16,
+             scale=1 / np.sqrt(128))
+    step("rows f16 padding chunks, 11-entry list, no mask")
+    O, L = run.rows(w, mask=None)
+    Oref, Lref = oracle_rows(w, mask=None)
+    assert_close(O, L, Oref, Lref, what="rows f16 padding")
 
 
 def test_rows_padding_ignored_without_mask(run):

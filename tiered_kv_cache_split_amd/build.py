@@ -14,7 +14,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "librkv.so")
-SOURCES = ["rkv_decode.hip", "rkv_decode_mma.hip", "rkv_prefill.hip", "rkv_merge.hip", "rkv_aux.hip", "rkv_runtime.cpp"]
+SOURCES = ["rkv_decode.hip", "rkv_decode_mma.hip", "rkv_decode_mma16.hip", "rkv_prefill.hip", "rkv_merge.hip", "rkv_aux.hip", "rkv_runtime.cpp"]
 ARCH = "gfx950"
 # Packed FP32 instructions are disabled for all device code (their generated forms are
 # avoided on this target); the host pass ignores the feature with a warning.

@@ -722,6 +722,7 @@ hipError_t launch_decode_r(const SegParams &p, hipStream_t s, int *occupancy) {
             if (p.cell_hw == 2) return launch_cell<KT, VT, R, 2>(p, s, occupancy);
         }
         if constexpr (KT == T_F16 && VT == T_F16) {
+            if (decode_mma16_ok(p)) return launch_decode_mma16(p, s, occupancy);
             if (p.cell_hw == 2) return launch_cell<KT, VT, R, 2>(p, s, occupancy);
         }
         return hipErrorInvalidValue;
@@ -762,7 +763,10 @@ hipError_t dispatch_decode(const SegParams &p, int k_type, int v_type, hipStream
 }  // namespace
 
 int cell_heads(int k_type, int v_type, int n_head_kv, int R, bool rows) {
-    if (R < 1 || R > kMaxRowsVec || rows) return 0;  // gathered rows: per-head kernel
+    if (R < 1 || R > kMaxRowsVec) return 0;
+    // binary16 with eight KV heads per cell group: the matrix-core kernel, also for row lists
+    if (k_type == T_F16 && v_type == T_F16 && n_head_kv % 8 == 0) return 8;
+    if (rows) return 0;  // other gathered rows: per-head kernel
     if (k_type == T_Q8_0 && v_type == T_Q4_0) {
         for (int hw : {8, 4, 2})
             if (n_head_kv % hw == 0) return hw;
@@ -783,6 +787,7 @@ int decode_kernel_variant(const SegParams &p, int k_type, int v_type) {
 #ifndef RKV_DECODE_VALU_CELL
     if (k_type == T_Q8_0 && v_type == T_Q4_0 && decode_mma_ok(p)) return RKV_KERNEL_DECODE_CELL_MFMA;
 #endif
+    if (k_type == T_F16 && v_type == T_F16 && decode_mma16_ok(p)) return RKV_KERNEL_DECODE_CELL_MFMA;
     return RKV_KERNEL_DECODE_CELL;
 }
 

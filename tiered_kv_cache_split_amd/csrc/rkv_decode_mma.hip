@@ -64,22 +64,6 @@ __device__ __forceinline__ float row16_sum(float x) {
     return x;
 }
 
-// Max of lane k over the four 16-lane rows, in every row.
-__device__ __forceinline__ float fold_rows_max(float x) {
-    const int xi = __builtin_bit_cast(int, x);
-    const auto r16 = __builtin_amdgcn_permlane16_swap(xi, xi, false, false);
-    x = fmaxf(__builtin_bit_cast(float, (int)r16[0]), __builtin_bit_cast(float, (int)r16[1]));
-    const int yi = __builtin_bit_cast(int, x);
-    const auto r32 = __builtin_amdgcn_permlane32_swap(yi, yi, false, false);
-    return fmaxf(__builtin_bit_cast(float, (int)r32[0]), __builtin_bit_cast(float, (int)r32[1]));
-}
-
-__device__ __forceinline__ void lds_order() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
 template <int HW>
 struct Stage {
     static constexpr int kNT = 64 * HW;

@@ -26,6 +26,7 @@ struct SegParams {
     // optional row list (unified pool): key j of sequence b is cell rows[j + rows_s*b]
     const int32_t *rows;
     int64_t rows_s;
+    int64_t n_pool;    // row lists: cells of the pool the rows index
     // optional additive binary16 mask: element strides of query i and sequence b;
     // column = pos0 + j (global key position)
     const _Float16 *mask;
@@ -69,6 +70,10 @@ hipError_t launch_decode_segment(const SegParams &p, int k_type, int v_type, hip
 // launching.
 bool decode_mma_ok(const SegParams &p);
 hipError_t launch_decode_mma(const SegParams &p, hipStream_t s, int *occupancy);
+// The binary16 matrix-core decode kernel (windows, tail tiles and row lists) over groups of
+// eight cell-major KV heads with gqa * n_q <= 8 rows per head; the same occupancy convention.
+bool decode_mma16_ok(const SegParams &p);
+hipError_t launch_decode_mma16(const SegParams &p, hipStream_t s, int *occupancy);
 hipError_t launch_prefill_segment(const SegParams &p, int k_type, int v_type, hipStream_t s);
 // Blocks the prefill kernel uses per (q tile, KV head) along the key axis.
 int prefill_rows_per_block();

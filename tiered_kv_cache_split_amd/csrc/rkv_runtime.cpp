@@ -268,6 +268,9 @@ int use_cell_kernel(const Seg &sg, const SegParams &p, int k_type, int v_type) {
     if (sg.k_s1 < p.n_head_kv * rk || sg.v_s1 < p.n_head_kv * rv) return 0;
     if ((sg.k_s1 | sg.v_s1) % 16 != 0) return 0;
     if (((uintptr_t)sg.k | (uintptr_t)sg.v) % 16 != 0) return 0;
+    // row lists: the cell-major kernel addresses the pool with 32-bit offsets
+    const int64_t lim = (int64_t)1 << 31;
+    if (p.rows && (p.n_pool * sg.k_s1 >= lim || p.n_pool * sg.v_s1 >= lim)) return 0;
     return hw;
 }
 
@@ -290,7 +293,9 @@ void seg_plan(const rkv_ctx *ctx, int64_t n_cells, const SegParams &p, bool mfma
         // cell-major kernel: one wave of resident workgroups over (split, head group, sequence),
         // at least 256 cells per split
         const int64_t groups = (int64_t)p.n_seq * (p.n_head_kv / p.cell_hw);
-        const int64_t slots = (int64_t)std::max(1, cell_occupancy) * ctx->n_cu;
+        // row lists of several sequences differ in length (the rest is padding): four rounds
+        // of workgroups let the short lists' CUs take further work
+        const int64_t slots = (int64_t)std::max(1, cell_occupancy) * ctx->n_cu * (p.rows && p.n_seq > 1 ? 4 : 1);
         int64_t want = ctx->splits_override > 0 ? ctx->splits_override : std::max<int64_t>(1, slots / groups);
         want = std::max<int64_t>(1, std::min(want, std::max<int64_t>(1, n_cells / 256)));
         cps = (n_cells + want - 1) / want;
@@ -779,6 +784,7 @@ int rkv_attn_rows(rkv_ctx *ctx, const rkv_tensor *q, const rkv_tensor *k_pool, c
     fill_mask(p, mask);
     p.rows = kv_rows;
     p.rows_s = n_kv;
+    p.n_pool = k_pool->ne[1];
     p.q_pos0 = -1;
     p.n_head = (int)n_head;
     p.n_head_kv = (int)n_head_kv;
