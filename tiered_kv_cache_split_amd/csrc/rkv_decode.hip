@@ -782,6 +782,10 @@ int cell_blocks_per_cu(const SegParams &p, int k_type, int v_type) {
     return n;
 }
 
+bool decode_kernel_persistent(const SegParams &p, int k_type, int v_type) {
+    return p.cell_hw > 0 && k_type == T_F16 && v_type == T_F16 && decode_mma16_ok(p);
+}
+
 int decode_kernel_variant(const SegParams &p, int k_type, int v_type) {
     if (p.cell_hw <= 0) return RKV_KERNEL_DECODE_HEAD;
 #ifndef RKV_DECODE_VALU_CELL

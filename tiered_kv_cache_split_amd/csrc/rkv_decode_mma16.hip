@@ -36,6 +36,8 @@ typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kHW = 8;                 // KV heads per workgroup
 constexpr int kCh = 16;                // cells per chunk
@@ -49,15 +51,29 @@ constexpr int kM = kCell / 16 / kTpc;  // 16-byte units per thread, cache and ch
 constexpr uint32_t kNowhere = 0x80000000u;  // buffer offset past every range: reads zero
 static_assert(kCell % (16 * kTpc) == 0 && kNT % kCh == 0, "thread mapping");
 
-// One chunk in registers: this thread's K and V units, the mask value it stages, whether its
-// cell is a key of the segment, and (row lists) the pool row its next fetch will use.
+// One chunk (task) in registers: this thread's K and V units, the mask value it stages,
+// whether its cell is a key of the segment, the task's pair and first cell, the Q^T operand
+// when the task starts a new pair, and (row lists) the pool rows the stage's next fetch uses.
+struct Meta {
+    int pair;   // (sequence, head group) pair of the task
+    int newq;   // the task starts a new pair for this workgroup (q holds its Q^T)
+    int64_t c0; // first cell
+};
 struct Stage16 {
     uint4 k[kM], v[kM];
+    half8_t q[4];
     uint32_t mk;
     int ok;
-    int2 rid;  // row lists: pool rows of the wave's two cells for the next fetch
+    Meta meta;
+    int2 rid, rin;  // row lists: raw pool rows of the wave's two cells for the next fetch, and
+                    // whether they are keys
 };
 
+// Work split: the tasks are the 16-cell chunks of every (sequence, head group) pair, numbered
+// pair-major; workgroup j of G takes tasks j, j + G, j + 2G, ...  Row lists of several sequences
+// are padded to one length and padding costs no memory traffic, so this interleaving balances
+// the real keys over the workgroups without knowing the list lengths.  A workgroup writes one
+// partial (slot j) for every pair: its own keys' partial, or the empty one.
 template <int R, bool ROWS>
 __global__ void __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2)))
 decode_mma16_kernel(const SegParams p) {
@@ -69,75 +85,99 @@ decode_mma16_kernel(const SegParams p) {
     const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int col = lane & 15, grp = lane >> 4;
     const int n_hgrp = p.n_head_kv / kHW;
-    int bid = blockIdx.x;
-    const int b = bid % p.n_seq;  // sequences fastest: long and short row lists interleave
-    bid /= p.n_seq;
-    const int hgrp = bid % n_hgrp;
-    const int split = bid / n_hgrp;
-    const int g = hgrp * kHW + wave;  // this wave's KV head
-    const int64_t c_beg = (int64_t)split * p.cells_per_split;
-    const int64_t c_end = min(p.n_cells, c_beg + (int64_t)p.cells_per_split);
-    const int64_t n_ch = (c_end > c_beg) ? (c_end - c_beg + kCh - 1) / kCh : 0;
+    const int n_pairs = p.n_seq * n_hgrp;
+    const uint32_t cpp = (uint32_t)((p.n_cells + kCh - 1) / kCh);  // chunks per pair
+    const uint32_t n_tasks = (uint32_t)n_pairs * cpp;
+    const uint32_t G = (uint32_t)p.n_splits, j = blockIdx.x;
+    if (j >= G) return;  // the grid is exactly G workgroups; slot j must exist
+    const uint32_t n_t = n_tasks > j ? (n_tasks - j + G - 1) / G : 0;  // this workgroup's tasks
+    const int64_t n_cells = p.n_cells;
     const int qi_row = min(col, R - 1) / p.gqa;  // query position of this lane's row
-
-    if (n_ch == 0) {  // empty split: the neutral partial
-        if (col < R) {
-            const int r = col % p.gqa, i = col / p.gqa;
-            const int64_t row = (g * p.gqa + r) + (int64_t)p.n_head * (i + (int64_t)p.n_q * b);
-            float *out = p.partials + ((int64_t)(p.slot0 + split) * p.n_rows + row) * kPartialStride;
-            if (grp == 0) {
-                out[0] = -INFINITY;
-                out[1] = 0.f;
-            }
-#pragma unroll
-            for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) out[2 + 16 * dt + 4 * grp + e] = 0.f;
-        }
-        return;
-    }
-
-    const uint8_t *kbase = p.k + (int64_t)(hgrp * kHW) * p.k_s2;
-    const uint8_t *vbase = p.v + (int64_t)(hgrp * kHW) * p.v_s2;
-    const int32_t *__restrict__ rows = ROWS ? p.rows + (int64_t)b * p.rows_s : nullptr;
     const int fcell = tid / kTpc, fsub = tid % kTpc;
-    // mask staging: thread t < R * kCh stages mask[row t / kCh][key t % kCh] of a chunk
-    const int mrow = tid / kCh, mkey = tid % kCh;
+    const int mrow = tid / kCh, mkey = tid % kCh;  // mask staging: row tid / 16, key tid % 16
     const bool mthread = p.mask != nullptr && tid < R * kCh;
-    const _Float16 *mbase = p.mask ? p.mask + p.pos0 + (int64_t)b * p.m_s3 + (int64_t)(min(mrow, R - 1) / p.gqa) * p.m_s1
-                                   : nullptr;
-    // row lists: one resource over the whole pool (its size is checked below 2^31 bytes)
-    const __amdgpu_buffer_rsrc_t rk_pool = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)kbase, (short)0, ROWS ? (int)(p.n_pool * p.k_s1) : 0, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rv_pool = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)vbase, (short)0, ROWS ? (int)(p.n_pool * p.v_s1) : 0, 0x00020000);
-    // pool rows of the wave's two cells 2*wave, 2*wave + 1 of the chunk at c0: uniform reads
-    // (scalar loads, so waiting for them never waits for the buffer loads in flight); entries
-    // past the segment end are padding
-    auto rows_of = [&](int64_t c0) __attribute__((always_inline)) {
-        const int64_t c = c0 + 2 * wave;
-        const int r0 = rows[min(c, c_end - 1)], r1 = rows[min(c + 1, c_end - 1)];
-        return make_int2(c < c_end ? r0 : -1, c + 1 < c_end ? r1 : -1);
+
+    // ---- partial of one pair for this lane's row (col < R): slot j.  Buffer stores of four
+    // values each keep the store count per partial small and fixed (9), so that the waits for
+    // the loads in flight, which count stores too, stay exact.
+    const __amdgpu_buffer_rsrc_t rpart = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(p.partials + (int64_t)(p.slot0 + j) * p.n_rows * kPartialStride), (short)0,
+        (int)(p.n_rows * kPartialStride * sizeof(float)), 0x00020000);
+    auto write_partial = [&](int pair, float M, float S, const float4_t *acc) __attribute__((always_inline)) {
+        if (col >= R) return;
+        const int bb = pair / n_hgrp, g = (pair % n_hgrp) * kHW + wave;
+        const int r = col % p.gqa, i = col / p.gqa;
+        const int row = (g * p.gqa + r) + p.n_head * (i + p.n_q * bb);
+        const int base = row * kPartialStride * (int)sizeof(float);
+        if (grp == 0)
+            __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{__builtin_bit_cast(uint32_t, M), __builtin_bit_cast(uint32_t, S)},
+                                                  rpart, base, 0, 0);
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+            const float4_t v = acc ? acc[dt] : float4_t{0.f, 0.f, 0.f, 0.f};
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), rpart,
+                                                   base + (2 + 16 * dt + 4 * grp) * (int)sizeof(float), 0, 0);
+        }
     };
 
-    auto fetch = [&](Stage16 &st, int64_t c0) __attribute__((always_inline)) {
-        const int64_t c = c0 + fcell;
+    // ---- task k of this workgroup: its pair and first cell (k past the end: a phantom task
+    // of the last pair with no keys)
+    auto task = [&](uint32_t k, int &pair, int64_t &c0) __attribute__((always_inline)) {
+        const uint32_t t = j + min(k, n_t - 1) * G;
+        pair = (int)(t / cpp);
+        c0 = (int64_t)(t - (uint32_t)pair * cpp) * kCh;
+    };
+    // pool rows of the wave's two cells 2*wave, 2*wave + 1 of task k's chunk, as read (always
+    // from inside the list), and whether each is a key: entries past the list end (or of a
+    // phantom task) are padding.  The raw value is only combined with the flag when the next
+    // fetch uses it, so that waiting for it never waits for the loads issued after it.
+    auto rows_of = [&](uint32_t k, int2 &raw, int2 &inl) __attribute__((always_inline)) {
+        int pair;
+        int64_t c0;
+        task(k, pair, c0);
+        const int32_t *__restrict__ rl = p.rows + (int64_t)(pair / n_hgrp) * p.rows_s;
+        const int64_t c = c0 + 2 * wave;
+        raw = make_int2(rl[min(c, n_cells - 1)], rl[min(c + 1, n_cells - 1)]);
+        const bool real = k < n_t;
+        inl = make_int2(real && c < n_cells, real && c + 1 < n_cells);
+    };
+
+    auto fetch = [&](Stage16 &st, uint32_t k) __attribute__((always_inline)) {
+        const bool real = k < n_t;
+        int pair;
+        int64_t c0;
+        task(k, pair, c0);
+        int prev_pair = -1;
+        int64_t pc0;
+        if (k > 0) task(k - 1, prev_pair, pc0);
+        st.meta.pair = pair;
+        st.meta.c0 = c0;
+        st.meta.newq = real && pair != prev_pair;
+        const int bb = pair / n_hgrp, hg = pair % n_hgrp;
+        const uint8_t *kbase = p.k + (int64_t)(hg * kHW) * p.k_s2;
+        const uint8_t *vbase = p.v + (int64_t)(hg * kHW) * p.v_s2;
         if constexpr (ROWS) {
-            const int r = (fcell & 1) ? st.rid.y : st.rid.x;
+            int r = (fcell & 1) ? (st.rin.y ? st.rid.y : -1) : (st.rin.x ? st.rid.x : -1);
+            if (r >= p.n_pool) r = -1;  // outside the pool: read nothing, like padding
             st.ok = r >= 0;
-            const uint32_t ok_ = kNowhere;
-            const uint32_t ko = r >= 0 ? (uint32_t)r * (uint32_t)p.k_s1 + 16u * fsub : ok_;
-            const uint32_t vo = r >= 0 ? (uint32_t)r * (uint32_t)p.v_s1 + 16u * fsub : ok_;
+            const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)kbase, (short)0, (int)(p.n_pool * p.k_s1), 0x00020000);
+            const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)vbase, (short)0, (int)(p.n_pool * p.v_s1), 0x00020000);
+            // 24-bit products (pool rows below 2^20 and cell strides below 2^11 here), so the
+            // offset is plain 32-bit arithmetic
+            const uint32_t ko = r >= 0 ? __umul24((uint32_t)r, (uint32_t)p.k_s1) + 16u * fsub : kNowhere;
+            const uint32_t vo = r >= 0 ? __umul24((uint32_t)r, (uint32_t)p.v_s1) + 16u * fsub : kNowhere;
 #pragma unroll
             for (int m = 0; m < kM; ++m)
-                st.k[m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk_pool, ko + 16 * kTpc * m, 0, 0));
+                st.k[m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, ko + 16 * kTpc * m, 0, 0));
 #pragma unroll
             for (int m = 0; m < kM; ++m)
-                st.v[m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv_pool, vo + 16 * kTpc * m, 0, 0));
-            st.rid = rows_of(c0 + 2 * kCh);  // for this stage's next fetch
+                st.v[m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, vo + 16 * kTpc * m, 0, 0));
+            rows_of(k + 2, st.rid, st.rin);  // for this stage's next fetch
         } else {
-            st.ok = c < c_end;
-            const int64_t nv = max((int64_t)0, min((int64_t)kCh, c_end - c0));
+            st.ok = real && c0 + fcell < n_cells;
+            const int64_t nv = real ? max((int64_t)0, min((int64_t)kCh, n_cells - c0)) : 0;
             const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
                 (void *)(kbase + c0 * p.k_s1), (short)0, (int)(nv * p.k_s1), 0x00020000);
             const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
@@ -151,8 +191,24 @@ decode_mma16_kernel(const SegParams p) {
             for (int m = 0; m < kM; ++m)
                 st.v[m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, vo + 16 * kTpc * m, 0, 0));
         }
-        if (mthread) st.mk = __builtin_bit_cast(uint16_t, mbase[min(c0 + mkey, c_end - 1)]);
+        if (mthread) {
+            const _Float16 *mb = p.mask + p.pos0 + (int64_t)bb * p.m_s3 + (int64_t)(mrow / p.gqa) * p.m_s1;
+            st.mk = __builtin_bit_cast(uint16_t, mb[min(c0 + mkey, n_cells - 1)]);
+        }
+        if (st.meta.newq) {
+            // Q^T of the pair: lane holds row `col` (rows >= R read row 0 and are never written),
+            // head_dim 32*blk + 8*grp + 0..7
+            const int r = col < R ? col : 0;
+            const int g = hg * kHW + wave;
+            const _Float16 *qrow = p.q + (int64_t)(r / p.gqa) * p.q_s1 + (int64_t)(g * p.gqa + r % p.gqa) * p.q_s2 +
+                                   (int64_t)bb * p.q_s3;
+#pragma unroll
+            for (int blk = 0; blk < 4; ++blk)
+                st.q[blk] = __builtin_bit_cast(half8_t, *reinterpret_cast<const uint4 *>(qrow + 32 * blk + 8 * grp));
+        }
     };
+    Meta mnext;         // the task stashed last: computed next
+    half8_t qnext[4];   // its Q^T when it starts a new pair
     auto stash = [&](const Stage16 &st, int buf) __attribute__((always_inline)) {
         uint8_t *dk = s_k + buf * kStage + fcell * kS + 16 * fsub;
         uint8_t *dv = s_v + buf * kStage + fcell * kS + 16 * fsub;
@@ -163,6 +219,11 @@ decode_mma16_kernel(const SegParams p) {
         }
         if (fsub == 0) s_ok[buf][fcell] = st.ok;
         if (mthread) s_mask[buf][mrow][mkey] = __builtin_bit_cast(_Float16, (uint16_t)st.mk);
+        mnext = st.meta;
+        if (st.meta.newq) {
+#pragma unroll
+            for (int blk = 0; blk < 4; ++blk) qnext[blk] = st.q[blk];
+        }
     };
 
     float4_t oacc[8];  // O^T[16*dt + 4*grp + e][col]
@@ -170,32 +231,37 @@ decode_mma16_kernel(const SegParams p) {
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) oacc[dt] = float4_t{0.f, 0.f, 0.f, 0.f};
     const float c = p.scale_log2;
-
-    // ---- Q^T as the B operand of Q.K: lane holds row `col`, head_dim 32*blk + 8*grp + 0..7.  Its
-    // loads go first so that waiting for them waits for nothing else.
     half8_t qb[4];
-    Stage16 sa, sb;  // chunks 2i (sa) and 2i + 1 (sb) of the split
-    sa.mk = sb.mk = 0;
-    {
-        const bool okq = col < R;
-        const int r = okq ? col : 0;
-        const _Float16 *qrow = p.q + (int64_t)(r / p.gqa) * p.q_s1 + (int64_t)(g * p.gqa + r % p.gqa) * p.q_s2 +
-                               (int64_t)b * p.q_s3;
-        uint4 qv[4];
-#pragma unroll
-        for (int blk = 0; blk < 4; ++blk) qv[blk] = *reinterpret_cast<const uint4 *>(qrow + 32 * blk + 8 * grp);
-        if constexpr (ROWS) {
-            sa.rid = rows_of(c_beg);
-            sb.rid = rows_of(c_beg + kCh);
+    int cur = -1;  // pair being accumulated
+    // finish the current pair (a fixed number of stores, so the waits for the loads in flight
+    // stay exact)
+    auto flush = [&]() __attribute__((always_inline)) {
+        if (cur >= 0) {
+            const float S = fold_rows(lrow);
+            write_partial(cur, mrun == -INFINITY ? -INFINITY : mrun * kLn2, S, oacc);
         }
-        fetch(sa, c_beg);
-        fetch(sb, c_beg + kCh);
-#pragma unroll
-        for (int blk = 0; blk < 4; ++blk) qb[blk] = __builtin_bit_cast(half8_t, okq ? qv[blk] : make_uint4(0, 0, 0, 0));
+    };
+    // pairs with no task in this workgroup get the empty partial up front: pair P's first task
+    // of residue j modulo G is P*cpp + ((j - P*cpp) mod G)
+    for (int pr = 0; pr < n_pairs; ++pr) {
+        const uint32_t lo = (uint32_t)pr * cpp;
+        const uint32_t first = lo + (j + G - lo % G) % G;
+        if (!(first < lo + cpp && first < n_tasks)) write_partial(pr, -INFINITY, 0.f, nullptr);
     }
 
-    // ---- one chunk from LDS stage `buf`
-    auto compute = [&](int buf, int64_t c0) __attribute__((always_inline)) {
+    // ---- one task from LDS stage `buf` (its metadata and, for a new pair, its Q^T were taken
+    // from the stage registers when the stage was stashed)
+    auto compute = [&](int buf, const Meta &mt_) __attribute__((always_inline)) {
+        if (mt_.newq) {
+            flush();
+            cur = mt_.pair;
+#pragma unroll
+            for (int blk = 0; blk < 4; ++blk) qb[blk] = qnext[blk];
+            mrun = -INFINITY;
+            lrow = 0.f;
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) oacc[dt] = float4_t{0.f, 0.f, 0.f, 0.f};
+        }
         const uint8_t *kw = s_k + buf * kStage + wave * kRowB;  // this head's K row of cell j at kw + j*kS
         const uint8_t *vw = s_v + buf * kStage + wave * kRowB;
 
@@ -217,7 +283,7 @@ decode_mma16_kernel(const SegParams p) {
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
             bool vis = okk[ii] != 0;
-            if (!ROWS && p.q_pos0 >= 0 && p.pos0 + c0 + 4 * grp + ii > p.q_pos0 + qi_row) vis = false;
+            if (!ROWS && p.q_pos0 >= 0 && p.pos0 + mt_.c0 + 4 * grp + ii > p.q_pos0 + qi_row) vis = false;
             float x = dq[ii] * c;
             if (p.mask) x = fmaf(mvals[ii], kLog2e, x);
             s[ii] = vis ? x : -INFINITY;
@@ -253,47 +319,43 @@ decode_mma16_kernel(const SegParams p) {
         }
     };
 
-    // ---- pipeline: chunk ch is computed from stage ch % 2 while chunks ch + 2 and ch + 3 are
-    // in flight in registers; the barrier before a stash orders it after every wave's reads of
-    // that stage (two chunks earlier) and the previous stash before this chunk's reads.  Chunks
-    // go in pairs with no exit in between (a chunk past the end has no visible key), so that
-    // every path into the loop head has the same loads in flight.
-    stash(sa, 0);
-    fetch(sa, c_beg + 2 * kCh);
-    for (int64_t ch = 0; ch < n_ch; ch += 2) {
-        __syncthreads();
-        stash(sb, 1);
-        fetch(sb, c_beg + (ch + 3) * kCh);
-        compute(0, c_beg + ch * kCh);
-        __syncthreads();
-        stash(sa, 0);
-        fetch(sa, c_beg + (ch + 4) * kCh);
-        compute(1, c_beg + (ch + 1) * kCh);
-    }
-
-    // ---- partial of row `col`: the sum is folded over the four lanes of the row
-    const float S = fold_rows(lrow);
-    if (col < R) {
-        const int r = col % p.gqa, i = col / p.gqa;
-        const int64_t row = (g * p.gqa + r) + (int64_t)p.n_head * (i + (int64_t)p.n_q * b);
-        float *out = p.partials + ((int64_t)(p.slot0 + split) * p.n_rows + row) * kPartialStride;
-        if (grp == 0) {
-            out[0] = (mrun == -INFINITY) ? -INFINITY : mrun * kLn2;
-            out[1] = S;
+    // ---- pipeline: task k is computed from stage k % 2 right after a barrier; then the stage
+    // of task k + 1 is stashed and task k + 3 fetched into its registers, so two tasks are in
+    // flight in registers while one computes.  The barrier orders a stash after every wave's
+    // reads of that stage (the task before) and a task's reads after its stash.  Tasks go in
+    // pairs with no exit in between (a phantom task has no visible key), so that every path
+    // into the loop head has the same loads in flight.
+    if (n_t > 0) {
+        Stage16 sa, sb;  // tasks 2i (sa) and 2i + 1 (sb)
+        sa.mk = sb.mk = 0;
+        if constexpr (ROWS) {
+            rows_of(0, sa.rid, sa.rin);
+            rows_of(1, sb.rid, sb.rin);
         }
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) out[2 + 16 * dt + 4 * grp + e] = oacc[dt][e];
+        fetch(sa, 0);
+        fetch(sb, 1);
+        stash(sa, 0);
+        fetch(sa, 2);
+        for (uint32_t k = 0; k < n_t; k += 2) {
+            __syncthreads();
+            compute(0, mnext);
+            stash(sb, 1);
+            fetch(sb, k + 3);
+            __syncthreads();
+            compute(1, mnext);
+            stash(sa, 0);
+            fetch(sa, k + 4);
+        }
     }
+    flush();
 }
 
 template <int R, bool ROWS>
 hipError_t launch16(const SegParams &p, hipStream_t s, int *occupancy) {
     if (occupancy)
         return hipOccupancyMaxActiveBlocksPerMultiprocessor(occupancy, decode_mma16_kernel<R, ROWS>, kNT, 0);
-    launch_seg(decode_mma16_kernel<R, ROWS>, dim3((unsigned)(p.n_splits * (p.n_head_kv / kHW) * p.n_seq)), dim3(kNT),
-               s, p);
+    // persistent: n_splits workgroups in all, each covering every pair
+    launch_seg(decode_mma16_kernel<R, ROWS>, dim3((unsigned)p.n_splits), dim3(kNT), s, p);
     return hipGetLastError();
 }
 
@@ -308,7 +370,8 @@ bool decode_mma16_ok(const SegParams &p) {
     const int R = p.gqa * p.n_q;
     if (p.cell_hw != kHW || R < 1 || R > 8 || p.n_head_kv % kHW != 0) return false;
     // row lists address the pool with 32-bit buffer offsets
-    if (p.rows && (p.n_pool <= 0 || p.n_pool * p.k_s1 >= ((int64_t)1 << 31) || p.n_pool * p.v_s1 >= ((int64_t)1 << 31)))
+    if (p.rows && (p.n_pool <= 0 || p.n_pool * p.k_s1 >= ((int64_t)1 << 31) || p.n_pool * p.v_s1 >= ((int64_t)1 << 31) ||
+                   p.k_s1 >= (1 << 24) || p.v_s1 >= (1 << 24)))
         return false;
     return true;
 }

@@ -73,6 +73,9 @@ hipError_t launch_decode_mma(const SegParams &p, hipStream_t s, int *occupancy);
 // The binary16 matrix-core decode kernel (windows, tail tiles and row lists) over groups of
 // eight cell-major KV heads with gqa * n_q <= 8 rows per head; the same occupancy convention.
 bool decode_mma16_ok(const SegParams &p);
+// Whether the decode kernel for p is the persistent one: n_splits workgroups then take every
+// n_splits-th 16-cell chunk of all (sequence, head group) pairs, and cells_per_split is unused.
+bool decode_kernel_persistent(const SegParams &p, int k_type, int v_type);
 hipError_t launch_decode_mma16(const SegParams &p, hipStream_t s, int *occupancy);
 hipError_t launch_prefill_segment(const SegParams &p, int k_type, int v_type, hipStream_t s);
 // Blocks the prefill kernel uses per (q tile, KV head) along the key axis.

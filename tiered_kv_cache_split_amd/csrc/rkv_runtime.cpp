@@ -270,14 +270,15 @@ int use_cell_kernel(const Seg &sg, const SegParams &p, int k_type, int v_type) {
     if (((uintptr_t)sg.k | (uintptr_t)sg.v) % 16 != 0) return 0;
     // row lists: the cell-major kernel addresses the pool with 32-bit offsets
     const int64_t lim = (int64_t)1 << 31;
-    if (p.rows && (p.n_pool * sg.k_s1 >= lim || p.n_pool * sg.v_s1 >= lim)) return 0;
+    if (p.rows && (p.n_pool * sg.k_s1 >= lim || p.n_pool * sg.v_s1 >= lim || sg.k_s1 >= (1 << 24) || sg.v_s1 >= (1 << 24)))
+        return 0;
     return hw;
 }
 
 // Split-K plan of one device segment: cells per split and number of splits.  The vector
 // kernel walks 64-cell chunks; the MFMA kernel walks key tiles of prefill_keys_per_iter().
-void seg_plan(const rkv_ctx *ctx, int64_t n_cells, const SegParams &p, bool mfma, int cell_occupancy, int64_t &cps,
-              int &n_splits) {
+void seg_plan(const rkv_ctx *ctx, int64_t n_cells, const SegParams &p, bool mfma, int cell_occupancy, bool persistent,
+              int64_t &cps, int &n_splits) {
     if (mfma) {
         const int kpi = prefill_keys_per_iter();
         const int64_t q_tiles = ((int64_t)p.gqa * p.n_q + prefill_rows_per_block() - 1) / prefill_rows_per_block();
@@ -289,13 +290,20 @@ void seg_plan(const rkv_ctx *ctx, int64_t n_cells, const SegParams &p, bool mfma
         want = std::min<int64_t>(want, std::max<int64_t>(1, (n_cells + kpi - 1) / kpi));
         cps = (n_cells + want - 1) / want;
         cps = std::max<int64_t>(kpi, (cps + kpi - 1) / kpi * kpi);
+    } else if (persistent) {
+        // binary16 matrix-core kernel: one resident workgroup per slot, each taking every G-th
+        // 16-cell chunk of all (sequence, head group) pairs
+        const int64_t tasks = (int64_t)p.n_seq * (p.n_head_kv / p.cell_hw) * ((n_cells + 15) / 16);
+        const int64_t slots = (int64_t)std::max(1, cell_occupancy) * ctx->n_cu;
+        const int64_t g = ctx->splits_override > 0 ? ctx->splits_override : slots;
+        n_splits = (int)std::max<int64_t>(1, std::min(g, tasks));
+        cps = n_cells;
+        return;
     } else if (p.cell_hw > 0) {
         // cell-major kernel: one wave of resident workgroups over (split, head group, sequence),
         // at least 256 cells per split
         const int64_t groups = (int64_t)p.n_seq * (p.n_head_kv / p.cell_hw);
-        // row lists of several sequences differ in length (the rest is padding): four rounds
-        // of workgroups let the short lists' CUs take further work
-        const int64_t slots = (int64_t)std::max(1, cell_occupancy) * ctx->n_cu * (p.rows && p.n_seq > 1 ? 4 : 1);
+        const int64_t slots = (int64_t)std::max(1, cell_occupancy) * ctx->n_cu;
         int64_t want = ctx->splits_override > 0 ? ctx->splits_override : std::max<int64_t>(1, slots / groups);
         want = std::max<int64_t>(1, std::min(want, std::max<int64_t>(1, n_cells / 256)));
         cps = (n_cells + want - 1) / want;
@@ -319,7 +327,8 @@ SegPlan plan_segment(const rkv_ctx *ctx, const SegParams &base, const Seg &sg, b
     p.cell_hw = mfma ? 0 : use_cell_kernel(sg, p, k_type, v_type);
     SegPlan pl{p.cell_hw, 0, 0};
     const int occ = p.cell_hw > 0 ? cell_blocks_per_cu(p, k_type, v_type) : 1;
-    seg_plan(ctx, sg.n_cells, p, mfma, occ, pl.cps, pl.n_splits);
+    seg_plan(ctx, sg.n_cells, p, mfma, occ, p.cell_hw > 0 && decode_kernel_persistent(p, k_type, v_type), pl.cps,
+             pl.n_splits);
     return pl;
 }
 
