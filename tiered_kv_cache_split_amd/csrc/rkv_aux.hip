@@ -34,6 +34,42 @@ __global__ void __launch_bounds__(128) dequant_kernel(const uint8_t *__restrict_
 
 }  // namespace
 
+// Extent of a padded row list (patch 0102's kv_rows with -1 padding), in kRowExtentParts pieces
+// per sequence: workgroup (b, part) writes 1 + the last index of its slice holding a pool row
+// (0 if none); the extent of sequence b is the maximum over its parts.  Every load of a thread
+// is issued before any is used, so the scan costs about one memory latency.
+__global__ void __launch_bounds__(256) row_extent_kernel(const int32_t *__restrict__ rows, int64_t rows_s, int64_t n_kv,
+                                                         int32_t *__restrict__ extent) {
+    __shared__ int s_red[4];
+    const int b = blockIdx.x / kRowExtentParts, part = blockIdx.x % kRowExtentParts;
+    const int32_t *r = rows + (int64_t)b * rows_s;
+    const int64_t len = (n_kv + kRowExtentParts - 1) / kRowExtentParts;
+    const int64_t j0 = part * len, j1 = min(n_kv, j0 + len);
+    int last = -1;
+    for (int64_t base = j0; base < j1; base += 256 * 8) {
+        int v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int64_t j = base + threadIdx.x + 256 * u;
+            v[u] = j < j1 ? r[j] : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if (v[u] >= 0) last = (int)(base + threadIdx.x + 256 * u);
+    }
+    for (int o = 32; o > 0; o >>= 1) last = max(last, __shfl_xor(last, o, 64));
+    if ((threadIdx.x & 63) == 0) s_red[threadIdx.x >> 6] = last;
+    __syncthreads();
+    if (threadIdx.x == 0) extent[blockIdx.x] = max(max(s_red[0], s_red[1]), max(s_red[2], s_red[3])) + 1;
+}
+
+hipError_t launch_row_extent(const int32_t *rows, int64_t rows_s, int64_t n_kv, int n_seq, int32_t *extent, hipStream_t s) {
+    if (n_seq <= 0) return hipSuccess;
+    hipLaunchKernelGGL(row_extent_kernel, dim3((unsigned)(n_seq * kRowExtentParts)), dim3(256), 0, s, rows, rows_s, n_kv,
+                       extent);
+    return hipGetLastError();
+}
+
 hipError_t launch_uva_read(const void *host_src, void *dst, int64_t nbytes, hipStream_t s) {
     void *dev_view = nullptr;
     hipError_t e = hipHostGetDevicePointer(&dev_view, const_cast<void *>(host_src), 0);

@@ -49,6 +49,7 @@ constexpr int kStage = kCh * kS;       // bytes of one LDS stage of one cache
 constexpr int kTpc = kNT / kCh;        // threads per cell (32)
 constexpr int kM = kCell / 16 / kTpc;  // 16-byte units per thread, cache and chunk (4)
 constexpr uint32_t kNowhere = 0x80000000u;  // buffer offset past every range: reads zero
+constexpr int kMaxPairs = 1024;        // (sequence, head group) pairs of one launch
 static_assert(kCell % (16 * kTpc) == 0 && kNT % kCh == 0, "thread mapping");
 
 // One chunk (task) in registers: this thread's K and V units, the mask value it stages,
@@ -70,10 +71,11 @@ struct Stage16 {
 };
 
 // Work split: the tasks are the 16-cell chunks of every (sequence, head group) pair, numbered
-// pair-major; workgroup j of G takes tasks j, j + G, j + 2G, ...  Row lists of several sequences
-// are padded to one length and padding costs no memory traffic, so this interleaving balances
-// the real keys over the workgroups without knowing the list lengths.  A workgroup writes one
-// partial (slot j) for every pair: its own keys' partial, or the empty one.
+// pair-major; workgroup j of G takes tasks j, j + G, j + 2G, ...  A row list only counts up to
+// its extent (1 + its last pool row, from a scan before the launch), so the padding at the end
+// of the shorter lists costs nothing, and the interleaving balances the real keys over the
+// workgroups.  A workgroup writes one partial (slot j) for every pair: its own keys' partial,
+// or the empty one.
 template <int R, bool ROWS>
 __global__ void __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2)))
 decode_mma16_kernel(const SegParams p) {
@@ -81,15 +83,42 @@ decode_mma16_kernel(const SegParams p) {
     __shared__ __attribute__((aligned(16))) uint8_t s_v[2 * kStage];
     __shared__ __attribute__((aligned(16))) int s_ok[2][kCh];                 // key is visible data
     __shared__ __attribute__((aligned(16))) _Float16 s_mask[2][kHW][kCh];     // mask[row][key]
+    __shared__ uint32_t s_off[kMaxPairs + 1];  // first task of each pair; s_off[n_pairs] = tasks
 
     const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int col = lane & 15, grp = lane >> 4;
     const int n_hgrp = p.n_head_kv / kHW;
     const int n_pairs = p.n_seq * n_hgrp;
-    const uint32_t cpp = (uint32_t)((p.n_cells + kCh - 1) / kCh);  // chunks per pair
-    const uint32_t n_tasks = (uint32_t)n_pairs * cpp;
     const uint32_t G = (uint32_t)p.n_splits, j = blockIdx.x;
     if (j >= G) return;  // the grid is exactly G workgroups; slot j must exist
+    // ---- task offsets of the pairs: chunks of each pair up to its extent, scanned in LDS
+    for (int pr = tid; pr < n_pairs; pr += kNT) {
+        int64_t ext = p.n_cells;
+        if (p.row_extent) {
+            int e = 0;
+            for (int q = 0; q < kRowExtentParts; ++q) e = max(e, p.row_extent[(pr / n_hgrp) * kRowExtentParts + q]);
+            ext = min(ext, (int64_t)e);
+        }
+        s_off[pr + 1] = (uint32_t)((ext + kCh - 1) / kCh);
+    }
+    if (tid == 0) s_off[0] = 0;
+    __syncthreads();
+    for (int d = 1; d < n_pairs; d <<= 1) {  // inclusive scan of s_off[1 .. n_pairs]
+        uint32_t add[2] = {0, 0};
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int pr = tid + u * kNT;
+            if (pr < n_pairs && pr >= d) add[u] = s_off[pr + 1 - d];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int pr = tid + u * kNT;
+            if (pr < n_pairs) s_off[pr + 1] += add[u];
+        }
+        __syncthreads();
+    }
+    const uint32_t n_tasks = s_off[n_pairs];
     const uint32_t n_t = n_tasks > j ? (n_tasks - j + G - 1) / G : 0;  // this workgroup's tasks
     const int64_t n_cells = p.n_cells;
     const int qi_row = min(col, R - 1) / p.gqa;  // query position of this lane's row
@@ -124,8 +153,14 @@ decode_mma16_kernel(const SegParams p) {
     // of the last pair with no keys)
     auto task = [&](uint32_t k, int &pair, int64_t &c0) __attribute__((always_inline)) {
         const uint32_t t = j + min(k, n_t - 1) * G;
-        pair = (int)(t / cpp);
-        c0 = (int64_t)(t - (uint32_t)pair * cpp) * kCh;
+        int lo = 0, hi = n_pairs - 1;  // the last pair whose first task is <= t (it is not empty)
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (s_off[mid] <= t) lo = mid;
+            else hi = mid - 1;
+        }
+        pair = lo;
+        c0 = (int64_t)(t - s_off[lo]) * kCh;
     };
     // pool rows of the wave's two cells 2*wave, 2*wave + 1 of task k's chunk, as read (always
     // from inside the list), and whether each is a key: entries past the list end (or of a
@@ -242,11 +277,11 @@ decode_mma16_kernel(const SegParams p) {
         }
     };
     // pairs with no task in this workgroup get the empty partial up front: pair P's first task
-    // of residue j modulo G is P*cpp + ((j - P*cpp) mod G)
+    // of residue j modulo G is lo + ((j - lo) mod G), lo = its first task
     for (int pr = 0; pr < n_pairs; ++pr) {
-        const uint32_t lo = (uint32_t)pr * cpp;
+        const uint32_t lo = s_off[pr], hi = s_off[pr + 1];
         const uint32_t first = lo + (j + G - lo % G) % G;
-        if (!(first < lo + cpp && first < n_tasks)) write_partial(pr, -INFINITY, 0.f, nullptr);
+        if (!(first < hi)) write_partial(pr, -INFINITY, 0.f, nullptr);
     }
 
     // ---- one task from LDS stage `buf` (its metadata and, for a new pair, its Q^T were taken
@@ -369,6 +404,7 @@ hipError_t launch16_r(const SegParams &p, hipStream_t s, int *occupancy) {
 bool decode_mma16_ok(const SegParams &p) {
     const int R = p.gqa * p.n_q;
     if (p.cell_hw != kHW || R < 1 || R > 8 || p.n_head_kv % kHW != 0) return false;
+    if ((int64_t)p.n_seq * (p.n_head_kv / kHW) > kMaxPairs) return false;
     // row lists address the pool with 32-bit buffer offsets
     if (p.rows && (p.n_pool <= 0 || p.n_pool * p.k_s1 >= ((int64_t)1 << 31) || p.n_pool * p.v_s1 >= ((int64_t)1 << 31) ||
                    p.k_s1 >= (1 << 24) || p.v_s1 >= (1 << 24)))

@@ -27,6 +27,9 @@ struct SegParams {
     const int32_t *rows;
     int64_t rows_s;
     int64_t n_pool;    // row lists: cells of the pool the rows index
+    // row lists (optional, device): per sequence, kRowExtentParts values whose maximum is 1 +
+    // the last list index holding a pool row
+    const int32_t *row_extent;
     // optional additive binary16 mask: element strides of query i and sequence b;
     // column = pos0 + j (global key position)
     const _Float16 *mask;
@@ -86,6 +89,11 @@ hipError_t launch_merge(const float *partials, int n_seg, int64_t n_rows, float 
                         float *lse, float *partial_out, hipStream_t s);
 // Writes (M=-inf, S=0, VKQ=0) for n_rows rows into partial slot 0.
 hipError_t launch_empty_partials(float *partials, int64_t n_rows, hipStream_t s);
+// Row-list extents in kRowExtentParts pieces per sequence: the maximum of
+// extent[b * kRowExtentParts + 0 .. kRowExtentParts - 1] is 1 + the last index j < n_kv with
+// rows[j + rows_s*b] >= 0, or 0 (n_seq sequences)
+constexpr int kRowExtentParts = 16;
+hipError_t launch_row_extent(const int32_t *rows, int64_t rows_s, int64_t n_kv, int n_seq, int32_t *extent, hipStream_t s);
 hipError_t launch_uva_read(const void *host_src, void *dst, int64_t nbytes, hipStream_t s);
 hipError_t launch_dequant_rows(const void *src, int type, int64_t n_rows, int64_t row_stride,
                                float *dst, hipStream_t s);

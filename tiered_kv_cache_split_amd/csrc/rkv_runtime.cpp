@@ -171,6 +171,8 @@ struct rkv_ctx {
     int n_slots = 2;
     float *partials = nullptr;
     size_t partials_cap = 0;  // floats
+    int32_t *row_extent = nullptr;  // row lists: per-sequence extents for the persistent kernel
+    size_t row_extent_cap = 0;      // bytes
     int lift_mode = RKV_LIFT_BULK;
     int splits_override = 0;
     rkv_stats stats = {};
@@ -652,6 +654,7 @@ void rkv_destroy(rkv_ctx *c) {
     }
     if (c->entry) (void)hipEventDestroy(c->entry);
     if (c->partials) (void)hipFree(c->partials);
+    if (c->row_extent) (void)hipFree(c->row_extent);
     if (c->copy_stream) (void)hipStreamDestroy(c->copy_stream);
     (void)hipGetLastError();
     delete c;
@@ -669,7 +672,13 @@ int rkv_reserve(rkv_ctx *ctx, int64_t max_tile_bytes_k, int64_t max_tile_bytes_v
         if (max_tile_bytes_k > 0 && (st = grow(&ctx->scr_k[sl], &ctx->cap_k[sl], (size_t)max_tile_bytes_k, nullptr))) return st;
         if (max_tile_bytes_v > 0 && (st = grow(&ctx->scr_v[sl], &ctx->cap_v[sl], (size_t)max_tile_bytes_v, nullptr))) return st;
     }
-    if (max_partial_floats > 0 && (st = ensure_partials(ctx, max_partial_floats, nullptr))) return st;
+    if (max_partial_floats > 0) {
+        if ((st = ensure_partials(ctx, max_partial_floats, nullptr))) return st;
+        void *buf = ctx->row_extent;  // row-list extents (up to 1024 sequences)
+        st = grow(&buf, &ctx->row_extent_cap, 1024 * kRowExtentParts * sizeof(int32_t), nullptr);
+        ctx->row_extent = static_cast<int32_t *>(buf);
+        if (st) return st;
+    }
     return RKV_OK;
 }
 
@@ -804,11 +813,25 @@ int rkv_attn_rows(rkv_ctx *ctx, const rkv_tensor *q, const rkv_tensor *k_pool, c
     p.n_rows = n_head * n_q * n_seq;
     const Seg pool{static_cast<const uint8_t *>(k_pool->data), static_cast<const uint8_t *>(v_pool->data),
                    k_pool->nb[1], k_pool->nb[2], v_pool->nb[1], v_pool->nb[2], n_kv, 0};
-    const int slots = plan_segment(ctx, p, pool, false, k_pool->type, v_pool->type).n_splits;
+    const SegPlan plan = plan_segment(ctx, p, pool, false, k_pool->type, v_pool->type);
+    const int slots = plan.n_splits;
     if ((st = ensure_partials(ctx, (int64_t)slots * p.n_rows * kPartialStride, stream))) return st;
     p.partials = ctx->partials;
     ctx->stats = rkv_stats{};
     int slot = 0;
+    SegParams pk = p;
+    pk.cell_hw = plan.cell_hw;
+    if (n_kv > 0 && decode_kernel_persistent(pk, k_pool->type, v_pool->type)) {
+        // the persistent kernel counts each list up to its last pool row
+        void *buf = ctx->row_extent;
+        st = grow(&buf, &ctx->row_extent_cap, std::max<size_t>(1024, (size_t)n_seq) * kRowExtentParts * sizeof(int32_t),
+                  stream);
+        ctx->row_extent = static_cast<int32_t *>(buf);
+        if (st) return st;
+        hipError_t e1 = launch_row_extent(kv_rows, n_kv, n_kv, (int)n_seq, ctx->row_extent, stream);
+        if (e1 != hipSuccess) return hip_fail(e1, "row extent launch");
+        p.row_extent = ctx->row_extent;
+    }
     if (n_kv > 0) {
         if ((st = run_segment(ctx, p, pool, false, k_pool->type, v_pool->type, slot, stream))) return st;
     } else {
