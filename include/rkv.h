@@ -97,7 +97,9 @@ enum rkv_kernel_variant {
     RKV_KERNEL_DECODE_HEAD = 0,       /* vector decode, one KV head per workgroup (any layout, rows) */
     RKV_KERNEL_PREFILL_MFMA = 1,      /* matrix-core prefill over 256-row query tiles                */
     RKV_KERNEL_DECODE_CELL = 2,       /* vector decode over cell-major groups of KV heads           */
-    RKV_KERNEL_DECODE_CELL_MFMA = 3   /* matrix-core decode over eight cell-major KV heads          */
+    RKV_KERNEL_DECODE_CELL_MFMA = 3,  /* matrix-core decode over eight cell-major q8_0/q4_0 heads   */
+    RKV_KERNEL_DECODE_CELL_MFMA16 = 4 /* persistent matrix-core decode over eight binary16 heads
+                                         (windows, tail tiles, row lists)                          */
 };
 
 /* ---- context ---------------------------------------------------------------------- */

@@ -305,7 +305,7 @@ def test_f16_matrix_core_window_and_tail(run, tail):
     mask = gen.random_mask_f16(rng, 1, w["n_kv"], p_hidden=0.2)
     step(f"decode f16 32/8 heads window 2048 + {tail} tail, mask")
     O, L = run.decode(w, wc=2000, tile_kv=700, tail=tail, mask=mask)
-    assert run.ctx.stats()["kernel_variant"] == 3
+    assert run.ctx.stats()["kernel_variant"] == 4
     Oref, Lref = oracle_decode(w, mask=mask)
     assert_close(O, L, Oref, Lref, what=f"f16 mfma {tail}")
 
@@ -324,7 +324,7 @@ def test_f16_matrix_core_partial_causal(run):
     run.ctx.attn_partial(rkv.q_desc(qd), rkv.kv_desc(kd, w["k_type"]), rkv.kv_desc(vd, w["v_type"]), None, 100,
                          q_pos0, w["scale"], part)
     torch.cuda.synchronize()
-    assert run.ctx.stats()["kernel_variant"] == 3
+    assert run.ctx.stats()["kernel_variant"] == 4
     P = part.cpu().numpy().astype(np.float64)
     qv = oracle.q_values(w["q"])
     kv = oracle.kv_values(w["k_type"], w["k"][seg])

@@ -17,7 +17,7 @@ def test_rows_config4_scaled(run):
     w = gen.make_workload(4, scale_down=16)  # pool 4096, lists 512/768/1280/1920 padded to 1920
     step("rows f16 pool=4096 4 seqs padded, mask given")
     O, L = run.rows(w)
-    assert run.ctx.stats()["kernel_variant"] == 3  # binary16 matrix-core cell-major kernel
+    assert run.ctx.stats()["kernel_variant"] == 4  # binary16 matrix-core cell-major kernel
     Oref, Lref = oracle_rows(w)
     assert_close(O, L, Oref, Lref, what="rows")
 
@@ -38,7 +38,7 @@ def test_rows_f16_matrix_core_shapes(run, n_head, n_head_kv, n_q):
              scale=1 / np.sqrt(128))
     step(f"rows f16 heads {n_head}/{n_head_kv} n_q={n_q} lists {lengths}")
     O, L = run.rows(w)
-    assert run.ctx.stats()["kernel_variant"] == 3
+    assert run.ctx.stats()["kernel_variant"] == 4
     Oref, Lref = oracle_rows(w)
     assert_close(O, L, Oref, Lref, what="rows f16 mfma")
 

@@ -791,7 +791,7 @@ int decode_kernel_variant(const SegParams &p, int k_type, int v_type) {
 #ifndef RKV_DECODE_VALU_CELL
     if (k_type == T_Q8_0 && v_type == T_Q4_0 && decode_mma_ok(p)) return RKV_KERNEL_DECODE_CELL_MFMA;
 #endif
-    if (k_type == T_F16 && v_type == T_F16 && decode_mma16_ok(p)) return RKV_KERNEL_DECODE_CELL_MFMA;
+    if (k_type == T_F16 && v_type == T_F16 && decode_mma16_ok(p)) return RKV_KERNEL_DECODE_CELL_MFMA16;
     return RKV_KERNEL_DECODE_CELL;
 }
 

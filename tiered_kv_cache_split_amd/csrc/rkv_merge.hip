@@ -18,6 +18,78 @@ constexpr int kMergeThreads = 1024;
 constexpr int kMergeGroups = kMergeThreads / 32;
 constexpr int kMergeTile = 2048;  // segment weights held in LDS per pass
 
+// Up to kMergeGroups * kMergeOnePass segments: every load of a thread (its segments' M, S and
+// four head_dim values each) is issued at once, so the merge costs one memory latency.
+constexpr int kMergeOnePass = 8;
+
+__global__ void __launch_bounds__(kMergeThreads) merge_one_pass_kernel(const float *__restrict__ part, int n_seg,
+                                                                       int64_t n_rows, float *__restrict__ o,
+                                                                       float *__restrict__ lse,
+                                                                       float *__restrict__ pout) {
+    __shared__ float s_red[kMergeThreads / 64];
+    __shared__ float s_acc[kMergeGroups][kHeadDim];
+    const int64_t row = blockIdx.x;
+    const int tid = threadIdx.x, q = tid & 31, grp = tid >> 5;  // lane q holds head_dim q + 32m
+    const int64_t step = n_rows * kPartialStride;
+    const float *base = part + row * kPartialStride;
+    float Ms[kMergeOnePass], Ss[kMergeOnePass], v[kMergeOnePass][4];
+#pragma unroll
+    for (int i = 0; i < kMergeOnePass; ++i) {
+        const int j = grp + kMergeGroups * i;
+        const float *pp = base + (int64_t)min(j, n_seg - 1) * step;
+        Ms[i] = j < n_seg ? pp[0] : -INFINITY;
+        Ss[i] = pp[1];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) v[i][m] = pp[2 + q + 32 * m];
+    }
+    float M = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < kMergeOnePass; ++i) M = fmaxf(M, Ms[i]);
+    M = wave_max(M);
+    if ((tid & 63) == 0) s_red[tid >> 6] = M;
+    __syncthreads();
+    M = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < kMergeThreads / 64; ++k) M = fmaxf(M, s_red[k]);
+    __syncthreads();
+    float S = 0.f, acc[4] = {0.f, 0.f, 0.f, 0.f};
+    if (M != -INFINITY) {
+#pragma unroll
+        for (int i = 0; i < kMergeOnePass; ++i) {
+            const float w = (Ms[i] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((Ms[i] - M) * kLog2e);
+            S = fmaf(Ss[i], w, S);
+#pragma unroll
+            for (int m = 0; m < 4; ++m) acc[m] = fmaf(v[i][m], w, acc[m]);
+        }
+    }
+    // S: each segment once (lane 0 of its group); acc folded over the groups
+    S = wave_sum(q == 0 ? S : 0.f);
+    if ((tid & 63) == 0) s_red[tid >> 6] = S;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) s_acc[grp][q + 32 * m] = acc[m];
+    __syncthreads();
+    if (tid >= kHeadDim) return;
+    const int d = tid;
+    S = 0.f;
+#pragma unroll
+    for (int k = 0; k < kMergeThreads / 64; ++k) S += s_red[k];
+    float a = 0.f;
+#pragma unroll
+    for (int k = 0; k < kMergeGroups; ++k) a += s_acc[k][d];
+    if (pout) {
+        float *dst = pout + row * kPartialStride;
+        if (d == 0) {
+            dst[0] = M;
+            dst[1] = S;
+        }
+        dst[2 + d] = a;
+        return;
+    }
+    const bool ok = (M != -INFINITY) && (S > 0.f);
+    o[row * kHeadDim + d] = ok ? a / S : 0.f;
+    if (lse && d == 0) lse[row] = ok ? M + logf(S) : -INFINITY;
+}
+
 __global__ void __launch_bounds__(kMergeThreads) merge_kernel(const float *__restrict__ part, int n_seg,
                                                               int64_t n_rows, float *__restrict__ o,
                                                               float *__restrict__ lse,
@@ -162,6 +234,9 @@ hipError_t launch_merge(const float *partials, int n_seg, int64_t n_rows, float 
         // enough rows to fill the chip one wave each (or too few segments to share a row)
         hipLaunchKernelGGL(merge_rows_kernel, dim3((unsigned)((n_rows + kMergeRowsPerBlock - 1) / kMergeRowsPerBlock)),
                            dim3(64 * kMergeRowsPerBlock), 0, s, partials, n_seg, n_rows, o, lse, partial_out);
+    } else if (n_seg <= kMergeGroups * kMergeOnePass) {
+        hipLaunchKernelGGL(merge_one_pass_kernel, dim3((unsigned)n_rows), dim3(kMergeThreads), 0, s, partials, n_seg,
+                           n_rows, o, lse, partial_out);
     } else {
         hipLaunchKernelGGL(merge_kernel, dim3((unsigned)n_rows), dim3(kMergeThreads), 0, s, partials, n_seg, n_rows,
                            o, lse, partial_out);
