@@ -714,9 +714,7 @@ template <int KT, int VT, int R>
 hipError_t launch_decode_r(const SegParams &p, hipStream_t s, int *occupancy) {
     if (p.cell_hw > 0) {
         if constexpr (KT == T_Q8_0 && VT == T_Q4_0) {
-#ifndef RKV_DECODE_VALU_CELL
             if (decode_mma_ok(p)) return launch_decode_mma(p, s, occupancy);
-#endif
             if (p.cell_hw == 8) return launch_cell<KT, VT, R, 8>(p, s, occupancy);
             if (p.cell_hw == 4) return launch_cell<KT, VT, R, 4>(p, s, occupancy);
             if (p.cell_hw == 2) return launch_cell<KT, VT, R, 2>(p, s, occupancy);
@@ -788,9 +786,7 @@ bool decode_kernel_persistent(const SegParams &p, int k_type, int v_type) {
 
 int decode_kernel_variant(const SegParams &p, int k_type, int v_type) {
     if (p.cell_hw <= 0) return RKV_KERNEL_DECODE_HEAD;
-#ifndef RKV_DECODE_VALU_CELL
     if (k_type == T_Q8_0 && v_type == T_Q4_0 && decode_mma_ok(p)) return RKV_KERNEL_DECODE_CELL_MFMA;
-#endif
     if (k_type == T_F16 && v_type == T_F16 && decode_mma16_ok(p)) return RKV_KERNEL_DECODE_CELL_MFMA16;
     return RKV_KERNEL_DECODE_CELL;
 }
