@@ -1,0 +1,99 @@
+"""Randomised GPU parity sweep: seeded random shapes, types, layouts, splits, tails, masks and
+row lists through every entry point, each case against the fp64 oracle.  The cases are small
+(the oracle runs them in well under a second) and cover combinations the targeted tests do
+not enumerate: every kernel family is reached (vector, matrix-core q8_0/q4_0, matrix-core
+binary16 window/tail/rows, prefill), with ragged lengths throughout."""
+import numpy as np
+import pytest
+
+import oracle
+import rkv_inputs as gen
+from rkv_testutil import Runner, assert_close, oracle_decode, oracle_rows, step
+
+pytestmark = pytest.mark.gpu
+
+TYPES = [(gen.TYPE_F16, gen.TYPE_F16), (gen.TYPE_Q8_0, gen.TYPE_Q4_0), (gen.TYPE_Q8_0, gen.TYPE_F16),
+         (gen.TYPE_F16, gen.TYPE_Q4_0)]
+
+
+@pytest.fixture(scope="module")
+def run():
+    return Runner()
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_decode(run, seed):
+    rng = np.random.default_rng(1000 + seed)
+    n_head_kv = int(rng.choice([1, 2, 4, 8, 8, 16]))
+    gqa = int(rng.choice([1, 2, 3, 4, 5, 8]))
+    n_q = int(rng.choice([1, 1, 2]))
+    n_kv = int(rng.integers(1, 2500))
+    kt, vt = TYPES[int(rng.integers(0, 4))]
+    tail = str(rng.choice(["host", "device", "none"]))
+    wc = n_kv if tail == "none" else int(rng.integers(0, n_kv + 1))
+    if wc == n_kv:
+        tail = "none"
+    tile = int(rng.integers(1, 1500))
+    layout = str(rng.choice(["cell", "cell", "head"]))
+    q, k, v = gen.draw_qkv(rng, n_head_kv * gqa, n_q, n_head_kv, n_kv, k_type=kt, v_type=vt)
+    w = dict(n_head=n_head_kv * gqa, n_head_kv=n_head_kv, q=q, k=k, v=v, k_type=kt, v_type=vt,
+             scale=1 / np.sqrt(128), n_kv=n_kv, wc=wc, tile_kv=tile)
+    mask = gen.random_mask_f16(rng, n_q, n_kv, p_hidden=0.3) if rng.random() < 0.5 else None
+    step(f"random decode seed {seed}: heads {n_head_kv}x{gqa} n_q {n_q} n_kv {n_kv} wc {wc} tile {tile} "
+         f"types {kt}/{vt} tail {tail} layout {layout} mask {mask is not None}")
+    O, L = run.decode(w, tail=None if tail == "none" else tail, mask=mask, layout=layout)
+    Oref, Lref = oracle_decode(w, mask=mask)
+    assert_close(O, L, Oref, Lref, what=f"random decode {seed}")
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_rows(run, seed):
+    rng = np.random.default_rng(2000 + seed)
+    n_head_kv = int(rng.choice([1, 2, 8, 8, 16]))
+    gqa = int(rng.choice([1, 2, 4, 8]))
+    n_q = 1 if gqa == 8 else int(rng.choice([1, 2]))
+    n_seq = int(rng.integers(1, 5))
+    n_pool = int(rng.integers(50, 2000))
+    kt, vt = TYPES[0] if rng.random() < 0.6 else TYPES[int(rng.integers(1, 4))]
+    lengths = tuple(int(x) for x in rng.integers(0, 1200, size=n_seq))
+    n_kv = max(1, max(lengths))
+    rows = gen.rows_lists(rng, n_pool, lengths, n_kv, shuffle=bool(rng.random() < 0.5))
+    if rng.random() < 0.5:  # holes inside the lists
+        rows[rng.random(rows.shape) < 0.2] = -1
+    q = gen.draw_normal(rng, (n_seq, n_head_kv * gqa, n_q, 128)).astype(np.float16)
+    k = gen.pack(kt, gen.draw_normal(rng, (n_pool, n_head_kv, 128)))
+    v = gen.pack(vt, gen.draw_normal(rng, (n_pool, n_head_kv, 128)))
+    mask = None
+    if rng.random() < 0.5:
+        mask = np.stack([gen.random_mask_f16(rng, n_q, n_kv, p_hidden=0.2) for _ in range(n_seq)])[:, None]
+    w = dict(q=q, k=k, v=v, kv_rows=rows, mask=mask, k_type=kt, v_type=vt, scale=1 / np.sqrt(128))
+    step(f"random rows seed {seed}: heads {n_head_kv}x{gqa} n_q {n_q} seqs {lengths} pool {n_pool} "
+         f"types {kt}/{vt} mask {mask is not None}")
+    O, L = run.rows(w)  # the mask (or None) travels in w
+    Oref, Lref = oracle_rows(w)
+    assert_close(O, L, Oref, Lref, what=f"random rows {seed}")
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_random_prefill(run, seed):
+    rng = np.random.default_rng(3000 + seed)
+    n_head_kv = int(rng.choice([1, 2, 8]))
+    gqa = int(rng.choice([1, 4, 5]))
+    n_q = int(rng.integers(2, 200))
+    n_kv = int(rng.integers(n_q, 2200))
+    kt, vt = TYPES[int(rng.integers(0, 4))]
+    wc = int(rng.integers(0, n_kv + 1))
+    tile = int(rng.integers(1, 1200))
+    q, k, v = gen.draw_qkv(rng, n_head_kv * gqa, n_q, n_head_kv, n_kv, k_type=kt, v_type=vt)
+    w = dict(n_head=n_head_kv * gqa, n_head_kv=n_head_kv, q=q, k=k, v=v, k_type=kt, v_type=vt,
+             scale=1 / np.sqrt(128), n_kv=n_kv, wc=wc, tile_kv=tile)
+    q_pos0 = n_kv - n_q if rng.random() < 0.7 else int(rng.integers(0, n_kv - n_q + 1))
+    mask = gen.random_mask_f16(rng, n_q, n_kv, p_hidden=0.2) if rng.random() < 0.3 else None
+    step(f"random prefill seed {seed}: heads {n_head_kv}x{gqa} n_q {n_q} n_kv {n_kv} wc {wc} tile {tile} "
+         f"types {kt}/{vt} q_pos0 {q_pos0} mask {mask is not None}")
+    O, L = run.decode(w, prefill=True, q_pos0=q_pos0, tail="host" if wc < n_kv else None, mask=mask)
+    m = oracle.causal_mask(n_q, n_kv, q_pos0)
+    if mask is not None:
+        m = m + np.asarray(mask, dtype=np.float64)
+    Oref, Lref = oracle_decode(w, mask=m)
+    assert_close(O, L, Oref, Lref, what=f"random prefill {seed}")
