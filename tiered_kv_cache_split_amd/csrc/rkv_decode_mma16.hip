@@ -150,17 +150,15 @@ decode_mma16_kernel(const SegParams p) {
     };
 
     // ---- task k of this workgroup: its pair and first cell (k past the end: a phantom task
-    // of the last pair with no keys)
-    auto task = [&](uint32_t k, int &pair, int64_t &c0) __attribute__((always_inline)) {
+    // of the last pair with no keys).  Tasks are looked up in increasing order, so a cursor
+    // over the pair offsets moves forward a step at a time (one for the fetches, one for the
+    // row-list lookahead) instead of searching.
+    int cur_f = 0, cur_r = 0, prev_fetch_pair = -1;
+    auto task_at = [&](int &cur, uint32_t k, int &pair, int64_t &c0) __attribute__((always_inline)) {
         const uint32_t t = j + min(k, n_t - 1) * G;
-        int lo = 0, hi = n_pairs - 1;  // the last pair whose first task is <= t (it is not empty)
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (s_off[mid] <= t) lo = mid;
-            else hi = mid - 1;
-        }
-        pair = lo;
-        c0 = (int64_t)(t - s_off[lo]) * kCh;
+        while (cur + 1 < n_pairs && s_off[cur + 1] <= t) ++cur;  // past empty pairs too
+        pair = cur;
+        c0 = (int64_t)(t - s_off[cur]) * kCh;
     };
     // pool rows of the wave's two cells 2*wave, 2*wave + 1 of task k's chunk, as read (always
     // from inside the list), and whether each is a key: entries past the list end (or of a
@@ -169,7 +167,7 @@ decode_mma16_kernel(const SegParams p) {
     auto rows_of = [&](uint32_t k, int2 &raw, int2 &inl) __attribute__((always_inline)) {
         int pair;
         int64_t c0;
-        task(k, pair, c0);
+        task_at(cur_r, k, pair, c0);
         const int32_t *__restrict__ rl = p.rows + (int64_t)(pair / n_hgrp) * p.rows_s;
         const int64_t c = c0 + 2 * wave;
         raw = make_int2(rl[min(c, n_cells - 1)], rl[min(c + 1, n_cells - 1)]);
@@ -181,13 +179,11 @@ decode_mma16_kernel(const SegParams p) {
         const bool real = k < n_t;
         int pair;
         int64_t c0;
-        task(k, pair, c0);
-        int prev_pair = -1;
-        int64_t pc0;
-        if (k > 0) task(k - 1, prev_pair, pc0);
+        task_at(cur_f, k, pair, c0);  // fetches come in task order 0, 1, 2, ...
         st.meta.pair = pair;
         st.meta.c0 = c0;
-        st.meta.newq = real && pair != prev_pair;
+        st.meta.newq = real && pair != prev_fetch_pair;
+        prev_fetch_pair = pair;
         const int bb = pair / n_hgrp, hg = pair % n_hgrp;
         const uint8_t *kbase = p.k + (int64_t)(hg * kHW) * p.k_s2;
         const uint8_t *vbase = p.v + (int64_t)(hg * kHW) * p.v_s2;
