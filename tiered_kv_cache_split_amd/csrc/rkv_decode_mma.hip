@@ -38,6 +38,7 @@ namespace {
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef int int2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kCh = 32;              // cells per chunk
 constexpr float kMagicK = 1152.0f;   // q8_0 code q as binary16 1024 + (q + 128)
@@ -64,29 +65,40 @@ __device__ __forceinline__ float row16_sum(float x) {
     return x;
 }
 
+// One chunk in registers.  K: 16-byte units of the cell rows.  V: the thread's half of one
+// head's q4_0 row (two blocks, 36 bytes as nine words).
 template <int HW>
 struct Stage {
     static constexpr int kNT = 64 * HW;
     static constexpr int kTpc = kNT / kCh;                    // threads per cell
-    static constexpr int kUk = HW * kQ8Row / 16, kUv = HW * kQ4Row / 16;  // 16-byte units per cell
-    static constexpr int kMk = (kUk + kTpc - 1) / kTpc, kMv = (kUv + kTpc - 1) / kTpc;
-    uint4 k[kMk], v[kMv];
+    static constexpr int kUk = HW * kQ8Row / 16;              // 16-byte units per cell
+    static constexpr int kMk = (kUk + kTpc - 1) / kTpc;
+    uint4 k[kMk];
+    uint4 va, vb;
+    uint32_t vc;
 };
 
 template <int R, int HW>
 __global__ void __launch_bounds__(64 * HW) __attribute__((amdgpu_waves_per_eu(2)))
 decode_mma_kernel(const SegParams p) {
     using St = Stage<HW>;
-    constexpr int kCk = HW * kQ8Row, kCv = HW * kQ4Row;     // bytes of one cell (head group)
-    constexpr int kSk = kCk + 8, kSv = kCv + 8;               // LDS cell strides
-    constexpr int kBk = kCh * kSk, kBv = kCh * kSv;           // bytes of one LDS stage
+    constexpr int kCk = HW * kQ8Row;                          // bytes of one K cell (head group)
+    constexpr int kSk = kCk + 8;                              // LDS K cell stride
+    constexpr int kBk = kCh * kSk;                            // bytes of one LDS K stage
+    // LDS V stage: the 16 data bytes of every q4_0 block at a 16-byte slot of its cell (the
+    // first block of each thread's pair in slots 0 .. 2HW-1, the second in 2HW .. 4HW-1), cells
+    // 16 bytes apart plus 64 more from cell 16 on (the transposing reads of 8 keys then meet 8
+    // distinct bank quads), followed by d_V as [head][block][P.V slot of the key]
+    constexpr int kVc = 64 * HW + 16;                         // V cell stride
+    constexpr int kVd = kCh * kVc + 64;                       // data bytes of a V stage
+    constexpr int kVh = 4 * 2 * kCh + 16;                     // d_V bytes per head
+    constexpr int kBv = kVd + HW * kVh;                       // bytes of one LDS V stage
     constexpr int kTpc = St::kTpc;
-    static_assert(St::kNT % kCh == 0 && kCk % 16 == 0 && kCv % 16 == 0, "thread mapping");
+    static_assert(St::kNT % kCh == 0 && kCk % 16 == 0 && kTpc == 2 * HW, "thread mapping");
     static_assert(kCh == 32, "the key permutation of P.V assumes 32-key chunks");
     __shared__ __attribute__((aligned(16))) uint8_t s_k[2 * kBk];
     __shared__ __attribute__((aligned(16))) uint8_t s_v[2 * kBv];
     __shared__ __attribute__((aligned(16))) _Float16 s_dk[HW][4 * kCh];  // d_K[block][key] per wave
-    __shared__ __attribute__((aligned(16))) _Float16 s_dv[HW][4 * kCh];  // d_V[block][slot(key)] per wave
 
     const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int col = lane & 15, grp = lane >> 4;
@@ -102,13 +114,17 @@ decode_mma_kernel(const SegParams p) {
     const uint8_t *kbase = p.k + (int64_t)(hgrp * HW) * p.k_s2;
     const uint8_t *vbase = p.v + (int64_t)(hgrp * HW) * p.v_s2;
 
-    // ---- chunk fetch (registers) and staging (LDS, padded cells).  Thread t moves the 16-byte
-    // units sub, sub + kTpc, ... of cell t / kTpc (sub = t % kTpc), so consecutive threads cover
-    // contiguous bytes of a cell and every offset is a per-thread base plus an immediate.  Cells
-    // past the segment end lie outside the buffer resource's range and read as zero.
+    // ---- chunk fetch (registers) and staging (LDS).  Thread t works on cell t / kTpc (sub =
+    // t % kTpc): K units sub, sub + kTpc, ... (consecutive threads cover contiguous bytes and
+    // every offset is a per-thread base plus an immediate) and V bytes 36 sub .. 36 sub + 35 of
+    // the cell, i.e. blocks 2 (sub % 2) and + 1 of head sub / 2.  Cells past the segment end lie
+    // outside the buffer resource's range and read as zero.
     const int fcell = tid / kTpc, fsub = tid % kTpc;
-    const int gkb = fcell * (int)p.k_s1 + 16 * fsub, gvb = fcell * (int)p.v_s1 + 16 * fsub;
-    const int lkb = fcell * kSk + 16 * fsub, lvb = fcell * kSv + 16 * fsub;
+    const int gkb = fcell * (int)p.k_s1 + 16 * fsub, gvb = fcell * (int)p.v_s1 + 36 * fsub;
+    const int lkb = fcell * kSk + 16 * fsub;
+    const int lvb = fcell * kVc + 64 * ((fcell >> 4) & 1) + 16 * fsub;
+    const int lvs = kVd + (fsub >> 1) * kVh + 2 * (fsub & 1) * (2 * kCh) +
+                    2 * (8 * ((fcell >> 2) & 3) + 4 * (fcell >> 4) + (fcell & 3));
     auto fetch = [&](St &st, int64_t c0) __attribute__((always_inline)) {
         const int64_t nv = max((int64_t)0, min((int64_t)kCh, c_end - c0));
         const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
@@ -119,10 +135,9 @@ decode_mma_kernel(const SegParams p) {
         for (int m = 0; m < St::kMk; ++m)
             if (kTpc * (m + 1) <= St::kUk || fsub + kTpc * m < St::kUk)
                 st.k[m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, gkb + 16 * kTpc * m, 0, 0));
-#pragma unroll
-        for (int m = 0; m < St::kMv; ++m)
-            if (kTpc * (m + 1) <= St::kUv || fsub + kTpc * m < St::kUv)
-                st.v[m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, gvb + 16 * kTpc * m, 0, 0));
+        st.va = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, gvb, 0, 0));
+        st.vb = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, gvb + 16, 0, 0));
+        st.vc = __builtin_amdgcn_raw_buffer_load_b32(rv, gvb + 32, 0, 0);
     };
     auto stash = [&](const St &st, int buf) __attribute__((always_inline)) {
 #pragma unroll
@@ -132,13 +147,15 @@ decode_mma_kernel(const SegParams p) {
                 d[0] = make_uint2(st.k[m].x, st.k[m].y);
                 d[1] = make_uint2(st.k[m].z, st.k[m].w);
             }
-#pragma unroll
-        for (int m = 0; m < St::kMv; ++m)
-            if (kTpc * (m + 1) <= St::kUv || fsub + kTpc * m < St::kUv) {
-                uint2 *d = reinterpret_cast<uint2 *>(s_v + buf * kBv + lvb + 16 * kTpc * m);
-                d[0] = make_uint2(st.v[m].x, st.v[m].y);
-                d[1] = make_uint2(st.v[m].z, st.v[m].w);
-            }
+        // V: the first block's data starts 2 bytes into the words, the second's is aligned
+        uint8_t *vd = s_v + buf * kBv;
+        *reinterpret_cast<uint4 *>(vd + lvb) = make_uint4(__builtin_amdgcn_alignbyte(st.va.y, st.va.x, 2),
+                                                          __builtin_amdgcn_alignbyte(st.va.z, st.va.y, 2),
+                                                          __builtin_amdgcn_alignbyte(st.va.w, st.va.z, 2),
+                                                          __builtin_amdgcn_alignbyte(st.vb.x, st.va.w, 2));
+        *reinterpret_cast<uint4 *>(vd + lvb + 16 * kTpc) = make_uint4(st.vb.y, st.vb.z, st.vb.w, st.vc);
+        *reinterpret_cast<uint16_t *>(vd + lvs) = (uint16_t)st.va.x;
+        *reinterpret_cast<uint16_t *>(vd + lvs + 2 * kCh) = (uint16_t)(st.vb.x >> 16);
     };
 
     // Lane (col, grp) owns query row `col` (rows >= R are padding and never written) and, within
@@ -159,7 +176,10 @@ decode_mma_kernel(const SegParams p) {
     asm volatile("" : "+v"(vmagic));
     const float c = p.scale_log2;
     _Float16 *dkw = s_dk[wave];
-    _Float16 *dvw = s_dv[wave];
+    // transposing V reads: lane col of 16-lane group grp reads 8 bytes (half col % 2) of the key
+    // in P.V slot 8 grp + col / 2; it receives byte col of the 8 keys of its slots
+    const int vkey = 4 * grp + ((col >> 1) & 3) + 16 * (col >> 3);
+    const int vrd = vkey * kVc + 64 * ((vkey >> 4) & 1) + 8 * (col & 1);
     const int64_t n_ch = (c_end > c_beg) ? (c_end - c_beg + kCh - 1) / kCh : 0;
     const int qi_row = min(col, R - 1) / p.gqa;  // query position of this lane's row
 
@@ -192,19 +212,16 @@ decode_mma_kernel(const SegParams p) {
     // ---- one chunk from LDS stage `buf`
     auto compute = [&](int buf, int64_t c0) __attribute__((always_inline)) {
         const uint8_t *kw = s_k + buf * kBk + wave * kQ8Row;  // this head's K row of cell j at kw + j*kSk
-        const uint8_t *vw = s_v + buf * kBv + wave * kQ4Row;
+        const uint8_t *vs = s_v + buf * kBv;
 
-        // block scales of the chunk: d_K as [block][key], d_V as [block][slot] with the key of P.V
-        // slot 8*gg + jj being 4*gg + jj (jj < 4) or 16 + 4*gg + jj - 4; lane = key (lane % 32),
-        // blocks 2 (lane / 32) + 0, 1
+        // block scales of K as [block][key]; lane = key (lane % 32), blocks 2 (lane / 32) + 0, 1.
+        // (d_V is staged in P.V slot order: the key of slot 8*gg + jj is 4*gg + jj (jj < 4) or
+        // 16 + 4*gg + jj - 4.)
         {
             const int key = lane & (kCh - 1), bb = 2 * (lane / kCh);
-            const int slot = 8 * ((key >> 2) & 3) + 4 * (key >> 4) + (key & 3);
 #pragma unroll
-            for (int u = 0; u < 2; ++u) {
+            for (int u = 0; u < 2; ++u)
                 dkw[(bb + u) * kCh + key] = __builtin_bit_cast(_Float16, (uint16_t)ld_u16(kw + key * kSk + kQ8Block * (bb + u)));
-                dvw[(bb + u) * kCh + slot] = __builtin_bit_cast(_Float16, (uint16_t)ld_u16(vw + key * kSv + kQ4Block * (bb + u)));
-            }
         }
 
         // ---- Q.K on the matrix cores: A = K (16 keys x 32 head_dim of one q8_0 block, codes as
@@ -315,7 +332,7 @@ decode_mma_kernel(const SegParams p) {
         // of the block: element col as the low nibble, element col + 16 as the high one)
 #pragma unroll
         for (int blk = 0; blk < 4; ++blk) {
-            const uint4 dv = *reinterpret_cast<const uint4 *>(dvw + blk * kCh + 8 * grp);
+            const uint4 dv = *reinterpret_cast<const uint4 *>(vs + kVd + wave * kVh + blk * (2 * kCh) + 16 * grp);
             const uint4 wu = make_uint4(u32v(pk[0] * h2v(dv.x)), u32v(pk[1] * h2v(dv.y)),
                                         u32v(pk[2] * h2v(dv.z)), u32v(pk[3] * h2v(dv.w)));
             const half8_t wf = __builtin_bit_cast(half8_t, wu);
@@ -323,14 +340,15 @@ decode_mma_kernel(const SegParams p) {
             swacc[blk] = __builtin_amdgcn_fdot2(h2v(wu.y), ones, swacc[blk], false);
             swacc[blk] = __builtin_amdgcn_fdot2(h2v(wu.z), ones, swacc[blk], false);
             swacc[blk] = __builtin_amdgcn_fdot2(h2v(wu.w), ones, swacc[blk], false);
-            const uint8_t *vb0 = vw + (4 * grp) * kSv + kQ4Block * blk + 2 + col;
-            uint32_t bt[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) bt[j] = vb0[((j & 3) + 16 * (j >> 2)) * kSv];
+            // block blk of head `wave` is slot 2*wave + blk/2 (+ 2HW for odd blk) of a cell
+            const int vslot = 2 * wave + (blk >> 1) + 2 * HW * (blk & 1);
+            const int2_t bt = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                (__attribute__((address_space(3))) int2_t *)(vs + vrd + 16 * vslot));
             uint32_t lo[4], hi[4];
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
-                const uint32_t y = __builtin_amdgcn_perm(bt[2 * jj + 1], bt[2 * jj], 0x0C040C00u);  // b0, 0, b1, 0
+                const uint32_t w = (uint32_t)bt[jj >> 1];
+                const uint32_t y = __builtin_amdgcn_perm(w, w, (jj & 1) ? 0x0C030C02u : 0x0C010C00u);  // b0, 0, b1, 0
                 lo[jj] = (y & 0x000F000Fu) | vmagic;  // 1024 + n
                 hi[jj] = (y & 0x00F000F0u) | vmagic;  // 1024 + 16 n: no shift needed
             }
