@@ -65,15 +65,14 @@ __device__ __forceinline__ float row16_sum(float x) {
     return x;
 }
 
-// One chunk in registers.  K: 16-byte units of the cell rows.  V: the thread's half of one
-// head's q4_0 row (two blocks, 36 bytes as nine words).
+// One chunk in registers: the thread's half of one head's q8_0 K row (two blocks, 68 bytes as
+// seventeen words) and of its q4_0 V row (two blocks, 36 bytes as nine words).
 template <int HW>
 struct Stage {
     static constexpr int kNT = 64 * HW;
-    static constexpr int kTpc = kNT / kCh;                    // threads per cell
-    static constexpr int kUk = HW * kQ8Row / 16;              // 16-byte units per cell
-    static constexpr int kMk = (kUk + kTpc - 1) / kTpc;
-    uint4 k[kMk];
+    static constexpr int kTpc = kNT / kCh;  // threads per cell
+    uint4 k[4];
+    uint32_t k4;
     uint4 va, vb;
     uint32_t vc;
 };
@@ -82,9 +81,12 @@ template <int R, int HW>
 __global__ void __launch_bounds__(64 * HW) __attribute__((amdgpu_waves_per_eu(2)))
 decode_mma_kernel(const SegParams p) {
     using St = Stage<HW>;
-    constexpr int kCk = HW * kQ8Row;                          // bytes of one K cell (head group)
-    constexpr int kSk = kCk + 8;                              // LDS K cell stride
-    constexpr int kBk = kCh * kSk;                            // bytes of one LDS K stage
+    // LDS K stage: two planes (code bytes 0..15 and 16..31 of every q8_0 block), each with the
+    // block's 16 bytes at a slot of its cell numbered as in V below, then d_K as [head][block][key]
+    constexpr int kKc = 64 * HW + 16;                         // K plane cell stride: 4HW slots + 16 bytes
+    constexpr int kKp = kCh * kKc;                            // bytes of one K plane
+    constexpr int kKh = 4 * 2 * kCh + 16;                     // d_K bytes per head
+    constexpr int kBk = 2 * kKp + HW * kKh;                   // bytes of one LDS K stage
     // LDS V stage: the 16 data bytes of every q4_0 block at a 16-byte slot of its cell (the
     // first block of each thread's pair in slots 0 .. 2HW-1, the second in 2HW .. 4HW-1), cells
     // 16 bytes apart plus 64 more from cell 16 on (the transposing reads of 8 keys then meet 8
@@ -94,11 +96,10 @@ decode_mma_kernel(const SegParams p) {
     constexpr int kVh = 4 * 2 * kCh + 16;                     // d_V bytes per head
     constexpr int kBv = kVd + HW * kVh;                       // bytes of one LDS V stage
     constexpr int kTpc = St::kTpc;
-    static_assert(St::kNT % kCh == 0 && kCk % 16 == 0 && kTpc == 2 * HW, "thread mapping");
+    static_assert(St::kNT % kCh == 0 && kTpc == 2 * HW, "thread mapping");
     static_assert(kCh == 32, "the key permutation of P.V assumes 32-key chunks");
     __shared__ __attribute__((aligned(16))) uint8_t s_k[2 * kBk];
     __shared__ __attribute__((aligned(16))) uint8_t s_v[2 * kBv];
-    __shared__ __attribute__((aligned(16))) _Float16 s_dk[HW][4 * kCh];  // d_K[block][key] per wave
 
     const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int col = lane & 15, grp = lane >> 4;
@@ -115,13 +116,15 @@ decode_mma_kernel(const SegParams p) {
     const uint8_t *vbase = p.v + (int64_t)(hgrp * HW) * p.v_s2;
 
     // ---- chunk fetch (registers) and staging (LDS).  Thread t works on cell t / kTpc (sub =
-    // t % kTpc): K units sub, sub + kTpc, ... (consecutive threads cover contiguous bytes and
-    // every offset is a per-thread base plus an immediate) and V bytes 36 sub .. 36 sub + 35 of
-    // the cell, i.e. blocks 2 (sub % 2) and + 1 of head sub / 2.  Cells past the segment end lie
-    // outside the buffer resource's range and read as zero.
+    // t % kTpc) and takes blocks 2 (sub % 2) and + 1 of head sub / 2 from both caches: K bytes
+    // 68 sub .. 68 sub + 67 and V bytes 36 sub .. 36 sub + 35 of the cell (word aligned, so
+    // consecutive threads cover contiguous bytes).  Staging splits the scales from the block
+    // data and puts the data on 16-byte slots.  Cells past the segment end lie outside the
+    // buffer resource's range and read as zero.
     const int fcell = tid / kTpc, fsub = tid % kTpc;
-    const int gkb = fcell * (int)p.k_s1 + 16 * fsub, gvb = fcell * (int)p.v_s1 + 36 * fsub;
-    const int lkb = fcell * kSk + 16 * fsub;
+    const int gkb = fcell * (int)p.k_s1 + 68 * fsub, gvb = fcell * (int)p.v_s1 + 36 * fsub;
+    const int lkb = fcell * kKc + 16 * fsub;
+    const int lks = 2 * kKp + (fsub >> 1) * kKh + 2 * (fsub & 1) * (2 * kCh) + 2 * fcell;
     const int lvb = fcell * kVc + 64 * ((fcell >> 4) & 1) + 16 * fsub;
     const int lvs = kVd + (fsub >> 1) * kVh + 2 * (fsub & 1) * (2 * kCh) +
                     2 * (8 * ((fcell >> 2) & 3) + 4 * (fcell >> 4) + (fcell & 3));
@@ -132,21 +135,30 @@ decode_mma_kernel(const SegParams p) {
         const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
             (void *)(vbase + c0 * p.v_s1), (short)0, (int)(nv * p.v_s1), 0x00020000);
 #pragma unroll
-        for (int m = 0; m < St::kMk; ++m)
-            if (kTpc * (m + 1) <= St::kUk || fsub + kTpc * m < St::kUk)
-                st.k[m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, gkb + 16 * kTpc * m, 0, 0));
+        for (int m = 0; m < 4; ++m)
+            st.k[m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, gkb + 16 * m, 0, 0));
+        st.k4 = __builtin_amdgcn_raw_buffer_load_b32(rk, gkb + 64, 0, 0);
         st.va = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, gvb, 0, 0));
         st.vb = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, gvb + 16, 0, 0));
         st.vc = __builtin_amdgcn_raw_buffer_load_b32(rv, gvb + 32, 0, 0);
     };
     auto stash = [&](const St &st, int buf) __attribute__((always_inline)) {
+        // K: words x0 .. x16; the first block's codes start 2 bytes into the words (its scale is
+        // the low half of x0), the second block's scale is the high half of x8 and its codes
+        // x9 .. x16 are aligned
+        const uint32_t x[17] = {st.k[0].x, st.k[0].y, st.k[0].z, st.k[0].w, st.k[1].x, st.k[1].y,
+                                st.k[1].z, st.k[1].w, st.k[2].x, st.k[2].y, st.k[2].z, st.k[2].w,
+                                st.k[3].x, st.k[3].y, st.k[3].z, st.k[3].w, st.k4};
+        uint32_t ca[8];
 #pragma unroll
-        for (int m = 0; m < St::kMk; ++m)
-            if (kTpc * (m + 1) <= St::kUk || fsub + kTpc * m < St::kUk) {
-                uint2 *d = reinterpret_cast<uint2 *>(s_k + buf * kBk + lkb + 16 * kTpc * m);
-                d[0] = make_uint2(st.k[m].x, st.k[m].y);
-                d[1] = make_uint2(st.k[m].z, st.k[m].w);
-            }
+        for (int i = 0; i < 8; ++i) ca[i] = __builtin_amdgcn_alignbyte(x[i + 1], x[i], 2);
+        uint8_t *kd = s_k + buf * kBk;
+        *reinterpret_cast<uint4 *>(kd + lkb) = make_uint4(ca[0], ca[1], ca[2], ca[3]);
+        *reinterpret_cast<uint4 *>(kd + kKp + lkb) = make_uint4(ca[4], ca[5], ca[6], ca[7]);
+        *reinterpret_cast<uint4 *>(kd + lkb + 16 * kTpc) = make_uint4(x[9], x[10], x[11], x[12]);
+        *reinterpret_cast<uint4 *>(kd + kKp + lkb + 16 * kTpc) = make_uint4(x[13], x[14], x[15], x[16]);
+        *reinterpret_cast<uint16_t *>(kd + lks) = (uint16_t)x[0];
+        *reinterpret_cast<uint16_t *>(kd + lks + 2 * kCh) = (uint16_t)(x[8] >> 16);
         // V: the first block's data starts 2 bytes into the words, the second's is aligned
         uint8_t *vd = s_v + buf * kBv;
         *reinterpret_cast<uint4 *>(vd + lvb) = make_uint4(__builtin_amdgcn_alignbyte(st.va.y, st.va.x, 2),
@@ -175,7 +187,6 @@ decode_mma_kernel(const SegParams p) {
     uint32_t vmagic = 0x64006400u;
     asm volatile("" : "+v"(vmagic));
     const float c = p.scale_log2;
-    _Float16 *dkw = s_dk[wave];
     // transposing V reads: lane col of 16-lane group grp reads 8 bytes (half col % 2) of the key
     // in P.V slot 8 grp + col / 2; it receives byte col of the 8 keys of its slots
     const int vkey = 4 * grp + ((col >> 1) & 3) + 16 * (col >> 3);
@@ -211,18 +222,11 @@ decode_mma_kernel(const SegParams p) {
 
     // ---- one chunk from LDS stage `buf`
     auto compute = [&](int buf, int64_t c0) __attribute__((always_inline)) {
-        const uint8_t *kw = s_k + buf * kBk + wave * kQ8Row;  // this head's K row of cell j at kw + j*kSk
+        const uint8_t *ks = s_k + buf * kBk;
         const uint8_t *vs = s_v + buf * kBv;
-
-        // block scales of K as [block][key]; lane = key (lane % 32), blocks 2 (lane / 32) + 0, 1.
+        const uint8_t *dkw = ks + 2 * kKp + wave * kKh;  // d_K[block][key] of this head
         // (d_V is staged in P.V slot order: the key of slot 8*gg + jj is 4*gg + jj (jj < 4) or
         // 16 + 4*gg + jj - 4.)
-        {
-            const int key = lane & (kCh - 1), bb = 2 * (lane / kCh);
-#pragma unroll
-            for (int u = 0; u < 2; ++u)
-                dkw[(bb + u) * kCh + key] = __builtin_bit_cast(_Float16, (uint16_t)ld_u16(kw + key * kSk + kQ8Block * (bb + u)));
-        }
 
         // ---- Q.K on the matrix cores: A = K (16 keys x 32 head_dim of one q8_0 block, codes as
         // binary16 1024 + (q + 128)), B = Q^T; d[ii] = score of key 16*kt + 4*grp + ii for row col
@@ -230,23 +234,14 @@ decode_mma_kernel(const SegParams p) {
         float4_t dq[2][4];
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
-            const uint8_t *kr = kw + (16 * kt + col) * kSk;
+            // codes 8*grp .. 8*grp+7 of the block: plane grp / 2, half grp % 2 of the slot
+            const uint8_t *kr = ks + (grp >> 1) * kKp + (16 * kt + col) * kKc + 8 * (grp & 1);
 #pragma unroll
             for (int blk = 0; blk < 4; ++blk) {
-                const int o = kQ8Block * blk + 2 + 8 * grp;  // codes 8*grp .. 8*grp+7 of the block
-                uint32_t w0, w1;
-                if ((kQ8Block * blk + 2) & 3) {
-                    const uint32_t *pw32 = reinterpret_cast<const uint32_t *>(kr + o - 2);
-                    const uint32_t x0 = pw32[0], x1 = pw32[1], x2 = pw32[2];
-                    w0 = __builtin_amdgcn_alignbyte(x1, x0, 2);
-                    w1 = __builtin_amdgcn_alignbyte(x2, x1, 2);
-                } else {
-                    const uint32_t *pw32 = reinterpret_cast<const uint32_t *>(kr + o);
-                    w0 = pw32[0];
-                    w1 = pw32[1];
-                }
-                w0 ^= 0x80808080u;  // q + 128 per byte
-                w1 ^= 0x80808080u;
+                const int kslot = 2 * wave + (blk >> 1) + 2 * HW * (blk & 1);
+                const uint2 w = *reinterpret_cast<const uint2 *>(kr + 16 * kslot);
+                const uint32_t w0 = w.x ^ 0x80808080u;  // q + 128 per byte
+                const uint32_t w1 = w.y ^ 0x80808080u;
                 const uint4 ak = make_uint4(__builtin_amdgcn_perm(0x64646464u, w0, 0x05010400u),
                                             __builtin_amdgcn_perm(0x64646464u, w0, 0x05030402u),
                                             __builtin_amdgcn_perm(0x64646464u, w1, 0x05010400u),
@@ -255,7 +250,6 @@ decode_mma_kernel(const SegParams p) {
                                                                      cneg[blk], 0, 0, 0);
             }
         }
-        lds_order();  // the block scales are in place
 
         // scores s[kt][ii] = sum over blocks of d_K * d
         float s[2][4];
@@ -265,7 +259,7 @@ decode_mma_kernel(const SegParams p) {
             for (int ii = 0; ii < 4; ++ii) s[kt][ii] = 0.f;
 #pragma unroll
             for (int blk = 0; blk < 4; ++blk) {
-                const uint2 dk2 = *reinterpret_cast<const uint2 *>(dkw + blk * kCh + 16 * kt + 4 * grp);
+                const uint2 dk2 = *reinterpret_cast<const uint2 *>(dkw + blk * (2 * kCh) + 2 * (16 * kt + 4 * grp));
                 const half2_t d01 = h2v(dk2.x), d23 = h2v(dk2.y);
                 s[kt][0] = fmaf((float)d01[0], dq[kt][blk][0], s[kt][0]);
                 s[kt][1] = fmaf((float)d01[1], dq[kt][blk][1], s[kt][1]);
