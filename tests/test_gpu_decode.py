@@ -185,6 +185,35 @@ def test_lse_merge_of_oracle_partials(run):
     assert_close(o.cpu().numpy(), lse.cpu().numpy(), Oref.reshape(n_rows, 128), Lref.reshape(-1), what="merge")
 
 
+@pytest.mark.parametrize("n_seg,n_rows", [(17, 24), (100, 40), (256, 40), (257, 24), (600, 8), (256, 1100)])
+def test_lse_merge_many_segments(run, n_seg, n_rows):
+    """The merge kernels for many segments (one thread per segment and head_dim part, and the
+    tiled one past 256 segments) against the oracle merge, with empty segments (M = -inf,
+    S = 0) scattered in and one row whose segments are all empty."""
+    import torch
+    import tiered_kv_cache_split_amd as rkv
+    rng = np.random.default_rng(1000 + n_seg)
+    M = rng.uniform(-6.0, 6.0, (n_seg, n_rows))
+    S = rng.uniform(0.5, 40.0, (n_seg, n_rows))
+    VKQ = rng.standard_normal((n_seg, n_rows, 128)) * S[..., None]
+    empty = rng.random((n_seg, n_rows)) < 0.2
+    empty[:, 3] = True
+    M[empty] = -np.inf
+    S[empty] = 0.0
+    VKQ[empty] = 0.0
+    P = np.zeros((n_seg, n_rows, 130), np.float32)
+    P[:, :, 0], P[:, :, 1], P[:, :, 2:] = M, S, VKQ
+    parts = [(P[s, :, 0].astype(np.float64)[None], P[s, :, 1].astype(np.float64)[None],
+              P[s, :, 2:].astype(np.float64)[None]) for s in range(n_seg)]
+    Oref, Lref = oracle.merge(parts)
+    o = torch.empty((n_rows, 128), dtype=torch.float32, device="cuda")
+    lse = torch.empty((n_rows,), dtype=torch.float32, device="cuda")
+    step(f"lse merge of {n_seg} synthetic partials x {n_rows} rows")
+    rkv.lse_merge(dev(P), n_seg, n_rows, o, lse)
+    torch.cuda.synchronize()
+    assert_close(o.cpu().numpy(), lse.cpu().numpy(), Oref.reshape(n_rows, 128), Lref.reshape(-1), what="merge")
+
+
 def test_attn_partial_matches_oracle_partial(run):
     import torch
     import tiered_kv_cache_split_amd as rkv

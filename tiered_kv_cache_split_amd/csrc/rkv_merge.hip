@@ -18,76 +18,79 @@ constexpr int kMergeThreads = 1024;
 constexpr int kMergeGroups = kMergeThreads / 32;
 constexpr int kMergeTile = 2048;  // segment weights held in LDS per pass
 
-// Up to kMergeGroups * kMergeOnePass segments: every load of a thread (its segments' M, S and
-// four head_dim values each) is issued at once, so the merge costs one memory latency.
-constexpr int kMergeOnePass = 8;
+// Up to kMergePartThreads segments over few rows: workgroup (row, part) merges head_dim values
+// 16*part .. 16*part+15 of one row with one thread per segment, so every load of the merge is
+// issued at once by kMergeParts times more workgroups than rows and the merge costs one memory
+// latency.  M and S are read by every part (8 bytes per segment).
+constexpr int kMergeParts = 8;
+constexpr int kMergePartDim = kHeadDim / kMergeParts;
+constexpr int kMergePartThreads = 256;
 
-__global__ void __launch_bounds__(kMergeThreads) merge_one_pass_kernel(const float *__restrict__ part, int n_seg,
-                                                                       int64_t n_rows, float *__restrict__ o,
-                                                                       float *__restrict__ lse,
-                                                                       float *__restrict__ pout) {
-    __shared__ float s_red[kMergeThreads / 64];
-    __shared__ float s_acc[kMergeGroups][kHeadDim];
+__global__ void __launch_bounds__(kMergePartThreads) merge_parts_kernel(const float *__restrict__ part, int n_seg,
+                                                                        int64_t n_rows, float *__restrict__ o,
+                                                                        float *__restrict__ lse,
+                                                                        float *__restrict__ pout) {
+    constexpr int kW = kMergePartThreads / 64;
+    __shared__ float s_m[kW];
+    __shared__ float s_acc[kW][kMergePartDim + 1];
     const int64_t row = blockIdx.x;
-    const int tid = threadIdx.x, q = tid & 31, grp = tid >> 5;  // lane q holds head_dim q + 32m
-    const int64_t step = n_rows * kPartialStride;
-    const float *base = part + row * kPartialStride;
-    float Ms[kMergeOnePass], Ss[kMergeOnePass], v[kMergeOnePass][4];
+    const int pt = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const bool has = tid < n_seg;
+    const float *pp = part + ((int64_t)(has ? tid : 0) * n_rows + row) * kPartialStride;
+    float2 ms = make_float2(-INFINITY, 0.f);
+    float v[kMergePartDim];
+    if (has) {
+        ms = *reinterpret_cast<const float2 *>(pp);
 #pragma unroll
-    for (int i = 0; i < kMergeOnePass; ++i) {
-        const int j = grp + kMergeGroups * i;
-        const float *pp = base + (int64_t)min(j, n_seg - 1) * step;
-        Ms[i] = j < n_seg ? pp[0] : -INFINITY;
-        Ss[i] = pp[1];
-#pragma unroll
-        for (int m = 0; m < 4; ++m) v[i][m] = pp[2 + q + 32 * m];
-    }
-    float M = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < kMergeOnePass; ++i) M = fmaxf(M, Ms[i]);
-    M = wave_max(M);
-    if ((tid & 63) == 0) s_red[tid >> 6] = M;
-    __syncthreads();
-    M = -INFINITY;
-#pragma unroll
-    for (int k = 0; k < kMergeThreads / 64; ++k) M = fmaxf(M, s_red[k]);
-    __syncthreads();
-    float S = 0.f, acc[4] = {0.f, 0.f, 0.f, 0.f};
-    if (M != -INFINITY) {
-#pragma unroll
-        for (int i = 0; i < kMergeOnePass; ++i) {
-            const float w = (Ms[i] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((Ms[i] - M) * kLog2e);
-            S = fmaf(Ss[i], w, S);
-#pragma unroll
-            for (int m = 0; m < 4; ++m) acc[m] = fmaf(v[i][m], w, acc[m]);
+        for (int j = 0; j < kMergePartDim / 2; ++j) {
+            const float2 x = *reinterpret_cast<const float2 *>(pp + 2 + kMergePartDim * pt + 2 * j);
+            v[2 * j] = x.x;
+            v[2 * j + 1] = x.y;
         }
+    } else {
+#pragma unroll
+        for (int j = 0; j < kMergePartDim; ++j) v[j] = 0.f;
     }
-    // S: each segment once (lane 0 of its group); acc folded over the groups
-    S = wave_sum(q == 0 ? S : 0.f);
-    if ((tid & 63) == 0) s_red[tid >> 6] = S;
-#pragma unroll
-    for (int m = 0; m < 4; ++m) s_acc[grp][q + 32 * m] = acc[m];
+    float M = wave_max(ms.x);
+    if (lane == 0) s_m[wv] = M;
     __syncthreads();
-    if (tid >= kHeadDim) return;
-    const int d = tid;
-    S = 0.f;
 #pragma unroll
-    for (int k = 0; k < kMergeThreads / 64; ++k) S += s_red[k];
+    for (int k = 0; k < kW; ++k) M = fmaxf(M, s_m[k]);
+    const float w = (M == -INFINITY || ms.x == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((ms.x - M) * kLog2e);
+    // per-wave sums of the weighted S and values, then across the waves through LDS
+    const float S = wave_sum(ms.y * w);
+    float acc[kMergePartDim];
+#pragma unroll
+    for (int j = 0; j < kMergePartDim; ++j) acc[j] = wave_sum(v[j] * w);
+    if (lane == 0) {
+#pragma unroll
+        for (int j = 0; j < kMergePartDim; ++j) s_acc[wv][j] = acc[j];
+        s_acc[wv][kMergePartDim] = S;
+    }
+    __syncthreads();
+    if (tid > kMergePartDim) return;
     float a = 0.f;
 #pragma unroll
-    for (int k = 0; k < kMergeGroups; ++k) a += s_acc[k][d];
+    for (int k = 0; k < kW; ++k) a += s_acc[k][tid];
+    // thread kMergePartDim holds S; the others one head_dim value
+    const float Stot = [&] {
+        float x = 0.f;
+#pragma unroll
+        for (int k = 0; k < kW; ++k) x += s_acc[k][kMergePartDim];
+        return x;
+    }();
     if (pout) {
         float *dst = pout + row * kPartialStride;
-        if (d == 0) {
+        if (tid < kMergePartDim) dst[2 + kMergePartDim * pt + tid] = a;
+        else if (pt == 0) {
             dst[0] = M;
-            dst[1] = S;
+            dst[1] = Stot;
         }
-        dst[2 + d] = a;
         return;
     }
-    const bool ok = (M != -INFINITY) && (S > 0.f);
-    o[row * kHeadDim + d] = ok ? a / S : 0.f;
-    if (lse && d == 0) lse[row] = ok ? M + logf(S) : -INFINITY;
+    const bool ok = (M != -INFINITY) && (Stot > 0.f);
+    if (tid < kMergePartDim) o[row * kHeadDim + kMergePartDim * pt + tid] = ok ? a / Stot : 0.f;
+    else if (lse && pt == 0) lse[row] = ok ? M + logf(Stot) : -INFINITY;
 }
 
 __global__ void __launch_bounds__(kMergeThreads) merge_kernel(const float *__restrict__ part, int n_seg,
@@ -234,9 +237,9 @@ hipError_t launch_merge(const float *partials, int n_seg, int64_t n_rows, float 
         // enough rows to fill the chip one wave each (or too few segments to share a row)
         hipLaunchKernelGGL(merge_rows_kernel, dim3((unsigned)((n_rows + kMergeRowsPerBlock - 1) / kMergeRowsPerBlock)),
                            dim3(64 * kMergeRowsPerBlock), 0, s, partials, n_seg, n_rows, o, lse, partial_out);
-    } else if (n_seg <= kMergeGroups * kMergeOnePass) {
-        hipLaunchKernelGGL(merge_one_pass_kernel, dim3((unsigned)n_rows), dim3(kMergeThreads), 0, s, partials, n_seg,
-                           n_rows, o, lse, partial_out);
+    } else if (n_seg <= kMergePartThreads) {
+        hipLaunchKernelGGL(merge_parts_kernel, dim3((unsigned)n_rows, kMergeParts), dim3(kMergePartThreads), 0, s,
+                           partials, n_seg, n_rows, o, lse, partial_out);
     } else {
         hipLaunchKernelGGL(merge_kernel, dim3((unsigned)n_rows), dim3(kMergeThreads), 0, s, partials, n_seg, n_rows,
                            o, lse, partial_out);
