@@ -716,9 +716,10 @@ int rkv_set_kernel_timing(rkv_ctx *ctx, int on) {
     if (on && ctx->kt0.empty()) {
         ctx->kt0.resize(kMaxKernelTiming);
         ctx->kt1.resize(kMaxKernelTiming);
+        // no system-scope fence at the events: they time the kernel, not a host-visible flush
         for (int i = 0; i < kMaxKernelTiming; ++i) {
-            RKV_HIP(hipEventCreate(&ctx->kt0[i]));
-            RKV_HIP(hipEventCreate(&ctx->kt1[i]));
+            RKV_HIP(hipEventCreateWithFlags(&ctx->kt0[i], hipEventDisableSystemFence));
+            RKV_HIP(hipEventCreateWithFlags(&ctx->kt1[i], hipEventDisableSystemFence));
         }
     }
     ctx->kernel_timing = on != 0;
