@@ -71,11 +71,12 @@ struct Stage16 {
 };
 
 // Work split: the tasks are the 16-cell chunks of every (sequence, head group) pair, numbered
-// pair-major; workgroup j of G takes tasks j, j + G, j + 2G, ...  A row list only counts up to
-// its extent (1 + its last pool row, from a scan before the launch), so the padding at the end
-// of the shorter lists costs nothing, and the interleaving balances the real keys over the
-// workgroups.  A workgroup writes one partial (slot j) for every pair: its own keys' partial,
-// or the empty one.
+// pair-major; workgroup j of G takes the contiguous run of tasks [jT/G, (j+1)T/G) of the T
+// tasks, so it meets few pairs (one unless a pair boundary falls in its run).  A row list only
+// counts up to its extent (1 + its last pool row, from a scan before the launch), so the
+// padding at the end of the shorter lists costs nothing.  A workgroup writes its partial of
+// each pair it meets into slot j, and M = -inf, S = 0 (no values) for the other pairs; when
+// asked, workgroup 0 also writes each pair's slot range for the merge.
 template <int R, bool ROWS>
 __global__ void __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2)))
 decode_mma16_kernel(const SegParams p) {
@@ -119,7 +120,21 @@ decode_mma16_kernel(const SegParams p) {
         __syncthreads();
     }
     const uint32_t n_tasks = s_off[n_pairs];
-    const uint32_t n_t = n_tasks > j ? (n_tasks - j + G - 1) / G : 0;  // this workgroup's tasks
+    const uint32_t t_lo = (uint32_t)((uint64_t)j * n_tasks / G);
+    const uint32_t n_t = (uint32_t)((uint64_t)(j + 1) * n_tasks / G) - t_lo;  // this workgroup's tasks
+    if (p.pair_range && j == 0) {
+        // workgroup of task t: the largest i with iT/G <= t, i.e. floor(((t + 1) G - 1) / T)
+        for (int pr = tid; pr < n_pairs; pr += kNT) {
+            const uint32_t lo = s_off[pr], hi = s_off[pr + 1];
+            int2 r = make_int2(0, 0);
+            if (hi > lo) {
+                const int a = (int)(((uint64_t)(lo + 1) * G - 1) / n_tasks);
+                const int b = (int)(((uint64_t)hi * G - 1) / n_tasks);
+                r = make_int2(p.slot0 + a, p.slot0 + b + 1);
+            }
+            p.pair_range[pr] = r;
+        }
+    }
     const int64_t n_cells = p.n_cells;
     const int qi_row = min(col, R - 1) / p.gqa;  // query position of this lane's row
     const int fcell = tid / kTpc, fsub = tid % kTpc;
@@ -132,6 +147,8 @@ decode_mma16_kernel(const SegParams p) {
     const __amdgpu_buffer_rsrc_t rpart = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(p.partials + (int64_t)(p.slot0 + j) * p.n_rows * kPartialStride), (short)0,
         (int)(p.n_rows * kPartialStride * sizeof(float)), 0x00020000);
+    // (acc null: the empty partial, M and S only -- the merge gives a segment with M = -inf
+    // no weight and ignores its values)
     auto write_partial = [&](int pair, float M, float S, const float4_t *acc) __attribute__((always_inline)) {
         if (col >= R) return;
         const int bb = pair / n_hgrp, g = (pair % n_hgrp) * kHW + wave;
@@ -141,12 +158,11 @@ decode_mma16_kernel(const SegParams p) {
         if (grp == 0)
             __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{__builtin_bit_cast(uint32_t, M), __builtin_bit_cast(uint32_t, S)},
                                                   rpart, base, 0, 0);
+        if (!acc) return;
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) {
-            const float4_t v = acc ? acc[dt] : float4_t{0.f, 0.f, 0.f, 0.f};
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), rpart,
+        for (int dt = 0; dt < 8; ++dt)
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, acc[dt]), rpart,
                                                    base + (2 + 16 * dt + 4 * grp) * (int)sizeof(float), 0, 0);
-        }
     };
 
     // ---- task k of this workgroup: its pair and first cell (k past the end: a phantom task
@@ -155,7 +171,7 @@ decode_mma16_kernel(const SegParams p) {
     // row-list lookahead) instead of searching.
     int cur_f = 0, cur_r = 0, prev_fetch_pair = -1;
     auto task_at = [&](int &cur, uint32_t k, int &pair, int64_t &c0) __attribute__((always_inline)) {
-        const uint32_t t = j + min(k, n_t - 1) * G;
+        const uint32_t t = t_lo + (n_t > 0 ? min(k, n_t - 1) : 0);
         while (cur + 1 < n_pairs && s_off[cur + 1] <= t) ++cur;  // past empty pairs too
         pair = cur;
         c0 = (int64_t)(t - s_off[cur]) * kCh;
@@ -272,12 +288,10 @@ decode_mma16_kernel(const SegParams p) {
             write_partial(cur, mrun == -INFINITY ? -INFINITY : mrun * kLn2, S, oacc);
         }
     };
-    // pairs with no task in this workgroup get the empty partial up front: pair P's first task
-    // of residue j modulo G is lo + ((j - lo) mod G), lo = its first task
+    // pairs with no task in this workgroup get the empty partial up front
     for (int pr = 0; pr < n_pairs; ++pr) {
         const uint32_t lo = s_off[pr], hi = s_off[pr + 1];
-        const uint32_t first = lo + (j + G - lo % G) % G;
-        if (!(first < hi)) write_partial(pr, -INFINITY, 0.f, nullptr);
+        if (!(lo < hi && n_t > 0 && lo < t_lo + n_t && hi > t_lo)) write_partial(pr, -INFINITY, 0.f, nullptr);
     }
 
     // ---- one task from LDS stage `buf` (its metadata and, for a new pair, its Q^T were taken

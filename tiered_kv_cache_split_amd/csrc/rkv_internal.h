@@ -44,6 +44,10 @@ struct SegParams {
     int slot0;         // first partial slot used by this segment
     int64_t n_rows;    // n_head * n_q * n_seq
     int cell_hw;       // > 0: cell-major kernel, cell_hw KV heads (packed per cell) per workgroup
+    // optional (device, persistent binary16 kernel): receives, per (sequence, head group) pair,
+    // the slot range [x, y) holding that pair's partials; slots outside it are not written
+    // for the pair beyond M = -inf, S = 0
+    int2 *pair_range;
     // optional: events the segment kernel's own dispatch records at its start and end
     hipEvent_t ev_start, ev_stop;
 };
@@ -76,8 +80,9 @@ hipError_t launch_decode_mma(const SegParams &p, hipStream_t s, int *occupancy);
 // The binary16 matrix-core decode kernel (windows, tail tiles and row lists) over groups of
 // eight cell-major KV heads with gqa * n_q <= 8 rows per head; the same occupancy convention.
 bool decode_mma16_ok(const SegParams &p);
-// Whether the decode kernel for p is the persistent one: n_splits workgroups then take every
-// n_splits-th 16-cell chunk of all (sequence, head group) pairs, and cells_per_split is unused.
+// Whether the decode kernel for p is the persistent one: n_splits workgroups then take equal
+// contiguous runs of the 16-cell chunks of all (sequence, head group) pairs, numbered
+// pair-major, and cells_per_split is unused.
 bool decode_kernel_persistent(const SegParams &p, int k_type, int v_type);
 hipError_t launch_decode_mma16(const SegParams &p, hipStream_t s, int *occupancy);
 hipError_t launch_prefill_segment(const SegParams &p, int k_type, int v_type, hipStream_t s);
@@ -85,8 +90,15 @@ hipError_t launch_prefill_segment(const SegParams &p, int k_type, int v_type, hi
 int prefill_rows_per_block();
 int prefill_keys_per_iter();
 int prefill_blocks_per_cu();  // workgroups of the prefill kernel resident per CU (LDS bound)
-hipError_t launch_merge(const float *partials, int n_seg, int64_t n_rows, float *o,
-                        float *lse, float *partial_out, hipStream_t s);
+// Optional per-row segment ranges for the merge: row r merges slots pair_range[pair(r)] with
+// pair(r) = (r / rows_per_seq) * n_hgrp + ((r % n_head) / heads_per_pair), clamped to n_seg.
+struct MergeRange {
+    const int2 *pair_range;
+    int n_head, heads_per_pair, n_hgrp;
+    int64_t rows_per_seq;
+};
+hipError_t launch_merge(const float *partials, int n_seg, int64_t n_rows, float *o, float *lse,
+                        float *partial_out, hipStream_t s, const MergeRange *range = nullptr);
 // Writes (M=-inf, S=0, VKQ=0) for n_rows rows into partial slot 0.
 hipError_t launch_empty_partials(float *partials, int64_t n_rows, hipStream_t s);
 // Row-list extents in kRowExtentParts pieces per sequence: the maximum of

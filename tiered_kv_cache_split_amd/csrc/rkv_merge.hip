@@ -18,6 +18,23 @@ constexpr int kMergeThreads = 1024;
 constexpr int kMergeGroups = kMergeThreads / 32;
 constexpr int kMergeTile = 2048;  // segment weights held in LDS per pass
 
+// Segments [a, b) of a row: all of them, or the row's pair range when one is given.  A segment
+// with M = -inf has weight 0 and its values are not used (they need not have been written).
+struct RowRange {
+    const int2 *pair_range;
+    int n_head, heads_per_pair, n_hgrp;
+    int64_t rows_per_seq;
+    __device__ void of(int64_t row, int n_seg, int &a, int &b) const {
+        a = 0;
+        b = n_seg;
+        if (!pair_range) return;
+        const int pair = (int)(row / rows_per_seq) * n_hgrp + (int)(row % n_head) / heads_per_pair;
+        const int2 r = pair_range[pair];
+        a = max(0, min(r.x, n_seg));
+        b = max(a, min(r.y, n_seg));
+    }
+};
+
 // Up to kMergePartThreads segments over few rows: workgroup (row, part) merges head_dim values
 // 16*part .. 16*part+15 of one row with one thread per segment, so every load of the merge is
 // issued at once by kMergeParts times more workgroups than rows and the merge costs one memory
@@ -29,14 +46,16 @@ constexpr int kMergePartThreads = 256;
 __global__ void __launch_bounds__(kMergePartThreads) merge_parts_kernel(const float *__restrict__ part, int n_seg,
                                                                         int64_t n_rows, float *__restrict__ o,
                                                                         float *__restrict__ lse,
-                                                                        float *__restrict__ pout) {
+                                                                        float *__restrict__ pout, RowRange rr) {
     constexpr int kW = kMergePartThreads / 64;
     __shared__ float s_m[kW];
     __shared__ float s_acc[kW][kMergePartDim + 1];
     const int64_t row = blockIdx.x;
     const int pt = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const bool has = tid < n_seg;
-    const float *pp = part + ((int64_t)(has ? tid : 0) * n_rows + row) * kPartialStride;
+    int sa, sb;
+    rr.of(row, n_seg, sa, sb);
+    const bool has = sa + tid < sb;
+    const float *pp = part + ((int64_t)(has ? sa + tid : 0) * n_rows + row) * kPartialStride;
     float2 ms = make_float2(-INFINITY, 0.f);
     float v[kMergePartDim];
     if (has) {
@@ -61,7 +80,7 @@ __global__ void __launch_bounds__(kMergePartThreads) merge_parts_kernel(const fl
     const float S = wave_sum(ms.y * w);
     float acc[kMergePartDim];
 #pragma unroll
-    for (int j = 0; j < kMergePartDim; ++j) acc[j] = wave_sum(v[j] * w);
+    for (int j = 0; j < kMergePartDim; ++j) acc[j] = wave_sum(w > 0.f ? v[j] * w : 0.f);
     if (lane == 0) {
 #pragma unroll
         for (int j = 0; j < kMergePartDim; ++j) s_acc[wv][j] = acc[j];
@@ -96,14 +115,17 @@ __global__ void __launch_bounds__(kMergePartThreads) merge_parts_kernel(const fl
 __global__ void __launch_bounds__(kMergeThreads) merge_kernel(const float *__restrict__ part, int n_seg,
                                                               int64_t n_rows, float *__restrict__ o,
                                                               float *__restrict__ lse,
-                                                              float *__restrict__ pout) {
+                                                              float *__restrict__ pout, RowRange rr) {
     __shared__ float s_wt[kMergeTile];
     __shared__ float s_red[kMergeThreads / 64];
     __shared__ float s_acc[kMergeGroups][kHeadDim];
     const int64_t row = blockIdx.x;
     const int tid = threadIdx.x, q = tid & 31, grp = tid >> 5;  // lane q holds head_dim q + 32m
     const int64_t step = n_rows * kPartialStride;
-    const float *base = part + row * kPartialStride;
+    int sa, sb;
+    rr.of(row, n_seg, sa, sb);
+    const float *base = part + (row + sa * n_rows) * kPartialStride;
+    n_seg = sb - sa;
 
     // M* = max over segments
     float M = -INFINITY;
@@ -132,8 +154,10 @@ __global__ void __launch_bounds__(kMergeThreads) merge_kernel(const float *__res
             for (int j = grp; j < nt; j += kMergeGroups) {
                 const float *v = base + (int64_t)(t0 + j) * step + 2 + q;
                 const float wj = s_wt[j];
+                if (wj > 0.f) {
 #pragma unroll
-                for (int m = 0; m < 4; ++m) acc[m] = fmaf(v[32 * m], wj, acc[m]);
+                    for (int m = 0; m < 4; ++m) acc[m] = fmaf(v[32 * m], wj, acc[m]);
+                }
             }
             __syncthreads();
         }
@@ -174,12 +198,15 @@ constexpr int kMergeRowsPerBlock = 4;
 __global__ void __launch_bounds__(64 * kMergeRowsPerBlock) merge_rows_kernel(const float *__restrict__ part, int n_seg,
                                                                            int64_t n_rows, float *__restrict__ o,
                                                                            float *__restrict__ lse,
-                                                                           float *__restrict__ pout) {
+                                                                           float *__restrict__ pout, RowRange rr) {
     const int lane = threadIdx.x & 63;
     const int64_t row = (int64_t)blockIdx.x * kMergeRowsPerBlock + (threadIdx.x >> 6);
     if (row >= n_rows) return;
     const int64_t step = n_rows * kPartialStride;
-    const float *base = part + row * kPartialStride;
+    int sa, sb;
+    rr.of(row, n_seg, sa, sb);
+    const float *base = part + (row + sa * n_rows) * kPartialStride;
+    n_seg = sb - sa;
     float M = -INFINITY;
     for (int s = lane; s < n_seg; s += 64) M = fmaxf(M, base[(int64_t)s * step]);
     M = wave_max(M);
@@ -196,9 +223,11 @@ __global__ void __launch_bounds__(64 * kMergeRowsPerBlock) merge_rows_kernel(con
             const int nt = min(64, n_seg - s0);
             for (int j = 0; j < nt; ++j) {
                 const float wj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), j));
-                const float *v = base + (int64_t)(s0 + j) * step + 2 + lane;
-                a0 = fmaf(v[0], wj, a0);
-                a1 = fmaf(v[64], wj, a1);
+                if (wj > 0.f) {
+                    const float *v = base + (int64_t)(s0 + j) * step + 2 + lane;
+                    a0 = fmaf(v[0], wj, a0);
+                    a1 = fmaf(v[64], wj, a1);
+                }
             }
         }
     }
@@ -231,18 +260,23 @@ __global__ void __launch_bounds__(128) empty_partials_kernel(float *__restrict__
 }  // namespace
 
 hipError_t launch_merge(const float *partials, int n_seg, int64_t n_rows, float *o, float *lse,
-                        float *partial_out, hipStream_t s) {
+                        float *partial_out, hipStream_t s, const MergeRange *range) {
     if (n_rows <= 0) return hipSuccess;
+    RowRange rr{};
+    if (range) {
+        if (range->n_head <= 0 || range->heads_per_pair <= 0 || range->rows_per_seq <= 0) return hipErrorInvalidValue;
+        rr = RowRange{range->pair_range, range->n_head, range->heads_per_pair, range->n_hgrp, range->rows_per_seq};
+    }
     if (n_rows >= 1024 || n_seg <= 16) {
         // enough rows to fill the chip one wave each (or too few segments to share a row)
         hipLaunchKernelGGL(merge_rows_kernel, dim3((unsigned)((n_rows + kMergeRowsPerBlock - 1) / kMergeRowsPerBlock)),
-                           dim3(64 * kMergeRowsPerBlock), 0, s, partials, n_seg, n_rows, o, lse, partial_out);
+                           dim3(64 * kMergeRowsPerBlock), 0, s, partials, n_seg, n_rows, o, lse, partial_out, rr);
     } else if (n_seg <= kMergePartThreads) {
         hipLaunchKernelGGL(merge_parts_kernel, dim3((unsigned)n_rows, kMergeParts), dim3(kMergePartThreads), 0, s,
-                           partials, n_seg, n_rows, o, lse, partial_out);
+                           partials, n_seg, n_rows, o, lse, partial_out, rr);
     } else {
         hipLaunchKernelGGL(merge_kernel, dim3((unsigned)n_rows), dim3(kMergeThreads), 0, s, partials, n_seg, n_rows,
-                           o, lse, partial_out);
+                           o, lse, partial_out, rr);
     }
     return hipGetLastError();
 }

@@ -173,6 +173,8 @@ struct rkv_ctx {
     size_t partials_cap = 0;  // floats
     int32_t *row_extent = nullptr;  // row lists: per-sequence extents for the persistent kernel
     size_t row_extent_cap = 0;      // bytes
+    int2 *pair_range = nullptr;     // row lists: slot range of each pair's partials (up to 1024 pairs)
+    size_t pair_range_cap = 0;      // bytes
     int lift_mode = RKV_LIFT_BULK;
     int splits_override = 0;
     rkv_stats stats = {};
@@ -655,6 +657,7 @@ void rkv_destroy(rkv_ctx *c) {
     if (c->entry) (void)hipEventDestroy(c->entry);
     if (c->partials) (void)hipFree(c->partials);
     if (c->row_extent) (void)hipFree(c->row_extent);
+    if (c->pair_range) (void)hipFree(c->pair_range);
     if (c->copy_stream) (void)hipStreamDestroy(c->copy_stream);
     (void)hipGetLastError();
     delete c;
@@ -677,6 +680,10 @@ int rkv_reserve(rkv_ctx *ctx, int64_t max_tile_bytes_k, int64_t max_tile_bytes_v
         void *buf = ctx->row_extent;  // row-list extents (up to 1024 sequences)
         st = grow(&buf, &ctx->row_extent_cap, 1024 * kRowExtentParts * sizeof(int32_t), nullptr);
         ctx->row_extent = static_cast<int32_t *>(buf);
+        if (st) return st;
+        buf = ctx->pair_range;  // slot ranges of up to 1024 pairs
+        st = grow(&buf, &ctx->pair_range_cap, 1024 * sizeof(int2), nullptr);
+        ctx->pair_range = static_cast<int2 *>(buf);
         if (st) return st;
     }
     return RKV_OK;
@@ -822,16 +829,27 @@ int rkv_attn_rows(rkv_ctx *ctx, const rkv_tensor *q, const rkv_tensor *k_pool, c
     int slot = 0;
     SegParams pk = p;
     pk.cell_hw = plan.cell_hw;
+    MergeRange mr{};
+    bool ranged = false;
     if (n_kv > 0 && decode_kernel_persistent(pk, k_pool->type, v_pool->type)) {
-        // the persistent kernel counts each list up to its last pool row
+        // the persistent kernel counts each list up to its last pool row, and reports which
+        // slots hold each pair's partials, so that the merge reads only those
         void *buf = ctx->row_extent;
         st = grow(&buf, &ctx->row_extent_cap, std::max<size_t>(1024, (size_t)n_seq) * kRowExtentParts * sizeof(int32_t),
                   stream);
         ctx->row_extent = static_cast<int32_t *>(buf);
         if (st) return st;
+        buf = ctx->pair_range;
+        st = grow(&buf, &ctx->pair_range_cap, 1024 * sizeof(int2), stream);
+        ctx->pair_range = static_cast<int2 *>(buf);
+        if (st) return st;
         hipError_t e1 = launch_row_extent(kv_rows, n_kv, n_kv, (int)n_seq, ctx->row_extent, stream);
         if (e1 != hipSuccess) return hip_fail(e1, "row extent launch");
         p.row_extent = ctx->row_extent;
+        p.pair_range = ctx->pair_range;
+        mr = MergeRange{ctx->pair_range, (int)n_head, (int)(gqa * plan.cell_hw), (int)(n_head_kv / plan.cell_hw),
+                        n_head * n_q};
+        ranged = true;
     }
     if (n_kv > 0) {
         if ((st = run_segment(ctx, p, pool, false, k_pool->type, v_pool->type, slot, stream))) return st;
@@ -842,7 +860,7 @@ int rkv_attn_rows(rkv_ctx *ctx, const rkv_tensor *q, const rkv_tensor *k_pool, c
     }
     ctx->stats.splits_window = slot;
     ctx->stats.n_partials = slot;
-    hipError_t e = launch_merge(ctx->partials, slot, p.n_rows, o, lse, nullptr, stream);
+    hipError_t e = launch_merge(ctx->partials, slot, p.n_rows, o, lse, nullptr, stream, ranged ? &mr : nullptr);
     if (e != hipSuccess) return hip_fail(e, "merge launch");
     return RKV_OK;
 }
