@@ -228,6 +228,17 @@ decode_mma_kernel(const SegParams p) {
         // (d_V is staged in P.V slot order: the key of slot 8*gg + jj is 4*gg + jj (jj < 4) or
         // 16 + 4*gg + jj - 4.)
 
+        // the V^T bytes (one transposing read per block) are read first: their latency then
+        // overlaps Q.K and the softmax
+        int2_t btr[4];
+#pragma unroll
+        for (int blk = 0; blk < 4; ++blk) {
+            // block blk of head `wave` is slot 2*wave + blk/2 (+ 2HW for odd blk) of a cell
+            const int vslot = 2 * wave + (blk >> 1) + 2 * HW * (blk & 1);
+            btr[blk] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                (__attribute__((address_space(3))) int2_t *)(vs + vrd + 16 * vslot));
+        }
+
         // ---- Q.K on the matrix cores: A = K (16 keys x 32 head_dim of one q8_0 block, codes as
         // binary16 1024 + (q + 128)), B = Q^T; d[ii] = score of key 16*kt + 4*grp + ii for row col
         // before the block scale
@@ -334,10 +345,7 @@ decode_mma_kernel(const SegParams p) {
             swacc[blk] = __builtin_amdgcn_fdot2(h2v(wu.y), ones, swacc[blk], false);
             swacc[blk] = __builtin_amdgcn_fdot2(h2v(wu.z), ones, swacc[blk], false);
             swacc[blk] = __builtin_amdgcn_fdot2(h2v(wu.w), ones, swacc[blk], false);
-            // block blk of head `wave` is slot 2*wave + blk/2 (+ 2HW for odd blk) of a cell
-            const int vslot = 2 * wave + (blk >> 1) + 2 * HW * (blk & 1);
-            const int2_t bt = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                (__attribute__((address_space(3))) int2_t *)(vs + vrd + 16 * vslot));
+            const int2_t bt = btr[blk];
             uint32_t lo[4], hi[4];
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
