@@ -74,6 +74,12 @@ enum rkv_lift_mode {
     RKV_LIFT_UVA = 1    /* contrast only: a kernel reads the pinned host bytes word by word  */
 };
 
+enum rkv_residency_mode {
+    RKV_RESIDENCY_AUTO = 0,      /* window + tail when eligible                            */
+    RKV_RESIDENCY_RESIDENT = 1,  /* never split the cache by position                      */
+    RKV_RESIDENCY_WINDOW = 2     /* window + tail when eligible, resident otherwise        */
+};
+
 typedef struct rkv_tensor {
     const void *data;
     int32_t type;   /* enum rkv_type */
@@ -222,6 +228,31 @@ int rkv_lse_merge(const float *partials, int n_seg, int64_t n_rows, int dv,
  * demand outside graph capture (RKV_ERR_CAPTURE inside it). */
 int rkv_tail_lift(rkv_ctx *ctx, const void *host_src, int64_t nbytes, int slot, int mode,
                   void **dev_dst, void *copy_stream);
+
+/* ---- residency policy (host) ----------------------------------------------------------- */
+
+/* Position-window sizing (patch 0070, KV-cache hunk: the position-axis residency sizer).
+ * A cache of kv_size cells whose K and V take per_cell bytes per cell (all layers and
+ * streams together) keeps its leading *wc cells resident in device memory; cells
+ * [*wc, kv_size) form the pinned-host tail.  Budget = free device bytes (free_bytes when
+ * >= 0; otherwise the context device's free memory, which needs ctx), capped at
+ * target_bytes when > 0, minus reserve_bytes, never below 0.  The whole cache fits ->
+ * *wc = kv_size.  Otherwise *wc = budget / per_cell rounded down to a multiple of align,
+ * at least align, and at most kv_size - align rounded down to align (so a tail remains);
+ * *wc never exceeds kv_size.  Host arithmetic only (no device work unless free_bytes < 0).
+ * Errors: RKV_ERR_ARG for per_cell <= 0, kv_size < 0, align <= 0, reserve_bytes < 0,
+ * wc NULL, or free_bytes < 0 without ctx. */
+int rkv_plan_window(rkv_ctx *ctx, int64_t per_cell, int64_t kv_size, int64_t free_bytes,
+                    int64_t target_bytes, int64_t reserve_bytes, int64_t align, int64_t *wc);
+
+/* Residency mode (patch 0070, KV-cache hunk: the window-mode eligibility rule after the
+ * sizer).  mode RKV_RESIDENCY_AUTO: window when eligible; RKV_RESIDENCY_RESIDENT: never;
+ * RKV_RESIDENCY_WINDOW: window when eligible, otherwise resident (not an error).
+ * Eligible: 0 < wc < kv_size (a real overflow), append_only != 0 (cell index = key
+ * position, so the window is the position range [0, wc)) and v_transposed == 0.
+ * *window receives 1 or 0.  Errors: RKV_ERR_ARG for an unknown mode or window NULL. */
+int rkv_window_mode(int mode, int64_t wc, int64_t kv_size, int append_only, int v_transposed,
+                    int *window);
 
 /* ---- testing aid ------------------------------------------------------------------ */
 

@@ -99,3 +99,47 @@ def test_no_device_is_reported(lib):
     from tiered_kv_cache_split_amd import _lib
     h = ctypes.c_void_p()
     assert lib.rkv_create(0, ctypes.byref(h)) == _lib.RKV_ERR_HIP
+
+
+# ---- residency policy: host arithmetic, checked against the oracle without a GPU
+
+def test_plan_window_matches_the_oracle(lib):
+    import numpy as np
+    import oracle
+    import tiered_kv_cache_split_amd as rkv
+    rng = np.random.default_rng(77)
+    cases = [(1664, 262144, 300 << 30, 0, 3 << 29, 256), (79872, 1 << 20, 300 << 30, 64 << 30, 3 << 29, 256),
+             (512, 0, 1 << 30, 0, 0, 32), (1, 1, 0, 0, 0, 1), (1 << 40, 1 << 20, 1 << 62, 0, 0, 1 << 20)]
+    for _ in range(3000):
+        per_cell = int(rng.integers(1, 1 << 20))
+        kv = int(rng.integers(0, 1 << 22))
+        free = int(rng.integers(0, 1 << 45))
+        target = int(rng.choice([0, int(rng.integers(1, 1 << 45))]))
+        reserve = int(rng.integers(0, 1 << 33))
+        align = int(rng.choice([1, 32, 256, 1024]))
+        cases.append((per_cell, kv, free, target, reserve, align))
+    for c in cases:
+        assert rkv.plan_window(*c) == oracle.plan_window(*c), c
+
+
+def test_plan_window_argument_errors(lib):
+    from tiered_kv_cache_split_amd import _lib
+    wc = ctypes.c_int64()
+    for args in [(0, 10, 100, 0, 0, 32), (16, -1, 100, 0, 0, 32), (16, 10, 100, 0, 0, 0), (16, 10, 100, 0, -1, 32),
+                 (16, 10, -1, 0, 0, 32)]:  # the last: free < 0 needs a context
+        assert lib.rkv_plan_window(None, *args, ctypes.byref(wc)) == _lib.RKV_ERR_ARG, args
+    assert lib.rkv_plan_window(None, 16, 10, 100, 0, 0, 32, None) == _lib.RKV_ERR_ARG
+
+
+def test_window_mode_matches_the_oracle(lib):
+    import oracle
+    import tiered_kv_cache_split_amd as rkv
+    from tiered_kv_cache_split_amd import _lib
+    for mode in (0, 1, 2):
+        for wc in (0, 1, 500, 999, 1000, 1001):
+            for ao in (False, True):
+                for vt in (False, True):
+                    assert rkv.window_mode(mode, wc, 1000, ao, vt) == oracle.window_mode(mode, wc, 1000, ao, vt)
+    out = ctypes.c_int()
+    assert lib.rkv_window_mode(3, 1, 2, 1, 0, ctypes.byref(out)) == _lib.RKV_ERR_ARG
+    assert lib.rkv_window_mode(0, 1, 2, 1, 0, None) == _lib.RKV_ERR_ARG

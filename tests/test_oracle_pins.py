@@ -317,3 +317,69 @@ def test_kv_values_cell_major_layout():
     vals = oracle.kv_values(gen.TYPE_F16, raw.view(np.uint8))
     assert vals.shape == (2, 3, 4)
     assert vals[1, 2, 3] == float(raw[2, 1, 3])
+
+
+# ---- residency sizer (patch 0070, KV-cache hunk: position-window sizing and mode rule)
+
+GIB = 1 << 30
+
+
+def test_plan_window_fits_exactly_or_not():
+    # whole cache exactly at the budget: resident; one byte less: a tail appears
+    per_cell, kv = 1664, 262144
+    need = per_cell * kv
+    assert oracle.plan_window(per_cell, kv, need + GIB, 0, GIB, 256) == kv
+    wc = oracle.plan_window(per_cell, kv, need + GIB - 1, 0, GIB, 256)
+    assert wc == kv - 256  # the largest aligned window that leaves a tail
+
+
+def test_plan_window_closed_forms():
+    # budget 100 cells' worth (after target cap and reserve) -> 96 at alignment 32
+    per_cell = 1000
+    assert oracle.plan_window(per_cell, 10_000, 10**12, 100_500 + 7, 7, 32) == 96
+    # the target caps the free bytes; the reserve eats the rest -> one unit
+    assert oracle.plan_window(per_cell, 10_000, 10**12, 5_000, 10**9, 32) == 32
+    # zero budget -> one unit of window
+    assert oracle.plan_window(per_cell, 10_000, 0, 0, 0, 256) == 256
+    # cache shorter than one unit that does not fit stays resident
+    assert oracle.plan_window(per_cell, 100, 0, 0, 0, 256) == 100
+    assert oracle.plan_window(per_cell, 0, 0, 0, 0, 256) == 0
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_plan_window_is_the_largest_aligned_fit(seed):
+    """Against the definition by enumeration: among aligned windows that fit the budget and
+    leave at least one unit of tail, the largest (one unit when none fits)."""
+    rng = np.random.default_rng(seed)
+    for _ in range(200):
+        per_cell = int(rng.integers(1, 5000))
+        align = int(rng.choice([1, 16, 32, 256]))
+        kv = int(rng.integers(1, 40)) * int(rng.choice([1, align])) + int(rng.integers(0, 3))
+        free = int(rng.integers(0, per_cell * kv * 2 + 10))
+        target = int(rng.choice([0, int(rng.integers(1, per_cell * kv * 2 + 10))]))
+        reserve = int(rng.integers(0, per_cell * 5 + 1))
+        wc = oracle.plan_window(per_cell, kv, free, target, reserve, align)
+        budget = max(0, (min(free, target) if target > 0 else free) - reserve)
+        if per_cell * kv <= budget:
+            assert wc == kv
+            continue
+        fitting = [m for m in range(align, kv, align) if m * per_cell <= budget and kv - m >= align]
+        tail_ok = [m for m in range(align, kv, align) if kv - m >= align]
+        if fitting:
+            expect = max(fitting)
+        elif tail_ok or kv <= align:
+            expect = align
+        else:
+            expect = align
+        assert wc == min(expect, kv), (per_cell, kv, free, target, reserve, align, wc, expect)
+
+
+def test_window_mode_rule():
+    kv = 1000
+    for mode in (0, 2):
+        assert oracle.window_mode(mode, 500, kv, True, False)
+        assert not oracle.window_mode(mode, kv, kv, True, False)   # no overflow
+        assert not oracle.window_mode(mode, 0, kv, True, False)
+        assert not oracle.window_mode(mode, 500, kv, False, False)  # rotating cells
+        assert not oracle.window_mode(mode, 500, kv, True, True)    # transposed V
+    assert not oracle.window_mode(1, 500, kv, True, False)

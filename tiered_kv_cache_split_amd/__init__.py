@@ -14,8 +14,9 @@ from __future__ import annotations
 
 import ctypes
 
-from ._lib import (RKV_LIFT_BULK, RKV_LIFT_UVA, RKV_TYPE_F16, RKV_TYPE_F32, RKV_TYPE_Q4_0,  # noqa: F401
-                   RKV_TYPE_Q8_0, RkvError, RkvStats, RkvTensor, check, load)
+from ._lib import (RKV_LIFT_BULK, RKV_LIFT_UVA, RKV_RESIDENCY_AUTO, RKV_RESIDENCY_RESIDENT,  # noqa: F401
+                   RKV_RESIDENCY_WINDOW, RKV_TYPE_F16, RKV_TYPE_F32, RKV_TYPE_Q4_0, RKV_TYPE_Q8_0, RkvError,
+                   RkvStats, RkvTensor, check, load)
 
 BLOCK_BYTES = {RKV_TYPE_F16: 2, RKV_TYPE_F32: 4, RKV_TYPE_Q8_0: 34, RKV_TYPE_Q4_0: 18}
 ROW_BYTES = {RKV_TYPE_F16: 256, RKV_TYPE_Q8_0: 136, RKV_TYPE_Q4_0: 72}
@@ -190,6 +191,27 @@ def dequant_rows(src, type_id: int, n_rows: int, row_stride: int, dst, stream=No
     lib = load()
     check(lib.rkv_dequant_rows(_ptr(src), int(type_id), int(n_rows), int(row_stride), _ptr(dst),
                                _stream(stream)), "rkv_dequant_rows")
+
+
+def plan_window(per_cell: int, kv_size: int, free_bytes: int = -1, target_bytes: int = 0,
+                reserve_bytes: int = 3 << 29, align: int = 256, ctx: "Context | None" = None) -> int:
+    """Resident cells of a position-windowed cache (rkv_plan_window); free_bytes < 0 reads the
+    free memory of ctx's device.  The default reserve is 1.5 GiB."""
+    lib = load()
+    wc = ctypes.c_int64()
+    check(lib.rkv_plan_window(ctx.h if ctx is not None else None, int(per_cell), int(kv_size), int(free_bytes),
+                              int(target_bytes), int(reserve_bytes), int(align), ctypes.byref(wc)),
+          "rkv_plan_window")
+    return int(wc.value)
+
+
+def window_mode(mode: int, wc: int, kv_size: int, append_only: bool = True, v_transposed: bool = False) -> bool:
+    """Whether the cache runs as window + tail (rkv_window_mode)."""
+    lib = load()
+    out = ctypes.c_int()
+    check(lib.rkv_window_mode(int(mode), int(wc), int(kv_size), int(bool(append_only)), int(bool(v_transposed)),
+                              ctypes.byref(out)), "rkv_window_mode")
+    return bool(out.value)
 
 
 def version() -> str:

@@ -10,6 +10,7 @@ LIB_PATH = os.path.join(_HERE, "librkv.so")
 RKV_TYPE_F32, RKV_TYPE_F16, RKV_TYPE_Q4_0, RKV_TYPE_Q8_0 = 0, 1, 2, 8
 RKV_OK, RKV_ERR_ARG, RKV_ERR_UNSUPPORTED, RKV_ERR_HIP, RKV_ERR_NOMEM, RKV_ERR_CAPTURE = 0, -1, -2, -3, -4, -5
 RKV_LIFT_BULK, RKV_LIFT_UVA = 0, 1
+RKV_RESIDENCY_AUTO, RKV_RESIDENCY_RESIDENT, RKV_RESIDENCY_WINDOW = 0, 1, 2
 
 i64 = ctypes.c_int64
 vp = ctypes.c_void_p
@@ -51,6 +52,9 @@ SIGNATURES = {
     "rkv_lse_merge": (ctypes.c_int, [vp, ctypes.c_int, i64, ctypes.c_int, vp, vp, vp]),
     "rkv_tail_lift": (ctypes.c_int, [vp, vp, i64, ctypes.c_int, ctypes.c_int, ctypes.POINTER(vp), vp]),
     "rkv_dequant_rows": (ctypes.c_int, [vp, ctypes.c_int, i64, i64, vp, vp]),
+    "rkv_plan_window": (ctypes.c_int, [vp, i64, i64, i64, i64, i64, i64, ctypes.POINTER(i64)]),
+    "rkv_window_mode": (ctypes.c_int, [ctypes.c_int, i64, i64, ctypes.c_int, ctypes.c_int,
+                                       ctypes.POINTER(ctypes.c_int)]),
 }
 
 _lib = None

@@ -689,6 +689,52 @@ int rkv_reserve(rkv_ctx *ctx, int64_t max_tile_bytes_k, int64_t max_tile_bytes_v
     return RKV_OK;
 }
 
+// Position-window sizing: the steps of the patch 0070 KV-cache sizer (budget, whole-cache
+// check, aligned largest fit, at least one unit of window and of tail), with wc <= kv_size.
+int rkv_plan_window(rkv_ctx *ctx, int64_t per_cell, int64_t kv_size, int64_t free_bytes, int64_t target_bytes,
+                    int64_t reserve_bytes, int64_t align, int64_t *wc) {
+    if (!wc) return fail(RKV_ERR_ARG, "wc is NULL");
+    if (per_cell <= 0 || kv_size < 0 || align <= 0 || reserve_bytes < 0)
+        return fail(RKV_ERR_ARG, "per_cell and align must be > 0, kv_size and reserve_bytes >= 0");
+    if (free_bytes < 0) {
+        if (!ctx) return fail(RKV_ERR_ARG, "free_bytes < 0 needs a context to query its device");
+        int st = ensure_device(ctx);
+        if (st) return st;
+        size_t fr = 0, tot = 0;
+        RKV_HIP(hipMemGetInfo(&fr, &tot));
+        free_bytes = (int64_t)fr;
+    }
+    if (kv_size == 0) {
+        *wc = 0;
+        return RKV_OK;
+    }
+    int64_t budget = free_bytes;
+    if (target_bytes > 0) budget = std::min(budget, target_bytes);
+    budget = budget > reserve_bytes ? budget - reserve_bytes : 0;
+    // whole cache fits: per_cell * kv_size <= budget, without overflowing the product
+    if (kv_size <= budget / per_cell) {
+        *wc = kv_size;
+        return RKV_OK;
+    }
+    int64_t cells = (budget / per_cell) / align * align;
+    if (cells < align) cells = align;
+    if (kv_size > align && cells > kv_size - align) {
+        cells = (kv_size - align) / align * align;
+        if (cells < align) cells = align;
+    }
+    *wc = std::min(cells, kv_size);
+    return RKV_OK;
+}
+
+int rkv_window_mode(int mode, int64_t wc, int64_t kv_size, int append_only, int v_transposed, int *window) {
+    if (!window) return fail(RKV_ERR_ARG, "window is NULL");
+    if (mode != RKV_RESIDENCY_AUTO && mode != RKV_RESIDENCY_RESIDENT && mode != RKV_RESIDENCY_WINDOW)
+        return fail(RKV_ERR_ARG, "unknown residency mode %d", mode);
+    const bool eligible = wc > 0 && wc < kv_size && append_only != 0 && v_transposed == 0;
+    *window = (eligible && mode != RKV_RESIDENCY_RESIDENT) ? 1 : 0;
+    return RKV_OK;
+}
+
 int rkv_get_stats(const rkv_ctx *ctx, rkv_stats *out) {
     if (!ctx || !out) return fail(RKV_ERR_ARG, "NULL argument");
     *out = ctx->stats;
