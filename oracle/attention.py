@@ -15,9 +15,11 @@ of opencoti-llamafile patch 0070-rolling-kv, fattn.cu ``streaming_lse_kernel``):
     O     = sum_{j in V} exp(s_j - LSE) * v_{j,g}
     V empty  ->  O = 0, LSE = -inf
 
-The scale is applied before the mask and no soft-cap is used (patch 0070,
-fattn.cu ``streaming_lse_kernel``: ``scale*part`` then ``+= mask``; a -inf
-key contributes nothing; ``lse = m + log l`` or -inf when ``l = 0``).
+The scale is applied before the mask (patch 0070, fattn.cu ``streaming_lse_kernel``:
+``scale*part`` then ``+= mask``; a -inf key contributes nothing; ``lse = m + log l``
+or -inf when ``l = 0``).  With a logit soft-cap ``c > 0`` the scaled score is
+replaced, still before the mask, by ``c * tanh(scale * <q, k> / c)`` (the same
+kernel's soft-cap branch); ``c = 0`` is the plain score.
 
 A *segment partial* over a subset of key positions is ``(M, S, VKQ)``:
 ``M = max s_j``, ``S = sum exp(s_j - M)``, ``VKQ = sum exp(s_j - M) v_j``
@@ -53,7 +55,7 @@ def q_values(q_f16: np.ndarray) -> np.ndarray:
     return np.asarray(q_f16, dtype=np.float16).astype(np.float64)
 
 
-def scores(q, k, scale, mask=None):
+def scores(q, k, scale, mask=None, softcap=0.0):
     """q (n_head, n_q, d), k (n_head_kv, n, d), mask (n_q, n) or None -> s (n_head, n_q, n)."""
     n_head = q.shape[0]
     n_head_kv = k.shape[0]
@@ -63,14 +65,16 @@ def scores(q, k, scale, mask=None):
     for h in range(n_head):
         g = h // gqa
         s[h] = scale * (q[h] @ k[g].T)
+    if softcap:
+        s = softcap * np.tanh(s / softcap)
     if mask is not None:
         s = s + np.asarray(mask, dtype=np.float64)[None, :, :]
     return s
 
 
-def partial(q, k, v, scale, mask=None):
+def partial(q, k, v, scale, mask=None, softcap=0.0):
     """Segment partial over all keys given: returns M, S (n_q, n_head) and VKQ (n_q, n_head, dv)."""
-    s = scores(q, k, scale, mask)  # (n_head, n_q, n)
+    s = scores(q, k, scale, mask, softcap)  # (n_head, n_q, n)
     n_head, n_q, n = s.shape
     gqa = n_head // k.shape[0]
     dv = v.shape[2]
@@ -108,17 +112,17 @@ def merge(parts):
     return O, LSE
 
 
-def attention(q, k, v, scale, mask=None):
+def attention(q, k, v, scale, mask=None, softcap=0.0):
     """Unsplit attention over all keys: O (n_q, n_head, dv), LSE (n_q, n_head)."""
-    return merge([partial(q, k, v, scale, mask)])
+    return merge([partial(q, k, v, scale, mask, softcap)])
 
 
-def split_attention(q, k, v, scale, mask, bounds):
+def split_attention(q, k, v, scale, mask, bounds, softcap=0.0):
     """Attention computed as partials over the position segments [b_t, b_{t+1}) then merged."""
     parts = []
     for a, b in zip(bounds[:-1], bounds[1:]):
         parts.append(partial(q, k[:, a:b], v[:, a:b], scale,
-                             None if mask is None else mask[:, a:b]))
+                             None if mask is None else mask[:, a:b], softcap))
     return merge(parts)
 
 
@@ -144,7 +148,7 @@ def causal_mask(n_q: int, n_kv: int, q_pos0: int) -> np.ndarray:
     return np.where(j <= i, 0.0, NEG_INF)
 
 
-def attention_rows(q, k_pool, v_pool, kv_rows, scale, mask=None):
+def attention_rows(q, k_pool, v_pool, kv_rows, scale, mask=None, softcap=0.0):
     """Unified-pool attention.
 
     q (n_seq, n_head, n_q, d); k_pool/v_pool (n_head_kv, n_pool, d); kv_rows (n_seq, n_kv)
@@ -157,7 +161,7 @@ def attention_rows(q, k_pool, v_pool, kv_rows, scale, mask=None):
         keep = rows >= 0
         r = rows[keep].astype(np.int64)
         m = None if mask is None else np.asarray(mask[b], dtype=np.float64)[:, keep]
-        O, L = attention(q[b], k_pool[:, r], v_pool[:, r], scale, m)
+        O, L = attention(q[b], k_pool[:, r], v_pool[:, r], scale, m, softcap)
         outs.append(O)
         lses.append(L)
     return np.stack(outs), np.stack(lses)

@@ -383,3 +383,44 @@ def test_window_mode_rule():
         assert not oracle.window_mode(mode, 500, kv, False, False)  # rotating cells
         assert not oracle.window_mode(mode, 500, kv, True, True)    # transposed V
     assert not oracle.window_mode(1, 500, kv, True, False)
+
+
+# ---- logit soft-cap (patch 0070, streaming_lse_kernel soft-cap branch: c*tanh(scale*qk/c) before the mask)
+
+def test_softcap_brute_force_tiny():
+    rng = np.random.default_rng(123)
+    q = rng.standard_normal((2, 1, 4))
+    k = rng.standard_normal((1, 5, 4)) * 4.0
+    v = rng.standard_normal((1, 5, 3))
+    mask = np.array([[0.0, -np.inf, 0.5, 0.0, -1.0]])
+    c, scale = 2.5, 0.7
+    O, L = oracle.attention(q, k, v, scale, mask, softcap=c)
+    for h in range(2):
+        s = []
+        for j in range(5):
+            raw = scale * math.fsum(q[h, 0, d] * k[0, j, d] for d in range(4))
+            s.append(c * math.tanh(raw / c) + mask[0, j])
+        vis = [j for j in range(5) if s[j] > -math.inf]
+        lse = math.log(math.fsum(math.exp(s[j]) for j in vis))
+        assert abs(L[0, h] - lse) < 1e-12
+        for e in range(3):
+            ref = math.fsum(math.exp(s[j] - lse) * v[0, j, e] for j in vis)
+            assert abs(O[0, h, e] - ref) < 1e-12
+
+
+def test_softcap_limits():
+    rng = np.random.default_rng(7)
+    q = rng.standard_normal((4, 2, 128))
+    k = rng.standard_normal((2, 50, 128))
+    v = rng.standard_normal((2, 50, 128))
+    # a huge cap is the plain score; every capped score lies in [-c, c]
+    O0, L0 = oracle.attention(q, k, v, 0.09)
+    O1, L1 = oracle.attention(q, k, v, 0.09, softcap=1e9)
+    assert np.abs(O0 - O1).max() < 1e-12 and np.abs(L0 - L1).max() < 1e-12
+    s = oracle.scores(q, k * 50.0, 0.09, softcap=3.0)
+    assert np.all(np.abs(s) <= 3.0) and np.abs(s).max() > 2.9  # saturates at the cap
+    # partition invariance holds with the cap too
+    parts = [oracle.partial(q, k[:, a:b], v[:, a:b], 0.09, None, 3.0) for a, b in [(0, 7), (7, 7), (7, 50)]]
+    Om, Lm = oracle.merge(parts)
+    Oa, La = oracle.attention(q, k, v, 0.09, softcap=3.0)
+    assert np.abs(Om - Oa).max() < 1e-12 and np.abs(Lm - La).max() < 1e-12
