@@ -191,7 +191,7 @@ def measured_copy_gbs(nbytes=1 << 30, reps=10) -> float:
 
 
 # ------------------------------------------------------------------ CPU baseline (oracle)
-def cpu_baseline(num: int, budget_s: float = 12.0, w=None):
+def cpu_baseline(num: int, budget_s: float = 12.0, w=None, softcap: float = 0.0):
     """Time the fp64 oracle on a bounded sample of the same workload and scale to GB/s of
     the full workload's algorithmic KV bytes."""
     import numpy as np
@@ -212,7 +212,7 @@ def cpu_baseline(num: int, budget_s: float = 12.0, w=None):
             rows = np.where(w["kv_rows"][:, :cells] >= 0, w["kv_rows"][:, :cells], -1)
             k = oracle.kv_values(w["k_type"], w["k"])
             v = oracle.kv_values(w["v_type"], w["v"])
-            oracle.attention_rows(q, k, v, rows, w["scale"], None)
+            oracle.attention_rows(q, k, v, rows, w["scale"], None, softcap)
             dt = time.perf_counter() - t0
             done = int((rows >= 0).sum())
             if dt >= budget_s / 2 or cells >= w["n_kv"]:
@@ -234,7 +234,7 @@ def cpu_baseline(num: int, budget_s: float = 12.0, w=None):
         t0 = time.perf_counter()
         k = oracle.kv_values(w["k_type"], w["k"][:cells])
         v = oracle.kv_values(w["v_type"], w["v"][:cells])
-        oracle.attention(q, k, v, w["scale"], None)
+        oracle.attention(q, k, v, w["scale"], None, softcap)
         dt = time.perf_counter() - t0
         if dt >= budget_s / 2 or cells >= n_kv:
             break
@@ -259,6 +259,7 @@ def main():
     ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--sets", type=int, default=4, help="independent device copies of the KV cache")
     ap.add_argument("--splits", type=int, default=0)
+    ap.add_argument("--softcap", type=float, default=0.0, help="logit soft-cap c (0: none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--lift-mode", type=int, default=0, help="0 bulk DMA, 1 word-granularity UVA read")
     ap.add_argument("--copy-only", action="store_true",
@@ -288,6 +289,8 @@ def main():
         ctx.set_splits(args.splits)
     if args.lift_mode:
         ctx.set_lift_mode(args.lift_mode)
+    if args.softcap:
+        ctx.set_softcap(args.softcap)
     for i in range(args.warmup):
         call(ctx, st, i)
     torch.cuda.synchronize()
@@ -341,7 +344,8 @@ def main():
         "config": {"workload": w["name"], "n_head": w["n_head"], "n_head_kv": w["n_head_kv"], "head_dim": 128,
                    "n_q": int(w["q"].shape[-2]), "n_kv": int(w["n_kv"]),
                    "k_type": gen.TYPE_NAMES[w["k_type"]], "v_type": gen.TYPE_NAMES[w["v_type"]],
-                   "kv_sets_rotated": args.sets, "parallelism": "single GPU"},
+                   "kv_sets_rotated": args.sets, "parallelism": "single GPU",
+                   **({"softcap": args.softcap} if args.softcap else {})},
         "tok_per_s_per_layer": round(1e3 / ms_per_step, 1),
         "pct_hbm_peak_whole_call": round(100 * kv_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
         "segment_launches_per_step": launches_per_step,
@@ -383,7 +387,7 @@ def main():
     out["measured_copy_GBps"] = round(measured_copy_gbs(), 1)
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host cores", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(args.workload, w=w)
+        out["cpu_baseline"] = cpu_baseline(args.workload, w=w, softcap=args.softcap)
     ctx.close()
     print(json.dumps(out), flush=True)
 

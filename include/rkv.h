@@ -229,6 +229,12 @@ int rkv_lse_merge(const float *partials, int n_seg, int64_t n_rows, int dv,
 int rkv_tail_lift(rkv_ctx *ctx, const void *host_src, int64_t nbytes, int slot, int mode,
                   void **dev_dst, void *copy_stream);
 
+/* Logit soft-cap of every later attention call on the context (patch 0070,
+ * streaming_lse_kernel soft-cap branch): each scaled score scale*<q,k> becomes
+ * softcap * tanh(scale*<q,k> / softcap), before the mask is added.  0 (the default) turns
+ * it off.  Errors: RKV_ERR_ARG for a NULL context or a negative or non-finite value. */
+int rkv_set_softcap(rkv_ctx *ctx, float softcap);
+
 /* ---- residency policy (host) ----------------------------------------------------------- */
 
 /* Position-window sizing (patch 0070, KV-cache hunk: the position-axis residency sizer).

@@ -54,7 +54,7 @@ def assert_close(O, L, Oref, Lref, o_tol=O_TOL, lse_tol=LSE_TOL, what=""):
     return err, lerr
 
 
-def oracle_decode(w, mask=None, heads=None):
+def oracle_decode(w, mask=None, heads=None, softcap=0.0):
     """fp64 oracle of a window/tail workload dict from rkv_inputs.make_workload.
     heads: optional list of KV heads to restrict to (full-size sampling)."""
     q = oracle.q_values(w["q"])
@@ -63,12 +63,12 @@ def oracle_decode(w, mask=None, heads=None):
     if heads is None:
         k = oracle.kv_values(w["k_type"], w["k"])
         v = oracle.kv_values(w["v_type"], w["v"])
-        return oracle.attention(q, k, v, w["scale"], m)
+        return oracle.attention(q, k, v, w["scale"], m, softcap)
     outs = {}
     for g in heads:
         k = oracle.kv_values(w["k_type"], w["k"][:, g:g + 1])
         v = oracle.kv_values(w["v_type"], w["v"][:, g:g + 1])
-        O, L = oracle.attention(q[g * gqa:(g + 1) * gqa], k, v, w["scale"], m)
+        O, L = oracle.attention(q[g * gqa:(g + 1) * gqa], k, v, w["scale"], m, softcap)
         outs[g] = (O, L)
     return outs
 
@@ -145,10 +145,10 @@ class Runner:
         return o.cpu().numpy(), lse.cpu().numpy()
 
 
-def oracle_rows(w, mask="given", rows=None):
+def oracle_rows(w, mask="given", rows=None, softcap=0.0):
     q = np.stack([oracle.q_values(w["q"][b]) for b in range(w["q"].shape[0])])
     k = oracle.kv_values(w["k_type"], w["k"])
     v = oracle.kv_values(w["v_type"], w["v"])
     m = w["mask"] if mask == "given" else mask
     mm = None if m is None else np.asarray(m, dtype=np.float64)[:, 0]
-    return oracle.attention_rows(q, k, v, w["kv_rows"] if rows is None else rows, w["scale"], mm)
+    return oracle.attention_rows(q, k, v, w["kv_rows"] if rows is None else rows, w["scale"], mm, softcap)

@@ -127,6 +127,10 @@ class Context:
     def set_splits(self, splits: int):
         check(self.lib.rkv_set_splits(self.h, int(splits)), "rkv_set_splits")
 
+    def set_softcap(self, softcap: float):
+        """Logit soft-cap of later calls: scale*qk -> softcap*tanh(scale*qk/softcap); 0 = off."""
+        check(self.lib.rkv_set_softcap(self.h, float(softcap)), "rkv_set_softcap")
+
     def set_lift_timing(self, on: bool):
         check(self.lib.rkv_set_lift_timing(self.h, int(bool(on))), "rkv_set_lift_timing")
 

@@ -52,6 +52,7 @@ SIGNATURES = {
     "rkv_lse_merge": (ctypes.c_int, [vp, ctypes.c_int, i64, ctypes.c_int, vp, vp, vp]),
     "rkv_tail_lift": (ctypes.c_int, [vp, vp, i64, ctypes.c_int, ctypes.c_int, ctypes.POINTER(vp), vp]),
     "rkv_dequant_rows": (ctypes.c_int, [vp, ctypes.c_int, i64, i64, vp, vp]),
+    "rkv_set_softcap": (ctypes.c_int, [vp, ctypes.c_float]),
     "rkv_plan_window": (ctypes.c_int, [vp, i64, i64, i64, i64, i64, i64, ctypes.POINTER(i64)]),
     "rkv_window_mode": (ctypes.c_int, [ctypes.c_int, i64, i64, ctypes.c_int, ctypes.c_int,
                                        ctypes.POINTER(ctypes.c_int)]),

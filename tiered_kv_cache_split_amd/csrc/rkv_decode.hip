@@ -166,7 +166,8 @@ template <int KT, int VT, int R, bool VLDS>
 __device__ __forceinline__ void process_chunk(const uint8_t *krow, const uint8_t *vbase, int vstride,
                                               const typename RowFmt<VT>::U *vreg, const uint32_t *const (&qw)[R],
                                               const float *qsum, _Float16 *wtab, const float (&xadd)[R],
-                                              float scale_log2, int lane, float (&m)[R], float (&l)[R],
+                                              float scale_log2, float cap_cs, float cap_l2, int lane,
+                                              float (&m)[R], float (&l)[R],
                                               float (&acc)[R][8], float (&sw)[R][n_wblocks<VT>()]) {
     constexpr bool kVq = (VT == T_Q4_0);
     constexpr int kNB = n_wblocks<VT>();
@@ -266,7 +267,7 @@ __device__ __forceinline__ void process_chunk(const uint8_t *krow, const uint8_t
     }
 #pragma unroll
     for (int rho = 0; rho < R; ++rho) {
-        const float x = fmaf(s[rho], scale_log2, xadd[rho]);
+        const float x = cap_l2 != 0.f ? softcap_log2(s[rho], cap_cs, cap_l2) + xadd[rho] : fmaf(s[rho], scale_log2, xadd[rho]);
         const float mn = fmaxf(m[rho], wave_max(x));
         float pr = 0.f;
         if (mn != -INFINITY) {
@@ -516,7 +517,7 @@ decode_seg_kernel(const SegParams p) {
         }
         if (any)
             process_chunk<KT, VT, R, kVq>(lk + lane * kKs, lv, kVs, vb, qw, s_qsum, s_w[wave], xadd, p.scale_log2,
-                                          lane, m, l, acc, sw);
+                                          p.cap_cs, p.cap_l2, lane, m, l, acc, sw);
         wave_sync();
     }
     finish_wave<VT, R>(lane, l, acc, sw);
@@ -679,7 +680,8 @@ decode_cell_kernel(const SegParams p) {
         __syncthreads();
         fetch(c0 + kChunk);  // past c_end nothing is read
         process_chunk<KT, VT, R, true>(s_k + lane * kSk + wave * kRk, s_v + wave * kRv, kSv, nullptr, qw,
-                                       s_qsum[wave], s_w[wave], xadd, p.scale_log2, lane, m, l, acc, sw);
+                                       s_qsum[wave], s_w[wave], xadd, p.scale_log2, p.cap_cs, p.cap_l2, lane, m, l,
+                                       acc, sw);
     }
     finish_wave<VT, R>(lane, l, acc, sw);
 

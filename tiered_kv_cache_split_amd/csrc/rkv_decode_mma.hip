@@ -282,7 +282,14 @@ decode_mma_kernel(const SegParams p) {
         // ---- visibility: whole chunk visible, or per element (chunk end, causal rule, mask)
         const bool full = (c0 + kCh <= c_end) && !p.mask && (p.q_pos0 < 0 || p.pos0 + c0 + kCh - 1 <= p.q_pos0);
         float cc = c;
-        if (!full) {
+        if (full && p.cap_l2 != 0.f) {
+            // every key visible: only the soft-cap
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii) s[kt][ii] = softcap_log2(s[kt][ii], p.cap_cs, p.cap_l2);
+            cc = 1.0f;
+        } else if (!full) {
             // in chunk-relative 32-bit terms: keys below n_in exist, keys up to lim are not after
             // the query (causal rule); mask reads clamp to the segment's last key
             const int n_in = (int)min((int64_t)kCh, c_end - c0);
@@ -295,7 +302,7 @@ decode_mma_kernel(const SegParams p) {
                 for (int ii = 0; ii < 4; ++ii) {
                     const int kr = 16 * kt + 4 * grp + ii;
                     const bool vis = kr < n_in && kr <= lim;
-                    float x = s[kt][ii] * c;
+                    float x = p.cap_l2 != 0.f ? softcap_log2(s[kt][ii], p.cap_cs, p.cap_l2) : s[kt][ii] * c;
                     if (mr) x = fmaf((float)mr[min(c0 + kr, c_end - 1)], kLog2e, x);
                     s[kt][ii] = vis ? x : -INFINITY;
                 }

@@ -329,7 +329,7 @@ decode_mma16_kernel(const SegParams p) {
         for (int ii = 0; ii < 4; ++ii) {
             bool vis = okk[ii] != 0;
             if (!ROWS && p.q_pos0 >= 0 && p.pos0 + mt_.c0 + 4 * grp + ii > p.q_pos0 + qi_row) vis = false;
-            float x = dq[ii] * c;
+            float x = p.cap_l2 != 0.f ? softcap_log2(dq[ii], p.cap_cs, p.cap_l2) : dq[ii] * c;
             if (p.mask) x = fmaf(mvals[ii], kLog2e, x);
             s[ii] = vis ? x : -INFINITY;
         }

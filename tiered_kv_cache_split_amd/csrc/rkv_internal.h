@@ -40,6 +40,9 @@ struct SegParams {
     int cells_per_split, n_splits;
     int n_head, n_head_kv, n_q, n_seq, gqa;
     float scale_log2;  // scale * log2(e)
+    // logit soft-cap: the score becomes cap_l2 * tanh(cap_cs * <q, k>) in the exp2 domain
+    // (cap_cs = scale / c, cap_l2 = c * log2(e)); cap_l2 = 0: no cap
+    float cap_cs, cap_l2;
     float *partials;   // [slot][n_rows][2 + 128]
     int slot0;         // first partial slot used by this segment
     int64_t n_rows;    // n_head * n_q * n_seq

@@ -24,6 +24,7 @@
 //      of the accumulator layout is matched by permuting keys when V^T is written);
 //   5. the wave writes its rows' partial (M in natural-log units).
 #include "rkv_internal.h"
+#include "rkv_wave.h"
 
 #include <math.h>
 
@@ -352,7 +353,14 @@ prefill_seg_kernel(const SegParams p, int q_tiles, int n_tasks) {
         const bool full = (c0 + kBN <= p.n_cells) && !p.mask &&
                           (p.q_pos0 < 0 || p.pos0 + c0 + kBN - 1 <= p.q_pos0 + wave_i_first);
         float cc = c;
-        if (!full) {
+        if (full && p.cap_l2 != 0.f) {
+            // every key visible to every row of the wave: only the soft-cap
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) sacc[kt][i] = softcap_log2(sacc[kt][i], p.cap_cs, p.cap_l2);
+            cc = 1.0f;
+        } else if (!full) {
             const int64_t nvalid = p.n_cells - c0;
             int64_t lim = p.q_pos0 >= 0 ? p.q_pos0 + qi - p.pos0 - c0 : (int64_t)kBN;
             if (lim > nvalid - 1) lim = nvalid - 1;
@@ -363,7 +371,7 @@ prefill_seg_kernel(const SegParams p, int q_tiles, int n_tasks) {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const int kk = 32 * kt + 8 * (i >> 2) + 4 * hh + (i & 3);
-                    float x = sacc[kt][i] * c;
+                    float x = p.cap_l2 != 0.f ? softcap_log2(sacc[kt][i], p.cap_cs, p.cap_l2) : sacc[kt][i] * c;
                     if (mrow && kk <= lim32) x = fmaf((float)mrow[kk], kLog2eP, x);
                     sacc[kt][i] = kk <= lim32 ? x : -INFINITY;
                 }

@@ -177,6 +177,7 @@ struct rkv_ctx {
     size_t pair_range_cap = 0;      // bytes
     int lift_mode = RKV_LIFT_BULK;
     int splits_override = 0;
+    float softcap = 0.f;  // logit soft-cap of later calls (0: none)
     rkv_stats stats = {};
 };
 
@@ -189,6 +190,16 @@ bool stream_capturing(hipStream_t s) {
         return false;
     }
     return st == hipStreamCaptureStatusActive;
+}
+
+// Logit soft-cap constants of a call: s -> c * tanh(scale * qk / c), in the exp2 domain.
+void fill_softcap(SegParams &p, const rkv_ctx *ctx, float scale) {
+    if (ctx->softcap > 0.f) {
+        p.cap_cs = scale / ctx->softcap;
+        p.cap_l2 = ctx->softcap * 1.4426950408889634f;
+    } else {
+        p.cap_cs = p.cap_l2 = 0.f;
+    }
 }
 
 int ensure_device(rkv_ctx *ctx) {
@@ -482,6 +493,7 @@ int attn_window_tail(rkv_ctx *ctx, const rkv_tensor *q, const rkv_tensor *k_win,
     base.n_seq = 1;
     base.gqa = (int)gqa;
     base.scale_log2 = scale * 1.4426950408889634f;
+    fill_softcap(base, ctx, scale);
     base.n_rows = n_head * n_q;
 
     // ---- plan: window segment, then tail (in place, or lifted tiles through the ring)
@@ -735,6 +747,13 @@ int rkv_window_mode(int mode, int64_t wc, int64_t kv_size, int append_only, int 
     return RKV_OK;
 }
 
+int rkv_set_softcap(rkv_ctx *ctx, float softcap) {
+    if (!ctx) return fail(RKV_ERR_ARG, "ctx is NULL");
+    if (!(softcap >= 0.f) || !std::isfinite(softcap)) return fail(RKV_ERR_ARG, "softcap must be finite and >= 0");
+    ctx->softcap = softcap;
+    return RKV_OK;
+}
+
 int rkv_get_stats(const rkv_ctx *ctx, rkv_stats *out) {
     if (!ctx || !out) return fail(RKV_ERR_ARG, "NULL argument");
     *out = ctx->stats;
@@ -864,6 +883,7 @@ int rkv_attn_rows(rkv_ctx *ctx, const rkv_tensor *q, const rkv_tensor *k_pool, c
     p.n_seq = (int)n_seq;
     p.gqa = (int)gqa;
     p.scale_log2 = scale * 1.4426950408889634f;
+    fill_softcap(p, ctx, scale);
     p.n_rows = n_head * n_q * n_seq;
     const Seg pool{static_cast<const uint8_t *>(k_pool->data), static_cast<const uint8_t *>(v_pool->data),
                    k_pool->nb[1], k_pool->nb[2], v_pool->nb[1], v_pool->nb[2], n_kv, 0};
@@ -940,6 +960,7 @@ int rkv_attn_partial(rkv_ctx *ctx, const rkv_tensor *q, const rkv_tensor *k, con
     p.n_seq = 1;
     p.gqa = (int)gqa;
     p.scale_log2 = scale * 1.4426950408889634f;
+    fill_softcap(p, ctx, scale);
     p.n_rows = n_head * n_q;
     const Seg sg{static_cast<const uint8_t *>(k->data), static_cast<const uint8_t *>(v->data), k->nb[1], k->nb[2],
                  v->nb[1], v->nb[2], k->ne[1], kv_pos0};

@@ -46,6 +46,13 @@ __device__ __forceinline__ float fold_rows_max(float x) {
     return fmaxf(__builtin_bit_cast(float, (int)r32[0]), __builtin_bit_cast(float, (int)r32[1]));
 }
 
+// Soft-capped score in the exp2 domain, l2 * tanh(cs * qk), with tanh(y) = 1 - 2 / (e^{2y} + 1):
+// one exp and one reciprocal, exact at both saturations (e^{2y} = inf gives 1, 0 gives -1).
+__device__ __forceinline__ float softcap_log2(float qk, float cs, float l2) {
+    const float e = __builtin_amdgcn_exp2f((2.0f * kLog2e) * cs * qk);
+    return l2 * fmaf(-2.0f, __builtin_amdgcn_rcpf(e + 1.0f), 1.0f);
+}
+
 // This wave's LDS writes complete before its later LDS reads (other waves are not ordered).
 __device__ __forceinline__ void lds_order() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
