@@ -77,7 +77,8 @@ struct Stage {
     uint32_t vc;
 };
 
-template <int R, int HW>
+// CAP: the logit soft-cap is on (a separate instantiation, so the plain path carries none of it)
+template <int R, int HW, bool CAP>
 __global__ void __launch_bounds__(64 * HW) __attribute__((amdgpu_waves_per_eu(2)))
 decode_mma_kernel(const SegParams p) {
     using St = Stage<HW>;
@@ -282,7 +283,7 @@ decode_mma_kernel(const SegParams p) {
         // ---- visibility: whole chunk visible, or per element (chunk end, causal rule, mask)
         const bool full = (c0 + kCh <= c_end) && !p.mask && (p.q_pos0 < 0 || p.pos0 + c0 + kCh - 1 <= p.q_pos0);
         float cc = c;
-        if (full && p.cap_l2 != 0.f) {
+        if (CAP && full) {
             // every key visible: only the soft-cap
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt)
@@ -302,7 +303,7 @@ decode_mma_kernel(const SegParams p) {
                 for (int ii = 0; ii < 4; ++ii) {
                     const int kr = 16 * kt + 4 * grp + ii;
                     const bool vis = kr < n_in && kr <= lim;
-                    float x = p.cap_l2 != 0.f ? softcap_log2(s[kt][ii], p.cap_cs, p.cap_l2) : s[kt][ii] * c;
+                    float x = CAP ? softcap_log2(s[kt][ii], p.cap_cs, p.cap_l2) : s[kt][ii] * c;
                     if (mr) x = fmaf((float)mr[min(c0 + kr, c_end - 1)], kLog2e, x);
                     s[kt][ii] = vis ? x : -INFINITY;
                 }
@@ -409,13 +410,18 @@ decode_mma_kernel(const SegParams p) {
     }
 }
 
-template <int R, int HW>
-hipError_t launch_mma(const SegParams &p, hipStream_t s, int *occupancy) {
+template <int R, int HW, bool CAP>
+hipError_t launch_mma_c(const SegParams &p, hipStream_t s, int *occupancy) {
     if (occupancy)
-        return hipOccupancyMaxActiveBlocksPerMultiprocessor(occupancy, decode_mma_kernel<R, HW>, 64 * HW, 0);
-    launch_seg(decode_mma_kernel<R, HW>, dim3((unsigned)(p.n_splits * (p.n_head_kv / HW) * p.n_seq)), dim3(64 * HW),
+        return hipOccupancyMaxActiveBlocksPerMultiprocessor(occupancy, decode_mma_kernel<R, HW, CAP>, 64 * HW, 0);
+    launch_seg(decode_mma_kernel<R, HW, CAP>, dim3((unsigned)(p.n_splits * (p.n_head_kv / HW) * p.n_seq)), dim3(64 * HW),
                s, p);
     return hipGetLastError();
+}
+
+template <int R, int HW>
+hipError_t launch_mma(const SegParams &p, hipStream_t s, int *occupancy) {
+    return p.cap_l2 != 0.f ? launch_mma_c<R, HW, true>(p, s, occupancy) : launch_mma_c<R, HW, false>(p, s, occupancy);
 }
 
 template <int R>

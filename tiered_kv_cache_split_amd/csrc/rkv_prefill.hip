@@ -221,7 +221,8 @@ __device__ __forceinline__ float lane_pair_sum(float x) {
     return __builtin_bit_cast(float, (int)r[0]) + __builtin_bit_cast(float, (int)r[1]);
 }
 
-template <int KT, int VT>
+// CAP: the logit soft-cap is on (a separate instantiation, so the plain path carries none of it)
+template <int KT, int VT, bool CAP>
 __global__ void __launch_bounds__(kThreadsP) __attribute__((amdgpu_waves_per_eu(2)))
 prefill_seg_kernel(const SegParams p, int q_tiles, int n_tasks) {
     using L = Lds<KT, VT>;
@@ -353,7 +354,7 @@ prefill_seg_kernel(const SegParams p, int q_tiles, int n_tasks) {
         const bool full = (c0 + kBN <= p.n_cells) && !p.mask &&
                           (p.q_pos0 < 0 || p.pos0 + c0 + kBN - 1 <= p.q_pos0 + wave_i_first);
         float cc = c;
-        if (full && p.cap_l2 != 0.f) {
+        if (CAP && full) {
             // every key visible to every row of the wave: only the soft-cap
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt)
@@ -371,7 +372,7 @@ prefill_seg_kernel(const SegParams p, int q_tiles, int n_tasks) {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const int kk = 32 * kt + 8 * (i >> 2) + 4 * hh + (i & 3);
-                    float x = p.cap_l2 != 0.f ? softcap_log2(sacc[kt][i], p.cap_cs, p.cap_l2) : sacc[kt][i] * c;
+                    float x = CAP ? softcap_log2(sacc[kt][i], p.cap_cs, p.cap_l2) : sacc[kt][i] * c;
                     if (mrow && kk <= lim32) x = fmaf((float)mrow[kk], kLog2eP, x);
                     sacc[kt][i] = kk <= lim32 ? x : -INFINITY;
                 }
@@ -461,7 +462,10 @@ hipError_t launch_t(const SegParams &p, hipStream_t s) {
     if (n_tasks <= 0) return hipSuccess;
     if (n_tasks > ((int64_t)1 << 30)) return hipErrorInvalidValue;
     const int64_t per = (n_tasks + 7) / 8;
-    launch_seg(prefill_seg_kernel<KT, VT>, dim3((unsigned)(8 * per)), dim3(kThreadsP), s, p, q_tiles, (int)n_tasks);
+    if (p.cap_l2 != 0.f)
+        launch_seg(prefill_seg_kernel<KT, VT, true>, dim3((unsigned)(8 * per)), dim3(kThreadsP), s, p, q_tiles, (int)n_tasks);
+    else
+        launch_seg(prefill_seg_kernel<KT, VT, false>, dim3((unsigned)(8 * per)), dim3(kThreadsP), s, p, q_tiles, (int)n_tasks);
     return hipGetLastError();
 }
 
