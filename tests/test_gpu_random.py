@@ -1,5 +1,5 @@
-"""Randomised GPU parity sweep: seeded random shapes, types, layouts, splits, tails, masks and
-row lists through every entry point, each case against the fp64 oracle.  The cases are small
+"""Randomised GPU parity sweep: seeded random shapes, types, layouts, splits, tails, masks, row
+lists and logit soft-caps through every entry point, each case against the fp64 oracle.  The cases are small
 (the oracle runs them in well under a second) and cover combinations the targeted tests do
 not enumerate: every kernel family is reached (vector, matrix-core q8_0/q4_0, matrix-core
 binary16 window/tail/rows, prefill), with ragged lengths throughout."""
@@ -18,7 +18,15 @@ TYPES = [(gen.TYPE_F16, gen.TYPE_F16), (gen.TYPE_Q8_0, gen.TYPE_Q4_0), (gen.TYPE
 
 @pytest.fixture(scope="module")
 def run():
-    return Runner()
+    r = Runner()
+    yield r
+    r.ctx.set_softcap(0.0)
+
+
+def draw_softcap(seed: int) -> float:
+    """A logit soft-cap for about a third of the cases, drawn apart from the case's own draws."""
+    rng = np.random.default_rng(5000 + seed)
+    return float(rng.uniform(0.5, 5.0)) if rng.random() < 0.35 else 0.0
 
 
 @pytest.mark.parametrize("seed", range(24))
@@ -41,8 +49,11 @@ def test_random_decode(run, seed):
     mask = gen.random_mask_f16(rng, n_q, n_kv, p_hidden=0.3) if rng.random() < 0.5 else None
     step(f"random decode seed {seed}: heads {n_head_kv}x{gqa} n_q {n_q} n_kv {n_kv} wc {wc} tile {tile} "
          f"types {kt}/{vt} tail {tail} layout {layout} mask {mask is not None}")
+    cap = draw_softcap(seed)
+    run.ctx.set_softcap(cap)
+    step(f"  softcap {cap:.3f}")
     O, L = run.decode(w, tail=None if tail == "none" else tail, mask=mask, layout=layout)
-    Oref, Lref = oracle_decode(w, mask=mask)
+    Oref, Lref = oracle_decode(w, mask=mask, softcap=cap)
     assert_close(O, L, Oref, Lref, what=f"random decode {seed}")
 
 
@@ -69,8 +80,11 @@ def test_random_rows(run, seed):
     w = dict(q=q, k=k, v=v, kv_rows=rows, mask=mask, k_type=kt, v_type=vt, scale=1 / np.sqrt(128))
     step(f"random rows seed {seed}: heads {n_head_kv}x{gqa} n_q {n_q} seqs {lengths} pool {n_pool} "
          f"types {kt}/{vt} mask {mask is not None}")
+    cap = draw_softcap(100 + seed)
+    run.ctx.set_softcap(cap)
+    step(f"  softcap {cap:.3f}")
     O, L = run.rows(w)  # the mask (or None) travels in w
-    Oref, Lref = oracle_rows(w)
+    Oref, Lref = oracle_rows(w, softcap=cap)
     assert_close(O, L, Oref, Lref, what=f"random rows {seed}")
 
 
@@ -91,9 +105,12 @@ def test_random_prefill(run, seed):
     mask = gen.random_mask_f16(rng, n_q, n_kv, p_hidden=0.2) if rng.random() < 0.3 else None
     step(f"random prefill seed {seed}: heads {n_head_kv}x{gqa} n_q {n_q} n_kv {n_kv} wc {wc} tile {tile} "
          f"types {kt}/{vt} q_pos0 {q_pos0} mask {mask is not None}")
+    cap = draw_softcap(200 + seed)
+    run.ctx.set_softcap(cap)
+    step(f"  softcap {cap:.3f}")
     O, L = run.decode(w, prefill=True, q_pos0=q_pos0, tail="host" if wc < n_kv else None, mask=mask)
     m = oracle.causal_mask(n_q, n_kv, q_pos0)
     if mask is not None:
         m = m + np.asarray(mask, dtype=np.float64)
-    Oref, Lref = oracle_decode(w, mask=m)
+    Oref, Lref = oracle_decode(w, mask=m, softcap=cap)
     assert_close(O, L, Oref, Lref, what=f"random prefill {seed}")
