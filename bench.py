@@ -339,7 +339,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "f16",  # matrix-core operands (q8_0/q4_0 codes as exact binary16 integers)
+        "accum_dtype": "f32",  # accumulation, softmax and partials
         "data": "synthetic",
         "config": {"workload": w["name"], "n_head": w["n_head"], "n_head_kv": w["n_head_kv"], "head_dim": 128,
                    "n_q": int(w["q"].shape[-2]), "n_kv": int(w["n_kv"]),
