@@ -13,18 +13,20 @@
 //        output layout a lane holds one query row for four keys, so the softmax of a row needs
 //        no LDS round trip and its probabilities are already the B operand of P.V.
 //   P.V  O^T[d][row] = V^T (A: 16 head_dim x 32 keys) times W^T (B: weights of 32 keys) where
-//        W = p * d_V folds the per-key block scale of V into the binary16 weights.  V^T is
-//        gathered from the staged raw bytes: a lane takes one byte position of eight keys,
-//        whose low and high nibbles are the elements e and e + 16 of the block.  The low
+//        W = p * d_V folds the per-key block scale of V into the binary16 weights.  V^T comes
+//        from one ds_read_b64_tr_b8 per block: a lane receives one byte position of eight
+//        keys, whose low and high nibbles are the elements e and e + 16 of the block.  The low
 //        nibble enters as exact 1024 + n, the high one in place as 1024 + 16 n; sum W (kept
 //        per V block) removes the offsets 1032 and 1152 at the end (n - 8 is the value).
 //
 // Workgroup = HW (8) waves for one (split, head group, sequence), wave w = KV head g0 + w, as in
 // the vector cell-major kernel.  A 32-cell chunk is one contiguous span of each cache, moved
-// with 16-byte buffer loads into registers and from there into one of two LDS stages; two
-// chunks are always in flight in registers, so one barrier per chunk separates the stage being
-// computed from the one being filled and the loads never pause.  The online softmax is exact
-// (the running max is raised whenever a chunk exceeds it) so the binary16 weights stay in range.
+// with buffer loads into registers (a thread takes two blocks of one head from each cache) and
+// from there into one of two LDS stages, where each block's scale is split from its data and
+// the data lands on 16-byte slots; two chunks are always in flight in registers, so one barrier
+// per chunk separates the stage being computed from the one being filled and the loads never
+// pause.  The online softmax is exact (the running max is raised whenever a chunk exceeds it)
+// so the binary16 weights stay in range.
 #include "rkv_internal.h"
 #include "rkv_quant.h"
 #include "rkv_wave.h"

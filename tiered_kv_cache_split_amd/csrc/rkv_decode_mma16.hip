@@ -15,8 +15,9 @@
 //        V^T read by ds_read_b64_tr_b16 (16 lanes fetch four keys x sixteen head_dim values and
 //        receive them transposed, one head_dim value of four keys per lane).
 //
-// Workgroup = 8 waves for one (split, group of 8 KV heads, sequence), wave w = KV head g0 + w.
-// A 16-cell chunk of the group (8 x 256 bytes of K and of V per cell) is moved with 16-byte
+// Workgroup = 8 waves, wave w = KV head g0 + w of the (sequence, group of 8 KV heads) pair of
+// its current task; the kernel is persistent (work split below).  A 16-cell chunk of the group
+// (8 x 256 bytes of K and of V per cell) is moved with 16-byte
 // buffer loads into registers and from there into one of two LDS stages; two chunks are always
 // in flight in registers, together with the chunk's mask values.  Row-list entries are read one
 // fetch ahead of the loads that use them; a padding entry's loads are pointed past the buffer
