@@ -262,6 +262,9 @@ def main():
     ap.add_argument("--softcap", type=float, default=0.0, help="logit soft-cap c (0: none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--lift-mode", type=int, default=0, help="0 bulk DMA, 1 word-granularity UVA read")
+    ap.add_argument("--tail-mode", choices=["lift", "host"], default="lift",
+                    help="host tail: lifted to the GPU in tiles, or its partial computed on the host cores")
+    ap.add_argument("--host-threads", type=int, default=16, help="host threads of the host tail partial")
     ap.add_argument("--copy-only", action="store_true",
                     help="only run a plain 1 GiB device copy (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -291,6 +294,9 @@ def main():
         ctx.set_lift_mode(args.lift_mode)
     if args.softcap:
         ctx.set_softcap(args.softcap)
+    host_tail = args.tail_mode == "host" and bool(st.get("tail_bytes"))
+    if host_tail:
+        ctx.set_tail_mode(rkv.RKV_TAIL_HOST, args.host_threads)
     for i in range(args.warmup):
         call(ctx, st, i)
     torch.cuda.synchronize()
@@ -311,15 +317,17 @@ def main():
     # in their own dispatches (roofline), and the tail lifts timed on the copy stream
     n_inst = min(args.steps, 50)
     ctx.set_kernel_timing(True)
-    lift_totals = []
-    if st.get("tail_bytes"):
+    lift_totals, host_ms = [], []
+    if st.get("tail_bytes") and not host_tail:
         ctx.set_lift_timing(True)
     torch.cuda.synchronize()
     for i in range(n_inst):
         call(ctx, st, i)
-        if st.get("tail_bytes"):
+        if st.get("tail_bytes") and not host_tail:
             tot, span, n = ctx.lift_timing_ms()  # waits for this call's lifts
             lift_totals.append((tot, span, n))
+        if host_tail:
+            host_ms.append(ctx.stats()["host_tail_ms"])
     torch.cuda.synchronize()
     k_ms, k_n = ctx.kernel_timing_ms()
     ctx.set_kernel_timing(False)
@@ -346,6 +354,7 @@ def main():
                    "n_q": int(w["q"].shape[-2]), "n_kv": int(w["n_kv"]),
                    "k_type": gen.TYPE_NAMES[w["k_type"]], "v_type": gen.TYPE_NAMES[w["v_type"]],
                    "kv_sets_rotated": args.sets, "parallelism": "single GPU",
+                   **({"tail_mode": "host"} if host_tail else {}),
                    **({"softcap": args.softcap} if args.softcap else {})},
         "tok_per_s_per_layer": round(1e3 / ms_per_step, 1),
         "pct_hbm_peak_whole_call": round(100 * kv_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
@@ -364,12 +373,13 @@ def main():
     else:
         name = {2: "decode_seg_q8q4_nkv131072", 4: "decode_seg_rows_f16_pool65536"}.get(args.workload, "")
         label = DECODE_KERNELS.get(stats.get("kernel_variant"), "decode segment kernel")
+        gpu_bytes = kv_bytes - (st["tail_bytes"] if host_tail else 0)  # a host tail partial reads no HBM
         if launches_per_step == 1:
             # one segment launch per step (resident window or pool): bytes of one launch / its time
-            achieved = kv_bytes / (kern_ms * 1e-3) / 1e9
+            achieved = gpu_bytes / (kern_ms * 1e-3) / 1e9
         else:
             # window plus tail tiles: all KV bytes over the step's total segment-kernel time
-            achieved = kv_bytes / ((k_ms / n_inst) * 1e-3) / 1e9
+            achieved = gpu_bytes / ((k_ms / n_inst) * 1e-3) / 1e9
             label += " (all segments of a step)"
         out["roofline"] = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -385,6 +395,11 @@ def main():
                        "lift_GBps_overlapped": round(lift_gbs, 2) if lift_gbs else None,
                        "measured_h2d_GBps": round(h2d, 2),
                        "frac_of_measured_h2d": round(lift_gbs / h2d, 4) if lift_gbs else None}
+    if host_tail:
+        hm = sorted(host_ms)[len(host_ms) // 2]
+        out["host_tail"] = {"tail_bytes": st["tail_bytes"], "threads": args.host_threads, "host_ms_median": round(hm, 4),
+                            "host_GBps": round(st["tail_bytes"] / (hm * 1e-3) / 1e9, 2),
+                            "partial_bytes_uploaded": int(w["n_head"] * w["q"].shape[-2] * 130 * 4)}
     out["measured_copy_GBps"] = round(measured_copy_gbs(), 1)
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host cores", file=sys.stderr, flush=True)

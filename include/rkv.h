@@ -80,6 +80,12 @@ enum rkv_residency_mode {
     RKV_RESIDENCY_WINDOW = 2     /* window + tail when eligible, resident otherwise        */
 };
 
+enum rkv_tail_mode {
+    RKV_TAIL_LIFT = 0,  /* host tail lifted tile by tile into the scratch ring (default)     */
+    RKV_TAIL_HOST = 1   /* decode: the host cores compute the tail's partial; only the
+                           partial crosses PCIe (rkv_set_tail_mode)                           */
+};
+
 typedef struct rkv_tensor {
     const void *data;
     int32_t type;   /* enum rkv_type */
@@ -96,6 +102,8 @@ typedef struct rkv_stats {
     int64_t lift_bytes;       /* raw bytes lifted host -> device                         */
     int32_t splits_window;    /* split-K factor used on the window segment               */
     int32_t kernel_variant;   /* enum rkv_kernel_variant of the last segment launched    */
+    int32_t tail_host;        /* 1 if the tail partial was computed on the host cores     */
+    float host_tail_ms;       /* wall time of that host computation                      */
 } rkv_stats;
 
 /* Segment kernel families (rkv_stats.kernel_variant). */
@@ -228,6 +236,42 @@ int rkv_lse_merge(const float *partials, int n_seg, int64_t n_rows, int dv,
  * demand outside graph capture (RKV_ERR_CAPTURE inside it). */
 int rkv_tail_lift(rkv_ctx *ctx, const void *host_src, int64_t nbytes, int slot, int mode,
                   void **dev_dst, void *copy_stream);
+
+/* Tail mode of later rkv_attn_decode calls (patch 0070, the CPU_FA_TAIL tactic: the CPU
+ * tail-partial op ggml_flash_attn_ext_tail_partial emits [M, S, VKQ] per output row over the
+ * host-resident tail, and the device merges that partial with the window's through the
+ * unchanged combine, so only 2 + dv floats per row cross PCIe).
+ *   mode      RKV_TAIL_LIFT (default) or RKV_TAIL_HOST.  In RKV_TAIL_HOST a decode call whose
+ *             tail is in host memory (pinned or pageable) copies Q and the tail's mask columns
+ *             to pinned host buffers of the context, enqueues the window kernels, computes
+ *             the tail partial on n_threads host threads while they run, uploads it into the
+ *             partials workspace and merges.  The call therefore blocks the calling thread
+ *             until Q has reached the host and the tail partial is done; it cannot be
+ *             captured (RKV_ERR_CAPTURE).  A tail in device memory, and rkv_attn_prefill,
+ *             are computed on the GPU as before.
+ *   n_threads host threads (0 = the hardware threads, at most 16).
+ * Errors: RKV_ERR_ARG for a NULL context, an unknown mode or n_threads outside [0, 256].
+ * The host computation needs a CPU with AVX2, FMA and F16C (RKV_ERR_UNSUPPORTED at the call
+ * otherwise). */
+int rkv_set_tail_mode(rkv_ctx *ctx, int mode, int n_threads);
+
+/* The tail partial on the host cores alone (the same computation RKV_TAIL_HOST runs):
+ * partial float32 [n_head * n_q][2 + 128] in host memory receives (M, S, VKQ) for every row
+ * r = h + n_head*i over the keys of k/v (fp32 accumulation; an empty row is (-inf, 0, 0...)).
+ *   q        F16 [128, n_q, n_head, 1] in host memory (rows contiguous, even strides).
+ *   k, v     [128, n_cells, n_head_kv, 1] in host memory: K F16 or Q8_0, V F16 or Q4_0,
+ *            any cell and head strides (cell-major or head-major).
+ *   mask     F16 [>= kv_pos0 + n_cells, >= n_q, 1, 1] additive, host memory, or NULL; column
+ *            kv_pos0 + j belongs to cell j (global positions, as on the device).
+ *   kv_pos0  global position of cell 0; q_pos0 >= 0 makes it causal as in rkv_attn_prefill,
+ *            -1 uses the mask alone.  softcap as rkv_set_softcap (0 = none).
+ *   n_threads host threads (0 = the hardware threads, at most 16).
+ * Synchronous; makes no HIP call, so it runs without a GPU.  Every pointer must be host
+ * memory (a device pointer is a contract violation).  Errors: RKV_ERR_ARG / RKV_ERR_UNSUPPORTED
+ * as for the device entry points, RKV_ERR_UNSUPPORTED on a CPU without AVX2, FMA and F16C. */
+int rkv_tail_partial_host(const rkv_tensor *q, const rkv_tensor *k, const rkv_tensor *v,
+                          const rkv_tensor *mask, int64_t kv_pos0, int64_t q_pos0, float scale,
+                          float softcap, float *partial, int n_threads);
 
 /* Logit soft-cap of every later attention call on the context (patch 0070,
  * streaming_lse_kernel soft-cap branch): each scaled score scale*<q,k> becomes

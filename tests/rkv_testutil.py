@@ -39,6 +39,12 @@ def pinned(a: np.ndarray):
     return t
 
 
+def pageable(a: np.ndarray):
+    """An ordinary (pageable) host tensor holding a copy of `a`."""
+    torch = torch_mod()
+    return torch.from_numpy(np.array(a, copy=True))
+
+
 def assert_close(O, L, Oref, Lref, o_tol=O_TOL, lse_tol=LSE_TOL, what=""):
     O = np.asarray(O, dtype=np.float64)
     L = np.asarray(L, dtype=np.float64)
@@ -106,7 +112,7 @@ class Runner:
             vd = rkv.kv_desc(tensors["vw"], w["v_type"], layout)
         n_tail = ktl.shape[0] if layout == "cell" else ktl.shape[1]
         if tail is not None and n_tail > 0:
-            mk = pinned if tail == "host" else dev
+            mk = {"host": pinned, "device": dev, "pageable": pageable}[tail]
             tensors["kt"], tensors["vt"] = mk(np.ascontiguousarray(ktl)), mk(np.ascontiguousarray(vtl))
             ktd = rkv.kv_desc(tensors["kt"], w["k_type"], layout)
             vtd = rkv.kv_desc(tensors["vt"], w["v_type"], layout)

@@ -15,7 +15,8 @@ from __future__ import annotations
 import ctypes
 
 from ._lib import (RKV_LIFT_BULK, RKV_LIFT_UVA, RKV_RESIDENCY_AUTO, RKV_RESIDENCY_RESIDENT,  # noqa: F401
-                   RKV_RESIDENCY_WINDOW, RKV_TYPE_F16, RKV_TYPE_F32, RKV_TYPE_Q4_0, RKV_TYPE_Q8_0, RkvError,
+                   RKV_RESIDENCY_WINDOW, RKV_TAIL_HOST, RKV_TAIL_LIFT, RKV_TYPE_F16, RKV_TYPE_F32, RKV_TYPE_Q4_0,
+                   RKV_TYPE_Q8_0, RkvError,
                    RkvStats, RkvTensor, check, load)
 
 BLOCK_BYTES = {RKV_TYPE_F16: 2, RKV_TYPE_F32: 4, RKV_TYPE_Q8_0: 34, RKV_TYPE_Q4_0: 18}
@@ -131,6 +132,11 @@ class Context:
         """Logit soft-cap of later calls: scale*qk -> softcap*tanh(scale*qk/softcap); 0 = off."""
         check(self.lib.rkv_set_softcap(self.h, float(softcap)), "rkv_set_softcap")
 
+    def set_tail_mode(self, mode: int, n_threads: int = 0):
+        """RKV_TAIL_LIFT (default) or RKV_TAIL_HOST: decode computes a host tail's partial on
+        n_threads host threads (0 = all) while the GPU computes the window."""
+        check(self.lib.rkv_set_tail_mode(self.h, int(mode), int(n_threads)), "rkv_set_tail_mode")
+
     def set_lift_timing(self, on: bool):
         check(self.lib.rkv_set_lift_timing(self.h, int(bool(on))), "rkv_set_lift_timing")
 
@@ -189,6 +195,16 @@ def lse_merge(partials, n_seg: int, n_rows: int, o, lse=None, stream=None):
     lib = load()
     check(lib.rkv_lse_merge(_ptr(partials), int(n_seg), int(n_rows), 128, _ptr(o), _ptr(lse), _stream(stream)),
           "rkv_lse_merge")
+
+
+def tail_partial_host(q, k, v, mask, kv_pos0: int, q_pos0: int, scale: float, partial, softcap: float = 0.0,
+                      n_threads: int = 0):
+    """Tail partial on the host cores: q, k, v, mask are descriptors of host (CPU) memory,
+    partial a float32 CPU tensor (n_q, n_head, 130) receiving (M, S, VKQ) per row."""
+    lib = load()
+    check(lib.rkv_tail_partial_host(_ref(q), _ref(k), _ref(v), _ref(mask), int(kv_pos0), int(q_pos0),
+                                    float(scale), float(softcap), _ptr(partial), int(n_threads)),
+          "rkv_tail_partial_host")
 
 
 def dequant_rows(src, type_id: int, n_rows: int, row_stride: int, dst, stream=None):

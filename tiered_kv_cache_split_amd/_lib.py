@@ -11,6 +11,7 @@ RKV_TYPE_F32, RKV_TYPE_F16, RKV_TYPE_Q4_0, RKV_TYPE_Q8_0 = 0, 1, 2, 8
 RKV_OK, RKV_ERR_ARG, RKV_ERR_UNSUPPORTED, RKV_ERR_HIP, RKV_ERR_NOMEM, RKV_ERR_CAPTURE = 0, -1, -2, -3, -4, -5
 RKV_LIFT_BULK, RKV_LIFT_UVA = 0, 1
 RKV_RESIDENCY_AUTO, RKV_RESIDENCY_RESIDENT, RKV_RESIDENCY_WINDOW = 0, 1, 2
+RKV_TAIL_LIFT, RKV_TAIL_HOST = 0, 1
 
 i64 = ctypes.c_int64
 vp = ctypes.c_void_p
@@ -24,7 +25,8 @@ class RkvStats(ctypes.Structure):
     _fields_ = [("n_segments", ctypes.c_int32), ("n_partials", ctypes.c_int32),
                 ("n_tail_tiles", ctypes.c_int32), ("lift_mode", ctypes.c_int32),
                 ("lift_bytes", i64), ("splits_window", ctypes.c_int32),
-                ("kernel_variant", ctypes.c_int32)]
+                ("kernel_variant", ctypes.c_int32), ("tail_host", ctypes.c_int32),
+                ("host_tail_ms", ctypes.c_float)]
 
 
 TP = ctypes.POINTER(RkvTensor)
@@ -53,6 +55,9 @@ SIGNATURES = {
     "rkv_tail_lift": (ctypes.c_int, [vp, vp, i64, ctypes.c_int, ctypes.c_int, ctypes.POINTER(vp), vp]),
     "rkv_dequant_rows": (ctypes.c_int, [vp, ctypes.c_int, i64, i64, vp, vp]),
     "rkv_set_softcap": (ctypes.c_int, [vp, ctypes.c_float]),
+    "rkv_set_tail_mode": (ctypes.c_int, [vp, ctypes.c_int, ctypes.c_int]),
+    "rkv_tail_partial_host": (ctypes.c_int, [TP, TP, TP, TP, i64, i64, ctypes.c_float, ctypes.c_float, vp,
+                                             ctypes.c_int]),
     "rkv_plan_window": (ctypes.c_int, [vp, i64, i64, i64, i64, i64, i64, ctypes.POINTER(i64)]),
     "rkv_window_mode": (ctypes.c_int, [ctypes.c_int, i64, i64, ctypes.c_int, ctypes.c_int,
                                        ctypes.POINTER(ctypes.c_int)]),

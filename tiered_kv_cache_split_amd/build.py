@@ -14,7 +14,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "librkv.so")
-SOURCES = ["rkv_decode.hip", "rkv_decode_mma.hip", "rkv_decode_mma16.hip", "rkv_prefill.hip", "rkv_merge.hip", "rkv_aux.hip", "rkv_runtime.cpp"]
+SOURCES = ["rkv_decode.hip", "rkv_decode_mma.hip", "rkv_decode_mma16.hip", "rkv_prefill.hip", "rkv_merge.hip", "rkv_aux.hip", "rkv_host_tail.cpp", "rkv_runtime.cpp"]
+# host code only (the CPU tail partial): no device pass
+HOST_ONLY = {"rkv_host_tail.cpp"}
 ARCH = "gfx950"
 # Packed FP32 instructions are disabled for all device code (their generated forms are
 # avoided on this target); the host pass ignores the feature with a warning.
@@ -38,7 +40,7 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
     for src in SOURCES:
         obj = os.path.join(objdir, src + ".o")
         objs.append(obj)
-        lang = ["-x", "hip"]
+        lang = ["-x", "hip"] + (["--offload-host-only"] if src in HOST_ONLY else [])
         cmd = [cc, *lang, f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-c",
                os.path.join(CSRC, src), "-o", obj, f"-I{INCLUDE}", f"-I{CSRC}", *DEVICE_FLAGS]
         if verbose:

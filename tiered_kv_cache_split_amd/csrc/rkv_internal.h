@@ -113,4 +113,24 @@ hipError_t launch_uva_read(const void *host_src, void *dst, int64_t nbytes, hipS
 hipError_t launch_dequant_rows(const void *src, int type, int64_t n_rows, int64_t row_stride,
                                float *dst, hipStream_t s);
 
+// Tail partial on the host cores (rkv_host_tail.cpp).  Every pointer is host memory.
+struct HostTailArgs {
+    const uint16_t *q;        // binary16 queries; element strides of query i and head h
+    int64_t q_s1, q_s2;
+    const uint8_t *k, *v;     // K/V rows of the segment; byte strides per cell and KV head
+    int64_t k_s1, k_s2, v_s1, v_s2;
+    int k_type, v_type;
+    const uint16_t *mask;     // additive binary16, column j = segment cell j; element stride
+    int64_t m_s1;             // of query i; NULL: all visible
+    int64_t n_cells;          // keys in the segment
+    int64_t kv_pos0;          // global position of cell 0 (causal rule)
+    int64_t q_pos0;           // >= 0: query i at q_pos0 + i sees positions <= its own
+    int n_head, n_head_kv, n_q;
+    float scale, softcap;     // softcap 0: none
+    float *partial;           // [n_head * n_q][2 + 128], row h + n_head * i
+};
+bool host_tail_supported();          // the CPU has AVX2, FMA and F16C
+int host_tail_threads(int requested);  // requested > 0, else the hardware threads (<= 16)
+void host_tail_partial(const HostTailArgs &a, int n_threads);
+
 }  // namespace rkv

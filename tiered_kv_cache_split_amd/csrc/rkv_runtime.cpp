@@ -16,6 +16,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <chrono>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -178,6 +179,14 @@ struct rkv_ctx {
     int lift_mode = RKV_LIFT_BULK;
     int splits_override = 0;
     float softcap = 0.f;  // logit soft-cap of later calls (0: none)
+    // host tail partial (RKV_TAIL_HOST): pinned staging of Q, the tail's mask columns and the
+    // partial; host_in marks Q/mask on the host, host_up the partial's upload
+    int tail_mode = RKV_TAIL_LIFT;
+    int host_threads = 0;
+    void *hq = nullptr, *hmask = nullptr, *hpart = nullptr;
+    size_t hq_cap = 0, hmask_cap = 0, hpart_cap = 0;
+    hipEvent_t host_in = nullptr, host_up = nullptr;
+    bool host_up_pending = false;
     rkv_stats stats = {};
 };
 
@@ -224,6 +233,23 @@ int grow(void **buf, size_t *cap, size_t need, hipStream_t s) {
         (void)hipGetLastError();
         *buf = nullptr;
         return fail(RKV_ERR_NOMEM, "hipMalloc(%zu) failed", need);
+    }
+    *cap = need;
+    return RKV_OK;
+}
+
+// Grow-only pinned host buffer (hipHostMalloc); the caller has made sure no copy still
+// reads or writes the old one.
+int grow_host(void **buf, size_t *cap, size_t need) {
+    if (need <= *cap) return RKV_OK;
+    if (*buf) (void)hipHostFree(*buf);
+    *buf = nullptr;
+    *cap = 0;
+    hipError_t e = hipHostMalloc(buf, need, hipHostMallocDefault);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        *buf = nullptr;
+        return fail(RKV_ERR_NOMEM, "pinned host allocation of %zu bytes failed", need);
     }
     *cap = need;
     return RKV_OK;
@@ -463,7 +489,8 @@ int attn_window_tail(rkv_ctx *ctx, const rkv_tensor *q, const rkv_tensor *k_win,
         if (n_tail > 0) {
             const Mem a = pointer_kind(k_tail->data), b = pointer_kind(v_tail->data);
             if (a != b) return fail(RKV_ERR_ARG, "k_tail and v_tail live in different memory kinds");
-            if (a == Mem::Other) return fail(RKV_ERR_ARG, "tail is neither device nor pinned host memory (pageable memory cannot be lifted)");
+            if (a == Mem::Other && (ctx->tail_mode != RKV_TAIL_HOST || mfma))
+                return fail(RKV_ERR_ARG, "tail is neither device nor pinned host memory (pageable memory cannot be lifted)");
             tail_kind = a;
         }
     }
@@ -496,8 +523,10 @@ int attn_window_tail(rkv_ctx *ctx, const rkv_tensor *q, const rkv_tensor *k_win,
     fill_softcap(base, ctx, scale);
     base.n_rows = n_head * n_q;
 
-    // ---- plan: window segment, then tail (in place, or lifted tiles through the ring)
-    const bool lifted = n_tail > 0 && tail_kind == Mem::PinnedHost;
+    // ---- plan: window segment, then tail (in place, lifted tiles through the ring, or a
+    // partial computed on the host cores)
+    const bool host_tail = n_tail > 0 && tail_kind != Mem::Device && ctx->tail_mode == RKV_TAIL_HOST && !mfma;
+    const bool lifted = n_tail > 0 && tail_kind == Mem::PinnedHost && !host_tail;
     const int64_t n_tiles = lifted ? (n_tail + tile_kv - 1) / tile_kv : 0;
     TailGeom gk{}, gv{};
     int n_slots = 0;
@@ -530,6 +559,7 @@ int attn_window_tail(rkv_ctx *ctx, const rkv_tensor *q, const rkv_tensor *k_win,
     if (wc > 0) total_slots += plan_segment(ctx, base, win, mfma, k_type, v_type).n_splits;
     if (n_tail > 0 && !lifted) total_slots += plan_segment(ctx, base, dtail, mfma, k_type, v_type).n_splits;
     for (int64_t t = 0; t < n_tiles; ++t) total_slots += plan_segment(ctx, base, tile_seg(t), mfma, k_type, v_type).n_splits;
+    if (host_tail) total_slots += 1;
     if (total_slots == 0) total_slots = 1;  // n_kv == 0: one empty partial
     if ((st = ensure_partials(ctx, total_slots * base.n_rows * kPartialStride, stream))) return st;
     base.partials = ctx->partials;
@@ -538,6 +568,29 @@ int attn_window_tail(rkv_ctx *ctx, const rkv_tensor *q, const rkv_tensor *k_win,
     ctx->stats.kernel_variant = mfma ? RKV_KERNEL_PREFILL_MFMA : RKV_KERNEL_DECODE_HEAD;
     ctx->stats.lift_mode = ctx->lift_mode;
     int slot = 0;
+
+    // host tail: Q (and the tail's mask columns) go to pinned host memory ahead of the window
+    // kernels, so the host computes the tail partial while the GPU computes the window
+    const int64_t q_span = (n_q - 1) * q->nb[1] + (n_head - 1) * q->nb[2] + kHeadDim * 2;
+    if (host_tail) {
+        if (stream_capturing(stream)) return fail(RKV_ERR_CAPTURE, "the host tail partial cannot run inside graph capture");
+        if (!host_tail_supported()) return fail(RKV_ERR_UNSUPPORTED, "the host tail partial needs a CPU with AVX2, FMA and F16C");
+        if (ctx->host_up_pending) {  // the previous call's upload still reads the partial buffer
+            RKV_HIP(hipEventSynchronize(ctx->host_up));
+            ctx->host_up_pending = false;
+        }
+        if ((st = grow_host(&ctx->hq, &ctx->hq_cap, (size_t)q_span)) ||
+            (mask && (st = grow_host(&ctx->hmask, &ctx->hmask_cap, (size_t)(n_q * n_tail * 2)))) ||
+            (st = grow_host(&ctx->hpart, &ctx->hpart_cap, (size_t)(base.n_rows * kPartialStride * 4))))
+            return st;
+        if (!ctx->host_in) RKV_HIP(hipEventCreateWithFlags(&ctx->host_in, hipEventDisableTiming));
+        if (!ctx->host_up) RKV_HIP(hipEventCreateWithFlags(&ctx->host_up, hipEventDisableTiming));
+        RKV_HIP(hipMemcpyAsync(ctx->hq, q->data, (size_t)q_span, hipMemcpyDeviceToHost, stream));
+        if (mask)
+            RKV_HIP(hipMemcpy2DAsync(ctx->hmask, (size_t)(n_tail * 2), static_cast<const uint8_t *>(mask->data) + wc * 2,
+                                     (size_t)mask->nb[1], (size_t)(n_tail * 2), (size_t)n_q, hipMemcpyDeviceToHost, stream));
+        RKV_HIP(hipEventRecord(ctx->host_in, stream));
+    }
 
     if (lifted) {
         // the copy stream starts after all earlier work on the compute stream, so a slot
@@ -568,8 +621,43 @@ int attn_window_tail(rkv_ctx *ctx, const rkv_tensor *q, const rkv_tensor *k_win,
         if ((st = run_segment(ctx, base, win, mfma, k_type, v_type, slot, stream))) return st;
         ctx->stats.splits_window = slot - before;
     }
-    if (n_tail > 0 && !lifted) {
+    if (n_tail > 0 && !lifted && !host_tail) {
         if ((st = run_segment(ctx, base, dtail, mfma, k_type, v_type, slot, stream))) return st;
+    }
+    if (host_tail) {
+        RKV_HIP(hipEventSynchronize(ctx->host_in));
+        HostTailArgs ha{};
+        ha.q = static_cast<const uint16_t *>(ctx->hq);
+        ha.q_s1 = q->nb[1] / 2;
+        ha.q_s2 = q->nb[2] / 2;
+        ha.k = static_cast<const uint8_t *>(k_tail->data);
+        ha.v = static_cast<const uint8_t *>(v_tail->data);
+        ha.k_s1 = k_tail->nb[1];
+        ha.k_s2 = k_tail->nb[2];
+        ha.v_s1 = v_tail->nb[1];
+        ha.v_s2 = v_tail->nb[2];
+        ha.k_type = k_type;
+        ha.v_type = v_type;
+        ha.mask = mask ? static_cast<const uint16_t *>(ctx->hmask) : nullptr;
+        ha.m_s1 = n_tail;
+        ha.n_cells = n_tail;
+        ha.kv_pos0 = wc;
+        ha.q_pos0 = q_pos0;
+        ha.n_head = (int)n_head;
+        ha.n_head_kv = (int)n_head_kv;
+        ha.n_q = (int)n_q;
+        ha.scale = scale;
+        ha.softcap = ctx->softcap;
+        ha.partial = static_cast<float *>(ctx->hpart);
+        const auto t0 = std::chrono::steady_clock::now();
+        host_tail_partial(ha, ctx->host_threads);
+        ctx->stats.host_tail_ms = std::chrono::duration<float, std::milli>(std::chrono::steady_clock::now() - t0).count();
+        ctx->stats.tail_host = 1;
+        RKV_HIP(hipMemcpyAsync(ctx->partials + (int64_t)slot * base.n_rows * kPartialStride, ctx->hpart,
+                               (size_t)(base.n_rows * kPartialStride * 4), hipMemcpyHostToDevice, stream));
+        RKV_HIP(hipEventRecord(ctx->host_up, stream));
+        ctx->host_up_pending = true;
+        slot += 1;
     }
     for (int64_t t = 0; t < n_tiles; ++t) {
         const int sl = (int)(t % n_slots);
@@ -671,6 +759,11 @@ void rkv_destroy(rkv_ctx *c) {
     if (c->row_extent) (void)hipFree(c->row_extent);
     if (c->pair_range) (void)hipFree(c->pair_range);
     if (c->copy_stream) (void)hipStreamDestroy(c->copy_stream);
+    if (c->host_in) (void)hipEventDestroy(c->host_in);
+    if (c->host_up) (void)hipEventDestroy(c->host_up);
+    if (c->hq) (void)hipHostFree(c->hq);
+    if (c->hmask) (void)hipHostFree(c->hmask);
+    if (c->hpart) (void)hipHostFree(c->hpart);
     (void)hipGetLastError();
     delete c;
 }
@@ -744,6 +837,70 @@ int rkv_window_mode(int mode, int64_t wc, int64_t kv_size, int append_only, int 
         return fail(RKV_ERR_ARG, "unknown residency mode %d", mode);
     const bool eligible = wc > 0 && wc < kv_size && append_only != 0 && v_transposed == 0;
     *window = (eligible && mode != RKV_RESIDENCY_RESIDENT) ? 1 : 0;
+    return RKV_OK;
+}
+
+int rkv_set_tail_mode(rkv_ctx *ctx, int mode, int n_threads) {
+    if (!ctx) return fail(RKV_ERR_ARG, "ctx is NULL");
+    if (mode != RKV_TAIL_LIFT && mode != RKV_TAIL_HOST) return fail(RKV_ERR_ARG, "unknown tail mode %d", mode);
+    if (n_threads < 0 || n_threads > 256) return fail(RKV_ERR_ARG, "n_threads must be in [0, 256]");
+    ctx->tail_mode = mode;
+    ctx->host_threads = n_threads;
+    return RKV_OK;
+}
+
+int rkv_tail_partial_host(const rkv_tensor *q, const rkv_tensor *k, const rkv_tensor *v, const rkv_tensor *mask,
+                          int64_t kv_pos0, int64_t q_pos0, float scale, float softcap, float *partial,
+                          int n_threads) {
+    if (!q || !q->data) return fail(RKV_ERR_ARG, "q is NULL");
+    if (q->type != RKV_TYPE_F16) return fail(RKV_ERR_UNSUPPORTED, "q must be F16");
+    if (q->ne[0] != kHeadDim) return fail(RKV_ERR_UNSUPPORTED, "q head dim must be 128");
+    if (q->ne[1] <= 0 || q->ne[2] <= 0 || q->ne[3] != 1) return fail(RKV_ERR_ARG, "q: bad shape");
+    if (q->nb[0] != 2 || q->nb[1] % 2 != 0 || q->nb[2] % 2 != 0 || q->nb[1] < 0 || q->nb[2] < 0)
+        return fail(RKV_ERR_ARG, "q rows must be contiguous and strides even");
+    int st;
+    if ((st = check_kv(k, "k", true)) || (st = check_kv(v, "v", false))) return st;
+    if (k->ne[1] != v->ne[1] || k->ne[2] != v->ne[2]) return fail(RKV_ERR_ARG, "k and v disagree in shape");
+    const int64_t n_q = q->ne[1], n_head = q->ne[2], n_head_kv = k->ne[2], n_cells = k->ne[1];
+    if (n_head % n_head_kv != 0) return fail(RKV_ERR_ARG, "n_head %% n_head_kv != 0");
+    if (kv_pos0 < 0) return fail(RKV_ERR_ARG, "kv_pos0 < 0");
+    if (q_pos0 < -1) return fail(RKV_ERR_ARG, "q_pos0 must be >= -1");
+    if (!std::isfinite(scale)) return fail(RKV_ERR_ARG, "scale is not finite");
+    if (!(softcap >= 0.f) || !std::isfinite(softcap)) return fail(RKV_ERR_ARG, "softcap must be finite and >= 0");
+    if (!partial) return fail(RKV_ERR_ARG, "partial is NULL");
+    if (n_threads < 0 || n_threads > 256) return fail(RKV_ERR_ARG, "n_threads must be in [0, 256]");
+    if (mask) {
+        if (!mask->data) return fail(RKV_ERR_ARG, "mask data is NULL");
+        if (mask->type != RKV_TYPE_F16 || mask->nb[0] != 2) return fail(RKV_ERR_UNSUPPORTED, "mask must be contiguous F16");
+        if (mask->ne[0] < kv_pos0 + n_cells || mask->ne[1] < n_q || mask->ne[3] != 1)
+            return fail(RKV_ERR_ARG, "mask smaller than [kv_pos0 + n_cells, n_q]");
+        if (mask->nb[1] % 2 != 0) return fail(RKV_ERR_ARG, "mask strides must be even");
+    }
+    if (!host_tail_supported()) return fail(RKV_ERR_UNSUPPORTED, "the host tail partial needs a CPU with AVX2, FMA and F16C");
+    HostTailArgs ha{};
+    ha.q = static_cast<const uint16_t *>(q->data);
+    ha.q_s1 = q->nb[1] / 2;
+    ha.q_s2 = q->nb[2] / 2;
+    ha.k = static_cast<const uint8_t *>(k->data);
+    ha.v = static_cast<const uint8_t *>(v->data);
+    ha.k_s1 = k->nb[1];
+    ha.k_s2 = k->nb[2];
+    ha.v_s1 = v->nb[1];
+    ha.v_s2 = v->nb[2];
+    ha.k_type = k->type;
+    ha.v_type = v->type;
+    ha.mask = mask ? static_cast<const uint16_t *>(mask->data) + kv_pos0 : nullptr;
+    ha.m_s1 = mask ? mask->nb[1] / 2 : 0;
+    ha.n_cells = n_cells;
+    ha.kv_pos0 = kv_pos0;
+    ha.q_pos0 = q_pos0;
+    ha.n_head = (int)n_head;
+    ha.n_head_kv = (int)n_head_kv;
+    ha.n_q = (int)n_q;
+    ha.scale = scale;
+    ha.softcap = softcap;
+    ha.partial = partial;
+    host_tail_partial(ha, n_threads);
     return RKV_OK;
 }
 
