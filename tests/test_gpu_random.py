@@ -114,3 +114,35 @@ def test_random_prefill(run, seed):
         m = m + np.asarray(mask, dtype=np.float64)
     Oref, Lref = oracle_decode(w, mask=m, softcap=cap)
     assert_close(O, L, Oref, Lref, what=f"random prefill {seed}")
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_host_tail(run, seed):
+    """Decode with the tail partial on the host cores: random shapes, types, layouts, window
+    sizes, masks, soft-caps, thread counts, pinned or pageable tails."""
+    rng = np.random.default_rng(4000 + seed)
+    n_head_kv = int(rng.choice([1, 2, 4, 8]))
+    gqa = int(rng.choice([1, 2, 4, 5, 8]))
+    n_q = 1 if gqa > 4 else int(rng.choice([1, 2]))
+    n_kv = int(rng.integers(2, 2500))
+    kt, vt = TYPES[int(rng.integers(0, 4))]
+    wc = int(rng.integers(0, n_kv))
+    layout = str(rng.choice(["cell", "head"]))
+    tail = str(rng.choice(["host", "pageable"]))
+    threads = int(rng.integers(1, 17))
+    q, k, v = gen.draw_qkv(rng, n_head_kv * gqa, n_q, n_head_kv, n_kv, k_type=kt, v_type=vt)
+    w = dict(n_head=n_head_kv * gqa, n_head_kv=n_head_kv, q=q, k=k, v=v, k_type=kt, v_type=vt,
+             scale=1 / np.sqrt(128), n_kv=n_kv, wc=wc, tile_kv=int(rng.integers(1, 2000)))
+    mask = gen.random_mask_f16(rng, n_q, n_kv, p_hidden=0.3) if rng.random() < 0.5 else None
+    cap = draw_softcap(300 + seed)
+    step(f"random host tail seed {seed}: heads {n_head_kv}x{gqa} n_q {n_q} n_kv {n_kv} wc {wc} types {kt}/{vt} "
+         f"layout {layout} tail {tail} threads {threads} mask {mask is not None} softcap {cap:.3f}")
+    run.ctx.set_softcap(cap)
+    run.ctx.set_tail_mode(run.rkv.RKV_TAIL_HOST, threads)
+    try:
+        O, L = run.decode(w, tail=tail, mask=mask, layout=layout)
+        assert run.ctx.stats()["tail_host"] == 1
+    finally:
+        run.ctx.set_tail_mode(run.rkv.RKV_TAIL_LIFT)
+    Oref, Lref = oracle_decode(w, mask=mask, softcap=cap)
+    assert_close(O, L, Oref, Lref, what=f"random host tail {seed}")

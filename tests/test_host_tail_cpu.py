@@ -165,3 +165,32 @@ def test_argument_errors(rkv):
     bad.type = _lib.RKV_TYPE_F32
     assert lib.rkv_tail_partial_host(ctypes.byref(qd), ctypes.byref(bad), ctypes.byref(vd), None, 0, -1, 0.1, 0.0,
                                      part.data_ptr(), 0) == _lib.RKV_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_shapes(rkv, seed):
+    """Random heads (gqa up to 16: several row groups of a KV head), queries, lengths, types,
+    layouts, masks, causal positions, soft-caps and thread counts."""
+    rng = np.random.default_rng(6000 + seed)
+    n_head_kv = int(rng.choice([1, 2, 3, 8]))
+    gqa = int(rng.choice([1, 3, 5, 8, 12, 16]))
+    n_q = int(rng.integers(1, 5))
+    n_cells = int(rng.integers(0, 1500))
+    kv_pos0 = int(rng.integers(0, 3000))
+    kt, vt = [(gen.TYPE_F16, gen.TYPE_F16), (gen.TYPE_Q8_0, gen.TYPE_Q4_0), (gen.TYPE_Q8_0, gen.TYPE_F16),
+              (gen.TYPE_F16, gen.TYPE_Q4_0)][int(rng.integers(0, 4))]
+    q, k, v = gen.draw_qkv(rng, n_head_kv * gqa, n_q, n_head_kv, n_cells, k_type=kt, v_type=vt)
+    mask = gen.random_mask_f16(rng, n_q, kv_pos0 + n_cells, p_hidden=0.3) if rng.random() < 0.5 else None
+    q_pos0 = int(rng.integers(kv_pos0 - 5, kv_pos0 + n_cells + 5)) if rng.random() < 0.4 else -1
+    q_pos0 = max(q_pos0, -1)
+    cap = float(rng.uniform(0.5, 5.0)) if rng.random() < 0.3 else 0.0
+    layout = str(rng.choice(["cell", "head"]))
+    host = run_host(rkv, q, k, v, kt, vt, mask=mask, kv_pos0=kv_pos0, q_pos0=q_pos0, softcap=cap, layout=layout,
+                    n_threads=int(rng.integers(1, 9)))
+    cols = np.zeros((n_q, n_cells))
+    if mask is not None:
+        cols = cols + np.asarray(mask[:, kv_pos0:kv_pos0 + n_cells], dtype=np.float64)
+    if q_pos0 >= 0:
+        cols = cols + oracle.causal_mask(n_q, kv_pos0 + n_cells, q_pos0)[:, kv_pos0:]
+    ref = oracle_partial(q, k, v, kt, vt, cols, softcap=cap)
+    check_partial(host, ref, f"random {seed}")
