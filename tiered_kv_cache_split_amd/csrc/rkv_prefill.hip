@@ -349,6 +349,16 @@ prefill_seg_kernel(const SegParams p, int q_tiles, int n_tasks) {
                 }
             }
         }
+        // schedule: three operand reads in flight ahead of the MFMA that consumes them (the
+        // default schedule issues each read one MFMA ahead and waits on it)
+        constexpr int kNM = KT == T_Q8_0 ? 32 : 16, LA = 3;
+        __builtin_amdgcn_sched_group_barrier(0x100, LA, 0);
+#pragma unroll
+        for (int i = 0; i < kNM - LA; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, LA, 0);
 
         // ---- visibility: whole tile visible to every row of the wave, or per element
         const bool full = (c0 + kBN <= p.n_cells) && !p.mask &&
