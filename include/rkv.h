@@ -65,7 +65,7 @@ enum rkv_status {
     RKV_ERR_ARG = -1,          /* malformed argument (shape, stride, pointer kind)        */
     RKV_ERR_UNSUPPORTED = -2,  /* well-formed but outside what the kernels implement      */
     RKV_ERR_HIP = -3,          /* a HIP runtime call failed                                */
-    RKV_ERR_NOMEM = -4,        /* device allocation failed                                 */
+    RKV_ERR_NOMEM = -4,        /* device, pinned or host allocation failed                */
     RKV_ERR_CAPTURE = -5       /* workspace growth needed while the stream is capturing    */
 };
 

@@ -260,7 +260,12 @@ void host_tail_partial(const HostTailArgs &a, int n_threads) {
     };
     const int nt = (int)std::min<int64_t>(threads, n_units);
     std::vector<std::thread> pool;
-    for (int t = 1; t < nt; ++t) pool.emplace_back(worker);
+    pool.reserve(nt);
+    try {
+        for (int t = 1; t < nt; ++t) pool.emplace_back(worker);
+    } catch (...) {
+        // no more threads available: the ones started and this one take every unit
+    }
     worker();
     for (auto &th : pool) th.join();
     // merge each row's chunks in chunk order

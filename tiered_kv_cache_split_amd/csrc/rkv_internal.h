@@ -131,6 +131,7 @@ struct HostTailArgs {
 };
 bool host_tail_supported();          // the CPU has AVX2, FMA and F16C
 int host_tail_threads(int requested);  // requested > 0, else the hardware threads (<= 16)
+// May throw std::bad_alloc (the chunk partials); thread creation failures are absorbed.
 void host_tail_partial(const HostTailArgs &a, int n_threads);
 
 }  // namespace rkv

@@ -650,7 +650,11 @@ int attn_window_tail(rkv_ctx *ctx, const rkv_tensor *q, const rkv_tensor *k_win,
         ha.softcap = ctx->softcap;
         ha.partial = static_cast<float *>(ctx->hpart);
         const auto t0 = std::chrono::steady_clock::now();
-        host_tail_partial(ha, ctx->host_threads);
+        try {
+            host_tail_partial(ha, ctx->host_threads);
+        } catch (...) {
+            return fail(RKV_ERR_NOMEM, "host memory for the tail partial's chunk partials");
+        }
         ctx->stats.host_tail_ms = std::chrono::duration<float, std::milli>(std::chrono::steady_clock::now() - t0).count();
         ctx->stats.tail_host = 1;
         RKV_HIP(hipMemcpyAsync(ctx->partials + (int64_t)slot * base.n_rows * kPartialStride, ctx->hpart,
@@ -900,7 +904,11 @@ int rkv_tail_partial_host(const rkv_tensor *q, const rkv_tensor *k, const rkv_te
     ha.scale = scale;
     ha.softcap = softcap;
     ha.partial = partial;
-    host_tail_partial(ha, n_threads);
+    try {
+        host_tail_partial(ha, n_threads);
+    } catch (...) {
+        return fail(RKV_ERR_NOMEM, "host memory for the tail partial's chunk partials");
+    }
     return RKV_OK;
 }
 
