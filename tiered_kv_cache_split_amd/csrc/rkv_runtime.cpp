@@ -579,6 +579,9 @@ int attn_window_tail(rkv_ctx *ctx, const rkv_tensor *q, const rkv_tensor *k_win,
             RKV_HIP(hipEventSynchronize(ctx->host_up));
             ctx->host_up_pending = false;
         }
+        // a previous call that failed between its Q copy and its wait may still be writing the
+        // staging buffers: let that copy land before they are reused or regrown
+        if (ctx->host_in) RKV_HIP(hipEventSynchronize(ctx->host_in));
         if ((st = grow_host(&ctx->hq, &ctx->hq_cap, (size_t)q_span)) ||
             (mask && (st = grow_host(&ctx->hmask, &ctx->hmask_cap, (size_t)(n_q * n_tail * 2)))) ||
             (st = grow_host(&ctx->hpart, &ctx->hpart_cap, (size_t)(base.n_rows * kPartialStride * 4))))
