@@ -262,8 +262,9 @@ def main():
     ap.add_argument("--softcap", type=float, default=0.0, help="logit soft-cap c (0: none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--lift-mode", type=int, default=0, help="0 bulk DMA, 1 word-granularity UVA read")
-    ap.add_argument("--tail-mode", choices=["lift", "host"], default="lift",
-                    help="host tail: lifted to the GPU in tiles, or its partial computed on the host cores")
+    ap.add_argument("--tail-mode", choices=["lift", "host", "auto"], default="lift",
+                    help="host tail: lifted to the GPU in tiles, its partial computed on the host cores, or "
+                         "whichever the measured link and host rates make faster")
     ap.add_argument("--host-threads", type=int, default=16, help="host threads of the host tail partial")
     ap.add_argument("--copy-only", action="store_true",
                     help="only run a plain 1 GiB device copy (calibrates HBM byte counters)")
@@ -294,6 +295,22 @@ def main():
         ctx.set_lift_mode(args.lift_mode)
     if args.softcap:
         ctx.set_softcap(args.softcap)
+    tail_choice = None
+    if args.tail_mode == "auto" and st.get("tail_bytes"):
+        # rates on this machine: pinned H2D copies, and two calls with the host partial
+        h2d = measured_h2d_gbs()
+        ctx.set_tail_mode(rkv.RKV_TAIL_HOST, args.host_threads)
+        host_ms = []
+        for i in range(2):
+            call(ctx, st, i)
+            host_ms.append(ctx.stats()["host_tail_ms"])
+        torch.cuda.synchronize()
+        host_gbs = st["tail_bytes"] / (min(host_ms) * 1e-3) / 1e9
+        mode = rkv.choose_tail_mode(st["tail_bytes"], h2d, host_gbs)
+        tail_choice = {"h2d_GBps": round(h2d, 2), "host_GBps": round(host_gbs, 2),
+                       "chosen": "host" if mode == rkv.RKV_TAIL_HOST else "lift"}
+        ctx.set_tail_mode(rkv.RKV_TAIL_LIFT)
+        args.tail_mode = tail_choice["chosen"]
     host_tail = args.tail_mode == "host" and bool(st.get("tail_bytes"))
     if host_tail:
         ctx.set_tail_mode(rkv.RKV_TAIL_HOST, args.host_threads)
@@ -400,6 +417,8 @@ def main():
         out["host_tail"] = {"tail_bytes": st["tail_bytes"], "threads": args.host_threads, "host_ms_median": round(hm, 4),
                             "host_GBps": round(st["tail_bytes"] / (hm * 1e-3) / 1e9, 2),
                             "partial_bytes_uploaded": int(w["n_head"] * w["q"].shape[-2] * 130 * 4)}
+    if tail_choice:
+        out["tail_choice"] = tail_choice
     out["measured_copy_GBps"] = round(measured_copy_gbs(), 1)
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host cores", file=sys.stderr, flush=True)

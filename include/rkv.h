@@ -273,6 +273,15 @@ int rkv_tail_partial_host(const rkv_tensor *q, const rkv_tensor *k, const rkv_te
                           const rkv_tensor *mask, int64_t kv_pos0, int64_t q_pos0, float scale,
                           float softcap, float *partial, int n_threads);
 
+/* Tail tactic from measured rates (patch 0070: the CPU_FA_TAIL tactic exists for slow links,
+ * and an effective host-to-device bandwidth knob, autodetected or set by hand, drives the
+ * streaming path).  A lifted tail moves its tail_bytes over the link at h2d_gbps; a host tail
+ * partial reads them on the host cores at host_gbps, and only 2 + dv floats per row cross the
+ * link.  *mode receives RKV_TAIL_HOST when tail_bytes / host_gbps < tail_bytes / h2d_gbps,
+ * RKV_TAIL_LIFT otherwise (the default wins ties and an empty tail).  Pure host arithmetic.
+ * Errors: RKV_ERR_ARG for a NULL mode, a negative size or a rate that is not finite and > 0. */
+int rkv_choose_tail_mode(int64_t tail_bytes, double h2d_gbps, double host_gbps, int *mode);
+
 /* Logit soft-cap of every later attention call on the context (patch 0070,
  * streaming_lse_kernel soft-cap branch): each scaled score scale*<q,k> becomes
  * softcap * tanh(scale*<q,k> / softcap), before the mask is added.  0 (the default) turns

@@ -194,3 +194,23 @@ def test_random_shapes(rkv, seed):
         cols = cols + oracle.causal_mask(n_q, kv_pos0 + n_cells, q_pos0)[:, kv_pos0:]
     ref = oracle_partial(q, k, v, kt, vt, cols, softcap=cap)
     check_partial(host, ref, f"random {seed}")
+
+
+def test_choose_tail_mode(rkv):
+    """The tactic with the shorter tail time: host partial only when the host cores read the
+    tail faster than the link lifts it; the lift wins ties, an empty tail and bad rates fail."""
+    from tiered_kv_cache_split_amd import _lib
+    tb = 218103808
+    assert rkv.choose_tail_mode(tb, 57.0, 48.9) == rkv.RKV_TAIL_LIFT      # the MI355X box measured here
+    assert rkv.choose_tail_mode(tb, 12.0, 48.9) == rkv.RKV_TAIL_HOST      # a slow link (UVA-class rates)
+    assert rkv.choose_tail_mode(tb, 30.0, 30.0) == rkv.RKV_TAIL_LIFT      # tie
+    assert rkv.choose_tail_mode(0, 1.0, 100.0) == rkv.RKV_TAIL_LIFT       # nothing to move
+    rng = np.random.default_rng(7)
+    for _ in range(200):
+        b, h, c = int(rng.integers(1, 1 << 40)), float(rng.uniform(0.1, 200)), float(rng.uniform(0.1, 200))
+        want = rkv.RKV_TAIL_HOST if b / c < b / h else rkv.RKV_TAIL_LIFT
+        assert rkv.choose_tail_mode(b, h, c) == want
+    for bad in ((-1, 1.0, 1.0), (1, 0.0, 1.0), (1, 1.0, -2.0), (1, float("inf"), 1.0), (1, 1.0, float("nan"))):
+        with pytest.raises(_lib.RkvError) as e:
+            rkv.choose_tail_mode(*bad)
+        assert e.value.status == _lib.RKV_ERR_ARG

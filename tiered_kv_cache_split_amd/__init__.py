@@ -207,6 +207,15 @@ def tail_partial_host(q, k, v, mask, kv_pos0: int, q_pos0: int, scale: float, pa
           "rkv_tail_partial_host")
 
 
+def choose_tail_mode(tail_bytes: int, h2d_gbps: float, host_gbps: float) -> int:
+    """RKV_TAIL_HOST when the host cores read the tail faster than the link lifts it, else RKV_TAIL_LIFT."""
+    lib = load()
+    m = ctypes.c_int()
+    check(lib.rkv_choose_tail_mode(int(tail_bytes), float(h2d_gbps), float(host_gbps), ctypes.byref(m)),
+          "rkv_choose_tail_mode")
+    return m.value
+
+
 def dequant_rows(src, type_id: int, n_rows: int, row_stride: int, dst, stream=None):
     lib = load()
     check(lib.rkv_dequant_rows(_ptr(src), int(type_id), int(n_rows), int(row_stride), _ptr(dst),

@@ -56,6 +56,7 @@ SIGNATURES = {
     "rkv_dequant_rows": (ctypes.c_int, [vp, ctypes.c_int, i64, i64, vp, vp]),
     "rkv_set_softcap": (ctypes.c_int, [vp, ctypes.c_float]),
     "rkv_set_tail_mode": (ctypes.c_int, [vp, ctypes.c_int, ctypes.c_int]),
+    "rkv_choose_tail_mode": (ctypes.c_int, [i64, ctypes.c_double, ctypes.c_double, ctypes.POINTER(ctypes.c_int)]),
     "rkv_tail_partial_host": (ctypes.c_int, [TP, TP, TP, TP, i64, i64, ctypes.c_float, ctypes.c_float, vp,
                                              ctypes.c_int]),
     "rkv_plan_window": (ctypes.c_int, [vp, i64, i64, i64, i64, i64, i64, ctypes.POINTER(i64)]),

@@ -847,6 +847,16 @@ int rkv_window_mode(int mode, int64_t wc, int64_t kv_size, int append_only, int 
     return RKV_OK;
 }
 
+int rkv_choose_tail_mode(int64_t tail_bytes, double h2d_gbps, double host_gbps, int *mode) {
+    if (!mode) return fail(RKV_ERR_ARG, "mode is NULL");
+    if (tail_bytes < 0) return fail(RKV_ERR_ARG, "tail_bytes < 0");
+    if (!(h2d_gbps > 0.0) || !std::isfinite(h2d_gbps) || !(host_gbps > 0.0) || !std::isfinite(host_gbps))
+        return fail(RKV_ERR_ARG, "rates must be finite and > 0");
+    // equal byte counts: the faster rate gives the shorter tail time
+    *mode = (tail_bytes > 0 && host_gbps > h2d_gbps) ? RKV_TAIL_HOST : RKV_TAIL_LIFT;
+    return RKV_OK;
+}
+
 int rkv_set_tail_mode(rkv_ctx *ctx, int mode, int n_threads) {
     if (!ctx) return fail(RKV_ERR_ARG, "ctx is NULL");
     if (mode != RKV_TAIL_LIFT && mode != RKV_TAIL_HOST) return fail(RKV_ERR_ARG, "unknown tail mode %d", mode);
