@@ -261,7 +261,9 @@ def main():
     ap.add_argument("--splits", type=int, default=0)
     ap.add_argument("--softcap", type=float, default=0.0, help="logit soft-cap c (0: none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--lift-mode", type=int, default=0, help="0 bulk DMA, 1 word-granularity UVA read")
+    ap.add_argument("--lift-mode", type=int, default=3,
+                    help="0 bulk DMA, 1 word-granularity UVA read, 2 bulk copy kernel on the copy stream, "
+                         "3 automatic (decode: copy kernel, prefill: DMA)")
     ap.add_argument("--tail-mode", choices=["lift", "host", "auto"], default="lift",
                     help="host tail: lifted to the GPU in tiles, its partial computed on the host cores, or "
                          "whichever the measured link and host rates make faster")
@@ -291,8 +293,7 @@ def main():
     ctx = rkv.Context(0)
     if args.splits:
         ctx.set_splits(args.splits)
-    if args.lift_mode:
-        ctx.set_lift_mode(args.lift_mode)
+    ctx.set_lift_mode(args.lift_mode)
     if args.softcap:
         ctx.set_softcap(args.softcap)
     tail_choice = None
@@ -407,7 +408,7 @@ def main():
         span = sum(t[1] for t in lift_totals) / len(lift_totals)
         h2d = measured_h2d_gbs()
         lift_gbs = st["tail_bytes"] / (tot * 1e-3) / 1e9 if tot > 0 else None
-        out["lift"] = {"mode": "bulk" if args.lift_mode == 0 else "uva", "tail_bytes": st["tail_bytes"],
+        out["lift"] = {"mode": {0: "bulk", 1: "uva", 2: "kernel"}[stats["lift_mode"]], "tail_bytes": st["tail_bytes"],
                        "lift_ms_sum": round(tot, 4), "lift_span_ms": round(span, 4),
                        "lift_GBps_overlapped": round(lift_gbs, 2) if lift_gbs else None,
                        "measured_h2d_GBps": round(h2d, 2),

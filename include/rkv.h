@@ -71,7 +71,13 @@ enum rkv_status {
 
 enum rkv_lift_mode {
     RKV_LIFT_BULK = 0,  /* hipMemcpyAsync DMA of the raw bytes into the scratch ring         */
-    RKV_LIFT_UVA = 1    /* contrast only: a kernel reads the pinned host bytes word by word  */
+    RKV_LIFT_UVA = 1,   /* contrast only: a kernel reads the pinned host bytes word by word  */
+    RKV_LIFT_KERNEL = 2,/* a copy kernel on the copy stream reads the pinned bytes 8 at a
+                           time, four reads in flight per thread: no hand-off between a DMA
+                           engine and the compute queue, which dominates small lifts        */
+    RKV_LIFT_AUTO = 3   /* default: decode lifts with the copy kernel, prefill with the DMA
+                           engine (the copy kernel's workgroups would slow the MFMA kernel
+                           it overlaps)                                                      */
 };
 
 enum rkv_residency_mode {
@@ -138,9 +144,10 @@ const char *rkv_strerror(int status);
 const char *rkv_last_error(void);
 int rkv_get_stats(const rkv_ctx *ctx, rkv_stats *out);
 
-/* Choose how tail tiles are lifted by later calls on this context (enum rkv_lift_mode).
- * RKV_LIFT_UVA exists only to measure the word-granularity host read of patch 0102's
- * commit message against the bulk DMA; it is never the default. */
+/* Choose how tail tiles are lifted by later calls on this context (enum rkv_lift_mode;
+ * RKV_LIFT_AUTO until set).  RKV_LIFT_UVA exists only to measure the word-granularity host
+ * read of patch 0102's commit message against the bulk copies; it is never the default.
+ * rkv_stats.lift_mode reports the mode a call used. */
 int rkv_set_lift_mode(rkv_ctx *ctx, int mode);
 
 /* Override the split-K factor of window/pool segments (0 = automatic). */
@@ -231,7 +238,8 @@ int rkv_lse_merge(const float *partials, int n_seg, int64_t n_rows, int dv,
  * tail into a persistent per-slot scratch ring; K uses the slot's first buffer).
  * *dev_dst receives the slot's device address.  mode RKV_LIFT_BULK issues one
  * hipMemcpyAsync on copy_stream; RKV_LIFT_UVA launches the word-granularity reader
- * kernel instead (contrast measurement).  The slot's copy-done event is recorded on
+ * kernel instead (contrast measurement); RKV_LIFT_KERNEL the bulk copy kernel (host_src
+ * 8-byte aligned).  The slot's copy-done event is recorded on
  * copy_stream.  copy_stream NULL means the context's own copy stream.  The ring grows on
  * demand outside graph capture (RKV_ERR_CAPTURE inside it). */
 int rkv_tail_lift(rkv_ctx *ctx, const void *host_src, int64_t nbytes, int slot, int mode,

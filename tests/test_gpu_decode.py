@@ -131,6 +131,38 @@ def test_empty_tail_equals_single_resident(run):
     assert np.array_equal(O1, O2) and np.array_equal(L1, L2)
 
 
+@pytest.mark.parametrize("num,sd,layout", [(1, 1, "cell"), (3, 64, "cell"), (3, 64, "head"), (3, 32, "cell")])
+def test_kernel_lift(run, num, sd, layout):
+    """Tail tiles lifted by the copy kernel (RKV_LIFT_KERNEL) instead of the DMA engine."""
+    w = gen.make_workload(num, scale_down=sd)
+    run.ctx.set_lift_mode(run.rkv.RKV_LIFT_KERNEL)
+    try:
+        step(f"decode kernel lift workload {num}/{sd} layout {layout} wc {w['wc']} tile {w['tile_kv']}")
+        O, L = run.decode(w, tail="host", layout=layout)
+        st = run.ctx.stats()
+    finally:
+        run.ctx.set_lift_mode(run.rkv.RKV_LIFT_AUTO)
+    assert st["lift_mode"] == 2 and st["n_tail_tiles"] >= 2
+    Oref, Lref = oracle_decode(w)
+    assert_close(O, L, Oref, Lref, what=f"kernel lift {num}/{sd} {layout}")
+
+
+def test_automatic_lift_mode_per_entry_point(run):
+    """Default lift: decode tails through the copy kernel, prefill tails through the DMA engine."""
+    w = gen.make_workload(3, scale_down=64)
+    step("automatic lift mode: decode")
+    O, L = run.decode(w, tail="host")
+    assert run.ctx.stats()["lift_mode"] == run.rkv.RKV_LIFT_KERNEL
+    Oref, Lref = oracle_decode(w)
+    assert_close(O, L, Oref, Lref, what="automatic lift, decode")
+    w5 = gen.make_workload(5, scale_down=52)
+    step("automatic lift mode: prefill")
+    O, L = run.decode(w5, tail="host", prefill=True, q_pos0=w5["q_pos0"])
+    assert run.ctx.stats()["lift_mode"] == run.rkv.RKV_LIFT_BULK
+    Oref, Lref = oracle_decode(w5, mask=oracle.causal_mask(w5["n_q"], w5["n_kv"], w5["q_pos0"]))
+    assert_close(O, L, Oref, Lref, what="automatic lift, prefill")
+
+
 def test_back_to_back_calls_reuse_slots(run):
     """Several calls with 4 tail tiles through a 2-slot ring, queued without syncing between them,
     each against other work on the stream (the reused-slot race classes)."""

@@ -56,8 +56,8 @@ def test_dequant_golden_blocks(name, t, blk):
     assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
 
 
-@pytest.mark.parametrize("mode", [0, 1])
-@pytest.mark.parametrize("nbytes", [1, 4, 4099, 3 * 1024 * 1024 + 5])
+@pytest.mark.parametrize("mode", [0, 1, 2])
+@pytest.mark.parametrize("nbytes", [1, 4, 8, 4099, 4103, 3 * 1024 * 1024 + 5])
 def test_tail_lift_is_a_byte_copy(mode, nbytes):
     import torch
     import tiered_kv_cache_split_amd as rkv

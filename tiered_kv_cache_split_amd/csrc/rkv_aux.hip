@@ -88,6 +88,42 @@ hipError_t launch_uva_read(const void *host_src, void *dst, int64_t nbytes, hipS
     return hipGetLastError();
 }
 
+// Bulk copy of pinned host bytes by a kernel on the copy stream: 8-byte reads, four in flight
+// per thread, grid-stride over the span.  Unlike a DMA-engine copy it needs no hand-off between
+// the copy engine and the compute queue, which is most of the cost of small lifts.
+__global__ void __launch_bounds__(256) lift_copy_kernel(const uint2 *__restrict__ src, uint2 *__restrict__ dst,
+                                                        int64_t n8) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    for (; i + 3 * stride < n8; i += 4 * stride) {
+        const uint2 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
+        dst[i] = a;
+        dst[i + stride] = b;
+        dst[i + 2 * stride] = c;
+        dst[i + 3 * stride] = d;
+    }
+    for (; i < n8; i += stride) dst[i] = src[i];
+}
+
+hipError_t launch_lift_copy(const void *host_src, void *dst, int64_t nbytes, hipStream_t s) {
+    if (nbytes <= 0) return hipSuccess;
+    void *dev_view = nullptr;
+    hipError_t e = hipHostGetDevicePointer(&dev_view, const_cast<void *>(host_src), 0);
+    if (e != hipSuccess) return e;
+    if (((uintptr_t)dev_view | (uintptr_t)dst) % 8 != 0) return hipErrorInvalidValue;
+    const int64_t n8 = nbytes / 8;
+    if (n8 > 0) {
+        const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>((n8 + 1023) / 1024, 256));
+        hipLaunchKernelGGL(lift_copy_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                           static_cast<const uint2 *>(dev_view), static_cast<uint2 *>(dst), n8);
+    }
+    const int64_t rem = nbytes - 8 * n8;
+    if (rem > 0)
+        hipLaunchKernelGGL(uva_tail_kernel, dim3(1), dim3(8), 0, s,
+                           static_cast<const uint8_t *>(dev_view) + 8 * n8, static_cast<uint8_t *>(dst) + 8 * n8, rem);
+    return hipGetLastError();
+}
+
 hipError_t launch_dequant_rows(const void *src, int type, int64_t n_rows, int64_t row_stride,
                                float *dst, hipStream_t s) {
     if (n_rows <= 0) return hipSuccess;

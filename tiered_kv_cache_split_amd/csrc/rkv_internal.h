@@ -110,6 +110,8 @@ hipError_t launch_empty_partials(float *partials, int64_t n_rows, hipStream_t s)
 constexpr int kRowExtentParts = 16;
 hipError_t launch_row_extent(const int32_t *rows, int64_t rows_s, int64_t n_kv, int n_seq, int32_t *extent, hipStream_t s);
 hipError_t launch_uva_read(const void *host_src, void *dst, int64_t nbytes, hipStream_t s);
+// Bulk copy kernel over pinned host memory (source and destination 8-byte aligned).
+hipError_t launch_lift_copy(const void *host_src, void *dst, int64_t nbytes, hipStream_t s);
 hipError_t launch_dequant_rows(const void *src, int type, int64_t n_rows, int64_t row_stride,
                                float *dst, hipStream_t s);
 

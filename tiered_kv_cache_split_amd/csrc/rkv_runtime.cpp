@@ -176,7 +176,7 @@ struct rkv_ctx {
     size_t row_extent_cap = 0;      // bytes
     int2 *pair_range = nullptr;     // row lists: slot range of each pair's partials (up to 1024 pairs)
     size_t pair_range_cap = 0;      // bytes
-    int lift_mode = RKV_LIFT_BULK;
+    int lift_mode = RKV_LIFT_AUTO;
     int splits_override = 0;
     float softcap = 0.f;  // logit soft-cap of later calls (0: none)
     // host tail partial (RKV_TAIL_HOST): pinned staging of Q, the tail's mask columns and the
@@ -427,24 +427,30 @@ int tail_geom(const rkv_tensor *t, TailGeom &g) {
 }
 
 // Enqueue the lift of cells [loc, loc+cells) of a host tail tensor into ring slot `slot`.
-int lift_tile(rkv_ctx *ctx, const rkv_tensor *t, const TailGeom &g, int64_t loc, int64_t cells,
+int lift_tile(rkv_ctx *ctx, int mode, const rkv_tensor *t, const TailGeom &g, int64_t loc, int64_t cells,
               int64_t tile_cap_cells, void *dst, hipStream_t cs) {
     const uint8_t *src = static_cast<const uint8_t *>(t->data) + loc * g.nb1;
     if (g.cell_major) {
         const int64_t bytes = cells * g.nb1;
-        if (ctx->lift_mode == RKV_LIFT_UVA) {
+        if (mode == RKV_LIFT_UVA) {
             hipError_t e = launch_uva_read(src, dst, bytes, cs);
             if (e != hipSuccess) return hip_fail(e, "uva lift");
+        } else if (mode == RKV_LIFT_KERNEL) {
+            hipError_t e = launch_lift_copy(src, dst, bytes, cs);
+            if (e != hipSuccess) return hip_fail(e, "kernel lift");
         } else {
             RKV_HIP(hipMemcpyAsync(dst, src, bytes, hipMemcpyHostToDevice, cs));
         }
         ctx->stats.lift_bytes += bytes;
     } else {
         const int64_t width = cells * g.nb1;
-        if (ctx->lift_mode == RKV_LIFT_UVA) {
+        if (mode == RKV_LIFT_UVA || mode == RKV_LIFT_KERNEL) {
             for (int64_t h = 0; h < g.n_head_kv; ++h) {
-                hipError_t e = launch_uva_read(src + h * g.nb2, static_cast<uint8_t *>(dst) + h * tile_cap_cells * g.nb1, width, cs);
-                if (e != hipSuccess) return hip_fail(e, "uva lift");
+                const uint8_t *hs = src + h * g.nb2;
+                uint8_t *hd = static_cast<uint8_t *>(dst) + h * tile_cap_cells * g.nb1;
+                hipError_t e = mode == RKV_LIFT_UVA ? launch_uva_read(hs, hd, width, cs)
+                                                              : launch_lift_copy(hs, hd, width, cs);
+                if (e != hipSuccess) return hip_fail(e, "kernel lift");
             }
         } else {
             RKV_HIP(hipMemcpy2DAsync(dst, (size_t)(tile_cap_cells * g.nb1), src, (size_t)g.nb2, (size_t)width,
@@ -566,7 +572,10 @@ int attn_window_tail(rkv_ctx *ctx, const rkv_tensor *q, const rkv_tensor *k_win,
 
     ctx->stats = rkv_stats{};
     ctx->stats.kernel_variant = mfma ? RKV_KERNEL_PREFILL_MFMA : RKV_KERNEL_DECODE_HEAD;
-    ctx->stats.lift_mode = ctx->lift_mode;
+    // lift mode of this call: the automatic choice lifts decode tails with the copy kernel and
+    // prefill tails with the DMA engine
+    const int lift_mode = ctx->lift_mode == RKV_LIFT_AUTO ? (mfma ? RKV_LIFT_BULK : RKV_LIFT_KERNEL) : ctx->lift_mode;
+    ctx->stats.lift_mode = lift_mode;
     int slot = 0;
 
     // host tail: Q (and the tail's mask columns) go to pinned host memory ahead of the window
@@ -606,8 +615,8 @@ int attn_window_tail(rkv_ctx *ctx, const rkv_tensor *q, const rkv_tensor *k_win,
         const int64_t loc = t * tile_kv, cells = std::min(tile_kv, n_tail - loc);
         const bool timed = ctx->lift_timing && ctx->n_lift_timed < kMaxLiftTiming;
         if (timed) RKV_HIP(hipEventRecord(ctx->lift_t0[ctx->n_lift_timed], ctx->copy_stream));
-        int r = lift_tile(ctx, k_tail, gk, loc, cells, cap_cells, ctx->scr_k[sl], ctx->copy_stream);
-        if (!r) r = lift_tile(ctx, v_tail, gv, loc, cells, cap_cells, ctx->scr_v[sl], ctx->copy_stream);
+        int r = lift_tile(ctx, lift_mode, k_tail, gk, loc, cells, cap_cells, ctx->scr_k[sl], ctx->copy_stream);
+        if (!r) r = lift_tile(ctx, lift_mode, v_tail, gv, loc, cells, cap_cells, ctx->scr_v[sl], ctx->copy_stream);
         if (r) return r;
         if (timed) RKV_HIP(hipEventRecord(ctx->lift_t1[ctx->n_lift_timed++], ctx->copy_stream));
         RKV_HIP(hipEventRecord(ctx->copy_done[sl], ctx->copy_stream));
@@ -940,7 +949,8 @@ int rkv_get_stats(const rkv_ctx *ctx, rkv_stats *out) {
 
 int rkv_set_lift_mode(rkv_ctx *ctx, int mode) {
     if (!ctx) return fail(RKV_ERR_ARG, "ctx is NULL");
-    if (mode != RKV_LIFT_BULK && mode != RKV_LIFT_UVA) return fail(RKV_ERR_ARG, "unknown lift mode %d", mode);
+    if (mode != RKV_LIFT_BULK && mode != RKV_LIFT_UVA && mode != RKV_LIFT_KERNEL && mode != RKV_LIFT_AUTO)
+        return fail(RKV_ERR_ARG, "unknown lift mode %d", mode);
     ctx->lift_mode = mode;
     return RKV_OK;
 }
@@ -1179,7 +1189,10 @@ int rkv_tail_lift(rkv_ctx *ctx, const void *host_src, int64_t nbytes, int slot, 
     if (!ctx || !host_src || !dev_dst) return fail(RKV_ERR_ARG, "NULL argument");
     if (slot < 0 || slot >= kMaxSlots) return fail(RKV_ERR_ARG, "slot out of range");
     if (nbytes < 0) return fail(RKV_ERR_ARG, "nbytes < 0");
-    if (mode != RKV_LIFT_BULK && mode != RKV_LIFT_UVA) return fail(RKV_ERR_ARG, "unknown lift mode");
+    if (mode != RKV_LIFT_BULK && mode != RKV_LIFT_UVA && mode != RKV_LIFT_KERNEL)
+        return fail(RKV_ERR_ARG, "unknown lift mode");
+    if (mode == RKV_LIFT_KERNEL && ((uintptr_t)host_src) % 8 != 0)
+        return fail(RKV_ERR_UNSUPPORTED, "the kernel lift needs an 8-byte aligned source");
     if (pointer_kind(host_src) != Mem::PinnedHost) return fail(RKV_ERR_ARG, "host_src is not pinned host memory");
     int st = ensure_device(ctx);
     if (st) return st;
@@ -1188,6 +1201,9 @@ int rkv_tail_lift(rkv_ctx *ctx, const void *host_src, int64_t nbytes, int slot, 
     if (mode == RKV_LIFT_UVA) {
         hipError_t e = launch_uva_read(host_src, ctx->scr_k[slot], nbytes, cs);
         if (e != hipSuccess) return hip_fail(e, "uva lift");
+    } else if (mode == RKV_LIFT_KERNEL) {
+        hipError_t e = launch_lift_copy(host_src, ctx->scr_k[slot], nbytes, cs);
+        if (e != hipSuccess) return hip_fail(e, "kernel lift");
     } else if (nbytes > 0) {
         RKV_HIP(hipMemcpyAsync(ctx->scr_k[slot], host_src, (size_t)nbytes, hipMemcpyHostToDevice, cs));
     }
