@@ -1,5 +1,5 @@
-"""Randomised GPU parity sweep: seeded random shapes, types, layouts, splits, tails, masks, row
-lists and logit soft-caps through every entry point, each case against the fp64 oracle.  The cases are small
+"""Randomised GPU parity sweep: seeded random shapes, types, layouts, splits, tails, lift modes,
+masks, row lists and logit soft-caps through every entry point, each case against the fp64 oracle.  The cases are small
 (the oracle runs them in well under a second) and cover combinations the targeted tests do
 not enumerate: every kernel family is reached (vector, matrix-core q8_0/q4_0, matrix-core
 binary16 window/tail/rows, prefill), with ragged lengths throughout."""
@@ -51,8 +51,14 @@ def test_random_decode(run, seed):
          f"types {kt}/{vt} tail {tail} layout {layout} mask {mask is not None}")
     cap = draw_softcap(seed)
     run.ctx.set_softcap(cap)
-    step(f"  softcap {cap:.3f}")
-    O, L = run.decode(w, tail=None if tail == "none" else tail, mask=mask, layout=layout)
+    lift = int(np.random.default_rng(7000 + seed).choice([run.rkv.RKV_LIFT_AUTO, run.rkv.RKV_LIFT_BULK,
+                                                          run.rkv.RKV_LIFT_KERNEL]))
+    run.ctx.set_lift_mode(lift)
+    step(f"  softcap {cap:.3f} lift mode {lift}")
+    try:
+        O, L = run.decode(w, tail=None if tail == "none" else tail, mask=mask, layout=layout)
+    finally:
+        run.ctx.set_lift_mode(run.rkv.RKV_LIFT_AUTO)
     Oref, Lref = oracle_decode(w, mask=mask, softcap=cap)
     assert_close(O, L, Oref, Lref, what=f"random decode {seed}")
 
