@@ -72,9 +72,9 @@ enum rkv_status {
 enum rkv_lift_mode {
     RKV_LIFT_BULK = 0,  /* hipMemcpyAsync DMA of the raw bytes into the scratch ring         */
     RKV_LIFT_UVA = 1,   /* contrast only: a kernel reads the pinned host bytes word by word  */
-    RKV_LIFT_KERNEL = 2,/* a copy kernel on the copy stream reads the pinned bytes 8 at a
-                           time, four reads in flight per thread: no hand-off between a DMA
-                           engine and the compute queue, which dominates small lifts        */
+    RKV_LIFT_KERNEL = 2,/* a copy kernel on the copy stream (at most 64 workgroups) reads the
+                           pinned bytes 8 at a time: no hand-off between a DMA engine and the
+                           compute queue, which dominates small lifts                        */
     RKV_LIFT_AUTO = 3   /* default: decode lifts with the copy kernel, prefill with the DMA
                            engine (the copy kernel's workgroups would slow the MFMA kernel
                            it overlaps)                                                      */

@@ -88,21 +88,29 @@ hipError_t launch_uva_read(const void *host_src, void *dst, int64_t nbytes, hipS
     return hipGetLastError();
 }
 
-// Bulk copy of pinned host bytes by a kernel on the copy stream: 8-byte reads, four in flight
-// per thread, grid-stride over the span.  Unlike a DMA-engine copy it needs no hand-off between
-// the copy engine and the compute queue, which is most of the cost of small lifts.
-__global__ void __launch_bounds__(256) lift_copy_kernel(const uint2 *__restrict__ src, uint2 *__restrict__ dst,
-                                                        int64_t n8) {
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    for (; i + 3 * stride < n8; i += 4 * stride) {
-        const uint2 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
-        dst[i] = a;
-        dst[i + stride] = b;
-        dst[i + 2 * stride] = c;
-        dst[i + 3 * stride] = d;
+// Bulk copy of pinned host bytes by a kernel on the copy stream: 8-byte buffer reads of the
+// bytes' device view, two in flight per thread, grid-stride over the span.  Unlike a DMA-engine
+// copy it needs no hand-off between the copy engine and the compute queue, which is most of the
+// cost of small lifts.  It is held to 16 VGPRs so that its waves fit beside two waves of a
+// segment kernel that uses up to 248 of a SIMD's 512 registers each, and to 64 workgroups:
+// 256 KB of reads in flight keep the link busy, while every CU that hosts a copy workgroup has
+// its memory pipeline full of slow host reads, which stalls the compute sharing it (measured:
+// 64 workgroups lift at the link's rate and slow an overlapping prefill kernel 8%, 256 by 50%).
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_num_vgpr(16)))
+lift_copy_kernel(const uint8_t *src_p, uint8_t *dst_p, uint32_t n8) {
+    const __amdgpu_buffer_rsrc_t src = __builtin_amdgcn_make_buffer_rsrc((void *)src_p, (short)0, (int)(8 * n8), 0x00020000);
+    const __amdgpu_buffer_rsrc_t dst = __builtin_amdgcn_make_buffer_rsrc((void *)dst_p, (short)0, (int)(8 * n8), 0x00020000);
+    const uint32_t stride = gridDim.x * blockDim.x;
+    uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+    for (; i + stride < n8; i += 2 * stride) {
+        const auto a = __builtin_amdgcn_raw_buffer_load_b64(src, (int)(8 * i), 0, 0);
+        const auto b = __builtin_amdgcn_raw_buffer_load_b64(src, (int)(8 * (i + stride)), 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b64(a, dst, (int)(8 * i), 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b64(b, dst, (int)(8 * (i + stride)), 0, 0);
     }
-    for (; i < n8; i += stride) dst[i] = src[i];
+    if (i < n8)
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_amdgcn_raw_buffer_load_b64(src, (int)(8 * i), 0, 0), dst,
+                                              (int)(8 * i), 0, 0);
 }
 
 hipError_t launch_lift_copy(const void *host_src, void *dst, int64_t nbytes, hipStream_t s) {
@@ -111,16 +119,21 @@ hipError_t launch_lift_copy(const void *host_src, void *dst, int64_t nbytes, hip
     hipError_t e = hipHostGetDevicePointer(&dev_view, const_cast<void *>(host_src), 0);
     if (e != hipSuccess) return e;
     if (((uintptr_t)dev_view | (uintptr_t)dst) % 8 != 0) return hipErrorInvalidValue;
-    const int64_t n8 = nbytes / 8;
-    if (n8 > 0) {
-        const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>((n8 + 1023) / 1024, 256));
+    // pieces of at most 1 GiB keep the byte offsets within 31 bits
+    constexpr int64_t kPiece = (int64_t)1 << 30;
+    const int64_t n8_all = nbytes / 8;
+    for (int64_t p0 = 0; p0 < n8_all; p0 += kPiece / 8) {
+        const int64_t n8 = std::min<int64_t>(n8_all - p0, kPiece / 8);
+        const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>((n8 + 511) / 512, 64));
         hipLaunchKernelGGL(lift_copy_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
-                           static_cast<const uint2 *>(dev_view), static_cast<uint2 *>(dst), n8);
+                           static_cast<const uint8_t *>(dev_view) + 8 * p0, static_cast<uint8_t *>(dst) + 8 * p0,
+                           (uint32_t)n8);
     }
-    const int64_t rem = nbytes - 8 * n8;
+    const int64_t rem = nbytes - 8 * n8_all;
     if (rem > 0)
         hipLaunchKernelGGL(uva_tail_kernel, dim3(1), dim3(8), 0, s,
-                           static_cast<const uint8_t *>(dev_view) + 8 * n8, static_cast<uint8_t *>(dst) + 8 * n8, rem);
+                           static_cast<const uint8_t *>(dev_view) + 8 * n8_all, static_cast<uint8_t *>(dst) + 8 * n8_all,
+                           rem);
     return hipGetLastError();
 }
 
