@@ -63,7 +63,9 @@ def test_null_context_is_an_argument_error(lib):
 
 def test_merge_rejects_bad_sizes_before_device_work(lib):
     from tiered_kv_cache_split_amd import _lib
-    assert lib.rkv_lse_merge(None, 2, 4, 64, None, None, None) == _lib.RKV_ERR_UNSUPPORTED
+    for dv in (32, 96, 512):  # head dims other than 64, 128 and 256
+        assert lib.rkv_lse_merge(None, 2, 4, dv, None, None, None) == _lib.RKV_ERR_UNSUPPORTED
+    assert lib.rkv_lse_merge(None, 0, 4, 64, None, None, None) == _lib.RKV_ERR_ARG
     assert lib.rkv_lse_merge(None, 0, 4, 128, None, None, None) == _lib.RKV_ERR_ARG
     assert lib.rkv_lse_merge(None, 1, 0, 128, None, None, None) == _lib.RKV_OK  # nothing to do
 
@@ -87,6 +89,9 @@ def test_descriptor_layouts():
     kh = torch.zeros(8, 100, 72, dtype=torch.uint8)
     d = rkv.kv_desc(kh, rkv.RKV_TYPE_Q4_0, "head")
     assert list(d.ne) == [128, 100, 8, 1] and list(d.nb)[:3] == [18, 72, 100 * 72]
+    for d_, t, rb in [(64, rkv.RKV_TYPE_Q8_0, 68), (256, rkv.RKV_TYPE_Q4_0, 144), (64, rkv.RKV_TYPE_F16, 128)]:
+        d = rkv.kv_desc(torch.zeros(10, 2, rb, dtype=torch.uint8), t)  # head dim read off the row size
+        assert list(d.ne) == [d_, 10, 2, 1] and list(d.nb)[:3] == [rkv.BLOCK_BYTES[t], 2 * rb, rb]
     m = torch.zeros(3, 500, dtype=torch.float16)
     d = rkv.mask_desc(m)
     assert list(d.ne) == [500, 3, 1, 1] and list(d.nb)[:2] == [2, 1000]

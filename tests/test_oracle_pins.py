@@ -119,11 +119,12 @@ def test_logit_shift_and_value_scaling():
     assert np.allclose(O3, 3.0 * O, atol=1e-13) and np.allclose(L3, L, atol=0)
 
 
-def test_library_special_case_sdpa_f64():
+@pytest.mark.parametrize("d", [16, 64, 256])
+def test_library_special_case_sdpa_f64(d):
     """torch SDPA on CPU in float64 with the KV heads repeated for the grouped-query map."""
     torch = pytest.importorskip("torch")
     rng = np.random.default_rng(9)
-    H, G, Qn, N, d = 8, 2, 5, 37, 16
+    H, G, Qn, N = 8, 2, 5, 37
     q = rng.standard_normal((H, Qn, d))
     k = rng.standard_normal((G, N, d))
     v = rng.standard_normal((G, N, d))

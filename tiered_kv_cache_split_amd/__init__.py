@@ -16,7 +16,7 @@ import ctypes
 
 from ._lib import (RKV_LIFT_AUTO, RKV_LIFT_BULK, RKV_LIFT_KERNEL, RKV_LIFT_UVA, RKV_RESIDENCY_AUTO, RKV_RESIDENCY_RESIDENT,  # noqa: F401
                    RKV_RESIDENCY_WINDOW, RKV_TAIL_HOST, RKV_TAIL_LIFT, RKV_TYPE_F16, RKV_TYPE_F32, RKV_TYPE_Q4_0,
-                   RKV_TYPE_Q8_0, RkvError,
+                   RKV_TYPE_Q8_0, RKV_ERR_ARG, RKV_ERR_UNSUPPORTED, RkvError,
                    RkvStats, RkvTensor, check, load)
 
 BLOCK_BYTES = {RKV_TYPE_F16: 2, RKV_TYPE_F32: 4, RKV_TYPE_Q8_0: 34, RKV_TYPE_Q4_0: 18}
@@ -60,16 +60,17 @@ def q_desc(q) -> RkvTensor:
 
 def kv_desc(cache, type_id: int, layout: str = "cell") -> RkvTensor:
     """uint8 cache: cell-major (n_cells, n_head_kv, row_bytes) or head-major
-    (n_head_kv, n_cells, row_bytes) -> [128, n_cells, n_head_kv, 1]."""
-    rb = ROW_BYTES[type_id]
+    (n_head_kv, n_cells, row_bytes) -> [d, n_cells, n_head_kv, 1], with the head dim d read
+    off the row size (a row of 128 values is ROW_BYTES[type_id] bytes)."""
     if layout == "cell":
         n_cells, n_head_kv, row = cache.shape
         nb1, nb2 = cache.stride(0), cache.stride(1)
     else:
         n_head_kv, n_cells, row = cache.shape
         nb1, nb2 = cache.stride(1), cache.stride(0)
-    assert row == rb and cache.stride(2) == 1, "rows must be contiguous bytes"
-    return tensor(cache.data_ptr(), type_id, [128, n_cells, n_head_kv, 1],
+    assert (row * 128) % ROW_BYTES[type_id] == 0 and cache.stride(2) == 1, "rows must be contiguous whole rows"
+    d = row * 128 // ROW_BYTES[type_id]
+    return tensor(cache.data_ptr(), type_id, [d, n_cells, n_head_kv, 1],
                   [BLOCK_BYTES[type_id], nb1, nb2, nb2 * n_head_kv])
 
 
@@ -191,9 +192,9 @@ class Context:
         return int(dst.value or 0)
 
 
-def lse_merge(partials, n_seg: int, n_rows: int, o, lse=None, stream=None):
+def lse_merge(partials, n_seg: int, n_rows: int, o, lse=None, stream=None, dv: int = 128):
     lib = load()
-    check(lib.rkv_lse_merge(_ptr(partials), int(n_seg), int(n_rows), 128, _ptr(o), _ptr(lse), _stream(stream)),
+    check(lib.rkv_lse_merge(_ptr(partials), int(n_seg), int(n_rows), int(dv), _ptr(o), _ptr(lse), _stream(stream)),
           "rkv_lse_merge")
 
 

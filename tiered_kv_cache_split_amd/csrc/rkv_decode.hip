@@ -787,6 +787,7 @@ bool decode_kernel_persistent(const SegParams &p, int k_type, int v_type) {
 }
 
 int decode_kernel_variant(const SegParams &p, int k_type, int v_type) {
+    if (p.d != kHeadDim) return RKV_KERNEL_DECODE_HD;
     if (p.cell_hw <= 0) return RKV_KERNEL_DECODE_HEAD;
     if (k_type == T_Q8_0 && v_type == T_Q4_0 && decode_mma_ok(p)) return RKV_KERNEL_DECODE_CELL_MFMA;
     if (k_type == T_F16 && v_type == T_F16 && decode_mma16_ok(p)) return RKV_KERNEL_DECODE_CELL_MFMA16;
@@ -794,6 +795,7 @@ int decode_kernel_variant(const SegParams &p, int k_type, int v_type) {
 }
 
 hipError_t launch_decode_segment(const SegParams &p, int k_type, int v_type, hipStream_t s) {
+    if (p.d != kHeadDim) return launch_decode_hd(p, k_type, v_type, s);
     return dispatch_decode(p, k_type, v_type, s, nullptr);
 }
 

@@ -43,7 +43,7 @@ struct SegParams {
     // logit soft-cap: the score becomes cap_l2 * tanh(cap_cs * <q, k>) in the exp2 domain
     // (cap_cs = scale / c, cap_l2 = c * log2(e)); cap_l2 = 0: no cap
     float cap_cs, cap_l2;
-    float *partials;   // [slot][n_rows][2 + 128]
+    float *partials;   // [slot][n_rows][2 + d]
     int slot0;         // first partial slot used by this segment
     int64_t n_rows;    // n_head * n_q * n_seq
     int cell_hw;       // > 0: cell-major kernel, cell_hw KV heads (packed per cell) per workgroup
@@ -53,6 +53,8 @@ struct SegParams {
     int2 *pair_range;
     // optional: events the segment kernel's own dispatch records at its start and end
     hipEvent_t ev_start, ev_stop;
+    // head dim (== dv): 128 for every kernel but the decode kernel for other head dims
+    int d = kHeadDim;
 };
 
 // Launch a segment kernel; with timing events set, the dispatch itself records them, so the
@@ -114,6 +116,13 @@ hipError_t launch_uva_read(const void *host_src, void *dst, int64_t nbytes, hipS
 hipError_t launch_lift_copy(const void *host_src, void *dst, int64_t nbytes, hipStream_t s);
 hipError_t launch_dequant_rows(const void *src, int type, int64_t n_rows, int64_t row_stride,
                                float *dst, hipStream_t s);
+
+// Head dims other than 128 (rkv_decode_hd.hip): decode segments (gqa * n_q <= 8, no row lists)
+// and the merge of partials with row stride 2 + dv.
+bool head_dim_supported(int d);  // 64, 128 or 256
+hipError_t launch_decode_hd(const SegParams &p, int k_type, int v_type, hipStream_t s);
+hipError_t launch_merge_hd(const float *partials, int n_seg, int64_t n_rows, int dv, float *o, float *lse,
+                           hipStream_t s);
 
 // Tail partial on the host cores (rkv_host_tail.cpp).  Every pointer is host memory.
 struct HostTailArgs {

@@ -65,11 +65,12 @@ int64_t type_block_bytes(int t) {
         default: return 0;
     }
 }
-int64_t row_bytes(int t) {
+// Bytes of one row of d values (d a multiple of 32).
+int64_t row_bytes(int t, int64_t d = kHeadDim) {
     switch (t) {
-        case RKV_TYPE_F16: return 256;
-        case RKV_TYPE_Q8_0: return 136;
-        case RKV_TYPE_Q4_0: return 72;
+        case RKV_TYPE_F16: return 2 * d;
+        case RKV_TYPE_Q8_0: return d / 32 * 34;
+        case RKV_TYPE_Q4_0: return d / 32 * 18;
         default: return 0;
     }
 }
@@ -95,33 +96,38 @@ int check_device_ptr(const void *p, const char *name) {
     return RKV_OK;
 }
 
-// K/V tensor [128, n_cells, n_head_kv, 1] with contiguous rows.
-int check_kv(const rkv_tensor *t, const char *name, bool is_k) {
+// K/V tensor [128, n_cells, n_head_kv, 1] with contiguous rows (any_d: head dim 64, 128 or 256).
+int check_kv(const rkv_tensor *t, const char *name, bool is_k, bool any_d = false) {
     if (!t) return fail(RKV_ERR_ARG, "%s is NULL", name);
     const bool ok_type = is_k ? (t->type == RKV_TYPE_F16 || t->type == RKV_TYPE_Q8_0)
                               : (t->type == RKV_TYPE_F16 || t->type == RKV_TYPE_Q4_0);
     if (!ok_type) return fail(RKV_ERR_UNSUPPORTED, "%s: type %d not supported", name, t->type);
-    if (t->ne[0] != kHeadDim) return fail(RKV_ERR_UNSUPPORTED, "%s: head dim %lld != 128", name, (long long)t->ne[0]);
+    if (any_d ? !head_dim_supported((int)std::min<int64_t>(t->ne[0], 1 << 20)) : t->ne[0] != kHeadDim)
+        return fail(RKV_ERR_UNSUPPORTED, "%s: head dim %lld not supported here", name, (long long)t->ne[0]);
     if (t->ne[1] < 0 || t->ne[2] <= 0 || t->ne[3] != 1)
         return fail(RKV_ERR_ARG, "%s: bad shape [%lld,%lld,%lld,%lld]", name, (long long)t->ne[0],
                     (long long)t->ne[1], (long long)t->ne[2], (long long)t->ne[3]);
     if (t->ne[1] >= (int64_t)1 << 31) return fail(RKV_ERR_UNSUPPORTED, "%s: more than 2^31 cells", name);
     if (t->nb[0] != type_block_bytes(t->type)) return fail(RKV_ERR_ARG, "%s: rows must be contiguous (nb[0])", name);
-    const int64_t rb = row_bytes(t->type);
+    const int64_t rb = row_bytes(t->type, t->ne[0]);
     if (t->ne[1] > 1 && t->nb[1] < rb) return fail(RKV_ERR_ARG, "%s: nb[1] smaller than a row", name);
     if (t->ne[2] > 1 && t->nb[2] < rb) return fail(RKV_ERR_ARG, "%s: nb[2] smaller than a row", name);
-    if ((t->nb[1] | t->nb[2]) % 8 != 0 || ((uintptr_t)t->data) % 8 != 0)
-        return fail(RKV_ERR_UNSUPPORTED, "%s: data and nb[1], nb[2] must be multiples of 8 bytes", name);
+    // the head-dim-128 kernels read rows in 8-byte pieces; the kernel for other head dims reads
+    // binary16 values and bytes
+    const int al = t->ne[0] == kHeadDim ? 8 : 2;
+    if ((t->nb[1] | t->nb[2]) % al != 0 || ((uintptr_t)t->data) % al != 0)
+        return fail(RKV_ERR_UNSUPPORTED, "%s: data and nb[1], nb[2] must be multiples of %d bytes", name, al);
     if (t->nb[1] >= ((int64_t)1 << 25) || t->nb[1] < 0 || t->nb[2] < 0)
         return fail(RKV_ERR_UNSUPPORTED, "%s: cell stride beyond 32 MiB", name);
     if (t->ne[1] > 0 && !t->data) return fail(RKV_ERR_ARG, "%s: data is NULL", name);
     return RKV_OK;
 }
 
-int check_q(const rkv_tensor *q, bool allow_seq) {
+int check_q(const rkv_tensor *q, bool allow_seq, bool any_d = false) {
     if (!q || !q->data) return fail(RKV_ERR_ARG, "q is NULL");
     if (q->type != RKV_TYPE_F16) return fail(RKV_ERR_UNSUPPORTED, "q must be F16");
-    if (q->ne[0] != kHeadDim) return fail(RKV_ERR_UNSUPPORTED, "q head dim must be 128");
+    if (any_d ? !head_dim_supported((int)std::min<int64_t>(q->ne[0], 1 << 20)) : q->ne[0] != kHeadDim)
+        return fail(RKV_ERR_UNSUPPORTED, "q head dim %lld not supported here", (long long)q->ne[0]);
     if (q->ne[1] <= 0 || q->ne[2] <= 0 || q->ne[3] <= 0) return fail(RKV_ERR_ARG, "q: bad shape");
     if (!allow_seq && q->ne[3] != 1) return fail(RKV_ERR_ARG, "q: ne[3] must be 1");
     if (q->nb[0] != 2) return fail(RKV_ERR_ARG, "q rows must be contiguous");
@@ -302,6 +308,7 @@ struct Seg {
 // apply: every cell must hold the KV heads packed (head stride == row size), cell strides and
 // bases must be 16-byte aligned, and the types and head count must have an instantiation.
 int use_cell_kernel(const Seg &sg, const SegParams &p, int k_type, int v_type) {
+    if (p.d != kHeadDim) return 0;
     const int64_t rk = row_bytes(k_type), rv = row_bytes(v_type);
     const int hw = cell_heads(k_type, v_type, p.n_head_kv, p.gqa * p.n_q, p.rows != nullptr);
     if (hw == 0) return 0;
@@ -411,7 +418,7 @@ struct TailGeom {
 };
 
 int tail_geom(const rkv_tensor *t, TailGeom &g) {
-    const int64_t rb = row_bytes(t->type);
+    const int64_t rb = row_bytes(t->type, t->ne[0]);
     g.nb1 = t->nb[1];
     g.nb2 = t->nb[2];
     g.n_head_kv = t->ne[2];
@@ -430,6 +437,11 @@ int tail_geom(const rkv_tensor *t, TailGeom &g) {
 int lift_tile(rkv_ctx *ctx, int mode, const rkv_tensor *t, const TailGeom &g, int64_t loc, int64_t cells,
               int64_t tile_cap_cells, void *dst, hipStream_t cs) {
     const uint8_t *src = static_cast<const uint8_t *>(t->data) + loc * g.nb1;
+    // the copy kernel moves 8-byte words: spans that do not start on one (rows of 68 or 36
+    // bytes, head dim 64) go through the DMA engine
+    if (mode == RKV_LIFT_KERNEL &&
+        ((uintptr_t)src | (uintptr_t)dst | (uintptr_t)g.nb1 | (uintptr_t)(g.cell_major ? 0 : g.nb2)) % 8 != 0)
+        mode = RKV_LIFT_BULK;
     if (g.cell_major) {
         const int64_t bytes = cells * g.nb1;
         if (mode == RKV_LIFT_UVA) {
@@ -467,7 +479,9 @@ int attn_window_tail(rkv_ctx *ctx, const rkv_tensor *q, const rkv_tensor *k_win,
                      const rkv_tensor *mask, int64_t wc, int64_t tile_kv, float scale,
                      int64_t q_pos0, bool mfma, float *o, float *lse, hipStream_t stream) {
     if (!ctx) return fail(RKV_ERR_ARG, "ctx is NULL");
-    int st = check_q(q, false);
+    // decode takes head dims 64, 128 and 256 (dv = dk); prefill 128 only
+    const bool any_d = !mfma;
+    int st = check_q(q, false, any_d);
     if (st) return st;
     if (wc < 0) return fail(RKV_ERR_ARG, "wc < 0");
     if (tile_kv <= 0) return fail(RKV_ERR_ARG, "tile_kv must be > 0");
@@ -480,14 +494,14 @@ int attn_window_tail(rkv_ctx *ctx, const rkv_tensor *q, const rkv_tensor *k_win,
     const rkv_tensor *vref = v_win ? v_win : v_tail;
     if (!kref) return fail(RKV_ERR_ARG, "no K/V given");
     if (k_win) {
-        if ((st = check_kv(k_win, "k_win", true)) || (st = check_kv(v_win, "v_win", false))) return st;
+        if ((st = check_kv(k_win, "k_win", true, any_d)) || (st = check_kv(v_win, "v_win", false, any_d))) return st;
         if (k_win->ne[1] < wc || v_win->ne[1] < wc) return fail(RKV_ERR_ARG, "window tensors hold fewer than wc cells");
         if (k_win->ne[2] != v_win->ne[2]) return fail(RKV_ERR_ARG, "k_win and v_win disagree in n_head_kv");
     }
     int64_t n_tail = 0;
     Mem tail_kind = Mem::Device;
     if (k_tail) {
-        if ((st = check_kv(k_tail, "k_tail", true)) || (st = check_kv(v_tail, "v_tail", false))) return st;
+        if ((st = check_kv(k_tail, "k_tail", true, any_d)) || (st = check_kv(v_tail, "v_tail", false, any_d))) return st;
         if (k_tail->ne[1] != v_tail->ne[1] || k_tail->ne[2] != v_tail->ne[2])
             return fail(RKV_ERR_ARG, "k_tail and v_tail disagree in shape");
         if (k_win && ((st = same_kv_shape(k_win, k_tail, "K")) || (st = same_kv_shape(v_win, v_tail, "V")))) return st;
@@ -504,6 +518,10 @@ int attn_window_tail(rkv_ctx *ctx, const rkv_tensor *q, const rkv_tensor *k_win,
     const int64_t n_head_kv = kref->ne[2];
     if (n_head % n_head_kv != 0) return fail(RKV_ERR_ARG, "n_head %% n_head_kv != 0");
     const int64_t gqa = n_head / n_head_kv;
+    const int d = (int)q->ne[0];
+    if (kref->ne[0] != d || vref->ne[0] != d || (k_tail && (k_tail->ne[0] != d || v_tail->ne[0] != d)))
+        return fail(RKV_ERR_UNSUPPORTED, "K and V head dims must equal Q's");
+    const int64_t ps = 2 + d;  // partial row stride
     if (!mfma && gqa * n_q > kMaxRowsVec)
         return fail(RKV_ERR_UNSUPPORTED, "decode handles n_q*gqa <= %d rows per KV head (got %lld); use rkv_attn_prefill",
                     kMaxRowsVec, (long long)(gqa * n_q));
@@ -528,10 +546,12 @@ int attn_window_tail(rkv_ctx *ctx, const rkv_tensor *q, const rkv_tensor *k_win,
     base.scale_log2 = scale * 1.4426950408889634f;
     fill_softcap(base, ctx, scale);
     base.n_rows = n_head * n_q;
+    base.d = d;
 
     // ---- plan: window segment, then tail (in place, lifted tiles through the ring, or a
     // partial computed on the host cores)
     const bool host_tail = n_tail > 0 && tail_kind != Mem::Device && ctx->tail_mode == RKV_TAIL_HOST && !mfma;
+    if (host_tail && d != kHeadDim) return fail(RKV_ERR_UNSUPPORTED, "the host tail partial takes head dim 128");
     const bool lifted = n_tail > 0 && tail_kind == Mem::PinnedHost && !host_tail;
     const int64_t n_tiles = lifted ? (n_tail + tile_kv - 1) / tile_kv : 0;
     TailGeom gk{}, gv{};
@@ -567,7 +587,7 @@ int attn_window_tail(rkv_ctx *ctx, const rkv_tensor *q, const rkv_tensor *k_win,
     for (int64_t t = 0; t < n_tiles; ++t) total_slots += plan_segment(ctx, base, tile_seg(t), mfma, k_type, v_type).n_splits;
     if (host_tail) total_slots += 1;
     if (total_slots == 0) total_slots = 1;  // n_kv == 0: one empty partial
-    if ((st = ensure_partials(ctx, total_slots * base.n_rows * kPartialStride, stream))) return st;
+    if ((st = ensure_partials(ctx, total_slots * base.n_rows * ps, stream))) return st;
     base.partials = ctx->partials;
 
     ctx->stats = rkv_stats{};
@@ -580,7 +600,7 @@ int attn_window_tail(rkv_ctx *ctx, const rkv_tensor *q, const rkv_tensor *k_win,
 
     // host tail: Q (and the tail's mask columns) go to pinned host memory ahead of the window
     // kernels, so the host computes the tail partial while the GPU computes the window
-    const int64_t q_span = (n_q - 1) * q->nb[1] + (n_head - 1) * q->nb[2] + kHeadDim * 2;
+    const int64_t q_span = (n_q - 1) * q->nb[1] + (n_head - 1) * q->nb[2] + d * 2;
     if (host_tail) {
         if (stream_capturing(stream)) return fail(RKV_ERR_CAPTURE, "the host tail partial cannot run inside graph capture");
         if (!host_tail_supported()) return fail(RKV_ERR_UNSUPPORTED, "the host tail partial needs a CPU with AVX2, FMA and F16C");
@@ -593,7 +613,7 @@ int attn_window_tail(rkv_ctx *ctx, const rkv_tensor *q, const rkv_tensor *k_win,
         if (ctx->host_in) RKV_HIP(hipEventSynchronize(ctx->host_in));
         if ((st = grow_host(&ctx->hq, &ctx->hq_cap, (size_t)q_span)) ||
             (mask && (st = grow_host(&ctx->hmask, &ctx->hmask_cap, (size_t)(n_q * n_tail * 2)))) ||
-            (st = grow_host(&ctx->hpart, &ctx->hpart_cap, (size_t)(base.n_rows * kPartialStride * 4))))
+            (st = grow_host(&ctx->hpart, &ctx->hpart_cap, (size_t)(base.n_rows * ps * 4))))
             return st;
         if (!ctx->host_in) RKV_HIP(hipEventCreateWithFlags(&ctx->host_in, hipEventDisableTiming));
         if (!ctx->host_up) RKV_HIP(hipEventCreateWithFlags(&ctx->host_up, hipEventDisableTiming));
@@ -669,8 +689,8 @@ int attn_window_tail(rkv_ctx *ctx, const rkv_tensor *q, const rkv_tensor *k_win,
         }
         ctx->stats.host_tail_ms = std::chrono::duration<float, std::milli>(std::chrono::steady_clock::now() - t0).count();
         ctx->stats.tail_host = 1;
-        RKV_HIP(hipMemcpyAsync(ctx->partials + (int64_t)slot * base.n_rows * kPartialStride, ctx->hpart,
-                               (size_t)(base.n_rows * kPartialStride * 4), hipMemcpyHostToDevice, stream));
+        RKV_HIP(hipMemcpyAsync(ctx->partials + (int64_t)slot * base.n_rows * ps, ctx->hpart,
+                               (size_t)(base.n_rows * ps * 4), hipMemcpyHostToDevice, stream));
         RKV_HIP(hipEventRecord(ctx->host_up, stream));
         ctx->host_up_pending = true;
         slot += 1;
@@ -685,6 +705,14 @@ int attn_window_tail(rkv_ctx *ctx, const rkv_tensor *q, const rkv_tensor *k_win,
         RKV_HIP(hipStreamWaitEvent(stream, ctx->copy_done[sl], 0));
         if ((st = run_segment(ctx, base, tile_seg(t), mfma, k_type, v_type, slot, stream))) return st;
         RKV_HIP(hipEventRecord(ctx->compute_done[sl], stream));
+    }
+    if (d != kHeadDim) {
+        // other head dims: the merge of partials with row stride 2 + d (no partial at all, as for
+        // n_kv == 0, gives every row O = 0 and LSE = -inf)
+        ctx->stats.n_partials = slot;
+        hipError_t e = launch_merge_hd(ctx->partials, slot, base.n_rows, d, o, lse, stream);
+        if (e != hipSuccess) return hip_fail(e, "merge launch");
+        return RKV_OK;
     }
     if (slot == 0) {
         // n_kv == 0: a single empty partial, so every row gets O = 0 and LSE = -inf
@@ -1172,14 +1200,16 @@ int rkv_attn_partial(rkv_ctx *ctx, const rkv_tensor *q, const rkv_tensor *k, con
 }
 
 int rkv_lse_merge(const float *partials, int n_seg, int64_t n_rows, int dv, float *o, float *lse, void *stream) {
-    if (dv != kHeadDim) return fail(RKV_ERR_UNSUPPORTED, "dv must be 128");
+    if (!head_dim_supported(dv)) return fail(RKV_ERR_UNSUPPORTED, "dv must be 64, 128 or 256");
     if (n_seg <= 0 || n_rows < 0) return fail(RKV_ERR_ARG, "n_seg must be > 0 and n_rows >= 0");
     if (n_rows == 0) return RKV_OK;
     int st = check_device_ptr(partials, "partials");
     if (st) return st;
     if ((st = check_device_ptr(o, "o"))) return st;
     if (lse && (st = check_device_ptr(lse, "lse"))) return st;
-    hipError_t e = launch_merge(partials, n_seg, n_rows, o, lse, nullptr, static_cast<hipStream_t>(stream));
+    hipError_t e = dv == kHeadDim
+                       ? launch_merge(partials, n_seg, n_rows, o, lse, nullptr, static_cast<hipStream_t>(stream))
+                       : launch_merge_hd(partials, n_seg, n_rows, dv, o, lse, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "merge launch");
     return RKV_OK;
 }
