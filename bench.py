@@ -80,14 +80,14 @@ def blas_threads() -> int:
 
 
 # ------------------------------------------------------------------ workloads on device
-def setup(num: int, sets: int):
+def setup(num: int, sets: int, head_dim: int = 128):
     import numpy as np
     import torch
 
     import rkv_inputs as gen
-    import tiered_kv_cache_split_amd as rkv
 
-    w = gen.make_workload(num)
+    w = gen.make_workload(num) if head_dim == 128 else gen.make_workload(num, d=head_dim)
+    rb = lambda t: gen.row_bytes(t, w["d"])
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
     def pinned(a):
@@ -105,8 +105,7 @@ def setup(num: int, sets: int):
         n_seq, n_head, n_q, _ = w["q"].shape
         st["o"] = torch.empty((n_seq, n_q, n_head, 128), dtype=torch.float32, device="cuda")
         st["lse"] = torch.empty((n_seq, n_q, n_head), dtype=torch.float32, device="cuda")
-        kv_bytes = int((w["kv_rows"] >= 0).sum()) * w["n_head_kv"] * (
-            rkv.ROW_BYTES[w["k_type"]] + rkv.ROW_BYTES[w["v_type"]])
+        kv_bytes = int((w["kv_rows"] >= 0).sum()) * w["n_head_kv"] * (rb(w["k_type"]) + rb(w["v_type"]))
         st["kv_bytes"] = kv_bytes
         st["tail_bytes"] = 0
         return st
@@ -117,9 +116,9 @@ def setup(num: int, sets: int):
     if w["n_kv"] > wc:
         st["tail"] = (pinned(w["k"][wc:]), pinned(w["v"][wc:]))
     n_head, n_q = w["n_head"], w["q"].shape[1]
-    st["o"] = torch.empty((n_q, n_head, 128), dtype=torch.float32, device="cuda")
+    st["o"] = torch.empty((n_q, n_head, w["d"]), dtype=torch.float32, device="cuda")
     st["lse"] = torch.empty((n_q, n_head), dtype=torch.float32, device="cuda")
-    per_cell = w["n_head_kv"] * (rkv.ROW_BYTES[w["k_type"]] + rkv.ROW_BYTES[w["v_type"]])
+    per_cell = w["n_head_kv"] * (rb(w["k_type"]) + rb(w["v_type"]))
     st["kv_bytes"] = w["n_kv"] * per_cell
     st["tail_bytes"] = (w["n_kv"] - wc) * per_cell
     st["window_bytes"] = wc * per_cell
@@ -127,7 +126,8 @@ def setup(num: int, sets: int):
 
 
 # kernel families reported in the context's stats (enum rkv_kernel_variant)
-DECODE_KERNELS = {0: "decode_seg_kernel", 2: "decode_cell_kernel", 3: "decode_mma_kernel", 4: "decode_mma16_kernel"}
+DECODE_KERNELS = {0: "decode_seg_kernel", 2: "decode_cell_kernel", 3: "decode_mma_kernel", 4: "decode_mma16_kernel",
+                  5: "decode_hd_kernel"}
 
 
 def call(ctx, st, i):
@@ -223,8 +223,7 @@ def cpu_baseline(num: int, budget_s: float = 12.0, w=None, softcap: float = 0.0)
         gbs = total_cells * per_cell / full_s / 1e9
         return {"value": round(gbs, 4), "unit": "GB/s", "cores": blas_threads(), "kind": "oracle",
                 "sample": sample, "oracle_s_full_extrapolated": round(full_s, 2)}
-    rb = {gen.TYPE_F16: 256, gen.TYPE_Q8_0: 136, gen.TYPE_Q4_0: 72}
-    per_cell = w["n_head_kv"] * (rb[w["k_type"]] + rb[w["v_type"]])
+    per_cell = w["n_head_kv"] * (gen.row_bytes(w["k_type"], w["d"]) + gen.row_bytes(w["v_type"], w["d"]))
     q = oracle.q_values(w["q"])
     n_q = w["q"].shape[1]
     if w["kind"] == "prefill":
@@ -261,6 +260,8 @@ def main():
     ap.add_argument("--splits", type=int, default=0)
     ap.add_argument("--softcap", type=float, default=0.0, help="logit soft-cap c (0: none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--head-dim", type=int, default=128, choices=[64, 128, 256],
+                    help="head dim of Q, K and V (64 and 256: decode workloads 1-3 only)")
     ap.add_argument("--lift-mode", type=int, default=3,
                     help="0 bulk DMA, 1 word-granularity UVA read, 2 bulk copy kernel on the copy stream, "
                          "3 automatic (decode: copy kernel, prefill: DMA)")
@@ -286,9 +287,12 @@ def main():
         gbs = measured_copy_gbs(1 << 30, reps=5)
         print(json.dumps({"copy_bytes_read": 1 << 30, "copy_bytes_written": 1 << 30, "copy_GBps": round(gbs, 1)}))
         return
+    if args.head_dim != 128 and args.workload not in (1, 2, 3):
+        print("head dims 64 and 256 are served by the decode path only (workloads 1-3)", file=sys.stderr)
+        sys.exit(2)
     print(f"[bench] workload {args.workload}: {gen.WORKLOADS[args.workload]['name']} setup", file=sys.stderr,
           flush=True)
-    st = setup(args.workload, args.sets)
+    st = setup(args.workload, args.sets, args.head_dim)
     w = st["w"]
     ctx = rkv.Context(0)
     if args.splits:
@@ -368,7 +372,7 @@ def main():
         "dtype": "f16",  # matrix-core operands (q8_0/q4_0 codes as exact binary16 integers)
         "accum_dtype": "f32",  # accumulation, softmax and partials
         "data": "synthetic",
-        "config": {"workload": w["name"], "n_head": w["n_head"], "n_head_kv": w["n_head_kv"], "head_dim": 128,
+        "config": {"workload": w["name"], "n_head": w["n_head"], "n_head_kv": w["n_head_kv"], "head_dim": w["d"],
                    "n_q": int(w["q"].shape[-2]), "n_kv": int(w["n_kv"]),
                    "k_type": gen.TYPE_NAMES[w["k_type"]], "v_type": gen.TYPE_NAMES[w["v_type"]],
                    "kv_sets_rotated": args.sets, "parallelism": "single GPU",
@@ -401,7 +405,7 @@ def main():
             label += " (all segments of a step)"
         out["roofline"] = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": round(achieved / HBM_PEAK_GBS, 4),
-                           "traffic": traffic_from_profiles(name, "decode") if name else None,
+                           "traffic": traffic_from_profiles(name, "decode") if name and w["d"] == 128 else None,
                            "kernel": label, "kernel_avg_ms": round(kern_ms, 5)}
     if lift_totals:
         tot = sum(t[0] for t in lift_totals) / len(lift_totals)
@@ -417,7 +421,7 @@ def main():
         hm = sorted(host_ms)[len(host_ms) // 2]
         out["host_tail"] = {"tail_bytes": st["tail_bytes"], "threads": args.host_threads, "host_ms_median": round(hm, 4),
                             "host_GBps": round(st["tail_bytes"] / (hm * 1e-3) / 1e9, 2),
-                            "partial_bytes_uploaded": int(w["n_head"] * w["q"].shape[-2] * 130 * 4)}
+                            "partial_bytes_uploaded": int(w["n_head"] * w["q"].shape[-2] * (2 + w["d"]) * 4)}
     if tail_choice:
         out["tail_choice"] = tail_choice
     out["measured_copy_GBps"] = round(measured_copy_gbs(), 1)
