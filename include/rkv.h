@@ -23,7 +23,7 @@
  * K in F16 or Q8_0; V in F16 or Q4_0.  Q8_0 is a 34-byte block (binary16 scale d, 32
  * int8 codes q; value d*q).  Q4_0 is an 18-byte block (binary16 scale d, 16 bytes; byte
  * j holds element j in its low nibble and element j+16 in its high nibble; value
- * d*(n-8)).  K/V data pointers and their nb[1], nb[2] must be multiples of 8 bytes (of 2
+ * d*(n-8)).  K/V data pointers and their nb[1], nb[2] must be multiples of 8 bytes (of 4
  * bytes for head dims 64 and 256); Q pointers and strides multiples of 4 bytes.
  *
  *   score s_j = scale * <q, k_j> + mask[j]   (mask additive binary16, -inf hides;

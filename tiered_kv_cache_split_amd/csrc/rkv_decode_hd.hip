@@ -4,13 +4,16 @@
 // shapes); the partial of a segment is the same (M, S, VKQ) triple as for head dim 128, stored
 // with row stride 2 + D.
 //
-// Workgroup = 4 waves for one (split, KV head, sequence); wave w takes every 4th 64-key chunk
-// of the split.  Q.K: a lane owns one key of the chunk and forms the scores of the R query rows
-// that read this KV head (Q in LDS, K dequantised value by value from its own row).  Softmax:
-// per row, a running max over chunks (wave reductions), weights to LDS.  P.V: a lane owns
-// D / 64 consecutive values of head_dim and walks the chunk's visible keys (a wave-wide bit
-// mask), so V rows are read with consecutive lanes on consecutive bytes.  The four waves'
-// states are combined through LDS at the end.
+// Workgroup = 256 threads for one (split, KV head, sequence); it walks the split in chunks of KC
+// keys (64 for D = 64, 16 for D = 256) as a pipeline: the next chunk's K and V rows are loaded
+// from HBM into registers (4-byte words, consecutive threads on consecutive words of a row)
+// while the current chunk is computed from LDS.
+//   Q.K  P = 256 / KC threads per key, each over 16 consecutive dims (half of a q8_0 block),
+//        partial dots summed across the P adjacent lanes; the R <= 8 query rows that
+//        read this KV head are done together.
+//   softmax  wave w owns rows w and w + 4: chunk max, rescale factor and weights, in natural-log
+//        units, kept in LDS for the P.V step.
+//   P.V  thread t owns output column t % D of rows t / D (+ 4 for D = 64).
 #include "rkv_internal.h"
 #include "rkv_wave.h"
 
@@ -20,53 +23,89 @@ namespace rkv {
 
 namespace {
 
-constexpr int kWavesH = 4;
 constexpr int kRmax = 8;  // gqa * n_q rows per KV head
+constexpr int kThreads = 256;
 
 template <int T, int D> constexpr int hd_row_bytes() { return T == T_F16 ? 2 * D : (T == T_Q8_0 ? D / 32 * 34 : D / 32 * 18); }
 
-__device__ __forceinline__ float h2f_bits(uint16_t x) { return (float)__builtin_bit_cast(_Float16, x); }
+__device__ __forceinline__ float h2f_bits(uint32_t x) { return (float)__builtin_bit_cast(_Float16, (uint16_t)x); }
 
-// Value e of a row (exact: binary16 as is, q8_0 d*q, q4_0 d*(n-8) with byte j holding element j
-// in its low nibble and element j+16 in its high nibble).
-template <int T>
-__device__ __forceinline__ float row_value(const uint8_t *row, int e) {
-    if constexpr (T == T_F16) {
-        return h2f_bits(*reinterpret_cast<const uint16_t *>(row + 2 * e));
-    } else if constexpr (T == T_Q8_0) {
-        const uint8_t *b = row + 34 * (e >> 5);
-        const float d = h2f_bits((uint16_t)(b[0] | (b[1] << 8)));
-        return d * (float)(int8_t)b[2 + (e & 31)];
-    } else {
-        const uint8_t *b = row + 18 * (e >> 5);
-        const float d = h2f_bits((uint16_t)(b[0] | (b[1] << 8)));
-        const int i = e & 31;
-        const int byte = b[2 + (i & 15)];
-        const int n = i < 16 ? (byte & 15) : (byte >> 4);
-        return d * (float)(n - 8);
+// Sum over each aligned group of P lanes (4 or 16), in every lane of the group: DPP quad swaps,
+// then rotations by 4 and 8 inside a 16-lane row.
+template <int P>
+__device__ __forceinline__ float group_sum(float x) {
+    x += dpp_f<kQuadSwap1>(x);
+    x += dpp_f<kQuadSwap2>(x);
+    if constexpr (P == 16) {
+        x += dpp_f<kRowRor4>(x);
+        x += dpp_f<kRowRor8>(x);
+    }
+    return x;
+}
+
+template <int D, int KT, int VT>
+struct HdGeom {
+    static constexpr int KC = D == 64 ? 64 : 16;           // keys per chunk
+    static constexpr int P = kThreads / KC;                // threads per key in Q.K
+    static constexpr int E = D / P;                        // dims per thread in Q.K (16 or 32)
+    static constexpr int KW = hd_row_bytes<KT, D>() / 4;   // 4-byte words per K row
+    static constexpr int VW = hd_row_bytes<VT, D>() / 4;
+    static constexpr int KWP = KW | 1, VWP = VW | 1;       // odd LDS row pitch: no bank conflicts
+    static constexpr int NK = (KC * KW + kThreads - 1) / kThreads;  // words per thread per chunk
+    static constexpr int NV = (KC * VW + kThreads - 1) / kThreads;
+    static constexpr int RPT = kRmax * D / kThreads;       // P.V rows per thread (8 or 2)
+    static_assert(P == 4 || P == 16, "Q.K groups are DPP quads or 16-lane rows");
+    static_assert(E == 16, "a thread's Q.K dims are half of one quant block");
+};
+
+// Chunk rows [c0, c0 + KC) of one KV head, words of row r in order; cells at or past c_end read
+// nothing (0).
+template <int NW, int W, int KC>
+__device__ __forceinline__ void load_rows(uint32_t (&buf)[NW], const uint8_t *base, int64_t s1, int64_t c0, int64_t c_end,
+                                          int tid) {
+#pragma unroll
+    for (int u = 0; u < NW; ++u) {
+        const int f = tid + kThreads * u;
+        const int r = f / W, w = f % W;
+        buf[u] = 0u;
+        if (f < KC * W && c0 + r < c_end) buf[u] = *reinterpret_cast<const uint32_t *>(base + (c0 + r) * s1 + 4 * w);
+    }
+}
+template <int NW, int W, int WP, int KC>
+__device__ __forceinline__ void store_rows(const uint32_t (&buf)[NW], uint32_t *lds, int tid) {
+#pragma unroll
+    for (int u = 0; u < NW; ++u) {
+        const int f = tid + kThreads * u;
+        if (f < KC * W) lds[(f / W) * WP + f % W] = buf[u];
     }
 }
 
-__device__ __forceinline__ float wave_max_f(float x) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
-    return x;
-}
-__device__ __forceinline__ float wave_sum_f(float x) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
-    return x;
+// Value e of a V row in LDS (exact: binary16 as is; q4_0 d*(n-8), byte j of a block holding
+// element j in its low nibble and element j+16 in its high nibble).
+template <int VT>
+__device__ __forceinline__ float v_value(const uint8_t *row, int e) {
+    if constexpr (VT == T_F16) {
+        return h2f_bits(*reinterpret_cast<const uint16_t *>(row + 2 * e));
+    } else {
+        const uint8_t *b = row + 18 * (e >> 5);
+        const float d = h2f_bits(*reinterpret_cast<const uint16_t *>(b));
+        const int i = e & 31;
+        const int byte = b[2 + (i & 15)];
+        return d * (float)((i < 16 ? (byte & 15) : (byte >> 4)) - 8);
+    }
 }
 
 template <int D, int KT, int VT, bool CAP>
-__global__ void __launch_bounds__(64 * kWavesH) decode_hd_kernel(const SegParams p) {
-    constexpr int EPL = D / 64;  // head_dim values per lane in P.V
-    constexpr int PS = 2 + D;    // partial row stride
-    __shared__ float s_q[kRmax][D];
-    __shared__ float s_p[kWavesH][kRmax][64];
-    __shared__ float s_m[kWavesH][kRmax][PS];
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4 : 3))) decode_hd_kernel(const SegParams p) {
+    using G = HdGeom<D, KT, VT>;
+    constexpr int KC = G::KC, P = G::P, E = G::E, PS = 2 + D;
+    __shared__ __align__(16) float s_q[kRmax][D];
+    __shared__ uint32_t s_k[KC * G::KWP];
+    __shared__ uint32_t s_v[KC * G::VWP];
+    __shared__ __align__(16) float s_s[kRmax][KC];  // scores, then weights
+    __shared__ float s_alpha[kRmax];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     int bid = blockIdx.x;
     const int split = bid % p.n_splits;
     bid /= p.n_splits;
@@ -79,131 +118,169 @@ __global__ void __launch_bounds__(64 * kWavesH) decode_hd_kernel(const SegParams
     const uint8_t *kbase = p.k + (int64_t)g * p.k_s2;
     const uint8_t *vbase = p.v + (int64_t)g * p.v_s2;
 
-    // Q rows rho = i * gqa + r (query i, head g * gqa + r), scaled, in LDS
-    for (int idx = tid; idx < R * D; idx += 64 * kWavesH) {
+    // Q rows rho = i * gqa + r (query i, head g * gqa + r) in LDS; rows past R are zero
+    for (int idx = tid; idx < kRmax * D; idx += kThreads) {
         const int rho = idx / D, e = idx % D;
         const int r = rho % p.gqa, i = rho / p.gqa;
-        s_q[rho][e] = (float)p.q[(int64_t)i * p.q_s1 + (int64_t)(g * p.gqa + r) * p.q_s2 + (int64_t)b * p.q_s3 + e];
-    }
-    __syncthreads();
-
-    float m[kRmax], l[kRmax], acc[kRmax][EPL];
-#pragma unroll
-    for (int rho = 0; rho < kRmax; ++rho) {
-        m[rho] = -INFINITY;
-        l[rho] = 0.f;
-#pragma unroll
-        for (int k = 0; k < EPL; ++k) acc[rho][k] = 0.f;
+        s_q[rho][e] = rho < R ? (float)p.q[(int64_t)i * p.q_s1 + (int64_t)(g * p.gqa + r) * p.q_s2 + (int64_t)b * p.q_s3 + e]
+                              : 0.f;
     }
 
-    const int64_t n_ch = c_end > c_beg ? (c_end - c_beg + 63) / 64 : 0;
-    for (int64_t ch = wave; ch < n_ch; ch += kWavesH) {
-        const int64_t c0 = c_beg + 64 * ch;
-        const int64_t j = c0 + lane;  // this lane's key (segment-local cell)
-        float s[kRmax];
+    // softmax state of the rows this wave owns (w, w + 4), the same in every lane
+    float m_own[2] = {-INFINITY, -INFINITY}, l_own[2] = {0.f, 0.f};
+    // P.V accumulators: column e_pv of rows rho_pv(k)
+    const int e_pv = tid % D, rg = tid / D;
+    float acc[G::RPT];
 #pragma unroll
-        for (int rho = 0; rho < kRmax; ++rho) s[rho] = -INFINITY;
-        if (j < c_end) {
-            const uint8_t *krow = kbase + j * p.k_s1;
+    for (int k = 0; k < G::RPT; ++k) acc[k] = 0.f;
+
+    const int kq = tid / P, pq = tid % P;  // Q.K: key kq of the chunk, dims [pq*E, pq*E + E)
+
+    const int64_t n_ch = c_end > c_beg ? (c_end - c_beg + KC - 1) / KC : 0;
+    uint32_t pk[G::NK], pv[G::NV];
+    if (n_ch > 0) {
+        load_rows<G::NK, G::KW, KC>(pk, kbase, p.k_s1, c_beg, c_end, tid);
+        load_rows<G::NV, G::VW, KC>(pv, vbase, p.v_s1, c_beg, c_end, tid);
+    }
+    for (int64_t ch = 0; ch < n_ch; ++ch) {
+        const int64_t c0 = c_beg + ch * KC;
+        __syncthreads();  // the previous chunk's P.V is done with s_k, s_v and s_s
+        store_rows<G::NK, G::KW, G::KWP, KC>(pk, s_k, tid);
+        store_rows<G::NV, G::VW, G::VWP, KC>(pv, s_v, tid);
+        __syncthreads();
+        if (ch + 1 < n_ch) {  // next chunk in flight during this one
+            load_rows<G::NK, G::KW, KC>(pk, kbase, p.k_s1, c0 + KC, c_end, tid);
+            load_rows<G::NV, G::VW, KC>(pv, vbase, p.v_s1, c0 + KC, c_end, tid);
+        }
+
+        // ---- Q.K
+        {
+            const uint8_t *krow = reinterpret_cast<const uint8_t *>(s_k + kq * G::KWP);
+            const int e0 = pq * E;
+            float kv[E];
+            float kscale = 1.f;
+            if constexpr (KT == T_F16) {
+#pragma unroll
+                for (int i = 0; i < E; i += 2) {
+                    const uint32_t w = *reinterpret_cast<const uint32_t *>(krow + 2 * (e0 + i));
+                    kv[i] = h2f_bits(w & 0xFFFFu);
+                    kv[i + 1] = h2f_bits(w >> 16);
+                }
+            } else {
+                const uint8_t *blk = krow + 34 * (e0 >> 5);
+                kscale = h2f_bits(*reinterpret_cast<const uint16_t *>(blk));
+                const uint8_t *codes = blk + 2 + (e0 & 31);
+#pragma unroll
+                for (int i = 0; i < E; i += 2) {
+                    const uint32_t w = *reinterpret_cast<const uint16_t *>(codes + i);
+                    kv[i] = (float)(int8_t)(w & 0xFFu);
+                    kv[i + 1] = (float)(int8_t)(w >> 8);
+                }
+            }
             float dot[kRmax];
 #pragma unroll
-            for (int rho = 0; rho < kRmax; ++rho) dot[rho] = 0.f;
-            for (int e = 0; e < D; ++e) {
-                const float kv = row_value<KT>(krow, e);
+            for (int rho = 0; rho < kRmax; ++rho) {
+                float a = 0.f;
+                if (rho < R) {
 #pragma unroll
-                for (int rho = 0; rho < kRmax; ++rho)
-                    if (rho < R) dot[rho] = fmaf(s_q[rho][e], kv, dot[rho]);
+                    for (int i = 0; i < E; i += 4) {
+                        const float4 q4 = *reinterpret_cast<const float4 *>(&s_q[rho][e0 + i]);
+                        a = fmaf(q4.x, kv[i], a);
+                        a = fmaf(q4.y, kv[i + 1], a);
+                        a = fmaf(q4.z, kv[i + 2], a);
+                        a = fmaf(q4.w, kv[i + 3], a);
+                    }
+                }
+                dot[rho] = a * kscale;
+                // one row's Q slice live at a time (the scheduler would otherwise hoist every
+                // row's LDS reads and spill)
+                __builtin_amdgcn_sched_barrier(0);
             }
 #pragma unroll
-            for (int rho = 0; rho < kRmax; ++rho) {
-                if (rho >= R) continue;
-                const int i = rho / p.gqa;
-                float x = p.scale_log2 * dot[rho] * 0.6931471805599453f;  // scale * <q, k>
-                if (CAP) x = p.cap_l2 * 0.6931471805599453f * tanhf(p.cap_cs * dot[rho]);
-                bool vis = p.q_pos0 < 0 || p.pos0 + j <= p.q_pos0 + i;
-                if (vis && p.mask) {
-                    const float mv = (float)p.mask[p.pos0 + j + (int64_t)i * p.m_s1 + (int64_t)b * p.m_s3];
-                    x += mv;
-                    vis = mv > -INFINITY;
+            for (int rho = 0; rho < kRmax; ++rho)
+                if (rho < R) dot[rho] = group_sum<P>(dot[rho]);
+            if (pq == 0) {
+                const int64_t j = c0 + kq;  // segment-local cell
+#pragma unroll
+                for (int rho = 0; rho < kRmax; ++rho) {
+                    if (rho >= R) continue;
+                    const int i = rho / p.gqa;
+                    float x = CAP ? p.cap_l2 * kLn2 * tanhf(p.cap_cs * dot[rho]) : p.scale_log2 * kLn2 * dot[rho];
+                    bool vis = j < c_end && (p.q_pos0 < 0 || p.pos0 + j <= p.q_pos0 + i);
+                    if (vis && p.mask) {
+                        const float mv = (float)p.mask[p.pos0 + j + (int64_t)i * p.m_s1 + (int64_t)b * p.m_s3];
+                        x += mv;
+                        vis = mv > -INFINITY;
+                    }
+                    s_s[rho][kq] = vis ? x : -INFINITY;
                 }
-                s[rho] = vis ? x : -INFINITY;
             }
         }
-        // online softmax per row over this chunk (natural-log units)
-        uint64_t live = 0;
+        __syncthreads();
+
+        // ---- online softmax: wave w, rows w and w + 4 (natural-log units)
 #pragma unroll
-        for (int rho = 0; rho < kRmax; ++rho) {
+        for (int h = 0; h < 2; ++h) {
+            const int rho = wave + 4 * h;
             if (rho >= R) continue;
-            const float cm = wave_max_f(s[rho]);
-            float pj = 0.f;
-            if (cm > -INFINITY) {
-                if (cm > m[rho]) {
-                    const float a = m[rho] == -INFINITY ? 0.f : __expf(m[rho] - cm);
-                    l[rho] *= a;
+            const float sj = lane < KC ? s_s[rho][lane] : -INFINITY;
+            const float cm = wave_max(sj);
+            float alpha = 1.f;
+            if (cm > m_own[h]) {
+                alpha = m_own[h] == -INFINITY ? 0.f : __expf(m_own[h] - cm);
+                m_own[h] = cm;
+            }
+            const float pj = sj == -INFINITY ? 0.f : __expf(sj - m_own[h]);
+            l_own[h] = fmaf(l_own[h], alpha, wave_sum(pj));
+            if (lane < KC) s_s[rho][lane] = pj;
+            if (lane == 0) s_alpha[rho] = alpha;
+        }
+        __syncthreads();
+
+        // ---- P.V over all KC rows of the chunk: rows past the segment's end hold zeros in LDS
+        // and have weight 0, as have masked keys
+        {
 #pragma unroll
-                    for (int k = 0; k < EPL; ++k) acc[rho][k] *= a;
-                    m[rho] = cm;
+            for (int k = 0; k < G::RPT; ++k) {
+                const int rho = rg + (kThreads / D) * k;
+                if (rho < R) acc[k] *= s_alpha[rho];
+            }
+            const uint8_t *vcol = reinterpret_cast<const uint8_t *>(s_v);
+#pragma unroll 1
+            for (int jj = 0; jj < KC; jj += 4) {
+                float v[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) v[u] = v_value<VT>(vcol + (jj + u) * (4 * G::VWP), e_pv);
+#pragma unroll
+                for (int k = 0; k < G::RPT; ++k) {
+                    const int rho = rg + (kThreads / D) * k;
+                    if (rho < R) {
+                        const float4 w = *reinterpret_cast<const float4 *>(&s_s[rho][jj]);
+                        acc[k] = fmaf(w.x, v[0], fmaf(w.y, v[1], fmaf(w.z, v[2], fmaf(w.w, v[3], acc[k]))));
+                    }
                 }
-                pj = s[rho] == -INFINITY ? 0.f : __expf(s[rho] - m[rho]);
-            }
-            l[rho] += pj;  // per-lane part; summed over the wave at the end
-            s_p[wave][rho][lane] = pj;
-            live |= __builtin_amdgcn_ballot_w64(pj > 0.f);
-        }
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-        // P.V over the chunk's keys with a nonzero weight
-        while (live) {
-            const int jj = __builtin_ctzll(live);
-            live &= live - 1;
-            const uint8_t *vrow = vbase + (c0 + jj) * p.v_s1;
-            float vv[EPL];
-#pragma unroll
-            for (int k = 0; k < EPL; ++k) vv[k] = row_value<VT>(vrow, EPL * lane + k);
-#pragma unroll
-            for (int rho = 0; rho < kRmax; ++rho) {
-                if (rho >= R) continue;
-                const float w = s_p[wave][rho][jj];
-#pragma unroll
-                for (int k = 0; k < EPL; ++k) acc[rho][k] = fmaf(w, vv[k], acc[rho][k]);
             }
         }
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
     }
 
-    // the wave's state per row to LDS, then the four waves combined
-#pragma unroll
-    for (int rho = 0; rho < kRmax; ++rho) {
-        if (rho >= R) continue;
-        const float lt = wave_sum_f(l[rho]);
-        if (lane == 0) {
-            s_m[wave][rho][0] = m[rho];
-            s_m[wave][rho][1] = lt;
-        }
-#pragma unroll
-        for (int k = 0; k < EPL; ++k) s_m[wave][rho][2 + EPL * lane + k] = acc[rho][k];
-    }
-    __syncthreads();
+    // ---- partials: M and S from the owning waves, VKQ from every thread
     const int slot = p.slot0 + split;
-    for (int idx = tid; idx < R * PS; idx += 64 * kWavesH) {
-        const int rho = idx / PS, c = idx % PS;
-        float M = -INFINITY;
-#pragma unroll
-        for (int wv = 0; wv < kWavesH; ++wv) M = fmaxf(M, s_m[wv][rho][0]);
-        float v = 0.f;
-        if (c == 0) {
-            v = M;
-        } else if (M > -INFINITY) {
-#pragma unroll
-            for (int wv = 0; wv < kWavesH; ++wv) {
-                const float mw = s_m[wv][rho][0];
-                if (mw > -INFINITY) v = fmaf(s_m[wv][rho][c], __expf(mw - M), v);
-            }
-        }
+    auto out_row = [&](int rho) {
         const int r = rho % p.gqa, i = rho / p.gqa;
-        const int64_t row = (g * p.gqa + r) + (int64_t)p.n_head * (i + (int64_t)p.n_q * b);
-        p.partials[((int64_t)slot * p.n_rows + row) * PS + c] = v;
+        return ((int64_t)slot * p.n_rows + (g * p.gqa + r) + (int64_t)p.n_head * (i + (int64_t)p.n_q * b)) * PS;
+    };
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int rho = wave + 4 * h;
+        if (rho < R && lane == 0) {
+            p.partials[out_row(rho)] = m_own[h];
+            p.partials[out_row(rho) + 1] = l_own[h];
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < G::RPT; ++k) {
+        const int rho = rg + (kThreads / D) * k;
+        if (rho < R) p.partials[out_row(rho) + 2 + e_pv] = acc[k];
     }
 }
 
@@ -216,15 +293,18 @@ __global__ void __launch_bounds__(D) merge_hd_kernel(const float *part, int n_se
     const int64_t row = blockIdx.x;
     const int t = threadIdx.x;
     float M = -INFINITY;
+#pragma unroll 8
     for (int sg = 0; sg < n_seg; ++sg) M = fmaxf(M, part[((int64_t)sg * n_rows + row) * PS]);
     float S = 0.f, a = 0.f;
     if (M > -INFINITY) {
+        // branch-free so that the unrolled loads of several segments are in flight together
+#pragma unroll 8
         for (int sg = 0; sg < n_seg; ++sg) {
             const float *q = part + ((int64_t)sg * n_rows + row) * PS;
-            if (q[0] == -INFINITY) continue;
-            const float w = __expf(q[0] - M);
-            S = fmaf(q[1], w, S);
-            a = fmaf(q[2 + t], w, a);
+            const float m = q[0], s = q[1], v = q[2 + t];
+            const float w = m == -INFINITY ? 0.f : __expf(m - M);
+            S = fmaf(s, w, S);
+            a = fmaf(v, w, a);
         }
     }
     const bool ok = M > -INFINITY && S > 0.f;
@@ -237,9 +317,9 @@ hipError_t launch_hd(const SegParams &p, hipStream_t s) {
     const int64_t blocks = (int64_t)p.n_splits * p.n_head_kv * p.n_seq;
     if (blocks <= 0) return hipSuccess;
     if (p.cap_l2 != 0.f)
-        launch_seg(decode_hd_kernel<D, KT, VT, true>, dim3((unsigned)blocks), dim3(64 * kWavesH), s, p);
+        launch_seg(decode_hd_kernel<D, KT, VT, true>, dim3((unsigned)blocks), dim3(kThreads), s, p);
     else
-        launch_seg(decode_hd_kernel<D, KT, VT, false>, dim3((unsigned)blocks), dim3(64 * kWavesH), s, p);
+        launch_seg(decode_hd_kernel<D, KT, VT, false>, dim3((unsigned)blocks), dim3(kThreads), s, p);
     return hipGetLastError();
 }
 

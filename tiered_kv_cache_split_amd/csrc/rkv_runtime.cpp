@@ -112,9 +112,9 @@ int check_kv(const rkv_tensor *t, const char *name, bool is_k, bool any_d = fals
     const int64_t rb = row_bytes(t->type, t->ne[0]);
     if (t->ne[1] > 1 && t->nb[1] < rb) return fail(RKV_ERR_ARG, "%s: nb[1] smaller than a row", name);
     if (t->ne[2] > 1 && t->nb[2] < rb) return fail(RKV_ERR_ARG, "%s: nb[2] smaller than a row", name);
-    // the head-dim-128 kernels read rows in 8-byte pieces; the kernel for other head dims reads
-    // binary16 values and bytes
-    const int al = t->ne[0] == kHeadDim ? 8 : 2;
+    // the head-dim-128 kernels read rows in 8-byte pieces, the kernel for other head dims in
+    // 4-byte words (every row size there is a multiple of 4 bytes)
+    const int al = t->ne[0] == kHeadDim ? 8 : 4;
     if ((t->nb[1] | t->nb[2]) % al != 0 || ((uintptr_t)t->data) % al != 0)
         return fail(RKV_ERR_UNSUPPORTED, "%s: data and nb[1], nb[2] must be multiples of %d bytes", name, al);
     if (t->nb[1] >= ((int64_t)1 << 25) || t->nb[1] < 0 || t->nb[2] < 0)
@@ -273,11 +273,11 @@ int ensure_partials(rkv_ctx *ctx, int64_t floats, hipStream_t s) {
 // Split-K factor of a device segment for the vector kernel (4-wave workgroups): about two
 // workgroups per CU, i.e. one full round of resident workgroups, with at least 256 cells
 // (one chunk per wave) per split.
-int vec_splits(const rkv_ctx *ctx, int64_t n_cells, int64_t n_groups) {
+int vec_splits(const rkv_ctx *ctx, int64_t n_cells, int64_t n_groups, int blocks_per_cu = 2) {
     if (ctx->splits_override > 0)
         return (int)std::max<int64_t>(1, std::min<int64_t>(ctx->splits_override, (n_cells + kChunk - 1) / kChunk));
     if (n_cells <= 0) return 1;
-    const int64_t target_blocks = 2LL * ctx->n_cu;
+    const int64_t target_blocks = (int64_t)blocks_per_cu * ctx->n_cu;
     int64_t want = (target_blocks + n_groups - 1) / std::max<int64_t>(1, n_groups);
     const int64_t max_by_len = std::max<int64_t>(1, n_cells / 256);
     want = std::max<int64_t>(1, std::min(want, max_by_len));
@@ -357,7 +357,8 @@ void seg_plan(const rkv_ctx *ctx, int64_t n_cells, const SegParams &p, bool mfma
         cps = (n_cells + want - 1) / want;
         cps = std::max<int64_t>(kChunk, (cps + kChunk - 1) / kChunk * kChunk);
     } else {
-        const int splits = vec_splits(ctx, n_cells, (int64_t)p.n_head_kv * p.n_seq);
+        // the kernel for head dims other than 128 holds four workgroups per CU
+        const int splits = vec_splits(ctx, n_cells, (int64_t)p.n_head_kv * p.n_seq, p.d == kHeadDim ? 2 : 4);
         cps = (n_cells + splits - 1) / splits;
         cps = std::max<int64_t>(kChunk, (cps + kChunk - 1) / kChunk * kChunk);
     }
