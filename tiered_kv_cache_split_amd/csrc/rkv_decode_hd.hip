@@ -99,7 +99,11 @@ template <int D, int KT, int VT, bool CAP>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4 : 3))) decode_hd_kernel(const SegParams p) {
     using G = HdGeom<D, KT, VT>;
     constexpr int KC = G::KC, P = G::P, E = G::E, PS = 2 + D;
-    __shared__ __align__(16) float s_q[kRmax][D];
+    // Q row rho, part pq (16 values) at rho * P * QP + pq * QP: a pitch of 20 floats puts the P
+    // parts that lanes of one wave read together on distinct LDS banks (a pitch of 16 maps every
+    // fourth part to the same banks)
+    constexpr int QP = E + 4;
+    __shared__ __align__(16) float s_q[kRmax * P * QP];
     __shared__ uint32_t s_k[KC * G::KWP];
     __shared__ uint32_t s_v[KC * G::VWP];
     __shared__ __align__(16) float s_s[kRmax][KC];  // scores, then weights
@@ -122,7 +126,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D
     for (int idx = tid; idx < kRmax * D; idx += kThreads) {
         const int rho = idx / D, e = idx % D;
         const int r = rho % p.gqa, i = rho / p.gqa;
-        s_q[rho][e] = rho < R ? (float)p.q[(int64_t)i * p.q_s1 + (int64_t)(g * p.gqa + r) * p.q_s2 + (int64_t)b * p.q_s3 + e]
+        s_q[rho * P * QP + (e / E) * QP + e % E] = rho < R ? (float)p.q[(int64_t)i * p.q_s1 + (int64_t)(g * p.gqa + r) * p.q_s2 + (int64_t)b * p.q_s3 + e]
                               : 0.f;
     }
 
@@ -184,7 +188,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D
                 if (rho < R) {
 #pragma unroll
                     for (int i = 0; i < E; i += 4) {
-                        const float4 q4 = *reinterpret_cast<const float4 *>(&s_q[rho][e0 + i]);
+                        const float4 q4 = *reinterpret_cast<const float4 *>(&s_q[rho * P * QP + pq * QP + i]);
                         a = fmaf(q4.x, kv[i], a);
                         a = fmaf(q4.y, kv[i + 1], a);
                         a = fmaf(q4.z, kv[i + 2], a);
