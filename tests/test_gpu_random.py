@@ -1,5 +1,5 @@
 """Randomised GPU parity sweep: seeded random shapes, types, layouts, splits, tails, lift modes,
-masks, row lists and logit soft-caps through every entry point, each case against the fp64 oracle.  The cases are small
+masks, row lists, logit soft-caps and head dims through every entry point, each case against the fp64 oracle.  The cases are small
 (the oracle runs them in well under a second) and cover combinations the targeted tests do
 not enumerate: every kernel family is reached (vector, matrix-core q8_0/q4_0, matrix-core
 binary16 window/tail/rows, prefill), with ragged lengths throughout."""
@@ -152,3 +152,40 @@ def test_random_host_tail(run, seed):
         run.ctx.set_tail_mode(run.rkv.RKV_TAIL_LIFT)
     Oref, Lref = oracle_decode(w, mask=mask, softcap=cap)
     assert_close(O, L, Oref, Lref, what=f"random host tail {seed}")
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_decode_head_dims(run, seed):
+    """Head dims 64 and 256 through the window + tail split: random heads (up to 8 query rows
+    per KV head), lengths, splits, types, layouts, tails, lift engines, masks and soft-caps."""
+    rng = np.random.default_rng(9000 + seed)
+    d = int(rng.choice([64, 256]))
+    n_head_kv = int(rng.choice([1, 2, 4, 8]))
+    n_q = int(rng.choice([1, 1, 2]))
+    gqa = int(rng.choice([g for g in (1, 2, 3, 4, 5, 8) if g * n_q <= 8]))
+    n_kv = int(rng.integers(1, 2500))
+    kt, vt = TYPES[int(rng.integers(0, 4))]
+    tail = str(rng.choice(["host", "device", "none"]))
+    wc = n_kv if tail == "none" else int(rng.integers(0, n_kv + 1))
+    if wc == n_kv:
+        tail = "none"
+    tile = int(rng.integers(1, 1500))
+    layout = str(rng.choice(["cell", "head"]))
+    q, k, v = gen.draw_qkv(rng, n_head_kv * gqa, n_q, n_head_kv, n_kv, d=d, dv=d, k_type=kt, v_type=vt)
+    w = dict(n_head=n_head_kv * gqa, n_head_kv=n_head_kv, q=q, k=k, v=v, k_type=kt, v_type=vt, d=d,
+             scale=1 / np.sqrt(d), n_kv=n_kv, wc=wc, tile_kv=tile)
+    mask = gen.random_mask_f16(rng, n_q, n_kv, p_hidden=0.3) if rng.random() < 0.5 else None
+    cap = draw_softcap(100 + seed)
+    lift = int(rng.choice([run.rkv.RKV_LIFT_BULK, run.rkv.RKV_LIFT_KERNEL]))
+    step(f"random head-dim decode seed {seed}: d {d} heads {n_head_kv}x{gqa} n_q {n_q} n_kv {n_kv} wc {wc} "
+         f"tile {tile} types {kt}/{vt} tail {tail} layout {layout} mask {mask is not None} softcap {cap:.3f} "
+         f"lift {lift}")
+    run.ctx.set_softcap(cap)
+    run.ctx.set_lift_mode(lift)
+    try:
+        O, L = run.decode(w, tail=None if tail == "none" else tail, mask=mask, layout=layout)
+    finally:
+        run.ctx.set_lift_mode(run.rkv.RKV_LIFT_AUTO)
+        run.ctx.set_softcap(0.0)
+    Oref, Lref = oracle_decode(w, mask=mask, softcap=cap)
+    assert_close(O, L, Oref, Lref, what=f"random head-dim decode {seed}")
