@@ -13,7 +13,9 @@
 //        read this KV head are done together.
 //   softmax  wave w owns rows w and w + 4: chunk max, rescale factor and weights, in natural-log
 //        units, kept in LDS for the P.V step.
-//   P.V  thread t owns output column t % D of rows t / D (+ 4 for D = 64).
+//   P.V  thread t owns output column t % D of every row over the chunk's keys j with
+//        j % KS = t / D (KS = 256 / D key subsets, so each V value is dequantised once); the
+//        subsets' sums are added through LDS at the end.
 #include "rkv_internal.h"
 #include "rkv_wave.h"
 
@@ -53,7 +55,8 @@ struct HdGeom {
     static constexpr int KWP = KW | 1, VWP = VW | 1;       // odd LDS row pitch: no bank conflicts
     static constexpr int NK = (KC * KW + kThreads - 1) / kThreads;  // words per thread per chunk
     static constexpr int NV = (KC * VW + kThreads - 1) / kThreads;
-    static constexpr int RPT = kRmax * D / kThreads;       // P.V rows per thread (8 or 2)
+    static constexpr int KS = kThreads / D;                // P.V: threads per column (key subsets)
+    static constexpr int KPS = KC / KS;                    // keys per subset (16)
     static_assert(P == 4 || P == 16, "Q.K groups are DPP quads or 16-lane rows");
     static_assert(E == 16, "a thread's Q.K dims are half of one quant block");
 };
@@ -106,7 +109,11 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D
     __shared__ __align__(16) float s_q[kRmax * P * QP];
     __shared__ uint32_t s_k[KC * G::KWP];
     __shared__ uint32_t s_v[KC * G::VWP];
-    __shared__ __align__(16) float s_s[kRmax][KC];  // scores, then weights
+    // scores, then weights; key j of the chunk at (j % KS) * KPS + j / KS so that each key
+    // subset's weights are contiguous
+    __shared__ __align__(16) float s_s[kRmax][KC];
+    __shared__ float s_red[G::KS > 1 ? G::KS * kRmax * D : 1];  // key-subset sums of P.V
+    auto widx = [](int j) { return (j % G::KS) * G::KPS + j / G::KS; };
     __shared__ float s_alpha[kRmax];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -132,11 +139,11 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D
 
     // softmax state of the rows this wave owns (w, w + 4), the same in every lane
     float m_own[2] = {-INFINITY, -INFINITY}, l_own[2] = {0.f, 0.f};
-    // P.V accumulators: column e_pv of rows rho_pv(k)
-    const int e_pv = tid % D, rg = tid / D;
-    float acc[G::RPT];
+    // P.V accumulators: column e_pv of every row, over key subset ks
+    const int e_pv = tid % D, ks = tid / D;
+    float acc[kRmax];
 #pragma unroll
-    for (int k = 0; k < G::RPT; ++k) acc[k] = 0.f;
+    for (int rho = 0; rho < kRmax; ++rho) acc[rho] = 0.f;
 
     const int kq = tid / P, pq = tid % P;  // Q.K: key kq of the chunk, dims [pq*E, pq*E + E)
 
@@ -216,7 +223,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D
                         x += mv;
                         vis = mv > -INFINITY;
                     }
-                    s_s[rho][kq] = vis ? x : -INFINITY;
+                    s_s[rho][widx(kq)] = vis ? x : -INFINITY;
                 }
             }
         }
@@ -227,7 +234,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D
         for (int h = 0; h < 2; ++h) {
             const int rho = wave + 4 * h;
             if (rho >= R) continue;
-            const float sj = lane < KC ? s_s[rho][lane] : -INFINITY;
+            const float sj = lane < KC ? s_s[rho][widx(lane)] : -INFINITY;
             const float cm = wave_max(sj);
             float alpha = 1.f;
             if (cm > m_own[h]) {
@@ -236,7 +243,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D
             }
             const float pj = sj == -INFINITY ? 0.f : __expf(sj - m_own[h]);
             l_own[h] = fmaf(l_own[h], alpha, wave_sum(pj));
-            if (lane < KC) s_s[rho][lane] = pj;
+            if (lane < KC) s_s[rho][widx(lane)] = pj;
             if (lane == 0) s_alpha[rho] = alpha;
         }
         __syncthreads();
@@ -245,22 +252,19 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D
         // and have weight 0, as have masked keys
         {
 #pragma unroll
-            for (int k = 0; k < G::RPT; ++k) {
-                const int rho = rg + (kThreads / D) * k;
-                if (rho < R) acc[k] *= s_alpha[rho];
-            }
+            for (int rho = 0; rho < kRmax; ++rho)
+                if (rho < R) acc[rho] *= s_alpha[rho];
             const uint8_t *vcol = reinterpret_cast<const uint8_t *>(s_v);
 #pragma unroll 1
-            for (int jj = 0; jj < KC; jj += 4) {
+            for (int t = 0; t < G::KPS; t += 4) {
                 float v[4];
 #pragma unroll
-                for (int u = 0; u < 4; ++u) v[u] = v_value<VT>(vcol + (jj + u) * (4 * G::VWP), e_pv);
+                for (int u = 0; u < 4; ++u) v[u] = v_value<VT>(vcol + (ks + G::KS * (t + u)) * (4 * G::VWP), e_pv);
 #pragma unroll
-                for (int k = 0; k < G::RPT; ++k) {
-                    const int rho = rg + (kThreads / D) * k;
+                for (int rho = 0; rho < kRmax; ++rho) {
                     if (rho < R) {
-                        const float4 w = *reinterpret_cast<const float4 *>(&s_s[rho][jj]);
-                        acc[k] = fmaf(w.x, v[0], fmaf(w.y, v[1], fmaf(w.z, v[2], fmaf(w.w, v[3], acc[k]))));
+                        const float4 w = *reinterpret_cast<const float4 *>(&s_s[rho][ks * G::KPS + t]);
+                        acc[rho] = fmaf(w.x, v[0], fmaf(w.y, v[1], fmaf(w.z, v[2], fmaf(w.w, v[3], acc[rho]))));
                     }
                 }
             }
@@ -281,10 +285,22 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D
             p.partials[out_row(rho) + 1] = l_own[h];
         }
     }
+    if constexpr (G::KS == 1) {
 #pragma unroll
-    for (int k = 0; k < G::RPT; ++k) {
-        const int rho = rg + (kThreads / D) * k;
-        if (rho < R) p.partials[out_row(rho) + 2 + e_pv] = acc[k];
+        for (int rho = 0; rho < kRmax; ++rho)
+            if (rho < R) p.partials[out_row(rho) + 2 + e_pv] = acc[rho];
+    } else {
+#pragma unroll
+        for (int rho = 0; rho < kRmax; ++rho)
+            if (rho < R) s_red[(ks * kRmax + rho) * D + e_pv] = acc[rho];
+        __syncthreads();
+        for (int idx = tid; idx < R * D; idx += kThreads) {
+            const int rho = idx / D, e = idx % D;
+            float a = 0.f;
+#pragma unroll
+            for (int k = 0; k < G::KS; ++k) a += s_red[(k * kRmax + rho) * D + e];
+            p.partials[out_row(rho) + 2 + e] = a;
+        }
     }
 }
 
