@@ -210,21 +210,21 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D
 #pragma unroll
             for (int rho = 0; rho < kRmax; ++rho)
                 if (rho < R) dot[rho] = group_sum<P>(dot[rho]);
-            if (pq == 0) {
-                const int64_t j = c0 + kq;  // segment-local cell
+            // every lane of the key's group holds all row dots: lane pq finishes rows pq, pq + P, ...
+            const int64_t j = c0 + kq;  // segment-local cell
+            for (int rho = pq; rho < R; rho += P) {
+                float dr = dot[0];
 #pragma unroll
-                for (int rho = 0; rho < kRmax; ++rho) {
-                    if (rho >= R) continue;
-                    const int i = rho / p.gqa;
-                    float x = CAP ? p.cap_l2 * kLn2 * tanhf(p.cap_cs * dot[rho]) : p.scale_log2 * kLn2 * dot[rho];
-                    bool vis = j < c_end && (p.q_pos0 < 0 || p.pos0 + j <= p.q_pos0 + i);
-                    if (vis && p.mask) {
-                        const float mv = (float)p.mask[p.pos0 + j + (int64_t)i * p.m_s1 + (int64_t)b * p.m_s3];
-                        x += mv;
-                        vis = mv > -INFINITY;
-                    }
-                    s_s[rho][widx(kq)] = vis ? x : -INFINITY;
+                for (int k = 1; k < kRmax; ++k) dr = rho == k ? dot[k] : dr;
+                const int i = rho / p.gqa;
+                float x = CAP ? p.cap_l2 * kLn2 * tanhf(p.cap_cs * dr) : p.scale_log2 * kLn2 * dr;
+                bool vis = j < c_end && (p.q_pos0 < 0 || p.pos0 + j <= p.q_pos0 + i);
+                if (vis && p.mask) {
+                    const float mv = (float)p.mask[p.pos0 + j + (int64_t)i * p.m_s1 + (int64_t)b * p.m_s3];
+                    x += mv;
+                    vis = mv > -INFINITY;
                 }
+                s_s[rho][widx(kq)] = vis ? x : -INFINITY;
             }
         }
         __syncthreads();
