@@ -68,15 +68,22 @@ def traffic_from_profiles(name: str, kind: str):
     return d.get("hbm_bytes_per_launch")
 
 
-def blas_threads() -> int:
+def physical_cores() -> int:
+    """Physical cores of this host from lscpu (cores per socket x sockets); the logical CPU
+    count if lscpu is unavailable."""
+    import subprocess
     try:
-        from threadpoolctl import threadpool_info
-        n = [i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas"]
-        if n:
-            return int(max(n))
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        kv = {}
+        for line in out.splitlines():
+            if ":" in line:
+                a, b = line.split(":", 1)
+                kv[a.strip()] = b.strip()
+        n = int(kv["Core(s) per socket"]) * int(kv.get("Socket(s)", "1"))
+        # a container may see fewer CPUs than the host has cores
+        return max(1, min(n, len(os.sched_getaffinity(0))))
     except Exception:
-        pass
-    return os.cpu_count() or 1
+        return os.cpu_count() or 1
 
 
 # ------------------------------------------------------------------ workloads on device
@@ -192,61 +199,83 @@ def measured_copy_gbs(nbytes=1 << 30, reps=10) -> float:
 
 # ------------------------------------------------------------------ CPU baseline (oracle)
 def cpu_baseline(num: int, budget_s: float = 12.0, w=None, softcap: float = 0.0):
-    """Time the fp64 oracle on a bounded sample of the same workload and scale to GB/s of
-    the full workload's algorithmic KV bytes."""
+    """Time the fp64 oracle on a bounded sample of the same workload and scale to GB/s of the
+    full workload's algorithmic KV bytes.  BLAS threads = the physical cores (lscpu); one
+    warm-up run (which also sizes the sample to about budget_s / 8), then the median of three;
+    then the same sample on one thread (median of three, or one run if that would exceed the
+    budget)."""
     import numpy as np
+    from threadpoolctl import threadpool_limits
 
     import oracle
     import rkv_inputs as gen
 
     w = gen.make_workload(num) if w is None else w
+    cores = physical_cores()
     n_kv = w["n_kv"]
-    per_cell = None
+    target = budget_s / 8
     if w["kind"] == "rows":
         per_cell = w["n_head_kv"] * (256 + 256)
         total_cells = int((w["kv_rows"] >= 0).sum())
         q = np.stack([oracle.q_values(w["q"][b]) for b in range(w["q"].shape[0])])
-        cells = 1024
-        while True:
-            t0 = time.perf_counter()
-            rows = np.where(w["kv_rows"][:, :cells] >= 0, w["kv_rows"][:, :cells], -1)
+
+        def run_sample(cells):
+            rows = w["kv_rows"][:, :cells]
             k = oracle.kv_values(w["k_type"], w["k"])
             v = oracle.kv_values(w["v_type"], w["v"])
             oracle.attention_rows(q, k, v, rows, w["scale"], None, softcap)
-            dt = time.perf_counter() - t0
-            done = int((rows >= 0).sum())
-            if dt >= budget_s / 2 or cells >= w["n_kv"]:
-                break
-            cells = min(w["n_kv"], cells * 4)
-        full_s = dt * total_cells / max(1, done)
-        sample = f"row lists cut to their first {cells} entries ({done} pool rows of {total_cells}); time scaled linearly"
-        gbs = total_cells * per_cell / full_s / 1e9
-        return {"value": round(gbs, 4), "unit": "GB/s", "cores": blas_threads(), "kind": "oracle",
-                "sample": sample, "oracle_s_full_extrapolated": round(full_s, 2)}
-    per_cell = w["n_head_kv"] * (gen.row_bytes(w["k_type"], w["d"]) + gen.row_bytes(w["v_type"], w["d"]))
-    q = oracle.q_values(w["q"])
-    n_q = w["q"].shape[1]
-    if w["kind"] == "prefill":
-        q = q[:, -min(n_q, 64):]
-    cells = 4096
-    while True:
+            return int((rows >= 0).sum())
+        full_units, unit_bytes = total_cells, per_cell
+    else:
+        per_cell = w["n_head_kv"] * (gen.row_bytes(w["k_type"], w["d"]) + gen.row_bytes(w["v_type"], w["d"]))
+        q = oracle.q_values(w["q"])
+        n_q = w["q"].shape[1]
+        if w["kind"] == "prefill":
+            q = q[:, -min(n_q, 64):]
+        q_scale = (n_q / q.shape[1]) if w["kind"] == "prefill" else 1.0
+
+        def run_sample(cells):
+            k = oracle.kv_values(w["k_type"], w["k"][:cells])
+            v = oracle.kv_values(w["v_type"], w["v"][:cells])
+            oracle.attention(q, k, v, w["scale"], None, softcap)
+            return cells / q_scale
+        full_units, unit_bytes = n_kv, per_cell
+
+    def timed(cells):
         t0 = time.perf_counter()
-        k = oracle.kv_values(w["k_type"], w["k"][:cells])
-        v = oracle.kv_values(w["v_type"], w["v"][:cells])
-        oracle.attention(q, k, v, w["scale"], None, softcap)
-        dt = time.perf_counter() - t0
-        if dt >= budget_s / 2 or cells >= n_kv:
-            break
-        cells = min(n_kv, cells * 4)
-    scale_q = (n_q / q.shape[1]) if w["kind"] == "prefill" else 1.0
-    full_s = dt * (n_kv / cells) * scale_q
-    sample = f"first {cells} of {n_kv} cells"
-    if w["kind"] == "prefill":
-        sample += f", last {q.shape[1]} of {n_q} queries (unmasked)"
-    sample += "; time scaled linearly to the full workload"
-    gbs = n_kv * per_cell / full_s / 1e9
-    return {"value": round(gbs, 4), "unit": "GB/s", "cores": blas_threads(), "kind": "oracle", "sample": sample,
-            "oracle_s_full_extrapolated": round(full_s, 2)}
+        done = run_sample(cells)
+        return time.perf_counter() - t0, done
+
+    with threadpool_limits(limits=cores, user_api="blas"):
+        cells = 1024
+        while True:  # warm-up and sizing
+            dt, done = timed(cells)
+            if dt >= target or cells >= n_kv:
+                break
+            cells = min(n_kv, cells * 2)
+        runs = [timed(cells) for _ in range(3)]
+    med = sorted(r[0] for r in runs)[1]
+    done = runs[0][1]
+    with threadpool_limits(limits=1, user_api="blas"):
+        t1, _ = timed(cells)
+        one = [t1]
+        if 3 * t1 < budget_s / 2:
+            one += [timed(cells)[0] for _ in range(2)]
+    med1 = sorted(one)[len(one) // 2]
+    full_s = med * full_units / max(1e-9, done)
+    full_s1 = med1 * full_units / max(1e-9, done)
+    if w["kind"] == "rows":
+        sample = f"row lists cut to their first {cells} entries ({done} pool rows of {total_cells})"
+    else:
+        sample = f"first {cells} of {n_kv} cells"
+        if w["kind"] == "prefill":
+            sample += f", last {q.shape[1]} of {w['q'].shape[1]} queries (unmasked)"
+    sample += "; median of 3 after one warm-up, time scaled linearly to the full workload"
+    gbs = full_units * unit_bytes / full_s / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": cores, "kind": "oracle", "sample": sample,
+            "oracle_s_full_extrapolated": round(full_s, 2), "sample_s_median": round(med, 3),
+            "single_core": {"value": round(full_units * unit_bytes / full_s1 / 1e9, 4), "unit": "GB/s",
+                            "sample_s_median": round(med1, 3), "runs": len(one)}}
 
 
 # ------------------------------------------------------------------ main

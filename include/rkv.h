@@ -199,8 +199,13 @@ int rkv_attn_decode(rkv_ctx *ctx, const rkv_tensor *q,
                     const rkv_tensor *mask, int64_t wc, int64_t tile_kv, float scale,
                     float *o, float *lse, void *stream);
 
-/* Prefill attention: the same arguments as rkv_attn_decode for any n_q, computed with
- * MFMA f16 tiles (K and V are dequantised to binary16 in LDS).  q_pos0 >= 0 makes it
+/* Prefill attention (patch 0070, fattn.cu ggml_cuda_streaming_flash_attn: the same window +
+ * tail streaming op serves a multi-token chunk, with the mask sliced at the global key
+ * position, a per-tile flash attention and an LSE per tile for the combine; patch 0102,
+ * commit message: 106k-token prefills through lifted tail tiles).  The same arguments as
+ * rkv_attn_decode for any n_q, computed with MFMA f16 tiles: q8_0 K codes and q4_0 V
+ * nibbles enter the matrix cores as exact binary16 integers and their block scales are
+ * applied in fp32 (K) or folded into the softmax weights (V).  q_pos0 >= 0 makes it
  * causal: query i sits at absolute position q_pos0 + i and sees keys at positions
  * <= q_pos0 + i (in addition to the mask); q_pos0 == -1 uses the mask alone. */
 int rkv_attn_prefill(rkv_ctx *ctx, const rkv_tensor *q,

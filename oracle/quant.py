@@ -71,7 +71,4 @@ def decode(type_id: int, raw: np.ndarray) -> np.ndarray:
         return decode_q8_0(raw)
     if type_id == 2:
         return decode_q4_0(raw)
-    if type_id == 0:
-        raw = np.ascontiguousarray(raw, dtype=np.uint8)
-        return raw.view(np.float32).astype(np.float64).reshape(*raw.shape[:-1], raw.shape[-1] // 4)
     raise ValueError(f"unsupported type {type_id}")

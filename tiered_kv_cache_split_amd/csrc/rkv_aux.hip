@@ -34,7 +34,8 @@ __global__ void __launch_bounds__(128) dequant_kernel(const uint8_t *__restrict_
 
 }  // namespace
 
-// Extent of a padded row list (patch 0102's kv_rows with -1 padding), in kRowExtentParts pieces
+// Extent of a padded row list (llama.cpp PR #29510 flash_attn_ext_rows, ggml.h API comment:
+// kv_rows with -1 padding), in kRowExtentParts pieces
 // per sequence: workgroup (b, part) writes 1 + the last index of its slice holding a pool row
 // (0 if none); the extent of sequence b is the maximum over its parts.  Every load of a thread
 // is issued before any is used, so the scan costs about one memory latency.

@@ -3,9 +3,10 @@
 //
 // Same partial as the other decode kernels (opencoti-llamafile patch 0070-rolling-kv, fattn.cu
 // streaming_lse_kernel and the tail-partial op: M = max s_j, S = sum exp(s_j - M),
-// VKQ = sum exp(s_j - M) v_j), and for the row-list form the semantics of patch 0102's
-// attention over kv_rows (a negative entry is padding and contributes nothing).  With binary16
-// data both contractions go straight to the matrix cores, without any conversion:
+// VKQ = sum exp(s_j - M) v_j), and for the row-list form the semantics of llama.cpp PR
+// #29510's flash_attn_ext_rows (ggml.h API comment) over kv_rows (a negative entry is padding
+// and contributes nothing).  With binary16 data both contractions go straight to the matrix
+// cores, without any conversion:
 //
 //   Q.K  D[key][row] = K (A: 16 keys x 32 head_dim, one 16-byte LDS read per lane) times Q^T
 //        (B, rows >= R zero): v_mfma_f32_16x16x32_f16.  A lane then holds one query row for

@@ -696,9 +696,14 @@ int attn_window_tail(rkv_ctx *ctx, const rkv_tensor *q, const rkv_tensor *k_win,
         ctx->host_up_pending = true;
         slot += 1;
     }
+    // Tile t+1 goes into slot (t+1) % n_slots once the tile that last used that slot,
+    // t+1-n_slots, is computed.  With two or more slots that tile is at most t-1, so the lift
+    // is enqueued ahead of tile t's kernel and overlaps it; with a single slot it is tile t
+    // itself, so the lift follows tile t's kernel (no prefetch).
     for (int64_t t = 0; t < n_tiles; ++t) {
         const int sl = (int)(t % n_slots);
-        if (t + 1 < n_tiles) {
+        const bool next = t + 1 < n_tiles;
+        if (next && n_slots > 1) {
             const int ns = (int)((t + 1) % n_slots);
             if (t + 1 >= n_slots) RKV_HIP(hipStreamWaitEvent(ctx->copy_stream, ctx->compute_done[ns], 0));
             if ((st = lift(t + 1))) return st;
@@ -706,6 +711,10 @@ int attn_window_tail(rkv_ctx *ctx, const rkv_tensor *q, const rkv_tensor *k_win,
         RKV_HIP(hipStreamWaitEvent(stream, ctx->copy_done[sl], 0));
         if ((st = run_segment(ctx, base, tile_seg(t), mfma, k_type, v_type, slot, stream))) return st;
         RKV_HIP(hipEventRecord(ctx->compute_done[sl], stream));
+        if (next && n_slots == 1) {
+            RKV_HIP(hipStreamWaitEvent(ctx->copy_stream, ctx->compute_done[0], 0));
+            if ((st = lift(t + 1))) return st;
+        }
     }
     if (d != kHeadDim) {
         // other head dims: the merge of partials with row stride 2 + d (no partial at all, as for
