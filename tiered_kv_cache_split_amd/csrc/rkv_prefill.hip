@@ -1,214 +1,73 @@
 // MFMA segment kernel for prefill on gfx950: many query rows per KV head, so Q.K^T and P.V
 // are dense contractions and run on the matrix cores (v_mfma_f32_32x32x16_f16).
 //
-// What a segment computes is the same partial as the vector kernel (opencoti-llamafile patch
+// What a segment computes is the same partial as the decode kernels (opencoti-llamafile patch
 // 0070-rolling-kv, tail-partial op and fattn.cu streaming_lse_kernel): per output row, over
 // the keys of the segment, M = max s_j, S = sum exp(s_j - M), VKQ = sum exp(s_j - M) v_j,
 // s_j = scale*<q, k_j> + mask_j, keys at positions after the query's own (causal) or with a
 // -inf mask contributing nothing.
 //
 // Workgroup = 8 waves = 256 query rows of one KV head (row rho = i*gqa + r: query i, head
-// g*gqa + r) over one split of the segment's keys, 64 keys per iteration:
-//   1. the tile's raw K/V bytes (binary16 or q8_0/q4_0 blocks) are fetched three tiles ahead
-//      into registers and staged in LDS (two staging and two operand buffers, one barrier
-//      per tile);
-//   2. they are decoded once per workgroup, a tile ahead of use, into binary16 MFMA
-//      operands in LDS: K as rows [key][d]; q8_0 K exactly, as a rounded binary16 part plus the binary16 residual
-//      (d*q has up to 18 significant bits; the two parts carry all of them), so that a large
-//      key is not perturbed by rounding; V transposed to [d][key] (q4_0 values d*(n-8)
-//      rounded once to binary16, the same rounding P gets);
-//   3. each wave forms S^T = K.Q^T for its 32 rows with Q^T held in registers, then an
-//      online softmax in the exp2 domain per query column (the running max is raised only
-//      when it grows by more than 8, so weights stay <= 256 and most tiles skip rescaling);
-//   4. O^T += V^T.P^T with P as binary16 straight from the S^T accumulators (the key order
-//      of the accumulator layout is matched by permuting keys when V^T is written);
-//   5. the wave writes its rows' partial (M in natural-log units).
+// g*gqa + r) over one split of the segment's keys, 64 keys per tile.  Operands are exact:
+//   K  rows [key][d] in LDS as binary16: copied, or for q8_0 the two-part sum hi + lo = d*q
+//      (both binary16, exact), so S^T = K.Q^T takes two MFMAs per step for q8_0;
+//   V  rows [key][d] in LDS as binary16: copied, or for q4_0 the exact integers n - 8, with the
+//      block scales d_V kept apart and folded into the binary16 weights of P.V
+//      (W = p * d_V per key and 32-value block: each 32-row output tile of O^T is one block).
+// The waves split into two groups of four (one wave of each per SIMD).  Each group alternates
+// a matrix phase (P.V of the previous tile, then Q.K of this tile) and a vector phase (online
+// softmax of this tile, and its share of the next tile's operand decode: group 0 decodes K,
+// group 1 decodes V, each straight from raw bytes it fetched two tiles ahead into registers).
+// Group 1 runs one phase behind group 0, so on every SIMD one wave feeds the matrix core while
+// the other keeps the vector unit busy; a workgroup barrier ends every phase.
 #include "rkv_internal.h"
+#include "rkv_unpack.h"
 #include "rkv_wave.h"
 
 #include <math.h>
+
+#include <type_traits>
 
 namespace rkv {
 
 namespace {
 
-typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef float f16x_t __attribute__((ext_vector_type(16)));
 
 constexpr int kWavesP = 8;
 constexpr int kThreadsP = 64 * kWavesP;
-constexpr int kBM = 32 * kWavesP;  // query rows per workgroup
-constexpr int kBN = 64;            // keys per iteration
-constexpr int kKStride = 272;      // LDS bytes per K row: 128 binary16 + 16 B (conflict-free 128-bit reads)
-constexpr int kVtStride = 144;     // LDS bytes per V^T row: 64 binary16 keys + 16 B
+constexpr int kGroupT = kThreadsP / 2;  // threads per wave group
+constexpr int kBM = 32 * kWavesP;       // query rows per workgroup
+constexpr int kBN = 64;                 // keys per tile
+constexpr int kKP = 272;                // LDS bytes per K row: 128 binary16 + 16 (conflict-free 16-byte reads)
+constexpr int kVP = 320;                // LDS bytes per V row: 128 binary16 + 64 (conflict-free transposing reads)
+constexpr int kPD = 4;                  // P.V steps whose operand reads run ahead of the current one
+constexpr int kKD = 4;                  // Q.K steps likewise
 constexpr float kLog2eP = 1.4426950408889634f;
 constexpr float kLn2P = 0.6931471805599453f;
-constexpr float kLazy = 8.0f;      // raise the running max only past this growth (log2 units)
 
-// Bytes of one 128-value row.
 template <int T> constexpr int row_bytes_of() { return T == T_F16 ? 256 : (T == T_Q8_0 ? 136 : 72); }
-// A tile of 64 rows is fetched as 8-byte units, unit u = row * (row_bytes/8) + column.
-template <int T> struct Tile {
-    static constexpr int kRow = row_bytes_of<T>();
-    static constexpr int kUnits = kRow / 8;
-    static constexpr int kTotal = kBN * kUnits;
-    static constexpr int kPer = (kTotal + kThreadsP - 1) / kThreadsP;
-};
+// 32-bit words a thread fetches for its quarter row (one block of 32 values, or 64 bytes of
+// binary16): a q8_0 block is 34 bytes from an even offset (9 words cover it), a q4_0 block 18
+// bytes (5 words)
+template <int T> constexpr int raw_words() { return T == T_F16 ? 16 : (T == T_Q8_0 ? 9 : 5); }
 
-// LDS layout (bytes): two operand sets (binary16 K rows, for q8_0 K also the residual rows,
-// and V^T) and two raw staging buffers, so one barrier per tile separates every producer from
-// its consumers.
+// LDS layout (bytes): two K buffers (binary16 hi rows, for q8_0 also the lo rows), then two V
+// buffers (binary16 rows, for q4_0 followed by d_V as [block][key slot]).
 template <int KT, int VT> struct Lds {
-    static constexpr int kKlo = kBN * kKStride;                                // q8_0 K only
-    static constexpr int kVt = kKlo + (KT == T_Q8_0 ? kBN * kKStride : 0);
-    static constexpr int kOp = kVt + kHeadDim * kVtStride;                     // one operand set
-    static constexpr int kSv = Tile<KT>::kTotal * 8;                            // raw V after raw K
-    static constexpr int kSt = kSv + Tile<VT>::kTotal * 8 + 16;                 // +16: block-window slack
-    static constexpr int kSize = 2 * kOp + 2 * kSt;
+    static constexpr int kKhalf = kBN * kKP;
+    static constexpr int kKbuf = kKhalf * (KT == T_Q8_0 ? 2 : 1);
+    static constexpr int kVdat = kBN * kVP;
+    static constexpr int kVbuf = kVdat + (VT == T_Q4_0 ? 4 * kBN * 2 : 0);
+    static constexpr int kV0 = 2 * kKbuf;
+    static constexpr int kSize = 2 * kKbuf + 2 * kVbuf;
 };
 
-__device__ __forceinline__ half2_t as_h2(uint32_t x) { return __builtin_bit_cast(half2_t, x); }
-__device__ __forceinline__ uint32_t as_u(half2_t x) { return __builtin_bit_cast(uint32_t, x); }
-
-// Word-aligned view of LDS bytes starting at an even offset o: out[j] = bytes o+4j .. o+4j+3.
-template <int NW>
-__device__ __forceinline__ void block_words(const uint8_t *lds, int o, uint32_t (&out)[NW]) {
-    const uint32_t *w = reinterpret_cast<const uint32_t *>(lds + (o & ~3));
-    const uint32_t sh = (uint32_t)(o & 3);  // 0 or 2
-    uint32_t x[NW + 1];
-#pragma unroll
-    for (int j = 0; j <= NW; ++j) x[j] = w[j];
-#pragma unroll
-    for (int j = 0; j < NW; ++j) out[j] = __builtin_amdgcn_alignbyte(x[j + 1], x[j], sh);
-}
-
-// Position of key k (0..63) in a V^T row: within each group of 16, bits 2 and 3 of the index
-// are swapped, which is the key order of the binary16 P fragments built from S^T.
-__device__ __forceinline__ int vt_pos(int k) { return (k & ~15) | (k & 3) | ((k & 4) << 1) | ((k & 8) >> 1); }
-
-// Fetch the 64-row tile's raw bytes into registers.  `rs` covers exactly the tile's valid rows,
-// so units of rows past the end read as zero.
-template <int T>
-__device__ __forceinline__ void fetch_tile(uint2 (&buf)[Tile<T>::kPer], __amdgpu_buffer_rsrc_t rs,
-                                           const int (&off)[Tile<T>::kPer], int tid) {
-#pragma unroll
-    for (int i = 0; i < Tile<T>::kPer; ++i) {
-        if (Tile<T>::kTotal % kThreadsP == 0 || tid + kThreadsP * i < Tile<T>::kTotal)
-            buf[i] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs, off[i], 0, 0));
-    }
-}
-template <int T>
-__device__ __forceinline__ void stash_tile(const uint2 (&buf)[Tile<T>::kPer], uint8_t *stage, int tid) {
-#pragma unroll
-    for (int i = 0; i < Tile<T>::kPer; ++i) {
-        const int u = tid + kThreadsP * i;
-        if (Tile<T>::kTotal % kThreadsP == 0 || u < Tile<T>::kTotal) *reinterpret_cast<uint2 *>(stage + 8 * u) = buf[i];
-    }
-}
-template <int T>
-__device__ __forceinline__ void tile_offsets(int (&off)[Tile<T>::kPer], int s1, int tid) {
-#pragma unroll
-    for (int i = 0; i < Tile<T>::kPer; ++i) {
-        const int u = tid + kThreadsP * i;
-        off[i] = (u / Tile<T>::kUnits) * s1 + (u % Tile<T>::kUnits) * 8;
-    }
-}
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint8_t *base, int64_t s1, int64_t nv, int rb) {
-    return __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, (int)((nv - 1) * s1 + rb), 0x00020000);
-}
-
-// ---- decode of a staged raw tile into binary16 MFMA operands (once per workgroup)
-
-// K rows: binary16 copy, or q8_0 as hi = rn(d*q) and lo = rn(d*q - hi) (exact).  A thread
-// takes 16 values of one key.
-template <int KT>
-__device__ __forceinline__ void decode_k(const uint8_t *sk, uint8_t *khi, uint8_t *klo, int tid) {
-    const int key = tid & 63;
-    if constexpr (KT == T_F16) {
-        const int part = tid >> 6;  // 32-byte eighth of the row
-        const uint4 *src = reinterpret_cast<const uint4 *>(sk + key * 256 + 32 * part);
-        uint4 *dst = reinterpret_cast<uint4 *>(khi + key * kKStride + 32 * part);
-        dst[0] = src[0];
-        dst[1] = src[1];
-    } else {
-        const int blk = (tid >> 6) & 3, hf = tid >> 8;
-        const uint8_t *row = sk + key * 136;
-        const int o = 34 * blk;
-        const uint32_t dbits = *reinterpret_cast<const uint16_t *>(row + o);
-        const half2_t dd = as_h2(dbits | (dbits << 16));
-        uint32_t qw[4];
-        block_words<4>(row, o + 2 + 16 * hf, qw);
-        const half2_t bias = {(_Float16)-1152.0f, (_Float16)-1152.0f};
-        uint32_t hi[8], lo[8];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            // q + 128 as the low byte of binary16 0x64xx = 1024 + (q + 128): exact integers
-            const uint32_t x = qw[j] ^ 0x80808080u;
-            const half2_t q01 = as_h2(__builtin_amdgcn_perm(0x64646464u, x, 0x04010400u)) + bias;
-            const half2_t q23 = as_h2(__builtin_amdgcn_perm(0x64646464u, x, 0x04030402u)) + bias;
-            const half2_t h01 = q01 * dd, h23 = q23 * dd;
-            hi[2 * j] = as_u(h01);
-            hi[2 * j + 1] = as_u(h23);
-            lo[2 * j] = as_u(__builtin_elementwise_fma(q01, dd, -h01));
-            lo[2 * j + 1] = as_u(__builtin_elementwise_fma(q23, dd, -h23));
-        }
-        uint4 *dh = reinterpret_cast<uint4 *>(khi + key * kKStride + 64 * blk + 32 * hf);
-        uint4 *dl = reinterpret_cast<uint4 *>(klo + key * kKStride + 64 * blk + 32 * hf);
-        dh[0] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-        dh[1] = make_uint4(hi[4], hi[5], hi[6], hi[7]);
-        dl[0] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
-        dl[1] = make_uint4(lo[4], lo[5], lo[6], lo[7]);
-    }
-}
-
-// V^T rows [d][key position]: a thread takes two adjacent keys (one 32-bit LDS word per d)
-// and 8 values of head_dim.
-template <int VT>
-__device__ __forceinline__ void decode_v(const uint8_t *sv, uint8_t *vt, int tid) {
-    const int kp = tid & 31;
-    const int ka = 2 * kp;
-    const int col = vt_pos(ka) * 2;  // byte offset of the key pair in a V^T row
-    if constexpr (VT == T_F16) {
-        const int dq = tid >> 5;  // 8 values of head_dim
-        const uint4 a = *reinterpret_cast<const uint4 *>(sv + ka * 256 + 16 * dq);
-        const uint4 b = *reinterpret_cast<const uint4 *>(sv + (ka + 1) * 256 + 16 * dq);
-        const uint32_t aw[4] = {a.x, a.y, a.z, a.w};
-        const uint32_t bw[4] = {b.x, b.y, b.z, b.w};
-        uint8_t *dst = vt + 8 * dq * kVtStride + col;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            *reinterpret_cast<uint32_t *>(dst + (2 * j) * kVtStride) = __builtin_amdgcn_perm(bw[j], aw[j], 0x05040100u);
-            *reinterpret_cast<uint32_t *>(dst + (2 * j + 1) * kVtStride) = __builtin_amdgcn_perm(bw[j], aw[j], 0x07060302u);
-        }
-    } else {
-        const int blk = (tid >> 5) & 3, half = (tid >> 7) & 1, qq = tid >> 8;
-        const int o = 18 * blk;
-        const uint8_t *ra = sv + ka * 72, *rb = sv + (ka + 1) * 72;
-        const uint32_t da = *reinterpret_cast<const uint16_t *>(ra + o);
-        const uint32_t db = *reinterpret_cast<const uint16_t *>(rb + o);
-        const half2_t dd = as_h2(da | (db << 16));
-        uint32_t wa[2], wb[2];
-        block_words<2>(ra, o + 2 + 8 * qq, wa);
-        block_words<2>(rb, o + 2 + 8 * qq, wb);
-        const half2_t bias = {(_Float16)-1032.0f, (_Float16)-1032.0f};
-        uint8_t *dst = vt + (32 * blk + 16 * half + 8 * qq) * kVtStride + col;
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            // nibbles of elements (low nibbles: 0..15 of the block, high nibbles: 16..31)
-            const uint32_t na = (wa[j] >> (4 * half)) & 0x0F0F0F0Fu;
-            const uint32_t nb = (wb[j] >> (4 * half)) & 0x0F0F0F0Fu;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                // halves (1024 + n_a, 1024 + n_b) -> (n - 8) exact -> times (d_a, d_b), rounded once
-                const uint32_t sel = 0x0C000C00u | ((uint32_t)(4 + e) << 16) | (uint32_t)e;
-                const half2_t x = as_h2(__builtin_amdgcn_perm(nb, na, sel) | 0x64006400u) + bias;
-                *reinterpret_cast<uint32_t *>(dst + (4 * j + e) * kVtStride) = as_u(x * dd);
-            }
-        }
-    }
-}
+// Slot of key k (0..63) within its 16-key P.V step: the order in which the binary16 P fragments
+// built from the S^T accumulators hold keys (bits 2 and 3 of the in-step index swapped).
+__device__ __forceinline__ int pv_slot(int k) { return (k & ~15) | (k & 3) | ((k & 4) << 1) | ((k & 8) >> 1); }
 
 __device__ __forceinline__ float lane_pair_max(float x) {
     const int xi = __builtin_bit_cast(int, x);
@@ -221,14 +80,94 @@ __device__ __forceinline__ float lane_pair_sum(float x) {
     return __builtin_bit_cast(float, (int)r[0]) + __builtin_bit_cast(float, (int)r[1]);
 }
 
+// Buffer resource over the valid rows of a tile (rows past the segment end read as zero).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint8_t *base, int64_t s1, int64_t nv, int rb) {
+    const int range = nv > 0 ? (int)((nv - 1) * s1 + rb) : 0;
+    return __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, range, 0x00020000);
+}
+
+// Fetch the thread's quarter row of tile key `key`, part `qq` (0..3): the block's bytes from
+// its word-aligned start (q8_0 / q4_0 blocks start 0 or 2 bytes into a word).
+template <int T>
+__device__ __forceinline__ void fetch_part(uint32_t (&w)[16], __amdgpu_buffer_rsrc_t rs, int off) {
+    if constexpr (T == T_F16) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const uint4 x = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16 * m, 0, 0));
+            w[4 * m] = x.x, w[4 * m + 1] = x.y, w[4 * m + 2] = x.z, w[4 * m + 3] = x.w;
+        }
+    } else if constexpr (T == T_Q8_0) {
+        const uint4 a = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+        const uint4 b = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16, 0, 0));
+        w[0] = a.x, w[1] = a.y, w[2] = a.z, w[3] = a.w, w[4] = b.x, w[5] = b.y, w[6] = b.z, w[7] = b.w;
+        w[8] = __builtin_amdgcn_raw_buffer_load_b32(rs, off + 32, 0, 0);
+    } else {
+        const uint4 a = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+        w[0] = a.x, w[1] = a.y, w[2] = a.z, w[3] = a.w;
+        w[4] = __builtin_amdgcn_raw_buffer_load_b32(rs, off + 16, 0, 0);
+    }
+}
+
+// K quarter row -> LDS: binary16 copy, or a q8_0 block as exact hi / lo binary16 rows.
+// `odd`: the block starts 2 bytes into its first word (its scale is that word's high half).
+template <int KT>
+__device__ __forceinline__ void decode_k_part(const uint32_t (&w)[16], bool odd, uint8_t *khi, uint8_t *klo) {
+    uint4 *dh = reinterpret_cast<uint4 *>(khi);
+    if constexpr (KT == T_F16) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) dh[m] = make_uint4(w[4 * m], w[4 * m + 1], w[4 * m + 2], w[4 * m + 3]);
+    } else {
+        const uint32_t dbits = odd ? (w[0] >> 16) : (w[0] & 0xFFFFu);
+        const uhalf2_t dd = u2h(dbits | (dbits << 16));
+        const uint32_t sel = odd ? 0x07060504u : 0x05040302u;  // codes start at byte 4 or 2
+        uint32_t hi[16], lo[16];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint2 b = q8_biased(__builtin_amdgcn_perm(w[i + 1], w[i], sel));
+            q8_hi_lo(q8_unbias(b.x), dd, hi[2 * i], lo[2 * i]);
+            q8_hi_lo(q8_unbias(b.y), dd, hi[2 * i + 1], lo[2 * i + 1]);
+        }
+        uint4 *dl = reinterpret_cast<uint4 *>(klo);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            dh[m] = make_uint4(hi[4 * m], hi[4 * m + 1], hi[4 * m + 2], hi[4 * m + 3]);
+            dl[m] = make_uint4(lo[4 * m], lo[4 * m + 1], lo[4 * m + 2], lo[4 * m + 3]);
+        }
+    }
+}
+
+// V quarter row -> LDS: binary16 copy, or a q4_0 block as the exact integers n - 8 (binary16)
+// plus its scale at the key's P.V slot of the block's d_V row.
+template <int VT>
+__device__ __forceinline__ void decode_v_part(const uint32_t (&w)[16], bool odd, uint8_t *vrow, uint16_t *dv_slot) {
+    uint4 *dst = reinterpret_cast<uint4 *>(vrow);
+    if constexpr (VT == T_F16) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) dst[m] = make_uint4(w[4 * m], w[4 * m + 1], w[4 * m + 2], w[4 * m + 3]);
+    } else {
+        const uint32_t dbits = odd ? (w[0] >> 16) : (w[0] & 0xFFFFu);
+        const uint32_t sel = odd ? 0x07060504u : 0x05040302u;  // data starts at byte 4 or 2
+        const uint32_t dw[4] = {__builtin_amdgcn_perm(w[1], w[0], sel), __builtin_amdgcn_perm(w[2], w[1], sel),
+                                __builtin_amdgcn_perm(w[3], w[2], sel), __builtin_amdgcn_perm(w[4], w[3], sel)};
+        uint32_t out[16];
+        q4_block_centered(dw, out);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) dst[m] = make_uint4(out[4 * m], out[4 * m + 1], out[4 * m + 2], out[4 * m + 3]);
+        *dv_slot = (uint16_t)dbits;
+    }
+}
+
 // CAP: the logit soft-cap is on (a separate instantiation, so the plain path carries none of it)
 template <int KT, int VT, bool CAP>
-__global__ void __launch_bounds__(kThreadsP) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ void __launch_bounds__(kThreadsP) __attribute__((amdgpu_waves_per_eu(2, 2)))
 prefill_seg_kernel(const SegParams p, int q_tiles, int n_tasks) {
     using L = Lds<KT, VT>;
+    constexpr int RW = raw_words<KT>() > raw_words<VT>() ? raw_words<KT>() : raw_words<VT>();
+    static_assert(RW <= 16, "raw words");
     __shared__ __attribute__((aligned(16))) uint8_t smem[L::kSize];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool grp0 = wave < 4;  // group 0 decodes K and leads; group 1 decodes V and lags one phase
 
     // Workgroups are dealt round-robin to the 8 XCDs; give each XCD a contiguous run of tasks,
     // q tile fastest, so the workgroups sharing one K/V range share an L2.
@@ -279,93 +218,103 @@ prefill_seg_kernel(const SegParams p, int q_tiles, int n_tasks) {
     // Q is complete before any tile load is issued, so no wait inside the loop covers it
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 
+    // ---- raw fetch of this thread's quarter row (group 0: K, group 1: V): key gt / 4, part gt % 4
+    const int gt = tid & (kGroupT - 1);
+    const int fkey = gt >> 2, fq = gt & 3;
+    const bool fodd = (fq & 1) != 0;  // q8_0 / q4_0 blocks 1 and 3 start 2 bytes into a word
     const uint8_t *kbase = p.k + (int64_t)g * p.k_s2;
     const uint8_t *vbase = p.v + (int64_t)g * p.v_s2;
-    int koff[Tile<KT>::kPer], voff[Tile<VT>::kPer];
-    tile_offsets<KT>(koff, (int)p.k_s1, tid);
-    tile_offsets<VT>(voff, (int)p.v_s1, tid);
-    uint2 kraw[Tile<KT>::kPer], vraw[Tile<VT>::kPer];
-    auto fetch = [&](int it) {
-        const int64_t c0 = c_begin + (int64_t)kBN * it;
-        const int64_t rem = p.n_cells - c0;
-        const int64_t nv = rem < kBN ? rem : (int64_t)kBN;
-        fetch_tile<KT>(kraw, tile_rsrc(kbase + c0 * p.k_s1, p.k_s1, nv, row_bytes_of<KT>()), koff, tid);
-        fetch_tile<VT>(vraw, tile_rsrc(vbase + c0 * p.v_s1, p.v_s1, nv, row_bytes_of<VT>()), voff, tid);
-    };
-    auto stash = [&](int s) {
-        uint8_t *st = smem + 2 * L::kOp + s * L::kSt;
-        stash_tile<KT>(kraw, st, tid);
-        stash_tile<VT>(vraw, st + L::kSv, tid);
-    };
-    auto decode = [&](int s) {
-        const uint8_t *st = smem + 2 * L::kOp + s * L::kSt;
-        uint8_t *op = smem + s * L::kOp;
-        decode_k<KT>(st, op, op + L::kKlo, tid);
-        decode_v<VT>(st + L::kSv, op + L::kVt, tid);
-    };
+    const int koff = fkey * (int)p.k_s1 + (((KT == T_F16 ? 64 : 34) * fq) & ~3);
+    const int voff = fkey * (int)p.v_s1 + (((VT == T_F16 ? 64 : 18) * fq) & ~3);
 
     const float c = p.scale_log2;
     float m_used = -INFINITY, l_sum = 0.f;
     f16x_t oacc[4];
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) oacc[dt] = f16x_t{};
-
-    // pipeline: tile it+3 in flight to registers, it+2 staged raw, it+1 being decoded while it
-    // is computed; one barrier per tile
-    if (n_it > 0) {
-        fetch(0);
-        stash(0);
-    }
-    if (n_it > 1) fetch(1);
-    __syncthreads();
-    if (n_it > 0) decode(0);
-    if (n_it > 1) stash(1);
-    if (n_it > 2) fetch(2);
-
-    for (int it = 0; it < n_it; ++it) {
-        const int cur = it & 1;
-        __syncthreads();
-        if (it + 1 < n_it) decode(cur ^ 1);
-        if (it + 2 < n_it) stash(cur);
-        if (it + 3 < n_it) fetch(it + 3);
-
-        const int64_t c0 = c_begin + (int64_t)kBN * it;
-        const uint8_t *khi = smem + cur * L::kOp;
-        const uint8_t *klo = khi + L::kKlo;
-        const uint8_t *vt = khi + L::kVt;
-
-        // ---- S^T = K.Q^T: two 32-key tiles, lane holds key 32kt + 8(i/4) + 4hh + i%4 of row rl
-        f16x_t sacc[2] = {f16x_t{}, f16x_t{}};
+    f16x_t sacc[2];
+    half8_t pf[4];
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
+    for (int s = 0; s < 4; ++s) pf[s] = half8_t{};
+
+    // ---- matrix phase: O^T += V^T.W^T for tile it-1 (W = P, times d_V per block for q4_0),
+    // then S^T = K.Q^T for tile it.  Operand reads run two MFMAs ahead of their use.
+    const int vl = lane & 15, vg = lane >> 4;
+    // V^T fragment of step (s, dt): lane (d = 16*(vg&1) + vl of block dt) receives keys
+    // 16s + 4*hh + 0..3 (first read) and 16s + 8 + 4*hh + 0..3 (second read): the P slot order
+    const int v_lane = (4 * hh + (vl >> 2)) * kVP + (16 * (vg & 1) + 4 * (vl & 3)) * 2;
+    const int k_lane = rl * kKP + 16 * hh;
+    auto matrix_phase = [&](int it) __attribute__((always_inline)) {
+        if (it > 0) {
+            const uint8_t *vb = smem + L::kV0 + ((it - 1) & 1) * L::kVbuf;
+            const uint8_t *va0 = vb + v_lane;
+            const uint8_t *dv0 = vb + L::kVdat + 16 * hh;
+            half8_t av[kPD + 1], dv[kPD + 1];
+            auto ld = [&](int n) __attribute__((always_inline)) {
+                const int s = n >> 2, dt = n & 3;
+                const uint8_t *va = va0 + 16 * s * kVP + 64 * dt;
+                const short4_t t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4_t *)va);
+                const short4_t t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) short4_t *)(va + 8 * kVP));
+                av[n % (kPD + 1)] = __builtin_bit_cast(half8_t, __builtin_shufflevector(t0, t1, 0, 1, 2, 3, 4, 5, 6, 7));
+                if constexpr (VT == T_Q4_0) dv[n % (kPD + 1)] = *reinterpret_cast<const half8_t *>(dv0 + 2 * (dt * kBN + 16 * s));
+            };
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt) {
-                const int off = (32 * kt + rl) * kKStride + (16 * ks + 8 * hh) * 2;
-                const half8_t a = *reinterpret_cast<const half8_t *>(khi + off);
-                sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qf[ks], sacc[kt], 0, 0, 0);
-                if constexpr (KT == T_Q8_0) {
-                    const half8_t al = *reinterpret_cast<const half8_t *>(klo + off);
-                    sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(al, qf[ks], sacc[kt], 0, 0, 0);
-                }
+            for (int n = 0; n < kPD; ++n) ld(n);
+#pragma unroll
+            for (int n = 0; n < 16; ++n) {
+                if (n + kPD < 16) ld(n + kPD);
+                const half8_t wv = (VT == T_Q4_0) ? pf[n >> 2] * dv[n % (kPD + 1)] : pf[n >> 2];
+                oacc[n & 3] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[n % (kPD + 1)], wv, oacc[n & 3], 0, 0, 0);
+            }
+            constexpr int kRd = VT == T_Q4_0 ? 3 : 2;  // LDS reads per step
+            __builtin_amdgcn_sched_group_barrier(0x100, kPD * kRd, 0);
+#pragma unroll
+            for (int n = 0; n < 16; ++n) {
+                if (n + kPD < 16) __builtin_amdgcn_sched_group_barrier(0x100, kRd, 0);
+                if constexpr (VT == T_Q4_0) __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             }
         }
-        // schedule: three operand reads in flight ahead of the MFMA that consumes them (the
-        // default schedule issues each read one MFMA ahead and waits on it)
-        constexpr int kNM = KT == T_Q8_0 ? 32 : 16, LA = 3;
-        __builtin_amdgcn_sched_group_barrier(0x100, LA, 0);
+        if (it < n_it) {
+            const uint8_t *ka0 = smem + (it & 1) * L::kKbuf + k_lane;
+            constexpr int kParts = KT == T_Q8_0 ? 2 : 1;
+            half8_t ak[kKD + 1][kParts];
+            auto ld = [&](int n) __attribute__((always_inline)) {
+                const int ks = n >> 1, kt = n & 1;
+                const uint8_t *a = ka0 + 32 * kt * kKP + 32 * ks;
+                ak[n % (kKD + 1)][0] = *reinterpret_cast<const half8_t *>(a);
+                if constexpr (KT == T_Q8_0) ak[n % (kKD + 1)][1] = *reinterpret_cast<const half8_t *>(a + L::kKhalf);
+            };
+            sacc[0] = f16x_t{};
+            sacc[1] = f16x_t{};
 #pragma unroll
-        for (int i = 0; i < kNM - LA; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            for (int n = 0; n < kKD; ++n) ld(n);
+#pragma unroll
+            for (int n = 0; n < 16; ++n) {
+                if (n + kKD < 16) ld(n + kKD);
+                const int ks = n >> 1, kt = n & 1;
+                sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ak[n % (kKD + 1)][0], qf[ks], sacc[kt], 0, 0, 0);
+                if constexpr (KT == T_Q8_0)
+                    sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ak[n % (kKD + 1)][1], qf[ks], sacc[kt], 0, 0, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x100, kKD * kParts, 0);
+#pragma unroll
+            for (int n = 0; n < 16; ++n) {
+                if (n + kKD < 16) __builtin_amdgcn_sched_group_barrier(0x100, kParts, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, kParts, 0);
+            }
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, LA, 0);
+    };
 
-        // ---- visibility: whole tile visible to every row of the wave, or per element
+    // ---- vector phase: online softmax of tile it (exp2 domain, exact running max) into pf
+    auto softmax = [&](int it) __attribute__((always_inline)) {
+        const int64_t c0 = c_begin + (int64_t)kBN * it;
+        // visibility: whole tile visible to every row of the wave, or per element
         const bool full = (c0 + kBN <= p.n_cells) && !p.mask &&
                           (p.q_pos0 < 0 || p.pos0 + c0 + kBN - 1 <= p.q_pos0 + wave_i_first);
         float cc = c;
         if (CAP && full) {
-            // every key visible to every row of the wave: only the soft-cap
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -376,21 +325,35 @@ prefill_seg_kernel(const SegParams p, int q_tiles, int n_tasks) {
             int64_t lim = p.q_pos0 >= 0 ? p.q_pos0 + qi - p.pos0 - c0 : (int64_t)kBN;
             if (lim > nvalid - 1) lim = nvalid - 1;
             const int lim32 = (int)(lim < -1 ? -1 : (lim > kBN ? kBN : lim));
-            const _Float16 *mrow = p.mask ? p.mask + p.pos0 + c0 + (int64_t)qi * p.m_s1 + (int64_t)b * p.m_s3 : nullptr;
+            // mask values of the lane's 32 keys, all loaded before any is used (indices clamped
+            // to the tile's last valid key, so every load is in bounds)
+            float mv[2][16];
+            if (p.mask) {
+                const _Float16 *mrow = p.mask + p.pos0 + c0 + (int64_t)qi * p.m_s1 + (int64_t)b * p.m_s3;
+                const int klast = (int)(nvalid < kBN ? nvalid - 1 : kBN - 1);
+#pragma unroll
+                for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i)
+                        mv[kt][i] = (float)mrow[min(32 * kt + 8 * (i >> 2) + 4 * hh + (i & 3), klast)];
+            } else {
+#pragma unroll
+                for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) mv[kt][i] = 0.f;
+            }
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const int kk = 32 * kt + 8 * (i >> 2) + 4 * hh + (i & 3);
                     float x = CAP ? softcap_log2(sacc[kt][i], p.cap_cs, p.cap_l2) : sacc[kt][i] * c;
-                    if (mrow && kk <= lim32) x = fmaf((float)mrow[kk], kLog2eP, x);
+                    x = fmaf(mv[kt][i], kLog2eP, x);
                     sacc[kt][i] = kk <= lim32 ? x : -INFINITY;
                 }
             }
             cc = 1.0f;
         }
-
-        // ---- online softmax (exp2 domain) for the lane's row; the lane pair (l, l^32) holds it
         float mx = -INFINITY;
         if (cc >= 0.f) {
 #pragma unroll
@@ -404,7 +367,7 @@ prefill_seg_kernel(const SegParams p, int q_tiles, int n_tasks) {
                 for (int i = 0; i < 16; ++i) mx = fmaxf(mx, -sacc[kt][i]);
         }
         const float mt = lane_pair_max(mx) * (cc >= 0.f ? cc : -cc);
-        const bool need = mt > m_used + kLazy;
+        const bool need = mt > m_used;
         if (__builtin_amdgcn_ballot_w64(need)) {
             const float mnew = need ? mt : m_used;
             const float alpha = need ? __builtin_amdgcn_exp2f(m_used - mnew) : 1.0f;
@@ -416,8 +379,7 @@ prefill_seg_kernel(const SegParams p, int q_tiles, int n_tasks) {
             m_used = mnew;
         }
         const float msub = m_used == -INFINITY ? 0.f : m_used;
-        half8_t pf[4];
-        const half2_t ones = {(_Float16)1.0f, (_Float16)1.0f};
+        const uhalf2_t ones = {(_Float16)1.0f, (_Float16)1.0f};
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             uint32_t w[4];
@@ -426,23 +388,86 @@ prefill_seg_kernel(const SegParams p, int q_tiles, int n_tasks) {
                 const int i = 8 * (s & 1) + 2 * j;
                 const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[s >> 1][i], cc, -msub));
                 const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[s >> 1][i + 1], cc, -msub));
-                const half2_t h = __builtin_convertvector((float __attribute__((ext_vector_type(2)))){p0, p1}, half2_t);
+                const uhalf2_t h = __builtin_convertvector((float __attribute__((ext_vector_type(2)))){p0, p1}, uhalf2_t);
                 l_sum = __builtin_amdgcn_fdot2(h, ones, l_sum, false);
-                w[j] = as_u(h);
+                w[j] = h2u(h);
             }
             pf[s] = __builtin_bit_cast(half8_t, make_uint4(w[0], w[1], w[2], w[3]));
         }
+    };
 
-        // ---- O^T += V^T.P^T
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-#pragma unroll
-            for (int dt = 0; dt < 4; ++dt) {
-                const half8_t a = *reinterpret_cast<const half8_t *>(vt + (32 * dt + rl) * kVtStride + (16 * s + 8 * hh) * 2);
-                oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pf[s], oacc[dt], 0, 0, 0);
+    // ---- the main loop, instantiated once per group so that each group's raw registers are
+    // indexed statically (group 0 fetches and decodes K, group 1 V)
+    auto body = [&](auto role) __attribute__((always_inline)) {
+        constexpr bool G0 = decltype(role)::value;
+        constexpr int RT = G0 ? KT : VT;
+        uint32_t raw0[16], raw1[16];
+        auto fetch = [&](uint32_t (&w)[16], int it) __attribute__((always_inline)) {
+            const int64_t c0 = c_begin + (int64_t)kBN * it;
+            const int64_t nv = it < n_it ? min((int64_t)kBN, p.n_cells - c0) : 0;
+            if constexpr (G0)
+                fetch_part<KT>(w, tile_rsrc(kbase + c0 * p.k_s1, p.k_s1, nv, row_bytes_of<KT>()), koff);
+            else
+                fetch_part<VT>(w, tile_rsrc(vbase + c0 * p.v_s1, p.v_s1, nv, row_bytes_of<VT>()), voff);
+        };
+        auto decode = [&](const uint32_t (&w)[16], int it) __attribute__((always_inline)) {
+            if constexpr (G0) {
+                uint8_t *kb = smem + (it & 1) * L::kKbuf;
+                decode_k_part<KT>(w, fodd, kb + fkey * kKP + 64 * fq, kb + L::kKhalf + fkey * kKP + 64 * fq);
+            } else {
+                uint8_t *vb = smem + L::kV0 + (it & 1) * L::kVbuf;
+                decode_v_part<VT>(w, fodd, vb + fkey * kVP + 64 * fq,
+                                  reinterpret_cast<uint16_t *>(vb + L::kVdat) + fq * kBN + pv_slot(fkey));
+            }
+        };
+        (void)RT;
+
+        // prologue: tiles 0 and 1 fetched, tile 0 decoded, tile 2 fetched
+        if (n_it > 0) {
+            fetch(raw0, 0);
+            fetch(raw1, 1);
+            decode(raw0, 0);
+            fetch(raw0, 2);
+        }
+        __syncthreads();
+        if constexpr (!G0) __syncthreads();  // group 1 starts one phase later
+
+        // phase pairs: matrix(it) | barrier | vector(it) (softmax, decode of tile it+1, fetch
+        // of tile it+3) | barrier.  Unrolled by two so the raw register sets alternate.
+        for (int it = 0; it <= n_it; it += 2) {
+            __builtin_amdgcn_sched_barrier(0);
+            matrix_phase(it);
+            __builtin_amdgcn_sched_barrier(0);
+            __syncthreads();
+            __builtin_amdgcn_sched_barrier(0);
+            if (it < n_it) {
+                softmax(it);
+                if (it + 1 < n_it) decode(raw1, it + 1);
+                fetch(raw1, it + 3);
+                __builtin_amdgcn_sched_barrier(0);
+                __syncthreads();
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            if (it + 1 > n_it) break;
+            matrix_phase(it + 1);
+            __builtin_amdgcn_sched_barrier(0);
+            __syncthreads();
+            __builtin_amdgcn_sched_barrier(0);
+            if (it + 1 < n_it) {
+                softmax(it + 1);
+                if (it + 2 < n_it) decode(raw0, it + 2);
+                fetch(raw0, it + 4);
+                __builtin_amdgcn_sched_barrier(0);
+                __syncthreads();
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
-    }
+        if constexpr (G0) __syncthreads();  // group 0 ends one phase earlier
+    };
+    if (grp0)
+        body(std::integral_constant<bool, true>{});
+    else
+        body(std::integral_constant<bool, false>{});
 
     // ---- partial of the lane's row: lane holds head_dim 32dt + 8(i/4) + 4hh + i%4
     const float l_tot = lane_pair_sum(l_sum);
