@@ -40,8 +40,8 @@ METRIC = "decode attn effective KV GB/s (% HBM peak) + tok/s/layer at n_kv=128K"
 
 KERNEL_SOURCES = {
     # sources whose change invalidates a committed traffic measurement of that kernel
-    "decode": ("rkv_decode.hip", "rkv_decode_mma.hip", "rkv_decode_mma16.hip", "rkv_quant.h", "rkv_wave.h", "rkv_internal.h", "rkv_runtime.cpp"),
-    "prefill": ("rkv_prefill.hip", "rkv_internal.h", "rkv_runtime.cpp"),
+    "decode": ("rkv_decode.hip", "rkv_decode_mma.hip", "rkv_decode_mma16.hip", "rkv_unpack.h", "rkv_wave.h", "rkv_internal.h", "rkv_runtime.cpp"),
+    "prefill": ("rkv_prefill.hip", "rkv_unpack.h", "rkv_internal.h", "rkv_runtime.cpp"),
 }
 
 

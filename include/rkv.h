@@ -335,12 +335,30 @@ int rkv_window_mode(int mode, int64_t wc, int64_t kv_size, int append_only, int 
 
 /* ---- testing aid ------------------------------------------------------------------ */
 
-/* Dequantise n_rows rows of 128 values (type F16, Q8_0 or Q4_0; row r at byte offset
- * r*row_stride from src, device memory) into float32 dst [n_rows][128] with the same
- * device routines the attention kernels use.  q8_0 gives d*q and q4_0 d*(n-8), both
- * exact in float32; binary16 subnormal scales are kept. */
-int rkv_dequant_rows(const void *src, int type, int64_t n_rows, int64_t row_stride,
-                     float *dst, void *stream);
+/* Kernel families whose in-register unpacking rkv_dequant_rows reproduces. */
+enum rkv_dequant_form {
+    RKV_DQ_DECODE_MMA = 0,  /* matrix-core decode: q8_0 codes as binary16 1152 + q, q4_0 low
+                               nibbles as 1024 + n and high nibbles in place as 1024 + 16 n    */
+    RKV_DQ_PREFILL = 1,     /* prefill: q8_0 d*q as an exact two-part binary16 sum, q4_0 n - 8
+                               as binary16 integers                                           */
+    RKV_DQ_VECTOR = 2,      /* vector decode: q8_0 as 1152 + q, q4_0 nibble fields paired
+                               across words as 1024 + n                                       */
+    RKV_DQ_HEAD_DIM = 3     /* head dims 64 / 256: codes and nibbles as float32 integers      */
+};
+
+/* Dequantise n_rows rows of row_values values (type F16, Q8_0 or Q4_0; row r at byte offset
+ * r*row_stride from src, device memory) into float32 dst [n_rows][row_values], rebuilding every
+ * value with the same device unpack routines (rkv_unpack.h) that the kernel family `form`
+ * executes: the codes or nibbles in that family's binary16 (or float32) integer form, the
+ * family's offset removed and the block scale applied in float32, or for RKV_DQ_PREFILL the
+ * exact two-part binary16 sum.  Every form is exact: q8_0 gives d*q and q4_0 d*(n-8) in
+ * float32, binary16 subnormal scales kept -- except that RKV_DQ_PREFILL's two parts overflow
+ * for q8_0 blocks with |d*q| > 65504 (|d| > 515).  row_values is a multiple of 32, at most
+ * 4096.  A testing aid for the exactness of the hot kernels' dequantisation.
+ * Errors: RKV_ERR_UNSUPPORTED for another type; RKV_ERR_ARG for an unknown form, a bad
+ * row_values, n_rows < 0 or a row_stride shorter than a row. */
+int rkv_dequant_rows(const void *src, int type, int form, int64_t n_rows, int64_t row_values,
+                     int64_t row_stride, float *dst, void *stream);
 
 /* Library version as "major.minor.patch". */
 const char *rkv_version(void);

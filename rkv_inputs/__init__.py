@@ -108,6 +108,42 @@ def pack(type_id: int, x: np.ndarray) -> np.ndarray:
     raise ValueError(f"unsupported type {type_id}")
 
 
+def pack_raw_edge(rng, type_id: int, lead_shape, d: int, p_zero=0.1, p_sub=0.1, p_tiny=0.1,
+                  scale_sigma=1.0 / 64) -> np.ndarray:
+    """Raw q8_0 / q4_0 rows of random bytes for edge coverage: every code byte (q8_0 -128
+    included) and every nibble (0 and 15 included) equally likely; block scales drawn as
+    binary16 bit patterns: +-0 with probability p_zero, a subnormal with p_sub, a tiny normal
+    (< 2**-10) with p_tiny, otherwise |N(0, scale_sigma)| with a random sign.  Shape
+    lead_shape + (row_bytes,)."""
+    lead = tuple(lead_shape)
+    nb = d // QK
+    blk = BLOCK_BYTES[type_id]
+    raw = rng.integers(0, 256, size=lead + (nb, blk), dtype=np.uint8)
+    normal = (rng.standard_normal(lead + (nb,)) * scale_sigma).astype(np.float16).view(np.uint16)
+    u = rng.random(lead + (nb,))
+    sign = rng.integers(0, 2, size=lead + (nb,)).astype(np.uint16) << 15
+    sub = (rng.integers(1, 1 << 10, size=lead + (nb,)).astype(np.uint16)) | sign
+    tiny = (rng.integers(1 << 10, 6 << 10, size=lead + (nb,)).astype(np.uint16)) | sign
+    bits = np.where(u < p_zero, sign, np.where(u < p_zero + p_sub, sub, np.where(u < p_zero + p_sub + p_tiny, tiny, normal)))
+    raw[..., 0] = (bits & 0xFF).astype(np.uint8)
+    raw[..., 1] = (bits >> 8).astype(np.uint8)
+    return raw.reshape(lead + (nb * blk,))
+
+
+def block_bytes(type_id: int, scale_bits: int, codes) -> np.ndarray:
+    """One q8_0 block (codes: 32 ints in [-128, 127]) or q4_0 block (codes: 32 nibbles in
+    [0, 15], element order) as bytes, with the given binary16 scale bit pattern."""
+    c = np.asarray(codes, dtype=np.int64)
+    assert c.shape == (QK,)
+    out = np.empty(BLOCK_BYTES[type_id], dtype=np.uint8)
+    out[0], out[1] = scale_bits & 0xFF, (scale_bits >> 8) & 0xFF
+    if type_id == TYPE_Q8_0:
+        out[2:] = (c & 0xFF).astype(np.uint8)
+    else:
+        out[2:] = (c[:16] | (c[16:] << 4)).astype(np.uint8)
+    return out
+
+
 # ---------------------------------------------------------------- draws
 def draw_normal(rng: np.random.Generator, shape) -> np.ndarray:
     return rng.standard_normal(size=shape, dtype=np.float32)

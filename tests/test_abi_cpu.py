@@ -72,8 +72,11 @@ def test_merge_rejects_bad_sizes_before_device_work(lib):
 
 def test_dequant_rejects_unknown_type(lib):
     from tiered_kv_cache_split_amd import _lib
-    assert lib.rkv_dequant_rows(None, 3, 4, 256, None, None) == _lib.RKV_ERR_UNSUPPORTED
-    assert lib.rkv_dequant_rows(None, 8, 4, 100, None, None) == _lib.RKV_ERR_ARG
+    assert lib.rkv_dequant_rows(None, 3, 0, 4, 128, 256, None, None) == _lib.RKV_ERR_UNSUPPORTED
+    assert lib.rkv_dequant_rows(None, 8, 0, 4, 128, 100, None, None) == _lib.RKV_ERR_ARG  # row_stride < 136
+    assert lib.rkv_dequant_rows(None, 8, 4, 4, 128, 136, None, None) == _lib.RKV_ERR_ARG  # unknown form
+    assert lib.rkv_dequant_rows(None, 8, 0, 4, 100, 136, None, None) == _lib.RKV_ERR_ARG  # row_values % 32
+    assert lib.rkv_dequant_rows(None, 8, 0, 0, 128, 136, None, None) == _lib.RKV_OK      # nothing to do
 
 
 def test_descriptor_layouts():

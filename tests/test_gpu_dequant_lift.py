@@ -13,14 +13,24 @@ pytestmark = pytest.mark.gpu
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
 
-def gpu_dequant(rows_bytes: np.ndarray, t: int) -> np.ndarray:
+FORMS = {"decode_mma": 0, "prefill": 1, "vector": 2, "head_dim": 3}
+
+
+def gpu_dequant(rows_bytes: np.ndarray, t: int, form: int = 0, row_values: int = 128) -> np.ndarray:
     import torch
     import tiered_kv_cache_split_amd as rkv
     src = dev(rows_bytes)
-    dst = torch.empty((rows_bytes.shape[0], 128), dtype=torch.float32, device="cuda")
-    rkv.dequant_rows(src, t, rows_bytes.shape[0], rows_bytes.shape[1], dst)
+    dst = torch.empty((rows_bytes.shape[0], row_values), dtype=torch.float32, device="cuda")
+    rkv.dequant_rows(src, t, rows_bytes.shape[0], rows_bytes.shape[1], dst, form=form, row_values=row_values)
     torch.cuda.synchronize()
     return dst.cpu().numpy()
+
+
+def assert_exact(got, want):
+    """Equal values (a signed zero may come back with either sign) and equal bits otherwise."""
+    assert np.array_equal(got, want), np.argwhere(got != want)[:5]
+    nz = want != 0
+    assert np.array_equal(got[nz].view(np.uint32), want[nz].view(np.uint32))
 
 
 def golden_rows(name, block):
@@ -34,26 +44,68 @@ def golden_rows(name, block):
     return np.concatenate(blocks).reshape(-1, 4 * block)
 
 
+def random_blocks(rng, t, n_rows, row_values, max_abs_scale=65504.0):
+    """Raw rows of random bytes: every code / nibble value (q8_0 -128 included) and scales drawn
+    from finite binary16 patterns -- zeros of both signs, subnormals, normals up to
+    max_abs_scale."""
+    nb = row_values // 32
+    blk = gen.BLOCK_BYTES[t]
+    raw = rng.integers(0, 256, size=(n_rows, nb, blk), dtype=np.uint8)
+    bits = rng.integers(0, 1 << 16, size=(n_rows, nb), dtype=np.uint32).astype(np.uint16)
+    kind = rng.integers(0, 8, size=(n_rows, nb))
+    bits = np.where(kind == 0, bits & 0x8000, bits)                       # +-0
+    bits = np.where(kind == 1, bits & 0x83FF, bits)                       # subnormal
+    vals = bits.view(np.float16).astype(np.float32)
+    bad = ~np.isfinite(vals) | (np.abs(vals) > max_abs_scale)
+    bits = np.where(bad, bits & 0x83FF, bits)                             # keep them finite and in range
+    raw[..., 0] = (bits & 0xFF).astype(np.uint8)
+    raw[..., 1] = (bits >> 8).astype(np.uint8)
+    return raw.reshape(n_rows, nb * blk)
+
+
+@pytest.mark.parametrize("form", list(FORMS))
 @pytest.mark.parametrize("t", [gen.TYPE_Q8_0, gen.TYPE_Q4_0, gen.TYPE_F16])
-def test_dequant_bit_exact_random(t):
+def test_dequant_bit_exact_random(t, form):
+    """Quantiser output (tiny and all-zero blocks included) through each kernel family's routine."""
     rng = np.random.default_rng(21)
     x = rng.standard_normal((4096, 128)).astype(np.float32)
     x[::7] *= 1e-6   # tiny blocks: binary16 subnormal scales
     x[1::97] = 0.0   # all-zero blocks: d = 0
     raw = gen.pack(t, x)
-    step(f"dequant type {t}")
-    got = gpu_dequant(raw, t)
+    step(f"dequant type {t} form {form}")
+    got = gpu_dequant(raw, t, FORMS[form])
     want = oracle.decode(t, raw).astype(np.float32)
-    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+    assert_exact(got, want)
 
 
+@pytest.mark.parametrize("form", list(FORMS))
+@pytest.mark.parametrize("t", [gen.TYPE_Q8_0, gen.TYPE_Q4_0])
+@pytest.mark.parametrize("row_values", [64, 128, 256])
+def test_dequant_bit_exact_raw_bytes(t, form, row_values):
+    """Random raw bytes: every code (q8_0 -128 too), nibbles 0 and 15, scales of every binary16
+    class up to 65504 (the prefill form's two-part q8_0 operands need |d*q| <= 65504, so its
+    scales stay below 511)."""
+    rng = np.random.default_rng(1000 + 10 * t + row_values)
+    lim = 511.0 if (form == "prefill" and t == gen.TYPE_Q8_0) else 65504.0
+    raw = random_blocks(rng, t, 2048, row_values, lim)
+    step(f"dequant raw bytes type {t} form {form} d={row_values}")
+    got = gpu_dequant(raw, t, FORMS[form], row_values)
+    want = oracle.decode(t, raw).astype(np.float32)
+    assert_exact(got, want)
+
+
+@pytest.mark.parametrize("form", list(FORMS))
 @pytest.mark.parametrize("name,t,blk", [("q8_0_blocks.txt", gen.TYPE_Q8_0, 34), ("q4_0_blocks.txt", gen.TYPE_Q4_0, 18)])
-def test_dequant_golden_blocks(name, t, blk):
+def test_dequant_golden_blocks(name, t, blk, form):
     raw = golden_rows(name, blk)
-    step(f"dequant golden {name}")
-    got = gpu_dequant(raw, t)
+    step(f"dequant golden {name} form {form}")
+    got = gpu_dequant(raw, t, FORMS[form])
     want = oracle.decode(t, raw).astype(np.float32)
-    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+    if form == "prefill" and t == gen.TYPE_Q8_0:
+        # the two-part binary16 operands cover |d*q| <= 65504 (the scale-65504 block is outside)
+        ok = np.abs(want) <= 65504.0
+        got, want = got[ok], want[ok]
+    assert_exact(got, want)
 
 
 @pytest.mark.parametrize("mode", [0, 1, 2])

@@ -15,7 +15,7 @@ from __future__ import annotations
 import ctypes
 
 from ._lib import (RKV_LIFT_AUTO, RKV_LIFT_BULK, RKV_LIFT_KERNEL, RKV_LIFT_UVA, RKV_RESIDENCY_AUTO, RKV_RESIDENCY_RESIDENT,  # noqa: F401
-                   RKV_RESIDENCY_WINDOW, RKV_TAIL_HOST, RKV_TAIL_LIFT, RKV_TYPE_F16, RKV_TYPE_F32, RKV_TYPE_Q4_0,
+                   RKV_RESIDENCY_WINDOW, RKV_TAIL_HOST, RKV_DQ_DECODE_MMA, RKV_DQ_PREFILL, RKV_DQ_VECTOR, RKV_DQ_HEAD_DIM, RKV_TAIL_LIFT, RKV_TYPE_F16, RKV_TYPE_F32, RKV_TYPE_Q4_0,
                    RKV_TYPE_Q8_0, RKV_ERR_ARG, RKV_ERR_UNSUPPORTED, RkvError,
                    RkvStats, RkvTensor, check, load)
 
@@ -217,10 +217,12 @@ def choose_tail_mode(tail_bytes: int, h2d_gbps: float, host_gbps: float) -> int:
     return m.value
 
 
-def dequant_rows(src, type_id: int, n_rows: int, row_stride: int, dst, stream=None):
+def dequant_rows(src, type_id: int, n_rows: int, row_stride: int, dst, stream=None, form: int = RKV_DQ_DECODE_MMA,
+                 row_values: int = 128):
+    """Rows of row_values values rebuilt through the unpack routines of kernel family `form`."""
     lib = load()
-    check(lib.rkv_dequant_rows(_ptr(src), int(type_id), int(n_rows), int(row_stride), _ptr(dst),
-                               _stream(stream)), "rkv_dequant_rows")
+    check(lib.rkv_dequant_rows(_ptr(src), int(type_id), int(form), int(n_rows), int(row_values), int(row_stride),
+                               _ptr(dst), _stream(stream)), "rkv_dequant_rows")
 
 
 def plan_window(per_cell: int, kv_size: int, free_bytes: int = -1, target_bytes: int = 0,

@@ -12,6 +12,7 @@ RKV_OK, RKV_ERR_ARG, RKV_ERR_UNSUPPORTED, RKV_ERR_HIP, RKV_ERR_NOMEM, RKV_ERR_CA
 RKV_LIFT_BULK, RKV_LIFT_UVA, RKV_LIFT_KERNEL, RKV_LIFT_AUTO = 0, 1, 2, 3
 RKV_RESIDENCY_AUTO, RKV_RESIDENCY_RESIDENT, RKV_RESIDENCY_WINDOW = 0, 1, 2
 RKV_TAIL_LIFT, RKV_TAIL_HOST = 0, 1
+RKV_DQ_DECODE_MMA, RKV_DQ_PREFILL, RKV_DQ_VECTOR, RKV_DQ_HEAD_DIM = 0, 1, 2, 3
 
 i64 = ctypes.c_int64
 vp = ctypes.c_void_p
@@ -53,7 +54,7 @@ SIGNATURES = {
     "rkv_attn_partial": (ctypes.c_int, [vp, TP, TP, TP, TP, i64, i64, ctypes.c_float, vp, vp]),
     "rkv_lse_merge": (ctypes.c_int, [vp, ctypes.c_int, i64, ctypes.c_int, vp, vp, vp]),
     "rkv_tail_lift": (ctypes.c_int, [vp, vp, i64, ctypes.c_int, ctypes.c_int, ctypes.POINTER(vp), vp]),
-    "rkv_dequant_rows": (ctypes.c_int, [vp, ctypes.c_int, i64, i64, vp, vp]),
+    "rkv_dequant_rows": (ctypes.c_int, [vp, ctypes.c_int, ctypes.c_int, i64, i64, i64, vp, vp]),
     "rkv_set_softcap": (ctypes.c_int, [vp, ctypes.c_float]),
     "rkv_set_tail_mode": (ctypes.c_int, [vp, ctypes.c_int, ctypes.c_int]),
     "rkv_choose_tail_mode": (ctypes.c_int, [i64, ctypes.c_double, ctypes.c_double, ctypes.POINTER(ctypes.c_int)]),

@@ -1,7 +1,7 @@
 // Auxiliary gfx950 kernels of librkv: the word-granularity host reader kept as a measured
 // contrast to the bulk DMA lift, and the exact row dequantiser behind rkv_dequant_rows.
 #include "rkv_internal.h"
-#include "rkv_quant.h"
+#include "rkv_unpack.h"
 
 #include <algorithm>
 
@@ -24,12 +24,63 @@ __global__ void uva_tail_kernel(const uint8_t *src, uint8_t *dst, int64_t n) {
     if (i < n) dst[i] = src[i];
 }
 
-__global__ void __launch_bounds__(128) dequant_kernel(const uint8_t *__restrict__ src, int type,
-                                                      int64_t row_stride,
-                                                      float *__restrict__ dst) {
+// One value of a q8_0 / q4_0 / binary16 row, rebuilt through the unpack routine of one kernel
+// family (enum rkv_dequant_form) so that a bitwise comparison covers the routine that family
+// runs: the codes or nibbles in the family's binary16 integer form, their offset removed in
+// float32 (exact: small integers), times the block scale in float32 (exact); for the prefill
+// form the exact two-part binary16 sum.
+__device__ __forceinline__ uint32_t word_at(const uint8_t *p) {
+    return (uint32_t)p[0] | ((uint32_t)p[1] << 8) | ((uint32_t)p[2] << 16) | ((uint32_t)p[3] << 24);
+}
+__device__ float dequant_value(const uint8_t *row, int type, int form, int e) {
+    if (type == T_F16) return f16_bits_to_f32((uint32_t)row[2 * e] | ((uint32_t)row[2 * e + 1] << 8));
+    const int i = e & 31;
+    if (type == T_Q8_0) {
+        const uint8_t *blk = row + kQ8Block * (e >> 5);
+        const uint32_t dbits = (uint32_t)blk[0] | ((uint32_t)blk[1] << 8);
+        const uint8_t *codes = blk + 2;
+        if (form == 3) return f16_bits_to_f32(dbits) * q8_code_f32(codes[i]);
+        const uint2 b = q8_biased(word_at(codes + 4 * (i >> 2)));
+        const uint32_t pair = (i & 2) ? b.y : b.x;
+        if (form == 1) {
+            uint32_t hi, lo;
+            q8_hi_lo(q8_unbias(pair), u2h(dbits | (dbits << 16)), hi, lo);
+            const int sh = 16 * (i & 1);
+            return f16_bits_to_f32(hi >> sh) + f16_bits_to_f32(lo >> sh);
+        }
+        return (f16_bits_to_f32(pair >> (16 * (i & 1))) - kQ8Bias) * f16_bits_to_f32(dbits);
+    }
+    // q4_0
+    const uint8_t *blk = row + kQ4Block * (e >> 5);
+    const uint32_t dbits = (uint32_t)blk[0] | ((uint32_t)blk[1] << 8);
+    const uint8_t *data = blk + 2;
+    const float d = f16_bits_to_f32(dbits);
+    const int j = i & 15;  // data byte of element i
+    if (form == 3) return d * q4_centered_f32(data, i);
+    if (form == 1) {
+        const uint32_t w[4] = {word_at(data), word_at(data + 4), word_at(data + 8), word_at(data + 12)};
+        uint32_t out[16];
+        q4_block_centered(w, out);
+        return f16_bits_to_f32(out[i >> 1] >> (16 * (i & 1))) * d;
+    }
+    const uint32_t word = word_at(data + 4 * (j >> 2));
+    if (form == 2) {
+        // the vector kernels isolate the nibble fields of a word, then pair byte t of two words
+        const uint32_t nib = i < 16 ? (word & 0x0F0F0F0Fu) : ((word >> 4) & 0x0F0F0F0Fu);
+        return (f16_bits_to_f32(q4_pair_biased(nib, 0u, j & 3)) - kQ4BiasLo) * d;
+    }
+    uint32_t lo, hi;
+    q4_nibbles_biased(word, (j & 2) ? 0x0C030C02u : 0x0C010C00u, 0x64006400u, lo, hi);
+    const int sh = 16 * (j & 1);
+    if (i < 16) return (f16_bits_to_f32(lo >> sh) - kQ4BiasLo) * d;
+    return (f16_bits_to_f32(hi >> sh) - kQ4BiasHi) * 0.0625f * d;
+}
+
+__global__ void __launch_bounds__(256) dequant_kernel(const uint8_t *__restrict__ src, int type, int form, int n_values,
+                                                      int64_t row_stride, float *__restrict__ dst) {
     const int64_t row = blockIdx.x;
-    const int e = threadIdx.x;
-    dst[row * kHeadDim + e] = row_value(src + row * row_stride, type, e);
+    for (int e = threadIdx.x; e < n_values; e += blockDim.x)
+        dst[row * n_values + e] = dequant_value(src + row * row_stride, type, form, e);
 }
 
 }  // namespace
@@ -138,11 +189,11 @@ hipError_t launch_lift_copy(const void *host_src, void *dst, int64_t nbytes, hip
     return hipGetLastError();
 }
 
-hipError_t launch_dequant_rows(const void *src, int type, int64_t n_rows, int64_t row_stride,
+hipError_t launch_dequant_rows(const void *src, int type, int form, int64_t n_rows, int n_values, int64_t row_stride,
                                float *dst, hipStream_t s) {
     if (n_rows <= 0) return hipSuccess;
-    hipLaunchKernelGGL(dequant_kernel, dim3((unsigned)n_rows), dim3(kHeadDim), 0, s,
-                       static_cast<const uint8_t *>(src), type, row_stride, dst);
+    hipLaunchKernelGGL(dequant_kernel, dim3((unsigned)n_rows), dim3(256), 0, s, static_cast<const uint8_t *>(src), type,
+                       form, n_values, row_stride, dst);
     return hipGetLastError();
 }
 

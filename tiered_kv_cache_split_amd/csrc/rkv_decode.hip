@@ -21,7 +21,7 @@
 // range and reads every chunk as one contiguous span (the cache layout of the pages).
 #include "rkv.h"
 #include "rkv_internal.h"
-#include "rkv_quant.h"
+#include "rkv_unpack.h"
 #include "rkv_wave.h"
 
 #include <math.h>
@@ -130,8 +130,8 @@ __device__ __forceinline__ int wslot(int c) {
     return 8 * (c >> 3) + 2 * (c & 3) + ((c >> 2) & 1);
 }
 
-constexpr float kQ8Bias = 1152.0f;  // q8_0 codes enter v_dot2 as 1024 + (q + 128)
-constexpr float kQ4Bias = 1032.0f;  // q4_0 nibbles enter v_dot2 as 1024 + n, value n - 8
+// q8_0 codes enter v_dot2 as 1152 + q (kQ8Bias); q4_0 nibbles as 1024 + n = kQ4BiasLo + (n - 8)
+constexpr float kQ4Bias = kQ4BiasLo;
 
 template <int VT> constexpr int n_wblocks() { return VT == T_Q4_0 ? 4 : 1; }
 
@@ -203,9 +203,9 @@ __device__ __forceinline__ void process_chunk(const uint8_t *krow, const uint8_t
                     const int off = base + 2 + 4 * t;  // codes of block blk, bytes off .. off+3
                     const uint32_t x = (off & 3) ? __builtin_amdgcn_alignbyte(w[(off >> 2) + 1], w[off >> 2], off & 3)
                                                  : w[off >> 2];
-                    const uint32_t u = x ^ 0x80808080u;  // q + 128 per byte
-                    a[8 * bb + t] = as_h2(__builtin_amdgcn_perm(0x64646464u, u, 0x05010400u));  // 1024+u0, 1024+u1
-                    c[8 * bb + t] = as_h2(__builtin_amdgcn_perm(0x64646464u, u, 0x05030402u));  // 1024+u2, 1024+u3
+                    const uint2 bq = q8_biased(x);  // 1152 + q per code, exact
+                    a[8 * bb + t] = as_h2(bq.x);
+                    c[8 * bb + t] = as_h2(bq.y);
                 }
             }
 #pragma unroll
@@ -309,9 +309,8 @@ __device__ __forceinline__ void process_chunk(const uint8_t *krow, const uint8_t
             half2_t pl[4], ph[4];
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
-                const uint32_t sel = 0x0C000C00u | ((uint32_t)(4 + t) << 16) | (uint32_t)t;
-                pl[t] = as_h2(__builtin_amdgcn_perm(lo1, lo0, sel) | 0x64006400u);  // 1024+n(c0), 1024+n(c1)
-                ph[t] = as_h2(__builtin_amdgcn_perm(hi1, hi0, sel) | 0x64006400u);
+                pl[t] = as_h2(q4_pair_biased(lo0, lo1, t));  // 1024+n(c0), 1024+n(c1)
+                ph[t] = as_h2(q4_pair_biased(hi0, hi1, t));
             }
 #pragma unroll
             for (int rho = 0; rho < R; ++rho) {

@@ -17,6 +17,7 @@
 //        j % KS = t / D (KS = 256 / D key subsets, so each V value is dequantised once); the
 //        subsets' sums are added through LDS at the end.
 #include "rkv_internal.h"
+#include "rkv_unpack.h"
 #include "rkv_wave.h"
 
 #include <math.h>
@@ -30,7 +31,7 @@ constexpr int kThreads = 256;
 
 template <int T, int D> constexpr int hd_row_bytes() { return T == T_F16 ? 2 * D : (T == T_Q8_0 ? D / 32 * 34 : D / 32 * 18); }
 
-__device__ __forceinline__ float h2f_bits(uint32_t x) { return (float)__builtin_bit_cast(_Float16, (uint16_t)x); }
+__device__ __forceinline__ float h2f_bits(uint32_t x) { return f16_bits_to_f32(x); }
 
 // Sum over each aligned group of P lanes (4 or 16), in every lane of the group: DPP quad swaps,
 // then rotations by 4 and 8 inside a 16-lane row.
@@ -91,10 +92,7 @@ __device__ __forceinline__ float v_value(const uint8_t *row, int e) {
         return h2f_bits(*reinterpret_cast<const uint16_t *>(row + 2 * e));
     } else {
         const uint8_t *b = row + 18 * (e >> 5);
-        const float d = h2f_bits(*reinterpret_cast<const uint16_t *>(b));
-        const int i = e & 31;
-        const int byte = b[2 + (i & 15)];
-        return d * (float)((i < 16 ? (byte & 15) : (byte >> 4)) - 8);
+        return h2f_bits(*reinterpret_cast<const uint16_t *>(b)) * q4_centered_f32(b + 2, e & 31);
     }
 }
 
@@ -184,8 +182,8 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D
 #pragma unroll
                 for (int i = 0; i < E; i += 2) {
                     const uint32_t w = *reinterpret_cast<const uint16_t *>(codes + i);
-                    kv[i] = (float)(int8_t)(w & 0xFFu);
-                    kv[i + 1] = (float)(int8_t)(w >> 8);
+                    kv[i] = q8_code_f32(w);
+                    kv[i + 1] = q8_code_f32(w >> 8);
                 }
             }
             float dot[kRmax];

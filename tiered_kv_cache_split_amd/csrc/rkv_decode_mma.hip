@@ -28,7 +28,7 @@
 // pause.  The online softmax is exact (the running max is raised whenever a chunk exceeds it)
 // so the binary16 weights stay in range.
 #include "rkv_internal.h"
-#include "rkv_quant.h"
+#include "rkv_unpack.h"
 #include "rkv_wave.h"
 
 #include <math.h>
@@ -43,9 +43,9 @@ typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef int int2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kCh = 32;              // cells per chunk
-constexpr float kMagicK = 1152.0f;   // q8_0 code q as binary16 1024 + (q + 128)
-constexpr float kMagicV = 1032.0f;   // q4_0 low nibble n (value n - 8) as binary16 1024 + n
-constexpr float kMagicVHi = 1152.0f; // q4_0 high nibble n kept in place: binary16 1024 + 16 n = 16 (n - 8) + 1152
+constexpr float kMagicK = kQ8Bias;     // q8_0 code q as binary16 1152 + q (q8_biased)
+constexpr float kMagicV = kQ4BiasLo;   // q4_0 low nibble n (value n - 8) as binary16 1032 + (n - 8)
+constexpr float kMagicVHi = kQ4BiasHi; // q4_0 high nibble n kept in place: binary16 1152 + 16 (n - 8)
 
 __device__ __forceinline__ half2_t h2v(uint32_t x) { return __builtin_bit_cast(half2_t, x); }
 __device__ __forceinline__ uint32_t u32v(half2_t x) { return __builtin_bit_cast(uint32_t, x); }
@@ -254,12 +254,8 @@ decode_mma_kernel(const SegParams p) {
             for (int blk = 0; blk < 4; ++blk) {
                 const int kslot = 2 * wave + (blk >> 1) + 2 * HW * (blk & 1);
                 const uint2 w = *reinterpret_cast<const uint2 *>(kr + 16 * kslot);
-                const uint32_t w0 = w.x ^ 0x80808080u;  // q + 128 per byte
-                const uint32_t w1 = w.y ^ 0x80808080u;
-                const uint4 ak = make_uint4(__builtin_amdgcn_perm(0x64646464u, w0, 0x05010400u),
-                                            __builtin_amdgcn_perm(0x64646464u, w0, 0x05030402u),
-                                            __builtin_amdgcn_perm(0x64646464u, w1, 0x05010400u),
-                                            __builtin_amdgcn_perm(0x64646464u, w1, 0x05030402u));
+                const uint2 b0 = q8_biased(w.x), b1 = q8_biased(w.y);  // 1152 + q, exact
+                const uint4 ak = make_uint4(b0.x, b0.y, b1.x, b1.y);
                 dq[kt][blk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, ak), qb[blk],
                                                                      cneg[blk], 0, 0, 0);
             }
@@ -359,10 +355,8 @@ decode_mma_kernel(const SegParams p) {
             uint32_t lo[4], hi[4];
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
-                const uint32_t w = (uint32_t)bt[jj >> 1];
-                const uint32_t y = __builtin_amdgcn_perm(w, w, (jj & 1) ? 0x0C030C02u : 0x0C010C00u);  // b0, 0, b1, 0
-                lo[jj] = (y & 0x000F000Fu) | vmagic;  // 1024 + n
-                hi[jj] = (y & 0x00F000F0u) | vmagic;  // 1024 + 16 n: no shift needed
+                // 1024 + n (low nibbles) and 1024 + 16 n (high nibbles, in place) of two bytes
+                q4_nibbles_biased((uint32_t)bt[jj >> 1], (jj & 1) ? 0x0C030C02u : 0x0C010C00u, vmagic, lo[jj], hi[jj]);
             }
             oacc[2 * blk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
                 __builtin_bit_cast(half8_t, make_uint4(lo[0], lo[1], lo[2], lo[3])), wf, oacc[2 * blk], 0, 0, 0);

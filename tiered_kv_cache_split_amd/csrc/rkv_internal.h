@@ -114,7 +114,7 @@ hipError_t launch_row_extent(const int32_t *rows, int64_t rows_s, int64_t n_kv, 
 hipError_t launch_uva_read(const void *host_src, void *dst, int64_t nbytes, hipStream_t s);
 // Bulk copy kernel over pinned host memory (source and destination 8-byte aligned).
 hipError_t launch_lift_copy(const void *host_src, void *dst, int64_t nbytes, hipStream_t s);
-hipError_t launch_dequant_rows(const void *src, int type, int64_t n_rows, int64_t row_stride,
+hipError_t launch_dequant_rows(const void *src, int type, int form, int64_t n_rows, int n_values, int64_t row_stride,
                                float *dst, hipStream_t s);
 
 // Head dims other than 128 (rkv_decode_hd.hip): decode segments (gqa * n_q <= 8, no row lists)

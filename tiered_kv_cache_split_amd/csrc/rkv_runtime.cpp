@@ -1252,16 +1252,20 @@ int rkv_tail_lift(rkv_ctx *ctx, const void *host_src, int64_t nbytes, int slot, 
     return RKV_OK;
 }
 
-int rkv_dequant_rows(const void *src, int type, int64_t n_rows, int64_t row_stride, float *dst, void *stream) {
+int rkv_dequant_rows(const void *src, int type, int form, int64_t n_rows, int64_t row_values, int64_t row_stride,
+                     float *dst, void *stream) {
     if (type != RKV_TYPE_F16 && type != RKV_TYPE_Q8_0 && type != RKV_TYPE_Q4_0)
         return fail(RKV_ERR_UNSUPPORTED, "type %d", type);
-    if (n_rows < 0 || row_stride < row_bytes(type)) return fail(RKV_ERR_ARG, "bad n_rows or row_stride");
+    if (form < RKV_DQ_DECODE_MMA || form > RKV_DQ_HEAD_DIM) return fail(RKV_ERR_ARG, "unknown form %d", form);
+    if (row_values <= 0 || row_values > 4096 || row_values % 32 != 0) return fail(RKV_ERR_ARG, "row_values must be a multiple of 32 in [32, 4096]");
+    if (n_rows < 0 || row_stride < row_bytes(type, row_values)) return fail(RKV_ERR_ARG, "bad n_rows or row_stride");
     if (n_rows == 0) return RKV_OK;
-    if (row_stride % 2 != 0 || ((uintptr_t)src) % 2 != 0) return fail(RKV_ERR_UNSUPPORTED, "rows must be 2-byte aligned");
+    if (n_rows > ((int64_t)1 << 30)) return fail(RKV_ERR_ARG, "too many rows");
     int st = check_device_ptr(src, "src");
     if (st) return st;
     if ((st = check_device_ptr(dst, "dst"))) return st;
-    hipError_t e = launch_dequant_rows(src, type, n_rows, row_stride, dst, static_cast<hipStream_t>(stream));
+    hipError_t e = launch_dequant_rows(src, type, form, n_rows, (int)row_values, row_stride, dst,
+                                       static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "dequant launch");
     return RKV_OK;
 }

@@ -20,6 +20,11 @@
 
 namespace rkv {
 
+constexpr int kQ8Block = 34;  // bytes of a q8_0 block
+constexpr int kQ4Block = 18;  // bytes of a q4_0 block
+constexpr int kQ8Row = 4 * kQ8Block;  // a row of 128 values
+constexpr int kQ4Row = 4 * kQ4Block;
+
 typedef _Float16 uhalf2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uhalf2_t u2h(uint32_t x) { return __builtin_bit_cast(uhalf2_t, x); }
@@ -29,6 +34,11 @@ __device__ __forceinline__ uint32_t h2u(uhalf2_t x) { return __builtin_bit_cast(
 __device__ __forceinline__ float f16_bits_to_f32(uint32_t bits16) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)(bits16 & 0xFFFFu));
 }
+
+__device__ __forceinline__ float h2f(uint32_t bits16) { return f16_bits_to_f32(bits16); }
+
+// Little-endian 16-bit load from a byte pointer that is at least 2-byte aligned.
+__device__ __forceinline__ uint32_t ld_u16(const uint8_t *p) { return *reinterpret_cast<const uint16_t *>(p); }
 
 // ---- q8_0 codes
 
