@@ -199,6 +199,22 @@ int rkv_attn_decode(rkv_ctx *ctx, const rkv_tensor *q,
                     const rkv_tensor *mask, int64_t wc, int64_t tile_kv, float scale,
                     float *o, float *lse, void *stream);
 
+/* Allocation-free decode, for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  The same computation
+ * and kernels as rkv_attn_decode over a device-resident cache (k, v hold all n_kv = k->ne[1]
+ * keys; no tail), without a context: its split-K partials live in a file-scope device array of
+ * 8 MiB (2^21 floats) that each GPU holds from the first call until the process ends.  The
+ * first call on a device looks that array's address up (hipGetSymbolAddress); no call
+ * allocates.  When the planned partials exceed the array, fewer splits are used (results stay
+ * within the decode tolerances, possibly not bit-identical to rkv_attn_decode); a shape whose
+ * single partial (n_head * n_q * (2 + dv) floats) exceeds it is RKV_ERR_UNSUPPORTED.
+ * Every call on a GPU shares that GPU's array: calls that overlap in time on one GPU (two
+ * streams, two threads) race and give wrong results; serialise them.
+ *   q, k, v, mask, scale, o, lse as rkv_attn_decode (k_win = k, v_win = v, wc = n_kv); the
+ *   logit soft-cap is off.  Enqueued on `stream` (the calling thread's current device). */
+int rkv_attn_decode_noalloc(const rkv_tensor *q, const rkv_tensor *k, const rkv_tensor *v,
+                            const rkv_tensor *mask, float scale, float *o, float *lse, void *stream);
+
 /* Prefill attention (patch 0070, fattn.cu ggml_cuda_streaming_flash_attn: the same window +
  * tail streaming op serves a multi-token chunk, with the mask sliced at the global key
  * position, a per-tile flash attention and an LSE per tile for the combine; patch 0102,

@@ -192,6 +192,14 @@ class Context:
         return int(dst.value or 0)
 
 
+def attn_decode_noalloc(q, k, v, mask, scale, o, lse=None, stream=None):
+    """rkv_attn_decode over a device-resident cache with no context and no allocation: the
+    partials live in the library's static device array (calls on one GPU must not overlap)."""
+    lib = load()
+    check(lib.rkv_attn_decode_noalloc(_ref(q), _ref(k), _ref(v), _ref(mask), float(scale), _ptr(o), _ptr(lse),
+                                      _stream(stream)), "rkv_attn_decode_noalloc")
+
+
 def lse_merge(partials, n_seg: int, n_rows: int, o, lse=None, stream=None, dv: int = 128):
     lib = load()
     check(lib.rkv_lse_merge(_ptr(partials), int(n_seg), int(n_rows), int(dv), _ptr(o), _ptr(lse), _stream(stream)),

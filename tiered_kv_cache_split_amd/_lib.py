@@ -54,6 +54,7 @@ SIGNATURES = {
     "rkv_attn_partial": (ctypes.c_int, [vp, TP, TP, TP, TP, i64, i64, ctypes.c_float, vp, vp]),
     "rkv_lse_merge": (ctypes.c_int, [vp, ctypes.c_int, i64, ctypes.c_int, vp, vp, vp]),
     "rkv_tail_lift": (ctypes.c_int, [vp, vp, i64, ctypes.c_int, ctypes.c_int, ctypes.POINTER(vp), vp]),
+    "rkv_attn_decode_noalloc": (ctypes.c_int, [TP, TP, TP, TP, ctypes.c_float, vp, vp, vp]),
     "rkv_dequant_rows": (ctypes.c_int, [vp, ctypes.c_int, ctypes.c_int, i64, i64, i64, vp, vp]),
     "rkv_set_softcap": (ctypes.c_int, [vp, ctypes.c_float]),
     "rkv_set_tail_mode": (ctypes.c_int, [vp, ctypes.c_int, ctypes.c_int]),

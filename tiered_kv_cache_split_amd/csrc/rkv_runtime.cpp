@@ -21,6 +21,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -475,10 +476,14 @@ int lift_tile(rkv_ctx *ctx, int mode, const rkv_tensor *t, const TailGeom &g, in
 }
 
 // Common body of decode and prefill.
+// ext_partials (optional): a device buffer of ext_cap floats that replaces the context's
+// partials workspace; then nothing is allocated, the split-K factor shrinks until the partials
+// fit, and the tail must be device-resident.
 int attn_window_tail(rkv_ctx *ctx, const rkv_tensor *q, const rkv_tensor *k_win,
                      const rkv_tensor *v_win, const rkv_tensor *k_tail, const rkv_tensor *v_tail,
                      const rkv_tensor *mask, int64_t wc, int64_t tile_kv, float scale,
-                     int64_t q_pos0, bool mfma, float *o, float *lse, hipStream_t stream) {
+                     int64_t q_pos0, bool mfma, float *o, float *lse, hipStream_t stream,
+                     float *ext_partials = nullptr, int64_t ext_cap = 0) {
     if (!ctx) return fail(RKV_ERR_ARG, "ctx is NULL");
     // decode takes head dims 64, 128 and 256 (dv = dk); prefill 128 only
     const bool any_d = !mfma;
@@ -582,14 +587,39 @@ int attn_window_tail(rkv_ctx *ctx, const rkv_tensor *q, const rkv_tensor *k_win,
                    gk.nb1, gk.cell_major ? gk.nb2 : cap_cells * gk.nb1,
                    gv.nb1, gv.cell_major ? gv.nb2 : cap_cells * gv.nb1, cells, wc + loc};
     };
-    int64_t total_slots = 0;
-    if (wc > 0) total_slots += plan_segment(ctx, base, win, mfma, k_type, v_type).n_splits;
-    if (n_tail > 0 && !lifted) total_slots += plan_segment(ctx, base, dtail, mfma, k_type, v_type).n_splits;
-    for (int64_t t = 0; t < n_tiles; ++t) total_slots += plan_segment(ctx, base, tile_seg(t), mfma, k_type, v_type).n_splits;
-    if (host_tail) total_slots += 1;
-    if (total_slots == 0) total_slots = 1;  // n_kv == 0: one empty partial
-    if ((st = ensure_partials(ctx, total_slots * base.n_rows * ps, stream))) return st;
-    base.partials = ctx->partials;
+    auto count_slots = [&]() {
+        int64_t n = 0;
+        if (wc > 0) n += plan_segment(ctx, base, win, mfma, k_type, v_type).n_splits;
+        if (n_tail > 0 && !lifted) n += plan_segment(ctx, base, dtail, mfma, k_type, v_type).n_splits;
+        for (int64_t t = 0; t < n_tiles; ++t) n += plan_segment(ctx, base, tile_seg(t), mfma, k_type, v_type).n_splits;
+        if (host_tail) n += 1;
+        return n == 0 ? (int64_t)1 : n;  // n_kv == 0: one empty partial
+    };
+    int64_t total_slots = count_slots();
+    if (ext_partials) {
+        if (lifted || host_tail) return fail(RKV_ERR_ARG, "a caller-provided partials buffer needs a device-resident tail");
+        const int64_t per_slot = base.n_rows * ps;
+        if (per_slot > ext_cap)
+            return fail(RKV_ERR_UNSUPPORTED, "one partial of %lld rows needs %lld floats, more than the %lld available",
+                        (long long)base.n_rows, (long long)per_slot, (long long)ext_cap);
+        // fewer splits until every segment's partials fit (each segment takes at least one slot)
+        const int n_seg = (wc > 0 ? 1 : 0) + (n_tail > 0 ? 1 : 0);
+        while (total_slots * per_slot > ext_cap) {
+            const int64_t cur = ctx->splits_override > 0 ? ctx->splits_override : total_slots;
+            const int64_t fit = std::max<int64_t>(1, ext_cap / per_slot / std::max(1, n_seg));
+            ctx->splits_override = (int)std::max<int64_t>(1, std::min(cur - 1, fit));
+            total_slots = count_slots();
+            if (ctx->splits_override == 1 && total_slots * per_slot > ext_cap)
+                return fail(RKV_ERR_UNSUPPORTED, "partials of %lld slots exceed the %lld floats available",
+                            (long long)total_slots, (long long)ext_cap);
+        }
+        base.partials = ext_partials;
+    } else {
+        if ((st = ensure_partials(ctx, total_slots * base.n_rows * ps, stream))) return st;
+        base.partials = ctx->partials;
+    }
+    // every kernel below (segments, empty partial, merge) reads and writes base.partials
+    if (!base.partials) return fail(RKV_ERR_HIP, "no partials workspace");
 
     ctx->stats = rkv_stats{};
     ctx->stats.kernel_variant = mfma ? RKV_KERNEL_PREFILL_MFMA : RKV_KERNEL_DECODE_HEAD;
@@ -690,7 +720,7 @@ int attn_window_tail(rkv_ctx *ctx, const rkv_tensor *q, const rkv_tensor *k_win,
         }
         ctx->stats.host_tail_ms = std::chrono::duration<float, std::milli>(std::chrono::steady_clock::now() - t0).count();
         ctx->stats.tail_host = 1;
-        RKV_HIP(hipMemcpyAsync(ctx->partials + (int64_t)slot * base.n_rows * ps, ctx->hpart,
+        RKV_HIP(hipMemcpyAsync(base.partials + (int64_t)slot * base.n_rows * ps, ctx->hpart,
                                (size_t)(base.n_rows * ps * 4), hipMemcpyHostToDevice, stream));
         RKV_HIP(hipEventRecord(ctx->host_up, stream));
         ctx->host_up_pending = true;
@@ -720,19 +750,64 @@ int attn_window_tail(rkv_ctx *ctx, const rkv_tensor *q, const rkv_tensor *k_win,
         // other head dims: the merge of partials with row stride 2 + d (no partial at all, as for
         // n_kv == 0, gives every row O = 0 and LSE = -inf)
         ctx->stats.n_partials = slot;
-        hipError_t e = launch_merge_hd(ctx->partials, slot, base.n_rows, d, o, lse, stream);
+        hipError_t e = launch_merge_hd(base.partials, slot, base.n_rows, d, o, lse, stream);
         if (e != hipSuccess) return hip_fail(e, "merge launch");
         return RKV_OK;
     }
     if (slot == 0) {
         // n_kv == 0: a single empty partial, so every row gets O = 0 and LSE = -inf
-        hipError_t e0 = launch_empty_partials(ctx->partials, base.n_rows, stream);
+        hipError_t e0 = launch_empty_partials(base.partials, base.n_rows, stream);
         if (e0 != hipSuccess) return hip_fail(e0, "empty partial");
         slot = 1;
     }
     ctx->stats.n_partials = slot;
-    hipError_t e = launch_merge(ctx->partials, slot, base.n_rows, o, lse, nullptr, stream);
+    hipError_t e = launch_merge(base.partials, slot, base.n_rows, o, lse, nullptr, stream);
     if (e != hipSuccess) return hip_fail(e, "merge launch");
+    return RKV_OK;
+}
+
+// ---- allocation-free decode: partials in a file-scope device array.  Each device holds its own
+// copy of the array (until the process ends); host code may use the array only through the
+// device address hipGetSymbolAddress returns on that device (the name itself is a host-side
+// stand-in), looked up once per device and kept here.
+constexpr int64_t kNoAllocFloats = (int64_t)2 << 20;  // 8 MiB of partials
+
+}  // namespace
+
+static __device__ __align__(256) float scratch[kNoAllocFloats];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_noalloc_mu;
+float *g_noalloc_ptr[kMaxDevices] = {};
+int g_noalloc_cu[kMaxDevices] = {};
+
+// The calling thread's current device, its copy of `scratch` and its compute-unit count.
+int noalloc_scratch(float **ptr, int *n_cu, int *device) {
+    int dev = -1;
+    RKV_HIP(hipGetDevice(&dev));
+    if (dev < 0 || dev >= kMaxDevices) return fail(RKV_ERR_UNSUPPORTED, "device %d beyond the %d supported", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_noalloc_mu);
+    if (!g_noalloc_ptr[dev]) {
+        void *p = nullptr;
+        hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) {
+            (void)hipGetLastError();
+            return fail(RKV_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+        }
+        int cus = 0;
+        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess || cus <= 0) {
+            (void)hipGetLastError();
+            return fail(RKV_ERR_HIP, "compute-unit count of device %d", dev);
+        }
+        g_noalloc_cu[dev] = cus;
+        g_noalloc_ptr[dev] = static_cast<float *>(p);
+    }
+    *ptr = g_noalloc_ptr[dev];
+    *n_cu = g_noalloc_cu[dev];
+    *device = dev;
     return RKV_OK;
 }
 
@@ -1056,6 +1131,20 @@ int rkv_lift_timing_ms(rkv_ctx *ctx, float *total_ms, float *span_ms, int *n_lif
     }
     if (n_lifts) *n_lifts = ctx->n_lift_timed;
     return RKV_OK;
+}
+
+int rkv_attn_decode_noalloc(const rkv_tensor *q, const rkv_tensor *k, const rkv_tensor *v, const rkv_tensor *mask,
+                            float scale, float *o, float *lse, void *stream) {
+    if (!k || !v) return fail(RKV_ERR_ARG, "k and v must be given");
+    float *scr = nullptr;
+    int n_cu = 0, dev = 0;
+    int st = noalloc_scratch(&scr, &n_cu, &dev);
+    if (st) return st;
+    rkv_ctx c;  // planning state only: no stream, event or buffer is created
+    c.device = dev;
+    c.n_cu = n_cu;
+    return attn_window_tail(&c, q, k, v, nullptr, nullptr, mask, k->ne[1], 1, scale, -1, false, o, lse,
+                            static_cast<hipStream_t>(stream), scr, kNoAllocFloats);
 }
 
 int rkv_attn_decode(rkv_ctx *ctx, const rkv_tensor *q, const rkv_tensor *k_win, const rkv_tensor *v_win,
