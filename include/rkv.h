@@ -324,6 +324,68 @@ int rkv_choose_tail_mode(int64_t tail_bytes, double h2d_gbps, double host_gbps, 
  * it off.  Errors: RKV_ERR_ARG for a NULL context or a negative or non-finite value. */
 int rkv_set_softcap(rkv_ctx *ctx, float softcap);
 
+/* ---- device-side block cache ---------------------------------------------------------- */
+/* Strata compare v0.1.2...v0.1.6, "KV streaming for the QSA layers" (kv_stream.hpp header
+ * comment, kv_stream.cu): the authoritative K/V stay in pinned host memory; device memory holds
+ * n_slots pages of page_size cells and a residency map; before a sparse read, a resolve call
+ * makes every page the selection names resident on the device, inside the stream (capturable:
+ * nothing is allocated after rkv_bcache_create), and translates the selection into rows of the
+ * device slot pools, which rkv_attn_rows then reads like any pool. */
+typedef struct rkv_bcache rkv_bcache;
+
+typedef struct rkv_bcache_stats {
+    uint64_t misses;      /* pages copied into slots over all resolve calls               */
+    uint64_t lookups;     /* selection entries whose predecessor names another page       */
+    uint64_t calls;       /* resolve calls                                                */
+    int32_t epoch;        /* = calls since the last reset                                 */
+    int32_t hand;         /* clock hand (next slot the sweep examines)                    */
+    int32_t last_misses;  /* pages placed by the last call                                */
+    int32_t overflow;     /* 1 once a call named more pages than it could place           */
+} rkv_bcache_stats;
+
+/* Create a block cache over the host copy k_host / v_host: [d, n_cells, n_head_kv, 1] (d in
+ * {64, 128, 256}; K F16 or Q8_0, V F16 or Q4_0), cell-major with the heads packed inside a cell,
+ * in pinned host memory the caller owns and keeps alive (16-byte aligned; page_size * nb[1] a
+ * multiple of 16 bytes; n_cells a multiple of page_size).  Allocates the map (page table,
+ * slot arrays, counters) and the two slot pools (n_slots * page_size cells each, cell stride
+ * nb[1]) on the current device, every page absent.  Errors: RKV_ERR_ARG / RKV_ERR_UNSUPPORTED
+ * for malformed or unsupported shapes and memory kinds, RKV_ERR_NOMEM. */
+int rkv_bcache_create(const rkv_tensor *k_host, const rkv_tensor *v_host, int64_t page_size,
+                      int64_t n_slots, rkv_bcache **out);
+void rkv_bcache_destroy(rkv_bcache *bc);
+
+/* Every page absent, every slot free, counters zero (enqueued on `stream`). */
+int rkv_bcache_reset(rkv_bcache *bc, void *stream);
+
+/* Make resident every page named by sel, int32 [n_sel, n_seq] device memory (cell ids, -1 =
+ * padding; each list preferably ascending, which makes one lookup per page run): resident pages
+ * take this call's epoch and reference bit; each missing page is claimed once and gets a victim
+ * slot from a CLOCK (second-chance) sweep that never takes a slot this call uses; the missed
+ * pages are copied from the host copy into their slots by a kernel reading host memory directly
+ * (zero-copy).  rows (int32 [n_sel, n_seq] device memory, or NULL) receives each entry's row in
+ * the slot pools (rkv_bcache_pools), -1 for padding.  The distinct pages of one call must fit
+ * in n_slots: pages beyond that stay absent, their rows are -1 and the overflow counter is set.
+ * Enqueued on `stream`; calls on one cache must be ordered on one stream. */
+int rkv_bcache_resolve(rkv_bcache *bc, const int32_t *sel, int64_t n_sel, int n_seq, int32_t *rows,
+                       void *stream);
+
+/* Descriptors of the device slot pools ([d, n_slots*page_size, n_head_kv, 1], the host copy's
+ * cell stride), to pass to rkv_attn_rows as k_pool / v_pool with the rows of a resolve call. */
+int rkv_bcache_pools(const rkv_bcache *bc, rkv_tensor *k_pool, rkv_tensor *v_pool);
+
+/* Write-through append of cell `cell`: k_cell / v_cell (device memory, n_head_kv rows of K / V
+ * in the cache's type, 4-byte aligned) are written to the host copy always and to the cell's
+ * slot when its page is resident, so no slot ever holds stale data. */
+int rkv_bcache_append(rkv_bcache *bc, const void *k_cell, const void *v_cell, int64_t cell, void *stream);
+
+/* Synchronous read of the counters (waits for the device). */
+int rkv_bcache_counters(rkv_bcache *bc, rkv_bcache_stats *out);
+
+/* Testing aid: device addresses of the page table (n_pages int32: slot or -1) and of the slot
+ * map (n_slots int32: page or -1). */
+int rkv_bcache_map(const rkv_bcache *bc, int32_t **page_table, int32_t **slot_page, int64_t *n_pages,
+                   int64_t *n_slots);
+
 /* ---- residency policy (host) ----------------------------------------------------------- */
 
 /* Position-window sizing (patch 0070, KV-cache hunk: the position-axis residency sizer).

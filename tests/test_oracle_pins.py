@@ -425,3 +425,60 @@ def test_softcap_limits():
     Om, Lm = oracle.merge(parts)
     Oa, La = oracle.attention(q, k, v, 0.09, softcap=3.0)
     assert np.abs(Om - Oa).max() < 1e-12 and np.abs(Lm - La).max() < 1e-12
+
+
+# ---- block cache residency policy (oracle/block_cache.py), pinned by hand-worked CLOCK runs
+# and invariants of the policy statement (Strata, "KV streaming for the QSA layers")
+
+def test_clock_cold_start_hand_order():
+    """4 slots of 2 cells: cells 0,1,2,3,8 name pages 0, 1, 4 -> three misses into the free
+    slots 0, 1, 2 in hand order; the hand stops at 3; lookups: one per run of equal pages."""
+    c = oracle.ClockCache(n_pages=8, n_slots=4, page_size=2)
+    victims, missed, ovf = c.resolve([[0, 1, 2, 3, 8]])
+    assert victims == [0, 1, 2] and missed == [0, 1, 4] and not ovf
+    assert c.hand == 3 and c.page_table[:5] == [0, 1, -1, -1, 2] and c.slot_page == [0, 1, 4, -1]
+    assert (c.misses, c.lookups, c.calls) == (3, 3, 1)
+
+
+def test_clock_second_chance():
+    """After the cold start, pages 1 (hit), 5, 6: slot 3 is free and taken; slot 0 (page 0,
+    referenced) loses its bit; slot 1 is used by this call and skipped; slot 2 (page 4,
+    referenced) loses its bit; slot 3 is now this call's; slot 0, unreferenced, is taken.  The
+    hand stops past slot 0; page 0 is evicted; page 4 stays with its bit cleared."""
+    c = oracle.ClockCache(n_pages=8, n_slots=4, page_size=2)
+    c.resolve([[0, 1, 2, 3, 8]])
+    victims, missed, ovf = c.resolve([[2, 10, 12]])
+    assert victims == [3, 0] and missed == [5, 6] and not ovf
+    assert c.hand == 1
+    assert c.page_table[0] == -1 and c.page_table[1] == 1 and c.page_table[4] == 2
+    assert c.page_table[5] == 3 and c.page_table[6] == 0
+    assert c.slot_ref == [1, 1, 0, 1]
+    assert (c.misses, c.lookups, c.calls) == (5, 6, 2)
+
+
+def test_clock_overflow_and_padding():
+    c = oracle.ClockCache(n_pages=16, n_slots=2, page_size=4)
+    victims, missed, ovf = c.resolve([[0, 4, -1, 8, -1, -1]])
+    assert ovf and len(victims) == 2 and len(missed) == 2 and c.overflow
+    assert c.lookups == 3  # padding never counts
+
+
+def test_clock_invariants_random():
+    """Random calls: the map is its own inverse, every page a call names is resident after it,
+    residency never exceeds the slots, and the victims are distinct slots."""
+    rng = np.random.default_rng(8)
+    c = oracle.ClockCache(n_pages=64, n_slots=12, page_size=4)
+    for _ in range(200):
+        k = int(rng.integers(1, 12))
+        pages = rng.choice(64, size=k, replace=False)
+        sel = np.sort(np.concatenate([p * 4 + rng.integers(0, 4, size=2) for p in pages]))
+        victims, missed, ovf = c.resolve([sel])
+        assert not ovf and len(set(victims)) == len(victims) == len(missed)
+        for p in pages:
+            s = c.page_table[p]
+            assert s >= 0 and c.slot_page[s] == p and c.slot_stamp[s] == c.epoch
+        for s, p in enumerate(c.slot_page):
+            if p >= 0:
+                assert c.page_table[p] == s
+        assert sum(1 for x in c.page_table if x >= 0) <= 12
+        assert c.rows(sel) == [c.page_table[x // 4] * 4 + x % 4 for x in sel]

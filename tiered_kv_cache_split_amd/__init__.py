@@ -17,7 +17,7 @@ import ctypes
 from ._lib import (RKV_LIFT_AUTO, RKV_LIFT_BULK, RKV_LIFT_KERNEL, RKV_LIFT_UVA, RKV_RESIDENCY_AUTO, RKV_RESIDENCY_RESIDENT,  # noqa: F401
                    RKV_RESIDENCY_WINDOW, RKV_TAIL_HOST, RKV_DQ_DECODE_MMA, RKV_DQ_PREFILL, RKV_DQ_VECTOR, RKV_DQ_HEAD_DIM, RKV_TAIL_LIFT, RKV_TYPE_F16, RKV_TYPE_F32, RKV_TYPE_Q4_0,
                    RKV_TYPE_Q8_0, RKV_ERR_ARG, RKV_ERR_UNSUPPORTED, RkvError,
-                   RkvStats, RkvTensor, check, load)
+                   RkvBcacheCounters, RkvStats, RkvTensor, check, load)
 
 BLOCK_BYTES = {RKV_TYPE_F16: 2, RKV_TYPE_F32: 4, RKV_TYPE_Q8_0: 34, RKV_TYPE_Q4_0: 18}
 ROW_BYTES = {RKV_TYPE_F16: 256, RKV_TYPE_Q8_0: 136, RKV_TYPE_Q4_0: 72}
@@ -190,6 +190,78 @@ class Context:
         check(self.lib.rkv_tail_lift(self.h, _ptr(host_src), int(nbytes), int(slot), int(mode),
                                      ctypes.byref(dst), cs), "rkv_tail_lift")
         return int(dst.value or 0)
+
+
+class BlockCache:
+    """Device-side block cache over a pinned host copy (rkv_bcache_*): k_host / v_host are pinned
+    uint8 caches (n_cells, n_head_kv, row_bytes) the caller keeps alive."""
+
+    def __init__(self, k_host, v_host, k_type: int, v_type: int, page_size: int, n_slots: int):
+        self.lib = load()
+        self.k_host, self.v_host = k_host, v_host
+        h = ctypes.c_void_p()
+        kd, vd = kv_desc(k_host, k_type), kv_desc(v_host, v_type)
+        check(self.lib.rkv_bcache_create(ctypes.byref(kd), ctypes.byref(vd), int(page_size), int(n_slots),
+                                         ctypes.byref(h)), "rkv_bcache_create")
+        self.h = h
+
+    def close(self):
+        if getattr(self, "h", None):
+            self.lib.rkv_bcache_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def reset(self, stream=None):
+        check(self.lib.rkv_bcache_reset(self.h, _stream(stream)), "rkv_bcache_reset")
+
+    def resolve(self, sel, rows=None, stream=None):
+        """sel: int32 device tensor (n_seq, n_sel) of cell ids (-1 padding); rows: int32 device
+        tensor of the same shape receiving slot-pool rows, or None."""
+        n_seq, n_sel = (1, sel.shape[0]) if sel.dim() == 1 else (sel.shape[0], sel.shape[1])
+        check(self.lib.rkv_bcache_resolve(self.h, _ptr(sel), int(n_sel), int(n_seq), _ptr(rows), _stream(stream)),
+              "rkv_bcache_resolve")
+
+    def pools(self):
+        k, v = RkvTensor(), RkvTensor()
+        check(self.lib.rkv_bcache_pools(self.h, ctypes.byref(k), ctypes.byref(v)), "rkv_bcache_pools")
+        return k, v
+
+    def append(self, k_cell, v_cell, cell: int, stream=None):
+        check(self.lib.rkv_bcache_append(self.h, _ptr(k_cell), _ptr(v_cell), int(cell), _stream(stream)),
+              "rkv_bcache_append")
+
+    def counters(self) -> dict:
+        c = RkvBcacheCounters()
+        check(self.lib.rkv_bcache_counters(self.h, ctypes.byref(c)), "rkv_bcache_counters")
+        return {f: getattr(c, f) for f, _ in RkvBcacheCounters._fields_}
+
+    def map_arrays(self):
+        """(page_table, slot_page) copied to host numpy arrays (synchronises the device)."""
+        import numpy as np
+        import torch
+        pt, sp = ctypes.c_void_p(), ctypes.c_void_p()
+        n_pages, n_slots = ctypes.c_int64(), ctypes.c_int64()
+        check(self.lib.rkv_bcache_map(self.h, ctypes.byref(pt), ctypes.byref(sp), ctypes.byref(n_pages),
+                                      ctypes.byref(n_slots)), "rkv_bcache_map")
+        torch.cuda.synchronize()
+        a = np.empty(n_pages.value, dtype=np.int32)
+        b = np.empty(n_slots.value, dtype=np.int32)
+        lib_hip = _hip()
+        lib_hip.hipMemcpy.restype = ctypes.c_int
+        lib_hip.hipMemcpy(ctypes.c_void_p(a.ctypes.data), pt, ctypes.c_size_t(a.nbytes), 2)
+        lib_hip.hipMemcpy(ctypes.c_void_p(b.ctypes.data), sp, ctypes.c_size_t(b.nbytes), 2)
+        return a, b
+
+
+def _hip():
+    """The HIP runtime the process already uses (the one torch loaded)."""
+    import torch  # noqa: F401
+    return ctypes.CDLL("libamdhip64.so")
 
 
 def attn_decode_noalloc(q, k, v, mask, scale, o, lse=None, stream=None):

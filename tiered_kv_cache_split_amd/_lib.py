@@ -30,6 +30,12 @@ class RkvStats(ctypes.Structure):
                 ("host_tail_ms", ctypes.c_float)]
 
 
+class RkvBcacheCounters(ctypes.Structure):
+    _fields_ = [("misses", ctypes.c_uint64), ("lookups", ctypes.c_uint64), ("calls", ctypes.c_uint64),
+                ("epoch", ctypes.c_int32), ("hand", ctypes.c_int32), ("last_misses", ctypes.c_int32),
+                ("overflow", ctypes.c_int32)]
+
+
 TP = ctypes.POINTER(RkvTensor)
 
 # name -> (restype, argtypes); every name is exported by librkv.so and declared in rkv.h
@@ -54,6 +60,15 @@ SIGNATURES = {
     "rkv_attn_partial": (ctypes.c_int, [vp, TP, TP, TP, TP, i64, i64, ctypes.c_float, vp, vp]),
     "rkv_lse_merge": (ctypes.c_int, [vp, ctypes.c_int, i64, ctypes.c_int, vp, vp, vp]),
     "rkv_tail_lift": (ctypes.c_int, [vp, vp, i64, ctypes.c_int, ctypes.c_int, ctypes.POINTER(vp), vp]),
+    "rkv_bcache_create": (ctypes.c_int, [TP, TP, i64, i64, ctypes.POINTER(vp)]),
+    "rkv_bcache_destroy": (None, [vp]),
+    "rkv_bcache_reset": (ctypes.c_int, [vp, vp]),
+    "rkv_bcache_resolve": (ctypes.c_int, [vp, vp, i64, ctypes.c_int, vp, vp]),
+    "rkv_bcache_pools": (ctypes.c_int, [vp, TP, TP]),
+    "rkv_bcache_append": (ctypes.c_int, [vp, vp, vp, i64, vp]),
+    "rkv_bcache_counters": (ctypes.c_int, [vp, ctypes.POINTER(RkvBcacheCounters)]),
+    "rkv_bcache_map": (ctypes.c_int, [vp, ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(i64),
+                                      ctypes.POINTER(i64)]),
     "rkv_attn_decode_noalloc": (ctypes.c_int, [TP, TP, TP, TP, ctypes.c_float, vp, vp, vp]),
     "rkv_dequant_rows": (ctypes.c_int, [vp, ctypes.c_int, ctypes.c_int, i64, i64, i64, vp, vp]),
     "rkv_set_softcap": (ctypes.c_int, [vp, ctypes.c_float]),
@@ -77,6 +92,13 @@ def load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(f"librkv.so not found at {LIB_PATH}: build it first "
                            "(python -m tiered_kv_cache_split_amd.build)")
+    # torch ships its own HIP runtime; loaded first, it also satisfies librkv's dependency, so
+    # the process holds one runtime (device pointers and streams are shared between the two).
+    # Loaded after librkv, a second copy would come up beside the system one and fail to start.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(LIB_PATH)
     for name, (res, args) in SIGNATURES.items():
         fn = getattr(lib, name)

@@ -14,7 +14,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "librkv.so")
-SOURCES = ["rkv_decode.hip", "rkv_decode_mma.hip", "rkv_decode_mma16.hip", "rkv_decode_hd.hip", "rkv_prefill.hip", "rkv_merge.hip", "rkv_aux.hip", "rkv_host_tail.cpp", "rkv_runtime.cpp"]
+SOURCES = ["rkv_decode.hip", "rkv_decode_mma.hip", "rkv_decode_mma16.hip", "rkv_decode_hd.hip", "rkv_prefill.hip", "rkv_merge.hip", "rkv_aux.hip", "rkv_bcache.hip", "rkv_host_tail.cpp", "rkv_runtime.cpp"]
 # host code only (the CPU tail partial): no device pass
 HOST_ONLY = {"rkv_host_tail.cpp"}
 ARCH = "gfx950"

@@ -124,6 +124,30 @@ hipError_t launch_decode_hd(const SegParams &p, int k_type, int v_type, hipStrea
 hipError_t launch_merge_hd(const float *partials, int n_seg, int64_t n_rows, int dv, float *o, float *lse,
                            hipStream_t s);
 
+// Device-side block cache (rkv_bcache.hip): residency map arrays, all device memory.
+constexpr int kBcCtl = 16;  // [0] epoch [1] hand [2] pages placed by the last call [3] overflow;
+                            // u64 at [4] misses, [6] lookups, [8] calls
+struct BcMap {
+    int32_t *page_table;  // (n_pages) page -> slot, -1 absent (-2 while a resolve claims it)
+    int32_t *slot_page;   // (n_slots) slot -> page, -1 free
+    int32_t *slot_stamp;  // (n_slots) epoch of the call that last used the slot
+    int32_t *slot_ref;    // (n_slots) clock reference bit
+    int32_t *miss_page;   // (n_slots) pages missed by the last call, in claim order
+    int32_t *miss_slot;   // (n_slots) their slots
+    int32_t *ctl;         // (kBcCtl)
+    int64_t n_pages, n_slots;
+    int page_size;
+};
+hipError_t launch_bc_reset(const BcMap &m, hipStream_t s);
+// Resolve a selection (int32 cells [n_seq][n_sel], -1 padding), copy the missed pages from the
+// host copy's device view into their slots, and (rows != NULL) write each cell's slot-pool row.
+hipError_t launch_bc_resolve(const BcMap &m, const int32_t *sel, int64_t n_sel, int n_seq, const uint8_t *host_k,
+                             const uint8_t *host_v, uint8_t *pool_k, uint8_t *pool_v, int64_t k_page_bytes,
+                             int64_t v_page_bytes, int32_t *rows, hipStream_t s);
+hipError_t launch_bc_append(const BcMap &m, const void *k_cell, const void *v_cell, int64_t k_cell_bytes,
+                            int64_t v_cell_bytes, int64_t cell, uint8_t *host_k, uint8_t *host_v, uint8_t *pool_k,
+                            uint8_t *pool_v, int64_t k_s1, int64_t v_s1, hipStream_t s);
+
 // Tail partial on the host cores (rkv_host_tail.cpp).  Every pointer is host memory.
 struct HostTailArgs {
     const uint16_t *q;        // binary16 queries; element strides of query i and head h

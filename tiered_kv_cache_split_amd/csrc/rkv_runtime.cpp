@@ -197,6 +197,17 @@ struct rkv_ctx {
     rkv_stats stats = {};
 };
 
+struct rkv_bcache {
+    int device = 0;
+    BcMap m{};
+    void *map_mem = nullptr;
+    uint8_t *pool_k = nullptr, *pool_v = nullptr;
+    uint8_t *view_k = nullptr, *view_v = nullptr;  // device views of the caller's pinned host copy
+    int k_type = 0, v_type = 0;
+    int64_t d = 0, n_cells = 0, n_head_kv = 0, k_s1 = 0, v_s1 = 0, k_row = 0, v_row = 0;
+    int64_t page_size = 0, n_slots = 0;
+};
+
 namespace {
 
 bool stream_capturing(hipStream_t s) {
@@ -1338,6 +1349,166 @@ int rkv_tail_lift(rkv_ctx *ctx, const void *host_src, int64_t nbytes, int slot, 
     }
     RKV_HIP(hipEventRecord(ctx->copy_done[slot], cs));
     *dev_dst = ctx->scr_k[slot];
+    return RKV_OK;
+}
+
+void rkv_bcache_destroy(rkv_bcache *bc) {
+    if (!bc) return;
+    int cur = -1;
+    if (hipGetDevice(&cur) == hipSuccess && cur != bc->device) (void)hipSetDevice(bc->device);
+    (void)hipDeviceSynchronize();
+    if (bc->map_mem) (void)hipFree(bc->map_mem);
+    if (bc->pool_k) (void)hipFree(bc->pool_k);
+    if (bc->pool_v) (void)hipFree(bc->pool_v);
+    (void)hipGetLastError();
+    delete bc;
+}
+
+int rkv_bcache_create(const rkv_tensor *k_host, const rkv_tensor *v_host, int64_t page_size, int64_t n_slots,
+                      rkv_bcache **out) {
+    if (!out) return fail(RKV_ERR_ARG, "out is NULL");
+    *out = nullptr;
+    if (!k_host || !v_host) return fail(RKV_ERR_ARG, "k_host and v_host must be given");
+    int st;
+    if ((st = check_kv(k_host, "k_host", true, true)) || (st = check_kv(v_host, "v_host", false, true))) return st;
+    const int64_t d = k_host->ne[0], n_cells = k_host->ne[1], n_head_kv = k_host->ne[2];
+    if (v_host->ne[0] != d || v_host->ne[1] != n_cells || v_host->ne[2] != n_head_kv)
+        return fail(RKV_ERR_ARG, "k_host and v_host disagree in shape");
+    if (page_size < 1 || n_slots < 1 || n_slots > ((int64_t)1 << 28)) return fail(RKV_ERR_ARG, "bad page_size or n_slots");
+    if (n_cells < 1 || n_cells % page_size != 0) return fail(RKV_ERR_ARG, "the host copy must hold whole pages");
+    const int64_t n_pages = n_cells / page_size;
+    if (n_pages > ((int64_t)1 << 30) || n_slots * page_size > ((int64_t)1 << 31) - 1)
+        return fail(RKV_ERR_UNSUPPORTED, "cache too large for 32-bit pages and rows");
+    const int64_t k_row = row_bytes(k_host->type, d), v_row = row_bytes(v_host->type, d);
+    for (const rkv_tensor *t : {k_host, v_host}) {
+        const int64_t rb = t == k_host ? k_row : v_row;
+        if (n_head_kv > 1 && t->nb[2] != rb) return fail(RKV_ERR_UNSUPPORTED, "the host copy must be cell-major (heads packed in a cell)");
+        if (t->nb[1] < n_head_kv * rb) return fail(RKV_ERR_ARG, "cell stride shorter than a cell");
+        if ((page_size * t->nb[1]) % 16 != 0 || ((uintptr_t)t->data) % 16 != 0 || (n_head_kv * rb) % 4 != 0)
+            return fail(RKV_ERR_UNSUPPORTED, "pages must be 16-byte multiples on 16-byte aligned host memory");
+        if (pointer_kind(t->data) != Mem::PinnedHost) return fail(RKV_ERR_ARG, "the host copy must be pinned host memory");
+    }
+    int dev = 0;
+    RKV_HIP(hipGetDevice(&dev));
+    rkv_bcache *bc = new rkv_bcache();
+    bc->device = dev;
+    bc->k_type = k_host->type;
+    bc->v_type = v_host->type;
+    bc->d = d;
+    bc->n_cells = n_cells;
+    bc->n_head_kv = n_head_kv;
+    bc->k_s1 = k_host->nb[1];
+    bc->v_s1 = v_host->nb[1];
+    bc->k_row = k_row;
+    bc->v_row = v_row;
+    bc->page_size = page_size;
+    bc->n_slots = n_slots;
+    auto bail = [&](int status, const char *what) {
+        rkv_bcache_destroy(bc);
+        return fail(status, "%s", what);
+    };
+    void *vk = nullptr, *vv = nullptr;
+    if (hipHostGetDevicePointer(&vk, const_cast<void *>(k_host->data), 0) != hipSuccess ||
+        hipHostGetDevicePointer(&vv, const_cast<void *>(v_host->data), 0) != hipSuccess) {
+        (void)hipGetLastError();
+        return bail(RKV_ERR_HIP, "no device view of the host copy");
+    }
+    bc->view_k = static_cast<uint8_t *>(vk);
+    bc->view_v = static_cast<uint8_t *>(vv);
+    const size_t map_ints = (size_t)n_pages + 6 * (size_t)n_slots + kBcCtl + 8;
+    if (hipMalloc(&bc->map_mem, map_ints * sizeof(int32_t)) != hipSuccess ||
+        hipMalloc(reinterpret_cast<void **>(&bc->pool_k), (size_t)(n_slots * page_size * bc->k_s1)) != hipSuccess ||
+        hipMalloc(reinterpret_cast<void **>(&bc->pool_v), (size_t)(n_slots * page_size * bc->v_s1)) != hipSuccess) {
+        (void)hipGetLastError();
+        return bail(RKV_ERR_NOMEM, "device memory for the block cache");
+    }
+    int32_t *base = static_cast<int32_t *>(bc->map_mem);
+    bc->m.ctl = base;  // first, so its 64-bit counters are 8-byte aligned
+    bc->m.page_table = base + kBcCtl;
+    bc->m.slot_page = bc->m.page_table + n_pages;
+    bc->m.slot_stamp = bc->m.slot_page + n_slots;
+    bc->m.slot_ref = bc->m.slot_stamp + n_slots;
+    bc->m.miss_page = bc->m.slot_ref + n_slots;
+    bc->m.miss_slot = bc->m.miss_page + n_slots;
+    bc->m.n_pages = n_pages;
+    bc->m.n_slots = n_slots;
+    bc->m.page_size = (int)page_size;
+    hipError_t e = launch_bc_reset(bc->m, nullptr);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return bail(RKV_ERR_HIP, "block cache reset");
+    }
+    *out = bc;
+    return RKV_OK;
+}
+
+int rkv_bcache_reset(rkv_bcache *bc, void *stream) {
+    if (!bc) return fail(RKV_ERR_ARG, "bc is NULL");
+    hipError_t e = launch_bc_reset(bc->m, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "block cache reset");
+    return RKV_OK;
+}
+
+int rkv_bcache_resolve(rkv_bcache *bc, const int32_t *sel, int64_t n_sel, int n_seq, int32_t *rows, void *stream) {
+    if (!bc) return fail(RKV_ERR_ARG, "bc is NULL");
+    if (n_sel < 0 || n_seq < 1 || n_sel * n_seq > ((int64_t)1 << 31) - 1) return fail(RKV_ERR_ARG, "bad n_sel or n_seq");
+    if (n_sel == 0) return RKV_OK;
+    int st;
+    if ((st = check_device_ptr(sel, "sel"))) return st;
+    if (rows && (st = check_device_ptr(rows, "rows"))) return st;
+    hipError_t e = launch_bc_resolve(bc->m, sel, n_sel, n_seq, bc->view_k, bc->view_v, bc->pool_k, bc->pool_v,
+                                     bc->page_size * bc->k_s1, bc->page_size * bc->v_s1, rows,
+                                     static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "block cache resolve");
+    return RKV_OK;
+}
+
+int rkv_bcache_pools(const rkv_bcache *bc, rkv_tensor *k_pool, rkv_tensor *v_pool) {
+    if (!bc || !k_pool || !v_pool) return fail(RKV_ERR_ARG, "NULL argument");
+    const int64_t rows = bc->n_slots * bc->page_size;
+    const int64_t kb = bc->k_type == RKV_TYPE_F16 ? 2 : 34, vb = bc->v_type == RKV_TYPE_F16 ? 2 : 18;
+    *k_pool = rkv_tensor{bc->pool_k, bc->k_type, {bc->d, rows, bc->n_head_kv, 1}, {kb, bc->k_s1, bc->k_row, rows * bc->k_s1}};
+    *v_pool = rkv_tensor{bc->pool_v, bc->v_type, {bc->d, rows, bc->n_head_kv, 1}, {vb, bc->v_s1, bc->v_row, rows * bc->v_s1}};
+    return RKV_OK;
+}
+
+int rkv_bcache_append(rkv_bcache *bc, const void *k_cell, const void *v_cell, int64_t cell, void *stream) {
+    if (!bc || !k_cell || !v_cell) return fail(RKV_ERR_ARG, "NULL argument");
+    if (cell < 0 || cell >= bc->n_cells) return fail(RKV_ERR_ARG, "cell %lld outside the cache", (long long)cell);
+    if (((uintptr_t)k_cell | (uintptr_t)v_cell) % 4 != 0) return fail(RKV_ERR_ARG, "cell data must be 4-byte aligned");
+    int st;
+    if ((st = check_device_ptr(k_cell, "k_cell")) || (st = check_device_ptr(v_cell, "v_cell"))) return st;
+    hipError_t e = launch_bc_append(bc->m, k_cell, v_cell, bc->n_head_kv * bc->k_row, bc->n_head_kv * bc->v_row, cell,
+                                    bc->view_k, bc->view_v, bc->pool_k, bc->pool_v, bc->k_s1, bc->v_s1,
+                                    static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "block cache append");
+    return RKV_OK;
+}
+
+int rkv_bcache_counters(rkv_bcache *bc, rkv_bcache_stats *out) {
+    if (!bc || !out) return fail(RKV_ERR_ARG, "NULL argument");
+    int32_t c[kBcCtl] = {};
+    RKV_HIP(hipDeviceSynchronize());
+    RKV_HIP(hipMemcpy(c, bc->m.ctl, sizeof c, hipMemcpyDeviceToHost));
+    uint64_t u[3];
+    std::memcpy(u, c + 4, sizeof u);
+    out->misses = u[0];
+    out->lookups = u[1];
+    out->calls = u[2];
+    out->epoch = c[0];
+    out->hand = c[1];
+    out->last_misses = c[2];
+    out->overflow = c[3];
+    return RKV_OK;
+}
+
+int rkv_bcache_map(const rkv_bcache *bc, int32_t **page_table, int32_t **slot_page, int64_t *n_pages, int64_t *n_slots) {
+    if (!bc || !page_table || !slot_page || !n_pages || !n_slots) return fail(RKV_ERR_ARG, "NULL argument");
+    *page_table = bc->m.page_table;
+    *slot_page = bc->m.slot_page;
+    *n_pages = bc->m.n_pages;
+    *n_slots = bc->m.n_slots;
     return RKV_OK;
 }
 
