@@ -35,6 +35,8 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense f16 MFMA, vendor figure
 PROFILES = os.path.join(ROOT, "profiles")
 
+LIFT_NAMES = {0: "bulk", 1: "uva", 2: "kernel", 4: "direct"}
+
 METRIC = "decode attn effective KV GB/s (% HBM peak) + tok/s/layer at n_kv=128K"
 
 
@@ -87,13 +89,20 @@ def physical_cores() -> int:
 
 
 # ------------------------------------------------------------------ workloads on device
+_DRAWN = {}
+
+
 def setup(num: int, sets: int, head_dim: int = 128):
     import numpy as np
     import torch
 
     import rkv_inputs as gen
 
-    w = gen.make_workload(num) if head_dim == 128 else gen.make_workload(num, d=head_dim)
+    key = (num, head_dim)
+    if key not in _DRAWN:  # the tail-read contrasts of one workload reuse its draw
+        _DRAWN.clear()
+        _DRAWN[key] = gen.make_workload(num) if head_dim == 128 else gen.make_workload(num, d=head_dim)
+    w = _DRAWN[key]
     rb = lambda t: gen.row_bytes(t, w["d"])
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
@@ -279,49 +288,16 @@ def cpu_baseline(num: int, budget_s: float = 12.0, w=None, softcap: float = 0.0)
 
 
 # ------------------------------------------------------------------ main
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
-    ap.add_argument("--sets", type=int, default=4, help="independent device copies of the KV cache")
-    ap.add_argument("--splits", type=int, default=0)
-    ap.add_argument("--softcap", type=float, default=0.0, help="logit soft-cap c (0: none)")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--head-dim", type=int, default=128, choices=[64, 128, 256],
-                    help="head dim of Q, K and V (64 and 256: decode workloads 1-3 only)")
-    ap.add_argument("--lift-mode", type=int, default=3,
-                    help="0 bulk DMA, 1 word-granularity UVA read, 2 bulk copy kernel on the copy stream, "
-                         "3 automatic (decode: copy kernel, prefill: DMA)")
-    ap.add_argument("--tail-mode", choices=["lift", "host", "auto"], default="lift",
-                    help="host tail: lifted to the GPU in tiles, its partial computed on the host cores, or "
-                         "whichever the measured link and host rates make faster")
-    ap.add_argument("--host-threads", type=int, default=16, help="host threads of the host tail partial")
-    ap.add_argument("--copy-only", action="store_true",
-                    help="only run a plain 1 GiB device copy (calibrates HBM byte counters)")
-    args = ap.parse_args()
-
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (--gpus must be 1).", file=sys.stderr)
-        sys.exit(2)
-
+def measure(args, num):
+    """One workload: warm-up, the timed calls, then an instrumented pass; returns the JSON fields
+    and the workload's host arrays."""
     import torch
 
     import rkv_inputs as gen
     import tiered_kv_cache_split_amd as rkv
 
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    if args.copy_only:
-        gbs = measured_copy_gbs(1 << 30, reps=5)
-        print(json.dumps({"copy_bytes_read": 1 << 30, "copy_bytes_written": 1 << 30, "copy_GBps": round(gbs, 1)}))
-        return
-    if args.head_dim != 128 and args.workload not in (1, 2, 3):
-        print("head dims 64 and 256 are served by the decode path only (workloads 1-3)", file=sys.stderr)
-        sys.exit(2)
-    print(f"[bench] workload {args.workload}: {gen.WORKLOADS[args.workload]['name']} setup", file=sys.stderr,
-          flush=True)
-    st = setup(args.workload, args.sets, args.head_dim)
+    print(f"[bench] workload {num}: {gen.WORKLOADS[num]['name']} setup", file=sys.stderr, flush=True)
+    st = setup(num, args.sets, args.head_dim)
     w = st["w"]
     ctx = rkv.Context(0)
     if args.splits:
@@ -351,7 +327,7 @@ def main():
     for i in range(args.warmup):
         call(ctx, st, i)
     torch.cuda.synchronize()
-    print(f"[bench] warmup done, timing {args.steps} steps", file=sys.stderr, flush=True)
+    print(f"[bench] workload {num}: warmup done, timing {args.steps} steps", file=sys.stderr, flush=True)
 
     # timed region: whole calls only, nothing else on the stream
     torch.cuda.synchronize()
@@ -422,7 +398,7 @@ def main():
                            "kernel": "prefill_seg_kernel (all segments of a step)",
                            "kernel_ms_per_step": round(kern_total_ms, 4)}
     else:
-        name = {2: "decode_seg_q8q4_nkv131072", 4: "decode_seg_rows_f16_pool65536"}.get(args.workload, "")
+        name = {2: "decode_seg_q8q4_nkv131072", 4: "decode_seg_rows_f16_pool65536"}.get(num, "")
         label = DECODE_KERNELS.get(stats.get("kernel_variant"), "decode segment kernel")
         gpu_bytes = kv_bytes - (st["tail_bytes"] if host_tail else 0)  # a host tail partial reads no HBM
         if launches_per_step == 1:
@@ -441,11 +417,17 @@ def main():
         span = sum(t[1] for t in lift_totals) / len(lift_totals)
         h2d = measured_h2d_gbs()
         lift_gbs = st["tail_bytes"] / (tot * 1e-3) / 1e9 if tot > 0 else None
-        out["lift"] = {"mode": {0: "bulk", 1: "uva", 2: "kernel"}[stats["lift_mode"]], "tail_bytes": st["tail_bytes"],
+        out["lift"] = {"mode": LIFT_NAMES[stats["lift_mode"]], "tail_bytes": st["tail_bytes"],
                        "lift_ms_sum": round(tot, 4), "lift_span_ms": round(span, 4),
                        "lift_GBps_overlapped": round(lift_gbs, 2) if lift_gbs else None,
                        "measured_h2d_GBps": round(h2d, 2),
                        "frac_of_measured_h2d": round(lift_gbs / h2d, 4) if lift_gbs else None}
+    if stats.get("lift_mode") == 4 and st.get("tail_bytes"):
+        # no lift: the segment kernels read the pinned tail through its device view; the tail's
+        # own read rate is at least its bytes over all segment-kernel time of a step
+        seg_ms = k_ms / n_inst
+        out["direct_tail"] = {"tail_bytes": st["tail_bytes"], "segment_kernel_ms_per_step": round(seg_ms, 4),
+                              "tail_GBps_at_least": round(st["tail_bytes"] / (seg_ms * 1e-3) / 1e9, 2)}
     if host_tail:
         hm = sorted(host_ms)[len(host_ms) // 2]
         out["host_tail"] = {"tail_bytes": st["tail_bytes"], "threads": args.host_threads, "host_ms_median": round(hm, 4),
@@ -453,11 +435,75 @@ def main():
                             "partial_bytes_uploaded": int(w["n_head"] * w["q"].shape[-2] * (2 + w["d"]) * 4)}
     if tail_choice:
         out["tail_choice"] = tail_choice
+    ctx.close()
+    w = st["w"]
+    del st
+    torch.cuda.empty_cache()
+    return out, w
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--sets", type=int, default=4, help="independent device copies of the KV cache")
+    ap.add_argument("--splits", type=int, default=0)
+    ap.add_argument("--softcap", type=float, default=0.0, help="logit soft-cap c (0: none)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--head-dim", type=int, default=128, choices=[64, 128, 256],
+                    help="head dim of Q, K and V (64 and 256: decode workloads 1-3 only)")
+    ap.add_argument("--lift-mode", type=int, default=3,
+                    help="0 bulk DMA, 1 word-granularity UVA read, 2 bulk copy kernel on the copy stream, "
+                         "3 automatic (decode: copy kernel, prefill: DMA)")
+    ap.add_argument("--tail-mode", choices=["lift", "host", "auto"], default="lift",
+                    help="host tail: lifted to the GPU in tiles, its partial computed on the host cores, or "
+                         "whichever the measured link and host rates make faster")
+    ap.add_argument("--host-threads", type=int, default=16, help="host threads of the host tail partial")
+    ap.add_argument("--no-secondary", dest="secondary", action="store_false",
+                    help="headline workload only (default: workloads 1, 3, 4 and 5 and the tail-read contrasts "
+                         "of workload 3 follow in the same run, under \"secondary\")")
+    ap.add_argument("--secondary-steps", type=int, default=30)
+    ap.add_argument("--copy-only", action="store_true",
+                    help="only run a plain 1 GiB device copy (calibrates HBM byte counters)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (--gpus must be 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import rkv_inputs as gen
+    import tiered_kv_cache_split_amd as rkv
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_only:
+        gbs = measured_copy_gbs(1 << 30, reps=5)
+        print(json.dumps({"copy_bytes_read": 1 << 30, "copy_bytes_written": 1 << 30, "copy_GBps": round(gbs, 1)}))
+        return
+    if args.head_dim != 128 and args.workload not in (1, 2, 3):
+        print("head dims 64 and 256 are served by the decode path only (workloads 1-3)", file=sys.stderr)
+        sys.exit(2)
+    out, w = measure(args, args.workload)
+    if args.secondary and args.workload == 2 and args.head_dim == 128 and not args.softcap:
+        # the other configurations, timed in the same run (fewer steps; the headline stays config 2)
+        sec = {}
+        base = dict(vars(args))
+        for num, over, key in ((1, {}, None), (3, {}, None), (3, {"lift_mode": 0}, "lift_dma"),
+                               (3, {"lift_mode": 4}, "direct_tail_read"), (4, {}, None), (5, {}, None)):
+            a2 = argparse.Namespace(**{**base, "steps": args.secondary_steps, "warmup": 5, "sets": 2, **over})
+            r, _ = measure(a2, num)
+            name = gen.WORKLOADS[num]["name"] + (f"_{key}" if key else "")
+            sec[name] = {k: r[k] for k in ("value", "unit", "ms_per_step", "tok_per_s_per_layer", "config", "roofline",
+                                           "lift", "direct_tail", "segment_launches_per_step") if k in r}
+            sec[name]["steps"] = a2.steps
+        out["secondary"] = sec
     out["measured_copy_GBps"] = round(measured_copy_gbs(), 1)
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host cores", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(args.workload, w=w, softcap=args.softcap)
-    ctx.close()
     print(json.dumps(out), flush=True)
 
 

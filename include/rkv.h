@@ -77,9 +77,14 @@ enum rkv_lift_mode {
     RKV_LIFT_KERNEL = 2,/* a copy kernel on the copy stream (at most 64 workgroups) reads the
                            pinned bytes 8 at a time: no hand-off between a DMA engine and the
                            compute queue, which dominates small lifts                        */
-    RKV_LIFT_AUTO = 3   /* default: decode lifts with the copy kernel, prefill with the DMA
+    RKV_LIFT_AUTO = 3,  /* default: decode lifts with the copy kernel, prefill with the DMA
                            engine (the copy kernel's workgroups would slow the MFMA kernel
                            it overlaps)                                                      */
+    RKV_LIFT_DIRECT = 4 /* contrast only (patch 0102, commit message: the kernel reading the
+                           pinned tail at word granularity): no lift; the segment kernels read
+                           a pinned tail in place through its device view, in their own
+                           access order; a device tail and the host tail partial are
+                           unaffected                                                        */
 };
 
 enum rkv_residency_mode {

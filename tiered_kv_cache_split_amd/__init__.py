@@ -14,7 +14,7 @@ from __future__ import annotations
 
 import ctypes
 
-from ._lib import (RKV_LIFT_AUTO, RKV_LIFT_BULK, RKV_LIFT_KERNEL, RKV_LIFT_UVA, RKV_RESIDENCY_AUTO, RKV_RESIDENCY_RESIDENT,  # noqa: F401
+from ._lib import (RKV_LIFT_AUTO, RKV_LIFT_BULK, RKV_LIFT_DIRECT, RKV_LIFT_KERNEL, RKV_LIFT_UVA, RKV_RESIDENCY_AUTO, RKV_RESIDENCY_RESIDENT,  # noqa: F401
                    RKV_RESIDENCY_WINDOW, RKV_TAIL_HOST, RKV_DQ_DECODE_MMA, RKV_DQ_PREFILL, RKV_DQ_VECTOR, RKV_DQ_HEAD_DIM, RKV_TAIL_LIFT, RKV_TYPE_F16, RKV_TYPE_F32, RKV_TYPE_Q4_0,
                    RKV_TYPE_Q8_0, RKV_ERR_ARG, RKV_ERR_UNSUPPORTED, RkvError,
                    RkvBcacheCounters, RkvStats, RkvTensor, check, load)

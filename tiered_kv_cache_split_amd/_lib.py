@@ -9,7 +9,7 @@ LIB_PATH = os.path.join(_HERE, "librkv.so")
 
 RKV_TYPE_F32, RKV_TYPE_F16, RKV_TYPE_Q4_0, RKV_TYPE_Q8_0 = 0, 1, 2, 8
 RKV_OK, RKV_ERR_ARG, RKV_ERR_UNSUPPORTED, RKV_ERR_HIP, RKV_ERR_NOMEM, RKV_ERR_CAPTURE = 0, -1, -2, -3, -4, -5
-RKV_LIFT_BULK, RKV_LIFT_UVA, RKV_LIFT_KERNEL, RKV_LIFT_AUTO = 0, 1, 2, 3
+RKV_LIFT_BULK, RKV_LIFT_UVA, RKV_LIFT_KERNEL, RKV_LIFT_AUTO, RKV_LIFT_DIRECT = 0, 1, 2, 3, 4
 RKV_RESIDENCY_AUTO, RKV_RESIDENCY_RESIDENT, RKV_RESIDENCY_WINDOW = 0, 1, 2
 RKV_TAIL_LIFT, RKV_TAIL_HOST = 0, 1
 RKV_DQ_DECODE_MMA, RKV_DQ_PREFILL, RKV_DQ_VECTOR, RKV_DQ_HEAD_DIM = 0, 1, 2, 3

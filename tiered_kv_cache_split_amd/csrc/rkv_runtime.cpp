@@ -569,7 +569,10 @@ int attn_window_tail(rkv_ctx *ctx, const rkv_tensor *q, const rkv_tensor *k_win,
     // partial computed on the host cores)
     const bool host_tail = n_tail > 0 && tail_kind != Mem::Device && ctx->tail_mode == RKV_TAIL_HOST && !mfma;
     if (host_tail && d != kHeadDim) return fail(RKV_ERR_UNSUPPORTED, "the host tail partial takes head dim 128");
-    const bool lifted = n_tail > 0 && tail_kind == Mem::PinnedHost && !host_tail;
+    // RKV_LIFT_DIRECT (contrast only): the segment kernels read a pinned tail in place through
+    // its device view, in their own access order, with no lift
+    const bool direct = n_tail > 0 && tail_kind == Mem::PinnedHost && !host_tail && ctx->lift_mode == RKV_LIFT_DIRECT;
+    const bool lifted = n_tail > 0 && tail_kind == Mem::PinnedHost && !host_tail && !direct;
     const int64_t n_tiles = lifted ? (n_tail + tile_kv - 1) / tile_kv : 0;
     TailGeom gk{}, gv{};
     int n_slots = 0;
@@ -586,9 +589,20 @@ int attn_window_tail(rkv_ctx *ctx, const rkv_tensor *q, const rkv_tensor *k_win,
     if (wc > 0)
         win = Seg{static_cast<const uint8_t *>(k_win->data), static_cast<const uint8_t *>(v_win->data),
                   k_win->nb[1], k_win->nb[2], v_win->nb[1], v_win->nb[2], wc, 0};
-    if (n_tail > 0 && !lifted)
-        dtail = Seg{static_cast<const uint8_t *>(k_tail->data), static_cast<const uint8_t *>(v_tail->data),
-                    k_tail->nb[1], k_tail->nb[2], v_tail->nb[1], v_tail->nb[2], n_tail, wc};
+    if (n_tail > 0 && !lifted) {
+        const uint8_t *tk = static_cast<const uint8_t *>(k_tail->data), *tv = static_cast<const uint8_t *>(v_tail->data);
+        if (direct) {
+            void *vk = nullptr, *vv = nullptr;
+            if (hipHostGetDevicePointer(&vk, const_cast<void *>(k_tail->data), 0) != hipSuccess ||
+                hipHostGetDevicePointer(&vv, const_cast<void *>(v_tail->data), 0) != hipSuccess) {
+                (void)hipGetLastError();
+                return fail(RKV_ERR_HIP, "no device view of the pinned tail");
+            }
+            tk = static_cast<const uint8_t *>(vk);
+            tv = static_cast<const uint8_t *>(vv);
+        }
+        dtail = Seg{tk, tv, k_tail->nb[1], k_tail->nb[2], v_tail->nb[1], v_tail->nb[2], n_tail, wc};
+    }
     // tile t of the lifted tail, read from ring slot t % n_slots (the ring keeps the tail's
     // cell layout; a head-major tail gets head planes of cap_cells cells)
     auto tile_seg = [&](int64_t t) {
@@ -636,7 +650,10 @@ int attn_window_tail(rkv_ctx *ctx, const rkv_tensor *q, const rkv_tensor *k_win,
     ctx->stats.kernel_variant = mfma ? RKV_KERNEL_PREFILL_MFMA : RKV_KERNEL_DECODE_HEAD;
     // lift mode of this call: the automatic choice lifts decode tails with the copy kernel and
     // prefill tails with the DMA engine
-    const int lift_mode = ctx->lift_mode == RKV_LIFT_AUTO ? (mfma ? RKV_LIFT_BULK : RKV_LIFT_KERNEL) : ctx->lift_mode;
+    const int lift_mode = direct ? RKV_LIFT_DIRECT
+                                 : (ctx->lift_mode == RKV_LIFT_AUTO || ctx->lift_mode == RKV_LIFT_DIRECT)
+                                       ? (mfma ? RKV_LIFT_BULK : RKV_LIFT_KERNEL)
+                                       : ctx->lift_mode;
     ctx->stats.lift_mode = lift_mode;
     int slot = 0;
 
@@ -1073,7 +1090,8 @@ int rkv_get_stats(const rkv_ctx *ctx, rkv_stats *out) {
 
 int rkv_set_lift_mode(rkv_ctx *ctx, int mode) {
     if (!ctx) return fail(RKV_ERR_ARG, "ctx is NULL");
-    if (mode != RKV_LIFT_BULK && mode != RKV_LIFT_UVA && mode != RKV_LIFT_KERNEL && mode != RKV_LIFT_AUTO)
+    if (mode != RKV_LIFT_BULK && mode != RKV_LIFT_UVA && mode != RKV_LIFT_KERNEL && mode != RKV_LIFT_AUTO &&
+        mode != RKV_LIFT_DIRECT)
         return fail(RKV_ERR_ARG, "unknown lift mode %d", mode);
     ctx->lift_mode = mode;
     return RKV_OK;
