@@ -16,8 +16,9 @@
 //        W = p * d_V folds the per-key block scale of V into the binary16 weights.  V^T comes
 //        from one ds_read_b64_tr_b8 per block: a lane receives one byte position of eight
 //        keys, whose low and high nibbles are the elements e and e + 16 of the block.  The low
-//        nibble enters as exact 1024 + n, the high one in place as 1024 + 16 n; sum W (kept
-//        per V block) removes the offsets 1032 and 1152 at the end (n - 8 is the value).
+//        nibble enters as exact 1024 + n, the high one in place as 1024 + 16 n; one more MFMA
+//        per tile with a constant A of -1032 (or -1152) removes the offset from the same
+//        accumulator, so the tiles hold n - 8 (and 16 (n - 8)) times the weights.
 //
 // Workgroup = HW (8) waves for one (split, head group, sequence), wave w = KV head g0 + w, as in
 // the vector cell-major kernel.  A 32-cell chunk is one contiguous span of each cache, moved
@@ -67,16 +68,18 @@ __device__ __forceinline__ float row16_sum(float x) {
     return x;
 }
 
-// One chunk in registers: the thread's half of one head's q8_0 K row (two blocks, 68 bytes as
-// seventeen words) and of its q4_0 V row (two blocks, 36 bytes as nine words).
+// One chunk in registers: the thread's half of one head's q8_0 K row (two blocks, 68 bytes:
+// bytes 0..35 as nine words, the second block's aligned codes 36..67 as two quads) and of its
+// q4_0 V row (two blocks, 36 bytes: bytes 0..19 as five words, the second block's aligned data
+// 20..35 as one quad).  The aligned quads go to LDS as loaded.
 template <int HW>
 struct Stage {
     static constexpr int kNT = 64 * HW;
     static constexpr int kTpc = kNT / kCh;  // threads per cell
-    uint4 k[4];
-    uint32_t k4;
+    uint4 ka0, ka1, kb0, kb1;
+    uint32_t kx;
     uint4 va, vb;
-    uint32_t vc;
+    uint32_t vx;
 };
 
 // CAP: the logit soft-cap is on (a separate instantiation, so the plain path carries none of it)
@@ -137,40 +140,39 @@ decode_mma_kernel(const SegParams p) {
             (void *)(kbase + c0 * p.k_s1), (short)0, (int)(nv * p.k_s1), 0x00020000);
         const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
             (void *)(vbase + c0 * p.v_s1), (short)0, (int)(nv * p.v_s1), 0x00020000);
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-            st.k[m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, gkb + 16 * m, 0, 0));
-        st.k4 = __builtin_amdgcn_raw_buffer_load_b32(rk, gkb + 64, 0, 0);
+        st.ka0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, gkb, 0, 0));
+        st.ka1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, gkb + 16, 0, 0));
+        st.kx = __builtin_amdgcn_raw_buffer_load_b32(rk, gkb + 32, 0, 0);
+        st.kb0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, gkb + 36, 0, 0));
+        st.kb1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, gkb + 52, 0, 0));
         st.va = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, gvb, 0, 0));
-        st.vb = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, gvb + 16, 0, 0));
-        st.vc = __builtin_amdgcn_raw_buffer_load_b32(rv, gvb + 32, 0, 0);
+        st.vx = __builtin_amdgcn_raw_buffer_load_b32(rv, gvb + 16, 0, 0);
+        st.vb = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, gvb + 20, 0, 0));
     };
     auto stash = [&](const St &st, int buf) __attribute__((always_inline)) {
-        // K: words x0 .. x16; the first block's codes start 2 bytes into the words (its scale is
-        // the low half of x0), the second block's scale is the high half of x8 and its codes
-        // x9 .. x16 are aligned
-        const uint32_t x[17] = {st.k[0].x, st.k[0].y, st.k[0].z, st.k[0].w, st.k[1].x, st.k[1].y,
-                                st.k[1].z, st.k[1].w, st.k[2].x, st.k[2].y, st.k[2].z, st.k[2].w,
-                                st.k[3].x, st.k[3].y, st.k[3].z, st.k[3].w, st.k4};
+        // K: words x0 .. x8 (bytes 0..35); the first block's codes start 2 bytes into them (its
+        // scale is the low half of x0), the second block's scale is the high half of x8
+        const uint32_t x[9] = {st.ka0.x, st.ka0.y, st.ka0.z, st.ka0.w, st.ka1.x, st.ka1.y, st.ka1.z, st.ka1.w, st.kx};
         uint32_t ca[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) ca[i] = __builtin_amdgcn_alignbyte(x[i + 1], x[i], 2);
         uint8_t *kd = s_k + buf * kBk;
         *reinterpret_cast<uint4 *>(kd + lkb) = make_uint4(ca[0], ca[1], ca[2], ca[3]);
         *reinterpret_cast<uint4 *>(kd + kKp + lkb) = make_uint4(ca[4], ca[5], ca[6], ca[7]);
-        *reinterpret_cast<uint4 *>(kd + lkb + 16 * kTpc) = make_uint4(x[9], x[10], x[11], x[12]);
-        *reinterpret_cast<uint4 *>(kd + kKp + lkb + 16 * kTpc) = make_uint4(x[13], x[14], x[15], x[16]);
+        *reinterpret_cast<uint4 *>(kd + lkb + 16 * kTpc) = st.kb0;
+        *reinterpret_cast<uint4 *>(kd + kKp + lkb + 16 * kTpc) = st.kb1;
         *reinterpret_cast<uint16_t *>(kd + lks) = (uint16_t)x[0];
         *reinterpret_cast<uint16_t *>(kd + lks + 2 * kCh) = (uint16_t)(x[8] >> 16);
-        // V: the first block's data starts 2 bytes into the words, the second's is aligned
+        // V: the first block's data starts 2 bytes into va, vx (its scale is the low half of
+        // va.x, the second block's the high half of vx); the second block's data is vb
         uint8_t *vd = s_v + buf * kBv;
         *reinterpret_cast<uint4 *>(vd + lvb) = make_uint4(__builtin_amdgcn_alignbyte(st.va.y, st.va.x, 2),
                                                           __builtin_amdgcn_alignbyte(st.va.z, st.va.y, 2),
                                                           __builtin_amdgcn_alignbyte(st.va.w, st.va.z, 2),
-                                                          __builtin_amdgcn_alignbyte(st.vb.x, st.va.w, 2));
-        *reinterpret_cast<uint4 *>(vd + lvb + 16 * kTpc) = make_uint4(st.vb.y, st.vb.z, st.vb.w, st.vc);
+                                                          __builtin_amdgcn_alignbyte(st.vx, st.va.w, 2));
+        *reinterpret_cast<uint4 *>(vd + lvb + 16 * kTpc) = st.vb;
         *reinterpret_cast<uint16_t *>(vd + lvs) = (uint16_t)st.va.x;
-        *reinterpret_cast<uint16_t *>(vd + lvs + 2 * kCh) = (uint16_t)(st.vb.x >> 16);
+        *reinterpret_cast<uint16_t *>(vd + lvs + 2 * kCh) = (uint16_t)(st.vx >> 16);
     };
 
     // Lane (col, grp) owns query row `col` (rows >= R are padding and never written) and, within
@@ -178,13 +180,15 @@ decode_mma_kernel(const SegParams p) {
     // accumulators hold O^T[d][col] for d = 16*dt + 4*grp + e, so the softmax state of a row lives
     // in the four lanes col, col + 16, col + 32, col + 48 and never crosses LDS.
     float4_t oacc[8];
-    float swacc[4];        // sum of the weights W of this lane's keys, per V block
     float mrow = -INFINITY, lrow = 0.f;  // running max (log2 domain) and this lane's part of the sum
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) oacc[dt] = float4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int blk = 0; blk < 4; ++blk) swacc[blk] = 0.f;
-    const half2_t ones = {(_Float16)1.0f, (_Float16)1.0f};
+    // A operands that remove the nibble offsets inside the P.V MFMAs: every entry -1032 (low
+    // nibbles) or -1152 (high nibbles), so each output gains -offset * (sum of its weights)
+    const half8_t bias_lo = {(_Float16)-kMagicV, (_Float16)-kMagicV, (_Float16)-kMagicV, (_Float16)-kMagicV,
+                             (_Float16)-kMagicV, (_Float16)-kMagicV, (_Float16)-kMagicV, (_Float16)-kMagicV};
+    const half8_t bias_hi = {(_Float16)-kMagicVHi, (_Float16)-kMagicVHi, (_Float16)-kMagicVHi, (_Float16)-kMagicVHi,
+                             (_Float16)-kMagicVHi, (_Float16)-kMagicVHi, (_Float16)-kMagicVHi, (_Float16)-kMagicVHi};
     // kept in a register so that mask-and-insert compiles to one v_and_or_b32 (two literals
     // cannot share an instruction)
     uint32_t vmagic = 0x64006400u;
@@ -312,11 +316,11 @@ decode_mma_kernel(const SegParams p) {
         // ---- online softmax of row `col` (exact: the max is raised whenever a chunk exceeds it)
         float mx;
         if (cc >= 0.f)
-            mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
-                       fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+            mx = max3_nn(max3_nn(s[0][0], s[0][1], s[0][2]), max3_nn(s[0][3], s[1][0], s[1][1]),
+                         max2_nn(s[1][2], s[1][3]));
         else
-            mx = -fminf(fminf(fminf(s[0][0], s[0][1]), fminf(s[0][2], s[0][3])),
-                        fminf(fminf(s[1][0], s[1][1]), fminf(s[1][2], s[1][3])));
+            mx = -min3_nn(min3_nn(s[0][0], s[0][1], s[0][2]), min3_nn(s[0][3], s[1][0], s[1][1]),
+                          -max2_nn(-s[1][2], -s[1][3]));
         const float mt = fold_rows_max(mx) * (cc >= 0.f ? cc : -cc);
         if (__builtin_amdgcn_ballot_w64(mt > mrow)) {
             const float mnew = fmaxf(mt, mrow);
@@ -325,8 +329,6 @@ decode_mma_kernel(const SegParams p) {
             lrow *= a;
 #pragma unroll
             for (int dt = 0; dt < 8; ++dt) oacc[dt] *= a;
-#pragma unroll
-            for (int blk = 0; blk < 4; ++blk) swacc[blk] *= a;
         }
         const float msub = mrow == -INFINITY ? 0.f : mrow;
         half2_t pk[4];  // P of P.V slots 8*grp + 2u, 2u + 1 (keys 16*(u/2) + 4*grp + 2*(u%2) + 0, 1)
@@ -347,10 +349,6 @@ decode_mma_kernel(const SegParams p) {
             const uint4 wu = make_uint4(u32v(pk[0] * h2v(dv.x)), u32v(pk[1] * h2v(dv.y)),
                                         u32v(pk[2] * h2v(dv.z)), u32v(pk[3] * h2v(dv.w)));
             const half8_t wf = __builtin_bit_cast(half8_t, wu);
-            swacc[blk] = __builtin_amdgcn_fdot2(h2v(wu.x), ones, swacc[blk], false);
-            swacc[blk] = __builtin_amdgcn_fdot2(h2v(wu.y), ones, swacc[blk], false);
-            swacc[blk] = __builtin_amdgcn_fdot2(h2v(wu.z), ones, swacc[blk], false);
-            swacc[blk] = __builtin_amdgcn_fdot2(h2v(wu.w), ones, swacc[blk], false);
             const int2_t bt = btr[blk];
             uint32_t lo[4], hi[4];
 #pragma unroll
@@ -362,6 +360,8 @@ decode_mma_kernel(const SegParams p) {
                 __builtin_bit_cast(half8_t, make_uint4(lo[0], lo[1], lo[2], lo[3])), wf, oacc[2 * blk], 0, 0, 0);
             oacc[2 * blk + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
                 __builtin_bit_cast(half8_t, make_uint4(hi[0], hi[1], hi[2], hi[3])), wf, oacc[2 * blk + 1], 0, 0, 0);
+            oacc[2 * blk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bias_lo, wf, oacc[2 * blk], 0, 0, 0);
+            oacc[2 * blk + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bias_hi, wf, oacc[2 * blk + 1], 0, 0, 0);
         }
     };
 
@@ -386,8 +386,6 @@ decode_mma_kernel(const SegParams p) {
 
     // ---- partial of row `col`: the sums are folded over the four lanes of the row
     const float S = fold_rows(lrow);
-#pragma unroll
-    for (int blk = 0; blk < 4; ++blk) swacc[blk] = fold_rows(swacc[blk]);
     if (col < R) {
         const int r = col % p.gqa, i = col / p.gqa;
         const int64_t row = (g * p.gqa + r) + (int64_t)p.n_head * (i + (int64_t)p.n_q * b);
@@ -396,13 +394,12 @@ decode_mma_kernel(const SegParams p) {
             out[0] = (mrow == -INFINITY) ? -INFINITY : mrow * kLn2;
             out[1] = S;
         }
-        // low nibbles: O = acc - 1032 sum W; high nibbles: O = (acc - 1152 sum W) / 16
+        // low nibbles: O = acc; high nibbles (16 (n - 8) after the offset): O = acc / 16
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                out[2 + 16 * dt + 4 * grp + e] = (dt & 1) ? fmaf(-kMagicVHi, swacc[dt >> 1], oacc[dt][e]) * 0.0625f
-                                                          : fmaf(-kMagicV, swacc[dt >> 1], oacc[dt][e]);
+                out[2 + 16 * dt + 4 * grp + e] = (dt & 1) ? oacc[dt][e] * 0.0625f : oacc[dt][e];
     }
 }
 

@@ -26,6 +26,24 @@ __device__ __forceinline__ float dpp_f(float x) {
 }
 inline constexpr int kQuadSwap1 = 0xB1, kQuadSwap2 = 0x4E, kRowRor4 = 0x124, kRowRor8 = 0x128;
 
+// Max and min of scores, which are never NaN (finite or -inf): plain v_max/v_min, without the
+// quieting of NaN operands that fmaxf / fminf add in IEEE mode.
+__device__ __forceinline__ float max2_nn(float a, float b) {
+    float r;
+    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+__device__ __forceinline__ float max3_nn(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+__device__ __forceinline__ float min3_nn(float a, float b, float c) {
+    float r;
+    asm("v_min3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
 // Value of lane k summed over the four 16-lane rows, in every row.
 __device__ __forceinline__ float fold_rows(float x) {
     const int xi = __builtin_bit_cast(int, x);
@@ -36,14 +54,14 @@ __device__ __forceinline__ float fold_rows(float x) {
     return __builtin_bit_cast(float, (int)r32[0]) + __builtin_bit_cast(float, (int)r32[1]);
 }
 
-// Max of lane k over the four 16-lane rows, in every row.
+// Max of lane k over the four 16-lane rows, in every row (x never NaN).
 __device__ __forceinline__ float fold_rows_max(float x) {
     const int xi = __builtin_bit_cast(int, x);
     const auto r16 = __builtin_amdgcn_permlane16_swap(xi, xi, false, false);
-    x = fmaxf(__builtin_bit_cast(float, (int)r16[0]), __builtin_bit_cast(float, (int)r16[1]));
+    x = max2_nn(__builtin_bit_cast(float, (int)r16[0]), __builtin_bit_cast(float, (int)r16[1]));
     const int yi = __builtin_bit_cast(int, x);
     const auto r32 = __builtin_amdgcn_permlane32_swap(yi, yi, false, false);
-    return fmaxf(__builtin_bit_cast(float, (int)r32[0]), __builtin_bit_cast(float, (int)r32[1]));
+    return max2_nn(__builtin_bit_cast(float, (int)r32[0]), __builtin_bit_cast(float, (int)r32[1]));
 }
 
 // Soft-capped score in the exp2 domain, l2 * tanh(cs * qk), with tanh(y) = 1 - 2 / (e^{2y} + 1):
