@@ -101,9 +101,11 @@ def setup(num: int, sets: int, head_dim: int = 128):
     key = (num, head_dim)
     if key not in _DRAWN:  # the tail-read contrasts of one workload reuse its draw
         _DRAWN.clear()
-        _DRAWN[key] = gen.make_workload(num) if head_dim == 128 else gen.make_workload(num, d=head_dim)
+        _DRAWN[key] = gen.make_workload(num) if head_dim == 128 else \
+            gen.make_workload(num, d=head_dim, dv=512 if head_dim == 576 else head_dim)
     w = _DRAWN[key]
-    rb = lambda t: gen.row_bytes(t, w["d"])
+    dv = w.get("dv", w["d"])
+    rb = lambda t, dd=w["d"]: gen.row_bytes(t, dd)
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
     def pinned(a):
@@ -132,9 +134,9 @@ def setup(num: int, sets: int, head_dim: int = 128):
     if w["n_kv"] > wc:
         st["tail"] = (pinned(w["k"][wc:]), pinned(w["v"][wc:]))
     n_head, n_q = w["n_head"], w["q"].shape[1]
-    st["o"] = torch.empty((n_q, n_head, w["d"]), dtype=torch.float32, device="cuda")
+    st["o"] = torch.empty((n_q, n_head, dv), dtype=torch.float32, device="cuda")
     st["lse"] = torch.empty((n_q, n_head), dtype=torch.float32, device="cuda")
-    per_cell = w["n_head_kv"] * (rb(w["k_type"]) + rb(w["v_type"]))
+    per_cell = w["n_head_kv"] * (rb(w["k_type"]) + rb(w["v_type"], dv))
     st["kv_bytes"] = w["n_kv"] * per_cell
     st["tail_bytes"] = (w["n_kv"] - wc) * per_cell
     st["window_bytes"] = wc * per_cell
@@ -236,7 +238,7 @@ def cpu_baseline(num: int, budget_s: float = 12.0, w=None, softcap: float = 0.0)
             return int((rows >= 0).sum())
         full_units, unit_bytes = total_cells, per_cell
     else:
-        per_cell = w["n_head_kv"] * (gen.row_bytes(w["k_type"], w["d"]) + gen.row_bytes(w["v_type"], w["d"]))
+        per_cell = w["n_head_kv"] * (gen.row_bytes(w["k_type"], w["d"]) + gen.row_bytes(w["v_type"], w.get("dv", w["d"])))
         q = oracle.q_values(w["q"])
         n_q = w["q"].shape[1]
         if w["kind"] == "prefill":
@@ -377,7 +379,7 @@ def measure(args, num):
         "dtype": "f16",  # matrix-core operands (q8_0/q4_0 codes as exact binary16 integers)
         "accum_dtype": "f32",  # accumulation, softmax and partials
         "data": "synthetic",
-        "config": {"workload": w["name"], "n_head": w["n_head"], "n_head_kv": w["n_head_kv"], "head_dim": w["d"],
+        "config": {"workload": w["name"], "n_head": w["n_head"], "n_head_kv": w["n_head_kv"], "head_dim": w["d"], **({"head_dim_v": w["dv"]} if w.get("dv", w["d"]) != w["d"] else {}),
                    "n_q": int(w["q"].shape[-2]), "n_kv": int(w["n_kv"]),
                    "k_type": gen.TYPE_NAMES[w["k_type"]], "v_type": gen.TYPE_NAMES[w["v_type"]],
                    "kv_sets_rotated": args.sets, "parallelism": "single GPU",
@@ -452,8 +454,9 @@ def main():
     ap.add_argument("--splits", type=int, default=0)
     ap.add_argument("--softcap", type=float, default=0.0, help="logit soft-cap c (0: none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--head-dim", type=int, default=128, choices=[64, 128, 256],
-                    help="head dim of Q, K and V (64 and 256: decode workloads 1-3 only)")
+    ap.add_argument("--head-dim", type=int, default=128, choices=[64, 128, 256, 512, 576],
+                    help="head dim of Q and K; V takes the same, or 512 with 576 (other than 128: decode "
+                         "workloads 1-3 only)")
     ap.add_argument("--lift-mode", type=int, default=3,
                     help="0 bulk DMA, 1 word-granularity UVA read, 2 bulk copy kernel on the copy stream, "
                          "3 automatic (decode: copy kernel, prefill: DMA)")

@@ -18,13 +18,15 @@
  * Tensors are described ggml-style: ne[0] is the fastest dimension, nb[] are byte
  * strides, nb[0] is the element (or quant block) size.  Rows of head_dim values must be
  * contiguous (nb[0] == type size).  Supported: head_dim == dv == 128 everywhere, and
- * head_dim == dv in {64, 256} for rkv_attn_decode (device window + device or lifted
- * tail, vector kernel) and rkv_lse_merge; Q in F16;
+ * for rkv_attn_decode (device window + device or lifted tail, vector kernel) also
+ * head_dim == dv in {64, 256, 512} and head_dim 576 with dv 512 (patch 0070, fattn.cu:
+ * the streaming op's supported head dims); rkv_lse_merge takes dv 64, 128, 256 or 512;
+ * Q in F16;
  * K in F16 or Q8_0; V in F16 or Q4_0.  Q8_0 is a 34-byte block (binary16 scale d, 32
  * int8 codes q; value d*q).  Q4_0 is an 18-byte block (binary16 scale d, 16 bytes; byte
  * j holds element j in its low nibble and element j+16 in its high nibble; value
  * d*(n-8)).  K/V data pointers and their nb[1], nb[2] must be multiples of 8 bytes (of 4
- * bytes for head dims 64 and 256); Q pointers and strides multiples of 4 bytes.
+ * bytes for head dims other than 128); Q pointers and strides multiples of 4 bytes.
  *
  *   score s_j = scale * <q, k_j> + mask[j]   (mask additive binary16, -inf hides;
  *                                             column j is the GLOBAL key position)
@@ -127,7 +129,7 @@ enum rkv_kernel_variant {
     RKV_KERNEL_DECODE_CELL_MFMA = 3,  /* matrix-core decode over eight cell-major q8_0/q4_0 heads   */
     RKV_KERNEL_DECODE_CELL_MFMA16 = 4, /* persistent matrix-core decode over eight binary16 heads
                                           (windows, tail tiles, row lists)                         */
-    RKV_KERNEL_DECODE_HD = 5           /* vector decode for head dims 64 and 256 (window + tail)   */
+    RKV_KERNEL_DECODE_HD = 5           /* vector decode for head dims other than 128 (window + tail) */
 };
 
 /* ---- context ---------------------------------------------------------------------- */
@@ -182,9 +184,10 @@ int rkv_kernel_timing_ms(rkv_ctx *ctx, float *total_ms, int *n_launches);
 /* Decode attention over a window + tail split (patch 0070, ggml_streaming_flash_attn_window:
  * window K/V in one pair of sources, tail K/V in another, a NULL tail meaning one region;
  * tiles never straddle wc; the mask is sliced at the global position).
- * Shown for head_dim 128; head_dim 64 or 256 (Q, K and V alike) takes the same arguments
- * with that leading extent, except the host tail partial (RKV_TAIL_HOST), which is
- * RKV_ERR_UNSUPPORTED for them.
+ * Shown for head_dim 128; head_dim 64, 256 or 512 (Q, K and V alike), or 576 for Q and K
+ * with 512 for V (o then [512, n_head, n_q]), takes the same arguments with those leading
+ * extents, except the host tail partial (RKV_TAIL_HOST), which is RKV_ERR_UNSUPPORTED for
+ * them; any other pair of head dims is RKV_ERR_UNSUPPORTED.
  *   q       F16 [128, n_q, n_head, 1], device.  n_q * (n_head/n_head_kv) <= 8.
  *   k_win   [128, >= wc, n_head_kv, 1] device (cells [0, wc) are used); NULL iff wc == 0.
  *   v_win   as k_win with V's type.
@@ -261,7 +264,7 @@ int rkv_attn_partial(rkv_ctx *ctx, const rkv_tensor *q, const rkv_tensor *k,
 /* Log-sum-exp merge (patch 0070 streaming_combine_kernel; the tail-partial rule of
  * tail_partial_to_tile_kernel): partials float32 [n_seg][n_rows][2 + dv] on the device
  * -> o float32 [dv, n_rows] and lse float32 [n_rows] (lse may be NULL).  Rows whose
- * segments are all empty get O = 0 and LSE = -inf.  dv is 64, 128 or 256 (otherwise
+ * segments are all empty get O = 0 and LSE = -inf.  dv is 64, 128, 256 or 512 (otherwise
  * RKV_ERR_UNSUPPORTED).  No context needed. */
 int rkv_lse_merge(const float *partials, int n_seg, int64_t n_rows, int dv,
                   float *o, float *lse, void *stream);

@@ -237,10 +237,11 @@ def make_workload(num: int, scale_down: int = 1, **over):
     n_kv = w["n_kv"] // sd
     wc = min(n_kv, w["wc"] // sd)
     tile = max(1, w["tile_kv"] // sd)
-    q, k, v = draw_qkv(rng, w["n_head"], w["n_q"], w["n_head_kv"], n_kv, w["d"], w["d"],
+    dv = w.get("dv", w["d"])  # V head dim (differs from Q/K's only in the 576/512 pair)
+    q, k, v = draw_qkv(rng, w["n_head"], w["n_q"], w["n_head_kv"], n_kv, w["d"], dv,
                        w["k_type"], w["v_type"])
     w.update(n_kv=n_kv, wc=wc, tile_kv=tile, q=q, k=k, v=v, scale=1.0 / np.sqrt(w["d"]),
-             mask=None)
+             mask=None, dv=dv)
     if w["kind"] == "prefill":
         w["q_pos0"] = n_kv - w["n_q"]
     return w

@@ -120,7 +120,7 @@ class Runner:
         if mask is not None:
             tensors["m"] = dev(np.asarray(mask, dtype=np.float16))
             md = rkv.mask_desc(tensors["m"])
-        o = torch.empty((n_q, n_head, w.get("d", 128)), dtype=torch.float32, device="cuda")
+        o = torch.empty((n_q, n_head, w.get("dv", w.get("d", 128))), dtype=torch.float32, device="cuda")
         lse = torch.empty((n_q, n_head), dtype=torch.float32, device="cuda")
         if prefill:
             self.ctx.attn_prefill(rkv.q_desc(q), kd, vd, ktd, vtd, md, wc, tile_kv, w["scale"], q_pos0, o, lse,

@@ -63,8 +63,9 @@ def test_null_context_is_an_argument_error(lib):
 
 def test_merge_rejects_bad_sizes_before_device_work(lib):
     from tiered_kv_cache_split_amd import _lib
-    for dv in (32, 96, 512):  # head dims other than 64, 128 and 256
+    for dv in (32, 96, 576, 1024):  # value widths other than 64, 128, 256 and 512
         assert lib.rkv_lse_merge(None, 2, 4, dv, None, None, None) == _lib.RKV_ERR_UNSUPPORTED
+    assert lib.rkv_lse_merge(None, 0, 4, 512, None, None, None) == _lib.RKV_ERR_ARG  # 512 passes the width check
     assert lib.rkv_lse_merge(None, 0, 4, 64, None, None, None) == _lib.RKV_ERR_ARG
     assert lib.rkv_lse_merge(None, 0, 4, 128, None, None, None) == _lib.RKV_ERR_ARG
     assert lib.rkv_lse_merge(None, 1, 0, 128, None, None, None) == _lib.RKV_OK  # nothing to do

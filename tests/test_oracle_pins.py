@@ -138,6 +138,28 @@ def test_library_special_case_sdpa_f64(d):
     assert np.allclose(O, ref, atol=1e-12)
 
 
+def test_library_special_case_sdpa_f64_dk_ne_dv():
+    """dk = 576, dv = 512 (Q/K wider than V): torch SDPA in float64 takes the two widths too."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(19)
+    H, G, Qn, N, dk, dv = 8, 1, 2, 29, 576, 512
+    q = rng.standard_normal((H, Qn, dk))
+    k = rng.standard_normal((G, N, dk))
+    v = rng.standard_normal((G, N, dv))
+    mask = np.where(rng.random((Qn, N)) < 0.2, NEG, 0.3 * rng.standard_normal((Qn, N)))
+    O, L = oracle.attention(q, k, v, 0.04, mask)
+    assert O.shape == (Qn, H, dv) and L.shape == (Qn, H)
+    kr = torch.from_numpy(k).repeat_interleave(H // G, dim=0)
+    vr = torch.from_numpy(v).repeat_interleave(H // G, dim=0)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q)[None], kr[None], vr[None], attn_mask=torch.from_numpy(mask), scale=0.04)
+    assert np.allclose(O, ref[0].permute(1, 0, 2).numpy(), atol=1e-12)
+    # LSE against its definition with math.fsum on one row
+    s = [0.04 * math.fsum(q[3, 1] * k[0, j]) + mask[1, j] for j in range(N)]
+    m = max(x for x in s if x > -np.inf)
+    assert abs(L[1, 3] - (m + math.log(math.fsum(math.exp(x - m) for x in s if x > -np.inf)))) < 1e-12
+
+
 # ------------------------------------------------------------- split method
 @pytest.mark.parametrize("seed", range(4))
 def test_partition_invariance(seed):

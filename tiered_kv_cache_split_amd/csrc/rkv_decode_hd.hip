@@ -1,21 +1,23 @@
-// Decode segment kernel for head dims other than 128 (64 and 256, dv = dk), and the log-sum-exp
-// merge for those value widths.  The streaming op of opencoti-llamafile patch 0070-rolling-kv
-// serves several head dims through the same split-and-combine (fattn.cu, the op's supported
-// shapes); the partial of a segment is the same (M, S, VKQ) triple as for head dim 128, stored
-// with row stride 2 + D.
+// Decode segment kernel for head dims other than 128 -- dk = dv in {64, 256, 512} and the
+// dk = 576 / dv = 512 pair -- and the log-sum-exp merge for those value widths.  The streaming
+// op of opencoti-llamafile patch 0070-rolling-kv serves several head dims through the same
+// split-and-combine (fattn.cu, the op's supported shapes, which list 512 and the 576/512 pair
+// next to 64 and 256); the partial of a segment is the same (M, S, VKQ) triple as for head dim
+// 128, stored with row stride 2 + dv.
 //
 // Workgroup = 256 threads for one (split, KV head, sequence); it walks the split in chunks of KC
-// keys (64 for D = 64, 16 for D = 256) as a pipeline: the next chunk's K and V rows are loaded
+// keys (64 for dk = 64, 16 otherwise) as a pipeline: the next chunk's K and V rows are loaded
 // from HBM into registers (4-byte words, consecutive threads on consecutive words of a row)
 // while the current chunk is computed from LDS.
-//   Q.K  P = 256 / KC threads per key, each over 16 consecutive dims (half of a q8_0 block),
-//        partial dots summed across the P adjacent lanes; the R <= 8 query rows that
-//        read this KV head are done together.
+//   Q.K  P = 256 / KC threads per key, each over E = dk / P dims (16: half of a q8_0 block;
+//        32: one block; at dk = 576, 32 dims of one block plus 4 of the last two blocks, each
+//        part times its own block's d), partial dots summed across the P adjacent lanes; the
+//        R <= 8 query rows that read this KV head are done together.
 //   softmax  wave w owns rows w and w + 4: chunk max, rescale factor and weights, in natural-log
 //        units, kept in LDS for the P.V step.
-//   P.V  thread t owns output column t % D of every row over the chunk's keys j with
-//        j % KS = t / D (KS = 256 / D key subsets, so each V value is dequantised once); the
-//        subsets' sums are added through LDS at the end.
+//   P.V  thread t owns output columns t % dv (+ 256 c for dv = 512) of every row over the
+//        chunk's keys j with j % KS = t / dv (KS = 256 / dv key subsets for dv < 256, so each V
+//        value is dequantised once); the subsets' sums are added through LDS at the end.
 #include "rkv_internal.h"
 #include "rkv_unpack.h"
 #include "rkv_wave.h"
@@ -46,20 +48,26 @@ __device__ __forceinline__ float group_sum(float x) {
     return x;
 }
 
-template <int D, int KT, int VT>
+template <int DK, int DV, int KT, int VT>
 struct HdGeom {
-    static constexpr int KC = D == 64 ? 64 : 16;           // keys per chunk
+    static constexpr int KC = DK == 64 ? 64 : 16;          // keys per chunk
     static constexpr int P = kThreads / KC;                // threads per key in Q.K
-    static constexpr int E = D / P;                        // dims per thread in Q.K (16 or 32)
-    static constexpr int KW = hd_row_bytes<KT, D>() / 4;   // 4-byte words per K row
-    static constexpr int VW = hd_row_bytes<VT, D>() / 4;
+    static constexpr int E = DK / P;                       // dims per thread in Q.K (16, 32 or 36)
+    // a thread's dims: EM consecutive ones from dim pq * EM (within one quant block), and at
+    // dk = 576 also EX = 4 from dim 512 + pq * EX (within one block of the last two)
+    static constexpr int EX = DK == 576 ? 4 : 0;
+    static constexpr int EM = E - EX;
+    static constexpr int KW = hd_row_bytes<KT, DK>() / 4;  // 4-byte words per K row
+    static constexpr int VW = hd_row_bytes<VT, DV>() / 4;
     static constexpr int KWP = KW | 1, VWP = VW | 1;       // odd LDS row pitch: no bank conflicts
     static constexpr int NK = (KC * KW + kThreads - 1) / kThreads;  // words per thread per chunk
     static constexpr int NV = (KC * VW + kThreads - 1) / kThreads;
-    static constexpr int KS = kThreads / D;                // P.V: threads per column (key subsets)
+    static constexpr int CPT = DV > kThreads ? DV / kThreads : 1;  // P.V: columns per thread
+    static constexpr int KS = DV >= kThreads ? 1 : kThreads / DV;  // P.V: threads per column (key subsets)
     static constexpr int KPS = KC / KS;                    // keys per subset (16)
     static_assert(P == 4 || P == 16, "Q.K groups are DPP quads or 16-lane rows");
-    static_assert(E == 16, "a thread's Q.K dims are half of one quant block");
+    static_assert(EM == 16 || EM == 32, "a thread's main Q.K dims: half a block or a block");
+    static_assert(E % 4 == 0 && DK % 32 == 0 && DV % 32 == 0, "whole quant blocks");
 };
 
 // Chunk rows [c0, c0 + KC) of one KV head, words of row r in order; cells at or past c_end read
@@ -96,10 +104,12 @@ __device__ __forceinline__ float v_value(const uint8_t *row, int e) {
     }
 }
 
-template <int D, int KT, int VT, bool CAP>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4 : 3))) decode_hd_kernel(const SegParams p) {
-    using G = HdGeom<D, KT, VT>;
-    constexpr int KC = G::KC, P = G::P, E = G::E, PS = 2 + D;
+template <int DK, int DV, int KT, int VT, bool CAP>
+__global__ void __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(DK == 64 ? 4 : (DK <= 256 ? 3 : (DK == 576 && KT == T_F16 ? 1 : 2)))))
+decode_hd_kernel(const SegParams p) {
+    using G = HdGeom<DK, DV, KT, VT>;
+    constexpr int KC = G::KC, P = G::P, E = G::E, PS = 2 + DV;
     // Q row rho, part pq (16 values) at rho * P * QP + pq * QP: a pitch of 20 floats puts the P
     // parts that lanes of one wave read together on distinct LDS banks (a pitch of 16 maps every
     // fourth part to the same banks)
@@ -110,7 +120,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D
     // scores, then weights; key j of the chunk at (j % KS) * KPS + j / KS so that each key
     // subset's weights are contiguous
     __shared__ __align__(16) float s_s[kRmax][KC];
-    __shared__ float s_red[G::KS > 1 ? G::KS * kRmax * D : 1];  // key-subset sums of P.V
+    __shared__ float s_red[G::KS > 1 ? G::KS * kRmax * DV : 1];  // key-subset sums of P.V
     auto widx = [](int j) { return (j % G::KS) * G::KPS + j / G::KS; };
     __shared__ float s_alpha[kRmax];
 
@@ -128,20 +138,24 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D
     const uint8_t *vbase = p.v + (int64_t)g * p.v_s2;
 
     // Q rows rho = i * gqa + r (query i, head g * gqa + r) in LDS; rows past R are zero
-    for (int idx = tid; idx < kRmax * D; idx += kThreads) {
-        const int rho = idx / D, e = idx % D;
+    for (int idx = tid; idx < kRmax * DK; idx += kThreads) {
+        const int rho = idx / DK, e = idx % DK;
         const int r = rho % p.gqa, i = rho / p.gqa;
-        s_q[rho * P * QP + (e / E) * QP + e % E] = rho < R ? (float)p.q[(int64_t)i * p.q_s1 + (int64_t)(g * p.gqa + r) * p.q_s2 + (int64_t)b * p.q_s3 + e]
+        const int part = (G::EX > 0 && e >= 512) ? (e - 512) / G::EX : e / G::EM;
+        const int off = (G::EX > 0 && e >= 512) ? G::EM + (e - 512) % G::EX : e % G::EM;
+        s_q[rho * P * QP + part * QP + off] = rho < R ? (float)p.q[(int64_t)i * p.q_s1 + (int64_t)(g * p.gqa + r) * p.q_s2 + (int64_t)b * p.q_s3 + e]
                               : 0.f;
     }
 
     // softmax state of the rows this wave owns (w, w + 4), the same in every lane
     float m_own[2] = {-INFINITY, -INFINITY}, l_own[2] = {0.f, 0.f};
-    // P.V accumulators: column e_pv of every row, over key subset ks
-    const int e_pv = tid % D, ks = tid / D;
-    float acc[kRmax];
+    // P.V accumulators: columns e_pv + 256 c of every row, over key subset ks
+    const int e_pv = tid % DV, ks = tid / DV;
+    float acc[G::CPT][kRmax];
 #pragma unroll
-    for (int rho = 0; rho < kRmax; ++rho) acc[rho] = 0.f;
+    for (int cp = 0; cp < G::CPT; ++cp)
+#pragma unroll
+        for (int rho = 0; rho < kRmax; ++rho) acc[cp][rho] = 0.f;
 
     const int kq = tid / P, pq = tid % P;  // Q.K: key kq of the chunk, dims [pq*E, pq*E + E)
 
@@ -165,17 +179,25 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D
         // ---- Q.K
         {
             const uint8_t *krow = reinterpret_cast<const uint8_t *>(s_k + kq * G::KWP);
-            const int e0 = pq * E;
+            constexpr int EM = G::EM, EX = G::EX;
+            const int e0 = pq * EM, e1 = 512 + pq * EX;
             float kv[E];
             float kscale = 1.f;
             if constexpr (KT == T_F16) {
 #pragma unroll
-                for (int i = 0; i < E; i += 2) {
+                for (int i = 0; i < EM; i += 2) {
                     const uint32_t w = *reinterpret_cast<const uint32_t *>(krow + 2 * (e0 + i));
                     kv[i] = h2f_bits(w & 0xFFFFu);
                     kv[i + 1] = h2f_bits(w >> 16);
                 }
-            } else {
+#pragma unroll
+                for (int i = 0; i < EX; i += 2) {
+                    const uint32_t w = *reinterpret_cast<const uint32_t *>(krow + 2 * (e1 + i));
+                    kv[EM + i] = h2f_bits(w & 0xFFFFu);
+                    kv[EM + i + 1] = h2f_bits(w >> 16);
+                }
+            } else if constexpr (EX == 0) {
+                // the thread's dims lie in one q8_0 block: its scale multiplies the dot
                 const uint8_t *blk = krow + 34 * (e0 >> 5);
                 kscale = h2f_bits(*reinterpret_cast<const uint16_t *>(blk));
                 const uint8_t *codes = blk + 2 + (e0 & 31);
@@ -184,6 +206,23 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D
                     const uint32_t w = *reinterpret_cast<const uint16_t *>(codes + i);
                     kv[i] = q8_code_f32(w);
                     kv[i + 1] = q8_code_f32(w >> 8);
+                }
+            } else {
+                // two blocks: each code times its own block's scale (d * q is exact in fp32)
+                const uint8_t *b0 = krow + 34 * (e0 >> 5), *b1 = krow + 34 * (e1 >> 5);
+                const float d0 = h2f_bits(*reinterpret_cast<const uint16_t *>(b0));
+                const float d1 = h2f_bits(*reinterpret_cast<const uint16_t *>(b1));
+#pragma unroll
+                for (int i = 0; i < EM; i += 2) {
+                    const uint32_t w = *reinterpret_cast<const uint16_t *>(b0 + 2 + (e0 & 31) + i);
+                    kv[i] = q8_code_f32(w) * d0;
+                    kv[i + 1] = q8_code_f32(w >> 8) * d0;
+                }
+#pragma unroll
+                for (int i = 0; i < EX; i += 2) {
+                    const uint32_t w = *reinterpret_cast<const uint16_t *>(b1 + 2 + (e1 & 31) + i);
+                    kv[EM + i] = q8_code_f32(w) * d1;
+                    kv[EM + i + 1] = q8_code_f32(w >> 8) * d1;
                 }
             }
             float dot[kRmax];
@@ -251,18 +290,26 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D
         {
 #pragma unroll
             for (int rho = 0; rho < kRmax; ++rho)
-                if (rho < R) acc[rho] *= s_alpha[rho];
+                if (rho < R) {
+                    const float al = s_alpha[rho];
+#pragma unroll
+                    for (int cp = 0; cp < G::CPT; ++cp) acc[cp][rho] *= al;
+                }
             const uint8_t *vcol = reinterpret_cast<const uint8_t *>(s_v);
 #pragma unroll 1
             for (int t = 0; t < G::KPS; t += 4) {
-                float v[4];
 #pragma unroll
-                for (int u = 0; u < 4; ++u) v[u] = v_value<VT>(vcol + (ks + G::KS * (t + u)) * (4 * G::VWP), e_pv);
+                for (int cp = 0; cp < G::CPT; ++cp) {
+                    float v[4];
 #pragma unroll
-                for (int rho = 0; rho < kRmax; ++rho) {
-                    if (rho < R) {
-                        const float4 w = *reinterpret_cast<const float4 *>(&s_s[rho][ks * G::KPS + t]);
-                        acc[rho] = fmaf(w.x, v[0], fmaf(w.y, v[1], fmaf(w.z, v[2], fmaf(w.w, v[3], acc[rho]))));
+                    for (int u = 0; u < 4; ++u)
+                        v[u] = v_value<VT>(vcol + (ks + G::KS * (t + u)) * (4 * G::VWP), e_pv + kThreads * cp);
+#pragma unroll
+                    for (int rho = 0; rho < kRmax; ++rho) {
+                        if (rho < R) {
+                            const float4 w = *reinterpret_cast<const float4 *>(&s_s[rho][ks * G::KPS + t]);
+                            acc[cp][rho] = fmaf(w.x, v[0], fmaf(w.y, v[1], fmaf(w.z, v[2], fmaf(w.w, v[3], acc[cp][rho]))));
+                        }
                     }
                 }
             }
@@ -286,17 +333,20 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D
     if constexpr (G::KS == 1) {
 #pragma unroll
         for (int rho = 0; rho < kRmax; ++rho)
-            if (rho < R) p.partials[out_row(rho) + 2 + e_pv] = acc[rho];
+            if (rho < R) {
+#pragma unroll
+                for (int cp = 0; cp < G::CPT; ++cp) p.partials[out_row(rho) + 2 + e_pv + kThreads * cp] = acc[cp][rho];
+            }
     } else {
 #pragma unroll
         for (int rho = 0; rho < kRmax; ++rho)
-            if (rho < R) s_red[(ks * kRmax + rho) * D + e_pv] = acc[rho];
+            if (rho < R) s_red[(ks * kRmax + rho) * DV + e_pv] = acc[0][rho];
         __syncthreads();
-        for (int idx = tid; idx < R * D; idx += kThreads) {
-            const int rho = idx / D, e = idx % D;
+        for (int idx = tid; idx < R * DV; idx += kThreads) {
+            const int rho = idx / DV, e = idx % DV;
             float a = 0.f;
 #pragma unroll
-            for (int k = 0; k < G::KS; ++k) a += s_red[(k * kRmax + rho) * D + e];
+            for (int k = 0; k < G::KS; ++k) a += s_red[(k * kRmax + rho) * DV + e];
             p.partials[out_row(rho) + 2 + e] = a;
         }
     }
@@ -330,34 +380,40 @@ __global__ void __launch_bounds__(D) merge_hd_kernel(const float *part, int n_se
     if (t == 0 && lse) lse[row] = ok ? M + logf(S) : -INFINITY;
 }
 
-template <int D, int KT, int VT>
+template <int DK, int DV, int KT, int VT>
 hipError_t launch_hd(const SegParams &p, hipStream_t s) {
     const int64_t blocks = (int64_t)p.n_splits * p.n_head_kv * p.n_seq;
     if (blocks <= 0) return hipSuccess;
     if (p.cap_l2 != 0.f)
-        launch_seg(decode_hd_kernel<D, KT, VT, true>, dim3((unsigned)blocks), dim3(kThreads), s, p);
+        launch_seg(decode_hd_kernel<DK, DV, KT, VT, true>, dim3((unsigned)blocks), dim3(kThreads), s, p);
     else
-        launch_seg(decode_hd_kernel<D, KT, VT, false>, dim3((unsigned)blocks), dim3(kThreads), s, p);
+        launch_seg(decode_hd_kernel<DK, DV, KT, VT, false>, dim3((unsigned)blocks), dim3(kThreads), s, p);
     return hipGetLastError();
 }
 
-template <int D>
+template <int DK, int DV>
 hipError_t launch_hd_types(const SegParams &p, int k_type, int v_type, hipStream_t s) {
-    if (k_type == T_F16 && v_type == T_F16) return launch_hd<D, T_F16, T_F16>(p, s);
-    if (k_type == T_Q8_0 && v_type == T_Q4_0) return launch_hd<D, T_Q8_0, T_Q4_0>(p, s);
-    if (k_type == T_Q8_0 && v_type == T_F16) return launch_hd<D, T_Q8_0, T_F16>(p, s);
-    if (k_type == T_F16 && v_type == T_Q4_0) return launch_hd<D, T_F16, T_Q4_0>(p, s);
+    if (k_type == T_F16 && v_type == T_F16) return launch_hd<DK, DV, T_F16, T_F16>(p, s);
+    if (k_type == T_Q8_0 && v_type == T_Q4_0) return launch_hd<DK, DV, T_Q8_0, T_Q4_0>(p, s);
+    if (k_type == T_Q8_0 && v_type == T_F16) return launch_hd<DK, DV, T_Q8_0, T_F16>(p, s);
+    if (k_type == T_F16 && v_type == T_Q4_0) return launch_hd<DK, DV, T_F16, T_Q4_0>(p, s);
     return hipErrorNotSupported;
 }
 
 }  // namespace
 
-bool head_dim_supported(int d) { return d == 64 || d == 128 || d == 256; }
+bool head_dim_supported(int d) { return d == 64 || d == 128 || d == 256 || d == 512 || d == 576; }
+
+bool head_dims_supported(int dk, int dv) {
+    return (dk == dv && (dk == 64 || dk == 128 || dk == 256 || dk == 512)) || (dk == 576 && dv == 512);
+}
 
 hipError_t launch_decode_hd(const SegParams &p, int k_type, int v_type, hipStream_t s) {
     if (p.rows || p.gqa * p.n_q > kRmax) return hipErrorNotSupported;
-    if (p.d == 64) return launch_hd_types<64>(p, k_type, v_type, s);
-    if (p.d == 256) return launch_hd_types<256>(p, k_type, v_type, s);
+    if (p.d == 64 && p.dv == 64) return launch_hd_types<64, 64>(p, k_type, v_type, s);
+    if (p.d == 256 && p.dv == 256) return launch_hd_types<256, 256>(p, k_type, v_type, s);
+    if (p.d == 512 && p.dv == 512) return launch_hd_types<512, 512>(p, k_type, v_type, s);
+    if (p.d == 576 && p.dv == 512) return launch_hd_types<576, 512>(p, k_type, v_type, s);
     return hipErrorNotSupported;
 }
 
@@ -368,6 +424,9 @@ hipError_t launch_merge_hd(const float *partials, int n_seg, int64_t n_rows, int
         hipLaunchKernelGGL(merge_hd_kernel<64>, dim3((unsigned)n_rows), dim3(64), 0, s, partials, n_seg, n_rows, o, lse);
     else if (dv == 256)
         hipLaunchKernelGGL(merge_hd_kernel<256>, dim3((unsigned)n_rows), dim3(256), 0, s, partials, n_seg, n_rows, o,
+                           lse);
+    else if (dv == 512)
+        hipLaunchKernelGGL(merge_hd_kernel<512>, dim3((unsigned)n_rows), dim3(512), 0, s, partials, n_seg, n_rows, o,
                            lse);
     else
         return hipErrorNotSupported;

@@ -53,8 +53,10 @@ struct SegParams {
     int2 *pair_range;
     // optional: events the segment kernel's own dispatch records at its start and end
     hipEvent_t ev_start, ev_stop;
-    // head dim (== dv): 128 for every kernel but the decode kernel for other head dims
+    // head dims of Q/K (d) and V (dv): 128 for every kernel but the decode kernel for other
+    // head dims (dk = dv in 64, 256, 512, or dk = 576 with dv = 512)
     int d = kHeadDim;
+    int dv = kHeadDim;
 };
 
 // Launch a segment kernel; with timing events set, the dispatch itself records them, so the
@@ -119,7 +121,8 @@ hipError_t launch_dequant_rows(const void *src, int type, int form, int64_t n_ro
 
 // Head dims other than 128 (rkv_decode_hd.hip): decode segments (gqa * n_q <= 8, no row lists)
 // and the merge of partials with row stride 2 + dv.
-bool head_dim_supported(int d);  // 64, 128 or 256
+bool head_dim_supported(int d);              // one tensor's head dim: 64, 128, 256, 512 or 576
+bool head_dims_supported(int dk, int dv);   // a (Q/K, V) pair: equal in 64..512, or 576 / 512
 hipError_t launch_decode_hd(const SegParams &p, int k_type, int v_type, hipStream_t s);
 hipError_t launch_merge_hd(const float *partials, int n_seg, int64_t n_rows, int dv, float *o, float *lse,
                            hipStream_t s);

@@ -97,7 +97,8 @@ int check_device_ptr(const void *p, const char *name) {
     return RKV_OK;
 }
 
-// K/V tensor [128, n_cells, n_head_kv, 1] with contiguous rows (any_d: head dim 64, 128 or 256).
+// K/V tensor [128, n_cells, n_head_kv, 1] with contiguous rows (any_d: head dim 64, 128, 256,
+// 512 or 576; which pairs of K and V dims go together is checked by the caller).
 int check_kv(const rkv_tensor *t, const char *name, bool is_k, bool any_d = false) {
     if (!t) return fail(RKV_ERR_ARG, "%s is NULL", name);
     const bool ok_type = is_k ? (t->type == RKV_TYPE_F16 || t->type == RKV_TYPE_Q8_0)
@@ -320,7 +321,7 @@ struct Seg {
 // apply: every cell must hold the KV heads packed (head stride == row size), cell strides and
 // bases must be 16-byte aligned, and the types and head count must have an instantiation.
 int use_cell_kernel(const Seg &sg, const SegParams &p, int k_type, int v_type) {
-    if (p.d != kHeadDim) return 0;
+    if (p.d != kHeadDim || p.dv != kHeadDim) return 0;
     const int64_t rk = row_bytes(k_type), rv = row_bytes(v_type);
     const int hw = cell_heads(k_type, v_type, p.n_head_kv, p.gqa * p.n_q, p.rows != nullptr);
     if (hw == 0) return 0;
@@ -496,7 +497,7 @@ int attn_window_tail(rkv_ctx *ctx, const rkv_tensor *q, const rkv_tensor *k_win,
                      int64_t q_pos0, bool mfma, float *o, float *lse, hipStream_t stream,
                      float *ext_partials = nullptr, int64_t ext_cap = 0) {
     if (!ctx) return fail(RKV_ERR_ARG, "ctx is NULL");
-    // decode takes head dims 64, 128 and 256 (dv = dk); prefill 128 only
+    // decode takes dk = dv in 64, 128, 256, 512 and the pair dk = 576 / dv = 512; prefill 128 only
     const bool any_d = !mfma;
     int st = check_q(q, false, any_d);
     if (st) return st;
@@ -536,9 +537,13 @@ int attn_window_tail(rkv_ctx *ctx, const rkv_tensor *q, const rkv_tensor *k_win,
     if (n_head % n_head_kv != 0) return fail(RKV_ERR_ARG, "n_head %% n_head_kv != 0");
     const int64_t gqa = n_head / n_head_kv;
     const int d = (int)q->ne[0];
-    if (kref->ne[0] != d || vref->ne[0] != d || (k_tail && (k_tail->ne[0] != d || v_tail->ne[0] != d)))
-        return fail(RKV_ERR_UNSUPPORTED, "K and V head dims must equal Q's");
-    const int64_t ps = 2 + d;  // partial row stride
+    const int dv = (int)vref->ne[0];
+    if (kref->ne[0] != d || (k_tail && (k_tail->ne[0] != d || v_tail->ne[0] != dv)) || (v_win && v_win->ne[0] != dv))
+        return fail(RKV_ERR_ARG, "K head dims must equal Q's and the V tensors must agree");
+    if (!head_dims_supported(d, dv))
+        return fail(RKV_ERR_UNSUPPORTED, "head dims dk=%d, dv=%d not supported (dk = dv in 64, 128, 256, 512, or 576/512)",
+                    d, dv);
+    const int64_t ps = 2 + dv;  // partial row stride
     if (!mfma && gqa * n_q > kMaxRowsVec)
         return fail(RKV_ERR_UNSUPPORTED, "decode handles n_q*gqa <= %d rows per KV head (got %lld); use rkv_attn_prefill",
                     kMaxRowsVec, (long long)(gqa * n_q));
@@ -564,11 +569,13 @@ int attn_window_tail(rkv_ctx *ctx, const rkv_tensor *q, const rkv_tensor *k_win,
     fill_softcap(base, ctx, scale);
     base.n_rows = n_head * n_q;
     base.d = d;
+    base.dv = dv;
 
     // ---- plan: window segment, then tail (in place, lifted tiles through the ring, or a
     // partial computed on the host cores)
     const bool host_tail = n_tail > 0 && tail_kind != Mem::Device && ctx->tail_mode == RKV_TAIL_HOST && !mfma;
-    if (host_tail && d != kHeadDim) return fail(RKV_ERR_UNSUPPORTED, "the host tail partial takes head dim 128");
+    if (host_tail && (d != kHeadDim || dv != kHeadDim))
+        return fail(RKV_ERR_UNSUPPORTED, "the host tail partial takes head dim 128");
     // RKV_LIFT_DIRECT (contrast only): the segment kernels read a pinned tail in place through
     // its device view, in their own access order, with no lift
     const bool direct = n_tail > 0 && tail_kind == Mem::PinnedHost && !host_tail && ctx->lift_mode == RKV_LIFT_DIRECT;
@@ -775,10 +782,10 @@ int attn_window_tail(rkv_ctx *ctx, const rkv_tensor *q, const rkv_tensor *k_win,
         }
     }
     if (d != kHeadDim) {
-        // other head dims: the merge of partials with row stride 2 + d (no partial at all, as for
-        // n_kv == 0, gives every row O = 0 and LSE = -inf)
+        // other head dims: the merge of partials with row stride 2 + dv (no partial at all, as
+        // for n_kv == 0, gives every row O = 0 and LSE = -inf)
         ctx->stats.n_partials = slot;
-        hipError_t e = launch_merge_hd(base.partials, slot, base.n_rows, d, o, lse, stream);
+        hipError_t e = launch_merge_hd(base.partials, slot, base.n_rows, dv, o, lse, stream);
         if (e != hipSuccess) return hip_fail(e, "merge launch");
         return RKV_OK;
     }
@@ -1328,7 +1335,7 @@ int rkv_attn_partial(rkv_ctx *ctx, const rkv_tensor *q, const rkv_tensor *k, con
 }
 
 int rkv_lse_merge(const float *partials, int n_seg, int64_t n_rows, int dv, float *o, float *lse, void *stream) {
-    if (!head_dim_supported(dv)) return fail(RKV_ERR_UNSUPPORTED, "dv must be 64, 128 or 256");
+    if (!head_dims_supported(dv, dv)) return fail(RKV_ERR_UNSUPPORTED, "dv must be 64, 128, 256 or 512");
     if (n_seg <= 0 || n_rows < 0) return fail(RKV_ERR_ARG, "n_seg must be > 0 and n_rows >= 0");
     if (n_rows == 0) return RKV_OK;
     int st = check_device_ptr(partials, "partials");
