@@ -17,11 +17,11 @@
  * ---------------------------------------
  * Tensors are described ggml-style: ne[0] is the fastest dimension, nb[] are byte
  * strides, nb[0] is the element (or quant block) size.  Rows of head_dim values must be
- * contiguous (nb[0] == type size).  Supported: head_dim == dv == 128 everywhere, and
- * for rkv_attn_decode (device window + device or lifted tail, vector kernel) also
- * head_dim == dv in {64, 256, 512} and head_dim 576 with dv 512 (patch 0070, fattn.cu:
- * the streaming op's supported head dims); rkv_lse_merge takes dv 64, 128, 256 or 512;
- * Q in F16;
+ * contiguous (nb[0] == type size).  Supported head dims (patch 0070, fattn.cu: the streaming
+ * op's supported shapes): head_dim == dv in {64, 128, 256, 512}, and head_dim 576 for Q and
+ * K with dv 512 for V, on every attention entry point and the host tail partial; head_dim
+ * 128 runs on the matrix-core kernels, the others on a vector kernel; rkv_lse_merge takes
+ * dv 64, 128, 256 or 512; Q in F16;
  * K in F16 or Q8_0; V in F16 or Q4_0.  Q8_0 is a 34-byte block (binary16 scale d, 32
  * int8 codes q; value d*q).  Q4_0 is an 18-byte block (binary16 scale d, 16 bytes; byte
  * j holds element j in its low nibble and element j+16 in its high nibble; value
@@ -186,9 +186,9 @@ int rkv_kernel_timing_ms(rkv_ctx *ctx, float *total_ms, int *n_launches);
  * tiles never straddle wc; the mask is sliced at the global position).
  * Shown for head_dim 128; head_dim 64, 256 or 512 (Q, K and V alike), or 576 for Q and K
  * with 512 for V (o then [512, n_head, n_q]), takes the same arguments with those leading
- * extents, except the host tail partial (RKV_TAIL_HOST), which is RKV_ERR_UNSUPPORTED for
- * them; any other pair of head dims is RKV_ERR_UNSUPPORTED.
- *   q       F16 [128, n_q, n_head, 1], device.  n_q * (n_head/n_head_kv) <= 8.
+ * extents; any other pair of head dims is RKV_ERR_UNSUPPORTED.
+ *   q       F16 [128, n_q, n_head, 1], device.  n_q * (n_head/n_head_kv) <= 8 at head dim
+ *           128 (any number at the other head dims, in groups of 8 rows).
  *   k_win   [128, >= wc, n_head_kv, 1] device (cells [0, wc) are used); NULL iff wc == 0.
  *   v_win   as k_win with V's type.
  *   k_tail  [128, n_tail, n_head_kv, 1] or NULL.  Pinned host memory (lifted in tiles of
@@ -227,9 +227,11 @@ int rkv_attn_decode_noalloc(const rkv_tensor *q, const rkv_tensor *k, const rkv_
  * tail streaming op serves a multi-token chunk, with the mask sliced at the global key
  * position, a per-tile flash attention and an LSE per tile for the combine; patch 0102,
  * commit message: 106k-token prefills through lifted tail tiles).  The same arguments as
- * rkv_attn_decode for any n_q, computed with MFMA f16 tiles: q8_0 K codes and q4_0 V
- * nibbles enter the matrix cores as exact binary16 integers and their block scales are
- * applied in fp32 (K) or folded into the softmax weights (V).  q_pos0 >= 0 makes it
+ * rkv_attn_decode for any n_q, computed at head dim 128 with MFMA f16 tiles: q8_0 K codes
+ * and q4_0 V nibbles enter the matrix cores as exact binary16 integers and their block scales
+ * are applied in fp32 (K) or folded into the softmax weights (V); the other head dims run on
+ * the vector kernel for them in groups of 8 rows.  The tail is always computed on the GPU
+ * (RKV_TAIL_HOST applies to decode only).  q_pos0 >= 0 makes it
  * causal: query i sits at absolute position q_pos0 + i and sees keys at positions
  * <= q_pos0 + i (in addition to the mask); q_pos0 == -1 uses the mask alone. */
 int rkv_attn_prefill(rkv_ctx *ctx, const rkv_tensor *q,
@@ -240,7 +242,8 @@ int rkv_attn_prefill(rkv_ctx *ctx, const rkv_tensor *q,
 
 /* Unified-pool attention (llama.cpp PR #29510, ggml_flash_attn_ext_rows): each sequence
  * b attends to its own list of pool rows.
- *   q       F16 [128, n_q, n_head, n_seq] device, n_q * (n_head/n_head_kv) <= 8.
+ *   q       F16 [128, n_q, n_head, n_seq] device, n_q * (n_head/n_head_kv) <= 8 at head dim
+ *           128 (other head dims as for rkv_attn_decode, any number of rows).
  *   k_pool  [128, n_pool, n_head_kv, 1] device, shared by all sequences; v_pool likewise.
  *   kv_rows int32 [n_kv, n_seq] device, contiguous: key j of sequence b is pool row
  *           kv_rows[j + n_kv*b].  A negative row is padding: it contributes nothing and is
@@ -300,7 +303,7 @@ int rkv_tail_lift(rkv_ctx *ctx, const void *host_src, int64_t nbytes, int slot, 
 int rkv_set_tail_mode(rkv_ctx *ctx, int mode, int n_threads);
 
 /* The tail partial on the host cores alone (the same computation RKV_TAIL_HOST runs):
- * partial float32 [n_head * n_q][2 + 128] in host memory receives (M, S, VKQ) for every row
+ * partial float32 [n_head * n_q][2 + dv] in host memory receives (M, S, VKQ) for every row
  * r = h + n_head*i over the keys of k/v (fp32 accumulation; an empty row is (-inf, 0, 0...)).
  *   q        F16 [128, n_q, n_head, 1] in host memory (rows contiguous, even strides).
  *   k, v     [128, n_cells, n_head_kv, 1] in host memory: K F16 or Q8_0, V F16 or Q4_0,

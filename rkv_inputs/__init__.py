@@ -51,6 +51,16 @@ def row_bytes(type_id: int, d: int) -> int:
     return (d // QK) * BLOCK_BYTES[type_id]
 
 
+def values_per_row(type_id: int, n_bytes: int) -> int:
+    """Values in a row of n_bytes bytes of the given type (the inverse of row_bytes)."""
+    if type_id == TYPE_F16:
+        return n_bytes // 2
+    if type_id == TYPE_F32:
+        return n_bytes // 4
+    assert n_bytes % BLOCK_BYTES[type_id] == 0
+    return n_bytes // BLOCK_BYTES[type_id] * QK
+
+
 # ---------------------------------------------------------------- packers
 def pack_f16(x: np.ndarray) -> np.ndarray:
     """float32 values -> raw binary16 bytes (last axis becomes 2*len)."""
@@ -225,14 +235,15 @@ def make_workload(num: int, scale_down: int = 1, **over):
         lengths = tuple(max(1, L // sd) for L in w["lengths"])
         n_kv = max(lengths)
         n_seq = len(lengths)
+        dv = w.get("dv", w["d"])
         q = draw_normal(rng, (n_seq, w["n_head"], w["n_q"], w["d"])).astype(np.float16)
         k = pack(w["k_type"], draw_normal(rng, (n_pool, w["n_head_kv"], w["d"])))
-        v = pack(w["v_type"], draw_normal(rng, (n_pool, w["n_head_kv"], w["d"])))
+        v = pack(w["v_type"], draw_normal(rng, (n_pool, w["n_head_kv"], dv)))
         rows = rows_lists(rng, n_pool, lengths, n_kv)
         mask = np.where(rows[:, None, None, :] >= 0, 0.0, -np.inf).astype(np.float16)
         mask = np.broadcast_to(mask, (n_seq, 1, w["n_q"], n_kv)).copy()
         w.update(n_pool=n_pool, lengths=lengths, n_kv=n_kv, n_seq=n_seq)
-        w.update(q=q, k=k, v=v, kv_rows=rows, mask=mask, scale=1.0 / np.sqrt(w["d"]))
+        w.update(q=q, k=k, v=v, kv_rows=rows, mask=mask, scale=1.0 / np.sqrt(w["d"]), dv=dv)
         return w
     n_kv = w["n_kv"] // sd
     wc = min(n_kv, w["wc"] // sd)

@@ -143,7 +143,7 @@ class Runner:
         mt = None if m is None else dev(np.asarray(m, dtype=np.float16))
         n_seq, n_head, n_q, _ = w["q"].shape
         n_kv = kvr.shape[1]
-        o = torch.empty((n_seq, n_q, n_head, 128), dtype=torch.float32, device="cuda")
+        o = torch.empty((n_seq, n_q, n_head, w.get("dv", w.get("d", 128))), dtype=torch.float32, device="cuda")
         lse = torch.empty((n_seq, n_q, n_head), dtype=torch.float32, device="cuda")
         self.ctx.attn_rows(rkv.q_desc(q), rkv.kv_desc(kp, w["k_type"]), rkv.kv_desc(vp, w["v_type"]), kvr, n_kv,
                            rkv.mask_desc(mt), w["scale"], o, lse)

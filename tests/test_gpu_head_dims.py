@@ -1,7 +1,7 @@
 """Head dims 64 and 256 (dk = dv) through rkv_attn_decode and rkv_lse_merge against the fp64
 oracle: the window + tail split with a lifted (both engines) or device-resident tail, every K/V
-type pair, masks with an empty row, the soft-cap, grouped-query rows up to eight per KV head and
-the empty cache; the entry points that take head dim 128 only refuse the others."""
+type pair, masks with an empty row, the soft-cap, grouped-query rows up to eight per KV head,
+the empty cache and the tail's partial computed on the host cores."""
 import numpy as np
 import pytest
 
@@ -139,19 +139,18 @@ def test_lse_merge(dv):
                  what=f"merge dv={dv}")
 
 
-def test_other_entry_points_refuse_other_head_dims(run):
-    import torch
+@pytest.mark.parametrize("d", [64, 256])
+def test_host_tail_partial(run, d):
+    """The tail's partial on the host cores (RKV_TAIL_HOST) at head dims 64 and 256, merged with
+    the window's on the GPU."""
     rkv = run.rkv
-    w = gen.make_workload(1, d=64)
-    step("head dim 64: prefill and host tail partial refused")
-    with pytest.raises(rkv.RkvError) as e:
-        run.decode(w, wc=2048, tile_kv=1024, tail="host", prefill=True, q_pos0=w["n_kv"] - 1)
-    assert e.value.status == rkv.RKV_ERR_UNSUPPORTED
+    w = gen.make_workload(3, scale_down=64, d=d)  # q8q4, 40/8 heads, n_kv 4096, wc 2048
     run.ctx.set_tail_mode(rkv.RKV_TAIL_HOST)
     try:
-        with pytest.raises(rkv.RkvError) as e:
-            run.decode(w, wc=2048, tile_kv=1024, tail="host")
-        assert e.value.status == rkv.RKV_ERR_UNSUPPORTED
+        step(f"head dim {d}: host tail partial")
+        O, L = run.decode(w, tail="host")
+        assert run.ctx.stats()["tail_host"] == 1
     finally:
         run.ctx.set_tail_mode(rkv.RKV_TAIL_LIFT)
-    torch.cuda.synchronize()
+    Oref, Lref = oracle_decode(w)
+    assert_close(O, L, Oref, Lref, what=f"d={d} host tail")

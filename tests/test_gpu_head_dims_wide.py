@@ -3,8 +3,8 @@ rkv_lse_merge against the fp64 oracle, as the streaming op of opencoti-llamafile
 0070-rolling-kv lists them among its shapes (fattn.cu, the op's supported head dims): the window
 + tail split with a lifted (both engines) or device-resident tail, every K/V type pair, masks
 with an empty row, the soft-cap, grouped-query rows up to eight per KV head, the empty cache,
-exact single-key V and one-hot K; unsupported pairs and the entry points that take head dim 128
-only are refused."""
+exact single-key V and one-hot K, the tail's partial on the host cores; unsupported pairs are
+refused."""
 import numpy as np
 import pytest
 
@@ -207,21 +207,27 @@ def test_lse_merge_dv512():
 def test_refusals(run):
     import torch
     rkv = run.rkv
-    step("head dims: unsupported pairs and entry points refused")
+    step("head dims: unsupported pairs refused")
     for dk, dv in [(576, 576), (512, 576), (512, 256), (576, 128)]:
         w = gen.make_workload(1, d=dk, dv=dv, k_type=gen.TYPE_F16, v_type=gen.TYPE_F16)
         with pytest.raises(rkv.RkvError) as e:
             run.decode(w, wc=2048, tile_kv=1024, tail="host")
         assert e.value.status in (rkv.RKV_ERR_UNSUPPORTED, rkv.RKV_ERR_ARG), (dk, dv)
-    w = gen.make_workload(1, d=576, dv=512)
-    with pytest.raises(rkv.RkvError) as e:
-        run.decode(w, wc=2048, tile_kv=1024, tail="host", prefill=True, q_pos0=w["n_kv"] - 1)
-    assert e.value.status == rkv.RKV_ERR_UNSUPPORTED
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("dk,dv", DIMS)
+def test_host_tail_partial(run, dk, dv):
+    """The tail's partial on the host cores (RKV_TAIL_HOST), merged with the window's."""
+    rkv = run.rkv
+    w = gen.make_workload(3, scale_down=64, d=dk, dv=dv)  # q8q4, 40/8 heads, n_kv 4096, wc 2048
+    mask = gen.random_mask_f16(np.random.default_rng(dk), 1, w["n_kv"], p_hidden=0.3)
     run.ctx.set_tail_mode(rkv.RKV_TAIL_HOST)
     try:
-        with pytest.raises(rkv.RkvError) as e:
-            run.decode(w, wc=2048, tile_kv=1024, tail="host")
-        assert e.value.status == rkv.RKV_ERR_UNSUPPORTED
+        step(f"head dims {dk}/{dv}: host tail partial with a mask")
+        O, L = run.decode(w, tail="host", mask=mask)
+        assert run.ctx.stats()["tail_host"] == 1
     finally:
         run.ctx.set_tail_mode(rkv.RKV_TAIL_LIFT)
-    torch.cuda.synchronize()
+    Oref, Lref = oracle_decode(w, mask=mask.astype(np.float64))
+    assert_close(O, L, Oref, Lref, what=f"d={dk}/{dv} host tail")

@@ -37,7 +37,8 @@ def run_host(rkv, q, k, v, k_type, v_type, mask=None, kv_pos0=0, q_pos0=-1, scal
     qt = torch.from_numpy(np.ascontiguousarray(q))
     kt, vt = host_cache(k, layout), host_cache(v, layout)
     mt = None if mask is None else torch.from_numpy(np.ascontiguousarray(mask))
-    part = torch.full((n_q, n_head, 130), float("nan"), dtype=torch.float32)
+    dv = gen.values_per_row(v_type, v.shape[-1])
+    part = torch.full((n_q, n_head, 2 + dv), float("nan"), dtype=torch.float32)
     rkv.tail_partial_host(rkv.q_desc(qt), rkv.kv_desc(kt, k_type, layout), rkv.kv_desc(vt, v_type, layout),
                           rkv.mask_desc(mt), kv_pos0, q_pos0, scale, part, softcap=softcap, n_threads=n_threads)
     p = part.numpy().astype(np.float64)
@@ -214,3 +215,23 @@ def test_choose_tail_mode(rkv):
         with pytest.raises(_lib.RkvError) as e:
             rkv.choose_tail_mode(*bad)
         assert e.value.status == _lib.RKV_ERR_ARG
+
+
+@pytest.mark.parametrize("dk,dv", [(64, 64), (256, 256), (512, 512), (576, 512)])
+@pytest.mark.parametrize("kt,vt", [(gen.TYPE_Q8_0, gen.TYPE_Q4_0), (gen.TYPE_F16, gen.TYPE_F16)])
+def test_other_head_dims(rkv, dk, dv, kt, vt):
+    """Head dims other than 128 (patch 0070: the streaming op's shapes): 10 query heads on 2 KV
+    heads, 2 queries, a causal limit and a mask, cell- and head-major."""
+    rng = np.random.default_rng(dk + 7 * kt)
+    n_q, n_cells, kv_pos0 = 2, 1500, 300
+    q, k, v = gen.draw_qkv(rng, 10, n_q, 2, n_cells, d=dk, dv=dv, k_type=kt, v_type=vt)
+    mask = gen.random_mask_f16(rng, n_q, kv_pos0 + n_cells, p_hidden=0.2)
+    scale = 1 / np.sqrt(dk)
+    q_pos0 = kv_pos0 + n_cells - 400  # the last 400 cells are after query 0's position
+    causal = oracle.causal_mask(n_q, kv_pos0 + n_cells, q_pos0)[:, kv_pos0:]
+    ref = oracle_partial(q, k, v, kt, vt, mask[:, kv_pos0:].astype(np.float64) + causal, scale=scale)
+    for layout in ("cell", "head"):
+        host = run_host(rkv, q, k, v, kt, vt, mask=mask, kv_pos0=kv_pos0, q_pos0=q_pos0, scale=scale,
+                        layout=layout)
+        check_partial(host, ref, f"d={dk}/{dv} {layout}")
+

@@ -281,7 +281,7 @@ def lse_merge(partials, n_seg: int, n_rows: int, o, lse=None, stream=None, dv: i
 def tail_partial_host(q, k, v, mask, kv_pos0: int, q_pos0: int, scale: float, partial, softcap: float = 0.0,
                       n_threads: int = 0):
     """Tail partial on the host cores: q, k, v, mask are descriptors of host (CPU) memory,
-    partial a float32 CPU tensor (n_q, n_head, 130) receiving (M, S, VKQ) per row."""
+    partial a float32 CPU tensor (n_q, n_head, 2 + dv) receiving (M, S, VKQ) per row."""
     lib = load()
     check(lib.rkv_tail_partial_host(_ref(q), _ref(k), _ref(v), _ref(mask), int(kv_pos0), int(q_pos0),
                                     float(scale), float(softcap), _ptr(partial), int(n_threads)),

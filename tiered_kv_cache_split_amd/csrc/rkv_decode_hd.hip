@@ -18,6 +18,11 @@
 //   P.V  thread t owns output columns t % dv (+ 256 c for dv = 512) of every row over the
 //        chunk's keys j with j % KS = t / dv (KS = 256 / dv key subsets for dv < 256, so each V
 //        value is dequantised once); the subsets' sums are added through LDS at the end.
+// More than 8 rows per KV head (prefill, or decode with a wide query group) are split into row
+// groups of 8, one workgroup each, adjacent in the grid so that the groups reading one chunk
+// of keys run together.  With a row list (the unified-pool form of llama.cpp PR #29510,
+// flash_attn_ext_rows) key j of sequence b is pool cell rows[j + rows_s * b]; a negative
+// entry, or one past the pool, reads nothing and is hidden.
 #include "rkv_internal.h"
 #include "rkv_unpack.h"
 #include "rkv_wave.h"
@@ -70,17 +75,27 @@ struct HdGeom {
     static_assert(E % 4 == 0 && DK % 32 == 0 && DV % 32 == 0, "whole quant blocks");
 };
 
-// Chunk rows [c0, c0 + KC) of one KV head, words of row r in order; cells at or past c_end read
-// nothing (0).
+// Pool cell of key j: j itself, or rows[j] for a row list (-1: no cell).
+__device__ __forceinline__ int64_t key_cell(const int32_t *rows, int64_t n_pool, int64_t j) {
+    if (!rows) return j;
+    const int32_t c = rows[j];
+    return (c >= 0 && c < n_pool) ? (int64_t)c : -1;
+}
+
+// Chunk rows [c0, c0 + KC) of one KV head, words of row r in order; keys at or past c_end, and
+// keys without a cell, read nothing (0).
 template <int NW, int W, int KC>
 __device__ __forceinline__ void load_rows(uint32_t (&buf)[NW], const uint8_t *base, int64_t s1, int64_t c0, int64_t c_end,
-                                          int tid) {
+                                          const int32_t *rows, int64_t n_pool, int tid) {
 #pragma unroll
     for (int u = 0; u < NW; ++u) {
         const int f = tid + kThreads * u;
         const int r = f / W, w = f % W;
         buf[u] = 0u;
-        if (f < KC * W && c0 + r < c_end) buf[u] = *reinterpret_cast<const uint32_t *>(base + (c0 + r) * s1 + 4 * w);
+        if (f < KC * W && c0 + r < c_end) {
+            const int64_t cell = key_cell(rows, n_pool, c0 + r);
+            if (cell >= 0) buf[u] = *reinterpret_cast<const uint32_t *>(base + cell * s1 + 4 * w);
+        }
     }
 }
 template <int NW, int W, int WP, int KC>
@@ -125,12 +140,20 @@ decode_hd_kernel(const SegParams p) {
     __shared__ float s_alpha[kRmax];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // block = ((b * n_head_kv + g) * n_splits + split) * n_rg + rg: the row groups of one
+    // (split, KV head, sequence) are adjacent
+    const int R_all = p.gqa * p.n_q;
+    const int n_rg = (R_all + kRmax - 1) / kRmax;
     int bid = blockIdx.x;
+    const int rg = bid % n_rg;
+    bid /= n_rg;
     const int split = bid % p.n_splits;
     bid /= p.n_splits;
     const int g = bid % p.n_head_kv;
     const int b = bid / p.n_head_kv;
-    const int R = p.gqa * p.n_q;  // <= kRmax (checked on the host)
+    const int R0 = kRmax * rg;              // first row (rho = i * gqa + r) of this group
+    const int R = min(kRmax, R_all - R0);   // rows of this group; local row rho is row R0 + rho
+    const int32_t *rows = p.rows ? p.rows + (int64_t)b * p.rows_s : nullptr;
 
     const int64_t c_beg = (int64_t)split * p.cells_per_split;
     const int64_t c_end = min(p.n_cells, c_beg + (int64_t)p.cells_per_split);
@@ -140,7 +163,7 @@ decode_hd_kernel(const SegParams p) {
     // Q rows rho = i * gqa + r (query i, head g * gqa + r) in LDS; rows past R are zero
     for (int idx = tid; idx < kRmax * DK; idx += kThreads) {
         const int rho = idx / DK, e = idx % DK;
-        const int r = rho % p.gqa, i = rho / p.gqa;
+        const int r = (R0 + rho) % p.gqa, i = (R0 + rho) / p.gqa;
         const int part = (G::EX > 0 && e >= 512) ? (e - 512) / G::EX : e / G::EM;
         const int off = (G::EX > 0 && e >= 512) ? G::EM + (e - 512) % G::EX : e % G::EM;
         s_q[rho * P * QP + part * QP + off] = rho < R ? (float)p.q[(int64_t)i * p.q_s1 + (int64_t)(g * p.gqa + r) * p.q_s2 + (int64_t)b * p.q_s3 + e]
@@ -162,8 +185,8 @@ decode_hd_kernel(const SegParams p) {
     const int64_t n_ch = c_end > c_beg ? (c_end - c_beg + KC - 1) / KC : 0;
     uint32_t pk[G::NK], pv[G::NV];
     if (n_ch > 0) {
-        load_rows<G::NK, G::KW, KC>(pk, kbase, p.k_s1, c_beg, c_end, tid);
-        load_rows<G::NV, G::VW, KC>(pv, vbase, p.v_s1, c_beg, c_end, tid);
+        load_rows<G::NK, G::KW, KC>(pk, kbase, p.k_s1, c_beg, c_end, rows, p.n_pool, tid);
+        load_rows<G::NV, G::VW, KC>(pv, vbase, p.v_s1, c_beg, c_end, rows, p.n_pool, tid);
     }
     for (int64_t ch = 0; ch < n_ch; ++ch) {
         const int64_t c0 = c_beg + ch * KC;
@@ -172,8 +195,8 @@ decode_hd_kernel(const SegParams p) {
         store_rows<G::NV, G::VW, G::VWP, KC>(pv, s_v, tid);
         __syncthreads();
         if (ch + 1 < n_ch) {  // next chunk in flight during this one
-            load_rows<G::NK, G::KW, KC>(pk, kbase, p.k_s1, c0 + KC, c_end, tid);
-            load_rows<G::NV, G::VW, KC>(pv, vbase, p.v_s1, c0 + KC, c_end, tid);
+            load_rows<G::NK, G::KW, KC>(pk, kbase, p.k_s1, c0 + KC, c_end, rows, p.n_pool, tid);
+            load_rows<G::NV, G::VW, KC>(pv, vbase, p.v_s1, c0 + KC, c_end, rows, p.n_pool, tid);
         }
 
         // ---- Q.K
@@ -253,9 +276,10 @@ decode_hd_kernel(const SegParams p) {
                 float dr = dot[0];
 #pragma unroll
                 for (int k = 1; k < kRmax; ++k) dr = rho == k ? dot[k] : dr;
-                const int i = rho / p.gqa;
+                const int i = (R0 + rho) / p.gqa;
                 float x = CAP ? p.cap_l2 * kLn2 * tanhf(p.cap_cs * dr) : p.scale_log2 * kLn2 * dr;
-                bool vis = j < c_end && (p.q_pos0 < 0 || p.pos0 + j <= p.q_pos0 + i);
+                bool vis = j < c_end && (p.q_pos0 < 0 || p.pos0 + j <= p.q_pos0 + i) &&
+                           (!rows || key_cell(rows, p.n_pool, j) >= 0);
                 if (vis && p.mask) {
                     const float mv = (float)p.mask[p.pos0 + j + (int64_t)i * p.m_s1 + (int64_t)b * p.m_s3];
                     x += mv;
@@ -319,7 +343,7 @@ decode_hd_kernel(const SegParams p) {
     // ---- partials: M and S from the owning waves, VKQ from every thread
     const int slot = p.slot0 + split;
     auto out_row = [&](int rho) {
-        const int r = rho % p.gqa, i = rho / p.gqa;
+        const int r = (R0 + rho) % p.gqa, i = (R0 + rho) / p.gqa;
         return ((int64_t)slot * p.n_rows + (g * p.gqa + r) + (int64_t)p.n_head * (i + (int64_t)p.n_q * b)) * PS;
     };
 #pragma unroll
@@ -382,7 +406,9 @@ __global__ void __launch_bounds__(D) merge_hd_kernel(const float *part, int n_se
 
 template <int DK, int DV, int KT, int VT>
 hipError_t launch_hd(const SegParams &p, hipStream_t s) {
-    const int64_t blocks = (int64_t)p.n_splits * p.n_head_kv * p.n_seq;
+    const int64_t n_rg = ((int64_t)p.gqa * p.n_q + kRmax - 1) / kRmax;
+    const int64_t blocks = (int64_t)p.n_splits * p.n_head_kv * p.n_seq * n_rg;
+    if (blocks > ((int64_t)1 << 31) - 1) return hipErrorInvalidValue;
     if (blocks <= 0) return hipSuccess;
     if (p.cap_l2 != 0.f)
         launch_seg(decode_hd_kernel<DK, DV, KT, VT, true>, dim3((unsigned)blocks), dim3(kThreads), s, p);
@@ -409,7 +435,7 @@ bool head_dims_supported(int dk, int dv) {
 }
 
 hipError_t launch_decode_hd(const SegParams &p, int k_type, int v_type, hipStream_t s) {
-    if (p.rows || p.gqa * p.n_q > kRmax) return hipErrorNotSupported;
+    if (p.gqa * p.n_q < 1) return hipErrorInvalidValue;
     if (p.d == 64 && p.dv == 64) return launch_hd_types<64, 64>(p, k_type, v_type, s);
     if (p.d == 256 && p.dv == 256) return launch_hd_types<256, 256>(p, k_type, v_type, s);
     if (p.d == 512 && p.dv == 512) return launch_hd_types<512, 512>(p, k_type, v_type, s);

@@ -11,7 +11,8 @@
 // row's chunks in chunk order, so the result does not depend on which thread ran which unit.
 //
 // The inner loops use eight-lane vector types compiled for AVX2 + FMA + F16C; the entry points
-// refuse to run on a CPU without them.
+// refuse to run on a CPU without them.  Head dims: dk = dv in {64, 128, 256, 512}, or dk = 576
+// with dv = 512 (the streaming op's shapes, patch 0070 fattn.cu); partial rows are 2 + dv.
 #include "rkv_internal.h"
 
 #include <algorithm>
@@ -52,20 +53,21 @@ RKV_HOST_SIMD __attribute__((always_inline)) inline V ldv(const void *p) {
     return v;
 }
 
-// One 128-value row of K or V in fp32, eight values at a time (q8_0: d*q; q4_0: d*(n-8), byte j
+// One D-value row of K or V in fp32, eight values at a time (q8_0: d*q; q4_0: d*(n-8), byte j
 // holding element j in its low nibble and element j+16 in its high nibble; binary16 as is).
+template <int D>
 RKV_HOST_SIMD __attribute__((always_inline)) inline void dequant_row(const uint8_t *row, int type, float *out) {
     if (type == T_F16) {
-        for (int e = 0; e < kHeadDim; e += 8) st8(out + e, __builtin_convertvector(ldv<h8>(row + 2 * e), f8));
+        for (int e = 0; e < D; e += 8) st8(out + e, __builtin_convertvector(ldv<h8>(row + 2 * e), f8));
     } else if (type == T_Q8_0) {
-        for (int blk = 0; blk < 4; ++blk) {
+        for (int blk = 0; blk < D / 32; ++blk) {
             const uint8_t *b = row + 34 * blk;
             const float d = h2f(ldv<uint16_t>(b));
             for (int e = 0; e < 32; e += 8)
                 st8(out + 32 * blk + e, __builtin_convertvector(ldv<c8>(b + 2 + e), f8) * d);
         }
     } else {  // T_Q4_0
-        for (int blk = 0; blk < 4; ++blk) {
+        for (int blk = 0; blk < D / 32; ++blk) {
             const uint8_t *b = row + 18 * blk;
             const float d = h2f(ldv<uint16_t>(b));
             for (int j = 0; j < 16; j += 8) {
@@ -100,22 +102,23 @@ RKV_HOST_SIMD inline f8 exp8(f8 x) {
 }
 
 // Partial of rows (g*gqa + r0 + r, i), r < R, over keys [c0, c1): out[r][0] = M, [1] = S,
-// [2 + d] = VKQ.  Per block of 32 keys: the visible K rows are dequantised once, the R scores
-// of a key are formed together (one pass over its K row), the weights exponentiated eight at a
-// time, and V accumulated with the R rows' accumulators of one eight-value slice in registers.
-template <int R>
+// [2 + e] = VKQ (row stride 2 + DV).  Per block of 32 keys: the visible K rows are dequantised
+// once, the R scores of a key are formed together (one pass over its K row), the weights
+// exponentiated eight at a time, and V accumulated with the R rows' accumulators of one
+// eight-value slice in registers.
+template <int R, int DK, int DV>
 RKV_HOST_SIMD void run_unit(const HostTailArgs &a, int g, int r0, int i, int64_t c0, int64_t c1, float *out) {
     const int gqa = a.n_head / a.n_head_kv;
-    alignas(32) float qv[R][kHeadDim];
-    alignas(32) float acc[R][kHeadDim];
-    alignas(32) float kt[kBlk][kHeadDim];
-    alignas(32) float vt[kBlk][kHeadDim];
+    alignas(32) float qv[R][DK];
+    alignas(32) float acc[R][DV];
+    alignas(32) float kt[kBlk][DK];
+    alignas(32) float vt[kBlk][DV];
     alignas(32) float sc[R][kBlk];
     float m[R], l[R];
     for (int r = 0; r < R; ++r) {
         const uint16_t *q = a.q + (int64_t)i * a.q_s1 + (int64_t)(g * gqa + r0 + r) * a.q_s2;
-        for (int e = 0; e < kHeadDim; ++e) qv[r][e] = a.scale * h2f(q[e]);
-        for (int e = 0; e < kHeadDim; ++e) acc[r][e] = 0.f;
+        for (int e = 0; e < DK; ++e) qv[r][e] = a.scale * h2f(q[e]);
+        for (int e = 0; e < DV; ++e) acc[r][e] = 0.f;
         m[r] = -INFINITY;
         l[r] = 0.f;
     }
@@ -141,7 +144,7 @@ RKV_HOST_SIMD void run_unit(const HostTailArgs &a, int g, int r0, int i, int64_t
         }
         if (!any) continue;
         for (int jj = 0; jj < nb; ++jj)
-            if (vis[jj]) dequant_row(kb + (j0 + jj) * a.k_s1, a.k_type, kt[jj]);
+            if (vis[jj]) dequant_row<DK>(kb + (j0 + jj) * a.k_s1, a.k_type, kt[jj]);
         // scores: one pass over each K row for all R rows
         for (int jj = 0; jj < kBlk; ++jj) {
             if (!vis[jj]) {
@@ -150,7 +153,7 @@ RKV_HOST_SIMD void run_unit(const HostTailArgs &a, int g, int r0, int i, int64_t
             }
             f8 s8[R];
             for (int r = 0; r < R; ++r) s8[r] = 0.f;
-            for (int e = 0; e < kHeadDim; e += 8) {
+            for (int e = 0; e < DK; e += 8) {
                 const f8 kv = ld8(&kt[jj][e]);
                 for (int r = 0; r < R; ++r) s8[r] = __builtin_elementwise_fma(ld8(&qv[r][e]), kv, s8[r]);
             }
@@ -171,7 +174,7 @@ RKV_HOST_SIMD void run_unit(const HostTailArgs &a, int g, int r0, int i, int64_t
             if (bm > m[r]) {
                 const float alpha = m[r] == -INFINITY ? 0.f : std::exp(m[r] - bm);
                 l[r] *= alpha;
-                for (int e = 0; e < kHeadDim; e += 8) st8(&acc[r][e], ld8(&acc[r][e]) * alpha);
+                for (int e = 0; e < DV; e += 8) st8(&acc[r][e], ld8(&acc[r][e]) * alpha);
                 m[r] = bm;
             }
             f8 lsum = 0.f;
@@ -184,9 +187,9 @@ RKV_HOST_SIMD void run_unit(const HostTailArgs &a, int g, int r0, int i, int64_t
             l[r] += hsum8(lsum);
         }
         for (int jj = 0; jj < nb; ++jj)
-            if (vis[jj]) dequant_row(vb + (j0 + jj) * a.v_s1, a.v_type, vt[jj]);
+            if (vis[jj]) dequant_row<DV>(vb + (j0 + jj) * a.v_s1, a.v_type, vt[jj]);
         // VKQ: the R accumulators of one 8-value slice stay in registers over the block's keys
-        for (int e = 0; e < kHeadDim; e += 8) {
+        for (int e = 0; e < DV; e += 8) {
             f8 ac[R];
             for (int r = 0; r < R; ++r) ac[r] = ld8(&acc[r][e]);
             for (int jj = 0; jj < nb; ++jj) {
@@ -198,27 +201,36 @@ RKV_HOST_SIMD void run_unit(const HostTailArgs &a, int g, int r0, int i, int64_t
         }
     }
     for (int r = 0; r < R; ++r) {
-        float *o = out + (size_t)r * kPartialStride;
+        float *o = out + (size_t)r * (2 + DV);
         o[0] = m[r];
         o[1] = l[r];
-        std::memcpy(o + 2, acc[r], kHeadDim * sizeof(float));
+        std::memcpy(o + 2, acc[r], DV * sizeof(float));
     }
 }
 
 // Rows of a unit: the gqa query heads of a KV head, taken eight at a time.
 constexpr int kMaxR = 8;
 
-void run_rows(const HostTailArgs &a, int g, int r0, int R, int i, int64_t c0, int64_t c1, float *out) {
+template <int DK, int DV>
+void run_rows_d(const HostTailArgs &a, int g, int r0, int R, int i, int64_t c0, int64_t c1, float *out) {
     switch (R) {
-        case 1: run_unit<1>(a, g, r0, i, c0, c1, out); break;
-        case 2: run_unit<2>(a, g, r0, i, c0, c1, out); break;
-        case 3: run_unit<3>(a, g, r0, i, c0, c1, out); break;
-        case 4: run_unit<4>(a, g, r0, i, c0, c1, out); break;
-        case 5: run_unit<5>(a, g, r0, i, c0, c1, out); break;
-        case 6: run_unit<6>(a, g, r0, i, c0, c1, out); break;
-        case 7: run_unit<7>(a, g, r0, i, c0, c1, out); break;
-        default: run_unit<8>(a, g, r0, i, c0, c1, out); break;
+        case 1: run_unit<1, DK, DV>(a, g, r0, i, c0, c1, out); break;
+        case 2: run_unit<2, DK, DV>(a, g, r0, i, c0, c1, out); break;
+        case 3: run_unit<3, DK, DV>(a, g, r0, i, c0, c1, out); break;
+        case 4: run_unit<4, DK, DV>(a, g, r0, i, c0, c1, out); break;
+        case 5: run_unit<5, DK, DV>(a, g, r0, i, c0, c1, out); break;
+        case 6: run_unit<6, DK, DV>(a, g, r0, i, c0, c1, out); break;
+        case 7: run_unit<7, DK, DV>(a, g, r0, i, c0, c1, out); break;
+        default: run_unit<8, DK, DV>(a, g, r0, i, c0, c1, out); break;
     }
+}
+
+void run_rows(const HostTailArgs &a, int g, int r0, int R, int i, int64_t c0, int64_t c1, float *out) {
+    if (a.d == 64) run_rows_d<64, 64>(a, g, r0, R, i, c0, c1, out);
+    else if (a.d == 256) run_rows_d<256, 256>(a, g, r0, R, i, c0, c1, out);
+    else if (a.d == 512) run_rows_d<512, 512>(a, g, r0, R, i, c0, c1, out);
+    else if (a.d == 576) run_rows_d<576, 512>(a, g, r0, R, i, c0, c1, out);
+    else run_rows_d<kHeadDim, kHeadDim>(a, g, r0, R, i, c0, c1, out);
 }
 
 }  // namespace
@@ -244,7 +256,8 @@ void host_tail_partial(const HostTailArgs &a, int n_threads) {
     n_chunks = std::max<int64_t>(1, std::min<int64_t>(n_chunks, (a.n_cells + 1023) / 1024));
     const int64_t chunk = a.n_cells > 0 ? (a.n_cells + n_chunks - 1) / n_chunks : 0;
     const int64_t n_units = groups * n_chunks;
-    std::vector<float> parts((size_t)n_units * kMaxR * kPartialStride);
+    const int ps = 2 + a.dv;  // partial row stride
+    std::vector<float> parts((size_t)n_units * kMaxR * ps);
     auto rows_of = [&](int rg) { return std::min(kMaxR, gqa - rg * kMaxR); };
     std::atomic<int64_t> next{0};
     auto worker = [&]() {
@@ -255,7 +268,7 @@ void host_tail_partial(const HostTailArgs &a, int n_threads) {
             t /= n_rg;
             const int g = (int)(t % a.n_head_kv), i = (int)(t / a.n_head_kv);
             const int64_t c0 = std::min(a.n_cells, c * chunk), c1 = std::min(a.n_cells, c0 + chunk);
-            run_rows(a, g, rg * kMaxR, rows_of(rg), i, c0, c1, &parts[(size_t)u * kMaxR * kPartialStride]);
+            run_rows(a, g, rg * kMaxR, rows_of(rg), i, c0, c1, &parts[(size_t)u * kMaxR * ps]);
         }
     };
     const int nt = (int)std::min<int64_t>(threads, n_units);
@@ -273,24 +286,24 @@ void host_tail_partial(const HostTailArgs &a, int n_threads) {
         const int rg = (int)(gr % n_rg);
         const int g = (int)((gr / n_rg) % a.n_head_kv), i = (int)(gr / n_rg / a.n_head_kv);
         for (int r = 0; r < rows_of(rg); ++r) {
-            auto part = [&](int64_t c) { return &parts[((size_t)(gr * n_chunks + c) * kMaxR + r) * kPartialStride]; };
+            auto part = [&](int64_t c) { return &parts[((size_t)(gr * n_chunks + c) * kMaxR + r) * ps]; };
             float M = -INFINITY;
             for (int64_t c = 0; c < n_chunks; ++c) M = std::max(M, part(c)[0]);
-            float *o = a.partial + (size_t)((g * gqa + rg * kMaxR + r) + (int64_t)a.n_head * i) * kPartialStride;
+            float *o = a.partial + (size_t)((g * gqa + rg * kMaxR + r) + (int64_t)a.n_head * i) * ps;
             float S = 0.f;
-            float V[kHeadDim] = {};
+            float V[512] = {};
             if (M > -INFINITY) {
                 for (int64_t c = 0; c < n_chunks; ++c) {
                     const float *pc = part(c);
                     if (pc[0] == -INFINITY) continue;
                     const float w = std::exp(pc[0] - M);
                     S += pc[1] * w;
-                    for (int e = 0; e < kHeadDim; ++e) V[e] += pc[2 + e] * w;
+                    for (int e = 0; e < a.dv; ++e) V[e] += pc[2 + e] * w;
                 }
             }
             o[0] = M;
             o[1] = S;
-            std::memcpy(o + 2, V, sizeof V);
+            std::memcpy(o + 2, V, (size_t)a.dv * sizeof(float));
         }
     }
 }

@@ -165,7 +165,9 @@ struct HostTailArgs {
     int64_t q_pos0;           // >= 0: query i at q_pos0 + i sees positions <= its own
     int n_head, n_head_kv, n_q;
     float scale, softcap;     // softcap 0: none
-    float *partial;           // [n_head * n_q][2 + 128], row h + n_head * i
+    float *partial;           // [n_head * n_q][2 + dv], row h + n_head * i
+    int d = kHeadDim;         // head dims of Q/K and V: equal in 64..512, or 576 / 512
+    int dv = kHeadDim;
 };
 bool host_tail_supported();          // the CPU has AVX2, FMA and F16C
 int host_tail_threads(int requested);  // requested > 0, else the hardware threads (<= 16)

@@ -495,9 +495,10 @@ int attn_window_tail(rkv_ctx *ctx, const rkv_tensor *q, const rkv_tensor *k_win,
                      const rkv_tensor *v_win, const rkv_tensor *k_tail, const rkv_tensor *v_tail,
                      const rkv_tensor *mask, int64_t wc, int64_t tile_kv, float scale,
                      int64_t q_pos0, bool mfma, float *o, float *lse, hipStream_t stream,
-                     float *ext_partials = nullptr, int64_t ext_cap = 0) {
+                     float *ext_partials = nullptr, int64_t ext_cap = 0, bool prefill = false) {
     if (!ctx) return fail(RKV_ERR_ARG, "ctx is NULL");
-    // decode takes dk = dv in 64, 128, 256, 512 and the pair dk = 576 / dv = 512; prefill 128 only
+    // dk = dv in 64, 128, 256, 512 and the pair dk = 576 / dv = 512 (head dim 128 prefill on the
+    // matrix-core kernel, everything else on the vector kernels)
     const bool any_d = !mfma;
     int st = check_q(q, false, any_d);
     if (st) return st;
@@ -527,7 +528,7 @@ int attn_window_tail(rkv_ctx *ctx, const rkv_tensor *q, const rkv_tensor *k_win,
         if (n_tail > 0) {
             const Mem a = pointer_kind(k_tail->data), b = pointer_kind(v_tail->data);
             if (a != b) return fail(RKV_ERR_ARG, "k_tail and v_tail live in different memory kinds");
-            if (a == Mem::Other && (ctx->tail_mode != RKV_TAIL_HOST || mfma))
+            if (a == Mem::Other && (ctx->tail_mode != RKV_TAIL_HOST || mfma || prefill))
                 return fail(RKV_ERR_ARG, "tail is neither device nor pinned host memory (pageable memory cannot be lifted)");
             tail_kind = a;
         }
@@ -544,7 +545,9 @@ int attn_window_tail(rkv_ctx *ctx, const rkv_tensor *q, const rkv_tensor *k_win,
         return fail(RKV_ERR_UNSUPPORTED, "head dims dk=%d, dv=%d not supported (dk = dv in 64, 128, 256, 512, or 576/512)",
                     d, dv);
     const int64_t ps = 2 + dv;  // partial row stride
-    if (!mfma && gqa * n_q > kMaxRowsVec)
+    // the head-dim-128 decode kernels take up to 8 rows per KV head; the kernel for other head
+    // dims takes any number in row groups of 8
+    if (!mfma && d == kHeadDim && gqa * n_q > kMaxRowsVec)
         return fail(RKV_ERR_UNSUPPORTED, "decode handles n_q*gqa <= %d rows per KV head (got %lld); use rkv_attn_prefill",
                     kMaxRowsVec, (long long)(gqa * n_q));
     const int64_t n_kv = wc + n_tail;
@@ -573,9 +576,8 @@ int attn_window_tail(rkv_ctx *ctx, const rkv_tensor *q, const rkv_tensor *k_win,
 
     // ---- plan: window segment, then tail (in place, lifted tiles through the ring, or a
     // partial computed on the host cores)
-    const bool host_tail = n_tail > 0 && tail_kind != Mem::Device && ctx->tail_mode == RKV_TAIL_HOST && !mfma;
-    if (host_tail && (d != kHeadDim || dv != kHeadDim))
-        return fail(RKV_ERR_UNSUPPORTED, "the host tail partial takes head dim 128");
+    // (prefill always computes the tail on the GPU)
+    const bool host_tail = n_tail > 0 && tail_kind != Mem::Device && ctx->tail_mode == RKV_TAIL_HOST && !mfma && !prefill;
     // RKV_LIFT_DIRECT (contrast only): the segment kernels read a pinned tail in place through
     // its device view, in their own access order, with no lift
     const bool direct = n_tail > 0 && tail_kind == Mem::PinnedHost && !host_tail && ctx->lift_mode == RKV_LIFT_DIRECT;
@@ -747,6 +749,8 @@ int attn_window_tail(rkv_ctx *ctx, const rkv_tensor *q, const rkv_tensor *k_win,
         ha.scale = scale;
         ha.softcap = ctx->softcap;
         ha.partial = static_cast<float *>(ctx->hpart);
+        ha.d = d;
+        ha.dv = dv;
         const auto t0 = std::chrono::steady_clock::now();
         try {
             host_tail_partial(ha, ctx->host_threads);
@@ -1028,13 +1032,17 @@ int rkv_tail_partial_host(const rkv_tensor *q, const rkv_tensor *k, const rkv_te
                           int n_threads) {
     if (!q || !q->data) return fail(RKV_ERR_ARG, "q is NULL");
     if (q->type != RKV_TYPE_F16) return fail(RKV_ERR_UNSUPPORTED, "q must be F16");
-    if (q->ne[0] != kHeadDim) return fail(RKV_ERR_UNSUPPORTED, "q head dim must be 128");
+    if (!head_dim_supported((int)std::min<int64_t>(q->ne[0], 1 << 20)))
+        return fail(RKV_ERR_UNSUPPORTED, "q head dim %lld not supported", (long long)q->ne[0]);
     if (q->ne[1] <= 0 || q->ne[2] <= 0 || q->ne[3] != 1) return fail(RKV_ERR_ARG, "q: bad shape");
     if (q->nb[0] != 2 || q->nb[1] % 2 != 0 || q->nb[2] % 2 != 0 || q->nb[1] < 0 || q->nb[2] < 0)
         return fail(RKV_ERR_ARG, "q rows must be contiguous and strides even");
     int st;
-    if ((st = check_kv(k, "k", true)) || (st = check_kv(v, "v", false))) return st;
+    if ((st = check_kv(k, "k", true, true)) || (st = check_kv(v, "v", false, true))) return st;
     if (k->ne[1] != v->ne[1] || k->ne[2] != v->ne[2]) return fail(RKV_ERR_ARG, "k and v disagree in shape");
+    if (k->ne[0] != q->ne[0]) return fail(RKV_ERR_ARG, "k head dim must equal q's");
+    if (!head_dims_supported((int)q->ne[0], (int)v->ne[0]))
+        return fail(RKV_ERR_UNSUPPORTED, "head dims dk=%lld, dv=%lld not supported", (long long)q->ne[0], (long long)v->ne[0]);
     const int64_t n_q = q->ne[1], n_head = q->ne[2], n_head_kv = k->ne[2], n_cells = k->ne[1];
     if (n_head % n_head_kv != 0) return fail(RKV_ERR_ARG, "n_head %% n_head_kv != 0");
     if (kv_pos0 < 0) return fail(RKV_ERR_ARG, "kv_pos0 < 0");
@@ -1074,6 +1082,8 @@ int rkv_tail_partial_host(const rkv_tensor *q, const rkv_tensor *k, const rkv_te
     ha.scale = scale;
     ha.softcap = softcap;
     ha.partial = partial;
+    ha.d = (int)q->ne[0];
+    ha.dv = (int)v->ne[0];
     try {
         host_tail_partial(ha, n_threads);
     } catch (...) {
@@ -1193,8 +1203,11 @@ int rkv_attn_decode(rkv_ctx *ctx, const rkv_tensor *q, const rkv_tensor *k_win, 
 int rkv_attn_prefill(rkv_ctx *ctx, const rkv_tensor *q, const rkv_tensor *k_win, const rkv_tensor *v_win,
                      const rkv_tensor *k_tail, const rkv_tensor *v_tail, const rkv_tensor *mask, int64_t wc,
                      int64_t tile_kv, float scale, int64_t q_pos0, float *o, float *lse, void *stream) {
-    return attn_window_tail(ctx, q, k_win, v_win, k_tail, v_tail, mask, wc, tile_kv, scale, q_pos0, true, o, lse,
-                            static_cast<hipStream_t>(stream));
+    // head dim 128 runs on the matrix-core prefill kernel; the other head dims on the vector
+    // kernel for them, in row groups of 8 (it takes the causal rule and the mask alike)
+    const bool mfma = !q || q->ne[0] == kHeadDim;
+    return attn_window_tail(ctx, q, k_win, v_win, k_tail, v_tail, mask, wc, tile_kv, scale, q_pos0, mfma, o, lse,
+                            static_cast<hipStream_t>(stream), nullptr, 0, true);
 }
 
 int rkv_attn_rows(rkv_ctx *ctx, const rkv_tensor *q, const rkv_tensor *k_pool, const rkv_tensor *v_pool,
@@ -1202,10 +1215,16 @@ int rkv_attn_rows(rkv_ctx *ctx, const rkv_tensor *q, const rkv_tensor *k_pool, c
                   void *stream_) {
     hipStream_t stream = static_cast<hipStream_t>(stream_);
     if (!ctx) return fail(RKV_ERR_ARG, "ctx is NULL");
-    int st = check_q(q, true);
+    int st = check_q(q, true, true);
     if (st) return st;
-    if ((st = check_kv(k_pool, "k_pool", true)) || (st = check_kv(v_pool, "v_pool", false))) return st;
+    if ((st = check_kv(k_pool, "k_pool", true, true)) || (st = check_kv(v_pool, "v_pool", false, true))) return st;
     if (k_pool->ne[1] != v_pool->ne[1] || k_pool->ne[2] != v_pool->ne[2]) return fail(RKV_ERR_ARG, "k_pool and v_pool disagree in shape");
+    const int d = (int)q->ne[0], dv = (int)v_pool->ne[0];
+    if (k_pool->ne[0] != d) return fail(RKV_ERR_ARG, "k_pool head dim must equal Q's");
+    if (!head_dims_supported(d, dv))
+        return fail(RKV_ERR_UNSUPPORTED, "head dims dk=%d, dv=%d not supported (dk = dv in 64, 128, 256, 512, or 576/512)",
+                    d, dv);
+    const int64_t ps = 2 + dv;  // partial row stride
     if (n_kv < 0 || n_kv >= ((int64_t)1 << 31)) return fail(RKV_ERR_ARG, "bad n_kv");
     if (!std::isfinite(scale)) return fail(RKV_ERR_ARG, "scale is not finite");
     if (!o) return fail(RKV_ERR_ARG, "o is NULL");
@@ -1213,7 +1232,8 @@ int rkv_attn_rows(rkv_ctx *ctx, const rkv_tensor *q, const rkv_tensor *k_pool, c
     const int64_t n_head_kv = k_pool->ne[2];
     if (n_head % n_head_kv != 0) return fail(RKV_ERR_ARG, "n_head %% n_head_kv != 0");
     const int64_t gqa = n_head / n_head_kv;
-    if (gqa * n_q > kMaxRowsVec) return fail(RKV_ERR_UNSUPPORTED, "rows attention handles n_q*gqa <= %d", kMaxRowsVec);
+    if (d == kHeadDim && gqa * n_q > kMaxRowsVec)
+        return fail(RKV_ERR_UNSUPPORTED, "rows attention at head dim 128 handles n_q*gqa <= %d", kMaxRowsVec);
     if ((st = check_mask(mask, n_kv, n_q, n_seq))) return st;
     if (n_kv > 0 && (st = check_device_ptr(kv_rows, "kv_rows"))) return st;
     if (k_pool->ne[1] > 0 && ((st = check_device_ptr(k_pool->data, "k_pool")) || (st = check_device_ptr(v_pool->data, "v_pool")))) return st;
@@ -1236,11 +1256,13 @@ int rkv_attn_rows(rkv_ctx *ctx, const rkv_tensor *q, const rkv_tensor *k_pool, c
     p.scale_log2 = scale * 1.4426950408889634f;
     fill_softcap(p, ctx, scale);
     p.n_rows = n_head * n_q * n_seq;
+    p.d = d;
+    p.dv = dv;
     const Seg pool{static_cast<const uint8_t *>(k_pool->data), static_cast<const uint8_t *>(v_pool->data),
                    k_pool->nb[1], k_pool->nb[2], v_pool->nb[1], v_pool->nb[2], n_kv, 0};
     const SegPlan plan = plan_segment(ctx, p, pool, false, k_pool->type, v_pool->type);
     const int slots = plan.n_splits;
-    if ((st = ensure_partials(ctx, (int64_t)slots * p.n_rows * kPartialStride, stream))) return st;
+    if ((st = ensure_partials(ctx, (int64_t)std::max(1, slots) * p.n_rows * ps, stream))) return st;
     p.partials = ctx->partials;
     ctx->stats = rkv_stats{};
     int slot = 0;
@@ -1267,6 +1289,16 @@ int rkv_attn_rows(rkv_ctx *ctx, const rkv_tensor *q, const rkv_tensor *k_pool, c
         mr = MergeRange{ctx->pair_range, (int)n_head, (int)(gqa * plan.cell_hw), (int)(n_head_kv / plan.cell_hw),
                         n_head * n_q};
         ranged = true;
+    }
+    if (d != kHeadDim) {
+        // other head dims: the vector kernel over the row list, then the merge with row stride
+        // 2 + dv (no partial at all gives every row O = 0 and LSE = -inf)
+        if (n_kv > 0 && (st = run_segment(ctx, p, pool, false, k_pool->type, v_pool->type, slot, stream))) return st;
+        ctx->stats.splits_window = slot;
+        ctx->stats.n_partials = slot;
+        hipError_t e = launch_merge_hd(ctx->partials, slot, p.n_rows, dv, o, lse, stream);
+        if (e != hipSuccess) return hip_fail(e, "merge launch");
+        return RKV_OK;
     }
     if (n_kv > 0) {
         if ((st = run_segment(ctx, p, pool, false, k_pool->type, v_pool->type, slot, stream))) return st;
