@@ -286,6 +286,31 @@ def test_large_logits_need_the_true_running_max(run, kt, vt):
 
 # ---- matrix-core decode kernel (cell-major q8_0 K / q4_0 V, eight KV heads per workgroup)
 
+@pytest.mark.parametrize("n_head_kv,n_head,n_q", [(4, 4, 1), (4, 20, 1), (4, 32, 1), (4, 8, 3), (2, 2, 1),
+                                                  (2, 10, 1), (2, 16, 1), (6, 24, 1), (12, 96, 1)])
+def test_mma_decode_smaller_head_groups(run, n_head_kv, n_head, n_q):
+    """Groups of 4 or 2 KV heads per workgroup (n_head_kv not a multiple of 8)."""
+    w = gen.make_workload(2, scale_down=32, n_head=n_head, n_head_kv=n_head_kv, n_q=n_q)
+    step(f"decode q8q4 {n_head_kv} kv heads n_head={n_head} n_q={n_q} wc=2500 tile=900")
+    O, L = run.decode(w, wc=2500, tile_kv=900, tail="host")
+    assert run.ctx.stats()["kernel_variant"] == 3
+    Oref, Lref = oracle_decode(w)
+    assert_close(O, L, Oref, Lref, what=f"mma kv heads {n_head_kv}")
+
+
+@pytest.mark.parametrize("kt,vt", [(gen.TYPE_Q8_0, gen.TYPE_Q4_0), (gen.TYPE_Q8_0, gen.TYPE_F16)])
+@pytest.mark.parametrize("n_head,n_head_kv,n_q", [(24, 4, 1), (28, 4, 1), (32, 4, 1), (8, 1, 1), (4, 1, 2)])
+def test_many_rows_per_head_major_kv_head(run, kt, vt, n_head, n_head_kv, n_q):
+    """Head-major caches with q8_0 K and 6 to 8 rows per KV head run on the head-dim kernel at
+    128 (rows in groups of 8)."""
+    w = gen.make_workload(2, scale_down=32, n_head=n_head, n_head_kv=n_head_kv, n_q=n_q, k_type=kt, v_type=vt)
+    mask = gen.random_mask_f16(np.random.default_rng(n_head + n_q), n_q, w["n_kv"], p_hidden=0.2)
+    step(f"decode head-major k={kt} v={vt} heads {n_head}/{n_head_kv} n_q {n_q}")
+    O, L = run.decode(w, wc=2500, tile_kv=900, tail="host", layout="head", mask=mask)
+    assert run.ctx.stats()["kernel_variant"] == 5
+    Oref, Lref = oracle_decode(w, mask=mask.astype(np.float64))
+    assert_close(O, L, Oref, Lref, what=f"head-major {n_head}/{n_head_kv}/{n_q}")
+
 @pytest.mark.parametrize("n_head,n_q", [(8, 1), (16, 1), (24, 1), (32, 1), (40, 1), (48, 1), (56, 1), (64, 1),
                                         (32, 2), (16, 3)])
 def test_mma_decode_row_counts(run, n_head, n_q):

@@ -1,9 +1,9 @@
 """Exact dequantisation where the hot kernels run it, with edge values end to end.
 
 * V: Q = 0 and a mask that leaves one key visible make every softmax weight exactly 1, so O
-  must equal that key's dequantised V row bit for bit -- through the matrix-core decode kernel,
-  the vector decode kernels (cell-major groups and per-head), the head-dim 64/256 kernel and the
-  prefill kernel.  The visible V rows hold nibbles 0 and 15 and scales that are zero, negative,
+  must equal that key's dequantised V row bit for bit -- through the matrix-core decode kernel
+  (groups of 8, 4 and 2 KV heads), the per-head vector kernel, the head-dim kernel (at 64, 256
+  and at 128 for 8 rows per KV head) and the prefill kernel.  The visible V rows hold nibbles 0 and 15 and scales that are zero, negative,
   binary16 subnormal and 65504.
 * K: one-hot Q and a single visible key make the LSE equal scale * d * q of one code; rounding
   d*q to binary16 anywhere on the path would move it by ~1e-4 relative, the exact path by
@@ -91,8 +91,10 @@ def assert_bits(got, want, what):
 # (name, n_head, n_head_kv, layout, d, expected kernel variant)
 DECODE_PATHS = [
     ("decode_mma", 40, 8, "cell", 128, 3),
-    ("vector_cell", 16, 4, "cell", 128, 2),
+    ("decode_mma_hw4", 16, 4, "cell", 128, 3),
+    ("decode_mma_hw2", 16, 2, "cell", 128, 3),
     ("vector_head", 16, 4, "head", 128, 0),
+    ("head_dim_kernel_at_128", 32, 4, "head", 128, 5),
     ("head_dim_64", 16, 4, "cell", 64, 5),
     ("head_dim_256", 16, 4, "cell", 256, 5),
 ]

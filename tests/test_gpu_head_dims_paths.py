@@ -104,3 +104,14 @@ def test_prefill_keeps_the_tail_on_the_gpu(run):
         run.ctx.set_tail_mode(rkv.RKV_TAIL_LIFT)
     Oref, Lref = oracle_decode(w, mask=oracle.causal_mask(8, w["n_kv"], w["q_pos0"]))
     assert_close(O, L, Oref, Lref, what="prefill d=64 tail on the GPU")
+
+
+def test_rows_q8q4_eight_rows_per_kv_head_at_128(run):
+    """Row lists over a q8_0 / q4_0 pool with 8 rows per KV head at head dim 128: the head-dim
+    kernel instantiated at 128 (the per-head vector kernel would spill its registers)."""
+    w = gen.make_workload(4, scale_down=16, n_head=16, n_head_kv=2, k_type=gen.TYPE_Q8_0, v_type=gen.TYPE_Q4_0)
+    step("rows q8q4 at 128, 8 rows per KV head")
+    O, L = run.rows(w)
+    assert run.ctx.stats()["kernel_variant"] == 5
+    Oref, Lref = oracle_rows(w)
+    assert_close(O, L, Oref, Lref, what="rows q8q4 128 gqa 8")

@@ -715,10 +715,8 @@ template <int KT, int VT, int R>
 hipError_t launch_decode_r(const SegParams &p, hipStream_t s, int *occupancy) {
     if (p.cell_hw > 0) {
         if constexpr (KT == T_Q8_0 && VT == T_Q4_0) {
+            // groups of 8, 4 or 2 KV heads: the matrix-core kernel
             if (decode_mma_ok(p)) return launch_decode_mma(p, s, occupancy);
-            if (p.cell_hw == 8) return launch_cell<KT, VT, R, 8>(p, s, occupancy);
-            if (p.cell_hw == 4) return launch_cell<KT, VT, R, 4>(p, s, occupancy);
-            if (p.cell_hw == 2) return launch_cell<KT, VT, R, 2>(p, s, occupancy);
         }
         if constexpr (KT == T_F16 && VT == T_F16) {
             if (decode_mma16_ok(p)) return launch_decode_mma16(p, s, occupancy);
@@ -727,12 +725,18 @@ hipError_t launch_decode_r(const SegParams &p, hipStream_t s, int *occupancy) {
         return hipErrorInvalidValue;
     }
     if (occupancy) return hipErrorInvalidValue;
-    const int64_t blocks = (int64_t)p.n_splits * p.n_head_kv * p.n_seq;
-    if (p.rows)
-        launch_seg(decode_seg_kernel<KT, VT, R, true>, dim3((unsigned)blocks), dim3(64 * kWaves), s, p);
-    else
-        launch_seg(decode_seg_kernel<KT, VT, R, false>, dim3((unsigned)blocks), dim3(64 * kWaves), s, p);
-    return hipGetLastError();
+    // with q8_0 K and 6 or more rows per KV head the per-head kernel's register arrays spill;
+    // the kernel for the other head dims (instantiated at 128, rows in groups of 8) does not
+    if constexpr (KT == T_Q8_0 && R >= 6) {
+        return launch_decode_hd(p, KT, VT, s);
+    } else {
+        const int64_t blocks = (int64_t)p.n_splits * p.n_head_kv * p.n_seq;
+        if (p.rows)
+            launch_seg(decode_seg_kernel<KT, VT, R, true>, dim3((unsigned)blocks), dim3(64 * kWaves), s, p);
+        else
+            launch_seg(decode_seg_kernel<KT, VT, R, false>, dim3((unsigned)blocks), dim3(64 * kWaves), s, p);
+        return hipGetLastError();
+    }
 }
 
 template <int KT, int VT>
@@ -787,7 +791,7 @@ bool decode_kernel_persistent(const SegParams &p, int k_type, int v_type) {
 
 int decode_kernel_variant(const SegParams &p, int k_type, int v_type) {
     if (p.d != kHeadDim) return RKV_KERNEL_DECODE_HD;
-    if (p.cell_hw <= 0) return RKV_KERNEL_DECODE_HEAD;
+    if (p.cell_hw <= 0) return (k_type == T_Q8_0 && p.gqa * p.n_q >= 6) ? RKV_KERNEL_DECODE_HD : RKV_KERNEL_DECODE_HEAD;
     if (k_type == T_Q8_0 && v_type == T_Q4_0 && decode_mma_ok(p)) return RKV_KERNEL_DECODE_CELL_MFMA;
     if (k_type == T_F16 && v_type == T_F16 && decode_mma16_ok(p)) return RKV_KERNEL_DECODE_CELL_MFMA16;
     return RKV_KERNEL_DECODE_CELL;

@@ -40,12 +40,14 @@ template <int T, int D> constexpr int hd_row_bytes() { return T == T_F16 ? 2 * D
 
 __device__ __forceinline__ float h2f_bits(uint32_t x) { return f16_bits_to_f32(x); }
 
-// Sum over each aligned group of P lanes (4 or 16), in every lane of the group: DPP quad swaps,
-// then rotations by 4 and 8 inside a 16-lane row.
+// Sum over each aligned group of P lanes (4, 8 or 16), in every lane of the group: DPP quad
+// swaps; for 8 lanes the mirror inside each half row (lane i and 7 - i: the two quads); for 16
+// rotations by 4 and 8 inside a 16-lane row.
 template <int P>
 __device__ __forceinline__ float group_sum(float x) {
     x += dpp_f<kQuadSwap1>(x);
     x += dpp_f<kQuadSwap2>(x);
+    if constexpr (P == 8) x += dpp_f<kRowHalfMirror>(x);
     if constexpr (P == 16) {
         x += dpp_f<kRowRor4>(x);
         x += dpp_f<kRowRor8>(x);
@@ -55,7 +57,7 @@ __device__ __forceinline__ float group_sum(float x) {
 
 template <int DK, int DV, int KT, int VT>
 struct HdGeom {
-    static constexpr int KC = DK == 64 ? 64 : 16;          // keys per chunk
+    static constexpr int KC = DK == 64 ? 64 : (DK == 128 ? 32 : 16);  // keys per chunk
     static constexpr int P = kThreads / KC;                // threads per key in Q.K
     static constexpr int E = DK / P;                       // dims per thread in Q.K (16, 32 or 36)
     // a thread's dims: EM consecutive ones from dim pq * EM (within one quant block), and at
@@ -70,7 +72,7 @@ struct HdGeom {
     static constexpr int CPT = DV > kThreads ? DV / kThreads : 1;  // P.V: columns per thread
     static constexpr int KS = DV >= kThreads ? 1 : kThreads / DV;  // P.V: threads per column (key subsets)
     static constexpr int KPS = KC / KS;                    // keys per subset (16)
-    static_assert(P == 4 || P == 16, "Q.K groups are DPP quads or 16-lane rows");
+    static_assert(P == 4 || P == 8 || P == 16, "Q.K groups are DPP quads, half rows or 16-lane rows");
     static_assert(EM == 16 || EM == 32, "a thread's main Q.K dims: half a block or a block");
     static_assert(E % 4 == 0 && DK % 32 == 0 && DV % 32 == 0, "whole quant blocks");
 };
@@ -437,6 +439,7 @@ bool head_dims_supported(int dk, int dv) {
 hipError_t launch_decode_hd(const SegParams &p, int k_type, int v_type, hipStream_t s) {
     if (p.gqa * p.n_q < 1) return hipErrorInvalidValue;
     if (p.d == 64 && p.dv == 64) return launch_hd_types<64, 64>(p, k_type, v_type, s);
+    if (p.d == 128 && p.dv == 128) return launch_hd_types<128, 128>(p, k_type, v_type, s);
     if (p.d == 256 && p.dv == 256) return launch_hd_types<256, 256>(p, k_type, v_type, s);
     if (p.d == 512 && p.dv == 512) return launch_hd_types<512, 512>(p, k_type, v_type, s);
     if (p.d == 576 && p.dv == 512) return launch_hd_types<576, 512>(p, k_type, v_type, s);

@@ -20,8 +20,8 @@
 //        per tile with a constant A of -1032 (or -1152) removes the offset from the same
 //        accumulator, so the tiles hold n - 8 (and 16 (n - 8)) times the weights.
 //
-// Workgroup = HW (8) waves for one (split, head group, sequence), wave w = KV head g0 + w, as in
-// the vector cell-major kernel.  A 32-cell chunk is one contiguous span of each cache, moved
+// Workgroup = HW (8, 4 or 2) waves for one (split, head group, sequence), wave w = KV head
+// g0 + w, as in the vector cell-major kernel.  A 32-cell chunk is one contiguous span of each cache, moved
 // with buffer loads into registers (a thread takes two blocks of one head from each cache) and
 // from there into one of two LDS stages, where each block's scale is split from its data and
 // the data lands on 16-byte slots; two chunks are always in flight in registers, so one barrier
@@ -420,12 +420,16 @@ hipError_t launch_mma(const SegParams &p, hipStream_t s, int *occupancy) {
 template <int R>
 hipError_t launch_mma_r(const SegParams &p, hipStream_t s, int *occupancy) {
     if (p.cell_hw == 8) return launch_mma<R, 8>(p, s, occupancy);
+    if (p.cell_hw == 4) return launch_mma<R, 4>(p, s, occupancy);
+    if (p.cell_hw == 2) return launch_mma<R, 2>(p, s, occupancy);
     return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-bool decode_mma_ok(const SegParams &p) { return p.cell_hw == 8 && p.gqa * p.n_q >= 1 && p.gqa * p.n_q <= 8; }
+bool decode_mma_ok(const SegParams &p) {
+    return (p.cell_hw == 8 || p.cell_hw == 4 || p.cell_hw == 2) && p.gqa * p.n_q >= 1 && p.gqa * p.n_q <= 8;
+}
 
 hipError_t launch_decode_mma(const SegParams &p, hipStream_t s, int *occupancy) {
     switch (p.gqa * p.n_q) {

@@ -25,6 +25,7 @@ __device__ __forceinline__ float dpp_f(float x) {
     return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
 }
 inline constexpr int kQuadSwap1 = 0xB1, kQuadSwap2 = 0x4E, kRowRor4 = 0x124, kRowRor8 = 0x128;
+inline constexpr int kRowHalfMirror = 0x141;  // lane i <-> 7 - i inside each half row
 
 // Max and min of scores, which are never NaN (finite or -inf): plain v_max/v_min, without the
 // quieting of NaN operands that fmaxf / fminf add in IEEE mode.
