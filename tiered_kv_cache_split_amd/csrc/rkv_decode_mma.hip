@@ -82,9 +82,11 @@ struct Stage {
     uint32_t vx;
 };
 
-// CAP: the logit soft-cap is on (a separate instantiation, so the plain path carries none of it)
-template <int R, int HW, bool CAP>
-__global__ void __launch_bounds__(64 * HW) __attribute__((amdgpu_waves_per_eu(2)))
+// CAP: the logit soft-cap is on (a separate instantiation, so the plain path carries none of it).
+// WS: HW / 2 more waves per workgroup only load and stage the chunks (each thread of theirs two
+// of the units below, two chunks in flight); the HW compute waves then never wait for memory.
+template <int R, int HW, bool CAP, bool WS>
+__global__ void __launch_bounds__(WS ? 96 * HW : 64 * HW) __attribute__((amdgpu_waves_per_eu(WS ? 3 : 2)))
 decode_mma_kernel(const SegParams p) {
     using St = Stage<HW>;
     // LDS K stage: two planes (code bytes 0..15 and 16..31 of every q8_0 block), each with the
@@ -115,7 +117,9 @@ decode_mma_kernel(const SegParams p) {
     bid /= p.n_splits;
     const int hgrp = bid % n_hgrp;
     const int b = bid / n_hgrp;
-    const int g = hgrp * HW + wave;  // this wave's KV head
+    constexpr int kNC = 64 * HW;     // compute threads (one wave per KV head)
+    const bool loader = WS && tid >= kNC;
+    const int g = hgrp * HW + (loader ? 0 : wave);  // this compute wave's KV head
     const int64_t c_beg = (int64_t)split * p.cells_per_split;
     const int64_t c_end = min(p.n_cells, c_beg + (int64_t)p.cells_per_split);
     const uint8_t *kbase = p.k + (int64_t)(hgrp * HW) * p.k_s2;
@@ -127,14 +131,19 @@ decode_mma_kernel(const SegParams p) {
     // consecutive threads cover contiguous bytes).  Staging splits the scales from the block
     // data and puts the data on 16-byte slots.  Cells past the segment end lie outside the
     // buffer resource's range and read as zero.
-    const int fcell = tid / kTpc, fsub = tid % kTpc;
-    const int gkb = fcell * (int)p.k_s1 + 68 * fsub, gvb = fcell * (int)p.v_s1 + 36 * fsub;
-    const int lkb = fcell * kKc + 16 * fsub;
-    const int lks = 2 * kKp + (fsub >> 1) * kKh + 2 * (fsub & 1) * (2 * kCh) + 2 * fcell;
-    const int lvb = fcell * kVc + 64 * ((fcell >> 4) & 1) + 16 * fsub;
-    const int lvs = kVd + (fsub >> 1) * kVh + 2 * (fsub & 1) * (2 * kCh) +
-                    2 * (8 * ((fcell >> 2) & 3) + 4 * (fcell >> 4) + (fcell & 3));
-    auto fetch = [&](St &st, int64_t c0) __attribute__((always_inline)) {
+    struct Unit {
+        int gkb, gvb, lkb, lks, lvb, lvs;
+    };
+    auto unit_of = [&](int t) __attribute__((always_inline)) {
+        const int fcell = t / kTpc, fsub = t % kTpc;
+        return Unit{fcell * (int)p.k_s1 + 68 * fsub, fcell * (int)p.v_s1 + 36 * fsub, fcell * kKc + 16 * fsub,
+                    2 * kKp + (fsub >> 1) * kKh + 2 * (fsub & 1) * (2 * kCh) + 2 * fcell,
+                    fcell * kVc + 64 * ((fcell >> 4) & 1) + 16 * fsub,
+                    kVd + (fsub >> 1) * kVh + 2 * (fsub & 1) * (2 * kCh) +
+                        2 * (8 * ((fcell >> 2) & 3) + 4 * (fcell >> 4) + (fcell & 3))};
+    };
+    auto fetch = [&](St &st, int64_t c0, const Unit &u) __attribute__((always_inline)) {
+        const int gkb = u.gkb, gvb = u.gvb;
         const int64_t nv = max((int64_t)0, min((int64_t)kCh, c_end - c0));
         const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
             (void *)(kbase + c0 * p.k_s1), (short)0, (int)(nv * p.k_s1), 0x00020000);
@@ -149,7 +158,8 @@ decode_mma_kernel(const SegParams p) {
         st.vx = __builtin_amdgcn_raw_buffer_load_b32(rv, gvb + 16, 0, 0);
         st.vb = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, gvb + 20, 0, 0));
     };
-    auto stash = [&](const St &st, int buf) __attribute__((always_inline)) {
+    auto stash = [&](const St &st, int buf, const Unit &u) __attribute__((always_inline)) {
+        const int lkb = u.lkb, lks = u.lks, lvb = u.lvb, lvs = u.lvs;
         // K: words x0 .. x8 (bytes 0..35); the first block's codes start 2 bytes into them (its
         // scale is the low half of x0), the second block's scale is the high half of x8
         const uint32_t x[9] = {st.ka0.x, st.ka0.y, st.ka0.z, st.ka0.w, st.ka1.x, st.ka1.y, st.ka1.z, st.ka1.w, st.kx};
@@ -214,8 +224,10 @@ decode_mma_kernel(const SegParams p) {
         uint4 qv[4];
 #pragma unroll
         for (int blk = 0; blk < 4; ++blk) qv[blk] = *reinterpret_cast<const uint4 *>(qrow + 32 * blk + 8 * grp);
-        fetch(sa, c_beg);
-        fetch(sb, c_beg + kCh);
+        if constexpr (!WS) {
+            fetch(sa, c_beg, unit_of(tid));
+            fetch(sb, c_beg + kCh, unit_of(tid));
+        }
 #pragma unroll
         for (int blk = 0; blk < 4; ++blk) {
             qb[blk] = __builtin_bit_cast(half8_t, ok ? qv[blk] : make_uint4(0, 0, 0, 0));
@@ -371,17 +383,54 @@ decode_mma_kernel(const SegParams p) {
     // past the segment end read nothing.  Chunks go in pairs with no exit in between (a chunk
     // past the end has no visible key and adds nothing), so that every path into the loop
     // head has the same loads in flight and the waits before a stash cover one chunk only.
-    stash(sa, 0);
-    fetch(sa, c_beg + 2 * kCh);
-    for (int64_t ch = 0; ch < n_ch; ch += 2) {
-        __syncthreads();
-        stash(sb, 1);
-        fetch(sb, c_beg + (ch + 3) * kCh);
-        compute(0, c_beg + ch * kCh);
-        __syncthreads();
-        stash(sa, 0);
-        fetch(sa, c_beg + (ch + 4) * kCh);
-        compute(1, c_beg + (ch + 1) * kCh);
+    if constexpr (!WS) {
+        const Unit u = unit_of(tid);
+        stash(sa, 0, u);
+        fetch(sa, c_beg + 2 * kCh, u);
+        for (int64_t ch = 0; ch < n_ch; ch += 2) {
+            __syncthreads();
+            stash(sb, 1, u);
+            fetch(sb, c_beg + (ch + 3) * kCh, u);
+            compute(0, c_beg + ch * kCh);
+            __syncthreads();
+            stash(sa, 0, u);
+            fetch(sa, c_beg + (ch + 4) * kCh, u);
+            compute(1, c_beg + (ch + 1) * kCh);
+        }
+    } else if (loader) {
+        // loader thread: units lt and lt + 32 HW of every chunk, chunks ch + 1 .. ch + 2 in flight
+        // while the compute waves take chunk ch; the same barriers as theirs
+        const int lt = tid - kNC;
+        const Unit u0 = unit_of(lt), u1 = unit_of(lt + kNC / 2);
+        St sa1, sb1;
+        fetch(sa, c_beg, u0);
+        fetch(sa1, c_beg, u1);
+        fetch(sb, c_beg + kCh, u0);
+        fetch(sb1, c_beg + kCh, u1);
+        stash(sa, 0, u0);
+        stash(sa1, 0, u1);
+        fetch(sa, c_beg + 2 * kCh, u0);
+        fetch(sa1, c_beg + 2 * kCh, u1);
+        for (int64_t ch = 0; ch < n_ch; ch += 2) {
+            __syncthreads();
+            stash(sb, 1, u0);
+            stash(sb1, 1, u1);
+            fetch(sb, c_beg + (ch + 3) * kCh, u0);
+            fetch(sb1, c_beg + (ch + 3) * kCh, u1);
+            __syncthreads();
+            stash(sa, 0, u0);
+            stash(sa1, 0, u1);
+            fetch(sa, c_beg + (ch + 4) * kCh, u0);
+            fetch(sa1, c_beg + (ch + 4) * kCh, u1);
+        }
+        return;
+    } else {
+        for (int64_t ch = 0; ch < n_ch; ch += 2) {
+            __syncthreads();
+            compute(0, c_beg + ch * kCh);
+            __syncthreads();
+            compute(1, c_beg + (ch + 1) * kCh);
+        }
     }
 
     // ---- partial of row `col`: the sums are folded over the four lanes of the row
@@ -403,12 +452,16 @@ decode_mma_kernel(const SegParams p) {
     }
 }
 
+constexpr bool kLoaderWaves = true;  // workgroups with loader waves (see decode_mma_kernel)
+
 template <int R, int HW, bool CAP>
 hipError_t launch_mma_c(const SegParams &p, hipStream_t s, int *occupancy) {
+    constexpr int kThreads = (kLoaderWaves ? 96 : 64) * HW;
     if (occupancy)
-        return hipOccupancyMaxActiveBlocksPerMultiprocessor(occupancy, decode_mma_kernel<R, HW, CAP>, 64 * HW, 0);
-    launch_seg(decode_mma_kernel<R, HW, CAP>, dim3((unsigned)(p.n_splits * (p.n_head_kv / HW) * p.n_seq)), dim3(64 * HW),
-               s, p);
+        return hipOccupancyMaxActiveBlocksPerMultiprocessor(occupancy, decode_mma_kernel<R, HW, CAP, kLoaderWaves>,
+                                                            kThreads, 0);
+    launch_seg(decode_mma_kernel<R, HW, CAP, kLoaderWaves>, dim3((unsigned)(p.n_splits * (p.n_head_kv / HW) * p.n_seq)),
+               dim3(kThreads), s, p);
     return hipGetLastError();
 }
 
