@@ -19,8 +19,11 @@
  * strides, nb[0] is the element (or quant block) size.  Rows of head_dim values must be
  * contiguous (nb[0] == type size).  Supported head dims (patch 0070, fattn.cu: the streaming
  * op's supported shapes): head_dim == dv in {64, 128, 256, 512}, and head_dim 576 for Q and
- * K with dv 512 for V, on every attention entry point and the host tail partial; head_dim
- * 128 runs on the matrix-core kernels, the others on a vector kernel; rkv_lse_merge takes
+ * K with dv 512 for V, on every attention entry point and the host tail partial.  Decode at
+ * head_dim == dv in {64, 128, 256, 512} over cell-major q8_0 K / q4_0 V (and binary16 at 128)
+ * runs on the matrix-core kernels when the KV heads form groups the kernel takes (8 or 4 at
+ * 64; 8, 4 or 2 at 128; 4, 2 or 1 at 256; 1 at 512) and n_q * gqa <= 8; prefill at 128 on the
+ * matrix-core prefill kernel; everything else on the vector kernels; rkv_lse_merge takes
  * dv 64, 128, 256 or 512; Q in F16;
  * K in F16 or Q8_0; V in F16 or Q4_0.  Q8_0 is a 34-byte block (binary16 scale d, 32
  * int8 codes q; value d*q).  Q4_0 is an 18-byte block (binary16 scale d, 16 bytes; byte
@@ -126,7 +129,7 @@ enum rkv_kernel_variant {
     RKV_KERNEL_DECODE_HEAD = 0,       /* vector decode, one KV head per workgroup (any layout, rows) */
     RKV_KERNEL_PREFILL_MFMA = 1,      /* matrix-core prefill over 256-row query tiles                */
     RKV_KERNEL_DECODE_CELL = 2,       /* vector decode over cell-major groups of KV heads           */
-    RKV_KERNEL_DECODE_CELL_MFMA = 3,  /* matrix-core decode over eight cell-major q8_0/q4_0 heads   */
+    RKV_KERNEL_DECODE_CELL_MFMA = 3,  /* matrix-core decode over cell-major q8_0/q4_0 head groups   */
     RKV_KERNEL_DECODE_CELL_MFMA16 = 4, /* persistent matrix-core decode over eight binary16 heads
                                           (windows, tail tiles, row lists)                         */
     RKV_KERNEL_DECODE_HD = 5           /* vector decode for head dims other than 128 (window + tail) */
@@ -230,7 +233,8 @@ int rkv_attn_decode_noalloc(const rkv_tensor *q, const rkv_tensor *k, const rkv_
  * rkv_attn_decode for any n_q, computed at head dim 128 with MFMA f16 tiles: q8_0 K codes
  * and q4_0 V nibbles enter the matrix cores as exact binary16 integers and their block scales
  * are applied in fp32 (K) or folded into the softmax weights (V); the other head dims run on
- * the vector kernel for them in groups of 8 rows.  The tail is always computed on the GPU
+ * the decode kernels (the matrix-core decode kernel when n_q * gqa <= 8 and the heads form its
+ * groups, else the vector kernel in groups of 8 rows).  The tail is always computed on the GPU
  * (RKV_TAIL_HOST applies to decode only).  q_pos0 >= 0 makes it
  * causal: query i sits at absolute position q_pos0 + i and sees keys at positions
  * <= q_pos0 + i (in addition to the mask); q_pos0 == -1 uses the mask alone. */
@@ -432,7 +436,7 @@ enum rkv_dequant_form {
                                as binary16 integers                                           */
     RKV_DQ_VECTOR = 2,      /* vector decode: q8_0 as 1152 + q, q4_0 nibble fields paired
                                across words as 1024 + n                                       */
-    RKV_DQ_HEAD_DIM = 3     /* head dims 64 / 256: codes and nibbles as float32 integers      */
+    RKV_DQ_HEAD_DIM = 3     /* vector head-dim kernel: codes and nibbles as float32 integers  */
 };
 
 /* Dequantise n_rows rows of row_values values (type F16, Q8_0 or Q4_0; row r at byte offset

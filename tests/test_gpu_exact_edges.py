@@ -93,10 +93,15 @@ DECODE_PATHS = [
     ("decode_mma", 40, 8, "cell", 128, 3),
     ("decode_mma_hw4", 16, 4, "cell", 128, 3),
     ("decode_mma_hw2", 16, 2, "cell", 128, 3),
+    ("decode_mma_64", 16, 4, "cell", 64, 3),
+    ("decode_mma_64_hw8", 40, 8, "cell", 64, 3),
+    ("decode_mma_256", 16, 4, "cell", 256, 3),
+    ("decode_mma_256_hw1", 5, 1, "cell", 256, 3),
+    ("decode_mma_512", 16, 2, "cell", 512, 3),
     ("vector_head", 16, 4, "head", 128, 0),
     ("head_dim_kernel_at_128", 32, 4, "head", 128, 5),
-    ("head_dim_64", 16, 4, "cell", 64, 5),
-    ("head_dim_256", 16, 4, "cell", 256, 5),
+    ("head_dim_64", 16, 4, "head", 64, 5),
+    ("head_dim_256", 16, 4, "head", 256, 5),
 ]
 
 

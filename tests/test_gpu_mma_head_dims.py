@@ -1,0 +1,99 @@
+"""The matrix-core decode kernel at head dims 64, 256 and 512 (dk = dv, q8_0 K / q4_0 V, cell-major
+KV heads) against the fp64 oracle: every head-group size it takes (8 and 4 KV heads at 64; 4, 2
+and 1 at 256; 1 at 512), one to eight rows per KV head, the window + lifted or device tail split,
+masks with an empty row, ragged lengths, the causal rule of a small prefill call, the soft-cap,
+and the full 131072-cell shape of the 128K decode at each head dim.  What a segment computes is
+the streaming partial of opencoti-llamafile patch 0070-rolling-kv (fattn.cu, streaming_lse_kernel);
+the head dims are those its streaming op supports."""
+import numpy as np
+import pytest
+
+import oracle
+import rkv_inputs as gen
+from rkv_testutil import Runner, assert_close, oracle_decode, step
+
+pytestmark = pytest.mark.gpu
+
+MMA = 3  # rkv_kernel_variant: matrix-core cell-major decode
+
+
+@pytest.fixture(scope="module")
+def run():
+    r = Runner()
+    yield r
+    r.ctx.set_lift_mode(r.rkv.RKV_LIFT_AUTO)
+    r.ctx.set_softcap(0.0)
+
+
+# (d, n_head, n_head_kv, n_q): the group sizes and 1..8 rows per KV head
+SHAPES = [
+    (64, 40, 8, 1), (64, 16, 4, 2), (64, 8, 8, 1),
+    (256, 40, 8, 1), (256, 8, 2, 2), (256, 3, 1, 2), (256, 7, 1, 1),
+    (512, 16, 2, 1), (512, 5, 1, 1), (512, 4, 1, 2), (512, 1, 1, 1),
+]
+
+
+@pytest.mark.parametrize("d,n_head,n_head_kv,n_q", SHAPES)
+def test_groups_and_rows(run, d, n_head, n_head_kv, n_q):
+    w = gen.make_workload(2, scale_down=32, d=d, n_head=n_head, n_head_kv=n_head_kv, n_q=n_q)  # n_kv 4096
+    step(f"mma d={d} heads {n_head}/{n_head_kv} n_q {n_q}: window 2900 + lifted tail in 600-cell tiles")
+    O, L = run.decode(w, wc=2900, tile_kv=600, tail="host")
+    assert run.ctx.stats()["kernel_variant"] == MMA
+    Oref, Lref = oracle_decode(w)
+    assert_close(O, L, Oref, Lref, what=f"mma d={d} {n_head}/{n_head_kv} n_q {n_q}")
+
+
+@pytest.mark.parametrize("d", [64, 256, 512])
+@pytest.mark.parametrize("tail", ["device", "host"])
+def test_ragged_mask_and_empty_row(run, d, tail):
+    w = dict(gen.make_workload(2, scale_down=32, d=d, n_head=16, n_head_kv=4, n_q=2))  # 8 rows per KV head
+    n_kv = 3001
+    w["k"], w["v"], w["n_kv"] = w["k"][:n_kv], w["v"][:n_kv], n_kv
+    mask = gen.random_mask_f16(np.random.default_rng(d), 2, n_kv, p_hidden=0.35)
+    mask[1, :] = -np.inf  # the second query sees nothing
+    step(f"mma d={d}: n_kv 3001, mask, empty row, {tail} tail")
+    O, L = run.decode(w, wc=1999, tile_kv=333, tail=tail, mask=mask)
+    assert run.ctx.stats()["kernel_variant"] == MMA
+    Oref, Lref = oracle_decode(w, mask=mask)
+    assert_close(O, L, Oref, Lref, what=f"mma d={d} mask")
+    assert np.all(O[1] == 0) and np.all(L[1] == -np.inf)
+
+
+@pytest.mark.parametrize("d", [64, 256, 512])
+def test_small_prefill_causal(run, d):
+    """Two queries of four heads per KV head (8 rows): the causal rule inside the kernel."""
+    w = gen.make_workload(2, scale_down=32, d=d, n_head=16, n_head_kv=4, n_q=2)
+    n_q, n_kv = 2, w["n_kv"]
+    q_pos0 = n_kv - 700  # the queries sit inside the window, so later keys and the tail are hidden
+    step(f"mma d={d}: prefill of 2 queries at {q_pos0}, window 3500 + lifted tail")
+    O, L = run.decode(w, wc=3500, tile_kv=300, tail="host", prefill=True, q_pos0=q_pos0)
+    assert run.ctx.stats()["kernel_variant"] == MMA
+    Oref, Lref = oracle_decode(w, mask=oracle.causal_mask(n_q, n_kv, q_pos0))
+    assert_close(O, L, Oref, Lref, what=f"mma d={d} causal")
+
+
+@pytest.mark.parametrize("d", [64, 256, 512])
+def test_softcap(run, d):
+    w = gen.make_workload(2, scale_down=32, d=d, n_head=16, n_head_kv=4)
+    run.ctx.set_softcap(20.0)
+    try:
+        step(f"mma d={d}: soft-cap 20, window 2600 + lifted tail")
+        O, L = run.decode(w, wc=2600, tile_kv=512, tail="host")
+        assert run.ctx.stats()["kernel_variant"] == MMA
+    finally:
+        run.ctx.set_softcap(0.0)
+    Oref, Lref = oracle_decode(w, softcap=20.0)
+    assert_close(O, L, Oref, Lref, what=f"mma d={d} softcap")
+
+
+@pytest.mark.parametrize("d", [64, 256, 512])
+def test_full_size_128k_all_heads(run, d):
+    """131072 resident cells, 40/8 heads, in the launch configuration the benchmark times at this
+    head dim; every query head against the oracle over all keys."""
+    w = gen.make_workload(2, d=d)
+    step(f"mma d={d}: full size 131072 cells, 40/8 heads")
+    O, L = run.decode(w, wc=w["n_kv"], tail=None)
+    assert run.ctx.stats()["kernel_variant"] == MMA
+    gqa = w["n_head"] // w["n_head_kv"]
+    for g, (Oref, Lref) in oracle_decode(w, heads=list(range(w["n_head_kv"]))).items():
+        assert_close(O[:, g * gqa:(g + 1) * gqa], L[:, g * gqa:(g + 1) * gqa], Oref, Lref, what=f"d={d} head {g}")

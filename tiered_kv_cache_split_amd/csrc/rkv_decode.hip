@@ -765,16 +765,14 @@ hipError_t dispatch_decode(const SegParams &p, int k_type, int v_type, hipStream
 
 }  // namespace
 
-int cell_heads(int k_type, int v_type, int n_head_kv, int R, bool rows) {
+int cell_heads(int d, int k_type, int v_type, int n_head_kv, int R, bool rows) {
     if (R < 1 || R > kMaxRowsVec) return 0;
+    // q8_0 / q4_0: the matrix-core kernel at head dims 64 .. 512 (not for gathered rows)
+    if (k_type == T_Q8_0 && v_type == T_Q4_0) return rows ? 0 : decode_mma_heads(d, n_head_kv);
+    if (d != kHeadDim) return 0;
     // binary16 with eight KV heads per cell group: the matrix-core kernel, also for row lists
     if (k_type == T_F16 && v_type == T_F16 && n_head_kv % 8 == 0) return 8;
     if (rows) return 0;  // other gathered rows: per-head kernel
-    if (k_type == T_Q8_0 && v_type == T_Q4_0) {
-        for (int hw : {8, 4, 2})
-            if (n_head_kv % hw == 0) return hw;
-        return 0;
-    }
     if (k_type == T_F16 && v_type == T_F16) return n_head_kv % 2 == 0 ? 2 : 0;
     return 0;
 }
@@ -790,7 +788,9 @@ bool decode_kernel_persistent(const SegParams &p, int k_type, int v_type) {
 }
 
 int decode_kernel_variant(const SegParams &p, int k_type, int v_type) {
-    if (p.d != kHeadDim) return RKV_KERNEL_DECODE_HD;
+    if (p.d != kHeadDim)
+        return (p.cell_hw > 0 && k_type == T_Q8_0 && v_type == T_Q4_0 && decode_mma_ok(p)) ? RKV_KERNEL_DECODE_CELL_MFMA
+                                                                                         : RKV_KERNEL_DECODE_HD;
     if (p.cell_hw <= 0) return (k_type == T_Q8_0 && p.gqa * p.n_q >= 6) ? RKV_KERNEL_DECODE_HD : RKV_KERNEL_DECODE_HEAD;
     if (k_type == T_Q8_0 && v_type == T_Q4_0 && decode_mma_ok(p)) return RKV_KERNEL_DECODE_CELL_MFMA;
     if (k_type == T_F16 && v_type == T_F16 && decode_mma16_ok(p)) return RKV_KERNEL_DECODE_CELL_MFMA16;
@@ -798,7 +798,7 @@ int decode_kernel_variant(const SegParams &p, int k_type, int v_type) {
 }
 
 hipError_t launch_decode_segment(const SegParams &p, int k_type, int v_type, hipStream_t s) {
-    if (p.d != kHeadDim) return launch_decode_hd(p, k_type, v_type, s);
+    if (p.d != kHeadDim && p.cell_hw <= 0) return launch_decode_hd(p, k_type, v_type, s);
     return dispatch_decode(p, k_type, v_type, s, nullptr);
 }
 

@@ -449,6 +449,8 @@ hipError_t launch_decode_hd(const SegParams &p, int k_type, int v_type, hipStrea
 hipError_t launch_merge_hd(const float *partials, int n_seg, int64_t n_rows, int dv, float *o, float *lse,
                            hipStream_t s) {
     if (n_rows <= 0) return hipSuccess;
+    // few rows and up to 256 segments: one thread per segment over 16-value parts of each row
+    if (n_seg <= 256 && n_rows < 1024) return launch_merge_parts(partials, n_seg, n_rows, dv, o, lse, s);
     if (dv == 64)
         hipLaunchKernelGGL(merge_hd_kernel<64>, dim3((unsigned)n_rows), dim3(64), 0, s, partials, n_seg, n_rows, o, lse);
     else if (dv == 256)

@@ -68,67 +68,96 @@ __device__ __forceinline__ float row16_sum(float x) {
     return x;
 }
 
-// One chunk in registers: the thread's half of one head's q8_0 K row (two blocks, 68 bytes:
-// bytes 0..35 as nine words, the second block's aligned codes 36..67 as two quads) and of its
-// q4_0 V row (two blocks, 36 bytes: bytes 0..19 as five words, the second block's aligned data
-// 20..35 as one quad).  The aligned quads go to LDS as loaded.
-template <int HW>
+// One chunk unit in registers: two q8_0 blocks of one head's K row (68 bytes: bytes 0..35 as
+// nine words, the second block's aligned codes 36..67 as two quads) and the two q4_0 blocks of
+// the same head_dim range of its V row (36 bytes: bytes 0..19 as five words, the second block's
+// aligned data 20..35 as one quad).  The aligned quads go to LDS as loaded.
 struct Stage {
-    static constexpr int kNT = 64 * HW;
-    static constexpr int kTpc = kNT / kCh;  // threads per cell
     uint4 ka0, ka1, kb0, kb1;
     uint32_t kx;
     uint4 va, vb;
     uint32_t vx;
 };
 
-// CAP: the logit soft-cap is on (a separate instantiation, so the plain path carries none of it).
-// WS: HW / 2 more waves per workgroup only load and stage the chunks (each thread of theirs two
-// of the units below, two chunks in flight); the HW compute waves then never wait for memory.
-template <int R, int HW, bool CAP, bool WS>
-__global__ void __launch_bounds__(WS ? 96 * HW : 64 * HW) __attribute__((amdgpu_waves_per_eu(WS ? 3 : 2)))
-decode_mma_kernel(const SegParams p) {
-    using St = Stage<HW>;
+// Geometry of a workgroup for head dim D (= dv), HW KV heads and SV compute waves per head
+// (each of them takes 1 / SV of the V blocks).  A unit is two blocks of one head (Stage
+// above); a cell holds kTpc units, a chunk kCh cells.  Loader threads take two units of every
+// chunk, so their count kNL is a whole number of waves when HW * D / 64 is a multiple of 4.
+template <int D, int HW, int SV>
+struct Geo {
+    static constexpr int NB = D / 32;        // q8_0 / q4_0 blocks per row
+    static constexpr int NBV = NB / SV;      // V blocks per compute wave
+    static constexpr int U = NB / 2;         // units per head and cell
+    static constexpr int kTpc = HW * U;      // units per cell
+    static constexpr int kNC = 64 * HW * SV; // compute threads
+    static constexpr int kNL = kCh * kTpc / 2;  // loader threads
+    static constexpr int kThreads = kNC + kNL;
+    static_assert(D % 64 == 0 && kNL % 64 == 0, "loader threads must fill whole waves");
     // LDS K stage: two planes (code bytes 0..15 and 16..31 of every q8_0 block), each with the
-    // block's 16 bytes at a slot of its cell numbered as in V below, then d_K as [head][block][key]
-    constexpr int kKc = 64 * HW + 16;                         // K plane cell stride: 4HW slots + 16 bytes
-    constexpr int kKp = kCh * kKc;                            // bytes of one K plane
-    constexpr int kKh = 4 * 2 * kCh + 16;                     // d_K bytes per head
-    constexpr int kBk = 2 * kKp + HW * kKh;                   // bytes of one LDS K stage
-    // LDS V stage: the 16 data bytes of every q4_0 block at a 16-byte slot of its cell (the
-    // first block of each thread's pair in slots 0 .. 2HW-1, the second in 2HW .. 4HW-1), cells
-    // 16 bytes apart plus 64 more from cell 16 on (the transposing reads of 8 keys then meet 8
-    // distinct bank quads), followed by d_V as [head][block][P.V slot of the key]
-    constexpr int kVc = 64 * HW + 16;                         // V cell stride
-    constexpr int kVd = kCh * kVc + 64;                       // data bytes of a V stage
-    constexpr int kVh = 4 * 2 * kCh + 16;                     // d_V bytes per head
-    constexpr int kBv = kVd + HW * kVh;                       // bytes of one LDS V stage
-    constexpr int kTpc = St::kTpc;
-    static_assert(St::kNT % kCh == 0 && kTpc == 2 * HW, "thread mapping");
+    // block's 16 bytes at a slot of its cell (the first block of each unit in slots 0 .. kTpc-1,
+    // the second in kTpc .. 2kTpc-1), then d_K as [head][block][key]
+    static constexpr int kKc = 32 * kTpc + 16;    // K plane cell stride: 2 kTpc slots + 16 bytes
+    static constexpr int kKp = kCh * kKc;         // bytes of one K plane
+    static constexpr int kKh = 2 * NB * kCh + 16; // d_K bytes per head
+    static constexpr int kBk = 2 * kKp + HW * kKh;  // bytes of one LDS K stage
+    // LDS V stage: the 16 data bytes of every q4_0 block at a 16-byte slot of its cell (slots as
+    // for K), cells kVc bytes apart plus 64 more from cell 16 on (the transposing reads of 8
+    // keys then meet 8 distinct bank quads), followed by d_V as [head][block][P.V slot of the key]
+    static constexpr int kVc = 32 * kTpc + 16;    // V cell stride
+    static constexpr int kVd = kCh * kVc + 64;    // data bytes of a V stage
+    static constexpr int kVh = 2 * NB * kCh + 16; // d_V bytes per head
+    static constexpr int kBv = kVd + HW * kVh;    // bytes of one LDS V stage
+    // waves of all resident workgroups per SIMD that the register budget allows
+    static constexpr int kWavesPerEu = D >= 256 ? 2 : 3;
+    static_assert(NB % SV == 0, "V blocks split evenly");
+    // wide heads keep the Q.K accumulator inputs (one float4 per block and row) in LDS rather
+    // than in registers, and at head dim 512 the Q^T fragments (16 bytes per lane and block)
+    // too; both per head, written by the head's first wave
+    static constexpr bool kCinLds = NB > 4, kQLds = NB > 8;
+    static constexpr int kCin = kCinLds ? HW * NB * 16 * 16 : 16;  // LDS bytes of the inputs
+    static constexpr int kQf = kQLds ? HW * NB * 64 * 16 : 16;     // LDS bytes of the fragments
+};
+
+// CAP: the logit soft-cap is on (a separate instantiation, so the plain path carries none of it).
+// The workgroup's first HW * SV waves compute (wave w: KV head g0 + w / SV, V blocks of part
+// w % SV); the remaining kNL threads
+// only load and stage the chunks (each two units of every chunk, two chunks in flight), so the
+// compute waves never wait for memory and hold no staging registers.
+template <int D, int HW, int SV, bool CAP>
+__global__ void __launch_bounds__((Geo<D, HW, SV>::kThreads))
+__attribute__((amdgpu_waves_per_eu((Geo<D, HW, SV>::kWavesPerEu)))) decode_mma_kernel(const SegParams p) {
+    using G = Geo<D, HW, SV>;
+    constexpr int NB = G::NB, NBV = G::NBV, U = G::U, kTpc = G::kTpc, kNC = G::kNC, kNL = G::kNL;
+    constexpr int kKc = G::kKc, kKp = G::kKp, kKh = G::kKh, kBk = G::kBk;
+    constexpr int kVc = G::kVc, kVd = G::kVd, kVh = G::kVh, kBv = G::kBv;
+    constexpr int kPs = 2 + D;  // partial row: M, S, VKQ[D]
     static_assert(kCh == 32, "the key permutation of P.V assumes 32-key chunks");
     __shared__ __attribute__((aligned(16))) uint8_t s_k[2 * kBk];
     __shared__ __attribute__((aligned(16))) uint8_t s_v[2 * kBv];
+    __shared__ __attribute__((aligned(16))) uint8_t s_cin[G::kCin];
+    __shared__ __attribute__((aligned(16))) uint8_t s_q[G::kQf];
 
     const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int col = lane & 15, grp = lane >> 4;
+    const int R = p.gqa * p.n_q;  // query rows of a KV head (at most 8: padding columns of the MFMAs)
     const int n_hgrp = p.n_head_kv / HW;
     int bid = blockIdx.x;
     const int split = bid % p.n_splits;
     bid /= p.n_splits;
     const int hgrp = bid % n_hgrp;
     const int b = bid / n_hgrp;
-    constexpr int kNC = 64 * HW;     // compute threads (one wave per KV head)
-    const bool loader = WS && tid >= kNC;
-    const int g = hgrp * HW + (loader ? 0 : wave);  // this compute wave's KV head
+    const bool loader = tid >= kNC;
+    const int wh = loader ? 0 : wave / SV, part = loader ? 0 : wave % SV;  // head in the group, V part
+    const int g = hgrp * HW + wh;  // this compute wave's KV head
     const int64_t c_beg = (int64_t)split * p.cells_per_split;
     const int64_t c_end = min(p.n_cells, c_beg + (int64_t)p.cells_per_split);
     const uint8_t *kbase = p.k + (int64_t)(hgrp * HW) * p.k_s2;
     const uint8_t *vbase = p.v + (int64_t)(hgrp * HW) * p.v_s2;
 
-    // ---- chunk fetch (registers) and staging (LDS).  Thread t works on cell t / kTpc (sub =
-    // t % kTpc) and takes blocks 2 (sub % 2) and + 1 of head sub / 2 from both caches: K bytes
-    // 68 sub .. 68 sub + 67 and V bytes 36 sub .. 36 sub + 35 of the cell (word aligned, so
-    // consecutive threads cover contiguous bytes).  Staging splits the scales from the block
+    // ---- chunk fetch (registers) and staging (LDS).  Unit t is cell t / kTpc, sub = t % kTpc:
+    // blocks 2 (sub % U) and + 1 of head sub / U from both caches, i.e. K bytes 68 sub .. 68 sub
+    // + 67 and V bytes 36 sub .. 36 sub + 35 of the cell (heads are packed in a cell, so
+    // consecutive units cover contiguous bytes).  Staging splits the scales from the block
     // data and puts the data on 16-byte slots.  Cells past the segment end lie outside the
     // buffer resource's range and read as zero.
     struct Unit {
@@ -136,13 +165,13 @@ decode_mma_kernel(const SegParams p) {
     };
     auto unit_of = [&](int t) __attribute__((always_inline)) {
         const int fcell = t / kTpc, fsub = t % kTpc;
+        const int fh = fsub / U, fb = 2 * (fsub % U);  // head and first block of the unit
         return Unit{fcell * (int)p.k_s1 + 68 * fsub, fcell * (int)p.v_s1 + 36 * fsub, fcell * kKc + 16 * fsub,
-                    2 * kKp + (fsub >> 1) * kKh + 2 * (fsub & 1) * (2 * kCh) + 2 * fcell,
+                    2 * kKp + fh * kKh + fb * (2 * kCh) + 2 * fcell,
                     fcell * kVc + 64 * ((fcell >> 4) & 1) + 16 * fsub,
-                    kVd + (fsub >> 1) * kVh + 2 * (fsub & 1) * (2 * kCh) +
-                        2 * (8 * ((fcell >> 2) & 3) + 4 * (fcell >> 4) + (fcell & 3))};
+                    kVd + fh * kVh + fb * (2 * kCh) + 2 * (8 * ((fcell >> 2) & 3) + 4 * (fcell >> 4) + (fcell & 3))};
     };
-    auto fetch = [&](St &st, int64_t c0, const Unit &u) __attribute__((always_inline)) {
+    auto fetch = [&](Stage &st, int64_t c0, const Unit &u) __attribute__((always_inline)) {
         const int gkb = u.gkb, gvb = u.gvb;
         const int64_t nv = max((int64_t)0, min((int64_t)kCh, c_end - c0));
         const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
@@ -158,7 +187,7 @@ decode_mma_kernel(const SegParams p) {
         st.vx = __builtin_amdgcn_raw_buffer_load_b32(rv, gvb + 16, 0, 0);
         st.vb = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, gvb + 20, 0, 0));
     };
-    auto stash = [&](const St &st, int buf, const Unit &u) __attribute__((always_inline)) {
+    auto stash = [&](const Stage &st, int buf, const Unit &u) __attribute__((always_inline)) {
         const int lkb = u.lkb, lks = u.lks, lvb = u.lvb, lvs = u.lvs;
         // K: words x0 .. x8 (bytes 0..35); the first block's codes start 2 bytes into them (its
         // scale is the low half of x0), the second block's scale is the high half of x8
@@ -185,14 +214,48 @@ decode_mma_kernel(const SegParams p) {
         *reinterpret_cast<uint16_t *>(vd + lvs + 2 * kCh) = (uint16_t)(st.vx >> 16);
     };
 
+    // ---- pipeline: chunk ch is computed from stage ch % 2 while the loader threads hold
+    // chunks ch + 2 and ch + 3 in registers; the barrier before a stash orders it after every
+    // compute wave's reads of that stage (two chunks earlier) and before this chunk's reads.
+    // Loads past the segment end read nothing.  The loader threads leave after their last
+    // stash; the compute waves meet them at every barrier until then.
+    const int64_t n_ch = (c_end > c_beg) ? (c_end - c_beg + kCh - 1) / kCh : 0;
+    if (loader) {
+        const int lt = tid - kNC;
+        const Unit u0 = unit_of(lt), u1 = unit_of(lt + kNL);
+        Stage sa, sa1, sb, sb1;  // chunks 2i (sa, sa1) and 2i + 1 (sb, sb1), units u0 and u1
+        fetch(sa, c_beg, u0);
+        fetch(sa1, c_beg, u1);
+        fetch(sb, c_beg + kCh, u0);
+        fetch(sb1, c_beg + kCh, u1);
+        stash(sa, 0, u0);
+        stash(sa1, 0, u1);
+        fetch(sa, c_beg + 2 * kCh, u0);
+        fetch(sa1, c_beg + 2 * kCh, u1);
+        for (int64_t ch = 0; ch < n_ch; ch += 2) {
+            __syncthreads();
+            stash(sb, 1, u0);
+            stash(sb1, 1, u1);
+            fetch(sb, c_beg + (ch + 3) * kCh, u0);
+            fetch(sb1, c_beg + (ch + 3) * kCh, u1);
+            if (ch + 1 >= n_ch) break;
+            __syncthreads();
+            stash(sa, 0, u0);
+            stash(sa1, 0, u1);
+            fetch(sa, c_beg + (ch + 4) * kCh, u0);
+            fetch(sa1, c_beg + (ch + 4) * kCh, u1);
+        }
+        return;
+    }
+
     // Lane (col, grp) owns query row `col` (rows >= R are padding and never written) and, within
     // a chunk, the keys 16*kt + 4*grp + ii (kt, ii < 2, 4): the Q.K output layout.  Its P.V
     // accumulators hold O^T[d][col] for d = 16*dt + 4*grp + e, so the softmax state of a row lives
     // in the four lanes col, col + 16, col + 32, col + 48 and never crosses LDS.
-    float4_t oacc[8];
+    float4_t oacc[2 * NBV];
     float mrow = -INFINITY, lrow = 0.f;  // running max (log2 domain) and this lane's part of the sum
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) oacc[dt] = float4_t{0.f, 0.f, 0.f, 0.f};
+    for (int dt = 0; dt < 2 * NBV; ++dt) oacc[dt] = float4_t{0.f, 0.f, 0.f, 0.f};
     // A operands that remove the nibble offsets inside the P.V MFMAs: every entry -1032 (low
     // nibbles) or -1152 (high nibbles), so each output gains -offset * (sum of its weights)
     const half8_t bias_lo = {(_Float16)-kMagicV, (_Float16)-kMagicV, (_Float16)-kMagicV, (_Float16)-kMagicV,
@@ -208,34 +271,42 @@ decode_mma_kernel(const SegParams p) {
     // in P.V slot 8 grp + col / 2; it receives byte col of the 8 keys of its slots
     const int vkey = 4 * grp + ((col >> 1) & 3) + 16 * (col >> 3);
     const int vrd = vkey * kVc + 64 * ((vkey >> 4) & 1) + 8 * (col & 1);
-    const int64_t n_ch = (c_end > c_beg) ? (c_end - c_beg + kCh - 1) / kCh : 0;
     const int qi_row = min(col, R - 1) / p.gqa;  // query position of this lane's row
 
-    // ---- Q^T as the B operand of Q.K: lane holds row `col`, head_dim 32*blk + 8*grp + 0..7.  Its
-    // loads are issued before the first two chunks' so that waiting for them waits for Q only.
-    half8_t qb[4];
-    float4_t cneg[4];  // accumulator inputs: -1152 * block sum of row `col` of Q
-    St sa, sb;         // chunks 2i (sa) and 2i + 1 (sb) of the split
+    // ---- Q^T as the B operand of Q.K: lane holds row `col`, head_dim 32*blk + 8*grp + 0..7
+    // accumulator inputs: -1152 * block sum of row `col` of Q, in registers or (wide heads) at
+    // s_cin[wh][blk][col]; Q^T fragments in registers or (head dim 512) at s_q[wh][blk][lane].
+    // The LDS copies are written before the first barrier and read once per block and chunk.
+    float4_t cneg[G::kCinLds ? 1 : NB];
+    half8_t qb[G::kQLds ? 1 : NB];
+    const int cin_off = 16 * (16 * NB * wh + col);
+    const int q_off = 16 * (64 * NB * wh + lane);
     {
         const bool ok = col < R;
         const int r = ok ? col : 0;
         const _Float16 *qrow = p.q + (int64_t)(r / p.gqa) * p.q_s1 + (int64_t)(g * p.gqa + r % p.gqa) * p.q_s2 +
                                (int64_t)b * p.q_s3;
-        uint4 qv[4];
+        uint4 qv[NB];
 #pragma unroll
-        for (int blk = 0; blk < 4; ++blk) qv[blk] = *reinterpret_cast<const uint4 *>(qrow + 32 * blk + 8 * grp);
-        if constexpr (!WS) {
-            fetch(sa, c_beg, unit_of(tid));
-            fetch(sb, c_beg + kCh, unit_of(tid));
-        }
+        for (int blk = 0; blk < NB; ++blk) qv[blk] = *reinterpret_cast<const uint4 *>(qrow + 32 * blk + 8 * grp);
 #pragma unroll
-        for (int blk = 0; blk < 4; ++blk) {
-            qb[blk] = __builtin_bit_cast(half8_t, ok ? qv[blk] : make_uint4(0, 0, 0, 0));
+        for (int blk = 0; blk < NB; ++blk) {
+            const half8_t qf = __builtin_bit_cast(half8_t, ok ? qv[blk] : make_uint4(0, 0, 0, 0));
             float sum = 0.f;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) sum += (float)qb[blk][j];
+            for (int j = 0; j < 8; ++j) sum += (float)qf[j];
             const float cb = -kMagicK * fold_rows(sum);  // block sum of row `col`, in every lane of the column
-            cneg[blk] = float4_t{cb, cb, cb, cb};
+            if constexpr (G::kQLds) {
+                if (part == 0) *reinterpret_cast<half8_t *>(s_q + q_off + 1024 * blk) = qf;
+            } else {
+                qb[blk] = qf;
+            }
+            if constexpr (G::kCinLds) {
+                if (grp == 0 && part == 0)
+                    *reinterpret_cast<float4_t *>(s_cin + cin_off + 256 * blk) = float4_t{cb, cb, cb, cb};
+            } else {
+                cneg[blk] = float4_t{cb, cb, cb, cb};
+            }
         }
     }
 
@@ -243,55 +314,78 @@ decode_mma_kernel(const SegParams p) {
     auto compute = [&](int buf, int64_t c0) __attribute__((always_inline)) {
         const uint8_t *ks = s_k + buf * kBk;
         const uint8_t *vs = s_v + buf * kBv;
-        const uint8_t *dkw = ks + 2 * kKp + wave * kKh;  // d_K[block][key] of this head
+        const uint8_t *dkw = ks + 2 * kKp + wh * kKh;  // d_K[block][key] of this head
         // (d_V is staged in P.V slot order: the key of slot 8*gg + jj is 4*gg + jj (jj < 4) or
         // 16 + 4*gg + jj - 4.)
 
         // the V^T bytes (one transposing read per block) are read first: their latency then
         // overlaps Q.K and the softmax
-        int2_t btr[4];
+        int2_t btr[NBV];
 #pragma unroll
-        for (int blk = 0; blk < 4; ++blk) {
-            // block blk of head `wave` is slot 2*wave + blk/2 (+ 2HW for odd blk) of a cell
-            const int vslot = 2 * wave + (blk >> 1) + 2 * HW * (blk & 1);
-            btr[blk] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+        for (int j = 0; j < NBV; ++j) {
+            // block blk of head wh is slot U*wh + blk/2 (+ kTpc for odd blk) of a cell
+            const int blk = NBV * part + j;
+            const int vslot = U * wh + (blk >> 1) + kTpc * (blk & 1);
+            btr[j] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
                 (__attribute__((address_space(3))) int2_t *)(vs + vrd + 16 * vslot));
         }
 
         // ---- Q.K on the matrix cores: A = K (16 keys x 32 head_dim of one q8_0 block, codes as
         // binary16 1024 + (q + 128)), B = Q^T; d[ii] = score of key 16*kt + 4*grp + ii for row col
         // before the block scale
-        float4_t dq[2][4];
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-            // codes 8*grp .. 8*grp+7 of the block: plane grp / 2, half grp % 2 of the slot
-            const uint8_t *kr = ks + (grp >> 1) * kKp + (16 * kt + col) * kKc + 8 * (grp & 1);
-#pragma unroll
-            for (int blk = 0; blk < 4; ++blk) {
-                const int kslot = 2 * wave + (blk >> 1) + 2 * HW * (blk & 1);
-                const uint2 w = *reinterpret_cast<const uint2 *>(kr + 16 * kslot);
-                const uint2 b0 = q8_biased(w.x), b1 = q8_biased(w.y);  // 1152 + q, exact
-                const uint4 ak = make_uint4(b0.x, b0.y, b1.x, b1.y);
-                dq[kt][blk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, ak), qb[blk],
-                                                                     cneg[blk], 0, 0, 0);
-            }
-        }
-
-        // scores s[kt][ii] = sum over blocks of d_K * d
+        // Blocks go in groups of four (all of them at head dim 128), with a scheduling fence
+        // between groups, so at most eight accumulators of raw scores are live at once.
+        constexpr int kQg = NB < 4 ? NB : 4;
         float s[2][4];
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
+        for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii) s[kt][ii] = 0.f;
 #pragma unroll
-            for (int blk = 0; blk < 4; ++blk) {
-                const uint2 dk2 = *reinterpret_cast<const uint2 *>(dkw + blk * (2 * kCh) + 2 * (16 * kt + 4 * grp));
-                const half2_t d01 = h2v(dk2.x), d23 = h2v(dk2.y);
-                s[kt][0] = fmaf((float)d01[0], dq[kt][blk][0], s[kt][0]);
-                s[kt][1] = fmaf((float)d01[1], dq[kt][blk][1], s[kt][1]);
-                s[kt][2] = fmaf((float)d23[0], dq[kt][blk][2], s[kt][2]);
-                s[kt][3] = fmaf((float)d23[1], dq[kt][blk][3], s[kt][3]);
+        for (int b0 = 0; b0 < NB; b0 += kQg) {
+            float4_t dq[2][kQg], cin[kQg];
+            half8_t qin[kQg];
+#pragma unroll
+            for (int j = 0; j < kQg; ++j) {
+                if constexpr (G::kCinLds)
+                    cin[j] = *reinterpret_cast<const float4_t *>(s_cin + cin_off + 256 * (b0 + j));
+                else
+                    cin[j] = cneg[b0 + j];
+                if constexpr (G::kQLds)
+                    qin[j] = *reinterpret_cast<const half8_t *>(s_q + q_off + 1024 * (b0 + j));
+                else
+                    qin[j] = qb[b0 + j];
             }
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) {
+                // codes 8*grp .. 8*grp+7 of the block: plane grp / 2, half grp % 2 of the slot
+                const uint8_t *kr = ks + (grp >> 1) * kKp + (16 * kt + col) * kKc + 8 * (grp & 1);
+#pragma unroll
+                for (int j = 0; j < kQg; ++j) {
+                    const int blk = b0 + j;
+                    const int kslot = U * wh + (blk >> 1) + kTpc * (blk & 1);
+                    const uint2 w = *reinterpret_cast<const uint2 *>(kr + 16 * kslot);
+                    const uint2 b0w = q8_biased(w.x), b1w = q8_biased(w.y);  // 1152 + q, exact
+                    const uint4 ak = make_uint4(b0w.x, b0w.y, b1w.x, b1w.y);
+                    dq[kt][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, ak), qin[j],
+                                                                       cin[j], 0, 0, 0);
+                }
+            }
+            // scores s[kt][ii] = sum over blocks of d_K * d
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+                for (int j = 0; j < kQg; ++j) {
+                    const int blk = b0 + j;
+                    const uint2 dk2 = *reinterpret_cast<const uint2 *>(dkw + blk * (2 * kCh) + 2 * (16 * kt + 4 * grp));
+                    const half2_t d01 = h2v(dk2.x), d23 = h2v(dk2.y);
+                    s[kt][0] = fmaf((float)d01[0], dq[kt][j][0], s[kt][0]);
+                    s[kt][1] = fmaf((float)d01[1], dq[kt][j][1], s[kt][1]);
+                    s[kt][2] = fmaf((float)d23[0], dq[kt][j][2], s[kt][2]);
+                    s[kt][3] = fmaf((float)d23[1], dq[kt][j][3], s[kt][3]);
+                }
+            }
+            if constexpr (NB > kQg) __builtin_amdgcn_sched_barrier(0);
         }
 
         // ---- visibility: whole chunk visible, or per element (chunk end, causal rule, mask)
@@ -340,7 +434,7 @@ decode_mma_kernel(const SegParams p) {
             mrow = mnew;
             lrow *= a;
 #pragma unroll
-            for (int dt = 0; dt < 8; ++dt) oacc[dt] *= a;
+            for (int dt = 0; dt < 2 * NBV; ++dt) oacc[dt] *= a;
         }
         const float msub = mrow == -INFINITY ? 0.f : mrow;
         half2_t pk[4];  // P of P.V slots 8*grp + 2u, 2u + 1 (keys 16*(u/2) + 4*grp + 2*(u%2) + 0, 1)
@@ -356,81 +450,34 @@ decode_mma_kernel(const SegParams p) {
         // order above, A = V^T gathered from the staged raw bytes in the same order (byte `col`
         // of the block: element col as the low nibble, element col + 16 as the high one)
 #pragma unroll
-        for (int blk = 0; blk < 4; ++blk) {
-            const uint4 dv = *reinterpret_cast<const uint4 *>(vs + kVd + wave * kVh + blk * (2 * kCh) + 16 * grp);
+        for (int j = 0; j < NBV; ++j) {
+            const int blk = NBV * part + j;
+            const uint4 dv = *reinterpret_cast<const uint4 *>(vs + kVd + wh * kVh + blk * (2 * kCh) + 16 * grp);
             const uint4 wu = make_uint4(u32v(pk[0] * h2v(dv.x)), u32v(pk[1] * h2v(dv.y)),
                                         u32v(pk[2] * h2v(dv.z)), u32v(pk[3] * h2v(dv.w)));
             const half8_t wf = __builtin_bit_cast(half8_t, wu);
-            const int2_t bt = btr[blk];
+            const int2_t bt = btr[j];
             uint32_t lo[4], hi[4];
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
                 // 1024 + n (low nibbles) and 1024 + 16 n (high nibbles, in place) of two bytes
                 q4_nibbles_biased((uint32_t)bt[jj >> 1], (jj & 1) ? 0x0C030C02u : 0x0C010C00u, vmagic, lo[jj], hi[jj]);
             }
-            oacc[2 * blk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                __builtin_bit_cast(half8_t, make_uint4(lo[0], lo[1], lo[2], lo[3])), wf, oacc[2 * blk], 0, 0, 0);
-            oacc[2 * blk + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                __builtin_bit_cast(half8_t, make_uint4(hi[0], hi[1], hi[2], hi[3])), wf, oacc[2 * blk + 1], 0, 0, 0);
-            oacc[2 * blk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bias_lo, wf, oacc[2 * blk], 0, 0, 0);
-            oacc[2 * blk + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bias_hi, wf, oacc[2 * blk + 1], 0, 0, 0);
+            oacc[2 * j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                __builtin_bit_cast(half8_t, make_uint4(lo[0], lo[1], lo[2], lo[3])), wf, oacc[2 * j], 0, 0, 0);
+            oacc[2 * j + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                __builtin_bit_cast(half8_t, make_uint4(hi[0], hi[1], hi[2], hi[3])), wf, oacc[2 * j + 1], 0, 0, 0);
+            oacc[2 * j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bias_lo, wf, oacc[2 * j], 0, 0, 0);
+            oacc[2 * j + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bias_hi, wf, oacc[2 * j + 1], 0, 0, 0);
         }
     };
 
-    // ---- pipeline: chunk ch is computed from stage ch % 2 while chunks ch + 2 and ch + 3 are
-    // in flight in registers; the barrier before a stash orders it after every wave's reads of
-    // that stage (two chunks earlier) and the previous stash before this chunk's reads.  Loads
-    // past the segment end read nothing.  Chunks go in pairs with no exit in between (a chunk
-    // past the end has no visible key and adds nothing), so that every path into the loop
-    // head has the same loads in flight and the waits before a stash cover one chunk only.
-    if constexpr (!WS) {
-        const Unit u = unit_of(tid);
-        stash(sa, 0, u);
-        fetch(sa, c_beg + 2 * kCh, u);
-        for (int64_t ch = 0; ch < n_ch; ch += 2) {
-            __syncthreads();
-            stash(sb, 1, u);
-            fetch(sb, c_beg + (ch + 3) * kCh, u);
-            compute(0, c_beg + ch * kCh);
-            __syncthreads();
-            stash(sa, 0, u);
-            fetch(sa, c_beg + (ch + 4) * kCh, u);
-            compute(1, c_beg + (ch + 1) * kCh);
-        }
-    } else if (loader) {
-        // loader thread: units lt and lt + 32 HW of every chunk, chunks ch + 1 .. ch + 2 in flight
-        // while the compute waves take chunk ch; the same barriers as theirs
-        const int lt = tid - kNC;
-        const Unit u0 = unit_of(lt), u1 = unit_of(lt + kNC / 2);
-        St sa1, sb1;
-        fetch(sa, c_beg, u0);
-        fetch(sa1, c_beg, u1);
-        fetch(sb, c_beg + kCh, u0);
-        fetch(sb1, c_beg + kCh, u1);
-        stash(sa, 0, u0);
-        stash(sa1, 0, u1);
-        fetch(sa, c_beg + 2 * kCh, u0);
-        fetch(sa1, c_beg + 2 * kCh, u1);
-        for (int64_t ch = 0; ch < n_ch; ch += 2) {
-            __syncthreads();
-            stash(sb, 1, u0);
-            stash(sb1, 1, u1);
-            fetch(sb, c_beg + (ch + 3) * kCh, u0);
-            fetch(sb1, c_beg + (ch + 3) * kCh, u1);
-            __syncthreads();
-            stash(sa, 0, u0);
-            stash(sa1, 0, u1);
-            fetch(sa, c_beg + (ch + 4) * kCh, u0);
-            fetch(sa1, c_beg + (ch + 4) * kCh, u1);
-        }
-        return;
-    } else {
-        for (int64_t ch = 0; ch < n_ch; ch += 2) {
-            __syncthreads();
-            compute(0, c_beg + ch * kCh);
-            __syncthreads();
-            compute(1, c_beg + (ch + 1) * kCh);
-        }
+    for (int64_t ch = 0; ch < n_ch; ch += 2) {
+        __syncthreads();
+        compute(0, c_beg + ch * kCh);
+        if (ch + 1 >= n_ch) break;
+        __syncthreads();
+        compute(1, c_beg + (ch + 1) * kCh);
     }
 
     // ---- partial of row `col`: the sums are folded over the four lanes of the row
@@ -438,62 +485,73 @@ decode_mma_kernel(const SegParams p) {
     if (col < R) {
         const int r = col % p.gqa, i = col / p.gqa;
         const int64_t row = (g * p.gqa + r) + (int64_t)p.n_head * (i + (int64_t)p.n_q * b);
-        float *out = p.partials + ((int64_t)(p.slot0 + split) * p.n_rows + row) * kPartialStride;
-        if (grp == 0) {
+        float *out = p.partials + ((int64_t)(p.slot0 + split) * p.n_rows + row) * kPs;
+        if (grp == 0 && part == 0) {
             out[0] = (mrow == -INFINITY) ? -INFINITY : mrow * kLn2;
             out[1] = S;
         }
         // low nibbles: O = acc; high nibbles (16 (n - 8) after the offset): O = acc / 16
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt)
+        for (int dt = 0; dt < 2 * NBV; ++dt)
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                out[2 + 16 * dt + 4 * grp + e] = (dt & 1) ? oacc[dt][e] * 0.0625f : oacc[dt][e];
+                out[2 + 16 * (2 * NBV * part + dt) + 4 * grp + e] = (dt & 1) ? oacc[dt][e] * 0.0625f : oacc[dt][e];
     }
 }
 
-constexpr bool kLoaderWaves = true;  // workgroups with loader waves (see decode_mma_kernel)
+// compute waves per head: two at head dim 512, where one wave's registers cannot hold the
+// output of all sixteen V blocks beside Q
+template <int D>
+constexpr int kSplitV = D >= 512 ? 2 : 1;
 
-template <int R, int HW, bool CAP>
+template <int D, int HW, bool CAP>
 hipError_t launch_mma_c(const SegParams &p, hipStream_t s, int *occupancy) {
-    constexpr int kThreads = (kLoaderWaves ? 96 : 64) * HW;
+    constexpr int SV = kSplitV<D>;
+    constexpr int kThreads = Geo<D, HW, SV>::kThreads;
     if (occupancy)
-        return hipOccupancyMaxActiveBlocksPerMultiprocessor(occupancy, decode_mma_kernel<R, HW, CAP, kLoaderWaves>,
-                                                            kThreads, 0);
-    launch_seg(decode_mma_kernel<R, HW, CAP, kLoaderWaves>, dim3((unsigned)(p.n_splits * (p.n_head_kv / HW) * p.n_seq)),
+        return hipOccupancyMaxActiveBlocksPerMultiprocessor(occupancy, decode_mma_kernel<D, HW, SV, CAP>, kThreads, 0);
+    launch_seg(decode_mma_kernel<D, HW, SV, CAP>, dim3((unsigned)(p.n_splits * (p.n_head_kv / HW) * p.n_seq)),
                dim3(kThreads), s, p);
     return hipGetLastError();
 }
 
-template <int R, int HW>
+template <int D, int HW>
 hipError_t launch_mma(const SegParams &p, hipStream_t s, int *occupancy) {
-    return p.cap_l2 != 0.f ? launch_mma_c<R, HW, true>(p, s, occupancy) : launch_mma_c<R, HW, false>(p, s, occupancy);
-}
-
-template <int R>
-hipError_t launch_mma_r(const SegParams &p, hipStream_t s, int *occupancy) {
-    if (p.cell_hw == 8) return launch_mma<R, 8>(p, s, occupancy);
-    if (p.cell_hw == 4) return launch_mma<R, 4>(p, s, occupancy);
-    if (p.cell_hw == 2) return launch_mma<R, 2>(p, s, occupancy);
-    return hipErrorInvalidValue;
+    return p.cap_l2 != 0.f ? launch_mma_c<D, HW, true>(p, s, occupancy) : launch_mma_c<D, HW, false>(p, s, occupancy);
 }
 
 }  // namespace
 
+// A group of hw KV heads at head dim d has an instantiation when its two LDS stages stay near
+// 110 KB (hw * d <= 1024) and its loader threads fill whole waves (hw * d / 64 a multiple of 4).
+static bool mma_group_ok(int d, int hw) {
+    if (d == 512) return hw == 1;  // one head and two workgroups per CU (Q in LDS)
+    return (d == 64 || d == 128 || d == 256) && (hw == 8 || hw == 4 || hw == 2 || hw == 1) && hw * d <= 1024 &&
+           (hw * d / 64) % 4 == 0;
+}
+
+int decode_mma_heads(int d, int n_head_kv) {
+    for (int hw : {8, 4, 2, 1})
+        if (n_head_kv % hw == 0 && mma_group_ok(d, hw)) return hw;
+    return 0;
+}
+
 bool decode_mma_ok(const SegParams &p) {
-    return (p.cell_hw == 8 || p.cell_hw == 4 || p.cell_hw == 2) && p.gqa * p.n_q >= 1 && p.gqa * p.n_q <= 8;
+    return p.d == p.dv && mma_group_ok(p.d, p.cell_hw) && p.gqa * p.n_q >= 1 && p.gqa * p.n_q <= 8;
 }
 
 hipError_t launch_decode_mma(const SegParams &p, hipStream_t s, int *occupancy) {
-    switch (p.gqa * p.n_q) {
-        case 1: return launch_mma_r<1>(p, s, occupancy);
-        case 2: return launch_mma_r<2>(p, s, occupancy);
-        case 3: return launch_mma_r<3>(p, s, occupancy);
-        case 4: return launch_mma_r<4>(p, s, occupancy);
-        case 5: return launch_mma_r<5>(p, s, occupancy);
-        case 6: return launch_mma_r<6>(p, s, occupancy);
-        case 7: return launch_mma_r<7>(p, s, occupancy);
-        case 8: return launch_mma_r<8>(p, s, occupancy);
+    if (!decode_mma_ok(p)) return hipErrorInvalidValue;
+    switch (p.d * 16 + p.cell_hw) {
+        case 64 * 16 + 8: return launch_mma<64, 8>(p, s, occupancy);
+        case 64 * 16 + 4: return launch_mma<64, 4>(p, s, occupancy);
+        case 128 * 16 + 8: return launch_mma<128, 8>(p, s, occupancy);
+        case 128 * 16 + 4: return launch_mma<128, 4>(p, s, occupancy);
+        case 128 * 16 + 2: return launch_mma<128, 2>(p, s, occupancy);
+        case 256 * 16 + 4: return launch_mma<256, 4>(p, s, occupancy);
+        case 256 * 16 + 2: return launch_mma<256, 2>(p, s, occupancy);
+        case 256 * 16 + 1: return launch_mma<256, 1>(p, s, occupancy);
+        case 512 * 16 + 1: return launch_mma<512, 1>(p, s, occupancy);
         default: return hipErrorInvalidValue;
     }
 }

@@ -69,9 +69,10 @@ inline void launch_seg(F kernel, dim3 grid, dim3 block, hipStream_t s, const Seg
         hipLaunchKernelGGL(kernel, grid, block, 0, s, p, args...);
 }
 
-// KV heads per workgroup of the cell-major vector kernel for these types (0: no instantiation):
-// a workgroup owns that many heads, packed inside each cell, over a cell range.
-int cell_heads(int k_type, int v_type, int n_head_kv, int R, bool rows);
+// KV heads per workgroup of the cell-major kernels for this head dim (dk = dv = d) and these
+// types (0: no instantiation): a workgroup owns that many heads, packed inside each cell, over a
+// cell range.
+int cell_heads(int d, int k_type, int v_type, int n_head_kv, int R, bool rows);
 // Resident workgroups per CU of the cell-major kernel selected by p.cell_hw (at least 1).
 int cell_blocks_per_cu(const SegParams &p, int k_type, int v_type);
 
@@ -79,9 +80,11 @@ int cell_blocks_per_cu(const SegParams &p, int k_type, int v_type);
 // Which decode kernel launch_decode_segment will run for p (enum rkv_kernel_variant).
 int decode_kernel_variant(const SegParams &p, int k_type, int v_type);
 hipError_t launch_decode_segment(const SegParams &p, int k_type, int v_type, hipStream_t s);
-// Matrix-core decode kernel for cell-major q8_0 K / q4_0 V with 8 KV heads per workgroup
-// (decode_mma_ok); with `occupancy` set it reports resident workgroups per CU instead of
-// launching.
+// Matrix-core decode kernel for cell-major q8_0 K / q4_0 V at head dims 64, 128, 256 and 512
+// (dk = dv) with p.cell_hw KV heads per workgroup (decode_mma_ok); with `occupancy` set it
+// reports resident workgroups per CU instead of launching.  decode_mma_heads gives the group
+// size it takes for n_head_kv heads at head dim d (0: none).
+int decode_mma_heads(int d, int n_head_kv);
 bool decode_mma_ok(const SegParams &p);
 hipError_t launch_decode_mma(const SegParams &p, hipStream_t s, int *occupancy);
 // The binary16 matrix-core decode kernel (windows, tail tiles and row lists) over groups of
@@ -106,6 +109,10 @@ struct MergeRange {
 };
 hipError_t launch_merge(const float *partials, int n_seg, int64_t n_rows, float *o, float *lse,
                         float *partial_out, hipStream_t s, const MergeRange *range = nullptr);
+// The same merge for partial rows of 2 + dv floats (dv = 64, 128, 256, 512), up to 256 segments:
+// one thread per segment over 16-value parts of each row.
+hipError_t launch_merge_parts(const float *partials, int n_seg, int64_t n_rows, int dv, float *o, float *lse,
+                              hipStream_t s);
 // Writes (M=-inf, S=0, VKQ=0) for n_rows rows into partial slot 0.
 hipError_t launch_empty_partials(float *partials, int64_t n_rows, hipStream_t s);
 // Row-list extents in kRowExtentParts pieces per sequence: the maximum of
@@ -119,8 +126,8 @@ hipError_t launch_lift_copy(const void *host_src, void *dst, int64_t nbytes, hip
 hipError_t launch_dequant_rows(const void *src, int type, int form, int64_t n_rows, int n_values, int64_t row_stride,
                                float *dst, hipStream_t s);
 
-// Head dims other than 128 (rkv_decode_hd.hip): decode segments (gqa * n_q <= 8, no row lists)
-// and the merge of partials with row stride 2 + dv.
+// Head dims other than 128 (rkv_decode_hd.hip): the vector decode kernel (any gqa * n_q, row
+// lists) and the merge of partials with row stride 2 + dv.
 bool head_dim_supported(int d);              // one tensor's head dim: 64, 128, 256, 512 or 576
 bool head_dims_supported(int dk, int dv);   // a (Q/K, V) pair: equal in 64..512, or 576 / 512
 hipError_t launch_decode_hd(const SegParams &p, int k_type, int v_type, hipStream_t s);

@@ -36,18 +36,20 @@ struct RowRange {
 };
 
 // Up to kMergePartThreads segments over few rows: workgroup (row, part) merges head_dim values
-// 16*part .. 16*part+15 of one row with one thread per segment, so every load of the merge is
-// issued at once by kMergeParts times more workgroups than rows and the merge costs one memory
-// latency.  M and S are read by every part (8 bytes per segment).
-constexpr int kMergeParts = 8;
-constexpr int kMergePartDim = kHeadDim / kMergeParts;
+// 16*part .. 16*part+15 of one row (D / 16 parts; partial rows of 2 + D floats) with one thread
+// per segment, so every load of the merge is issued at once by D / 16 times more workgroups
+// than rows and the merge costs one memory latency.  M and S are read by every part (8 bytes
+// per segment).
+constexpr int kMergePartDim = 16;
 constexpr int kMergePartThreads = 256;
 
+template <int D>
 __global__ void __launch_bounds__(kMergePartThreads) merge_parts_kernel(const float *__restrict__ part, int n_seg,
                                                                         int64_t n_rows, float *__restrict__ o,
                                                                         float *__restrict__ lse,
                                                                         float *__restrict__ pout, RowRange rr) {
     constexpr int kW = kMergePartThreads / 64;
+    constexpr int kPs = 2 + D;
     __shared__ float s_m[kW];
     __shared__ float s_acc[kW][kMergePartDim + 1];
     const int64_t row = blockIdx.x;
@@ -55,7 +57,7 @@ __global__ void __launch_bounds__(kMergePartThreads) merge_parts_kernel(const fl
     int sa, sb;
     rr.of(row, n_seg, sa, sb);
     const bool has = sa + tid < sb;
-    const float *pp = part + ((int64_t)(has ? sa + tid : 0) * n_rows + row) * kPartialStride;
+    const float *pp = part + ((int64_t)(has ? sa + tid : 0) * n_rows + row) * kPs;
     float2 ms = make_float2(-INFINITY, 0.f);
     float v[kMergePartDim];
     if (has) {
@@ -99,7 +101,7 @@ __global__ void __launch_bounds__(kMergePartThreads) merge_parts_kernel(const fl
         return x;
     }();
     if (pout) {
-        float *dst = pout + row * kPartialStride;
+        float *dst = pout + row * kPs;
         if (tid < kMergePartDim) dst[2 + kMergePartDim * pt + tid] = a;
         else if (pt == 0) {
             dst[0] = M;
@@ -108,7 +110,7 @@ __global__ void __launch_bounds__(kMergePartThreads) merge_parts_kernel(const fl
         return;
     }
     const bool ok = (M != -INFINITY) && (Stot > 0.f);
-    if (tid < kMergePartDim) o[row * kHeadDim + kMergePartDim * pt + tid] = ok ? a / Stot : 0.f;
+    if (tid < kMergePartDim) o[row * D + kMergePartDim * pt + tid] = ok ? a / Stot : 0.f;
     else if (lse && pt == 0) lse[row] = ok ? M + logf(Stot) : -INFINITY;
 }
 
@@ -272,12 +274,35 @@ hipError_t launch_merge(const float *partials, int n_seg, int64_t n_rows, float 
         hipLaunchKernelGGL(merge_rows_kernel, dim3((unsigned)((n_rows + kMergeRowsPerBlock - 1) / kMergeRowsPerBlock)),
                            dim3(64 * kMergeRowsPerBlock), 0, s, partials, n_seg, n_rows, o, lse, partial_out, rr);
     } else if (n_seg <= kMergePartThreads) {
-        hipLaunchKernelGGL(merge_parts_kernel, dim3((unsigned)n_rows, kMergeParts), dim3(kMergePartThreads), 0, s,
-                           partials, n_seg, n_rows, o, lse, partial_out, rr);
+        hipLaunchKernelGGL(merge_parts_kernel<kHeadDim>, dim3((unsigned)n_rows, kHeadDim / kMergePartDim),
+                           dim3(kMergePartThreads), 0, s, partials, n_seg, n_rows, o, lse, partial_out, rr);
     } else {
         hipLaunchKernelGGL(merge_kernel, dim3((unsigned)n_rows), dim3(kMergeThreads), 0, s, partials, n_seg, n_rows,
                            o, lse, partial_out, rr);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_merge_parts(const float *partials, int n_seg, int64_t n_rows, int dv, float *o, float *lse,
+                              hipStream_t s) {
+    if (n_rows <= 0) return hipSuccess;
+    if (n_seg > kMergePartThreads || n_rows > ((int64_t)1 << 31) - 1) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)n_rows, (unsigned)(dv / kMergePartDim));
+    const RowRange rr{};
+    if (dv == 64)
+        hipLaunchKernelGGL(merge_parts_kernel<64>, grid, dim3(kMergePartThreads), 0, s, partials, n_seg, n_rows, o, lse,
+                           nullptr, rr);
+    else if (dv == 128)
+        hipLaunchKernelGGL(merge_parts_kernel<128>, grid, dim3(kMergePartThreads), 0, s, partials, n_seg, n_rows, o,
+                           lse, nullptr, rr);
+    else if (dv == 256)
+        hipLaunchKernelGGL(merge_parts_kernel<256>, grid, dim3(kMergePartThreads), 0, s, partials, n_seg, n_rows, o,
+                           lse, nullptr, rr);
+    else if (dv == 512)
+        hipLaunchKernelGGL(merge_parts_kernel<512>, grid, dim3(kMergePartThreads), 0, s, partials, n_seg, n_rows, o,
+                           lse, nullptr, rr);
+    else
+        return hipErrorNotSupported;
     return hipGetLastError();
 }
 

@@ -321,9 +321,9 @@ struct Seg {
 // apply: every cell must hold the KV heads packed (head stride == row size), cell strides and
 // bases must be 16-byte aligned, and the types and head count must have an instantiation.
 int use_cell_kernel(const Seg &sg, const SegParams &p, int k_type, int v_type) {
-    if (p.d != kHeadDim || p.dv != kHeadDim) return 0;
-    const int64_t rk = row_bytes(k_type), rv = row_bytes(v_type);
-    const int hw = cell_heads(k_type, v_type, p.n_head_kv, p.gqa * p.n_q, p.rows != nullptr);
+    if (p.d != p.dv) return 0;
+    const int64_t rk = row_bytes(k_type, p.d), rv = row_bytes(v_type, p.dv);
+    const int hw = cell_heads(p.d, k_type, v_type, p.n_head_kv, p.gqa * p.n_q, p.rows != nullptr);
     if (hw == 0) return 0;
     if (p.n_head_kv > 1 && (sg.k_s2 != rk || sg.v_s2 != rv)) return 0;
     if (sg.k_s1 < p.n_head_kv * rk || sg.v_s1 < p.n_head_kv * rv) return 0;
