@@ -388,6 +388,12 @@ __attribute__((amdgpu_waves_per_eu((Geo<D, HW, SV>::kWavesPerEu)))) decode_mma_k
             if constexpr (NB > kQg) __builtin_amdgcn_sched_barrier(0);
         }
 
+        // the scores are complete here: without this pin the compiler defers the block sums
+        // past the visibility branch below and keeps every raw-score accumulator live across it
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) asm volatile("" : "+v"(s[kt][ii]));
         // ---- visibility: whole chunk visible, or per element (chunk end, causal rule, mask)
         const bool full = (c0 + kCh <= c_end) && !p.mask && (p.q_pos0 < 0 || p.pos0 + c0 + kCh - 1 <= p.q_pos0);
         float cc = c;
