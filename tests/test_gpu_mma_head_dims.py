@@ -1,8 +1,9 @@
 """The matrix-core decode kernel at head dims 64, 256 and 512 (dk = dv, q8_0 K / q4_0 V, cell-major
 KV heads) against the fp64 oracle: every head-group size it takes (8 and 4 KV heads at 64; 4, 2
-and 1 at 256; 1 at 512), one to eight rows per KV head, the window + lifted or device tail split,
-masks with an empty row, ragged lengths, the causal rule of a small prefill call, the soft-cap,
-and the full 131072-cell shape of the 128K decode at each head dim.  What a segment computes is
+and 1 at 256; 1 at 512), one to eight rows per KV head and more in row groups of 16, the window
++ lifted or device tail split, masks with an empty row, ragged lengths, the causal rule of a
+small prefill call, the soft-cap, and the full 131072-cell shape of the 128K decode at each
+head dim.  What a segment computes is
 the streaming partial of opencoti-llamafile patch 0070-rolling-kv (fattn.cu, streaming_lse_kernel);
 the head dims are those its streaming op supports."""
 import numpy as np
@@ -70,6 +71,22 @@ def test_small_prefill_causal(run, d):
     assert run.ctx.stats()["kernel_variant"] == MMA
     Oref, Lref = oracle_decode(w, mask=oracle.causal_mask(n_q, n_kv, q_pos0))
     assert_close(O, L, Oref, Lref, what=f"mma d={d} causal")
+
+
+# (d, n_head, n_head_kv, n_q): more than 16 rows per KV head, in row groups of 16 (the last one
+# ragged), down to a single KV head with 128 query heads
+ROW_GROUPS = [(64, 64, 4, 2), (64, 40, 8, 5), (256, 16, 1, 1), (256, 48, 2, 3), (512, 128, 1, 1), (512, 20, 1, 3)]
+
+
+@pytest.mark.parametrize("d,n_head,n_head_kv,n_q", ROW_GROUPS)
+def test_row_groups(run, d, n_head, n_head_kv, n_q):
+    w = gen.make_workload(2, scale_down=64, d=d, n_head=n_head, n_head_kv=n_head_kv, n_q=n_q)  # n_kv 2048
+    mask = gen.random_mask_f16(np.random.default_rng(d + n_head), n_q, w["n_kv"], p_hidden=0.2)
+    step(f"mma d={d} heads {n_head}/{n_head_kv} n_q {n_q} ({n_q * n_head // n_head_kv} rows per KV head)")
+    O, L = run.decode(w, wc=1300, tile_kv=400, tail="host", mask=mask)
+    assert run.ctx.stats()["kernel_variant"] == MMA
+    Oref, Lref = oracle_decode(w, mask=mask)
+    assert_close(O, L, Oref, Lref, what=f"mma row groups d={d} {n_head}/{n_head_kv} n_q {n_q}")
 
 
 @pytest.mark.parametrize("d", [64, 256, 512])

@@ -714,10 +714,7 @@ hipError_t launch_cell(const SegParams &p, hipStream_t s, int *occupancy) {
 template <int KT, int VT, int R>
 hipError_t launch_decode_r(const SegParams &p, hipStream_t s, int *occupancy) {
     if (p.cell_hw > 0) {
-        if constexpr (KT == T_Q8_0 && VT == T_Q4_0) {
-            // groups of 8, 4 or 2 KV heads: the matrix-core kernel
-            if (decode_mma_ok(p)) return launch_decode_mma(p, s, occupancy);
-        }
+        // (q8_0 / q4_0 cell groups go to the matrix-core kernel before the rows are dispatched)
         if constexpr (KT == T_F16 && VT == T_F16) {
             if (decode_mma16_ok(p)) return launch_decode_mma16(p, s, occupancy);
             if (p.cell_hw == 2) return launch_cell<KT, VT, R, 2>(p, s, occupancy);
@@ -756,6 +753,10 @@ hipError_t launch_decode_t(const SegParams &p, int R, hipStream_t s, int *occupa
 
 hipError_t dispatch_decode(const SegParams &p, int k_type, int v_type, hipStream_t s, int *occupancy) {
     const int R = p.gqa * p.n_q;
+    // cell groups of q8_0 / q4_0 heads: the matrix-core kernel, any number of rows at head dims
+    // other than 128 (row groups of 16)
+    if (p.cell_hw > 0 && k_type == T_Q8_0 && v_type == T_Q4_0)
+        return decode_mma_ok(p) ? launch_decode_mma(p, s, occupancy) : hipErrorInvalidValue;
     if (k_type == T_Q8_0 && v_type == T_Q4_0) return launch_decode_t<T_Q8_0, T_Q4_0>(p, R, s, occupancy);
     if (k_type == T_F16 && v_type == T_F16) return launch_decode_t<T_F16, T_F16>(p, R, s, occupancy);
     if (k_type == T_Q8_0 && v_type == T_F16) return launch_decode_t<T_Q8_0, T_F16>(p, R, s, occupancy);
@@ -766,10 +767,12 @@ hipError_t dispatch_decode(const SegParams &p, int k_type, int v_type, hipStream
 }  // namespace
 
 int cell_heads(int d, int k_type, int v_type, int n_head_kv, int R, bool rows) {
-    if (R < 1 || R > kMaxRowsVec) return 0;
-    // q8_0 / q4_0: the matrix-core kernel at head dims 64 .. 512 (not for gathered rows)
-    if (k_type == T_Q8_0 && v_type == T_Q4_0) return rows ? 0 : decode_mma_heads(d, n_head_kv);
-    if (d != kHeadDim) return 0;
+    if (R < 1) return 0;
+    // q8_0 / q4_0: the matrix-core kernel at head dims 64 .. 512 (not for gathered rows; up to 8
+    // rows per KV head at 128, any number at the other head dims)
+    if (k_type == T_Q8_0 && v_type == T_Q4_0)
+        return (rows || (d == kHeadDim && R > kMaxRowsVec)) ? 0 : decode_mma_heads(d, n_head_kv);
+    if (d != kHeadDim || R > kMaxRowsVec) return 0;
     // binary16 with eight KV heads per cell group: the matrix-core kernel, also for row lists
     if (k_type == T_F16 && v_type == T_F16 && n_head_kv % 8 == 0) return 8;
     if (rows) return 0;  // other gathered rows: per-head kernel

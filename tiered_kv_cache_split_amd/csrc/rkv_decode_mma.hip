@@ -139,9 +139,15 @@ __attribute__((amdgpu_waves_per_eu((Geo<D, HW, SV>::kWavesPerEu)))) decode_mma_k
 
     const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int col = lane & 15, grp = lane >> 4;
-    const int R = p.gqa * p.n_q;  // query rows of a KV head (at most 8: padding columns of the MFMAs)
+    // query rows rho = i * gqa + r of a KV head, in groups of 16 (the columns of the MFMA tiles;
+    // columns past the group's rows are padding); the row group is the fastest grid index, so
+    // the groups reading one chunk run together
+    const int R_all = p.gqa * p.n_q, n_rg = (R_all + 15) >> 4;
     const int n_hgrp = p.n_head_kv / HW;
     int bid = blockIdx.x;
+    const int rg = bid % n_rg;
+    bid /= n_rg;
+    const int R0 = 16 * rg, R = min(16, R_all - R0);  // this workgroup's rows R0 .. R0 + R - 1
     const int split = bid % p.n_splits;
     bid /= p.n_splits;
     const int hgrp = bid % n_hgrp;
@@ -271,7 +277,7 @@ __attribute__((amdgpu_waves_per_eu((Geo<D, HW, SV>::kWavesPerEu)))) decode_mma_k
     // in P.V slot 8 grp + col / 2; it receives byte col of the 8 keys of its slots
     const int vkey = 4 * grp + ((col >> 1) & 3) + 16 * (col >> 3);
     const int vrd = vkey * kVc + 64 * ((vkey >> 4) & 1) + 8 * (col & 1);
-    const int qi_row = min(col, R - 1) / p.gqa;  // query position of this lane's row
+    const int qi_row = (R0 + min(col, R - 1)) / p.gqa;  // query position of this lane's row
 
     // ---- Q^T as the B operand of Q.K: lane holds row `col`, head_dim 32*blk + 8*grp + 0..7
     // accumulator inputs: -1152 * block sum of row `col` of Q, in registers or (wide heads) at
@@ -283,7 +289,7 @@ __attribute__((amdgpu_waves_per_eu((Geo<D, HW, SV>::kWavesPerEu)))) decode_mma_k
     const int q_off = 16 * (64 * NB * wh + lane);
     {
         const bool ok = col < R;
-        const int r = ok ? col : 0;
+        const int r = R0 + (ok ? col : 0);
         const _Float16 *qrow = p.q + (int64_t)(r / p.gqa) * p.q_s1 + (int64_t)(g * p.gqa + r % p.gqa) * p.q_s2 +
                                (int64_t)b * p.q_s3;
         uint4 qv[NB];
@@ -489,7 +495,7 @@ __attribute__((amdgpu_waves_per_eu((Geo<D, HW, SV>::kWavesPerEu)))) decode_mma_k
     // ---- partial of row `col`: the sums are folded over the four lanes of the row
     const float S = fold_rows(lrow);
     if (col < R) {
-        const int r = col % p.gqa, i = col / p.gqa;
+        const int rho = R0 + col, r = rho % p.gqa, i = rho / p.gqa;
         const int64_t row = (g * p.gqa + r) + (int64_t)p.n_head * (i + (int64_t)p.n_q * b);
         float *out = p.partials + ((int64_t)(p.slot0 + split) * p.n_rows + row) * kPs;
         if (grp == 0 && part == 0) {
@@ -516,8 +522,9 @@ hipError_t launch_mma_c(const SegParams &p, hipStream_t s, int *occupancy) {
     constexpr int kThreads = Geo<D, HW, SV>::kThreads;
     if (occupancy)
         return hipOccupancyMaxActiveBlocksPerMultiprocessor(occupancy, decode_mma_kernel<D, HW, SV, CAP>, kThreads, 0);
-    launch_seg(decode_mma_kernel<D, HW, SV, CAP>, dim3((unsigned)(p.n_splits * (p.n_head_kv / HW) * p.n_seq)),
-               dim3(kThreads), s, p);
+    const int64_t blocks = (int64_t)p.n_splits * (p.n_head_kv / HW) * p.n_seq * decode_mma_row_groups(p);
+    if (blocks > ((int64_t)1 << 31) - 1) return hipErrorInvalidValue;
+    launch_seg(decode_mma_kernel<D, HW, SV, CAP>, dim3((unsigned)blocks), dim3(kThreads), s, p);
     return hipGetLastError();
 }
 
@@ -536,6 +543,8 @@ static bool mma_group_ok(int d, int hw) {
            (hw * d / 64) % 4 == 0;
 }
 
+int decode_mma_row_groups(const SegParams &p) { return (int)(((int64_t)p.gqa * p.n_q + 15) / 16); }
+
 int decode_mma_heads(int d, int n_head_kv) {
     for (int hw : {8, 4, 2, 1})
         if (n_head_kv % hw == 0 && mma_group_ok(d, hw)) return hw;
@@ -543,7 +552,10 @@ int decode_mma_heads(int d, int n_head_kv) {
 }
 
 bool decode_mma_ok(const SegParams &p) {
-    return p.d == p.dv && mma_group_ok(p.d, p.cell_hw) && p.gqa * p.n_q >= 1 && p.gqa * p.n_q <= 8;
+    // rows per KV head: up to 8 at head dim 128 (the decode contract there), any number at the
+    // other head dims (row groups of 16)
+    const int64_t R = (int64_t)p.gqa * p.n_q;
+    return p.d == p.dv && mma_group_ok(p.d, p.cell_hw) && R >= 1 && (p.d != kHeadDim || R <= kMaxRowsVec);
 }
 
 hipError_t launch_decode_mma(const SegParams &p, hipStream_t s, int *occupancy) {

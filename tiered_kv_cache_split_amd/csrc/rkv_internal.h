@@ -81,11 +81,14 @@ int cell_blocks_per_cu(const SegParams &p, int k_type, int v_type);
 int decode_kernel_variant(const SegParams &p, int k_type, int v_type);
 hipError_t launch_decode_segment(const SegParams &p, int k_type, int v_type, hipStream_t s);
 // Matrix-core decode kernel for cell-major q8_0 K / q4_0 V at head dims 64, 128, 256 and 512
-// (dk = dv) with p.cell_hw KV heads per workgroup (decode_mma_ok); with `occupancy` set it
+// (dk = dv) with p.cell_hw KV heads per workgroup and up to 16 query rows per KV head per
+// workgroup (more in row groups; at most 8 in all at head dim 128) (decode_mma_ok); with `occupancy` set it
 // reports resident workgroups per CU instead of launching.  decode_mma_heads gives the group
 // size it takes for n_head_kv heads at head dim d (0: none).
 int decode_mma_heads(int d, int n_head_kv);
 bool decode_mma_ok(const SegParams &p);
+// Row groups of 16 query rows per KV head (one workgroup each) of the cell-major decode launch.
+int decode_mma_row_groups(const SegParams &p);
 hipError_t launch_decode_mma(const SegParams &p, hipStream_t s, int *occupancy);
 // The binary16 matrix-core decode kernel (windows, tail tiles and row lists) over groups of
 // eight cell-major KV heads with gqa * n_q <= 8 rows per head; the same occupancy convention.

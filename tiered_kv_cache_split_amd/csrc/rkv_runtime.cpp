@@ -361,9 +361,9 @@ void seg_plan(const rkv_ctx *ctx, int64_t n_cells, const SegParams &p, bool mfma
         cps = n_cells;
         return;
     } else if (p.cell_hw > 0) {
-        // cell-major kernel: one wave of resident workgroups over (split, head group, sequence),
-        // at least 256 cells per split
-        const int64_t groups = (int64_t)p.n_seq * (p.n_head_kv / p.cell_hw);
+        // cell-major kernel: one wave of resident workgroups over (split, head group, sequence,
+        // row group of 16), at least 256 cells per split
+        const int64_t groups = (int64_t)p.n_seq * (p.n_head_kv / p.cell_hw) * decode_mma_row_groups(p);
         const int64_t slots = (int64_t)std::max(1, cell_occupancy) * ctx->n_cu;
         int64_t want = ctx->splits_override > 0 ? ctx->splits_override : std::max<int64_t>(1, slots / groups);
         want = std::max<int64_t>(1, std::min(want, std::max<int64_t>(1, n_cells / 256)));
