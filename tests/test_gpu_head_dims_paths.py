@@ -1,7 +1,7 @@
 """Head dims other than 128 on the prefill and row-list entry points and with more than eight
-rows per KV head, against the fp64 oracle.  Cell-major q8_0 / q4_0 decode and prefill at
-dk = dv run on the matrix-core kernel in row groups of 16; row lists, the other type pairs and
-576 / 512 run on the vector kernel in row groups of eight (opencoti-llamafile patch
+rows per KV head, against the fp64 oracle.  Cell-major q8_0 / q4_0 decode and prefill run on
+the matrix-core kernel in row groups of 16; row lists and the other type pairs run on the vector
+kernel in row groups of eight (opencoti-llamafile patch
 0070-rolling-kv: the streaming op's split-and-combine over several head dims; llama.cpp PR
 #29510: the row-list form)."""
 import numpy as np
@@ -65,8 +65,8 @@ def test_prefill_causal_window_plus_tail(run, dk, dv, lift):
     step(f"prefill head dims {dk}/{dv}: 48 queries causal, lift {lift}")
     O, L = run.decode(w, tail="host", prefill=True, q_pos0=w["q_pos0"])
     st = run.ctx.stats()
-    # 240 rows per KV head: the matrix-core kernel in 15 row groups at dk = dv, else vector
-    assert st["kernel_variant"] == (3 if dk == dv else 5) and st["n_tail_tiles"] == 2
+    # 240 rows per KV head over q8_0 / q4_0: the matrix-core kernel in 15 row groups
+    assert st["kernel_variant"] == 3 and st["n_tail_tiles"] == 2
     Oref, Lref = oracle_decode(w, mask=oracle.causal_mask(n_q, w["n_kv"], w["q_pos0"]))
     assert_close(O, L, Oref, Lref, what=f"prefill d={dk}/{dv}")
 

@@ -37,8 +37,8 @@ def test_window_plus_lifted_tail(run, dk, dv, kt, vt, lift):
     step(f"head dims {dk}/{dv}: k={kt} v={vt} wc=1333 tile=700 lift {lift}")
     O, L = run.decode(w, wc=1333, tile_kv=700, tail="host")
     st = run.ctx.stats()
-    # q8_0 / q4_0 at 512 / 512: the matrix-core kernel; 576 / 512 and the other pairs: vector
-    mma = dk == dv == 512 and (kt, vt) == (gen.TYPE_Q8_0, gen.TYPE_Q4_0)
+    # q8_0 / q4_0 (512 / 512 and 576 / 512): the matrix-core kernel; the other pairs: vector
+    mma = (kt, vt) == (gen.TYPE_Q8_0, gen.TYPE_Q4_0)
     assert st["kernel_variant"] == (3 if mma else 5) and st["n_tail_tiles"] == -(-(4096 - 1333) // 700)
     assert O.shape == (1, 8, dv)
     Oref, Lref = oracle_decode(w)
@@ -151,13 +151,15 @@ def test_single_key_v_bit_exact(run, dk, dv):
     assert np.all(L[0] == 0.0)
 
 
-def test_one_hot_k_exact_at_576():
+@pytest.mark.parametrize("vt", [gen.TYPE_F16, gen.TYPE_Q4_0])
+def test_one_hot_k_exact_at_576(vt):
     """dk = 576: one-hot Q on each of the last two blocks' dims and on a main block, one visible
-    key: the LSE is scale * d * q of one code (codes -128 / 127, scales needing 11 bits)."""
+    key: the LSE is scale * d * q of one code (codes -128 / 127, scales needing 11 bits); binary16
+    V runs on the vector kernel, q4_0 V on the matrix-core kernel."""
     run = Runner()
     rng = np.random.default_rng(576)
     n_kv, j0 = 300, 123
-    w = gen.make_workload(1, d=576, dv=512, n_head=8, n_head_kv=2, k_type=gen.TYPE_Q8_0, v_type=gen.TYPE_F16)
+    w = gen.make_workload(1, d=576, dv=512, n_head=8, n_head_kv=2, k_type=gen.TYPE_Q8_0, v_type=vt)
     w["n_kv"] = n_kv
     w["k"], w["v"] = w["k"][:n_kv].copy(), w["v"][:n_kv].copy()
     for g in range(2):
@@ -173,8 +175,9 @@ def test_one_hot_k_exact_at_576():
     w["q"] = q
     mask = np.full((1, n_kv), -np.inf, np.float16)
     mask[0, j0] = 0
-    step("head dims 576/512: one-hot K exactness")
+    step(f"head dims 576/512: one-hot K exactness, V type {vt}")
     O, L = run.decode(w, wc=200, tile_kv=64, tail="host", mask=mask)
+    assert run.ctx.stats()["kernel_variant"] == (3 if vt == gen.TYPE_Q4_0 else 5)
     Oref, Lref = oracle_decode(w, mask=mask.astype(np.float64))
     err = np.abs(L - Lref) / np.maximum(np.abs(Lref), 1e-30)
     assert np.all((err <= 2e-6) | (L == Lref)), err.max()

@@ -1,6 +1,6 @@
-"""The matrix-core decode kernel at head dims 64, 256 and 512 (dk = dv, q8_0 K / q4_0 V, cell-major
-KV heads) against the fp64 oracle: every head-group size it takes (8 and 4 KV heads at 64; 4, 2
-and 1 at 256; 1 at 512), one to eight rows per KV head and more in row groups of 16, the window
+"""The matrix-core decode kernel at head dims 64, 256, 512 (dk = dv) and the 576 / 512 pair (q8_0 K
+/ q4_0 V, cell-major KV heads) against the fp64 oracle: every head-group size it takes (8 and 4
+KV heads at 64; 4, 2 and 1 at 256; 1 at 512 and 576), one to eight rows per KV head and more in row groups of 16, the window
 + lifted or device tail split, masks with an empty row, ragged lengths, the causal rule of a
 small prefill call, the soft-cap, and the full 131072-cell shape of the 128K decode at each
 head dim.  What a segment computes is
@@ -18,6 +18,11 @@ pytestmark = pytest.mark.gpu
 MMA = 3  # rkv_kernel_variant: matrix-core cell-major decode
 
 
+def workload(d, **kw):
+    """Workload 2's shape at Q/K head dim d (V head dim 512 with d = 576)."""
+    return gen.make_workload(2, d=d, dv=512 if d == 576 else d, **kw)
+
+
 @pytest.fixture(scope="module")
 def run():
     r = Runner()
@@ -31,12 +36,13 @@ SHAPES = [
     (64, 40, 8, 1), (64, 16, 4, 2), (64, 8, 8, 1),
     (256, 40, 8, 1), (256, 8, 2, 2), (256, 3, 1, 2), (256, 7, 1, 1),
     (512, 16, 2, 1), (512, 5, 1, 1), (512, 4, 1, 2), (512, 1, 1, 1),
+    (576, 8, 2, 1), (576, 3, 1, 2), (576, 1, 1, 1),
 ]
 
 
 @pytest.mark.parametrize("d,n_head,n_head_kv,n_q", SHAPES)
 def test_groups_and_rows(run, d, n_head, n_head_kv, n_q):
-    w = gen.make_workload(2, scale_down=32, d=d, n_head=n_head, n_head_kv=n_head_kv, n_q=n_q)  # n_kv 4096
+    w = workload(d, scale_down=32, n_head=n_head, n_head_kv=n_head_kv, n_q=n_q)  # n_kv 4096
     step(f"mma d={d} heads {n_head}/{n_head_kv} n_q {n_q}: window 2900 + lifted tail in 600-cell tiles")
     O, L = run.decode(w, wc=2900, tile_kv=600, tail="host")
     assert run.ctx.stats()["kernel_variant"] == MMA
@@ -44,10 +50,10 @@ def test_groups_and_rows(run, d, n_head, n_head_kv, n_q):
     assert_close(O, L, Oref, Lref, what=f"mma d={d} {n_head}/{n_head_kv} n_q {n_q}")
 
 
-@pytest.mark.parametrize("d", [64, 256, 512])
+@pytest.mark.parametrize("d", [64, 256, 512, 576])
 @pytest.mark.parametrize("tail", ["device", "host"])
 def test_ragged_mask_and_empty_row(run, d, tail):
-    w = dict(gen.make_workload(2, scale_down=32, d=d, n_head=16, n_head_kv=4, n_q=2))  # 8 rows per KV head
+    w = dict(workload(d, scale_down=32, n_head=16, n_head_kv=4, n_q=2))  # 8 rows per KV head
     n_kv = 3001
     w["k"], w["v"], w["n_kv"] = w["k"][:n_kv], w["v"][:n_kv], n_kv
     mask = gen.random_mask_f16(np.random.default_rng(d), 2, n_kv, p_hidden=0.35)
@@ -60,10 +66,10 @@ def test_ragged_mask_and_empty_row(run, d, tail):
     assert np.all(O[1] == 0) and np.all(L[1] == -np.inf)
 
 
-@pytest.mark.parametrize("d", [64, 256, 512])
+@pytest.mark.parametrize("d", [64, 256, 512, 576])
 def test_small_prefill_causal(run, d):
     """Two queries of four heads per KV head (8 rows): the causal rule inside the kernel."""
-    w = gen.make_workload(2, scale_down=32, d=d, n_head=16, n_head_kv=4, n_q=2)
+    w = workload(d, scale_down=32, n_head=16, n_head_kv=4, n_q=2)
     n_q, n_kv = 2, w["n_kv"]
     q_pos0 = n_kv - 700  # the queries sit inside the window, so later keys and the tail are hidden
     step(f"mma d={d}: prefill of 2 queries at {q_pos0}, window 3500 + lifted tail")
@@ -75,12 +81,13 @@ def test_small_prefill_causal(run, d):
 
 # (d, n_head, n_head_kv, n_q): more than 16 rows per KV head, in row groups of 16 (the last one
 # ragged), down to a single KV head with 128 query heads
-ROW_GROUPS = [(64, 64, 4, 2), (64, 40, 8, 5), (256, 16, 1, 1), (256, 48, 2, 3), (512, 128, 1, 1), (512, 20, 1, 3)]
+ROW_GROUPS = [(64, 64, 4, 2), (64, 40, 8, 5), (256, 16, 1, 1), (256, 48, 2, 3), (512, 128, 1, 1), (512, 20, 1, 3),
+              (576, 128, 1, 1), (576, 16, 1, 2)]
 
 
 @pytest.mark.parametrize("d,n_head,n_head_kv,n_q", ROW_GROUPS)
 def test_row_groups(run, d, n_head, n_head_kv, n_q):
-    w = gen.make_workload(2, scale_down=64, d=d, n_head=n_head, n_head_kv=n_head_kv, n_q=n_q)  # n_kv 2048
+    w = workload(d, scale_down=64, n_head=n_head, n_head_kv=n_head_kv, n_q=n_q)  # n_kv 2048
     mask = gen.random_mask_f16(np.random.default_rng(d + n_head), n_q, w["n_kv"], p_hidden=0.2)
     step(f"mma d={d} heads {n_head}/{n_head_kv} n_q {n_q} ({n_q * n_head // n_head_kv} rows per KV head)")
     O, L = run.decode(w, wc=1300, tile_kv=400, tail="host", mask=mask)
@@ -89,9 +96,9 @@ def test_row_groups(run, d, n_head, n_head_kv, n_q):
     assert_close(O, L, Oref, Lref, what=f"mma row groups d={d} {n_head}/{n_head_kv} n_q {n_q}")
 
 
-@pytest.mark.parametrize("d", [64, 256, 512])
+@pytest.mark.parametrize("d", [64, 256, 512, 576])
 def test_softcap(run, d):
-    w = gen.make_workload(2, scale_down=32, d=d, n_head=16, n_head_kv=4)
+    w = workload(d, scale_down=32, n_head=16, n_head_kv=4)
     run.ctx.set_softcap(20.0)
     try:
         step(f"mma d={d}: soft-cap 20, window 2600 + lifted tail")
@@ -103,11 +110,11 @@ def test_softcap(run, d):
     assert_close(O, L, Oref, Lref, what=f"mma d={d} softcap")
 
 
-@pytest.mark.parametrize("d", [64, 256, 512])
+@pytest.mark.parametrize("d", [64, 256, 512, 576])
 def test_full_size_128k_all_heads(run, d):
     """131072 resident cells, 40/8 heads, in the launch configuration the benchmark times at this
     head dim; every query head against the oracle over all keys."""
-    w = gen.make_workload(2, d=d)
+    w = workload(d)
     step(f"mma d={d}: full size 131072 cells, 40/8 heads")
     O, L = run.decode(w, wc=w["n_kv"], tail=None)
     assert run.ctx.stats()["kernel_variant"] == MMA

@@ -68,69 +68,76 @@ __device__ __forceinline__ float row16_sum(float x) {
     return x;
 }
 
-// One chunk unit in registers: two q8_0 blocks of one head's K row (68 bytes: bytes 0..35 as
-// nine words, the second block's aligned codes 36..67 as two quads) and the two q4_0 blocks of
-// the same head_dim range of its V row (36 bytes: bytes 0..19 as five words, the second block's
-// aligned data 20..35 as one quad).  The aligned quads go to LDS as loaded.
-struct Stage {
+// A chunk unit in registers: two q8_0 blocks of one head's K row (68 bytes: bytes 0..35 as nine
+// words, the second block's aligned codes 36..67 as two quads), or two q4_0 blocks of its V row
+// (36 bytes: bytes 0..19 as five words, the second block's aligned data 20..35 as one quad).
+// The aligned quads go to LDS as loaded.
+struct KStage {
     uint4 ka0, ka1, kb0, kb1;
     uint32_t kx;
+};
+struct VStage {
     uint4 va, vb;
     uint32_t vx;
 };
 
-// Geometry of a workgroup for head dim D (= dv), HW KV heads and SV compute waves per head
-// (each of them takes 1 / SV of the V blocks).  A unit is two blocks of one head (Stage
-// above); a cell holds kTpc units, a chunk kCh cells.  Loader threads take two units of every
-// chunk, so their count kNL is a whole number of waves when HW * D / 64 is a multiple of 4.
-template <int D, int HW, int SV>
+// Geometry of a workgroup for head dims DK (Q, K) and DV (V), HW KV heads and SV compute waves
+// per head (each of them takes 1 / SV of the V blocks).  A K unit is two blocks of one head's K
+// row, a V unit two blocks of its V row; a cell holds kTpcK and kTpcV of them, a chunk kCh cells.
+// Loader threads take two V units and NIK K units (the last of them only for the first threads
+// when DK > DV) of every chunk; their count kNL is a whole number of waves when HW * DV / 64 is
+// a multiple of 4.
+template <int DK, int DV, int HW, int SV>
 struct Geo {
-    static constexpr int NB = D / 32;        // q8_0 / q4_0 blocks per row
-    static constexpr int NBV = NB / SV;      // V blocks per compute wave
-    static constexpr int U = NB / 2;         // units per head and cell
-    static constexpr int kTpc = HW * U;      // units per cell
-    static constexpr int kNC = 64 * HW * SV; // compute threads
-    static constexpr int kNL = kCh * kTpc / 2;  // loader threads
+    static constexpr int NBK = DK / 32;       // q8_0 blocks per K row
+    static constexpr int NBVT = DV / 32;      // q4_0 blocks per V row
+    static constexpr int NBV = NBVT / SV;     // V blocks per compute wave
+    static constexpr int UK = NBK / 2, UV = NBVT / 2;  // units per head and cell
+    static constexpr int kTpcK = HW * UK, kTpcV = HW * UV;  // units per cell
+    static constexpr int kNC = 64 * HW * SV;  // compute threads
+    static constexpr int kNL = kCh * kTpcV / 2;  // loader threads
+    static constexpr int kKU = kCh * kTpcK;   // K units per chunk
+    static constexpr int NIK = (kKU + kNL - 1) / kNL, NIKF = kKU / kNL;  // K units per loader thread (all, full)
     static constexpr int kThreads = kNC + kNL;
-    static_assert(D % 64 == 0 && kNL % 64 == 0, "loader threads must fill whole waves");
+    static_assert(DK % 64 == 0 && DV % 64 == 0 && kNL % 64 == 0 && NIK <= 3, "loader threads must fill whole waves");
     // LDS K stage: two planes (code bytes 0..15 and 16..31 of every q8_0 block), each with the
-    // block's 16 bytes at a slot of its cell (the first block of each unit in slots 0 .. kTpc-1,
-    // the second in kTpc .. 2kTpc-1), then d_K as [head][block][key]
-    static constexpr int kKc = 32 * kTpc + 16;    // K plane cell stride: 2 kTpc slots + 16 bytes
-    static constexpr int kKp = kCh * kKc;         // bytes of one K plane
-    static constexpr int kKh = 2 * NB * kCh + 16; // d_K bytes per head
-    static constexpr int kBk = 2 * kKp + HW * kKh;  // bytes of one LDS K stage
+    // block's 16 bytes at a slot of its cell (the first block of each unit in slots 0 .. kTpcK-1,
+    // the second in kTpcK .. 2kTpcK-1), then d_K as [head][block][key]
+    static constexpr int kKc = 32 * kTpcK + 16;    // K plane cell stride: 2 kTpcK slots + 16 bytes
+    static constexpr int kKp = kCh * kKc;          // bytes of one K plane
+    static constexpr int kKh = 2 * NBK * kCh + 16; // d_K bytes per head
+    static constexpr int kBk = 2 * kKp + HW * kKh; // bytes of one LDS K stage
     // LDS V stage: the 16 data bytes of every q4_0 block at a 16-byte slot of its cell (slots as
     // for K), cells kVc bytes apart plus 64 more from cell 16 on (the transposing reads of 8
     // keys then meet 8 distinct bank quads), followed by d_V as [head][block][P.V slot of the key]
-    static constexpr int kVc = 32 * kTpc + 16;    // V cell stride
-    static constexpr int kVd = kCh * kVc + 64;    // data bytes of a V stage
-    static constexpr int kVh = 2 * NB * kCh + 16; // d_V bytes per head
-    static constexpr int kBv = kVd + HW * kVh;    // bytes of one LDS V stage
+    static constexpr int kVc = 32 * kTpcV + 16;     // V cell stride
+    static constexpr int kVd = kCh * kVc + 64;      // data bytes of a V stage
+    static constexpr int kVh = 2 * NBVT * kCh + 16; // d_V bytes per head
+    static constexpr int kBv = kVd + HW * kVh;      // bytes of one LDS V stage
     // waves of all resident workgroups per SIMD that the register budget allows
-    static constexpr int kWavesPerEu = D >= 256 ? 2 : 3;
-    static_assert(NB % SV == 0, "V blocks split evenly");
+    static constexpr int kWavesPerEu = DK >= 256 ? 2 : 3;
+    static_assert(NBVT % SV == 0, "V blocks split evenly");
     // wide heads keep the Q.K accumulator inputs (one float4 per block and row) in LDS rather
-    // than in registers, and at head dim 512 the Q^T fragments (16 bytes per lane and block)
-    // too; both per head, written by the head's first wave
-    static constexpr bool kCinLds = NB > 4, kQLds = NB > 8;
-    static constexpr int kCin = kCinLds ? HW * NB * 16 * 16 : 16;  // LDS bytes of the inputs
-    static constexpr int kQf = kQLds ? HW * NB * 64 * 16 : 16;     // LDS bytes of the fragments
+    // than in registers, and from 512 on the Q^T fragments (16 bytes per lane and block) too;
+    // both per head, written by the head's first wave
+    static constexpr bool kCinLds = NBK > 4, kQLds = NBK > 8;
+    static constexpr int kCin = kCinLds ? HW * NBK * 16 * 16 : 16;  // LDS bytes of the inputs
+    static constexpr int kQf = kQLds ? HW * NBK * 64 * 16 : 16;     // LDS bytes of the fragments
 };
 
 // CAP: the logit soft-cap is on (a separate instantiation, so the plain path carries none of it).
 // The workgroup's first HW * SV waves compute (wave w: KV head g0 + w / SV, V blocks of part
-// w % SV); the remaining kNL threads
-// only load and stage the chunks (each two units of every chunk, two chunks in flight), so the
-// compute waves never wait for memory and hold no staging registers.
-template <int D, int HW, int SV, bool CAP>
-__global__ void __launch_bounds__((Geo<D, HW, SV>::kThreads))
-__attribute__((amdgpu_waves_per_eu((Geo<D, HW, SV>::kWavesPerEu)))) decode_mma_kernel(const SegParams p) {
-    using G = Geo<D, HW, SV>;
-    constexpr int NB = G::NB, NBV = G::NBV, U = G::U, kTpc = G::kTpc, kNC = G::kNC, kNL = G::kNL;
+// w % SV); the remaining kNL threads only load and stage the chunks (two chunks in flight), so
+// the compute waves never wait for memory and hold no staging registers.
+template <int DK, int DV, int HW, int SV, bool CAP>
+__global__ void __launch_bounds__((Geo<DK, DV, HW, SV>::kThreads))
+__attribute__((amdgpu_waves_per_eu((Geo<DK, DV, HW, SV>::kWavesPerEu)))) decode_mma_kernel(const SegParams p) {
+    using G = Geo<DK, DV, HW, SV>;
+    constexpr int NBK = G::NBK, NBV = G::NBV, UK = G::UK, UV = G::UV, kTpcK = G::kTpcK, kTpcV = G::kTpcV;
+    constexpr int kNC = G::kNC, kNL = G::kNL, NIK = G::NIK, NIKF = G::NIKF;
     constexpr int kKc = G::kKc, kKp = G::kKp, kKh = G::kKh, kBk = G::kBk;
     constexpr int kVc = G::kVc, kVd = G::kVd, kVh = G::kVh, kBv = G::kBv;
-    constexpr int kPs = 2 + D;  // partial row: M, S, VKQ[D]
+    constexpr int kPs = 2 + DV;  // partial row: M, S, VKQ[DV]
     static_assert(kCh == 32, "the key permutation of P.V assumes 32-key chunks");
     __shared__ __attribute__((aligned(16))) uint8_t s_k[2 * kBk];
     __shared__ __attribute__((aligned(16))) uint8_t s_v[2 * kBv];
@@ -160,42 +167,55 @@ __attribute__((amdgpu_waves_per_eu((Geo<D, HW, SV>::kWavesPerEu)))) decode_mma_k
     const uint8_t *kbase = p.k + (int64_t)(hgrp * HW) * p.k_s2;
     const uint8_t *vbase = p.v + (int64_t)(hgrp * HW) * p.v_s2;
 
-    // ---- chunk fetch (registers) and staging (LDS).  Unit t is cell t / kTpc, sub = t % kTpc:
-    // blocks 2 (sub % U) and + 1 of head sub / U from both caches, i.e. K bytes 68 sub .. 68 sub
-    // + 67 and V bytes 36 sub .. 36 sub + 35 of the cell (heads are packed in a cell, so
-    // consecutive units cover contiguous bytes).  Staging splits the scales from the block
-    // data and puts the data on 16-byte slots.  Cells past the segment end lie outside the
-    // buffer resource's range and read as zero.
-    struct Unit {
-        int gkb, gvb, lkb, lks, lvb, lvs;
+    // ---- chunk fetch (registers) and staging (LDS).  K unit t is cell t / kTpcK, sub = t %
+    // kTpcK: blocks 2 (sub % UK) and + 1 of head sub / UK, K bytes 68 sub .. 68 sub + 67 of the
+    // cell; V unit t likewise with kTpcV, UV and V bytes 36 sub .. 36 sub + 35 (heads are packed
+    // in a cell, so consecutive units cover contiguous bytes).  Staging splits the scales from
+    // the block data and puts the data on 16-byte slots.  Cells past the segment end lie outside
+    // the buffer resource's range and read as zero.
+    struct KUnit {
+        int gb, lb, ls;
     };
-    auto unit_of = [&](int t) __attribute__((always_inline)) {
-        const int fcell = t / kTpc, fsub = t % kTpc;
-        const int fh = fsub / U, fb = 2 * (fsub % U);  // head and first block of the unit
-        return Unit{fcell * (int)p.k_s1 + 68 * fsub, fcell * (int)p.v_s1 + 36 * fsub, fcell * kKc + 16 * fsub,
-                    2 * kKp + fh * kKh + fb * (2 * kCh) + 2 * fcell,
-                    fcell * kVc + 64 * ((fcell >> 4) & 1) + 16 * fsub,
-                    kVd + fh * kVh + fb * (2 * kCh) + 2 * (8 * ((fcell >> 2) & 3) + 4 * (fcell >> 4) + (fcell & 3))};
+    struct VUnit {
+        int gb, lb, ls;
     };
-    auto fetch = [&](Stage &st, int64_t c0, const Unit &u) __attribute__((always_inline)) {
-        const int gkb = u.gkb, gvb = u.gvb;
+    auto k_unit_of = [&](int t) __attribute__((always_inline)) {
+        const int fcell = t / kTpcK, fsub = t % kTpcK;
+        const int fh = fsub / UK, fb = 2 * (fsub % UK);  // head and first block of the unit
+        return KUnit{fcell * (int)p.k_s1 + 68 * fsub, fcell * kKc + 16 * fsub,
+                     2 * kKp + fh * kKh + fb * (2 * kCh) + 2 * fcell};
+    };
+    auto v_unit_of = [&](int t) __attribute__((always_inline)) {
+        const int fcell = t / kTpcV, fsub = t % kTpcV;
+        const int fh = fsub / UV, fb = 2 * (fsub % UV);
+        return VUnit{fcell * (int)p.v_s1 + 36 * fsub, fcell * kVc + 64 * ((fcell >> 4) & 1) + 16 * fsub,
+                     kVd + fh * kVh + fb * (2 * kCh) + 2 * (8 * ((fcell >> 2) & 3) + 4 * (fcell >> 4) + (fcell & 3))};
+    };
+    auto rsrc_k = [&](int64_t c0) __attribute__((always_inline)) {
         const int64_t nv = max((int64_t)0, min((int64_t)kCh, c_end - c0));
-        const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(kbase + c0 * p.k_s1), (short)0, (int)(nv * p.k_s1), 0x00020000);
-        const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(vbase + c0 * p.v_s1), (short)0, (int)(nv * p.v_s1), 0x00020000);
+        return __builtin_amdgcn_make_buffer_rsrc((void *)(kbase + c0 * p.k_s1), (short)0, (int)(nv * p.k_s1), 0x00020000);
+    };
+    auto rsrc_v = [&](int64_t c0) __attribute__((always_inline)) {
+        const int64_t nv = max((int64_t)0, min((int64_t)kCh, c_end - c0));
+        return __builtin_amdgcn_make_buffer_rsrc((void *)(vbase + c0 * p.v_s1), (short)0, (int)(nv * p.v_s1), 0x00020000);
+    };
+    auto fetch_k = [&](KStage &st, __amdgpu_buffer_rsrc_t rk, const KUnit &u) __attribute__((always_inline)) {
+        const int gkb = u.gb;
         st.ka0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, gkb, 0, 0));
         st.ka1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, gkb + 16, 0, 0));
         st.kx = __builtin_amdgcn_raw_buffer_load_b32(rk, gkb + 32, 0, 0);
         st.kb0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, gkb + 36, 0, 0));
         st.kb1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, gkb + 52, 0, 0));
+    };
+    auto fetch_v = [&](VStage &st, __amdgpu_buffer_rsrc_t rv, const VUnit &u) __attribute__((always_inline)) {
+        const int gvb = u.gb;
         st.va = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, gvb, 0, 0));
         st.vx = __builtin_amdgcn_raw_buffer_load_b32(rv, gvb + 16, 0, 0);
         st.vb = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, gvb + 20, 0, 0));
     };
-    auto stash = [&](const Stage &st, int buf, const Unit &u) __attribute__((always_inline)) {
-        const int lkb = u.lkb, lks = u.lks, lvb = u.lvb, lvs = u.lvs;
-        // K: words x0 .. x8 (bytes 0..35); the first block's codes start 2 bytes into them (its
+    auto stash_k = [&](const KStage &st, int buf, const KUnit &u) __attribute__((always_inline)) {
+        const int lkb = u.lb, lks = u.ls;
+        // words x0 .. x8 (bytes 0..35); the first block's codes start 2 bytes into them (its
         // scale is the low half of x0), the second block's scale is the high half of x8
         const uint32_t x[9] = {st.ka0.x, st.ka0.y, st.ka0.z, st.ka0.w, st.ka1.x, st.ka1.y, st.ka1.z, st.ka1.w, st.kx};
         uint32_t ca[8];
@@ -204,18 +224,21 @@ __attribute__((amdgpu_waves_per_eu((Geo<D, HW, SV>::kWavesPerEu)))) decode_mma_k
         uint8_t *kd = s_k + buf * kBk;
         *reinterpret_cast<uint4 *>(kd + lkb) = make_uint4(ca[0], ca[1], ca[2], ca[3]);
         *reinterpret_cast<uint4 *>(kd + kKp + lkb) = make_uint4(ca[4], ca[5], ca[6], ca[7]);
-        *reinterpret_cast<uint4 *>(kd + lkb + 16 * kTpc) = st.kb0;
-        *reinterpret_cast<uint4 *>(kd + kKp + lkb + 16 * kTpc) = st.kb1;
+        *reinterpret_cast<uint4 *>(kd + lkb + 16 * kTpcK) = st.kb0;
+        *reinterpret_cast<uint4 *>(kd + kKp + lkb + 16 * kTpcK) = st.kb1;
         *reinterpret_cast<uint16_t *>(kd + lks) = (uint16_t)x[0];
         *reinterpret_cast<uint16_t *>(kd + lks + 2 * kCh) = (uint16_t)(x[8] >> 16);
-        // V: the first block's data starts 2 bytes into va, vx (its scale is the low half of
-        // va.x, the second block's the high half of vx); the second block's data is vb
+    };
+    auto stash_v = [&](const VStage &st, int buf, const VUnit &u) __attribute__((always_inline)) {
+        const int lvb = u.lb, lvs = u.ls;
+        // the first block's data starts 2 bytes into va, vx (its scale is the low half of va.x,
+        // the second block's the high half of vx); the second block's data is vb
         uint8_t *vd = s_v + buf * kBv;
         *reinterpret_cast<uint4 *>(vd + lvb) = make_uint4(__builtin_amdgcn_alignbyte(st.va.y, st.va.x, 2),
                                                           __builtin_amdgcn_alignbyte(st.va.z, st.va.y, 2),
                                                           __builtin_amdgcn_alignbyte(st.va.w, st.va.z, 2),
                                                           __builtin_amdgcn_alignbyte(st.vx, st.va.w, 2));
-        *reinterpret_cast<uint4 *>(vd + lvb + 16 * kTpc) = st.vb;
+        *reinterpret_cast<uint4 *>(vd + lvb + 16 * kTpcV) = st.vb;
         *reinterpret_cast<uint16_t *>(vd + lvs) = (uint16_t)st.va.x;
         *reinterpret_cast<uint16_t *>(vd + lvs + 2 * kCh) = (uint16_t)(st.vx >> 16);
     };
@@ -227,29 +250,44 @@ __attribute__((amdgpu_waves_per_eu((Geo<D, HW, SV>::kWavesPerEu)))) decode_mma_k
     // stash; the compute waves meet them at every barrier until then.
     const int64_t n_ch = (c_end > c_beg) ? (c_end - c_beg + kCh - 1) / kCh : 0;
     if (loader) {
+        // loader thread lt: K units lt + i kNL (i < NIK; beyond NIKF only while inside the
+        // chunk's kKU units) and V units lt, lt + kNL
         const int lt = tid - kNC;
-        const Unit u0 = unit_of(lt), u1 = unit_of(lt + kNL);
-        Stage sa, sa1, sb, sb1;  // chunks 2i (sa, sa1) and 2i + 1 (sb, sb1), units u0 and u1
-        fetch(sa, c_beg, u0);
-        fetch(sa1, c_beg, u1);
-        fetch(sb, c_beg + kCh, u0);
-        fetch(sb1, c_beg + kCh, u1);
-        stash(sa, 0, u0);
-        stash(sa1, 0, u1);
-        fetch(sa, c_beg + 2 * kCh, u0);
-        fetch(sa1, c_beg + 2 * kCh, u1);
+        const bool k_last = lt + NIKF * kNL < G::kKU;  // this thread has a K unit at i = NIKF
+        KUnit ku[NIK];
+#pragma unroll
+        for (int i = 0; i < NIK; ++i) ku[i] = k_unit_of(min(lt + i * kNL, G::kKU - 1));
+        const VUnit v0 = v_unit_of(lt), v1 = v_unit_of(lt + kNL);
+        KStage ka[NIK], kb[NIK];  // chunks 2i (a) and 2i + 1 (b)
+        VStage va0, va1, vb0, vb1;
+        auto fetch_all = [&](KStage (&ks)[NIK], VStage &x0, VStage &x1, int64_t c0) __attribute__((always_inline)) {
+            const __amdgpu_buffer_rsrc_t rk = rsrc_k(c0), rv = rsrc_v(c0);
+#pragma unroll
+            for (int i = 0; i < NIK; ++i)
+                if (i < NIKF || k_last) fetch_k(ks[i], rk, ku[i]);
+            fetch_v(x0, rv, v0);
+            fetch_v(x1, rv, v1);
+        };
+        auto stash_all = [&](const KStage (&ks)[NIK], const VStage &x0, const VStage &x1, int buf)
+            __attribute__((always_inline)) {
+#pragma unroll
+            for (int i = 0; i < NIK; ++i)
+                if (i < NIKF || k_last) stash_k(ks[i], buf, ku[i]);
+            stash_v(x0, buf, v0);
+            stash_v(x1, buf, v1);
+        };
+        fetch_all(ka, va0, va1, c_beg);
+        fetch_all(kb, vb0, vb1, c_beg + kCh);
+        stash_all(ka, va0, va1, 0);
+        fetch_all(ka, va0, va1, c_beg + 2 * kCh);
         for (int64_t ch = 0; ch < n_ch; ch += 2) {
             __syncthreads();
-            stash(sb, 1, u0);
-            stash(sb1, 1, u1);
-            fetch(sb, c_beg + (ch + 3) * kCh, u0);
-            fetch(sb1, c_beg + (ch + 3) * kCh, u1);
+            stash_all(kb, vb0, vb1, 1);
+            fetch_all(kb, vb0, vb1, c_beg + (ch + 3) * kCh);
             if (ch + 1 >= n_ch) break;
             __syncthreads();
-            stash(sa, 0, u0);
-            stash(sa1, 0, u1);
-            fetch(sa, c_beg + (ch + 4) * kCh, u0);
-            fetch(sa1, c_beg + (ch + 4) * kCh, u1);
+            stash_all(ka, va0, va1, 0);
+            fetch_all(ka, va0, va1, c_beg + (ch + 4) * kCh);
         }
         return;
     }
@@ -283,20 +321,20 @@ __attribute__((amdgpu_waves_per_eu((Geo<D, HW, SV>::kWavesPerEu)))) decode_mma_k
     // accumulator inputs: -1152 * block sum of row `col` of Q, in registers or (wide heads) at
     // s_cin[wh][blk][col]; Q^T fragments in registers or (head dim 512) at s_q[wh][blk][lane].
     // The LDS copies are written before the first barrier and read once per block and chunk.
-    float4_t cneg[G::kCinLds ? 1 : NB];
-    half8_t qb[G::kQLds ? 1 : NB];
-    const int cin_off = 16 * (16 * NB * wh + col);
-    const int q_off = 16 * (64 * NB * wh + lane);
+    float4_t cneg[G::kCinLds ? 1 : NBK];
+    half8_t qb[G::kQLds ? 1 : NBK];
+    const int cin_off = 16 * (16 * NBK * wh + col);
+    const int q_off = 16 * (64 * NBK * wh + lane);
     {
         const bool ok = col < R;
         const int r = R0 + (ok ? col : 0);
         const _Float16 *qrow = p.q + (int64_t)(r / p.gqa) * p.q_s1 + (int64_t)(g * p.gqa + r % p.gqa) * p.q_s2 +
                                (int64_t)b * p.q_s3;
-        uint4 qv[NB];
+        uint4 qv[NBK];
 #pragma unroll
-        for (int blk = 0; blk < NB; ++blk) qv[blk] = *reinterpret_cast<const uint4 *>(qrow + 32 * blk + 8 * grp);
+        for (int blk = 0; blk < NBK; ++blk) qv[blk] = *reinterpret_cast<const uint4 *>(qrow + 32 * blk + 8 * grp);
 #pragma unroll
-        for (int blk = 0; blk < NB; ++blk) {
+        for (int blk = 0; blk < NBK; ++blk) {
             const half8_t qf = __builtin_bit_cast(half8_t, ok ? qv[blk] : make_uint4(0, 0, 0, 0));
             float sum = 0.f;
 #pragma unroll
@@ -329,9 +367,9 @@ __attribute__((amdgpu_waves_per_eu((Geo<D, HW, SV>::kWavesPerEu)))) decode_mma_k
         int2_t btr[NBV];
 #pragma unroll
         for (int j = 0; j < NBV; ++j) {
-            // block blk of head wh is slot U*wh + blk/2 (+ kTpc for odd blk) of a cell
+            // block blk of head wh is slot UV*wh + blk/2 (+ kTpcV for odd blk) of a cell
             const int blk = NBV * part + j;
-            const int vslot = U * wh + (blk >> 1) + kTpc * (blk & 1);
+            const int vslot = UV * wh + (blk >> 1) + kTpcV * (blk & 1);
             btr[j] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
                 (__attribute__((address_space(3))) int2_t *)(vs + vrd + 16 * vslot));
         }
@@ -339,16 +377,17 @@ __attribute__((amdgpu_waves_per_eu((Geo<D, HW, SV>::kWavesPerEu)))) decode_mma_k
         // ---- Q.K on the matrix cores: A = K (16 keys x 32 head_dim of one q8_0 block, codes as
         // binary16 1024 + (q + 128)), B = Q^T; d[ii] = score of key 16*kt + 4*grp + ii for row col
         // before the block scale
-        // Blocks go in groups of four (all of them at head dim 128), with a scheduling fence
-        // between groups, so at most eight accumulators of raw scores are live at once.
-        constexpr int kQg = NB < 4 ? NB : 4;
+        // Blocks go in groups of four (all of them at head dim 128; three at 576), with a
+        // scheduling fence between groups, so at most eight accumulators of raw scores are live.
+        constexpr int kQg = NBK <= 4 ? NBK : (NBK % 4 == 0 ? 4 : 3);
+        static_assert(NBK % kQg == 0, "Q.K block groups");
         float s[2][4];
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii) s[kt][ii] = 0.f;
 #pragma unroll
-        for (int b0 = 0; b0 < NB; b0 += kQg) {
+        for (int b0 = 0; b0 < NBK; b0 += kQg) {
             float4_t dq[2][kQg], cin[kQg];
             half8_t qin[kQg];
 #pragma unroll
@@ -369,7 +408,7 @@ __attribute__((amdgpu_waves_per_eu((Geo<D, HW, SV>::kWavesPerEu)))) decode_mma_k
 #pragma unroll
                 for (int j = 0; j < kQg; ++j) {
                     const int blk = b0 + j;
-                    const int kslot = U * wh + (blk >> 1) + kTpc * (blk & 1);
+                    const int kslot = UK * wh + (blk >> 1) + kTpcK * (blk & 1);
                     const uint2 w = *reinterpret_cast<const uint2 *>(kr + 16 * kslot);
                     const uint2 b0w = q8_biased(w.x), b1w = q8_biased(w.y);  // 1152 + q, exact
                     const uint4 ak = make_uint4(b0w.x, b0w.y, b1w.x, b1w.y);
@@ -391,7 +430,7 @@ __attribute__((amdgpu_waves_per_eu((Geo<D, HW, SV>::kWavesPerEu)))) decode_mma_k
                     s[kt][3] = fmaf((float)d23[1], dq[kt][j][3], s[kt][3]);
                 }
             }
-            if constexpr (NB > kQg) __builtin_amdgcn_sched_barrier(0);
+            if constexpr (NBK > kQg) __builtin_amdgcn_sched_barrier(0);
         }
 
         // the scores are complete here: without this pin the compiler defers the block sums
@@ -511,43 +550,48 @@ __attribute__((amdgpu_waves_per_eu((Geo<D, HW, SV>::kWavesPerEu)))) decode_mma_k
     }
 }
 
-// compute waves per head: two at head dim 512, where one wave's registers cannot hold the
-// output of all sixteen V blocks beside Q
-template <int D>
-constexpr int kSplitV = D >= 512 ? 2 : 1;
+// compute waves per head: two when dv = 512, where one wave's registers cannot hold the output
+// of all sixteen V blocks beside Q
+template <int DV>
+constexpr int kSplitV = DV >= 512 ? 2 : 1;
 
-template <int D, int HW, bool CAP>
+template <int DK, int DV, int HW, bool CAP>
 hipError_t launch_mma_c(const SegParams &p, hipStream_t s, int *occupancy) {
-    constexpr int SV = kSplitV<D>;
-    constexpr int kThreads = Geo<D, HW, SV>::kThreads;
+    constexpr int SV = kSplitV<DV>;
+    constexpr int kThreads = Geo<DK, DV, HW, SV>::kThreads;
     if (occupancy)
-        return hipOccupancyMaxActiveBlocksPerMultiprocessor(occupancy, decode_mma_kernel<D, HW, SV, CAP>, kThreads, 0);
+        return hipOccupancyMaxActiveBlocksPerMultiprocessor(occupancy, decode_mma_kernel<DK, DV, HW, SV, CAP>, kThreads,
+                                                            0);
     const int64_t blocks = (int64_t)p.n_splits * (p.n_head_kv / HW) * p.n_seq * decode_mma_row_groups(p);
     if (blocks > ((int64_t)1 << 31) - 1) return hipErrorInvalidValue;
-    launch_seg(decode_mma_kernel<D, HW, SV, CAP>, dim3((unsigned)blocks), dim3(kThreads), s, p);
+    launch_seg(decode_mma_kernel<DK, DV, HW, SV, CAP>, dim3((unsigned)blocks), dim3(kThreads), s, p);
     return hipGetLastError();
 }
 
-template <int D, int HW>
+template <int DK, int DV, int HW>
 hipError_t launch_mma(const SegParams &p, hipStream_t s, int *occupancy) {
-    return p.cap_l2 != 0.f ? launch_mma_c<D, HW, true>(p, s, occupancy) : launch_mma_c<D, HW, false>(p, s, occupancy);
+    return p.cap_l2 != 0.f ? launch_mma_c<DK, DV, HW, true>(p, s, occupancy)
+                           : launch_mma_c<DK, DV, HW, false>(p, s, occupancy);
 }
 
 }  // namespace
 
-// A group of hw KV heads at head dim d has an instantiation when its two LDS stages stay near
-// 110 KB (hw * d <= 1024) and its loader threads fill whole waves (hw * d / 64 a multiple of 4).
-static bool mma_group_ok(int d, int hw) {
-    if (d == 512) return hw == 1;  // one head and two workgroups per CU (Q in LDS)
-    return (d == 64 || d == 128 || d == 256) && (hw == 8 || hw == 4 || hw == 2 || hw == 1) && hw * d <= 1024 &&
-           (hw * d / 64) % 4 == 0;
+// A group of hw KV heads at head dims (dk, dv) has an instantiation when dk = dv, its two LDS
+// stages stay near 110 KB (hw * d <= 1024) and its loader threads fill whole waves (hw * d / 64
+// a multiple of 4); and for the 576 / 512 pair one head at a time.
+static bool mma_group_ok(int dk, int dv, int hw) {
+    if (dk == 576) return dv == 512 && hw == 1;
+    if (dk != dv) return false;
+    if (dk == 512) return hw == 1;  // one head and two workgroups per CU (Q in LDS)
+    return (dk == 64 || dk == 128 || dk == 256) && (hw == 8 || hw == 4 || hw == 2 || hw == 1) && hw * dk <= 1024 &&
+           (hw * dk / 64) % 4 == 0;
 }
 
 int decode_mma_row_groups(const SegParams &p) { return (int)(((int64_t)p.gqa * p.n_q + 15) / 16); }
 
-int decode_mma_heads(int d, int n_head_kv) {
+int decode_mma_heads(int dk, int dv, int n_head_kv) {
     for (int hw : {8, 4, 2, 1})
-        if (n_head_kv % hw == 0 && mma_group_ok(d, hw)) return hw;
+        if (n_head_kv % hw == 0 && mma_group_ok(dk, dv, hw)) return hw;
     return 0;
 }
 
@@ -555,21 +599,22 @@ bool decode_mma_ok(const SegParams &p) {
     // rows per KV head: up to 8 at head dim 128 (the decode contract there), any number at the
     // other head dims (row groups of 16)
     const int64_t R = (int64_t)p.gqa * p.n_q;
-    return p.d == p.dv && mma_group_ok(p.d, p.cell_hw) && R >= 1 && (p.d != kHeadDim || R <= kMaxRowsVec);
+    return mma_group_ok(p.d, p.dv, p.cell_hw) && R >= 1 && (p.d != kHeadDim || R <= kMaxRowsVec);
 }
 
 hipError_t launch_decode_mma(const SegParams &p, hipStream_t s, int *occupancy) {
     if (!decode_mma_ok(p)) return hipErrorInvalidValue;
+    if (p.d == 576) return launch_mma<576, 512, 1>(p, s, occupancy);
     switch (p.d * 16 + p.cell_hw) {
-        case 64 * 16 + 8: return launch_mma<64, 8>(p, s, occupancy);
-        case 64 * 16 + 4: return launch_mma<64, 4>(p, s, occupancy);
-        case 128 * 16 + 8: return launch_mma<128, 8>(p, s, occupancy);
-        case 128 * 16 + 4: return launch_mma<128, 4>(p, s, occupancy);
-        case 128 * 16 + 2: return launch_mma<128, 2>(p, s, occupancy);
-        case 256 * 16 + 4: return launch_mma<256, 4>(p, s, occupancy);
-        case 256 * 16 + 2: return launch_mma<256, 2>(p, s, occupancy);
-        case 256 * 16 + 1: return launch_mma<256, 1>(p, s, occupancy);
-        case 512 * 16 + 1: return launch_mma<512, 1>(p, s, occupancy);
+        case 64 * 16 + 8: return launch_mma<64, 64, 8>(p, s, occupancy);
+        case 64 * 16 + 4: return launch_mma<64, 64, 4>(p, s, occupancy);
+        case 128 * 16 + 8: return launch_mma<128, 128, 8>(p, s, occupancy);
+        case 128 * 16 + 4: return launch_mma<128, 128, 4>(p, s, occupancy);
+        case 128 * 16 + 2: return launch_mma<128, 128, 2>(p, s, occupancy);
+        case 256 * 16 + 4: return launch_mma<256, 256, 4>(p, s, occupancy);
+        case 256 * 16 + 2: return launch_mma<256, 256, 2>(p, s, occupancy);
+        case 256 * 16 + 1: return launch_mma<256, 256, 1>(p, s, occupancy);
+        case 512 * 16 + 1: return launch_mma<512, 512, 1>(p, s, occupancy);
         default: return hipErrorInvalidValue;
     }
 }

@@ -69,10 +69,10 @@ inline void launch_seg(F kernel, dim3 grid, dim3 block, hipStream_t s, const Seg
         hipLaunchKernelGGL(kernel, grid, block, 0, s, p, args...);
 }
 
-// KV heads per workgroup of the cell-major kernels for this head dim (dk = dv = d) and these
+// KV heads per workgroup of the cell-major kernels for these head dims (dk, dv) and these
 // types (0: no instantiation): a workgroup owns that many heads, packed inside each cell, over a
 // cell range.
-int cell_heads(int d, int k_type, int v_type, int n_head_kv, int R, bool rows);
+int cell_heads(int dk, int dv, int k_type, int v_type, int n_head_kv, int R, bool rows);
 // Resident workgroups per CU of the cell-major kernel selected by p.cell_hw (at least 1).
 int cell_blocks_per_cu(const SegParams &p, int k_type, int v_type);
 
@@ -81,11 +81,11 @@ int cell_blocks_per_cu(const SegParams &p, int k_type, int v_type);
 int decode_kernel_variant(const SegParams &p, int k_type, int v_type);
 hipError_t launch_decode_segment(const SegParams &p, int k_type, int v_type, hipStream_t s);
 // Matrix-core decode kernel for cell-major q8_0 K / q4_0 V at head dims 64, 128, 256 and 512
-// (dk = dv) with p.cell_hw KV heads per workgroup and up to 16 query rows per KV head per
+// (dk = dv) and 576 / 512 with p.cell_hw KV heads per workgroup and up to 16 query rows per KV head per
 // workgroup (more in row groups; at most 8 in all at head dim 128) (decode_mma_ok); with `occupancy` set it
 // reports resident workgroups per CU instead of launching.  decode_mma_heads gives the group
 // size it takes for n_head_kv heads at head dim d (0: none).
-int decode_mma_heads(int d, int n_head_kv);
+int decode_mma_heads(int dk, int dv, int n_head_kv);
 bool decode_mma_ok(const SegParams &p);
 // Row groups of 16 query rows per KV head (one workgroup each) of the cell-major decode launch.
 int decode_mma_row_groups(const SegParams &p);

@@ -319,16 +319,17 @@ struct Seg {
 
 // KV heads per workgroup of the cell-major kernel for this segment, or 0 when it does not
 // apply: every cell must hold the KV heads packed (head stride == row size), cell strides and
-// bases must be 16-byte aligned, and the types and head count must have an instantiation.
+// bases must be aligned (4 bytes for the q8_0 / q4_0 kernel, whose loads start on words; 16
+// for the others), and the types and head count must have an instantiation.
 int use_cell_kernel(const Seg &sg, const SegParams &p, int k_type, int v_type) {
-    if (p.d != p.dv) return 0;
     const int64_t rk = row_bytes(k_type, p.d), rv = row_bytes(v_type, p.dv);
-    const int hw = cell_heads(p.d, k_type, v_type, p.n_head_kv, p.gqa * p.n_q, p.rows != nullptr);
+    const int hw = cell_heads(p.d, p.dv, k_type, v_type, p.n_head_kv, p.gqa * p.n_q, p.rows != nullptr);
     if (hw == 0) return 0;
+    const int64_t al = (k_type == T_Q8_0 && v_type == T_Q4_0) ? 4 : 16;
     if (p.n_head_kv > 1 && (sg.k_s2 != rk || sg.v_s2 != rv)) return 0;
     if (sg.k_s1 < p.n_head_kv * rk || sg.v_s1 < p.n_head_kv * rv) return 0;
-    if ((sg.k_s1 | sg.v_s1) % 16 != 0) return 0;
-    if (((uintptr_t)sg.k | (uintptr_t)sg.v) % 16 != 0) return 0;
+    if ((sg.k_s1 | sg.v_s1) % al != 0) return 0;
+    if (((uintptr_t)sg.k | (uintptr_t)sg.v) % al != 0) return 0;
     // row lists: the cell-major kernel addresses the pool with 32-bit offsets
     const int64_t lim = (int64_t)1 << 31;
     if (p.rows && (p.n_pool * sg.k_s1 >= lim || p.n_pool * sg.v_s1 >= lim || sg.k_s1 >= (1 << 24) || sg.v_s1 >= (1 << 24)))
