@@ -139,7 +139,7 @@ class Runner:
         q = dev(w["q"])
         kp, vp = dev(w["k"]), dev(w["v"])
         kvr = dev(np.ascontiguousarray(w["kv_rows"] if rows is None else rows, dtype=np.int32))
-        m = w["mask"] if mask == "given" else mask
+        m = w["mask"] if isinstance(mask, str) and mask == "given" else mask
         mt = None if m is None else dev(np.asarray(m, dtype=np.float16))
         n_seq, n_head, n_q, _ = w["q"].shape
         n_kv = kvr.shape[1]
@@ -155,6 +155,6 @@ def oracle_rows(w, mask="given", rows=None, softcap=0.0):
     q = np.stack([oracle.q_values(w["q"][b]) for b in range(w["q"].shape[0])])
     k = oracle.kv_values(w["k_type"], w["k"])
     v = oracle.kv_values(w["v_type"], w["v"])
-    m = w["mask"] if mask == "given" else mask
+    m = w["mask"] if isinstance(mask, str) and mask == "given" else mask
     mm = None if m is None else np.asarray(m, dtype=np.float64)[:, 0]
     return oracle.attention_rows(q, k, v, w["kv_rows"] if rows is None else rows, w["scale"], mm, softcap)

@@ -11,7 +11,7 @@ import pytest
 
 import oracle
 import rkv_inputs as gen
-from rkv_testutil import Runner, assert_close, oracle_decode, step
+from rkv_testutil import Runner, assert_close, oracle_decode, oracle_rows, step
 
 pytestmark = pytest.mark.gpu
 
@@ -121,3 +121,47 @@ def test_full_size_128k_all_heads(run, d):
     gqa = w["n_head"] // w["n_head_kv"]
     for g, (Oref, Lref) in oracle_decode(w, heads=list(range(w["n_head_kv"]))).items():
         assert_close(O[:, g * gqa:(g + 1) * gqa], L[:, g * gqa:(g + 1) * gqa], Oref, Lref, what=f"d={d} head {g}")
+
+
+# row lists over a q8_0 / q4_0 pool (llama.cpp PR #29510, flash_attn_ext_rows): (d, n_head,
+# n_head_kv, n_q)
+ROW_LISTS = [(64, 32, 8, 1), (128, 32, 8, 1), (128, 16, 2, 1), (256, 16, 4, 2), (512, 16, 1, 1), (576, 40, 1, 1)]
+
+
+@pytest.mark.parametrize("d,n_head,n_head_kv,n_q", ROW_LISTS)
+def test_row_lists(run, d, n_head, n_head_kv, n_q):
+    """Four shuffled lists with -1 holes, entries past the pool and -1 padding at the end, the
+    lists' own mask; an entry past the pool reads nothing, so the oracle takes it as -1."""
+    w = gen.make_workload(4, scale_down=16, d=d, dv=512 if d == 576 else d, n_head=n_head, n_head_kv=n_head_kv,
+                          n_q=n_q, k_type=gen.TYPE_Q8_0, v_type=gen.TYPE_Q4_0)  # pool 4096, lists <= 1920
+    rng = np.random.default_rng(d + n_head)
+    rows = w["kv_rows"].copy()
+    for b in range(rows.shape[0]):
+        n = int((rows[b] >= 0).sum())
+        rows[b, :n] = rows[b, :n][rng.permutation(n)]
+        rows[b, rng.choice(n, size=n // 10, replace=False)] = -1
+        rows[b, rng.choice(n, size=3, replace=False)] = w["n_pool"] + 7
+    mask = np.where(rng.random((rows.shape[0], 1, n_q, rows.shape[1])) < 0.1, -np.inf, 0.0).astype(np.float16)
+    step(f"mma rows d={d} heads {n_head}/{n_head_kv} n_q {n_q}: holes, entries past the pool")
+    O, L = run.rows(w, mask=mask, rows=rows)
+    assert run.ctx.stats()["kernel_variant"] == MMA
+    Oref, Lref = oracle_rows(w, mask=mask, rows=np.where(rows < w["n_pool"], rows, -1))
+    assert_close(O, L, Oref, Lref, what=f"mma rows d={d}")
+
+
+@pytest.mark.parametrize("d", [128, 256])
+def test_row_lists_softcap_and_empty_list(run, d):
+    """Soft-cap over a q8_0 / q4_0 pool; one sequence's list is all padding (O = 0, LSE = -inf)."""
+    w = gen.make_workload(4, scale_down=16, d=d, n_head=32, n_head_kv=8, k_type=gen.TYPE_Q8_0, v_type=gen.TYPE_Q4_0)
+    rows = w["kv_rows"].copy()
+    rows[2, :] = -1
+    run.ctx.set_softcap(25.0)
+    try:
+        step(f"mma rows d={d}: soft-cap 25, an empty list")
+        O, L = run.rows(w, mask=None, rows=rows)
+        assert run.ctx.stats()["kernel_variant"] == MMA
+    finally:
+        run.ctx.set_softcap(0.0)
+    Oref, Lref = oracle_rows(w, mask=None, rows=rows, softcap=25.0)
+    assert_close(O, L, Oref, Lref, what=f"mma rows softcap d={d}")
+    assert np.all(O[2] == 0) and np.all(L[2] == -np.inf)

@@ -125,11 +125,16 @@ struct Geo {
     static constexpr int kQf = kQLds ? HW * NBK * 64 * 16 : 16;     // LDS bytes of the fragments
 };
 
-// CAP: the logit soft-cap is on (a separate instantiation, so the plain path carries none of it).
+// Kernel modes: a segment without a mask, a segment with one, a row list (with or without).
+enum : int { kModePlain = 0, kModeMask = 1, kModeRows = 2 };
+
+// CAP: the logit soft-cap is on; MODE: the chunk cells are segment cells or row-list entries
+// naming pool rows, and with a mask the compute waves fetch each chunk's mask values ahead of
+// its Q.K (separate instantiations, so the plain path carries none of it).
 // The workgroup's first HW * SV waves compute (wave w: KV head g0 + w / SV, V blocks of part
 // w % SV); the remaining kNL threads only load and stage the chunks (two chunks in flight), so
 // the compute waves never wait for memory and hold no staging registers.
-template <int DK, int DV, int HW, int SV, bool CAP>
+template <int DK, int DV, int HW, int SV, bool CAP, int MODE>
 __global__ void __launch_bounds__((Geo<DK, DV, HW, SV>::kThreads))
 __attribute__((amdgpu_waves_per_eu((Geo<DK, DV, HW, SV>::kWavesPerEu)))) decode_mma_kernel(const SegParams p) {
     using G = Geo<DK, DV, HW, SV>;
@@ -138,11 +143,13 @@ __attribute__((amdgpu_waves_per_eu((Geo<DK, DV, HW, SV>::kWavesPerEu)))) decode_
     constexpr int kKc = G::kKc, kKp = G::kKp, kKh = G::kKh, kBk = G::kBk;
     constexpr int kVc = G::kVc, kVd = G::kVd, kVh = G::kVh, kBv = G::kBv;
     constexpr int kPs = 2 + DV;  // partial row: M, S, VKQ[DV]
+    constexpr bool ROWS = MODE == kModeRows, MSK = MODE != kModePlain;
     static_assert(kCh == 32, "the key permutation of P.V assumes 32-key chunks");
     __shared__ __attribute__((aligned(16))) uint8_t s_k[2 * kBk];
     __shared__ __attribute__((aligned(16))) uint8_t s_v[2 * kBv];
     __shared__ __attribute__((aligned(16))) uint8_t s_cin[G::kCin];
     __shared__ __attribute__((aligned(16))) uint8_t s_q[G::kQf];
+    __shared__ __attribute__((aligned(16))) int s_ok[2][ROWS ? kCh : 4];  // row lists: cell j of the stage is a key
 
     const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int col = lane & 15, grp = lane >> 4;
@@ -162,10 +169,27 @@ __attribute__((amdgpu_waves_per_eu((Geo<DK, DV, HW, SV>::kWavesPerEu)))) decode_
     const bool loader = tid >= kNC;
     const int wh = loader ? 0 : wave / SV, part = loader ? 0 : wave % SV;  // head in the group, V part
     const int g = hgrp * HW + wh;  // this compute wave's KV head
-    const int64_t c_beg = (int64_t)split * p.cells_per_split;
-    const int64_t c_end = min(p.n_cells, c_beg + (int64_t)p.cells_per_split);
+    int64_t c_beg = (int64_t)split * p.cells_per_split;
+    int64_t c_end = min(p.n_cells, c_beg + (int64_t)p.cells_per_split);
+    if constexpr (ROWS) {
+        // a list ends at its extent (1 + its last pool row, from a scan before the launch): the
+        // splits share the entries up to it evenly, in whole chunks, and the padding after it
+        // is not walked
+        if (p.row_extent) {
+            int e = 0;
+#pragma unroll
+            for (int q = 0; q < kRowExtentParts; ++q) e = max(e, p.row_extent[b * kRowExtentParts + q]);
+            const int64_t ext = min(p.n_cells, (int64_t)e);
+            const int64_t per = ((ext + p.n_splits - 1) / p.n_splits + kCh - 1) / kCh * kCh;
+            c_beg = (int64_t)split * per;
+            c_end = min(ext, c_beg + per);
+        }
+    }
     const uint8_t *kbase = p.k + (int64_t)(hgrp * HW) * p.k_s2;
     const uint8_t *vbase = p.v + (int64_t)(hgrp * HW) * p.v_s2;
+    // row lists: chunk cells are list entries of sequence b, each naming a pool row (a negative
+    // entry, or one outside the pool, is no key)
+    const int32_t *rlist = ROWS ? p.rows + (int64_t)b * p.rows_s : nullptr;
 
     // ---- chunk fetch (registers) and staging (LDS).  K unit t is cell t / kTpcK, sub = t %
     // kTpcK: blocks 2 (sub % UK) and + 1 of head sub / UK, K bytes 68 sub .. 68 sub + 67 of the
@@ -173,42 +197,56 @@ __attribute__((amdgpu_waves_per_eu((Geo<DK, DV, HW, SV>::kWavesPerEu)))) decode_
     // in a cell, so consecutive units cover contiguous bytes).  Staging splits the scales from
     // the block data and puts the data on 16-byte slots.  Cells past the segment end lie outside
     // the buffer resource's range and read as zero.
+    // A unit's global offset is gb within its chunk (cell-major segment), or sub plus its pool
+    // row times the row stride (row list); cell is its cell in the chunk.
     struct KUnit {
-        int gb, lb, ls;
+        int gb, lb, ls, cell, sub;
     };
     struct VUnit {
-        int gb, lb, ls;
+        int gb, lb, ls, cell, sub;
     };
     auto k_unit_of = [&](int t) __attribute__((always_inline)) {
         const int fcell = t / kTpcK, fsub = t % kTpcK;
         const int fh = fsub / UK, fb = 2 * (fsub % UK);  // head and first block of the unit
         return KUnit{fcell * (int)p.k_s1 + 68 * fsub, fcell * kKc + 16 * fsub,
-                     2 * kKp + fh * kKh + fb * (2 * kCh) + 2 * fcell};
+                     2 * kKp + fh * kKh + fb * (2 * kCh) + 2 * fcell, fcell, 68 * fsub};
     };
     auto v_unit_of = [&](int t) __attribute__((always_inline)) {
         const int fcell = t / kTpcV, fsub = t % kTpcV;
         const int fh = fsub / UV, fb = 2 * (fsub % UV);
         return VUnit{fcell * (int)p.v_s1 + 36 * fsub, fcell * kVc + 64 * ((fcell >> 4) & 1) + 16 * fsub,
-                     kVd + fh * kVh + fb * (2 * kCh) + 2 * (8 * ((fcell >> 2) & 3) + 4 * (fcell >> 4) + (fcell & 3))};
+                     kVd + fh * kVh + fb * (2 * kCh) + 2 * (8 * ((fcell >> 2) & 3) + 4 * (fcell >> 4) + (fcell & 3)),
+                     fcell, 36 * fsub};
     };
+    // buffer resources: the chunk's cells (segment) or the whole pool (row list)
     auto rsrc_k = [&](int64_t c0) __attribute__((always_inline)) {
         const int64_t nv = max((int64_t)0, min((int64_t)kCh, c_end - c0));
-        return __builtin_amdgcn_make_buffer_rsrc((void *)(kbase + c0 * p.k_s1), (short)0, (int)(nv * p.k_s1), 0x00020000);
+        return ROWS ? __builtin_amdgcn_make_buffer_rsrc((void *)kbase, (short)0, (int)(p.n_pool * p.k_s1), 0x00020000)
+                     : __builtin_amdgcn_make_buffer_rsrc((void *)(kbase + c0 * p.k_s1), (short)0, (int)(nv * p.k_s1),
+                                                         0x00020000);
     };
     auto rsrc_v = [&](int64_t c0) __attribute__((always_inline)) {
         const int64_t nv = max((int64_t)0, min((int64_t)kCh, c_end - c0));
-        return __builtin_amdgcn_make_buffer_rsrc((void *)(vbase + c0 * p.v_s1), (short)0, (int)(nv * p.v_s1), 0x00020000);
+        return ROWS ? __builtin_amdgcn_make_buffer_rsrc((void *)vbase, (short)0, (int)(p.n_pool * p.v_s1), 0x00020000)
+                     : __builtin_amdgcn_make_buffer_rsrc((void *)(vbase + c0 * p.v_s1), (short)0, (int)(nv * p.v_s1),
+                                                         0x00020000);
     };
-    auto fetch_k = [&](KStage &st, __amdgpu_buffer_rsrc_t rk, const KUnit &u) __attribute__((always_inline)) {
-        const int gkb = u.gb;
+    // row lists: the pool row of cell `cell` of the chunk at c0, or -1 (no key: a negative entry,
+    // one outside the pool, or a cell past the segment)
+    auto pool_row = [&](int64_t c0, int cell) __attribute__((always_inline)) {
+        const int64_t c = c0 + cell;
+        const int r = c < c_end ? rlist[c] : -1;
+        return (r >= 0 && (int64_t)r < p.n_pool) ? r : -1;
+    };
+    constexpr uint32_t kNowhere = 0x80000000u;  // a buffer offset past every range: reads zero
+    auto fetch_k = [&](KStage &st, __amdgpu_buffer_rsrc_t rk, int gkb) __attribute__((always_inline)) {
         st.ka0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, gkb, 0, 0));
         st.ka1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, gkb + 16, 0, 0));
         st.kx = __builtin_amdgcn_raw_buffer_load_b32(rk, gkb + 32, 0, 0);
         st.kb0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, gkb + 36, 0, 0));
         st.kb1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, gkb + 52, 0, 0));
     };
-    auto fetch_v = [&](VStage &st, __amdgpu_buffer_rsrc_t rv, const VUnit &u) __attribute__((always_inline)) {
-        const int gvb = u.gb;
+    auto fetch_v = [&](VStage &st, __amdgpu_buffer_rsrc_t rv, int gvb) __attribute__((always_inline)) {
         st.va = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, gvb, 0, 0));
         st.vx = __builtin_amdgcn_raw_buffer_load_b32(rv, gvb + 16, 0, 0);
         st.vb = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, gvb + 20, 0, 0));
@@ -260,13 +298,44 @@ __attribute__((amdgpu_waves_per_eu((Geo<DK, DV, HW, SV>::kWavesPerEu)))) decode_
         const VUnit v0 = v_unit_of(lt), v1 = v_unit_of(lt + kNL);
         KStage ka[NIK], kb[NIK];  // chunks 2i (a) and 2i + 1 (b)
         VStage va0, va1, vb0, vb1;
-        auto fetch_all = [&](KStage (&ks)[NIK], VStage &x0, VStage &x1, int64_t c0) __attribute__((always_inline)) {
-            const __amdgpu_buffer_rsrc_t rk = rsrc_k(c0), rv = rsrc_v(c0);
+        // row lists: pool rows of the units' cells for the next fetch of each register set,
+        // read one fetch ahead
+        int rka[ROWS ? NIK : 1], rkb[ROWS ? NIK : 1], rva[2], rvb[2];
+        auto rows_for = [&](int (&rk)[ROWS ? NIK : 1], int (&rv)[2], int64_t c0) __attribute__((always_inline)) {
 #pragma unroll
-            for (int i = 0; i < NIK; ++i)
-                if (i < NIKF || k_last) fetch_k(ks[i], rk, ku[i]);
-            fetch_v(x0, rv, v0);
-            fetch_v(x1, rv, v1);
+            for (int i = 0; i < NIK; ++i) rk[i] = pool_row(c0, ku[i].cell);
+            rv[0] = pool_row(c0, v0.cell);
+            rv[1] = pool_row(c0, v1.cell);
+        };
+        auto fetch_all = [&](KStage (&ks)[NIK], VStage &x0, VStage &x1, int (&rk)[ROWS ? NIK : 1], int (&rv)[2], int64_t c0)
+            __attribute__((always_inline)) {
+            const __amdgpu_buffer_rsrc_t rsk = rsrc_k(c0), rsv = rsrc_v(c0);
+            if constexpr (ROWS) {
+#pragma unroll
+                for (int i = 0; i < NIK; ++i)
+                    if (i < NIKF || k_last)
+                        fetch_k(ks[i], rsk, rk[i] >= 0 ? rk[i] * (int)p.k_s1 + ku[i].sub : (int)kNowhere);
+                fetch_v(x0, rsv, rv[0] >= 0 ? rv[0] * (int)p.v_s1 + v0.sub : (int)kNowhere);
+                fetch_v(x1, rsv, rv[1] >= 0 ? rv[1] * (int)p.v_s1 + v1.sub : (int)kNowhere);
+                rows_for(rk, rv, c0 + 2 * kCh);  // this set's next fetch
+            } else {
+#pragma unroll
+                for (int i = 0; i < NIK; ++i)
+                    if (i < NIKF || k_last) fetch_k(ks[i], rsk, ku[i].gb);
+                fetch_v(x0, rsv, v0.gb);
+                fetch_v(x1, rsv, v1.gb);
+            }
+        };
+        // row lists: whether each cell of the chunk at c0 is a key, for the compute waves (the
+        // thread holding the cell's first K unit writes it)
+        auto stash_ok = [&](int buf, int64_t c0) __attribute__((always_inline)) {
+            if constexpr (ROWS) {
+#pragma unroll
+                for (int i = 0; i < NIK; ++i) {
+                    const int t = lt + i * kNL;
+                    if (t < G::kKU && t % kTpcK == 0) s_ok[buf][ku[i].cell] = pool_row(c0, ku[i].cell) >= 0;
+                }
+            }
         };
         auto stash_all = [&](const KStage (&ks)[NIK], const VStage &x0, const VStage &x1, int buf)
             __attribute__((always_inline)) {
@@ -276,18 +345,25 @@ __attribute__((amdgpu_waves_per_eu((Geo<DK, DV, HW, SV>::kWavesPerEu)))) decode_
             stash_v(x0, buf, v0);
             stash_v(x1, buf, v1);
         };
-        fetch_all(ka, va0, va1, c_beg);
-        fetch_all(kb, vb0, vb1, c_beg + kCh);
+        if constexpr (ROWS) {
+            rows_for(rka, rva, c_beg);
+            rows_for(rkb, rvb, c_beg + kCh);
+        }
+        fetch_all(ka, va0, va1, rka, rva, c_beg);
+        fetch_all(kb, vb0, vb1, rkb, rvb, c_beg + kCh);
         stash_all(ka, va0, va1, 0);
-        fetch_all(ka, va0, va1, c_beg + 2 * kCh);
+        stash_ok(0, c_beg);
+        fetch_all(ka, va0, va1, rka, rva, c_beg + 2 * kCh);
         for (int64_t ch = 0; ch < n_ch; ch += 2) {
             __syncthreads();
             stash_all(kb, vb0, vb1, 1);
-            fetch_all(kb, vb0, vb1, c_beg + (ch + 3) * kCh);
+            stash_ok(1, c_beg + (ch + 1) * kCh);
+            fetch_all(kb, vb0, vb1, rkb, rvb, c_beg + (ch + 3) * kCh);
             if (ch + 1 >= n_ch) break;
             __syncthreads();
             stash_all(ka, va0, va1, 0);
-            fetch_all(ka, va0, va1, c_beg + (ch + 4) * kCh);
+            stash_ok(0, c_beg + (ch + 2) * kCh);
+            fetch_all(ka, va0, va1, rka, rva, c_beg + (ch + 4) * kCh);
         }
         return;
     }
@@ -362,6 +438,21 @@ __attribute__((amdgpu_waves_per_eu((Geo<DK, DV, HW, SV>::kWavesPerEu)))) decode_
         // (d_V is staged in P.V slot order: the key of slot 8*gg + jj is 4*gg + jj (jj < 4) or
         // 16 + 4*gg + jj - 4.)
 
+        // the mask values of the lane's keys (keys past the segment end read its last one and
+        // are hidden below) are fetched first, pinned here so that their latency overlaps Q.K
+        float mpre[2][4];
+        if constexpr (MSK) {
+            if (p.mask) {
+                const _Float16 *mr = p.mask + p.pos0 + (int64_t)b * p.m_s3 + (int64_t)qi_row * p.m_s1;
+#pragma unroll
+                for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                    for (int ii = 0; ii < 4; ++ii) {
+                        mpre[kt][ii] = (float)mr[min(c0 + 16 * kt + 4 * grp + ii, c_end - 1)];
+                        asm volatile("" : "+v"(mpre[kt][ii]));
+                    }
+            }
+        }
         // the V^T bytes (one transposing read per block) are read first: their latency then
         // overlaps Q.K and the softmax
         int2_t btr[NBV];
@@ -440,7 +531,7 @@ __attribute__((amdgpu_waves_per_eu((Geo<DK, DV, HW, SV>::kWavesPerEu)))) decode_
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii) asm volatile("" : "+v"(s[kt][ii]));
         // ---- visibility: whole chunk visible, or per element (chunk end, causal rule, mask)
-        const bool full = (c0 + kCh <= c_end) && !p.mask && (p.q_pos0 < 0 || p.pos0 + c0 + kCh - 1 <= p.q_pos0);
+        const bool full = !ROWS && (c0 + kCh <= c_end) && !p.mask && (p.q_pos0 < 0 || p.pos0 + c0 + kCh - 1 <= p.q_pos0);
         float cc = c;
         if (CAP && full) {
             // every key visible: only the soft-cap
@@ -455,15 +546,18 @@ __attribute__((amdgpu_waves_per_eu((Geo<DK, DV, HW, SV>::kWavesPerEu)))) decode_
             const int n_in = (int)min((int64_t)kCh, c_end - c0);
             const int lim = p.q_pos0 < 0 ? kCh
                                          : (int)max((int64_t)-1, min((int64_t)kCh, p.q_pos0 + qi_row - p.pos0 - c0));
-            const _Float16 *mr = p.mask ? p.mask + p.pos0 + (int64_t)b * p.m_s3 + (int64_t)qi_row * p.m_s1 : nullptr;
+            // row lists: the loaders' flags of the lane's keys
+            const int4 ok0 = ROWS ? *reinterpret_cast<const int4 *>(&s_ok[buf][4 * grp]) : make_int4(1, 1, 1, 1);
+            const int4 ok1 = ROWS ? *reinterpret_cast<const int4 *>(&s_ok[buf][16 + 4 * grp]) : make_int4(1, 1, 1, 1);
+            const int okk[2][4] = {{ok0.x, ok0.y, ok0.z, ok0.w}, {ok1.x, ok1.y, ok1.z, ok1.w}};
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
                 for (int ii = 0; ii < 4; ++ii) {
                     const int kr = 16 * kt + 4 * grp + ii;
-                    const bool vis = kr < n_in && kr <= lim;
+                    const bool vis = kr < n_in && kr <= lim && okk[kt][ii] != 0;
                     float x = CAP ? softcap_log2(s[kt][ii], p.cap_cs, p.cap_l2) : s[kt][ii] * c;
-                    if (mr) x = fmaf((float)mr[min(c0 + kr, c_end - 1)], kLog2e, x);
+                    if (MSK && p.mask) x = fmaf(mpre[kt][ii], kLog2e, x);
                     s[kt][ii] = vis ? x : -INFINITY;
                 }
             }
@@ -555,23 +649,29 @@ __attribute__((amdgpu_waves_per_eu((Geo<DK, DV, HW, SV>::kWavesPerEu)))) decode_
 template <int DV>
 constexpr int kSplitV = DV >= 512 ? 2 : 1;
 
-template <int DK, int DV, int HW, bool CAP>
+template <int DK, int DV, int HW, bool CAP, int MODE>
 hipError_t launch_mma_c(const SegParams &p, hipStream_t s, int *occupancy) {
     constexpr int SV = kSplitV<DV>;
     constexpr int kThreads = Geo<DK, DV, HW, SV>::kThreads;
     if (occupancy)
-        return hipOccupancyMaxActiveBlocksPerMultiprocessor(occupancy, decode_mma_kernel<DK, DV, HW, SV, CAP>, kThreads,
-                                                            0);
+        return hipOccupancyMaxActiveBlocksPerMultiprocessor(occupancy, decode_mma_kernel<DK, DV, HW, SV, CAP, MODE>,
+                                                            kThreads, 0);
     const int64_t blocks = (int64_t)p.n_splits * (p.n_head_kv / HW) * p.n_seq * decode_mma_row_groups(p);
     if (blocks > ((int64_t)1 << 31) - 1) return hipErrorInvalidValue;
-    launch_seg(decode_mma_kernel<DK, DV, HW, SV, CAP>, dim3((unsigned)blocks), dim3(kThreads), s, p);
+    launch_seg(decode_mma_kernel<DK, DV, HW, SV, CAP, MODE>, dim3((unsigned)blocks), dim3(kThreads), s, p);
     return hipGetLastError();
 }
 
 template <int DK, int DV, int HW>
 hipError_t launch_mma(const SegParams &p, hipStream_t s, int *occupancy) {
-    return p.cap_l2 != 0.f ? launch_mma_c<DK, DV, HW, true>(p, s, occupancy)
-                           : launch_mma_c<DK, DV, HW, false>(p, s, occupancy);
+    if (p.rows)
+        return p.cap_l2 != 0.f ? launch_mma_c<DK, DV, HW, true, kModeRows>(p, s, occupancy)
+                               : launch_mma_c<DK, DV, HW, false, kModeRows>(p, s, occupancy);
+    if (p.mask)
+        return p.cap_l2 != 0.f ? launch_mma_c<DK, DV, HW, true, kModeMask>(p, s, occupancy)
+                               : launch_mma_c<DK, DV, HW, false, kModeMask>(p, s, occupancy);
+    return p.cap_l2 != 0.f ? launch_mma_c<DK, DV, HW, true, kModePlain>(p, s, occupancy)
+                           : launch_mma_c<DK, DV, HW, false, kModePlain>(p, s, occupancy);
 }
 
 }  // namespace

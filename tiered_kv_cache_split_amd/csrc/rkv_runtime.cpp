@@ -1271,21 +1271,25 @@ int rkv_attn_rows(rkv_ctx *ctx, const rkv_tensor *q, const rkv_tensor *k_pool, c
     pk.cell_hw = plan.cell_hw;
     MergeRange mr{};
     bool ranged = false;
-    if (n_kv > 0 && decode_kernel_persistent(pk, k_pool->type, v_pool->type)) {
-        // the persistent kernel counts each list up to its last pool row, and reports which
-        // slots hold each pair's partials, so that the merge reads only those
+    const bool persistent = n_kv > 0 && decode_kernel_persistent(pk, k_pool->type, v_pool->type);
+    if (n_kv > 0 && pk.cell_hw > 0) {
+        // the cell-major kernels walk each list up to its last pool row only
         void *buf = ctx->row_extent;
         st = grow(&buf, &ctx->row_extent_cap, std::max<size_t>(1024, (size_t)n_seq) * kRowExtentParts * sizeof(int32_t),
                   stream);
         ctx->row_extent = static_cast<int32_t *>(buf);
         if (st) return st;
-        buf = ctx->pair_range;
-        st = grow(&buf, &ctx->pair_range_cap, 1024 * sizeof(int2), stream);
-        ctx->pair_range = static_cast<int2 *>(buf);
-        if (st) return st;
         hipError_t e1 = launch_row_extent(kv_rows, n_kv, n_kv, (int)n_seq, ctx->row_extent, stream);
         if (e1 != hipSuccess) return hip_fail(e1, "row extent launch");
         p.row_extent = ctx->row_extent;
+    }
+    if (persistent) {
+        // the persistent kernel reports which slots hold each pair's partials, so that the merge
+        // reads only those
+        void *buf = ctx->pair_range;
+        st = grow(&buf, &ctx->pair_range_cap, 1024 * sizeof(int2), stream);
+        ctx->pair_range = static_cast<int2 *>(buf);
+        if (st) return st;
         p.pair_range = ctx->pair_range;
         mr = MergeRange{ctx->pair_range, (int)n_head, (int)(gqa * plan.cell_hw), (int)(n_head_kv / plan.cell_hw),
                         n_head * n_q};
