@@ -250,9 +250,11 @@ int rkv_attn_prefill(rkv_ctx *ctx, const rkv_tensor *q,
  *           128 (other head dims as for rkv_attn_decode, any number of rows).
  *   k_pool  [128, n_pool, n_head_kv, 1] device, shared by all sequences; v_pool likewise.
  *   kv_rows int32 [n_kv, n_seq] device, contiguous: key j of sequence b is pool row
- *           kv_rows[j + n_kv*b].  A negative row is padding: it contributes nothing and is
- *           never dereferenced.  Rows >= n_pool are a contract violation (not checked on
- *           the device).
+ *           kv_rows[j + n_kv*b].  A negative row, or one >= n_pool, is padding: it
+ *           contributes nothing and is never dereferenced.  Cell-major q8_0 K / q4_0 V pools
+ *           run on the matrix-core decode kernel at every supported head dim, binary16 pools
+ *           of groups of 8 KV heads at head dim 128 on the persistent binary16 kernel, the rest
+ *           on the vector kernels.
  *   mask    F16 [>= n_kv, >= n_q, 1, n_seq] additive, device, or NULL.
  *   o       float32 [128, n_head, n_q, n_seq]; lse float32 [n_head, n_q, n_seq] or NULL. */
 int rkv_attn_rows(rkv_ctx *ctx, const rkv_tensor *q, const rkv_tensor *k_pool,

@@ -162,3 +162,29 @@ def test_rows_full_size_config4_all_heads(run):
         Oref, Lref = oracle.attention_rows(q, k, v, w["kv_rows"], w["scale"], mm)
         assert_close(O[:, :, g * gqa:(g + 1) * gqa], L[:, :, g * gqa:(g + 1) * gqa], Oref, Lref,
                      what=f"rows full size head group {g}")
+
+
+@pytest.mark.parametrize("n_head,n_head_kv,kt,vt,variant", [
+    (8, 4, gen.TYPE_F16, gen.TYPE_F16, 0),      # per-head vector kernel
+    (32, 8, gen.TYPE_F16, gen.TYPE_F16, 4),     # persistent binary16 matrix-core kernel
+    (16, 4, gen.TYPE_Q8_0, gen.TYPE_F16, 0),    # per-head vector kernel, q8_0 K
+    (32, 8, gen.TYPE_Q8_0, gen.TYPE_Q4_0, 3),   # matrix-core q8_0 / q4_0 kernel
+])
+def test_rows_entries_outside_the_pool(run, n_head, n_head_kv, kt, vt, variant):
+    """List entries >= n_pool are padding on every kernel: nothing is read and the key does not
+    count, so the result equals the oracle's for the same list with those entries set to -1."""
+    rng = gen.rng_for(61)
+    n_pool = 1800
+    q = gen.draw_normal(rng, (2, n_head, 1, 128)).astype(np.float16)
+    k = gen.pack(kt, gen.draw_normal(rng, (n_pool, n_head_kv, 128)))
+    v = gen.pack(vt, gen.draw_normal(rng, (n_pool, n_head_kv, 128)))
+    rows = gen.rows_lists(rng, n_pool, (1000, 700), 1000, shuffle=True)
+    bad = (rng.random(rows.shape) < 0.05) & (rows >= 0)
+    rows[bad] = n_pool + rng.integers(0, 1 << 20, int(bad.sum()))
+    w = dict(q=q, k=k, v=v, kv_rows=rows, mask=None, k_type=kt, v_type=vt, n_head=n_head,
+             n_head_kv=n_head_kv, scale=1 / np.sqrt(128))
+    step(f"rows with entries past the pool: {n_head}/{n_head_kv} types {kt}/{vt}")
+    O, L = run.rows(w, mask=None)
+    assert run.ctx.stats()["kernel_variant"] == variant
+    Oref, Lref = oracle_rows(w, mask=None, rows=np.where(rows < n_pool, rows, -1))
+    assert_close(O, L, Oref, Lref, what="rows past the pool")

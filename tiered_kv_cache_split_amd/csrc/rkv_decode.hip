@@ -463,11 +463,16 @@ decode_seg_kernel(const SegParams p) {
     typename KF::U kb[KF::kMain + KF::kTail];
     typename VF::U vb[VF::kMain + VF::kTail];
 
-    // Row (cell or pool row) of this lane's cell in the chunk starting at c0, -1 if none.
+    // Row (cell or pool row) of this lane's cell in the chunk starting at c0, -1 if none (a
+    // list entry outside the pool is none too).
     auto row_of = [&](int64_t c0) -> int {
         const int64_t c = c0 + lane;
         if (c >= c_end) return -1;
-        return ROWS ? rows[c] : (int)c;
+        if constexpr (ROWS) {
+            const int r = rows[c];
+            return (r >= 0 && (int64_t)r < p.n_pool) ? r : -1;
+        }
+        return (int)c;
     };
     auto nvalid = [&](int64_t c0) { return max((int64_t)0, min((int64_t)kChunk, c_end - c0)); };
 
