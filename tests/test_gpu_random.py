@@ -1,5 +1,5 @@
 """Randomised GPU parity sweep: seeded random shapes, types, layouts, splits, tails, lift modes,
-masks, row lists, logit soft-caps and head dims through every entry point, each case against the fp64 oracle.  The cases are small
+masks, row lists (with holes and entries past the pool), logit soft-caps and head dims through every entry point, each case against the fp64 oracle.  The cases are small
 (the oracle runs them in well under a second) and cover combinations the targeted tests do
 not enumerate: every kernel family is reached (vector, matrix-core q8_0/q4_0, matrix-core
 binary16 window/tail/rows, prefill), with ragged lengths throughout."""
@@ -154,30 +154,32 @@ def test_random_host_tail(run, seed):
     assert_close(O, L, Oref, Lref, what=f"random host tail {seed}")
 
 
-@pytest.mark.parametrize("seed", range(16))
+@pytest.mark.parametrize("seed", range(24))
 def test_random_decode_head_dims(run, seed):
-    """Head dims 64 and 256 through the window + tail split: random heads (up to 8 query rows
-    per KV head), lengths, splits, types, layouts, tails, lift engines, masks and soft-caps."""
+    """Head dims 64, 256, 512 and 576/512 through the window + tail split: random heads (up to
+    48 query rows per KV head: row groups on the matrix-core kernel, groups of 8 on the vector
+    kernel), lengths, splits, types, layouts, tails, lift engines, masks and soft-caps."""
     rng = np.random.default_rng(9000 + seed)
-    d = int(rng.choice([64, 256]))
+    d = int(rng.choice([64, 256, 512, 576]))
+    dv = 512 if d == 576 else d
     n_head_kv = int(rng.choice([1, 2, 4, 8]))
-    n_q = int(rng.choice([1, 1, 2]))
-    gqa = int(rng.choice([g for g in (1, 2, 3, 4, 5, 8) if g * n_q <= 8]))
+    n_q = int(rng.choice([1, 1, 2, 3]))
+    gqa = int(rng.choice([1, 2, 3, 4, 5, 8, 16]))
     n_kv = int(rng.integers(1, 2500))
-    kt, vt = TYPES[int(rng.integers(0, 4))]
+    kt, vt = TYPES[1] if rng.random() < 0.5 else TYPES[int(rng.integers(0, 4))]
     tail = str(rng.choice(["host", "device", "none"]))
     wc = n_kv if tail == "none" else int(rng.integers(0, n_kv + 1))
     if wc == n_kv:
         tail = "none"
     tile = int(rng.integers(1, 1500))
     layout = str(rng.choice(["cell", "head"]))
-    q, k, v = gen.draw_qkv(rng, n_head_kv * gqa, n_q, n_head_kv, n_kv, d=d, dv=d, k_type=kt, v_type=vt)
-    w = dict(n_head=n_head_kv * gqa, n_head_kv=n_head_kv, q=q, k=k, v=v, k_type=kt, v_type=vt, d=d,
+    q, k, v = gen.draw_qkv(rng, n_head_kv * gqa, n_q, n_head_kv, n_kv, d=d, dv=dv, k_type=kt, v_type=vt)
+    w = dict(n_head=n_head_kv * gqa, n_head_kv=n_head_kv, q=q, k=k, v=v, k_type=kt, v_type=vt, d=d, dv=dv,
              scale=1 / np.sqrt(d), n_kv=n_kv, wc=wc, tile_kv=tile)
     mask = gen.random_mask_f16(rng, n_q, n_kv, p_hidden=0.3) if rng.random() < 0.5 else None
     cap = draw_softcap(100 + seed)
     lift = int(rng.choice([run.rkv.RKV_LIFT_BULK, run.rkv.RKV_LIFT_KERNEL]))
-    step(f"random head-dim decode seed {seed}: d {d} heads {n_head_kv}x{gqa} n_q {n_q} n_kv {n_kv} wc {wc} "
+    step(f"random head-dim decode seed {seed}: d {d}/{dv} heads {n_head_kv}x{gqa} n_q {n_q} n_kv {n_kv} wc {wc} "
          f"tile {tile} types {kt}/{vt} tail {tail} layout {layout} mask {mask is not None} softcap {cap:.3f} "
          f"lift {lift}")
     run.ctx.set_softcap(cap)
@@ -189,3 +191,46 @@ def test_random_decode_head_dims(run, seed):
         run.ctx.set_softcap(0.0)
     Oref, Lref = oracle_decode(w, mask=mask, softcap=cap)
     assert_close(O, L, Oref, Lref, what=f"random head-dim decode {seed}")
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_rows_head_dims(run, seed):
+    """Row lists at every head dim: random pools (q8_0/q4_0 on the matrix-core kernel, binary16
+    on the vector or persistent binary16 kernel), sequences, list lengths, shuffled order,
+    -1 holes, entries past the pool (no key: the oracle takes them as -1), up to 32 query rows
+    per KV head away from head dim 128, masks and soft-caps."""
+    rng = np.random.default_rng(11000 + seed)
+    d = int(rng.choice([64, 128, 256, 512, 576]))
+    dv = 512 if d == 576 else d
+    n_head_kv = int(rng.choice([1, 2, 4, 8]))
+    n_q = int(rng.choice([1, 1, 2]))
+    gqas = (1, 2, 4, 8) if d == 128 else (1, 2, 4, 5, 8, 16)
+    gqa = int(rng.choice([g for g in gqas if d != 128 or g * n_q <= 8]))
+    n_seq = int(rng.integers(1, 4))
+    n_pool = int(rng.integers(50, 1500))
+    kt, vt = TYPES[1] if rng.random() < 0.7 else TYPES[0]
+    lengths = tuple(int(x) for x in rng.integers(0, 1100, size=n_seq))
+    n_kv = max(1, max(lengths))
+    rows = gen.rows_lists(rng, n_pool, lengths, n_kv, shuffle=bool(rng.random() < 0.5))
+    holes = (rng.random(rows.shape) < 0.1) & (rows >= 0)
+    rows[holes] = -1
+    past = (rng.random(rows.shape) < 0.03) & (rows >= 0)
+    rows[past] = n_pool + rng.integers(0, 5000, int(past.sum()))
+    q = gen.draw_normal(rng, (n_seq, n_head_kv * gqa, n_q, d)).astype(np.float16)
+    k = gen.pack(kt, gen.draw_normal(rng, (n_pool, n_head_kv, d)))
+    v = gen.pack(vt, gen.draw_normal(rng, (n_pool, n_head_kv, dv)))
+    mask = None
+    if rng.random() < 0.5:
+        mask = np.where(rng.random((n_seq, 1, n_q, n_kv)) < 0.2, -np.inf, 0.0).astype(np.float16)
+    w = dict(q=q, k=k, v=v, kv_rows=rows, mask=mask, k_type=kt, v_type=vt, n_head=n_head_kv * gqa,
+             n_head_kv=n_head_kv, scale=1 / np.sqrt(d), d=d, dv=dv)
+    cap = draw_softcap(300 + seed)
+    step(f"random rows seed {seed}: d {d}/{dv} heads {n_head_kv}x{gqa} n_q {n_q} seqs {lengths} pool {n_pool} "
+         f"types {kt}/{vt} mask {mask is not None} softcap {cap:.3f}")
+    run.ctx.set_softcap(cap)
+    try:
+        O, L = run.rows(w)
+    finally:
+        run.ctx.set_softcap(0.0)
+    Oref, Lref = oracle_rows(w, rows=np.where(rows < n_pool, rows, -1), softcap=cap)
+    assert_close(O, L, Oref, Lref, what=f"random rows {seed}")
