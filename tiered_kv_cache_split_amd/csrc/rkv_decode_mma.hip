@@ -1,10 +1,12 @@
-// Matrix-core segment kernel for decode over cell-major q8_0 K / q4_0 V caches on gfx950.
+// Matrix-core segment kernel for decode over cell-major q8_0 K / q4_0 V caches on gfx950, at
+// head dims 64, 128, 256, 512 and the 576 / 512 pair, over a segment of cells or a row list.
 //
-// It computes the same partial as the vector kernel (opencoti-llamafile patch 0070-rolling-kv,
+// It computes the same partial as the vector kernels (opencoti-llamafile patch 0070-rolling-kv,
 // fattn.cu streaming_lse_kernel and the tail-partial op: M = max s_j, S = sum exp(s_j - M),
-// VKQ = sum exp(s_j - M) v_j over the segment's keys), but both contractions of a KV head's
-// few query rows (gqa x n_q <= 8) run on v_mfma_f32_16x16x32_f16, which frees the vector
-// units for the dequantisation and the softmax:
+// VKQ = sum exp(s_j - M) v_j over the segment's keys; for row lists the semantics of
+// llama.cpp PR #29510's flash_attn_ext_rows), but both contractions of a KV head's query rows
+// (up to 16 per workgroup) run on v_mfma_f32_16x16x32_f16, which frees the vector units for
+// the dequantisation and the softmax:
 //
 //   Q.K  D[key][row] = K (A: 16 keys x 32 head_dim of one q8_0 block) times Q^T (B, rows >= R
 //        zero).  The codes q enter A as exact binary16 integers 1024 + (q + 128) built by one
@@ -20,14 +22,13 @@
 //        per tile with a constant A of -1032 (or -1152) removes the offset from the same
 //        accumulator, so the tiles hold n - 8 (and 16 (n - 8)) times the weights.
 //
-// Workgroup = HW (8, 4 or 2) waves for one (split, head group, sequence), wave w = KV head
-// g0 + w, as in the vector cell-major kernel.  A 32-cell chunk is one contiguous span of each cache, moved
-// with buffer loads into registers (a thread takes two blocks of one head from each cache) and
-// from there into one of two LDS stages, where each block's scale is split from its data and
-// the data lands on 16-byte slots; two chunks are always in flight in registers, so one barrier
-// per chunk separates the stage being computed from the one being filled and the loads never
-// pause.  The online softmax is exact (the running max is raised whenever a chunk exceeds it)
-// so the binary16 weights stay in range.
+// Workgroup = one (row group, split, group of HW KV heads, sequence): HW * SV compute waves
+// (wave w computes KV head g0 + w / SV) and loader waves that move every 32-cell chunk with
+// buffer loads into registers (two chunks in flight) and from there into one of two LDS stages,
+// where each block's scale is split from its data and the data lands on 16-byte slots; one
+// barrier per chunk separates the stage being computed from the one being filled.  The online
+// softmax is exact (the running max is raised whenever a chunk exceeds it), so the binary16
+// weights stay in range.
 #include "rkv_internal.h"
 #include "rkv_unpack.h"
 #include "rkv_wave.h"
