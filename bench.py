@@ -121,9 +121,9 @@ def setup(num: int, sets: int, head_dim: int = 128):
         st["rows"] = dev(w["kv_rows"].astype(np.int32))
         st["mask"] = dev(w["mask"])
         n_seq, n_head, n_q, _ = w["q"].shape
-        st["o"] = torch.empty((n_seq, n_q, n_head, 128), dtype=torch.float32, device="cuda")
+        st["o"] = torch.empty((n_seq, n_q, n_head, dv), dtype=torch.float32, device="cuda")
         st["lse"] = torch.empty((n_seq, n_q, n_head), dtype=torch.float32, device="cuda")
-        kv_bytes = int((w["kv_rows"] >= 0).sum()) * w["n_head_kv"] * (rb(w["k_type"]) + rb(w["v_type"]))
+        kv_bytes = int((w["kv_rows"] >= 0).sum()) * w["n_head_kv"] * (rb(w["k_type"]) + rb(w["v_type"], dv))
         st["kv_bytes"] = kv_bytes
         st["tail_bytes"] = 0
         return st
@@ -169,10 +169,11 @@ def call(ctx, st, i):
 
 
 def prefill_flops(w) -> float:
-    """QK^T and PV flops over the visible (query, key) pairs of a causal chunk at the end."""
+    """QK^T and PV flops over the visible (query, key) pairs of a causal chunk at the end:
+    2 dk + 2 dv per pair and query head."""
     n_q, n_kv, q0 = w["q"].shape[1], w["n_kv"], w["q_pos0"]
     pairs = sum(min(n_kv, q0 + i + 1) for i in range(n_q))
-    return 4.0 * 128 * pairs * w["n_head"]
+    return 2.0 * (w["d"] + w.get("dv", w["d"])) * pairs * w["n_head"]
 
 
 def measured_h2d_gbs(nbytes=256 << 20, reps=10) -> float:
@@ -226,7 +227,7 @@ def cpu_baseline(num: int, budget_s: float = 12.0, w=None, softcap: float = 0.0)
     n_kv = w["n_kv"]
     target = budget_s / 8
     if w["kind"] == "rows":
-        per_cell = w["n_head_kv"] * (256 + 256)
+        per_cell = w["n_head_kv"] * (gen.row_bytes(w["k_type"], w["d"]) + gen.row_bytes(w["v_type"], w.get("dv", w["d"])))
         total_cells = int((w["kv_rows"] >= 0).sum())
         q = np.stack([oracle.q_values(w["q"][b]) for b in range(w["q"].shape[0])])
 
@@ -396,8 +397,10 @@ def measure(args, num):
         achieved = flops / (kern_total_ms * 1e-3) / 1e12
         out["roofline"] = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_F16_PEAK_TFLOPS,
                            "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4),
-                           "traffic": traffic_from_profiles("prefill_seg_q8q4_nq512_nkv106496", "prefill"),
-                           "kernel": "prefill_seg_kernel (all segments of a step)",
+                           "traffic": traffic_from_profiles("prefill_seg_q8q4_nq512_nkv106496", "prefill")
+                           if w["d"] == 128 else None,
+                           "kernel": (DECODE_KERNELS.get(stats.get("kernel_variant"), "segment kernel")
+                                      if w["d"] != 128 else "prefill_seg_kernel") + " (all segments of a step)",
                            "kernel_ms_per_step": round(kern_total_ms, 4)}
     else:
         name = {2: "decode_seg_q8q4_nkv131072", 4: "decode_seg_rows_f16_pool65536"}.get(num, "")
@@ -486,9 +489,6 @@ def main():
         gbs = measured_copy_gbs(1 << 30, reps=5)
         print(json.dumps({"copy_bytes_read": 1 << 30, "copy_bytes_written": 1 << 30, "copy_GBps": round(gbs, 1)}))
         return
-    if args.head_dim != 128 and args.workload not in (1, 2, 3):
-        print("head dims 64 and 256 are served by the decode path only (workloads 1-3)", file=sys.stderr)
-        sys.exit(2)
     out, w = measure(args, args.workload)
     if args.secondary and args.workload == 2 and args.head_dim == 128 and not args.softcap:
         # the other configurations, timed in the same run (fewer steps; the headline stays config 2)
