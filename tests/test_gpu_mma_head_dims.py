@@ -1,11 +1,11 @@
 """The matrix-core decode kernel at head dims 64, 256, 512 (dk = dv) and the 576 / 512 pair (q8_0 K
 / q4_0 V, cell-major KV heads) against the fp64 oracle: every head-group size it takes (8 and 4
-KV heads at 64; 4, 2 and 1 at 256; 1 at 512 and 576), one to eight rows per KV head and more in row groups of 16, the window
-+ lifted or device tail split, masks with an empty row, ragged lengths, the causal rule of a
-small prefill call, the soft-cap, and the full 131072-cell shape of the 128K decode at each
-head dim.  What a segment computes is
-the streaming partial of opencoti-llamafile patch 0070-rolling-kv (fattn.cu, streaming_lse_kernel);
-the head dims are those its streaming op supports."""
+KV heads at 64; 4, 2 and 1 at 256; 1 at 512 and 576), one to eight rows per KV head and more
+in row groups of 16 (several per workgroup at 64, 256 and 512), the window + lifted or device
+tail split, masks with an empty row, ragged lengths, the causal rule of a small prefill call,
+the soft-cap, and the full 131072-cell shape of the 128K decode at each head dim.  What a
+segment computes is the streaming partial of opencoti-llamafile patch 0070-rolling-kv (fattn.cu,
+streaming_lse_kernel); the head dims are those its streaming op supports."""
 import numpy as np
 import pytest
 
@@ -80,7 +80,9 @@ def test_small_prefill_causal(run, d):
 
 
 # (d, n_head, n_head_kv, n_q): more than 16 rows per KV head, in row groups of 16 (the last one
-# ragged), down to a single KV head with 128 query heads
+# ragged), down to a single KV head with 128 query heads; at 64 / 256 / 512 a workgroup takes
+# 2 / 4 / 2 row groups over one staged chunk, so the last workgroup can hold empty row groups
+# (72 rows at 256: five groups, three of the second workgroup's four empty)
 ROW_GROUPS = [(64, 64, 4, 2), (64, 40, 8, 5), (256, 16, 1, 1), (256, 48, 2, 3), (512, 128, 1, 1), (512, 20, 1, 3),
               (576, 128, 1, 1), (576, 16, 1, 2)]
 
@@ -125,7 +127,8 @@ def test_full_size_128k_all_heads(run, d):
 
 # row lists over a q8_0 / q4_0 pool (llama.cpp PR #29510, flash_attn_ext_rows): (d, n_head,
 # n_head_kv, n_q)
-ROW_LISTS = [(64, 32, 8, 1), (128, 32, 8, 1), (128, 16, 2, 1), (256, 16, 4, 2), (512, 16, 1, 1), (576, 40, 1, 1)]
+ROW_LISTS = [(64, 32, 8, 1), (128, 32, 8, 1), (128, 16, 2, 1), (256, 16, 4, 2), (512, 16, 1, 1), (576, 40, 1, 1),
+             (64, 96, 4, 1), (256, 32, 1, 1), (512, 40, 1, 1)]  # the last three: several row groups per workgroup
 
 
 @pytest.mark.parametrize("d,n_head,n_head_kv,n_q", ROW_LISTS)

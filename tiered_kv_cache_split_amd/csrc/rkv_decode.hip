@@ -776,7 +776,7 @@ int cell_heads(int dk, int dv, int k_type, int v_type, int n_head_kv, int R, boo
     // q8_0 / q4_0: the matrix-core kernel at head dims 64 .. 512 and 576 / 512, over segments
     // and row lists (up to 8 rows per KV head at 128, any number at the other head dims)
     if (k_type == T_Q8_0 && v_type == T_Q4_0)
-        return (dk == kHeadDim && R > kMaxRowsVec) ? 0 : decode_mma_heads(dk, dv, n_head_kv);
+        return (dk == kHeadDim && R > kMaxRowsVec) ? 0 : decode_mma_heads(dk, dv, n_head_kv, R);
     if (dk != kHeadDim || dv != kHeadDim || R > kMaxRowsVec) return 0;
     // binary16 with eight KV heads per cell group: the matrix-core kernel, also for row lists
     if (k_type == T_F16 && v_type == T_F16 && n_head_kv % 8 == 0) return 8;

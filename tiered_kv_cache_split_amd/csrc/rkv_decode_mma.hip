@@ -22,13 +22,13 @@
 //        per tile with a constant A of -1032 (or -1152) removes the offset from the same
 //        accumulator, so the tiles hold n - 8 (and 16 (n - 8)) times the weights.
 //
-// Workgroup = one (row group, split, group of HW KV heads, sequence): HW * SV compute waves
-// (wave w computes KV head g0 + w / SV) and loader waves that move every 32-cell chunk with
-// buffer loads into registers (two chunks in flight) and from there into one of two LDS stages,
-// where each block's scale is split from its data and the data lands on 16-byte slots; one
-// barrier per chunk separates the stage being computed from the one being filled.  The online
-// softmax is exact (the running max is raised whenever a chunk exceeds it), so the binary16
-// weights stay in range.
+// Workgroup = one (block of RG row groups, split, group of HW KV heads, sequence): HW * SV * RG
+// compute waves (one row group and KV head each, SV waves per head) and loader waves that move
+// every 32-cell chunk with buffer loads into registers (two chunks in flight) and from there
+// into one of two LDS stages, where each block's scale is split from its data and the data
+// lands on 16-byte slots; one barrier per chunk separates the stage being computed from the
+// one being filled.  The online softmax is exact (the running max is raised whenever a chunk
+// exceeds it), so the binary16 weights stay in range.
 #include "rkv_internal.h"
 #include "rkv_unpack.h"
 #include "rkv_wave.h"
@@ -82,20 +82,21 @@ struct VStage {
     uint32_t vx;
 };
 
-// Geometry of a workgroup for head dims DK (Q, K) and DV (V), HW KV heads and SV compute waves
-// per head (each of them takes 1 / SV of the V blocks).  A K unit is two blocks of one head's K
+// Geometry of a workgroup for head dims DK (Q, K) and DV (V), HW KV heads, SV compute waves
+// per head (each of them takes 1 / SV of the V blocks) and RG groups of 16 query rows, each
+// with compute waves of its own over the same staged chunks.  A K unit is two blocks of one head's K
 // row, a V unit two blocks of its V row; a cell holds kTpcK and kTpcV of them, a chunk kCh cells.
 // Loader threads take two V units and NIK K units (the last of them only for the first threads
 // when DK > DV) of every chunk; their count kNL is a whole number of waves when HW * DV / 64 is
 // a multiple of 4.
-template <int DK, int DV, int HW, int SV>
+template <int DK, int DV, int HW, int SV, int RG>
 struct Geo {
     static constexpr int NBK = DK / 32;       // q8_0 blocks per K row
     static constexpr int NBVT = DV / 32;      // q4_0 blocks per V row
     static constexpr int NBV = NBVT / SV;     // V blocks per compute wave
     static constexpr int UK = NBK / 2, UV = NBVT / 2;  // units per head and cell
     static constexpr int kTpcK = HW * UK, kTpcV = HW * UV;  // units per cell
-    static constexpr int kNC = 64 * HW * SV;  // compute threads
+    static constexpr int kNC = 64 * HW * SV * RG;  // compute threads (RG row groups of 16)
     static constexpr int kNL = kCh * kTpcV / 2;  // loader threads
     static constexpr int kKU = kCh * kTpcK;   // K units per chunk
     static constexpr int NIK = (kKU + kNL - 1) / kNL, NIKF = kKU / kNL;  // K units per loader thread (all, full)
@@ -122,8 +123,8 @@ struct Geo {
     // than in registers, and from 512 on the Q^T fragments (16 bytes per lane and block) too;
     // both per head, written by the head's first wave
     static constexpr bool kCinLds = NBK > 4, kQLds = NBK > 8;
-    static constexpr int kCin = kCinLds ? HW * NBK * 16 * 16 : 16;  // LDS bytes of the inputs
-    static constexpr int kQf = kQLds ? HW * NBK * 64 * 16 : 16;     // LDS bytes of the fragments
+    static constexpr int kCin = kCinLds ? RG * HW * NBK * 16 * 16 : 16;  // LDS bytes of the inputs
+    static constexpr int kQf = kQLds ? RG * HW * NBK * 64 * 16 : 16;     // LDS bytes of the fragments
 };
 
 // Kernel modes: a segment without a mask, a segment with one, a row list (with or without).
@@ -132,13 +133,14 @@ enum : int { kModePlain = 0, kModeMask = 1, kModeRows = 2 };
 // CAP: the logit soft-cap is on; MODE: the chunk cells are segment cells or row-list entries
 // naming pool rows, and with a mask the compute waves fetch each chunk's mask values ahead of
 // its Q.K (separate instantiations, so the plain path carries none of it).
-// The workgroup's first HW * SV waves compute (wave w: KV head g0 + w / SV, V blocks of part
-// w % SV); the remaining kNL threads only load and stage the chunks (two chunks in flight), so
-// the compute waves never wait for memory and hold no staging registers.
-template <int DK, int DV, int HW, int SV, bool CAP, int MODE>
-__global__ void __launch_bounds__((Geo<DK, DV, HW, SV>::kThreads))
-__attribute__((amdgpu_waves_per_eu((Geo<DK, DV, HW, SV>::kWavesPerEu)))) decode_mma_kernel(const SegParams p) {
-    using G = Geo<DK, DV, HW, SV>;
+// The workgroup's first HW * SV * RG waves compute (wave w: row group w / (HW SV) of the
+// workgroup's RG, KV head g0 + (w % (HW SV)) / SV, V blocks of part w % SV); the remaining kNL
+// threads only load and stage the chunks (two chunks in flight), so the compute waves never
+// wait for memory and hold no staging registers.
+template <int DK, int DV, int HW, int SV, int RG, bool CAP, int MODE>
+__global__ void __launch_bounds__((Geo<DK, DV, HW, SV, RG>::kThreads))
+__attribute__((amdgpu_waves_per_eu((Geo<DK, DV, HW, SV, RG>::kWavesPerEu)))) decode_mma_kernel(const SegParams p) {
+    using G = Geo<DK, DV, HW, SV, RG>;
     constexpr int NBK = G::NBK, NBV = G::NBV, UK = G::UK, UV = G::UV, kTpcK = G::kTpcK, kTpcV = G::kTpcV;
     constexpr int kNC = G::kNC, kNL = G::kNL, NIK = G::NIK, NIKF = G::NIKF;
     constexpr int kKc = G::kKc, kKp = G::kKp, kKh = G::kKh, kBk = G::kBk;
@@ -155,20 +157,22 @@ __attribute__((amdgpu_waves_per_eu((Geo<DK, DV, HW, SV>::kWavesPerEu)))) decode_
     const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int col = lane & 15, grp = lane >> 4;
     // query rows rho = i * gqa + r of a KV head, in groups of 16 (the columns of the MFMA tiles;
-    // columns past the group's rows are padding); the row group is the fastest grid index, so
-    // the groups reading one chunk run together
-    const int R_all = p.gqa * p.n_q, n_rg = (R_all + 15) >> 4;
+    // columns past the group's rows are padding), RG of them per workgroup; the block of row
+    // groups is the fastest grid index, so the workgroups reading one chunk run together
+    const int R_all = p.gqa * p.n_q, n_rg = (R_all + 15) >> 4, n_rgb = (n_rg + RG - 1) / RG;
     const int n_hgrp = p.n_head_kv / HW;
     int bid = blockIdx.x;
-    const int rg = bid % n_rg;
-    bid /= n_rg;
-    const int R0 = 16 * rg, R = min(16, R_all - R0);  // this workgroup's rows R0 .. R0 + R - 1
+    const int rgb = bid % n_rgb;
+    bid /= n_rgb;
     const int split = bid % p.n_splits;
     bid /= p.n_splits;
     const int hgrp = bid % n_hgrp;
     const int b = bid / n_hgrp;
     const bool loader = tid >= kNC;
-    const int wh = loader ? 0 : wave / SV, part = loader ? 0 : wave % SV;  // head in the group, V part
+    const int rgw = loader ? 0 : wave / (HW * SV);  // this compute wave's row group in the workgroup
+    const int wh = loader ? 0 : (wave % (HW * SV)) / SV, part = loader ? 0 : wave % SV;  // head, V part
+    // this wave's rows R0 .. R0 + R - 1 (none when R <= 0: the last block's spare row groups)
+    const int R0 = 16 * (RG * rgb + rgw), R = min(16, R_all - R0);
     const int g = hgrp * HW + wh;  // this compute wave's KV head
     int64_t c_beg = (int64_t)split * p.cells_per_split;
     int64_t c_end = min(p.n_cells, c_beg + (int64_t)p.cells_per_split);
@@ -392,7 +396,7 @@ __attribute__((amdgpu_waves_per_eu((Geo<DK, DV, HW, SV>::kWavesPerEu)))) decode_
     // in P.V slot 8 grp + col / 2; it receives byte col of the 8 keys of its slots
     const int vkey = 4 * grp + ((col >> 1) & 3) + 16 * (col >> 3);
     const int vrd = vkey * kVc + 64 * ((vkey >> 4) & 1) + 8 * (col & 1);
-    const int qi_row = (R0 + min(col, R - 1)) / p.gqa;  // query position of this lane's row
+    const int qi_row = min(R0 + min(col, max(R, 1) - 1), R_all - 1) / p.gqa;  // query of this lane's row
 
     // ---- Q^T as the B operand of Q.K: lane holds row `col`, head_dim 32*blk + 8*grp + 0..7
     // accumulator inputs: -1152 * block sum of row `col` of Q, in registers or (wide heads) at
@@ -400,11 +404,11 @@ __attribute__((amdgpu_waves_per_eu((Geo<DK, DV, HW, SV>::kWavesPerEu)))) decode_
     // The LDS copies are written before the first barrier and read once per block and chunk.
     float4_t cneg[G::kCinLds ? 1 : NBK];
     half8_t qb[G::kQLds ? 1 : NBK];
-    const int cin_off = 16 * (16 * NBK * wh + col);
-    const int q_off = 16 * (64 * NBK * wh + lane);
+    const int cin_off = 16 * (16 * NBK * (wh + HW * rgw) + col);
+    const int q_off = 16 * (64 * NBK * (wh + HW * rgw) + lane);
     {
         const bool ok = col < R;
-        const int r = R0 + (ok ? col : 0);
+        const int r = min(R0 + (ok ? col : 0), R_all - 1);
         const _Float16 *qrow = p.q + (int64_t)(r / p.gqa) * p.q_s1 + (int64_t)(g * p.gqa + r % p.gqa) * p.q_s2 +
                                (int64_t)b * p.q_s3;
         uint4 qv[NBK];
@@ -650,29 +654,29 @@ __attribute__((amdgpu_waves_per_eu((Geo<DK, DV, HW, SV>::kWavesPerEu)))) decode_
 template <int DV>
 constexpr int kSplitV = DV >= 512 ? 2 : 1;
 
-template <int DK, int DV, int HW, bool CAP, int MODE>
+template <int DK, int DV, int HW, int RG, bool CAP, int MODE>
 hipError_t launch_mma_c(const SegParams &p, hipStream_t s, int *occupancy) {
     constexpr int SV = kSplitV<DV>;
-    constexpr int kThreads = Geo<DK, DV, HW, SV>::kThreads;
+    constexpr int kThreads = Geo<DK, DV, HW, SV, RG>::kThreads;
     if (occupancy)
-        return hipOccupancyMaxActiveBlocksPerMultiprocessor(occupancy, decode_mma_kernel<DK, DV, HW, SV, CAP, MODE>,
-                                                            kThreads, 0);
+        return hipOccupancyMaxActiveBlocksPerMultiprocessor(occupancy,
+                                                            decode_mma_kernel<DK, DV, HW, SV, RG, CAP, MODE>, kThreads, 0);
     const int64_t blocks = (int64_t)p.n_splits * (p.n_head_kv / HW) * p.n_seq * decode_mma_row_groups(p);
     if (blocks > ((int64_t)1 << 31) - 1) return hipErrorInvalidValue;
-    launch_seg(decode_mma_kernel<DK, DV, HW, SV, CAP, MODE>, dim3((unsigned)blocks), dim3(kThreads), s, p);
+    launch_seg(decode_mma_kernel<DK, DV, HW, SV, RG, CAP, MODE>, dim3((unsigned)blocks), dim3(kThreads), s, p);
     return hipGetLastError();
 }
 
-template <int DK, int DV, int HW>
+template <int DK, int DV, int HW, int RG>
 hipError_t launch_mma(const SegParams &p, hipStream_t s, int *occupancy) {
     if (p.rows)
-        return p.cap_l2 != 0.f ? launch_mma_c<DK, DV, HW, true, kModeRows>(p, s, occupancy)
-                               : launch_mma_c<DK, DV, HW, false, kModeRows>(p, s, occupancy);
+        return p.cap_l2 != 0.f ? launch_mma_c<DK, DV, HW, RG, true, kModeRows>(p, s, occupancy)
+                               : launch_mma_c<DK, DV, HW, RG, false, kModeRows>(p, s, occupancy);
     if (p.mask)
-        return p.cap_l2 != 0.f ? launch_mma_c<DK, DV, HW, true, kModeMask>(p, s, occupancy)
-                               : launch_mma_c<DK, DV, HW, false, kModeMask>(p, s, occupancy);
-    return p.cap_l2 != 0.f ? launch_mma_c<DK, DV, HW, true, kModePlain>(p, s, occupancy)
-                           : launch_mma_c<DK, DV, HW, false, kModePlain>(p, s, occupancy);
+        return p.cap_l2 != 0.f ? launch_mma_c<DK, DV, HW, RG, true, kModeMask>(p, s, occupancy)
+                               : launch_mma_c<DK, DV, HW, RG, false, kModeMask>(p, s, occupancy);
+    return p.cap_l2 != 0.f ? launch_mma_c<DK, DV, HW, RG, true, kModePlain>(p, s, occupancy)
+                           : launch_mma_c<DK, DV, HW, RG, false, kModePlain>(p, s, occupancy);
 }
 
 }  // namespace
@@ -688,11 +692,32 @@ static bool mma_group_ok(int dk, int dv, int hw) {
            (hw * dk / 64) % 4 == 0;
 }
 
-int decode_mma_row_groups(const SegParams &p) { return (int)(((int64_t)p.gqa * p.n_q + 15) / 16); }
+// More than 16 rows per KV head: a workgroup of fewer heads takes several row groups over one
+// staged chunk, where that fits the register budget (row groups rg of hw heads; 0: none).
+static int mma_multi_rows(int dk, int dv, int &hw) {
+    if (dk == 64 && dv == 64) return hw = 4, 2;
+    if (dk == 256 && dv == 256) return hw = 1, 4;
+    if (dk == 512 && dv == 512) return hw = 1, 2;
+    return 0;
+}
 
-int decode_mma_heads(int dk, int dv, int n_head_kv) {
-    for (int hw : {8, 4, 2, 1})
-        if (n_head_kv % hw == 0 && mma_group_ok(dk, dv, hw)) return hw;
+// Row groups per workgroup of the cell-major decode launch for p.
+static int mma_rg(const SegParams &p) {
+    int hw = 0;
+    const int rg = (int64_t)p.gqa * p.n_q > 16 ? mma_multi_rows(p.d, p.dv, hw) : 0;
+    return (rg > 0 && hw == p.cell_hw) ? rg : 1;
+}
+
+int decode_mma_row_groups(const SegParams &p) {
+    const int64_t n_rg = ((int64_t)p.gqa * p.n_q + 15) / 16;
+    return (int)((n_rg + mma_rg(p) - 1) / mma_rg(p));
+}
+
+int decode_mma_heads(int dk, int dv, int n_head_kv, int R) {
+    int hw = 0;
+    if (R > 16 && mma_multi_rows(dk, dv, hw) > 0 && n_head_kv % hw == 0) return hw;
+    for (int h : {8, 4, 2, 1})
+        if (n_head_kv % h == 0 && mma_group_ok(dk, dv, h)) return h;
     return 0;
 }
 
@@ -705,17 +730,21 @@ bool decode_mma_ok(const SegParams &p) {
 
 hipError_t launch_decode_mma(const SegParams &p, hipStream_t s, int *occupancy) {
     if (!decode_mma_ok(p)) return hipErrorInvalidValue;
-    if (p.d == 576) return launch_mma<576, 512, 1>(p, s, occupancy);
-    switch (p.d * 16 + p.cell_hw) {
-        case 64 * 16 + 8: return launch_mma<64, 64, 8>(p, s, occupancy);
-        case 64 * 16 + 4: return launch_mma<64, 64, 4>(p, s, occupancy);
-        case 128 * 16 + 8: return launch_mma<128, 128, 8>(p, s, occupancy);
-        case 128 * 16 + 4: return launch_mma<128, 128, 4>(p, s, occupancy);
-        case 128 * 16 + 2: return launch_mma<128, 128, 2>(p, s, occupancy);
-        case 256 * 16 + 4: return launch_mma<256, 256, 4>(p, s, occupancy);
-        case 256 * 16 + 2: return launch_mma<256, 256, 2>(p, s, occupancy);
-        case 256 * 16 + 1: return launch_mma<256, 256, 1>(p, s, occupancy);
-        case 512 * 16 + 1: return launch_mma<512, 512, 1>(p, s, occupancy);
+    if (p.d == 576) return launch_mma<576, 512, 1, 1>(p, s, occupancy);
+    const int rg = mma_rg(p);
+    switch (p.d * 64 + p.cell_hw * 8 + rg) {
+        case 64 * 64 + 8 * 8 + 1: return launch_mma<64, 64, 8, 1>(p, s, occupancy);
+        case 64 * 64 + 4 * 8 + 1: return launch_mma<64, 64, 4, 1>(p, s, occupancy);
+        case 64 * 64 + 4 * 8 + 2: return launch_mma<64, 64, 4, 2>(p, s, occupancy);
+        case 128 * 64 + 8 * 8 + 1: return launch_mma<128, 128, 8, 1>(p, s, occupancy);
+        case 128 * 64 + 4 * 8 + 1: return launch_mma<128, 128, 4, 1>(p, s, occupancy);
+        case 128 * 64 + 2 * 8 + 1: return launch_mma<128, 128, 2, 1>(p, s, occupancy);
+        case 256 * 64 + 4 * 8 + 1: return launch_mma<256, 256, 4, 1>(p, s, occupancy);
+        case 256 * 64 + 2 * 8 + 1: return launch_mma<256, 256, 2, 1>(p, s, occupancy);
+        case 256 * 64 + 1 * 8 + 1: return launch_mma<256, 256, 1, 1>(p, s, occupancy);
+        case 256 * 64 + 1 * 8 + 4: return launch_mma<256, 256, 1, 4>(p, s, occupancy);
+        case 512 * 64 + 1 * 8 + 1: return launch_mma<512, 512, 1, 1>(p, s, occupancy);
+        case 512 * 64 + 1 * 8 + 2: return launch_mma<512, 512, 1, 2>(p, s, occupancy);
         default: return hipErrorInvalidValue;
     }
 }

@@ -84,10 +84,11 @@ hipError_t launch_decode_segment(const SegParams &p, int k_type, int v_type, hip
 // (dk = dv) and 576 / 512 with p.cell_hw KV heads per workgroup and up to 16 query rows per KV head per
 // workgroup (more in row groups; at most 8 in all at head dim 128) (decode_mma_ok); with `occupancy` set it
 // reports resident workgroups per CU instead of launching.  decode_mma_heads gives the group
-// size it takes for n_head_kv heads at head dim d (0: none).
-int decode_mma_heads(int dk, int dv, int n_head_kv);
+// size it takes for n_head_kv heads at head dims (dk, dv) with R rows per KV head (0: none).
+int decode_mma_heads(int dk, int dv, int n_head_kv, int R);
 bool decode_mma_ok(const SegParams &p);
-// Row groups of 16 query rows per KV head (one workgroup each) of the cell-major decode launch.
+// Workgroups per (split, head group, sequence) of the cell-major decode launch: blocks of the
+// row groups of 16 query rows per KV head that one workgroup takes together.
 int decode_mma_row_groups(const SegParams &p);
 hipError_t launch_decode_mma(const SegParams &p, hipStream_t s, int *occupancy);
 // The binary16 matrix-core decode kernel (windows, tail tiles and row lists) over groups of
