@@ -92,17 +92,22 @@ def physical_cores() -> int:
 _DRAWN = {}
 
 
-def setup(num: int, sets: int, head_dim: int = 128):
+def setup(num: int, sets: int, head_dim: int = 128, f16: bool = False):
     import numpy as np
     import torch
 
     import rkv_inputs as gen
 
-    key = (num, head_dim)
+    key = (num, head_dim, f16)
     if key not in _DRAWN:  # the tail-read contrasts of one workload reuse its draw
         _DRAWN.clear()
-        _DRAWN[key] = gen.make_workload(num) if head_dim == 128 else \
-            gen.make_workload(num, d=head_dim, dv=512 if head_dim == 576 else head_dim)
+        over = {} if head_dim == 128 else {"d": head_dim, "dv": 512 if head_dim == 576 else head_dim}
+        if f16:  # binary16 K and V in place of the workload's own types
+            over.update(k_type=gen.TYPE_F16, v_type=gen.TYPE_F16)
+        w = gen.make_workload(num, **over)
+        if f16:
+            w["name"] = w["name"].replace("q8q4", "f16")
+        _DRAWN[key] = w
     w = _DRAWN[key]
     dv = w.get("dv", w["d"])
     rb = lambda t, dd=w["d"]: gen.row_bytes(t, dd)
@@ -300,7 +305,7 @@ def measure(args, num):
     import tiered_kv_cache_split_amd as rkv
 
     print(f"[bench] workload {num}: {gen.WORKLOADS[num]['name']} setup", file=sys.stderr, flush=True)
-    st = setup(num, args.sets, args.head_dim)
+    st = setup(num, args.sets, args.head_dim, args.kv_types == "f16")
     w = st["w"]
     ctx = rkv.Context(0)
     if args.splits:
@@ -415,7 +420,8 @@ def measure(args, num):
             label += " (all segments of a step)"
         out["roofline"] = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": round(achieved / HBM_PEAK_GBS, 4),
-                           "traffic": traffic_from_profiles(name, "decode") if name and w["d"] == 128 else None,
+                           "traffic": traffic_from_profiles(name, "decode")
+                           if name and w["d"] == 128 and args.kv_types == "own" else None,
                            "kernel": label, "kernel_avg_ms": round(kern_ms, 5)}
     if lift_totals:
         tot = sum(t[0] for t in lift_totals) / len(lift_totals)
@@ -458,8 +464,9 @@ def main():
     ap.add_argument("--softcap", type=float, default=0.0, help="logit soft-cap c (0: none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--head-dim", type=int, default=128, choices=[64, 128, 256, 512, 576],
-                    help="head dim of Q and K; V takes the same, or 512 with 576 (other than 128: decode "
-                         "workloads 1-3 only)")
+                    help="head dim of Q and K; V takes the same, or 512 with 576")
+    ap.add_argument("--kv-types", choices=["own", "f16"], default="own",
+                    help="K / V types: the workload's own, or binary16 for both")
     ap.add_argument("--lift-mode", type=int, default=3,
                     help="0 bulk DMA, 1 word-granularity UVA read, 2 bulk copy kernel on the copy stream, "
                          "3 automatic (decode: copy kernel, prefill: DMA)")
@@ -490,7 +497,7 @@ def main():
         print(json.dumps({"copy_bytes_read": 1 << 30, "copy_bytes_written": 1 << 30, "copy_GBps": round(gbs, 1)}))
         return
     out, w = measure(args, args.workload)
-    if args.secondary and args.workload == 2 and args.head_dim == 128 and not args.softcap:
+    if args.secondary and args.workload == 2 and args.head_dim == 128 and not args.softcap and args.kv_types == "own":
         # the other configurations, timed in the same run (fewer steps; the headline stays config 2)
         sec = {}
         base = dict(vars(args))

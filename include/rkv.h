@@ -19,11 +19,13 @@
  * strides, nb[0] is the element (or quant block) size.  Rows of head_dim values must be
  * contiguous (nb[0] == type size).  Supported head dims (patch 0070, fattn.cu: the streaming
  * op's supported shapes): head_dim == dv in {64, 128, 256, 512}, and head_dim 576 for Q and
- * K with dv 512 for V, on every attention entry point and the host tail partial.  Decode at
- * head_dim == dv in {64, 128, 256, 512} over cell-major q8_0 K / q4_0 V (and binary16 at 128)
- * runs on the matrix-core kernels when the KV heads form groups the kernel takes (8 or 4 at
- * 64; 8, 4 or 2 at 128; 4, 2 or 1 at 256; 1 at 512) and n_q * gqa <= 8; prefill at 128 on the
- * matrix-core prefill kernel; everything else on the vector kernels; rkv_lse_merge takes
+ * K with dv 512 for V, on every attention entry point and the host tail partial.  Decode
+ * over cell-major caches runs on the matrix-core kernels: q8_0 K / q4_0 V at head_dim == dv in
+ * {64, 128, 256, 512} and at 576 / 512 when the KV heads form groups the kernel takes (8 or 4
+ * at 64; 8, 4 or 2 at 128; 4, 2 or 1 at 256; 1 at 512 and 576), with n_q * gqa <= 8 at 128 and
+ * any number of rows at the other head dims; binary16 K and V at head_dim == dv in {64, 128,
+ * 256, 512} in groups of 8, 8, 4 and 2 KV heads with n_q * gqa <= 8.  Prefill at 128 runs on
+ * the matrix-core prefill kernel; everything else on the vector kernels; rkv_lse_merge takes
  * dv 64, 128, 256 or 512; Q in F16;
  * K in F16 or Q8_0; V in F16 or Q4_0.  Q8_0 is a 34-byte block (binary16 scale d, 32
  * int8 codes q; value d*q).  Q4_0 is an 18-byte block (binary16 scale d, 16 bytes; byte
@@ -130,7 +132,8 @@ enum rkv_kernel_variant {
     RKV_KERNEL_PREFILL_MFMA = 1,      /* matrix-core prefill over 256-row query tiles                */
     RKV_KERNEL_DECODE_CELL = 2,       /* vector decode over cell-major groups of KV heads           */
     RKV_KERNEL_DECODE_CELL_MFMA = 3,  /* matrix-core decode over cell-major q8_0/q4_0 head groups   */
-    RKV_KERNEL_DECODE_CELL_MFMA16 = 4, /* persistent matrix-core decode over eight binary16 heads
+    RKV_KERNEL_DECODE_CELL_MFMA16 = 4, /* persistent matrix-core decode over cell groups of binary16
+                                          heads: 8 at head dims 64 and 128, 4 at 256, 2 at 512
                                           (windows, tail tiles, row lists)                         */
     RKV_KERNEL_DECODE_HD = 5           /* vector decode for head dims other than 128 (window + tail) */
 };
@@ -253,8 +256,8 @@ int rkv_attn_prefill(rkv_ctx *ctx, const rkv_tensor *q,
  *           kv_rows[j + n_kv*b].  A negative row, or one >= n_pool, is padding: it
  *           contributes nothing and is never dereferenced.  Cell-major q8_0 K / q4_0 V pools
  *           run on the matrix-core decode kernel at every supported head dim, binary16 pools
- *           of groups of 8 KV heads at head dim 128 on the persistent binary16 kernel, the rest
- *           on the vector kernels.
+ *           in groups of 8, 8, 4 or 2 KV heads at head dims 64, 128, 256 or 512 (dk = dv) on
+ *           the persistent binary16 kernel, the rest on the vector kernels.
  *   mask    F16 [>= n_kv, >= n_q, 1, n_seq] additive, device, or NULL.
  *   o       float32 [128, n_head, n_q, n_seq]; lse float32 [n_head, n_q, n_seq] or NULL. */
 int rkv_attn_rows(rkv_ctx *ctx, const rkv_tensor *q, const rkv_tensor *k_pool,

@@ -141,6 +141,37 @@ def test_lse_merge(dv):
                  what=f"merge dv={dv}")
 
 
+@pytest.mark.parametrize("dv,n_seg,n_rows", [(64, 512, 40), (256, 1024, 20), (512, 300, 16), (64, 1500, 8),
+                                           (128, 700, 40)])
+def test_lse_merge_many_segments(dv, n_seg, n_rows):
+    """Synthetic partials, a fifth of them empty (M = -inf, S = 0) with NaN where their values
+    would be -- a segment with no keys need not write them -- merged on the device: up to 1024
+    segments take the part merge with several segments per thread, more the per-row merge."""
+    import torch
+    import tiered_kv_cache_split_amd as rkv
+    rng = np.random.default_rng(n_seg + dv)
+    M = rng.uniform(-6.0, 6.0, (n_seg, n_rows))
+    S = rng.uniform(0.5, 40.0, (n_seg, n_rows))
+    VKQ = rng.standard_normal((n_seg, n_rows, dv)) * S[..., None]
+    empty = rng.random((n_seg, n_rows)) < 0.2
+    empty[:, 3] = True  # every segment of row 3 is empty: O = 0, LSE = -inf
+    M[empty], S[empty], VKQ[empty] = -np.inf, 0.0, 0.0
+    P = np.zeros((n_seg, n_rows, 2 + dv), np.float32)
+    P[:, :, 0], P[:, :, 1], P[:, :, 2:] = M, S, VKQ
+    P[empty, 2:] = np.nan
+    parts = [(P[s_, :, 0].astype(np.float64)[None], P[s_, :, 1].astype(np.float64)[None],
+              np.where(empty[s_][:, None], 0.0, P[s_, :, 2:]).astype(np.float64)[None]) for s_ in range(n_seg)]
+    Oref, Lref = oracle.merge(parts)
+    o = torch.empty((n_rows, dv), dtype=torch.float32, device="cuda")
+    lse = torch.empty((n_rows,), dtype=torch.float32, device="cuda")
+    step(f"lse merge dv {dv}: {n_seg} segments x {n_rows} rows, empty ones with NaN values")
+    rkv.lse_merge(dev(P), n_seg, n_rows, o, lse, dv=dv)
+    torch.cuda.synchronize()
+    O, L = o.cpu().numpy(), lse.cpu().numpy()
+    assert np.all(O[3] == 0) and L[3] == -np.inf
+    assert_close(O, L, Oref.reshape(n_rows, dv), Lref.reshape(-1), what=f"merge dv={dv} n_seg={n_seg}")
+
+
 @pytest.mark.parametrize("d", [64, 256])
 def test_host_tail_partial(run, d):
     """The tail's partial on the host cores (RKV_TAIL_HOST) at head dims 64 and 256, merged with

@@ -30,8 +30,9 @@ def test_rows(run, dk, dv, kt, vt):
     w = gen.make_workload(4, scale_down=16, d=dk, dv=dv, k_type=kt, v_type=vt)  # pool 4096, lists <= 1920
     step(f"rows head dims {dk}/{dv} types {kt}/{vt}")
     O, L = run.rows(w)
-    # q8_0 / q4_0 pools: the matrix-core kernel; binary16 at these dims: the vector kernel
-    assert run.ctx.stats()["kernel_variant"] == (3 if kt == gen.TYPE_Q8_0 else 5)
+    # q8_0 / q4_0 pools: the matrix-core kernel; binary16 pools of 8 KV heads: the binary16
+    # matrix-core kernel where dk = dv, the vector kernel at 576 / 512
+    assert run.ctx.stats()["kernel_variant"] == (3 if kt == gen.TYPE_Q8_0 else 4 if dk == dv else 5)
     Oref, Lref = oracle_rows(w)
     assert_close(O, L, Oref, Lref, what=f"rows d={dk}/{dv}")
 

@@ -722,7 +722,7 @@ hipError_t launch_decode_r(const SegParams &p, hipStream_t s, int *occupancy) {
         // (q8_0 / q4_0 cell groups go to the matrix-core kernel before the rows are dispatched)
         if constexpr (KT == T_F16 && VT == T_F16) {
             if (decode_mma16_ok(p)) return launch_decode_mma16(p, s, occupancy);
-            if (p.cell_hw == 2) return launch_cell<KT, VT, R, 2>(p, s, occupancy);
+            if (p.cell_hw == 2 && p.d == kHeadDim) return launch_cell<KT, VT, R, 2>(p, s, occupancy);
         }
         return hipErrorInvalidValue;
     }
@@ -777,9 +777,13 @@ int cell_heads(int dk, int dv, int k_type, int v_type, int n_head_kv, int R, boo
     // and row lists (up to 8 rows per KV head at 128, any number at the other head dims)
     if (k_type == T_Q8_0 && v_type == T_Q4_0)
         return (dk == kHeadDim && R > kMaxRowsVec) ? 0 : decode_mma_heads(dk, dv, n_head_kv, R);
+    // binary16 in cell groups (8 KV heads at 64 and 128, 4 at 256, 2 at 512): the persistent
+    // matrix-core kernel, also for row lists
+    if (k_type == T_F16 && v_type == T_F16 && R <= kMaxRowsVec) {
+        const int hw = decode_mma16_heads(dk, dv);
+        if (hw > 0 && n_head_kv % hw == 0) return hw;
+    }
     if (dk != kHeadDim || dv != kHeadDim || R > kMaxRowsVec) return 0;
-    // binary16 with eight KV heads per cell group: the matrix-core kernel, also for row lists
-    if (k_type == T_F16 && v_type == T_F16 && n_head_kv % 8 == 0) return 8;
     if (rows) return 0;  // other gathered rows: per-head kernel
     if (k_type == T_F16 && v_type == T_F16) return n_head_kv % 2 == 0 ? 2 : 0;
     return 0;
@@ -796,9 +800,12 @@ bool decode_kernel_persistent(const SegParams &p, int k_type, int v_type) {
 }
 
 int decode_kernel_variant(const SegParams &p, int k_type, int v_type) {
-    if (p.d != kHeadDim)
-        return (p.cell_hw > 0 && k_type == T_Q8_0 && v_type == T_Q4_0 && decode_mma_ok(p)) ? RKV_KERNEL_DECODE_CELL_MFMA
-                                                                                         : RKV_KERNEL_DECODE_HD;
+    if (p.d != kHeadDim) {
+        if (p.cell_hw > 0 && k_type == T_Q8_0 && v_type == T_Q4_0 && decode_mma_ok(p)) return RKV_KERNEL_DECODE_CELL_MFMA;
+        if (p.cell_hw > 0 && k_type == T_F16 && v_type == T_F16 && decode_mma16_ok(p))
+            return RKV_KERNEL_DECODE_CELL_MFMA16;
+        return RKV_KERNEL_DECODE_HD;
+    }
     if (p.cell_hw <= 0) return (k_type == T_Q8_0 && p.gqa * p.n_q >= 6) ? RKV_KERNEL_DECODE_HD : RKV_KERNEL_DECODE_HEAD;
     if (k_type == T_Q8_0 && v_type == T_Q4_0 && decode_mma_ok(p)) return RKV_KERNEL_DECODE_CELL_MFMA;
     if (k_type == T_F16 && v_type == T_F16 && decode_mma16_ok(p)) return RKV_KERNEL_DECODE_CELL_MFMA16;

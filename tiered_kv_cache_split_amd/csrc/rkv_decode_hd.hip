@@ -396,9 +396,10 @@ __global__ void __launch_bounds__(D) merge_hd_kernel(const float *part, int n_se
         for (int sg = 0; sg < n_seg; ++sg) {
             const float *q = part + ((int64_t)sg * n_rows + row) * PS;
             const float m = q[0], s = q[1], v = q[2 + t];
+            // (an empty partial, M = -inf, need not have written its values)
             const float w = m == -INFINITY ? 0.f : __expf(m - M);
             S = fmaf(s, w, S);
-            a = fmaf(v, w, a);
+            a = w > 0.f ? fmaf(v, w, a) : a;
         }
     }
     const bool ok = M > -INFINITY && S > 0.f;
@@ -449,8 +450,9 @@ hipError_t launch_decode_hd(const SegParams &p, int k_type, int v_type, hipStrea
 hipError_t launch_merge_hd(const float *partials, int n_seg, int64_t n_rows, int dv, float *o, float *lse,
                            hipStream_t s) {
     if (n_rows <= 0) return hipSuccess;
-    // few rows and up to 256 segments: one thread per segment over 16-value parts of each row
-    if (n_seg <= 256 && n_rows < 1024) return launch_merge_parts(partials, n_seg, n_rows, dv, o, lse, s);
+    // few rows and up to 1024 segments: up to four segments per thread over 16-value parts of
+    // each row
+    if (n_seg <= 1024 && n_rows < 1024) return launch_merge_parts(partials, n_seg, n_rows, dv, o, lse, s);
     if (dv == 64)
         hipLaunchKernelGGL(merge_hd_kernel<64>, dim3((unsigned)n_rows), dim3(64), 0, s, partials, n_seg, n_rows, o, lse);
     else if (dv == 256)

@@ -16,11 +16,15 @@
 //        V^T read by ds_read_b64_tr_b16 (16 lanes fetch four keys x sixteen head_dim values and
 //        receive them transposed, one head_dim value of four keys per lane).
 //
-// Workgroup = 8 waves, wave w = KV head g0 + w of the (sequence, group of 8 KV heads) pair of
-// its current task; the kernel is persistent (work split below).  A 16-cell chunk of the group
-// (8 x 256 bytes of K and of V per cell) is moved with 16-byte
-// buffer loads into registers and from there into one of two LDS stages; two chunks are always
-// in flight in registers, together with the chunk's mask values.  Row-list entries are read one
+// Head dims 64, 128, 256 and 512 (dk = dv): a KV head group of HW heads (8, 8, 4, 2) keeps the
+// cell at 1 or 2 KB per cache, and each head gets SV = 8 / HW waves (1, 1, 2, 4), each of which
+// computes the head's Q.K (the same scores in every one of them) and 1 / SV of its P.V tiles.
+//
+// Workgroup = 8 waves, wave w = KV head g0 + w / SV (P.V part w % SV) of the (sequence, group of
+// HW KV heads) pair of its current task; the kernel is persistent (work split below).  A 16-cell
+// chunk of the group (HW x 2d bytes of K and of V per cell) is moved with 16-byte buffer loads
+// into registers and from there into one of two LDS stages; two chunks are always in flight in
+// registers, together with the chunk's mask values.  Row-list entries are read one
 // fetch ahead of the loads that use them; a padding entry's loads are pointed past the buffer
 // range (they read nothing) and its key is masked.  The online softmax is exact (the running
 // max is raised whenever a chunk exceeds it).
@@ -41,18 +45,34 @@ typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kHW = 8;                 // KV heads per workgroup
 constexpr int kCh = 16;                // cells per chunk
-constexpr int kNT = 64 * kHW;          // threads
-constexpr int kRowB = 2 * kHeadDim;    // bytes of one head's K or V row
-constexpr int kCell = kHW * kRowB;     // bytes of one cell of the group
-constexpr int kS = kCell + 32;         // LDS cell stride: 520 dwords, 8 mod 32 banks
-constexpr int kStage = kCh * kS;       // bytes of one LDS stage of one cache
-constexpr int kTpc = kNT / kCh;        // threads per cell (32)
-constexpr int kM = kCell / 16 / kTpc;  // 16-byte units per thread, cache and chunk (4)
+constexpr int kNT = 512;               // threads (8 waves)
+constexpr int kTpc = kNT / kCh;        // threads per cell (32): wave w stages cells 2w, 2w + 1
+constexpr int kMaxR = 8;               // query rows per KV head
 constexpr uint32_t kNowhere = 0x80000000u;  // buffer offset past every range: reads zero
 constexpr int kMaxPairs = 1024;        // (sequence, head group) pairs of one launch
-static_assert(kCell % (16 * kTpc) == 0 && kNT % kCh == 0, "thread mapping");
+
+// Geometry at head dim D.
+template <int D>
+struct G16 {
+    static constexpr int HW = D <= 128 ? 8 : 1024 / D;  // KV heads per workgroup
+    static constexpr int SV = 8 / HW;                    // waves per KV head
+    static constexpr int kRowB = 2 * D;                  // bytes of one head's K or V row
+    static constexpr int kCell = HW * kRowB;             // bytes of one cell of the group
+    static constexpr int kS = kCell + 32;                // LDS cell stride: 8 mod 32 banks
+    static constexpr int kStage = kCh * kS;              // bytes of one LDS stage of one cache
+    static constexpr int kM = kCell / 16 / kTpc;         // 16-byte units per thread, cache and chunk
+    static constexpr int NB = D / 32;                    // Q.K steps of 32 head_dim values
+    static constexpr int NT = D / 16 / SV;               // P.V tiles of 16 head_dim values per wave
+    static constexpr int kPs = 2 + D;                    // partial row: M, S, VKQ[D]
+    // Q^T of a new pair rides in the stage registers up to 128; wider heads load it when the
+    // pair starts (a workgroup meets one or two pairs)
+    static constexpr bool kQStage = D <= 128;
+    // resident waves per SIMD the registers allow: one workgroup per CU (at 64 two would fit
+    // the LDS, but within 128 registers the kernel spilled and ran 9% slower)
+    static constexpr int kWavesPerEu = 2;
+    static_assert(kCell % (16 * kTpc) == 0 && HW * SV == 8 && kS % 128 == 32, "thread and bank mapping");
+};
 
 // One chunk (task) in registers: this thread's K and V units, the mask value it stages,
 // whether its cell is a key of the segment, the task's pair and first cell, the Q^T operand
@@ -62,9 +82,10 @@ struct Meta {
     int newq;   // the task starts a new pair for this workgroup (q holds its Q^T)
     int64_t c0; // first cell
 };
+template <int D>
 struct Stage16 {
-    uint4 k[kM], v[kM];
-    half8_t q[4];
+    uint4 k[G16<D>::kM], v[G16<D>::kM];
+    half8_t q[G16<D>::kQStage ? G16<D>::NB : 1];
     uint32_t mk;
     int ok;
     Meta meta;
@@ -79,17 +100,21 @@ struct Stage16 {
 // padding at the end of the shorter lists costs nothing.  A workgroup writes its partial of
 // each pair it meets into slot j, and M = -inf, S = 0 (no values) for the other pairs; when
 // asked, workgroup 0 also writes each pair's slot range for the merge.
-template <int R, bool ROWS>
-__global__ void __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2)))
+template <int D, int R, bool ROWS>
+__global__ void __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(G16<D>::kWavesPerEu)))
 decode_mma16_kernel(const SegParams p) {
+    using GD = G16<D>;
+    constexpr int kHW = GD::HW, SV = GD::SV, kRowB = GD::kRowB, kCell = GD::kCell, kS = GD::kS, kStage = GD::kStage;
+    constexpr int kM = GD::kM, NB = GD::NB, NT = GD::NT, kPs = GD::kPs;
     __shared__ __attribute__((aligned(16))) uint8_t s_k[2 * kStage];
     __shared__ __attribute__((aligned(16))) uint8_t s_v[2 * kStage];
     __shared__ __attribute__((aligned(16))) int s_ok[2][kCh];                 // key is visible data
-    __shared__ __attribute__((aligned(16))) _Float16 s_mask[2][kHW][kCh];     // mask[row][key]
+    __shared__ __attribute__((aligned(16))) _Float16 s_mask[2][kMaxR][kCh];   // mask[row][key]
     __shared__ uint32_t s_off[kMaxPairs + 1];  // first task of each pair; s_off[n_pairs] = tasks
 
     const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int col = lane & 15, grp = lane >> 4;
+    const int head = wave / SV, part = wave % SV;  // KV head in the group, P.V part
     const int n_hgrp = p.n_head_kv / kHW;
     const int n_pairs = p.n_seq * n_hgrp;
     const uint32_t G = (uint32_t)p.n_splits, j = blockIdx.x;
@@ -144,27 +169,27 @@ decode_mma16_kernel(const SegParams p) {
     const bool mthread = p.mask != nullptr && tid < R * kCh;
 
     // ---- partial of one pair for this lane's row (col < R): slot j.  Buffer stores of four
-    // values each keep the store count per partial small and fixed (9), so that the waits for
-    // the loads in flight, which count stores too, stay exact.
+    // values each keep the store count per partial small and fixed (NT + 1), so that the waits
+    // for the loads in flight, which count stores too, stay exact.
     const __amdgpu_buffer_rsrc_t rpart = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(p.partials + (int64_t)(p.slot0 + j) * p.n_rows * kPartialStride), (short)0,
-        (int)(p.n_rows * kPartialStride * sizeof(float)), 0x00020000);
+        (void *)(p.partials + (int64_t)(p.slot0 + j) * p.n_rows * kPs), (short)0,
+        (int)(p.n_rows * kPs * sizeof(float)), 0x00020000);
     // (acc null: the empty partial, M and S only -- the merge gives a segment with M = -inf
     // no weight and ignores its values)
     auto write_partial = [&](int pair, float M, float S, const float4_t *acc) __attribute__((always_inline)) {
         if (col >= R) return;
-        const int bb = pair / n_hgrp, g = (pair % n_hgrp) * kHW + wave;
+        const int bb = pair / n_hgrp, g = (pair % n_hgrp) * kHW + head;
         const int r = col % p.gqa, i = col / p.gqa;
         const int row = (g * p.gqa + r) + p.n_head * (i + p.n_q * bb);
-        const int base = row * kPartialStride * (int)sizeof(float);
-        if (grp == 0)
+        const int base = row * kPs * (int)sizeof(float);
+        if (grp == 0 && part == 0)
             __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{__builtin_bit_cast(uint32_t, M), __builtin_bit_cast(uint32_t, S)},
                                                   rpart, base, 0, 0);
         if (!acc) return;
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt)
+        for (int dt = 0; dt < NT; ++dt)
             __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, acc[dt]), rpart,
-                                                   base + (2 + 16 * dt + 4 * grp) * (int)sizeof(float), 0, 0);
+                                                   base + (2 + 16 * (NT * part + dt) + 4 * grp) * (int)sizeof(float), 0, 0);
     };
 
     // ---- task k of this workgroup: its pair and first cell (k past the end: a phantom task
@@ -193,7 +218,19 @@ decode_mma16_kernel(const SegParams p) {
         inl = make_int2(real && c < n_cells, real && c + 1 < n_cells);
     };
 
-    auto fetch = [&](Stage16 &st, uint32_t k) __attribute__((always_inline)) {
+    // Q^T of pair `pair`: lane holds row `col` (rows >= R read row 0 and are never written),
+    // head_dim 32*blk + 8*grp + 0..7
+    auto load_q = [&](int pair, half8_t *q) __attribute__((always_inline)) {
+        const int bb = pair / n_hgrp, hg = pair % n_hgrp;
+        const int r = col < R ? col : 0;
+        const int g = hg * kHW + head;
+        const _Float16 *qrow = p.q + (int64_t)(r / p.gqa) * p.q_s1 + (int64_t)(g * p.gqa + r % p.gqa) * p.q_s2 +
+                               (int64_t)bb * p.q_s3;
+#pragma unroll
+        for (int blk = 0; blk < NB; ++blk)
+            q[blk] = __builtin_bit_cast(half8_t, *reinterpret_cast<const uint4 *>(qrow + 32 * blk + 8 * grp));
+    };
+    auto fetch = [&](Stage16<D> &st, uint32_t k) __attribute__((always_inline)) {
         const bool real = k < n_t;
         int pair;
         int64_t c0;
@@ -244,21 +281,13 @@ decode_mma16_kernel(const SegParams p) {
             const _Float16 *mb = p.mask + p.pos0 + (int64_t)bb * p.m_s3 + (int64_t)(mrow / p.gqa) * p.m_s1;
             st.mk = __builtin_bit_cast(uint16_t, mb[min(c0 + mkey, n_cells - 1)]);
         }
-        if (st.meta.newq) {
-            // Q^T of the pair: lane holds row `col` (rows >= R read row 0 and are never written),
-            // head_dim 32*blk + 8*grp + 0..7
-            const int r = col < R ? col : 0;
-            const int g = hg * kHW + wave;
-            const _Float16 *qrow = p.q + (int64_t)(r / p.gqa) * p.q_s1 + (int64_t)(g * p.gqa + r % p.gqa) * p.q_s2 +
-                                   (int64_t)bb * p.q_s3;
-#pragma unroll
-            for (int blk = 0; blk < 4; ++blk)
-                st.q[blk] = __builtin_bit_cast(half8_t, *reinterpret_cast<const uint4 *>(qrow + 32 * blk + 8 * grp));
+        if constexpr (GD::kQStage) {
+            if (st.meta.newq) load_q(pair, st.q);
         }
     };
-    Meta mnext;         // the task stashed last: computed next
-    half8_t qnext[4];   // its Q^T when it starts a new pair
-    auto stash = [&](const Stage16 &st, int buf) __attribute__((always_inline)) {
+    Meta mnext;                                 // the task stashed last: computed next
+    half8_t qnext[GD::kQStage ? NB : 1];         // its Q^T when it starts a new pair
+    auto stash = [&](const Stage16<D> &st, int buf) __attribute__((always_inline)) {
         uint8_t *dk = s_k + buf * kStage + fcell * kS + 16 * fsub;
         uint8_t *dv = s_v + buf * kStage + fcell * kS + 16 * fsub;
 #pragma unroll
@@ -269,18 +298,20 @@ decode_mma16_kernel(const SegParams p) {
         if (fsub == 0) s_ok[buf][fcell] = st.ok;
         if (mthread) s_mask[buf][mrow][mkey] = __builtin_bit_cast(_Float16, (uint16_t)st.mk);
         mnext = st.meta;
-        if (st.meta.newq) {
+        if constexpr (GD::kQStage) {
+            if (st.meta.newq) {
 #pragma unroll
-            for (int blk = 0; blk < 4; ++blk) qnext[blk] = st.q[blk];
+                for (int blk = 0; blk < NB; ++blk) qnext[blk] = st.q[blk];
+            }
         }
     };
 
-    float4_t oacc[8];  // O^T[16*dt + 4*grp + e][col]
+    float4_t oacc[NT];  // O^T[16*(NT*part + dt) + 4*grp + e][col]
     float mrun = -INFINITY, lrow = 0.f;  // running max (log2 domain), this lane's part of the sum
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) oacc[dt] = float4_t{0.f, 0.f, 0.f, 0.f};
+    for (int dt = 0; dt < NT; ++dt) oacc[dt] = float4_t{0.f, 0.f, 0.f, 0.f};
     const float c = p.scale_log2;
-    half8_t qb[4];
+    half8_t qb[NB];
     int cur = -1;  // pair being accumulated
     // finish the current pair (a fixed number of stores, so the waits for the loads in flight
     // stay exact)
@@ -302,20 +333,24 @@ decode_mma16_kernel(const SegParams p) {
         if (mt_.newq) {
             flush();
             cur = mt_.pair;
+            if constexpr (GD::kQStage) {
 #pragma unroll
-            for (int blk = 0; blk < 4; ++blk) qb[blk] = qnext[blk];
+                for (int blk = 0; blk < NB; ++blk) qb[blk] = qnext[blk];
+            } else {
+                load_q(cur, qb);
+            }
             mrun = -INFINITY;
             lrow = 0.f;
 #pragma unroll
-            for (int dt = 0; dt < 8; ++dt) oacc[dt] = float4_t{0.f, 0.f, 0.f, 0.f};
+            for (int dt = 0; dt < NT; ++dt) oacc[dt] = float4_t{0.f, 0.f, 0.f, 0.f};
         }
-        const uint8_t *kw = s_k + buf * kStage + wave * kRowB;  // this head's K row of cell j at kw + j*kS
-        const uint8_t *vw = s_v + buf * kStage + wave * kRowB;
+        const uint8_t *kw = s_k + buf * kStage + head * kRowB;  // this head's K row of cell j at kw + j*kS
+        const uint8_t *vw = s_v + buf * kStage + head * kRowB;
 
         // ---- Q.K: D[key 4*grp + ii][row col]
         float4_t dq = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int blk = 0; blk < 4; ++blk) {
+        for (int blk = 0; blk < NB; ++blk) {
             const uint4 a = *reinterpret_cast<const uint4 *>(kw + col * kS + 64 * blk + 16 * grp);
             dq = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a), qb[blk], dq, 0, 0, 0);
         }
@@ -344,7 +379,7 @@ decode_mma16_kernel(const SegParams p) {
             mrun = mnew;
             lrow *= a;
 #pragma unroll
-            for (int dt = 0; dt < 8; ++dt) oacc[dt] *= a;
+            for (int dt = 0; dt < NT; ++dt) oacc[dt] *= a;
         }
         const float msub = mrun == -INFINITY ? 0.f : mrun;
         float pr[4];
@@ -357,9 +392,10 @@ decode_mma16_kernel(const SegParams p) {
 
         // ---- P.V: A = V^T tile (head_dim 16*dt + col, keys 4*grp + 0..3) by a transposing read:
         // lane col of group grp fetches key 4*grp + col / 4, head_dim 16*dt + 4*(col % 4) + 0..3
-        const uint8_t *vr = vw + (4 * grp + (col >> 2)) * kS + 8 * (col & 3);
+        // (this wave's tiles: dt = NT*part .. NT*part + NT - 1)
+        const uint8_t *vr = vw + (4 * grp + (col >> 2)) * kS + 8 * (col & 3) + 32 * NT * part;
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) {
+        for (int dt = 0; dt < NT; ++dt) {
             const short4_t t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                 (__attribute__((address_space(3))) short4_t *)(vr + 32 * dt));
             oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(half4_t, t), pb, oacc[dt], 0, 0, 0);
@@ -373,7 +409,7 @@ decode_mma16_kernel(const SegParams p) {
     // pairs with no exit in between (a phantom task has no visible key), so that every path
     // into the loop head has the same loads in flight.
     if (n_t > 0) {
-        Stage16 sa, sb;  // tasks 2i (sa) and 2i + 1 (sb)
+        Stage16<D> sa, sb;  // tasks 2i (sa) and 2i + 1 (sb)
         sa.mk = sb.mk = 0;
         if constexpr (ROWS) {
             rows_of(0, sa.rid, sa.rin);
@@ -397,26 +433,49 @@ decode_mma16_kernel(const SegParams p) {
     flush();
 }
 
-template <int R, bool ROWS>
+template <int D, int R, bool ROWS>
 hipError_t launch16(const SegParams &p, hipStream_t s, int *occupancy) {
     if (occupancy)
-        return hipOccupancyMaxActiveBlocksPerMultiprocessor(occupancy, decode_mma16_kernel<R, ROWS>, kNT, 0);
+        return hipOccupancyMaxActiveBlocksPerMultiprocessor(occupancy, decode_mma16_kernel<D, R, ROWS>, kNT, 0);
     // persistent: n_splits workgroups in all, each covering every pair
-    launch_seg(decode_mma16_kernel<R, ROWS>, dim3((unsigned)p.n_splits), dim3(kNT), s, p);
+    launch_seg(decode_mma16_kernel<D, R, ROWS>, dim3((unsigned)p.n_splits), dim3(kNT), s, p);
     return hipGetLastError();
 }
 
-template <int R>
-hipError_t launch16_r(const SegParams &p, hipStream_t s, int *occupancy) {
-    return p.rows ? launch16<R, true>(p, s, occupancy) : launch16<R, false>(p, s, occupancy);
+template <int D>
+hipError_t launch16_d(const SegParams &p, hipStream_t s, int *occupancy) {
+    const bool rows = p.rows != nullptr;
+    switch (p.gqa * p.n_q) {
+        case 1: return rows ? launch16<D, 1, true>(p, s, occupancy) : launch16<D, 1, false>(p, s, occupancy);
+        case 2: return rows ? launch16<D, 2, true>(p, s, occupancy) : launch16<D, 2, false>(p, s, occupancy);
+        case 3: return rows ? launch16<D, 3, true>(p, s, occupancy) : launch16<D, 3, false>(p, s, occupancy);
+        case 4: return rows ? launch16<D, 4, true>(p, s, occupancy) : launch16<D, 4, false>(p, s, occupancy);
+        case 5: return rows ? launch16<D, 5, true>(p, s, occupancy) : launch16<D, 5, false>(p, s, occupancy);
+        case 6: return rows ? launch16<D, 6, true>(p, s, occupancy) : launch16<D, 6, false>(p, s, occupancy);
+        case 7: return rows ? launch16<D, 7, true>(p, s, occupancy) : launch16<D, 7, false>(p, s, occupancy);
+        case 8: return rows ? launch16<D, 8, true>(p, s, occupancy) : launch16<D, 8, false>(p, s, occupancy);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace
 
+int decode_mma16_heads(int d, int dv) {
+    if (d != dv) return 0;
+    switch (d) {
+        case 64: return G16<64>::HW;
+        case 128: return G16<128>::HW;
+        case 256: return G16<256>::HW;
+        case 512: return G16<512>::HW;
+        default: return 0;
+    }
+}
+
 bool decode_mma16_ok(const SegParams &p) {
     const int R = p.gqa * p.n_q;
-    if (p.cell_hw != kHW || R < 1 || R > 8 || p.n_head_kv % kHW != 0) return false;
-    if ((int64_t)p.n_seq * (p.n_head_kv / kHW) > kMaxPairs) return false;
+    const int hw = decode_mma16_heads(p.d, p.dv);
+    if (hw == 0 || p.cell_hw != hw || R < 1 || R > kMaxR || p.n_head_kv % hw != 0) return false;
+    if ((int64_t)p.n_seq * (p.n_head_kv / hw) > kMaxPairs) return false;
     // row lists address the pool with 32-bit buffer offsets
     if (p.rows && (p.n_pool <= 0 || p.n_pool * p.k_s1 >= ((int64_t)1 << 31) || p.n_pool * p.v_s1 >= ((int64_t)1 << 31) ||
                    p.k_s1 >= (1 << 24) || p.v_s1 >= (1 << 24)))
@@ -425,15 +484,12 @@ bool decode_mma16_ok(const SegParams &p) {
 }
 
 hipError_t launch_decode_mma16(const SegParams &p, hipStream_t s, int *occupancy) {
-    switch (p.gqa * p.n_q) {
-        case 1: return launch16_r<1>(p, s, occupancy);
-        case 2: return launch16_r<2>(p, s, occupancy);
-        case 3: return launch16_r<3>(p, s, occupancy);
-        case 4: return launch16_r<4>(p, s, occupancy);
-        case 5: return launch16_r<5>(p, s, occupancy);
-        case 6: return launch16_r<6>(p, s, occupancy);
-        case 7: return launch16_r<7>(p, s, occupancy);
-        case 8: return launch16_r<8>(p, s, occupancy);
+    if (!decode_mma16_ok(p)) return hipErrorInvalidValue;
+    switch (p.d) {
+        case 64: return launch16_d<64>(p, s, occupancy);
+        case 128: return launch16_d<128>(p, s, occupancy);
+        case 256: return launch16_d<256>(p, s, occupancy);
+        case 512: return launch16_d<512>(p, s, occupancy);
         default: return hipErrorInvalidValue;
     }
 }

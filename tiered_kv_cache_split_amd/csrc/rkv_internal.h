@@ -92,8 +92,11 @@ bool decode_mma_ok(const SegParams &p);
 int decode_mma_row_groups(const SegParams &p);
 hipError_t launch_decode_mma(const SegParams &p, hipStream_t s, int *occupancy);
 // The binary16 matrix-core decode kernel (windows, tail tiles and row lists) over groups of
-// eight cell-major KV heads with gqa * n_q <= 8 rows per head; the same occupancy convention.
+// cell-major KV heads (8 at head dims 64 and 128, 4 at 256, 2 at 512) with gqa * n_q <= 8 rows
+// per head; the same occupancy convention.
 bool decode_mma16_ok(const SegParams &p);
+// KV heads per cell group of the binary16 matrix-core kernel at head dims (d, dv) (0: none).
+int decode_mma16_heads(int d, int dv);
 // Whether the decode kernel for p is the persistent one: n_splits workgroups then take equal
 // contiguous runs of the 16-cell chunks of all (sequence, head group) pairs, numbered
 // pair-major, and cells_per_split is unused.
@@ -113,8 +116,8 @@ struct MergeRange {
 };
 hipError_t launch_merge(const float *partials, int n_seg, int64_t n_rows, float *o, float *lse,
                         float *partial_out, hipStream_t s, const MergeRange *range = nullptr);
-// The same merge for partial rows of 2 + dv floats (dv = 64, 128, 256, 512), up to 256 segments:
-// one thread per segment over 16-value parts of each row.
+// The same merge for partial rows of 2 + dv floats (dv = 64, 128, 256, 512), up to 1024
+// segments: up to four segments per thread over 16-value parts of each row.
 hipError_t launch_merge_parts(const float *partials, int n_seg, int64_t n_rows, int dv, float *o, float *lse,
                               hipStream_t s);
 // Writes (M=-inf, S=0, VKQ=0) for n_rows rows into partial slot 0.

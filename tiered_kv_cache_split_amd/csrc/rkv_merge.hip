@@ -35,15 +35,16 @@ struct RowRange {
     }
 };
 
-// Up to kMergePartThreads segments over few rows: workgroup (row, part) merges head_dim values
-// 16*part .. 16*part+15 of one row (D / 16 parts; partial rows of 2 + D floats) with one thread
-// per segment, so every load of the merge is issued at once by D / 16 times more workgroups
-// than rows and the merge costs one memory latency.  M and S are read by every part (8 bytes
-// per segment).
+// Up to NS * kMergePartThreads segments over few rows: workgroup (row, part) merges head_dim
+// values 16*part .. 16*part+15 of one row (D / 16 parts; partial rows of 2 + D floats) with
+// NS segments per thread (thread t: segments t, t + 256, ...), so every load of the merge is
+// issued at once by D / 16 times more workgroups than rows and the merge costs one memory
+// latency.  M and S are read by every part (8 bytes per segment).
 constexpr int kMergePartDim = 16;
 constexpr int kMergePartThreads = 256;
+constexpr int kMergePartMaxNs = 4;  // segments per thread: up to 1024 segments
 
-template <int D>
+template <int D, int NS>
 __global__ void __launch_bounds__(kMergePartThreads) merge_parts_kernel(const float *__restrict__ part, int n_seg,
                                                                         int64_t n_rows, float *__restrict__ o,
                                                                         float *__restrict__ lse,
@@ -56,33 +57,50 @@ __global__ void __launch_bounds__(kMergePartThreads) merge_parts_kernel(const fl
     const int pt = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     int sa, sb;
     rr.of(row, n_seg, sa, sb);
-    const bool has = sa + tid < sb;
-    const float *pp = part + ((int64_t)(has ? sa + tid : 0) * n_rows + row) * kPs;
-    float2 ms = make_float2(-INFINITY, 0.f);
-    float v[kMergePartDim];
-    if (has) {
-        ms = *reinterpret_cast<const float2 *>(pp);
+    float2 ms[NS];
+    float v[NS][kMergePartDim];
+    float mloc = -INFINITY;
 #pragma unroll
-        for (int j = 0; j < kMergePartDim / 2; ++j) {
-            const float2 x = *reinterpret_cast<const float2 *>(pp + 2 + kMergePartDim * pt + 2 * j);
-            v[2 * j] = x.x;
-            v[2 * j + 1] = x.y;
+    for (int u = 0; u < NS; ++u) {
+        const int sg = sa + tid + u * kMergePartThreads;
+        const bool has = sg < sb;
+        const float *pp = part + ((int64_t)(has ? sg : 0) * n_rows + row) * kPs;
+        ms[u] = make_float2(-INFINITY, 0.f);
+        if (has) {
+            ms[u] = *reinterpret_cast<const float2 *>(pp);
+#pragma unroll
+            for (int j = 0; j < kMergePartDim / 2; ++j) {
+                const float2 x = *reinterpret_cast<const float2 *>(pp + 2 + kMergePartDim * pt + 2 * j);
+                v[u][2 * j] = x.x;
+                v[u][2 * j + 1] = x.y;
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < kMergePartDim; ++j) v[u][j] = 0.f;
         }
-    } else {
-#pragma unroll
-        for (int j = 0; j < kMergePartDim; ++j) v[j] = 0.f;
+        mloc = fmaxf(mloc, ms[u].x);
     }
-    float M = wave_max(ms.x);
+    float M = wave_max(mloc);
     if (lane == 0) s_m[wv] = M;
     __syncthreads();
 #pragma unroll
     for (int k = 0; k < kW; ++k) M = fmaxf(M, s_m[k]);
-    const float w = (M == -INFINITY || ms.x == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((ms.x - M) * kLog2e);
-    // per-wave sums of the weighted S and values, then across the waves through LDS
-    const float S = wave_sum(ms.y * w);
+    // this thread's weighted S and values (an empty partial, M = -inf, has weight 0 and its
+    // values need not have been written), then per-wave sums, then across the waves via LDS
+    float sl = 0.f, al[kMergePartDim];
+#pragma unroll
+    for (int j = 0; j < kMergePartDim; ++j) al[j] = 0.f;
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+        const float w = (M == -INFINITY || ms[u].x == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((ms[u].x - M) * kLog2e);
+        sl = fmaf(ms[u].y, w, sl);
+#pragma unroll
+        for (int j = 0; j < kMergePartDim; ++j) al[j] = w > 0.f ? fmaf(v[u][j], w, al[j]) : al[j];
+    }
+    const float S = wave_sum(sl);
     float acc[kMergePartDim];
 #pragma unroll
-    for (int j = 0; j < kMergePartDim; ++j) acc[j] = wave_sum(w > 0.f ? v[j] * w : 0.f);
+    for (int j = 0; j < kMergePartDim; ++j) acc[j] = wave_sum(al[j]);
     if (lane == 0) {
 #pragma unroll
         for (int j = 0; j < kMergePartDim; ++j) s_acc[wv][j] = acc[j];
@@ -274,7 +292,7 @@ hipError_t launch_merge(const float *partials, int n_seg, int64_t n_rows, float 
         hipLaunchKernelGGL(merge_rows_kernel, dim3((unsigned)((n_rows + kMergeRowsPerBlock - 1) / kMergeRowsPerBlock)),
                            dim3(64 * kMergeRowsPerBlock), 0, s, partials, n_seg, n_rows, o, lse, partial_out, rr);
     } else if (n_seg <= kMergePartThreads) {
-        hipLaunchKernelGGL(merge_parts_kernel<kHeadDim>, dim3((unsigned)n_rows, kHeadDim / kMergePartDim),
+        hipLaunchKernelGGL((merge_parts_kernel<kHeadDim, 1>), dim3((unsigned)n_rows, kHeadDim / kMergePartDim),
                            dim3(kMergePartThreads), 0, s, partials, n_seg, n_rows, o, lse, partial_out, rr);
     } else {
         hipLaunchKernelGGL(merge_kernel, dim3((unsigned)n_rows), dim3(kMergeThreads), 0, s, partials, n_seg, n_rows,
@@ -283,24 +301,30 @@ hipError_t launch_merge(const float *partials, int n_seg, int64_t n_rows, float 
     return hipGetLastError();
 }
 
+template <int D>
+void launch_parts_d(const float *partials, int n_seg, int64_t n_rows, float *o, float *lse, hipStream_t s) {
+    const dim3 grid((unsigned)n_rows, (unsigned)(D / kMergePartDim));
+    const RowRange rr{};
+    if (n_seg <= kMergePartThreads)
+        hipLaunchKernelGGL((merge_parts_kernel<D, 1>), grid, dim3(kMergePartThreads), 0, s, partials, n_seg, n_rows, o,
+                           lse, nullptr, rr);
+    else
+        hipLaunchKernelGGL((merge_parts_kernel<D, kMergePartMaxNs>), grid, dim3(kMergePartThreads), 0, s, partials,
+                           n_seg, n_rows, o, lse, nullptr, rr);
+}
+
 hipError_t launch_merge_parts(const float *partials, int n_seg, int64_t n_rows, int dv, float *o, float *lse,
                               hipStream_t s) {
     if (n_rows <= 0) return hipSuccess;
-    if (n_seg > kMergePartThreads || n_rows > ((int64_t)1 << 31) - 1) return hipErrorInvalidValue;
-    const dim3 grid((unsigned)n_rows, (unsigned)(dv / kMergePartDim));
-    const RowRange rr{};
+    if (n_seg > kMergePartMaxNs * kMergePartThreads || n_rows > ((int64_t)1 << 31) - 1) return hipErrorInvalidValue;
     if (dv == 64)
-        hipLaunchKernelGGL(merge_parts_kernel<64>, grid, dim3(kMergePartThreads), 0, s, partials, n_seg, n_rows, o, lse,
-                           nullptr, rr);
+        launch_parts_d<64>(partials, n_seg, n_rows, o, lse, s);
     else if (dv == 128)
-        hipLaunchKernelGGL(merge_parts_kernel<128>, grid, dim3(kMergePartThreads), 0, s, partials, n_seg, n_rows, o,
-                           lse, nullptr, rr);
+        launch_parts_d<128>(partials, n_seg, n_rows, o, lse, s);
     else if (dv == 256)
-        hipLaunchKernelGGL(merge_parts_kernel<256>, grid, dim3(kMergePartThreads), 0, s, partials, n_seg, n_rows, o,
-                           lse, nullptr, rr);
+        launch_parts_d<256>(partials, n_seg, n_rows, o, lse, s);
     else if (dv == 512)
-        hipLaunchKernelGGL(merge_parts_kernel<512>, grid, dim3(kMergePartThreads), 0, s, partials, n_seg, n_rows, o,
-                           lse, nullptr, rr);
+        launch_parts_d<512>(partials, n_seg, n_rows, o, lse, s);
     else
         return hipErrorNotSupported;
     return hipGetLastError();
