@@ -650,13 +650,16 @@ __attribute__((amdgpu_waves_per_eu((Geo<DK, DV, HW, SV, RG>::kWavesPerEu)))) dec
 }
 
 // compute waves per head: two when dv = 512, where one wave's registers cannot hold the output
-// of all sixteen V blocks beside Q
-template <int DV>
-constexpr int kSplitV = DV >= 512 ? 2 : 1;
+// of all sixteen V blocks beside Q; four for the 576 / 512 pair, whose LDS (Q fragments of 18
+// blocks) leaves room for one workgroup per CU, so that each SIMD still runs one compute wave
+// (every wave computes the whole Q.K: 0.38 of the HBM roofline against 0.29 with two; at
+// 512 / 512, two workgroups per CU with two waves per head stay faster, 0.50 against 0.39)
+template <int DK, int DV>
+constexpr int kSplitV = DK == 576 ? 4 : DV >= 512 ? 2 : 1;
 
 template <int DK, int DV, int HW, int RG, bool CAP, int MODE>
 hipError_t launch_mma_c(const SegParams &p, hipStream_t s, int *occupancy) {
-    constexpr int SV = kSplitV<DV>;
+    constexpr int SV = kSplitV<DK, DV>;
     constexpr int kThreads = Geo<DK, DV, HW, SV, RG>::kThreads;
     if (occupancy)
         return hipOccupancyMaxActiveBlocksPerMultiprocessor(occupancy,
