@@ -21,10 +21,10 @@
 // computes the head's Q.K (the same scores in every one of them) and 1 / SV of its P.V tiles.
 //
 // Workgroup = 8 waves, wave w = KV head g0 + w / SV (P.V part w % SV) of the (sequence, group of
-// HW KV heads) pair of its current task; the kernel is persistent (work split below).  A 16-cell
-// chunk of the group (HW x 2d bytes of K and of V per cell) is moved with 16-byte buffer loads
-// into registers and from there into one of two LDS stages; two chunks are always in flight in
-// registers, together with the chunk's mask values.  Row-list entries are read one
+// HW KV heads) pair of its current task; the kernel is persistent (work split below).  A chunk
+// of 16 cells of the group (32 over a segment at head dim 64; HW x 2d bytes of K and of V per
+// cell) is moved with 16-byte buffer loads into registers and from there into one of two LDS
+// stages; two chunks are always in flight in registers, together with the chunk's mask values.  Row-list entries are read one
 // fetch ahead of the loads that use them; a padding entry's loads are pointed past the buffer
 // range (they read nothing) and its key is masked.  The online softmax is exact (the running
 // max is raised whenever a chunk exceeds it).
@@ -45,20 +45,25 @@ typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kCh = 16;                // cells per chunk
 constexpr int kNT = 512;               // threads (8 waves)
-constexpr int kTpc = kNT / kCh;        // threads per cell (32): wave w stages cells 2w, 2w + 1
 constexpr int kMaxR = 8;               // query rows per KV head
 constexpr uint32_t kNowhere = 0x80000000u;  // buffer offset past every range: reads zero
 constexpr int kMaxPairs = 1024;        // (sequence, head group) pairs of one launch
 
-// Geometry at head dim D.
-template <int D>
+// Geometry at head dim D, over a segment of cells or (ROWS) a row list.
+template <int D, bool ROWS = false>
 struct G16 {
     static constexpr int HW = D <= 128 ? 8 : 1024 / D;  // KV heads per workgroup
     static constexpr int SV = 8 / HW;                    // waves per KV head
     static constexpr int kRowB = 2 * D;                  // bytes of one head's K or V row
     static constexpr int kCell = HW * kRowB;             // bytes of one cell of the group
+    // cells per chunk: 16 (one 16-key tile), and 32 over a segment at 64, where a cell is half
+    // as large, so that a chunk keeps 64 KB of K and V (0.60 of the HBM roofline against 0.55
+    // with 16); row lists keep 16, as a workgroup's run of a list's chunks is short and twice
+    // the chunk made its first load and last compute cost more than they saved (41 against 37 us)
+    static constexpr int kCh = (kCell >= 2048 || ROWS) ? 16 : 32;
+    static constexpr int kTpc = kNT / kCh;               // threads per cell (32 or 16)
+    static constexpr int kCpw = 64 / kTpc;               // cells staged by one wave (2 or 4)
     static constexpr int kS = kCell + 32;                // LDS cell stride: 8 mod 32 banks
     static constexpr int kStage = kCh * kS;              // bytes of one LDS stage of one cache
     static constexpr int kM = kCell / 16 / kTpc;         // 16-byte units per thread, cache and chunk
@@ -82,18 +87,18 @@ struct Meta {
     int newq;   // the task starts a new pair for this workgroup (q holds its Q^T)
     int64_t c0; // first cell
 };
-template <int D>
+template <int D, bool ROWS>
 struct Stage16 {
-    uint4 k[G16<D>::kM], v[G16<D>::kM];
-    half8_t q[G16<D>::kQStage ? G16<D>::NB : 1];
+    uint4 k[G16<D, ROWS>::kM], v[G16<D, ROWS>::kM];
+    half8_t q[G16<D, ROWS>::kQStage ? G16<D, ROWS>::NB : 1];
     uint32_t mk;
     int ok;
     Meta meta;
-    int2 rid, rin;  // row lists: raw pool rows of the wave's two cells for the next fetch, and
-                    // whether they are keys
+    int rid[G16<D, ROWS>::kCpw], rin[G16<D, ROWS>::kCpw];  // row lists: raw pool rows of the wave's cells for
+                                               // the next fetch, and whether they are keys
 };
 
-// Work split: the tasks are the 16-cell chunks of every (sequence, head group) pair, numbered
+// Work split: the tasks are the chunks of every (sequence, head group) pair, numbered
 // pair-major; workgroup j of G takes the contiguous run of tasks [jT/G, (j+1)T/G) of the T
 // tasks, so it meets few pairs (one unless a pair boundary falls in its run).  A row list only
 // counts up to its extent (1 + its last pool row, from a scan before the launch), so the
@@ -101,11 +106,12 @@ struct Stage16 {
 // each pair it meets into slot j, and M = -inf, S = 0 (no values) for the other pairs; when
 // asked, workgroup 0 also writes each pair's slot range for the merge.
 template <int D, int R, bool ROWS>
-__global__ void __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(G16<D>::kWavesPerEu)))
+__global__ void __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(G16<D, ROWS>::kWavesPerEu)))
 decode_mma16_kernel(const SegParams p) {
-    using GD = G16<D>;
+    using GD = G16<D, ROWS>;
     constexpr int kHW = GD::HW, SV = GD::SV, kRowB = GD::kRowB, kCell = GD::kCell, kS = GD::kS, kStage = GD::kStage;
     constexpr int kM = GD::kM, NB = GD::NB, NT = GD::NT, kPs = GD::kPs;
+    constexpr int kCh = GD::kCh, kTpc = GD::kTpc, kCpw = GD::kCpw, NU = kCh / 16;  // NU 16-key tiles per chunk
     __shared__ __attribute__((aligned(16))) uint8_t s_k[2 * kStage];
     __shared__ __attribute__((aligned(16))) uint8_t s_v[2 * kStage];
     __shared__ __attribute__((aligned(16))) int s_ok[2][kCh];                 // key is visible data
@@ -165,7 +171,7 @@ decode_mma16_kernel(const SegParams p) {
     const int64_t n_cells = p.n_cells;
     const int qi_row = min(col, R - 1) / p.gqa;  // query position of this lane's row
     const int fcell = tid / kTpc, fsub = tid % kTpc;
-    const int mrow = tid / kCh, mkey = tid % kCh;  // mask staging: row tid / 16, key tid % 16
+    const int mrow = tid / kCh, mkey = tid % kCh;  // mask staging: row tid / kCh, key tid % kCh
     const bool mthread = p.mask != nullptr && tid < R * kCh;
 
     // ---- partial of one pair for this lane's row (col < R): slot j.  Buffer stores of four
@@ -203,19 +209,22 @@ decode_mma16_kernel(const SegParams p) {
         pair = cur;
         c0 = (int64_t)(t - s_off[cur]) * kCh;
     };
-    // pool rows of the wave's two cells 2*wave, 2*wave + 1 of task k's chunk, as read (always
-    // from inside the list), and whether each is a key: entries past the list end (or of a
-    // phantom task) are padding.  The raw value is only combined with the flag when the next
-    // fetch uses it, so that waiting for it never waits for the loads issued after it.
-    auto rows_of = [&](uint32_t k, int2 &raw, int2 &inl) __attribute__((always_inline)) {
+    // pool rows of the wave's cells kCpw*wave .. kCpw*wave + kCpw - 1 of task k's chunk, as read
+    // (always from inside the list), and whether each is a key: entries past the list end (or
+    // of a phantom task) are padding.  The raw value is only combined with the flag when the
+    // next fetch uses it, so that waiting for it never waits for the loads issued after it.
+    auto rows_of = [&](uint32_t k, int (&raw)[kCpw], int (&inl)[kCpw]) __attribute__((always_inline)) {
         int pair;
         int64_t c0;
         task_at(cur_r, k, pair, c0);
         const int32_t *__restrict__ rl = p.rows + (int64_t)(pair / n_hgrp) * p.rows_s;
-        const int64_t c = c0 + 2 * wave;
-        raw = make_int2(rl[min(c, n_cells - 1)], rl[min(c + 1, n_cells - 1)]);
+        const int64_t c = c0 + kCpw * wave;
         const bool real = k < n_t;
-        inl = make_int2(real && c < n_cells, real && c + 1 < n_cells);
+#pragma unroll
+        for (int i = 0; i < kCpw; ++i) {
+            raw[i] = rl[min(c + i, n_cells - 1)];
+            inl[i] = real && c + i < n_cells;
+        }
     };
 
     // Q^T of pair `pair`: lane holds row `col` (rows >= R read row 0 and are never written),
@@ -230,7 +239,7 @@ decode_mma16_kernel(const SegParams p) {
         for (int blk = 0; blk < NB; ++blk)
             q[blk] = __builtin_bit_cast(half8_t, *reinterpret_cast<const uint4 *>(qrow + 32 * blk + 8 * grp));
     };
-    auto fetch = [&](Stage16<D> &st, uint32_t k) __attribute__((always_inline)) {
+    auto fetch = [&](Stage16<D, ROWS> &st, uint32_t k) __attribute__((always_inline)) {
         const bool real = k < n_t;
         int pair;
         int64_t c0;
@@ -243,7 +252,10 @@ decode_mma16_kernel(const SegParams p) {
         const uint8_t *kbase = p.k + (int64_t)(hg * kHW) * p.k_s2;
         const uint8_t *vbase = p.v + (int64_t)(hg * kHW) * p.v_s2;
         if constexpr (ROWS) {
-            int r = (fcell & 1) ? (st.rin.y ? st.rid.y : -1) : (st.rin.x ? st.rid.x : -1);
+            int r = -1;
+#pragma unroll
+            for (int i = 0; i < kCpw; ++i)
+                if (fcell % kCpw == i) r = st.rin[i] ? st.rid[i] : -1;
             if (r >= p.n_pool) r = -1;  // outside the pool: read nothing, like padding
             st.ok = r >= 0;
             const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
@@ -287,7 +299,7 @@ decode_mma16_kernel(const SegParams p) {
     };
     Meta mnext;                                 // the task stashed last: computed next
     half8_t qnext[GD::kQStage ? NB : 1];         // its Q^T when it starts a new pair
-    auto stash = [&](const Stage16<D> &st, int buf) __attribute__((always_inline)) {
+    auto stash = [&](const Stage16<D, ROWS> &st, int buf) __attribute__((always_inline)) {
         uint8_t *dk = s_k + buf * kStage + fcell * kS + 16 * fsub;
         uint8_t *dv = s_v + buf * kStage + fcell * kS + 16 * fsub;
 #pragma unroll
@@ -347,32 +359,42 @@ decode_mma16_kernel(const SegParams p) {
         const uint8_t *kw = s_k + buf * kStage + head * kRowB;  // this head's K row of cell j at kw + j*kS
         const uint8_t *vw = s_v + buf * kStage + head * kRowB;
 
-        // ---- Q.K: D[key 4*grp + ii][row col]
-        float4_t dq = float4_t{0.f, 0.f, 0.f, 0.f};
+        // ---- Q.K: D[key 16*u + 4*grp + ii][row col] for each 16-key tile u of the chunk
+        float4_t dq[NU];
 #pragma unroll
-        for (int blk = 0; blk < NB; ++blk) {
-            const uint4 a = *reinterpret_cast<const uint4 *>(kw + col * kS + 64 * blk + 16 * grp);
-            dq = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a), qb[blk], dq, 0, 0, 0);
+        for (int u = 0; u < NU; ++u) {
+            dq[u] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int blk = 0; blk < NB; ++blk) {
+                const uint4 a = *reinterpret_cast<const uint4 *>(kw + (16 * u + col) * kS + 64 * blk + 16 * grp);
+                dq[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a), qb[blk], dq[u], 0, 0, 0);
+            }
         }
 
         // ---- visibility: the key is data (chunk end, padding row), the causal rule, the mask
-        const int4 okv = *reinterpret_cast<const int4 *>(&s_ok[buf][4 * grp]);
-        const uint2 mv = p.mask ? *reinterpret_cast<const uint2 *>(&s_mask[buf][min(col, R - 1)][4 * grp]) : make_uint2(0, 0);
-        const half2_t m01 = __builtin_bit_cast(half2_t, mv.x), m23 = __builtin_bit_cast(half2_t, mv.y);
-        const float mvals[4] = {(float)m01[0], (float)m01[1], (float)m23[0], (float)m23[1]};
-        const int okk[4] = {okv.x, okv.y, okv.z, okv.w};
-        float s[4];
+        float s[NU][4];
+        float mx = -INFINITY;
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-            bool vis = okk[ii] != 0;
-            if (!ROWS && p.q_pos0 >= 0 && p.pos0 + mt_.c0 + 4 * grp + ii > p.q_pos0 + qi_row) vis = false;
-            float x = p.cap_l2 != 0.f ? softcap_log2(dq[ii], p.cap_cs, p.cap_l2) : dq[ii] * c;
-            if (p.mask) x = fmaf(mvals[ii], kLog2e, x);
-            s[ii] = vis ? x : -INFINITY;
+        for (int u = 0; u < NU; ++u) {
+            const int k0 = 16 * u + 4 * grp;  // the lane's first key in the chunk
+            const int4 okv = *reinterpret_cast<const int4 *>(&s_ok[buf][k0]);
+            const uint2 mv = p.mask ? *reinterpret_cast<const uint2 *>(&s_mask[buf][min(col, R - 1)][k0]) : make_uint2(0, 0);
+            const half2_t m01 = __builtin_bit_cast(half2_t, mv.x), m23 = __builtin_bit_cast(half2_t, mv.y);
+            const float mvals[4] = {(float)m01[0], (float)m01[1], (float)m23[0], (float)m23[1]};
+            const int okk[4] = {okv.x, okv.y, okv.z, okv.w};
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) {
+                bool vis = okk[ii] != 0;
+                if (!ROWS && p.q_pos0 >= 0 && p.pos0 + mt_.c0 + k0 + ii > p.q_pos0 + qi_row) vis = false;
+                float x = p.cap_l2 != 0.f ? softcap_log2(dq[u][ii], p.cap_cs, p.cap_l2) : dq[u][ii] * c;
+                if (p.mask) x = fmaf(mvals[ii], kLog2e, x);
+                s[u][ii] = vis ? x : -INFINITY;
+                mx = fmaxf(mx, s[u][ii]);
+            }
         }
 
         // ---- online softmax of row `col` (exact: the max is raised whenever a chunk exceeds it)
-        const float mt = fold_rows_max(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])));
+        const float mt = fold_rows_max(mx);
         if (__builtin_amdgcn_ballot_w64(mt > mrun)) {
             const float mnew = fmaxf(mt, mrun);
             const float a = (mnew > mrun) ? __builtin_amdgcn_exp2f(mrun - mnew) : 1.0f;
@@ -382,23 +404,30 @@ decode_mma16_kernel(const SegParams p) {
             for (int dt = 0; dt < NT; ++dt) oacc[dt] *= a;
         }
         const float msub = mrun == -INFINITY ? 0.f : mrun;
-        float pr[4];
+        half4_t pb[NU];
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-            pr[ii] = __builtin_amdgcn_exp2f(s[ii] - msub);
-            lrow += pr[ii];
+        for (int u = 0; u < NU; ++u) {
+            float pr[4];
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) {
+                pr[ii] = __builtin_amdgcn_exp2f(s[u][ii] - msub);
+                lrow += pr[ii];
+            }
+            pb[u] = half4_t{(_Float16)pr[0], (_Float16)pr[1], (_Float16)pr[2], (_Float16)pr[3]};
         }
-        const half4_t pb = half4_t{(_Float16)pr[0], (_Float16)pr[1], (_Float16)pr[2], (_Float16)pr[3]};
 
-        // ---- P.V: A = V^T tile (head_dim 16*dt + col, keys 4*grp + 0..3) by a transposing read:
-        // lane col of group grp fetches key 4*grp + col / 4, head_dim 16*dt + 4*(col % 4) + 0..3
-        // (this wave's tiles: dt = NT*part .. NT*part + NT - 1)
+        // ---- P.V: A = V^T tile (head_dim 16*dt + col, keys 16*u + 4*grp + 0..3) by a transposing
+        // read: lane col of group grp fetches key 16*u + 4*grp + col / 4, head_dim 16*dt +
+        // 4*(col % 4) + 0..3 (this wave's tiles: dt = NT*part .. NT*part + NT - 1)
         const uint8_t *vr = vw + (4 * grp + (col >> 2)) * kS + 8 * (col & 3) + 32 * NT * part;
 #pragma unroll
-        for (int dt = 0; dt < NT; ++dt) {
-            const short4_t t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) short4_t *)(vr + 32 * dt));
-            oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(half4_t, t), pb, oacc[dt], 0, 0, 0);
+        for (int u = 0; u < NU; ++u) {
+#pragma unroll
+            for (int dt = 0; dt < NT; ++dt) {
+                const short4_t t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) short4_t *)(vr + 16 * u * kS + 32 * dt));
+                oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(half4_t, t), pb[u], oacc[dt], 0, 0, 0);
+            }
         }
     };
 
@@ -409,7 +438,7 @@ decode_mma16_kernel(const SegParams p) {
     // pairs with no exit in between (a phantom task has no visible key), so that every path
     // into the loop head has the same loads in flight.
     if (n_t > 0) {
-        Stage16<D> sa, sb;  // tasks 2i (sa) and 2i + 1 (sb)
+        Stage16<D, ROWS> sa, sb;  // tasks 2i (sa) and 2i + 1 (sb)
         sa.mk = sb.mk = 0;
         if constexpr (ROWS) {
             rows_of(0, sa.rid, sa.rin);
@@ -459,6 +488,16 @@ hipError_t launch16_d(const SegParams &p, hipStream_t s, int *occupancy) {
 }
 
 }  // namespace
+
+int decode_mma16_chunk(int d, bool rows) {
+    switch (d) {
+        case 64: return rows ? G16<64, true>::kCh : G16<64>::kCh;
+        case 128: return rows ? G16<128, true>::kCh : G16<128>::kCh;
+        case 256: return rows ? G16<256, true>::kCh : G16<256>::kCh;
+        case 512: return rows ? G16<512, true>::kCh : G16<512>::kCh;
+        default: return 16;
+    }
+}
 
 int decode_mma16_heads(int d, int dv) {
     if (d != dv) return 0;

@@ -95,8 +95,10 @@ hipError_t launch_decode_mma(const SegParams &p, hipStream_t s, int *occupancy);
 // cell-major KV heads (8 at head dims 64 and 128, 4 at 256, 2 at 512) with gqa * n_q <= 8 rows
 // per head; the same occupancy convention.
 bool decode_mma16_ok(const SegParams &p);
-// KV heads per cell group of the binary16 matrix-core kernel at head dims (d, dv) (0: none).
+// KV heads per cell group of the binary16 matrix-core kernel at head dims (d, dv) (0: none),
+// and the cells of one of its tasks (chunks) at head dim d over a segment or a row list.
 int decode_mma16_heads(int d, int dv);
+int decode_mma16_chunk(int d, bool rows);
 // Whether the decode kernel for p is the persistent one: n_splits workgroups then take equal
 // contiguous runs of the 16-cell chunks of all (sequence, head group) pairs, numbered
 // pair-major, and cells_per_split is unused.

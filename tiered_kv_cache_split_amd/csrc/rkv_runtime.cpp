@@ -353,9 +353,10 @@ void seg_plan(const rkv_ctx *ctx, int64_t n_cells, const SegParams &p, bool mfma
         cps = (n_cells + want - 1) / want;
         cps = std::max<int64_t>(kpi, (cps + kpi - 1) / kpi * kpi);
     } else if (persistent) {
-        // binary16 matrix-core kernel: one resident workgroup per slot, each taking every G-th
-        // 16-cell chunk of all (sequence, head group) pairs
-        const int64_t tasks = (int64_t)p.n_seq * (p.n_head_kv / p.cell_hw) * ((n_cells + 15) / 16);
+        // binary16 matrix-core kernel: one resident workgroup per slot, each taking a contiguous
+        // run of the chunks (16 or 32 cells) of all (sequence, head group) pairs
+        const int64_t ch = decode_mma16_chunk(p.d, p.rows != nullptr);
+        const int64_t tasks = (int64_t)p.n_seq * (p.n_head_kv / p.cell_hw) * ((n_cells + ch - 1) / ch);
         const int64_t slots = (int64_t)std::max(1, cell_occupancy) * ctx->n_cu;
         const int64_t g = ctx->splits_override > 0 ? ctx->splits_override : slots;
         n_splits = (int)std::max<int64_t>(1, std::min(g, tasks));
