@@ -234,3 +234,45 @@ def test_random_rows_head_dims(run, seed):
         run.ctx.set_softcap(0.0)
     Oref, Lref = oracle_rows(w, rows=np.where(rows < n_pool, rows, -1), softcap=cap)
     assert_close(O, L, Oref, Lref, what=f"random rows {seed}")
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_random_binary16_cell_groups(run, seed):
+    """The persistent binary16 matrix-core kernel at head dims 64, 128, 256 and 512: random
+    head groups (KV heads a multiple of the group of 8, 8, 4 or 2), up to 8 rows per KV head,
+    lengths, window + tail splits (lifted or on the device), masks, a small causal prefill in a
+    quarter of the cases, and soft-caps; every case but prefill at 128 must run on that kernel."""
+    rng = np.random.default_rng(13000 + seed)
+    d = int(rng.choice([64, 128, 256, 512]))
+    hw = {64: 8, 128: 8, 256: 4, 512: 2}[d]
+    n_head_kv = hw * int(rng.choice([1, 1, 2]))
+    n_q = int(rng.choice([1, 1, 2]))
+    gqa = int(rng.choice([g for g in (1, 2, 3, 4, 5, 8) if g * n_q <= 8]))
+    n_kv = int(rng.integers(1, 3000))
+    tail = str(rng.choice(["host", "device", "none"]))
+    wc = n_kv if tail == "none" else int(rng.integers(0, n_kv + 1))
+    if wc == n_kv:
+        tail = "none"
+    tile = int(rng.integers(1, 1500))
+    q, k, v = gen.draw_qkv(rng, n_head_kv * gqa, n_q, n_head_kv, n_kv, d=d, dv=d, k_type=gen.TYPE_F16,
+                           v_type=gen.TYPE_F16)
+    w = dict(n_head=n_head_kv * gqa, n_head_kv=n_head_kv, q=q, k=k, v=v, k_type=gen.TYPE_F16,
+             v_type=gen.TYPE_F16, d=d, dv=d, scale=1 / np.sqrt(d), n_kv=n_kv, wc=wc, tile_kv=tile)
+    mask = gen.random_mask_f16(rng, n_q, n_kv, p_hidden=0.3) if rng.random() < 0.5 else None
+    prefill = n_q > 1 and rng.random() < 0.5
+    q_pos0 = int(rng.integers(0, n_kv)) if prefill else -1
+    cap = draw_softcap(700 + seed)
+    step(f"random binary16 cell groups seed {seed}: d {d} heads {n_head_kv}x{gqa} n_q {n_q} n_kv {n_kv} wc {wc} "
+         f"tile {tile} tail {tail} mask {mask is not None} prefill {prefill} q_pos0 {q_pos0} softcap {cap:.3f}")
+    run.ctx.set_softcap(cap)
+    try:
+        O, L = run.decode(w, tail=None if tail == "none" else tail, mask=mask, prefill=prefill, q_pos0=q_pos0)
+        # (prefill at 128 runs on the matrix-core prefill kernel)
+        assert run.ctx.stats()["kernel_variant"] == (1 if prefill and d == 128 else 4)
+    finally:
+        run.ctx.set_softcap(0.0)
+    full = mask if mask is not None else np.zeros((n_q, n_kv), np.float16)
+    if prefill:
+        full = np.where(oracle.causal_mask(n_q, n_kv, q_pos0) == -np.inf, -np.inf, full.astype(np.float64))
+    Oref, Lref = oracle_decode(w, mask=full if (prefill or mask is not None) else None, softcap=cap)
+    assert_close(O, L, Oref, Lref, what=f"random binary16 cell groups {seed}")

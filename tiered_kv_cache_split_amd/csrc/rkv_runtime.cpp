@@ -1205,8 +1205,9 @@ int rkv_attn_decode(rkv_ctx *ctx, const rkv_tensor *q, const rkv_tensor *k_win, 
 int rkv_attn_prefill(rkv_ctx *ctx, const rkv_tensor *q, const rkv_tensor *k_win, const rkv_tensor *v_win,
                      const rkv_tensor *k_tail, const rkv_tensor *v_tail, const rkv_tensor *mask, int64_t wc,
                      int64_t tile_kv, float scale, int64_t q_pos0, float *o, float *lse, void *stream) {
-    // head dim 128 runs on the matrix-core prefill kernel; the other head dims on the vector
-    // kernel for them, in row groups of 8 (it takes the causal rule and the mask alike)
+    // head dim 128 runs on the matrix-core prefill kernel; the other head dims on the decode
+    // kernels (matrix-core where they take the types and head groups, else the vector kernel),
+    // which take the causal rule and the mask alike
     const bool mfma = !q || q->ne[0] == kHeadDim;
     return attn_window_tail(ctx, q, k_win, v_win, k_tail, v_tail, mask, wc, tile_kv, scale, q_pos0, mfma, o, lse,
                             static_cast<hipStream_t>(stream), nullptr, 0, true);
