@@ -233,11 +233,12 @@ int rkv_attn_decode_noalloc(const rkv_tensor *q, const rkv_tensor *k, const rkv_
  * tail streaming op serves a multi-token chunk, with the mask sliced at the global key
  * position, a per-tile flash attention and an LSE per tile for the combine; patch 0102,
  * commit message: 106k-token prefills through lifted tail tiles).  The same arguments as
- * rkv_attn_decode for any n_q, computed at head dim 128 with MFMA f16 tiles: q8_0 K codes
- * and q4_0 V nibbles enter the matrix cores as exact binary16 integers and their block scales
- * are applied in fp32 (K) or folded into the softmax weights (V); the other head dims run on
- * the decode kernels (the matrix-core decode kernel when n_q * gqa <= 8 and the heads form its
- * groups, else the vector kernel in groups of 8 rows).  The tail is always computed on the GPU
+ * rkv_attn_decode for any n_q, computed at head dim 128 with MFMA f16 tiles: q8_0 K enters
+ * the matrix cores as the exact two-part binary16 sum hi + lo = d*q, q4_0 V as the exact
+ * binary16 integers n - 8 with the block scales folded into the softmax weights; the other
+ * head dims run on the decode kernels (the q8_0 / q4_0 matrix-core kernel for any n_q * gqa,
+ * in row groups of 16, and the binary16 one for n_q * gqa <= 8, when the KV heads form their
+ * groups; else the vector kernel in groups of 8 rows).  The tail is always computed on the GPU
  * (RKV_TAIL_HOST applies to decode only).  q_pos0 >= 0 makes it
  * causal: query i sits at absolute position q_pos0 + i and sees keys at positions
  * <= q_pos0 + i (in addition to the mask); q_pos0 == -1 uses the mask alone. */
