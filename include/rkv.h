@@ -84,14 +84,16 @@ enum rkv_lift_mode {
     RKV_LIFT_KERNEL = 2,/* a copy kernel on the copy stream (at most 64 workgroups) reads the
                            pinned bytes 8 at a time: no hand-off between a DMA engine and the
                            compute queue, which dominates small lifts                        */
-    RKV_LIFT_AUTO = 3,  /* default: decode lifts with the copy kernel, prefill with the DMA
-                           engine (the copy kernel's workgroups would slow the MFMA kernel
-                           it overlaps)                                                      */
-    RKV_LIFT_DIRECT = 4 /* contrast only (patch 0102, commit message: the kernel reading the
-                           pinned tail at word granularity): no lift; the segment kernels read
-                           a pinned tail in place through its device view, in their own
-                           access order; a device tail and the host tail partial are
-                           unaffected                                                        */
+    RKV_LIFT_AUTO = 3,  /* default: decode reads a small tail in place (RKV_LIFT_DIRECT's
+                           read; at most rkv_set_direct_tail_max bytes, 8 MiB by default, and
+                           up to 8 rows per KV head) and lifts larger ones with the copy
+                           kernel; prefill lifts with the DMA engine (the copy kernel's
+                           workgroups would slow the MFMA kernel it overlaps)               */
+    RKV_LIFT_DIRECT = 4 /* no lift (patch 0102, commit message: the kernel reading the pinned
+                           tail at word granularity, there the slow contrast to the bulk
+                           lift): the segment kernels read a pinned tail in place through
+                           its device view, in their own access order; a device tail and the
+                           host tail partial are unaffected                                  */
 };
 
 enum rkv_residency_mode {
@@ -165,6 +167,14 @@ int rkv_get_stats(const rkv_ctx *ctx, rkv_stats *out);
  * read of patch 0102's commit message against the bulk copies; it is never the default.
  * rkv_stats.lift_mode reports the mode a call used. */
 int rkv_set_lift_mode(rkv_ctx *ctx, int mode);
+
+/* Under RKV_LIFT_AUTO, decode calls read a pinned tail of at most `bytes` bytes (its K plus
+ * V bytes) in place instead of lifting it, when there are at most 8 query rows per KV head
+ * (each segment kernel then reads every tail byte once).  Default 8 MiB: on the 128-dim
+ * decode the in-place read beat the lift below that (one launch and one hand-off between
+ * streams fewer) and the two were even above it.  0 lifts every tail; bytes < 0 is
+ * RKV_ERR_ARG. */
+int rkv_set_direct_tail_max(rkv_ctx *ctx, int64_t bytes);
 
 /* Override the split-K factor of window/pool segments (0 = automatic). */
 int rkv_set_splits(rkv_ctx *ctx, int splits);

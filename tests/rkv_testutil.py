@@ -86,6 +86,9 @@ class Runner:
         import tiered_kv_cache_split_amd as rkv
         self.rkv = rkv
         self.ctx = rkv.Context(0)
+        # the tests lift every pinned tail under the automatic lift mode; the in-place read
+        # the automatic mode gives small decode tails is tested where it is switched back on
+        self.ctx.set_direct_tail_max(0)
 
     def decode(self, w, wc=None, tile_kv=None, tail="host", mask=None, layout="cell", prefill=False,
                q_pos0=-1, stream=None, keep=None):

@@ -55,6 +55,7 @@ def test_null_context_is_an_argument_error(lib):
     assert lib.rkv_attn_rows(None, None, None, None, None, 0, None, 1.0, None, None, None) == _lib.RKV_ERR_ARG
     assert lib.rkv_attn_prefill(None, None, None, None, None, None, None, 0, 1, 1.0, -1, None, None, None) == _lib.RKV_ERR_ARG
     assert lib.rkv_reserve(None, 0, 0, 2, 0) == _lib.RKV_ERR_ARG
+    assert lib.rkv_set_direct_tail_max(None, 0) == _lib.RKV_ERR_ARG
     assert b"ctx" in lib.rkv_last_error()
     d = ctypes.c_void_p()
     assert lib.rkv_tail_lift(None, None, 0, 0, 0, ctypes.byref(d), None) == _lib.RKV_ERR_ARG

@@ -41,19 +41,25 @@ def reserve_for(ctx, w):
     ctx.reserve(kb, vb, 2, 2048 * w["n_head"] * w["q"].shape[1] * 130)
 
 
-@pytest.mark.parametrize("num,sd,tail", [(3, 32, True), (1, 1, True), (2, 16, False)])
-def test_decode_graph_replays(num, sd, tail):
+@pytest.mark.parametrize("num,sd,tail,in_place", [(3, 32, True, False), (1, 1, True, False), (2, 16, False, False),
+                                                  (1, 1, True, True)])
+def test_decode_graph_replays(num, sd, tail, in_place):
+    """in_place: the 2 MB tail read in place by the segment kernels (the automatic mode's choice
+    for a small decode tail); otherwise lifted through the ring."""
     import tiered_kv_cache_split_amd as rkv
     w = gen.make_workload(num, scale_down=sd)
     if not tail:
         w["wc"] = w["n_kv"]
     ctx = rkv.Context(0)
+    ctx.set_direct_tail_max(8 << 20 if in_place else 0)
     try:
         reserve_for(ctx, w)
         t, d = tensors(rkv, w, tail)
         step(f"graph: eager decode workload {num}/{sd} tail={tail}")
         decode(ctx, w, t, d)
         torch.cuda.synchronize()
+        if tail:
+            assert (ctx.stats()["lift_mode"] == rkv.RKV_LIFT_DIRECT) == in_place
         O0, L0 = t["o"].cpu().numpy().copy(), t["lse"].cpu().numpy().copy()
         Oref, Lref = oracle_decode(w)
         assert_close(O0, L0, Oref, Lref, what="eager")
@@ -90,6 +96,7 @@ def test_growth_inside_capture_is_refused():
     from tiered_kv_cache_split_amd import _lib
     w = gen.make_workload(1)
     ctx = rkv.Context(0)
+    ctx.set_direct_tail_max(0)  # the tails below are lifted (the small ones would be read in place)
     try:
         t, d = tensors(rkv, w, True)
         g = torch.cuda.CUDAGraph()

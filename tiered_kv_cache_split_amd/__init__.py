@@ -126,6 +126,9 @@ class Context:
     def set_lift_mode(self, mode: int):
         check(self.lib.rkv_set_lift_mode(self.h, int(mode)), "rkv_set_lift_mode")
 
+    def set_direct_tail_max(self, nbytes: int):
+        check(self.lib.rkv_set_direct_tail_max(self.h, int(nbytes)), "rkv_set_direct_tail_max")
+
     def set_splits(self, splits: int):
         check(self.lib.rkv_set_splits(self.h, int(splits)), "rkv_set_splits")
 

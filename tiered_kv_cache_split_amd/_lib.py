@@ -48,6 +48,7 @@ SIGNATURES = {
     "rkv_destroy": (None, [vp]),
     "rkv_get_stats": (ctypes.c_int, [vp, ctypes.POINTER(RkvStats)]),
     "rkv_set_lift_mode": (ctypes.c_int, [vp, ctypes.c_int]),
+    "rkv_set_direct_tail_max": (ctypes.c_int, [vp, ctypes.c_int64]),
     "rkv_set_splits": (ctypes.c_int, [vp, ctypes.c_int]),
     "rkv_set_lift_timing": (ctypes.c_int, [vp, ctypes.c_int]),
     "rkv_lift_timing_ms": (ctypes.c_int, [vp, ctypes.POINTER(ctypes.c_float),

@@ -159,6 +159,12 @@ int same_kv_shape(const rkv_tensor *a, const rkv_tensor *b, const char *what) {
 
 }  // namespace
 
+// Decode tails up to this many bytes (K plus V) are read in place under RKV_LIFT_AUTO: below
+// it the in-place read beat the copy-kernel lift on the 128-dim decode (1.7 MB q8_0 / q4_0
+// tail: 56 against 82 us per call; 4.2 MB binary16: 107 against 121 us), above it the two
+// trade places (16.8 MB binary16: 361 against 347 us).
+constexpr int64_t kDirectTailMaxDefault = (int64_t)8 << 20;
+
 struct rkv_ctx {
     int device = 0;
     int n_cu = 256;
@@ -185,6 +191,8 @@ struct rkv_ctx {
     int2 *pair_range = nullptr;     // row lists: slot range of each pair's partials (up to 1024 pairs)
     size_t pair_range_cap = 0;      // bytes
     int lift_mode = RKV_LIFT_AUTO;
+    // RKV_LIFT_AUTO reads a decode tail of at most this many bytes (K plus V) in place
+    int64_t direct_tail_max = kDirectTailMaxDefault;
     int splits_override = 0;
     float softcap = 0.f;  // logit soft-cap of later calls (0: none)
     // host tail partial (RKV_TAIL_HOST): pinned staging of Q, the tail's mask columns and the
@@ -580,9 +588,15 @@ int attn_window_tail(rkv_ctx *ctx, const rkv_tensor *q, const rkv_tensor *k_win,
     // partial computed on the host cores)
     // (prefill always computes the tail on the GPU)
     const bool host_tail = n_tail > 0 && tail_kind != Mem::Device && ctx->tail_mode == RKV_TAIL_HOST && !mfma && !prefill;
-    // RKV_LIFT_DIRECT (contrast only): the segment kernels read a pinned tail in place through
-    // its device view, in their own access order, with no lift
-    const bool direct = n_tail > 0 && tail_kind == Mem::PinnedHost && !host_tail && ctx->lift_mode == RKV_LIFT_DIRECT;
+    // In place: the segment kernels read a pinned tail through its device view, in their own
+    // access order, with no lift -- always under RKV_LIFT_DIRECT, and under RKV_LIFT_AUTO for a
+    // small decode tail whose cells each kernel reads once (up to 8 rows per KV head), where
+    // the lift's extra launch and hand-off between streams cost more than the copy saves
+    const int64_t tail_bytes = n_tail * n_head_kv * (row_bytes(kref->type, d) + row_bytes(vref->type, dv));
+    const bool auto_direct = ctx->lift_mode == RKV_LIFT_AUTO && !mfma && !prefill && gqa * n_q <= kMaxRowsVec &&
+                             tail_bytes <= ctx->direct_tail_max;
+    const bool direct = n_tail > 0 && tail_kind == Mem::PinnedHost && !host_tail &&
+                        (ctx->lift_mode == RKV_LIFT_DIRECT || auto_direct);
     const bool lifted = n_tail > 0 && tail_kind == Mem::PinnedHost && !host_tail && !direct;
     const int64_t n_tiles = lifted ? (n_tail + tile_kv - 1) / tile_kv : 0;
     TailGeom gk{}, gv{};
@@ -659,8 +673,8 @@ int attn_window_tail(rkv_ctx *ctx, const rkv_tensor *q, const rkv_tensor *k_win,
 
     ctx->stats = rkv_stats{};
     ctx->stats.kernel_variant = mfma ? RKV_KERNEL_PREFILL_MFMA : RKV_KERNEL_DECODE_HEAD;
-    // lift mode of this call: the automatic choice lifts decode tails with the copy kernel and
-    // prefill tails with the DMA engine
+    // lift mode of this call: the automatic choice reads small decode tails in place (above),
+    // lifts the other decode tails with the copy kernel and prefill tails with the DMA engine
     const int lift_mode = direct ? RKV_LIFT_DIRECT
                                  : (ctx->lift_mode == RKV_LIFT_AUTO || ctx->lift_mode == RKV_LIFT_DIRECT)
                                        ? (mfma ? RKV_LIFT_BULK : RKV_LIFT_KERNEL)
@@ -1113,6 +1127,13 @@ int rkv_set_lift_mode(rkv_ctx *ctx, int mode) {
         mode != RKV_LIFT_DIRECT)
         return fail(RKV_ERR_ARG, "unknown lift mode %d", mode);
     ctx->lift_mode = mode;
+    return RKV_OK;
+}
+
+int rkv_set_direct_tail_max(rkv_ctx *ctx, int64_t bytes) {
+    if (!ctx) return fail(RKV_ERR_ARG, "ctx is NULL");
+    if (bytes < 0) return fail(RKV_ERR_ARG, "bytes < 0");
+    ctx->direct_tail_max = bytes;
     return RKV_OK;
 }
 
