@@ -58,7 +58,7 @@ struct G16 {
     static constexpr int kRowB = 2 * D;                  // bytes of one head's K or V row
     static constexpr int kCell = HW * kRowB;             // bytes of one cell of the group
     // cells per chunk: 16 (one 16-key tile), and 32 over a segment at 64, where a cell is half
-    // as large, so that a chunk keeps 64 KB of K and V (0.60 of the HBM roofline against 0.55
+    // as large, so that a chunk keeps 64 KB of K and V (0.61 of the HBM roofline against 0.55
     // with 16); row lists keep 16, as a workgroup's run of a list's chunks is short and twice
     // the chunk made its first load and last compute cost more than they saved (41 against 37 us)
     static constexpr int kCh = (kCell >= 2048 || ROWS) ? 16 : 32;
@@ -73,8 +73,9 @@ struct G16 {
     // Q^T of a new pair rides in the stage registers up to 128; wider heads load it when the
     // pair starts (a workgroup meets one or two pairs)
     static constexpr bool kQStage = D <= 128;
-    // resident waves per SIMD the registers allow: one workgroup per CU (at 64 two would fit
-    // the LDS, but within 128 registers the kernel spilled and ran 9% slower)
+    // resident waves per SIMD the registers allow: one workgroup per CU (at 64 with 16-cell
+    // chunks two would fit the LDS, but within 128 registers the kernel spilled and ran 9%
+    // slower over a segment and 15% slower over row lists)
     static constexpr int kWavesPerEu = 2;
     static_assert(kCell % (16 * kTpc) == 0 && HW * SV == 8 && kS % 128 == 32, "thread and bank mapping");
 };
