@@ -403,7 +403,7 @@ def measure(args, num):
         out["roofline"] = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_F16_PEAK_TFLOPS,
                            "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4),
                            "traffic": traffic_from_profiles("prefill_seg_q8q4_nq512_nkv106496", "prefill")
-                           if w["d"] == 128 else None,
+                           if w["d"] == 128 and args.kv_types == "own" else None,
                            "kernel": (DECODE_KERNELS.get(stats.get("kernel_variant"), "segment kernel")
                                       if w["d"] != 128 else "prefill_seg_kernel") + " (all segments of a step)",
                            "kernel_ms_per_step": round(kern_total_ms, 4)}
