@@ -138,3 +138,55 @@ def test_growth_inside_capture_is_refused():
     finally:
         torch.cuda.synchronize()
         ctx.close()
+
+
+@pytest.mark.parametrize("kt,vt", [(gen.TYPE_F16, gen.TYPE_F16), (gen.TYPE_Q8_0, gen.TYPE_Q4_0)])
+def test_rows_graph_replays_with_new_lists(kt, vt):
+    """A captured rkv_attn_rows replayed after the lists in its buffer changed (longer, shorter,
+    all padding): every replay rescans the lists' extents and must match the oracle for its own
+    lists."""
+    import tiered_kv_cache_split_amd as rkv
+    from rkv_testutil import oracle_rows
+    rng = gen.rng_for(91)
+    n_pool, n_kv = 2500, 2000
+    q = gen.draw_normal(rng, (2, 32, 1, 128)).astype(np.float16)
+    k = gen.pack(kt, gen.draw_normal(rng, (n_pool, 8, 128)))
+    v = gen.pack(vt, gen.draw_normal(rng, (n_pool, 8, 128)))
+    ctx = rkv.Context(0)
+    try:
+        ctx.reserve(0, 0, 0, 1024 * 2 * 32 * 130)
+        qd, kd, vd = dev(q), dev(k), dev(v)
+        kvr = dev(gen.rows_lists(rng, n_pool, (1500, 1900), n_kv, shuffle=True))
+        o = torch.empty((2, 1, 32, 128), dtype=torch.float32, device="cuda")
+        lse = torch.empty((2, 1, 32), dtype=torch.float32, device="cuda")
+
+        def call(stream=None):
+            ctx.attn_rows(rkv.q_desc(qd), rkv.kv_desc(kd, kt), rkv.kv_desc(vd, vt), kvr, n_kv, None,
+                          1 / np.sqrt(128), o, lse, stream=stream)
+
+        step(f"graph rows {kt}/{vt}: eager call, then capture")
+        call()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g, stream=side):
+                call(stream=side)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        for lengths in ((2000, 300), (100, 1700), (0, 0), (1999, 2000)):
+            rows = gen.rows_lists(rng, n_pool, lengths, n_kv, shuffle=True)
+            kvr.copy_(torch.from_numpy(rows))
+            o.fill_(float("nan"))
+            torch.cuda.synchronize()
+            step(f"graph rows {kt}/{vt}: replay with lists {lengths}")
+            g.replay()
+            torch.cuda.synchronize()
+            w = dict(q=q, k=k, v=v, kv_rows=rows, mask=None, k_type=kt, v_type=vt, scale=1 / np.sqrt(128))
+            Oref, Lref = oracle_rows(w, mask=None)
+            assert_close(o.cpu().numpy(), lse.cpu().numpy(), Oref, Lref, what=f"graph rows {lengths}")
+        del g
+    finally:
+        torch.cuda.synchronize()
+        ctx.close()

@@ -188,3 +188,28 @@ def test_rows_entries_outside_the_pool(run, n_head, n_head_kv, kt, vt, variant):
     assert run.ctx.stats()["kernel_variant"] == variant
     Oref, Lref = oracle_rows(w, mask=None, rows=np.where(rows < n_pool, rows, -1))
     assert_close(O, L, Oref, Lref, what="rows past the pool")
+
+
+@pytest.mark.parametrize("kt,vt", [(gen.TYPE_F16, gen.TYPE_F16), (gen.TYPE_Q8_0, gen.TYPE_Q4_0)])
+def test_rows_extent_shrinks_between_calls(kt, vt):
+    """One context, lists that end earlier (or later) from call to call, down to all padding:
+    each call's extent scan bounds the walk by its own lists, so every call matches the oracle."""
+    r = Runner()
+    try:
+        rng = gen.rng_for(77)
+        n_pool = 3000
+        q = gen.draw_normal(rng, (2, 32, 1, 128)).astype(np.float16)
+        k = gen.pack(kt, gen.draw_normal(rng, (n_pool, 8, 128)))
+        v = gen.pack(vt, gen.draw_normal(rng, (n_pool, 8, 128)))
+        for lengths in ((2500, 2000), (900, 1300), (40, 0), (0, 0), (2400, 17)):
+            rows = gen.rows_lists(rng, n_pool, lengths, 2500, shuffle=True)
+            w = dict(q=q, k=k, v=v, kv_rows=rows, mask=None, k_type=kt, v_type=vt, scale=1 / np.sqrt(128))
+            step(f"rows extent: types {kt}/{vt} lists {lengths} on one context")
+            O, L = r.rows(w, mask=None)
+            Oref, Lref = oracle_rows(w, mask=None)
+            assert_close(O, L, Oref, Lref, what=f"rows extent {lengths}")
+            for b, n in enumerate(lengths):
+                if n == 0:
+                    assert np.all(O[b] == 0) and np.all(L[b] == -np.inf)
+    finally:
+        r.ctx.close()

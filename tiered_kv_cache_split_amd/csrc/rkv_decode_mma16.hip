@@ -126,15 +126,18 @@ decode_mma16_kernel(const SegParams p) {
     const int n_pairs = p.n_seq * n_hgrp;
     const uint32_t G = (uint32_t)p.n_splits, j = blockIdx.x;
     if (j >= G) return;  // the grid is exactly G workgroups; slot j must exist
-    // ---- task offsets of the pairs: chunks of each pair up to its extent, scanned in LDS
-    for (int pr = tid; pr < n_pairs; pr += kNT) {
+    // ---- task offsets of the pairs: chunks of each pair up to its extent, scanned in LDS (one
+    // wave per pair; its lanes read the kRowExtentParts = 64 pieces of the extent at once)
+    static_assert(kRowExtentParts == 64, "one extent piece per lane");
+    for (int pr = wave; pr < n_pairs; pr += kNT / 64) {
         int64_t ext = p.n_cells;
         if (p.row_extent) {
-            int e = 0;
-            for (int q = 0; q < kRowExtentParts; ++q) e = max(e, p.row_extent[(pr / n_hgrp) * kRowExtentParts + q]);
+            int e = p.row_extent[(pr / n_hgrp) * kRowExtentParts + lane];
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) e = max(e, __shfl_xor(e, o, 64));
             ext = min(ext, (int64_t)e);
         }
-        s_off[pr + 1] = (uint32_t)((ext + kCh - 1) / kCh);
+        if (lane == 0) s_off[pr + 1] = (uint32_t)((ext + kCh - 1) / kCh);
     }
     if (tid == 0) s_off[0] = 0;
     __syncthreads();

@@ -127,7 +127,7 @@ hipError_t launch_empty_partials(float *partials, int64_t n_rows, hipStream_t s)
 // Row-list extents in kRowExtentParts pieces per sequence: the maximum of
 // extent[b * kRowExtentParts + 0 .. kRowExtentParts - 1] is 1 + the last index j < n_kv with
 // rows[j + rows_s*b] >= 0, or 0 (n_seq sequences)
-constexpr int kRowExtentParts = 16;
+constexpr int kRowExtentParts = 64;  // one wave's lanes (the binary16 kernel reads them so)
 hipError_t launch_row_extent(const int32_t *rows, int64_t rows_s, int64_t n_kv, int n_seq, int32_t *extent, hipStream_t s);
 hipError_t launch_uva_read(const void *host_src, void *dst, int64_t nbytes, hipStream_t s);
 // Bulk copy kernel over pinned host memory (source and destination 8-byte aligned).
