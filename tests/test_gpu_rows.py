@@ -213,3 +213,22 @@ def test_rows_extent_shrinks_between_calls(kt, vt):
                     assert np.all(O[b] == 0) and np.all(L[b] == -np.inf)
     finally:
         r.ctx.close()
+
+
+def test_rows_more_pairs_than_the_persistent_kernel_plans(run):
+    """1100 sequences of one head group (more than the 1024 sequence and head-group pairs the
+    persistent binary16 kernel plans): the call falls back to the per-head vector kernel and
+    still matches the oracle."""
+    rng = gen.rng_for(55)
+    n_seq, n_pool = 1100, 300
+    lengths = tuple(int(x) for x in rng.integers(0, 24, size=n_seq))
+    rows = gen.rows_lists(rng, n_pool, lengths, 24, shuffle=True)
+    q = gen.draw_normal(rng, (n_seq, 16, 1, 128)).astype(np.float16)
+    k = gen.pack_f16(gen.draw_normal(rng, (n_pool, 8, 128)))
+    v = gen.pack_f16(gen.draw_normal(rng, (n_pool, 8, 128)))
+    w = dict(q=q, k=k, v=v, kv_rows=rows, mask=None, k_type=gen.TYPE_F16, v_type=gen.TYPE_F16, scale=1 / np.sqrt(128))
+    step("rows f16: 1100 sequences of 8 KV heads")
+    O, L = run.rows(w, mask=None)
+    assert run.ctx.stats()["kernel_variant"] == 0
+    Oref, Lref = oracle_rows(w, mask=None)
+    assert_close(O, L, Oref, Lref, what="rows 1100 sequences")

@@ -342,6 +342,13 @@ int use_cell_kernel(const Seg &sg, const SegParams &p, int k_type, int v_type) {
     const int64_t lim = (int64_t)1 << 31;
     if (p.rows && (p.n_pool * sg.k_s1 >= lim || p.n_pool * sg.v_s1 >= lim || sg.k_s1 >= (1 << 24) || sg.v_s1 >= (1 << 24)))
         return 0;
+    // binary16 groups the persistent kernel cannot plan (more than 1024 sequence and head-group
+    // pairs) go to the vector kernels (the cell kernel of pairs of heads at 128 has no such limit)
+    if (k_type == T_F16 && v_type == T_F16 && !(hw == 2 && p.d == kHeadDim)) {
+        SegParams pc = p;
+        pc.cell_hw = hw;
+        if (!decode_mma16_ok(pc)) return 0;
+    }
     return hw;
 }
 
