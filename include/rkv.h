@@ -24,7 +24,8 @@
  * {64, 128, 256, 512} and at 576 / 512 when the KV heads form groups the kernel takes (8 or 4
  * at 64; 8, 4 or 2 at 128; 4, 2 or 1 at 256; 1 at 512 and 576), with n_q * gqa <= 8 at 128 and
  * any number of rows at the other head dims; binary16 K and V at head_dim == dv in {64, 128,
- * 256, 512} in groups of 8, 8, 4 and 2 KV heads with n_q * gqa <= 8.  Prefill at 128 runs on
+ * 256, 512} in groups of 8, 8, 4 and 2 KV heads, and at 576 / 512 one head at a time, with
+ * n_q * gqa <= 8.  Prefill at 128 runs on
  * the matrix-core prefill kernel; everything else on the vector kernels; rkv_lse_merge takes
  * dv 64, 128, 256 or 512; Q in F16;
  * K in F16 or Q8_0; V in F16 or Q4_0.  Q8_0 is a 34-byte block (binary16 scale d, 32
@@ -135,7 +136,8 @@ enum rkv_kernel_variant {
     RKV_KERNEL_DECODE_CELL = 2,       /* vector decode over cell-major groups of KV heads           */
     RKV_KERNEL_DECODE_CELL_MFMA = 3,  /* matrix-core decode over cell-major q8_0/q4_0 head groups   */
     RKV_KERNEL_DECODE_CELL_MFMA16 = 4, /* persistent matrix-core decode over cell groups of binary16
-                                          heads: 8 at head dims 64 and 128, 4 at 256, 2 at 512
+                                          heads: 8 at head dims 64 and 128, 4 at 256, 2 at 512,
+                                          1 at 576 / 512
                                           (windows, tail tiles, row lists)                         */
     RKV_KERNEL_DECODE_HD = 5           /* vector decode for head dims other than 128 (window + tail) */
 };
@@ -267,8 +269,8 @@ int rkv_attn_prefill(rkv_ctx *ctx, const rkv_tensor *q,
  *           kv_rows[j + n_kv*b].  A negative row, or one >= n_pool, is padding: it
  *           contributes nothing and is never dereferenced.  Cell-major q8_0 K / q4_0 V pools
  *           run on the matrix-core decode kernel at every supported head dim, binary16 pools
- *           in groups of 8, 8, 4 or 2 KV heads at head dims 64, 128, 256 or 512 (dk = dv) on
- *           the persistent binary16 kernel, the rest on the vector kernels.
+ *           in groups of 8, 8, 4 or 2 KV heads at head dims 64, 128, 256 or 512 (dk = dv), and
+ *           at 576 / 512, on the persistent binary16 kernel, the rest on the vector kernels.
  *   mask    F16 [>= n_kv, >= n_q, 1, n_seq] additive, device, or NULL.
  *   o       float32 [128, n_head, n_q, n_seq]; lse float32 [n_head, n_q, n_seq] or NULL. */
 int rkv_attn_rows(rkv_ctx *ctx, const rkv_tensor *q, const rkv_tensor *k_pool,

@@ -31,8 +31,8 @@ def test_rows(run, dk, dv, kt, vt):
     step(f"rows head dims {dk}/{dv} types {kt}/{vt}")
     O, L = run.rows(w)
     # q8_0 / q4_0 pools: the matrix-core kernel; binary16 pools of 8 KV heads: the binary16
-    # matrix-core kernel where dk = dv, the vector kernel at 576 / 512
-    assert run.ctx.stats()["kernel_variant"] == (3 if kt == gen.TYPE_Q8_0 else 4 if dk == dv else 5)
+    # matrix-core kernel
+    assert run.ctx.stats()["kernel_variant"] == (3 if kt == gen.TYPE_Q8_0 else 4)
     Oref, Lref = oracle_rows(w)
     assert_close(O, L, Oref, Lref, what=f"rows d={dk}/{dv}")
 

@@ -37,10 +37,10 @@ def test_window_plus_lifted_tail(run, dk, dv, kt, vt, lift):
     step(f"head dims {dk}/{dv}: k={kt} v={vt} wc=1333 tile=700 lift {lift}")
     O, L = run.decode(w, wc=1333, tile_kv=700, tail="host")
     st = run.ctx.stats()
-    # q8_0 / q4_0 (512 / 512 and 576 / 512): the matrix-core kernel; binary16 at 512 / 512 (two
-    # KV heads, one cell group): the binary16 matrix-core kernel; the other pairs: vector
+    # q8_0 / q4_0 (512 / 512 and 576 / 512): the matrix-core kernel; binary16 (two KV heads: one
+    # cell group at 512, two groups of one at 576): the binary16 matrix-core kernel; mixed: vector
     mma = (kt, vt) == (gen.TYPE_Q8_0, gen.TYPE_Q4_0)
-    mma16 = (kt, vt) == (gen.TYPE_F16, gen.TYPE_F16) and dk == dv
+    mma16 = (kt, vt) == (gen.TYPE_F16, gen.TYPE_F16)
     assert st["kernel_variant"] == (3 if mma else 4 if mma16 else 5) and st["n_tail_tiles"] == -(-(4096 - 1333) // 700)
     assert O.shape == (1, 8, dv)
     Oref, Lref = oracle_decode(w)

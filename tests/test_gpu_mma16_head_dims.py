@@ -1,6 +1,7 @@
 """The binary16 matrix-core decode kernel at head dims 64, 256 and 512 (dk = dv; cell groups of
 8, 4 and 2 KV heads, so one, two and four waves per KV head, each with its share of the P.V
-tiles) against the fp64 oracle: several head groups, one to eight rows per KV head, the window
+tiles) and at the 576 / 512 pair (one KV head per workgroup, eight waves) against the fp64
+oracle: several head groups, one to eight rows per KV head, the window
 + lifted or device tail split, masks with an empty row, ragged lengths, the causal rule of a
 small prefill call, the soft-cap, the full 131072-cell shape of the 128K decode, and row lists
 (holes, entries past the pool, an empty list) over several sequences, so that the persistent
@@ -22,8 +23,8 @@ F16 = gen.TYPE_F16
 
 
 def workload(num, d, **kw):
-    """Workload `num` with binary16 K and V at head dim d."""
-    return gen.make_workload(num, d=d, k_type=F16, v_type=F16, **kw)
+    """Workload `num` with binary16 K and V at Q / K head dim d (V head dim 512 with 576)."""
+    return gen.make_workload(num, d=d, dv=512 if d == 576 else d, k_type=F16, v_type=F16, **kw)
 
 
 @pytest.fixture(scope="module")
@@ -39,6 +40,7 @@ SHAPES = [
     (64, 40, 8, 1), (64, 64, 16, 2), (64, 8, 8, 1),
     (256, 40, 8, 1), (256, 16, 4, 2), (256, 12, 4, 1),
     (512, 16, 2, 1), (512, 6, 2, 1), (512, 8, 4, 2),
+    (576, 16, 2, 1), (576, 3, 1, 2), (576, 8, 1, 1),
 ]
 
 
@@ -52,7 +54,7 @@ def test_groups_and_rows(run, d, n_head, n_head_kv, n_q):
     assert_close(O, L, Oref, Lref, what=f"f16 mma d={d} {n_head}/{n_head_kv} n_q {n_q}")
 
 
-@pytest.mark.parametrize("d", [64, 256, 512])
+@pytest.mark.parametrize("d", [64, 256, 512, 576])
 @pytest.mark.parametrize("tail", ["device", "host"])
 def test_ragged_mask_and_empty_row(run, d, tail):
     w = dict(workload(2, d, scale_down=32, n_head=32, n_head_kv=8, n_q=2))  # 8 rows per KV head
@@ -68,7 +70,7 @@ def test_ragged_mask_and_empty_row(run, d, tail):
     assert np.all(O[1] == 0) and np.all(L[1] == -np.inf)
 
 
-@pytest.mark.parametrize("d", [64, 256, 512])
+@pytest.mark.parametrize("d", [64, 256, 512, 576])
 def test_small_prefill_causal(run, d):
     """Two queries of four heads per KV head (8 rows): the causal rule inside the kernel."""
     w = workload(2, d, scale_down=32, n_head=32, n_head_kv=8, n_q=2)
@@ -81,7 +83,7 @@ def test_small_prefill_causal(run, d):
     assert_close(O, L, Oref, Lref, what=f"f16 mma d={d} causal")
 
 
-@pytest.mark.parametrize("d", [64, 256, 512])
+@pytest.mark.parametrize("d", [64, 256, 512, 576])
 def test_softcap(run, d):
     w = workload(2, d, scale_down=32, n_head=16, n_head_kv=8)
     run.ctx.set_softcap(20.0)
@@ -95,7 +97,7 @@ def test_softcap(run, d):
     assert_close(O, L, Oref, Lref, what=f"f16 mma d={d} softcap")
 
 
-@pytest.mark.parametrize("d", [64, 256, 512])
+@pytest.mark.parametrize("d", [64, 256, 512, 576])
 def test_full_size_128k(run, d):
     """131072 resident cells, 40/8 heads, in the launch configuration of the 128K decode at this
     head dim; the query heads of KV heads 0, 3 and 7 against the oracle over all keys."""
@@ -109,7 +111,7 @@ def test_full_size_128k(run, d):
 
 
 @pytest.mark.parametrize("d,n_head,n_head_kv,n_q", [(64, 32, 8, 1), (256, 32, 8, 1), (256, 16, 4, 2), (512, 16, 8, 1),
-                                                    (512, 8, 2, 1)])
+                                                    (512, 8, 2, 1), (576, 16, 2, 1), (576, 8, 1, 1)])
 def test_row_lists(run, d, n_head, n_head_kv, n_q):
     """Four shuffled lists with -1 holes, entries past the pool and -1 padding at the end, the
     lists' own mask; an entry past the pool reads nothing, so the oracle takes it as -1."""
@@ -129,7 +131,7 @@ def test_row_lists(run, d, n_head, n_head_kv, n_q):
     assert_close(O, L, Oref, Lref, what=f"f16 mma rows d={d}")
 
 
-@pytest.mark.parametrize("d", [64, 512])
+@pytest.mark.parametrize("d", [64, 512, 576])
 def test_row_lists_softcap_and_empty_list(run, d):
     """Soft-cap over a binary16 pool; one sequence's list is all padding (O = 0, LSE = -inf)."""
     w = workload(4, d, scale_down=16, n_head=32, n_head_kv=8)

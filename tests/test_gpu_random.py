@@ -238,13 +238,14 @@ def test_random_rows_head_dims(run, seed):
 
 @pytest.mark.parametrize("seed", range(20))
 def test_random_binary16_cell_groups(run, seed):
-    """The persistent binary16 matrix-core kernel at head dims 64, 128, 256 and 512: random
-    head groups (KV heads a multiple of the group of 8, 8, 4 or 2), up to 8 rows per KV head,
+    """The persistent binary16 matrix-core kernel at head dims 64, 128, 256, 512 and 576 / 512:
+    random head groups (KV heads a multiple of the group of 8, 8, 4, 2 or 1), up to 8 rows per KV head,
     lengths, window + tail splits (lifted or on the device), masks, a small causal prefill in a
     quarter of the cases, and soft-caps; every case but prefill at 128 must run on that kernel."""
     rng = np.random.default_rng(13000 + seed)
-    d = int(rng.choice([64, 128, 256, 512]))
-    hw = {64: 8, 128: 8, 256: 4, 512: 2}[d]
+    d = int(rng.choice([64, 128, 256, 512, 576]))
+    dv = 512 if d == 576 else d
+    hw = {64: 8, 128: 8, 256: 4, 512: 2, 576: 1}[d]
     n_head_kv = hw * int(rng.choice([1, 1, 2]))
     n_q = int(rng.choice([1, 1, 2]))
     gqa = int(rng.choice([g for g in (1, 2, 3, 4, 5, 8) if g * n_q <= 8]))
@@ -254,10 +255,10 @@ def test_random_binary16_cell_groups(run, seed):
     if wc == n_kv:
         tail = "none"
     tile = int(rng.integers(1, 1500))
-    q, k, v = gen.draw_qkv(rng, n_head_kv * gqa, n_q, n_head_kv, n_kv, d=d, dv=d, k_type=gen.TYPE_F16,
+    q, k, v = gen.draw_qkv(rng, n_head_kv * gqa, n_q, n_head_kv, n_kv, d=d, dv=dv, k_type=gen.TYPE_F16,
                            v_type=gen.TYPE_F16)
     w = dict(n_head=n_head_kv * gqa, n_head_kv=n_head_kv, q=q, k=k, v=v, k_type=gen.TYPE_F16,
-             v_type=gen.TYPE_F16, d=d, dv=d, scale=1 / np.sqrt(d), n_kv=n_kv, wc=wc, tile_kv=tile)
+             v_type=gen.TYPE_F16, d=d, dv=dv, scale=1 / np.sqrt(d), n_kv=n_kv, wc=wc, tile_kv=tile)
     mask = gen.random_mask_f16(rng, n_q, n_kv, p_hidden=0.3) if rng.random() < 0.5 else None
     prefill = n_q > 1 and rng.random() < 0.5
     q_pos0 = int(rng.integers(0, n_kv)) if prefill else -1

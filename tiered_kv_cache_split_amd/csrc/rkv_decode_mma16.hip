@@ -19,6 +19,9 @@
 // Head dims 64, 128, 256 and 512 (dk = dv): a KV head group of HW heads (8, 8, 4, 2) keeps the
 // cell at 1 or 2 KB per cache, and each head gets SV = 8 / HW waves (1, 1, 2, 4), each of which
 // computes the head's Q.K (the same scores in every one of them) and 1 / SV of its P.V tiles.
+// The 576 / 512 pair takes one KV head per workgroup (8 waves, 1152-byte K and 1024-byte V
+// rows, the K stage with its own cell stride; a thread's last K unit slot lies past the cell
+// and is left out).
 //
 // Workgroup = 8 waves, wave w = KV head g0 + w / SV (P.V part w % SV) of the (sequence, group of
 // HW KV heads) pair of its current task; the kernel is persistent (work split below).  A chunk
@@ -50,13 +53,16 @@ constexpr int kMaxR = 8;               // query rows per KV head
 constexpr uint32_t kNowhere = 0x80000000u;  // buffer offset past every range: reads zero
 constexpr int kMaxPairs = 1024;        // (sequence, head group) pairs of one launch
 
-// Geometry at head dim D, over a segment of cells or (ROWS) a row list.
+// Geometry at Q / K head dim D (V: the same, or 512 with 576), over a segment of cells or
+// (ROWS) a row list.
 template <int D, bool ROWS = false>
 struct G16 {
-    static constexpr int HW = D <= 128 ? 8 : 1024 / D;  // KV heads per workgroup
+    static constexpr int DV = D == 576 ? 512 : D;        // V head dim
+    static constexpr int HW = D == 576 ? 1 : D <= 128 ? 8 : 1024 / D;  // KV heads per workgroup
     static constexpr int SV = 8 / HW;                    // waves per KV head
-    static constexpr int kRowB = 2 * D;                  // bytes of one head's K or V row
-    static constexpr int kCell = HW * kRowB;             // bytes of one cell of the group
+    static constexpr int kRowK = 2 * D, kRowV = 2 * DV;  // bytes of one head's K / V row
+    static constexpr int kCellK = HW * kRowK;            // bytes of one cell of the group: K
+    static constexpr int kCell = HW * kRowV;             // and V
     // cells per chunk: 16 (one 16-key tile), and 32 over a segment at 64, where a cell is half
     // as large, so that a chunk keeps 64 KB of K and V (0.61 of the HBM roofline against 0.55
     // with 16); row lists keep 16, as a workgroup's run of a list's chunks is short and twice
@@ -64,12 +70,14 @@ struct G16 {
     static constexpr int kCh = (kCell >= 2048 || ROWS) ? 16 : 32;
     static constexpr int kTpc = kNT / kCh;               // threads per cell (32 or 16)
     static constexpr int kCpw = 64 / kTpc;               // cells staged by one wave (2 or 4)
-    static constexpr int kS = kCell + 32;                // LDS cell stride: 8 mod 32 banks
-    static constexpr int kStage = kCh * kS;              // bytes of one LDS stage of one cache
-    static constexpr int kM = kCell / 16 / kTpc;         // 16-byte units per thread, cache and chunk
+    static constexpr int kS = kCell + 32, kSK = kCellK + 32;  // LDS cell strides (V, K): 8 mod 32 banks
+    static constexpr int kStage = kCh * kS, kStageK = kCh * kSK;  // bytes of one LDS stage of V / K
+    static constexpr int kM = kCell / 16 / kTpc;         // 16-byte units per thread and chunk: V
+    static constexpr int kMK = (kCellK / 16 + kTpc - 1) / kTpc;  // and K (the last slot may fall past
+    static constexpr bool kKPart = kMK * kTpc * 16 != kCellK;    // the cell, at 576: then unused)
     static constexpr int NB = D / 32;                    // Q.K steps of 32 head_dim values
-    static constexpr int NT = D / 16 / SV;               // P.V tiles of 16 head_dim values per wave
-    static constexpr int kPs = 2 + D;                    // partial row: M, S, VKQ[D]
+    static constexpr int NT = DV / 16 / SV;              // P.V tiles of 16 head_dim values per wave
+    static constexpr int kPs = 2 + DV;                   // partial row: M, S, VKQ[DV]
     // Q^T of a new pair rides in the stage registers up to 128; wider heads load it when the
     // pair starts (a workgroup meets one or two pairs)
     static constexpr bool kQStage = D <= 128;
@@ -77,7 +85,8 @@ struct G16 {
     // chunks two would fit the LDS, but within 128 registers the kernel spilled and ran 9%
     // slower over a segment and 15% slower over row lists)
     static constexpr int kWavesPerEu = 2;
-    static_assert(kCell % (16 * kTpc) == 0 && HW * SV == 8 && kS % 128 == 32, "thread and bank mapping");
+    static_assert(kCell % (16 * kTpc) == 0 && HW * SV == 8 && kS % 128 == 32 && kSK % 128 == 32,
+                  "thread and bank mapping");
 };
 
 // One chunk (task) in registers: this thread's K and V units, the mask value it stages,
@@ -90,7 +99,7 @@ struct Meta {
 };
 template <int D, bool ROWS>
 struct Stage16 {
-    uint4 k[G16<D, ROWS>::kM], v[G16<D, ROWS>::kM];
+    uint4 k[G16<D, ROWS>::kMK], v[G16<D, ROWS>::kM];
     half8_t q[G16<D, ROWS>::kQStage ? G16<D, ROWS>::NB : 1];
     uint32_t mk;
     int ok;
@@ -110,10 +119,11 @@ template <int D, int R, bool ROWS>
 __global__ void __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(G16<D, ROWS>::kWavesPerEu)))
 decode_mma16_kernel(const SegParams p) {
     using GD = G16<D, ROWS>;
-    constexpr int kHW = GD::HW, SV = GD::SV, kRowB = GD::kRowB, kCell = GD::kCell, kS = GD::kS, kStage = GD::kStage;
+    constexpr int kHW = GD::HW, SV = GD::SV, kRowK = GD::kRowK, kRowV = GD::kRowV, kS = GD::kS, kStage = GD::kStage;
+    constexpr int kSK = GD::kSK, kStageK = GD::kStageK, kCellK = GD::kCellK, kMK = GD::kMK;
     constexpr int kM = GD::kM, NB = GD::NB, NT = GD::NT, kPs = GD::kPs;
     constexpr int kCh = GD::kCh, kTpc = GD::kTpc, kCpw = GD::kCpw, NU = kCh / 16;  // NU 16-key tiles per chunk
-    __shared__ __attribute__((aligned(16))) uint8_t s_k[2 * kStage];
+    __shared__ __attribute__((aligned(16))) uint8_t s_k[2 * kStageK];
     __shared__ __attribute__((aligned(16))) uint8_t s_v[2 * kStage];
     __shared__ __attribute__((aligned(16))) int s_ok[2][kCh];                 // key is visible data
     __shared__ __attribute__((aligned(16))) _Float16 s_mask[2][kMaxR][kCh];   // mask[row][key]
@@ -271,8 +281,9 @@ decode_mma16_kernel(const SegParams p) {
             const uint32_t ko = r >= 0 ? __umul24((uint32_t)r, (uint32_t)p.k_s1) + 16u * fsub : kNowhere;
             const uint32_t vo = r >= 0 ? __umul24((uint32_t)r, (uint32_t)p.v_s1) + 16u * fsub : kNowhere;
 #pragma unroll
-            for (int m = 0; m < kM; ++m)
-                st.k[m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, ko + 16 * kTpc * m, 0, 0));
+            for (int m = 0; m < kMK; ++m)
+                if (!GD::kKPart || 16 * (fsub + kTpc * m) < kCellK)
+                    st.k[m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, ko + 16 * kTpc * m, 0, 0));
 #pragma unroll
             for (int m = 0; m < kM; ++m)
                 st.v[m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, vo + 16 * kTpc * m, 0, 0));
@@ -287,8 +298,9 @@ decode_mma16_kernel(const SegParams p) {
             const uint32_t ko = (uint32_t)fcell * (uint32_t)p.k_s1 + 16u * fsub;
             const uint32_t vo = (uint32_t)fcell * (uint32_t)p.v_s1 + 16u * fsub;
 #pragma unroll
-            for (int m = 0; m < kM; ++m)
-                st.k[m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, ko + 16 * kTpc * m, 0, 0));
+            for (int m = 0; m < kMK; ++m)
+                if (!GD::kKPart || 16 * (fsub + kTpc * m) < kCellK)
+                    st.k[m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, ko + 16 * kTpc * m, 0, 0));
 #pragma unroll
             for (int m = 0; m < kM; ++m)
                 st.v[m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, vo + 16 * kTpc * m, 0, 0));
@@ -304,13 +316,13 @@ decode_mma16_kernel(const SegParams p) {
     Meta mnext;                                 // the task stashed last: computed next
     half8_t qnext[GD::kQStage ? NB : 1];         // its Q^T when it starts a new pair
     auto stash = [&](const Stage16<D, ROWS> &st, int buf) __attribute__((always_inline)) {
-        uint8_t *dk = s_k + buf * kStage + fcell * kS + 16 * fsub;
+        uint8_t *dk = s_k + buf * kStageK + fcell * kSK + 16 * fsub;
         uint8_t *dv = s_v + buf * kStage + fcell * kS + 16 * fsub;
 #pragma unroll
-        for (int m = 0; m < kM; ++m) {
-            *reinterpret_cast<uint4 *>(dk + 16 * kTpc * m) = st.k[m];
-            *reinterpret_cast<uint4 *>(dv + 16 * kTpc * m) = st.v[m];
-        }
+        for (int m = 0; m < kMK; ++m)
+            if (!GD::kKPart || 16 * (fsub + kTpc * m) < kCellK) *reinterpret_cast<uint4 *>(dk + 16 * kTpc * m) = st.k[m];
+#pragma unroll
+        for (int m = 0; m < kM; ++m) *reinterpret_cast<uint4 *>(dv + 16 * kTpc * m) = st.v[m];
         if (fsub == 0) s_ok[buf][fcell] = st.ok;
         if (mthread) s_mask[buf][mrow][mkey] = __builtin_bit_cast(_Float16, (uint16_t)st.mk);
         mnext = st.meta;
@@ -360,8 +372,8 @@ decode_mma16_kernel(const SegParams p) {
 #pragma unroll
             for (int dt = 0; dt < NT; ++dt) oacc[dt] = float4_t{0.f, 0.f, 0.f, 0.f};
         }
-        const uint8_t *kw = s_k + buf * kStage + head * kRowB;  // this head's K row of cell j at kw + j*kS
-        const uint8_t *vw = s_v + buf * kStage + head * kRowB;
+        const uint8_t *kw = s_k + buf * kStageK + head * kRowK;  // this head's K row of cell j at kw + j*kSK
+        const uint8_t *vw = s_v + buf * kStage + head * kRowV;
 
         // ---- Q.K: D[key 16*u + 4*grp + ii][row col] for each 16-key tile u of the chunk
         float4_t dq[NU];
@@ -370,7 +382,7 @@ decode_mma16_kernel(const SegParams p) {
             dq[u] = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int blk = 0; blk < NB; ++blk) {
-                const uint4 a = *reinterpret_cast<const uint4 *>(kw + (16 * u + col) * kS + 64 * blk + 16 * grp);
+                const uint4 a = *reinterpret_cast<const uint4 *>(kw + (16 * u + col) * kSK + 64 * blk + 16 * grp);
                 dq[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a), qb[blk], dq[u], 0, 0, 0);
             }
         }
@@ -499,11 +511,13 @@ int decode_mma16_chunk(int d, bool rows) {
         case 128: return rows ? G16<128, true>::kCh : G16<128>::kCh;
         case 256: return rows ? G16<256, true>::kCh : G16<256>::kCh;
         case 512: return rows ? G16<512, true>::kCh : G16<512>::kCh;
+        case 576: return rows ? G16<576, true>::kCh : G16<576>::kCh;
         default: return 16;
     }
 }
 
 int decode_mma16_heads(int d, int dv) {
+    if (d == 576) return dv == 512 ? G16<576>::HW : 0;
     if (d != dv) return 0;
     switch (d) {
         case 64: return G16<64>::HW;
@@ -533,6 +547,7 @@ hipError_t launch_decode_mma16(const SegParams &p, hipStream_t s, int *occupancy
         case 128: return launch16_d<128>(p, s, occupancy);
         case 256: return launch16_d<256>(p, s, occupancy);
         case 512: return launch16_d<512>(p, s, occupancy);
+        case 576: return launch16_d<576>(p, s, occupancy);
         default: return hipErrorInvalidValue;
     }
 }
