@@ -147,3 +147,38 @@ def test_row_lists_softcap_and_empty_list(run, d):
     Oref, Lref = oracle_rows(w, mask=None, rows=rows, softcap=25.0)
     assert_close(O, L, Oref, Lref, what=f"f16 mma rows softcap d={d}")
     assert np.all(O[2] == 0) and np.all(L[2] == -np.inf)
+
+
+# (d, n_head, n_head_kv, n_q): more than 8 rows per KV head over a segment: row groups of 16 (the
+# last one ragged), one workgroup per (row group, split, head group)
+ROW_GROUPS = [(64, 64, 8, 2), (64, 40, 8, 5), (256, 48, 4, 3), (512, 20, 2, 3), (576, 16, 1, 2), (576, 40, 2, 1)]
+
+
+@pytest.mark.parametrize("d,n_head,n_head_kv,n_q", ROW_GROUPS)
+def test_row_groups(run, d, n_head, n_head_kv, n_q):
+    w = workload(2, d, scale_down=64, n_head=n_head, n_head_kv=n_head_kv, n_q=n_q)  # n_kv 2048
+    mask = gen.random_mask_f16(np.random.default_rng(d + n_head), n_q, w["n_kv"], p_hidden=0.2)
+    step(f"f16 mma row groups d={d} heads {n_head}/{n_head_kv} n_q {n_q} ({n_q * n_head // n_head_kv} rows per KV head)")
+    O, L = run.decode(w, wc=1300, tile_kv=400, tail="host", mask=mask)
+    assert run.ctx.stats()["kernel_variant"] == MMA16
+    Oref, Lref = oracle_decode(w, mask=mask)
+    assert_close(O, L, Oref, Lref, what=f"f16 mma row groups d={d} {n_head}/{n_head_kv} n_q {n_q}")
+
+
+@pytest.mark.parametrize("d", [64, 256, 512, 576])
+def test_prefill_row_groups_causal(run, d):
+    """A prefill chunk of 24 queries of 4 heads per KV head (96 rows: six row groups) at the end
+    of a window + lifted tail, causal, with a mask hiding some keys and one query seeing none."""
+    w = workload(5, d, scale_down=64, n_head=32, n_head_kv=8)  # n_kv 1664
+    n_q = 24
+    w["q"] = w["q"][:, -n_q:]
+    q_pos0 = w["n_kv"] - n_q
+    mask = gen.random_mask_f16(np.random.default_rng(d), n_q, w["n_kv"], p_hidden=0.1)
+    mask[5, :] = -np.inf
+    step(f"f16 mma prefill row groups d={d}: {n_q} queries, causal, masked")
+    O, L = run.decode(w, wc=1000, tile_kv=256, tail="host", mask=mask, prefill=True, q_pos0=q_pos0)
+    assert run.ctx.stats()["kernel_variant"] == MMA16
+    full = np.where(oracle.causal_mask(n_q, w["n_kv"], q_pos0) == -np.inf, -np.inf, mask.astype(np.float64))
+    Oref, Lref = oracle_decode(w, mask=full)
+    assert_close(O, L, Oref, Lref, what=f"f16 prefill row groups d={d}")
+    assert np.all(O[5] == 0) and np.all(L[5] == -np.inf)

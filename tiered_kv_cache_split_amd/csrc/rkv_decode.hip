@@ -763,6 +763,9 @@ hipError_t dispatch_decode(const SegParams &p, int k_type, int v_type, hipStream
     if (p.cell_hw > 0 && k_type == T_Q8_0 && v_type == T_Q4_0)
         return decode_mma_ok(p) ? launch_decode_mma(p, s, occupancy) : hipErrorInvalidValue;
     if (k_type == T_Q8_0 && v_type == T_Q4_0) return launch_decode_t<T_Q8_0, T_Q4_0>(p, R, s, occupancy);
+    // binary16 cell groups: the matrix-core kernel for any number of rows it takes
+    if (p.cell_hw > 0 && k_type == T_F16 && v_type == T_F16 && decode_mma16_ok(p))
+        return launch_decode_mma16(p, s, occupancy);
     if (k_type == T_F16 && v_type == T_F16) return launch_decode_t<T_F16, T_F16>(p, R, s, occupancy);
     if (k_type == T_Q8_0 && v_type == T_F16) return launch_decode_t<T_Q8_0, T_F16>(p, R, s, occupancy);
     if (k_type == T_F16 && v_type == T_Q4_0) return launch_decode_t<T_F16, T_Q4_0>(p, R, s, occupancy);
@@ -777,9 +780,10 @@ int cell_heads(int dk, int dv, int k_type, int v_type, int n_head_kv, int R, boo
     // and row lists (up to 8 rows per KV head at 128, any number at the other head dims)
     if (k_type == T_Q8_0 && v_type == T_Q4_0)
         return (dk == kHeadDim && R > kMaxRowsVec) ? 0 : decode_mma_heads(dk, dv, n_head_kv, R);
-    // binary16 in cell groups (8 KV heads at 64 and 128, 4 at 256, 2 at 512): the persistent
-    // matrix-core kernel, also for row lists
-    if (k_type == T_F16 && v_type == T_F16 && R <= kMaxRowsVec) {
+    // binary16 in cell groups (8 KV heads at 64 and 128, 4 at 256, 2 at 512, 1 at 576 / 512):
+    // the matrix-core kernel -- persistent up to 8 rows per KV head (also for row lists), in row
+    // groups of 16 over segments beyond that (head dims other than 128)
+    if (k_type == T_F16 && v_type == T_F16 && (R <= kMaxRowsVec || (!rows && dk != kHeadDim))) {
         const int hw = decode_mma16_heads(dk, dv);
         if (hw > 0 && n_head_kv % hw == 0) return hw;
     }
@@ -796,7 +800,13 @@ int cell_blocks_per_cu(const SegParams &p, int k_type, int v_type) {
 }
 
 bool decode_kernel_persistent(const SegParams &p, int k_type, int v_type) {
-    return p.cell_hw > 0 && k_type == T_F16 && v_type == T_F16 && decode_mma16_ok(p);
+    return p.cell_hw > 0 && k_type == T_F16 && v_type == T_F16 && p.gqa * p.n_q <= kMaxRowsVec && decode_mma16_ok(p);
+}
+
+int cell_row_groups(const SegParams &p, int k_type, int v_type) {
+    if (k_type == T_Q8_0 && v_type == T_Q4_0) return decode_mma_row_groups(p);
+    const int R = p.gqa * p.n_q;
+    return R > kMaxRowsVec ? (R + 15) / 16 : 1;  // binary16: row groups of 16 beyond 8 rows
 }
 
 int decode_kernel_variant(const SegParams &p, int k_type, int v_type) {

@@ -123,22 +123,47 @@ decode_mma16_kernel(const SegParams p) {
     constexpr int kSK = GD::kSK, kStageK = GD::kStageK, kCellK = GD::kCellK, kMK = GD::kMK;
     constexpr int kM = GD::kM, NB = GD::NB, NT = GD::NT, kPs = GD::kPs;
     constexpr int kCh = GD::kCh, kTpc = GD::kTpc, kCpw = GD::kCpw, NU = kCh / 16;  // NU 16-key tiles per chunk
+    // R > kMaxR: row groups of 16 (more rows per KV head than the persistent form takes, over a
+    // segment): workgroup = (row group, split, head group, sequence), not persistent
+    constexpr bool RGM = R > kMaxR;
+    static_assert(!(RGM && ROWS), "row groups over segments only");
     __shared__ __attribute__((aligned(16))) uint8_t s_k[2 * kStageK];
     __shared__ __attribute__((aligned(16))) uint8_t s_v[2 * kStage];
-    __shared__ __attribute__((aligned(16))) int s_ok[2][kCh];                 // key is visible data
-    __shared__ __attribute__((aligned(16))) _Float16 s_mask[2][kMaxR][kCh];   // mask[row][key]
-    __shared__ uint32_t s_off[kMaxPairs + 1];  // first task of each pair; s_off[n_pairs] = tasks
+    __shared__ __attribute__((aligned(16))) int s_ok[2][kCh];                         // key is visible data
+    __shared__ __attribute__((aligned(16))) _Float16 s_mask[2][RGM ? 16 : kMaxR][kCh];  // mask[row][key]
+    __shared__ uint32_t s_off[RGM ? 1 : kMaxPairs + 1];  // first task of each pair; s_off[n_pairs] = tasks
 
     const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int col = lane & 15, grp = lane >> 4;
     const int head = wave / SV, part = wave % SV;  // KV head in the group, P.V part
     const int n_hgrp = p.n_head_kv / kHW;
     const int n_pairs = p.n_seq * n_hgrp;
-    const uint32_t G = (uint32_t)p.n_splits, j = blockIdx.x;
-    if (j >= G) return;  // the grid is exactly G workgroups; slot j must exist
+    // row-group form: this workgroup's rows R0 .. R0 + RR - 1, pair, split and cells
+    int R0 = 0, RR = R, rg_pair = 0;
+    int64_t c_beg = 0, c_lim = p.n_cells;
+    uint32_t G = (uint32_t)p.n_splits, j = blockIdx.x;
+    if constexpr (RGM) {
+        const int R_all = p.gqa * p.n_q, n_rg = (R_all + 15) >> 4;
+        int bid = blockIdx.x;
+        const int rg = bid % n_rg;
+        bid /= n_rg;
+        j = (uint32_t)(bid % p.n_splits);  // the split: partial slot slot0 + j
+        bid /= p.n_splits;
+        rg_pair = bid;  // (sequence, head group) pair: b * n_hgrp + hgrp
+        R0 = 16 * rg;
+        RR = min(16, R_all - R0);
+        c_beg = (int64_t)j * p.cells_per_split;
+        c_lim = min(p.n_cells, c_beg + (int64_t)p.cells_per_split);
+    } else {
+        if (j >= G) return;  // the grid is exactly G workgroups; slot j must exist
+    }
     // ---- task offsets of the pairs: chunks of each pair up to its extent, scanned in LDS (one
     // wave per pair; its lanes read the kRowExtentParts = 64 pieces of the extent at once)
     static_assert(kRowExtentParts == 64, "one extent piece per lane");
+    uint32_t n_tasks = 0, t_lo = 0, n_t = 0;  // all tasks, this workgroup's first and count
+    if constexpr (RGM) {
+        n_t = c_lim > c_beg ? (uint32_t)((c_lim - c_beg + kCh - 1) / kCh) : 0;
+    } else {
     for (int pr = wave; pr < n_pairs; pr += kNT / 64) {
         int64_t ext = p.n_cells;
         if (p.row_extent) {
@@ -166,9 +191,9 @@ decode_mma16_kernel(const SegParams p) {
         }
         __syncthreads();
     }
-    const uint32_t n_tasks = s_off[n_pairs];
-    const uint32_t t_lo = (uint32_t)((uint64_t)j * n_tasks / G);
-    const uint32_t n_t = (uint32_t)((uint64_t)(j + 1) * n_tasks / G) - t_lo;  // this workgroup's tasks
+    n_tasks = s_off[n_pairs];
+    t_lo = (uint32_t)((uint64_t)j * n_tasks / G);
+    n_t = (uint32_t)((uint64_t)(j + 1) * n_tasks / G) - t_lo;  // this workgroup's tasks
     if (p.pair_range && j == 0) {
         // workgroup of task t: the largest i with iT/G <= t, i.e. floor(((t + 1) G - 1) / T)
         for (int pr = tid; pr < n_pairs; pr += kNT) {
@@ -182,11 +207,12 @@ decode_mma16_kernel(const SegParams p) {
             p.pair_range[pr] = r;
         }
     }
-    const int64_t n_cells = p.n_cells;
-    const int qi_row = min(col, R - 1) / p.gqa;  // query position of this lane's row
+    }  // persistent form
+    const int64_t n_cells = c_lim;  // keys end here (segment end, or this split's end)
+    const int qi_row = (R0 + min(col, RR - 1)) / p.gqa;  // query position of this lane's row
     const int fcell = tid / kTpc, fsub = tid % kTpc;
     const int mrow = tid / kCh, mkey = tid % kCh;  // mask staging: row tid / kCh, key tid % kCh
-    const bool mthread = p.mask != nullptr && tid < R * kCh;
+    const bool mthread = p.mask != nullptr && tid < RR * kCh;
 
     // ---- partial of one pair for this lane's row (col < R): slot j.  Buffer stores of four
     // values each keep the store count per partial small and fixed (NT + 1), so that the waits
@@ -197,9 +223,9 @@ decode_mma16_kernel(const SegParams p) {
     // (acc null: the empty partial, M and S only -- the merge gives a segment with M = -inf
     // no weight and ignores its values)
     auto write_partial = [&](int pair, float M, float S, const float4_t *acc) __attribute__((always_inline)) {
-        if (col >= R) return;
+        if (col >= RR) return;
         const int bb = pair / n_hgrp, g = (pair % n_hgrp) * kHW + head;
-        const int r = col % p.gqa, i = col / p.gqa;
+        const int r = (R0 + col) % p.gqa, i = (R0 + col) / p.gqa;
         const int row = (g * p.gqa + r) + p.n_head * (i + p.n_q * bb);
         const int base = row * kPs * (int)sizeof(float);
         if (grp == 0 && part == 0)
@@ -218,10 +244,15 @@ decode_mma16_kernel(const SegParams p) {
     // row-list lookahead) instead of searching.
     int cur_f = 0, cur_r = 0, prev_fetch_pair = -1;
     auto task_at = [&](int &cur, uint32_t k, int &pair, int64_t &c0) __attribute__((always_inline)) {
-        const uint32_t t = t_lo + (n_t > 0 ? min(k, n_t - 1) : 0);
-        while (cur + 1 < n_pairs && s_off[cur + 1] <= t) ++cur;  // past empty pairs too
-        pair = cur;
-        c0 = (int64_t)(t - s_off[cur]) * kCh;
+        if constexpr (RGM) {
+            pair = rg_pair;
+            c0 = c_beg + (int64_t)(n_t > 0 ? min(k, n_t - 1) : 0) * kCh;
+        } else {
+            const uint32_t t = t_lo + (n_t > 0 ? min(k, n_t - 1) : 0);
+            while (cur + 1 < n_pairs && s_off[cur + 1] <= t) ++cur;  // past empty pairs too
+            pair = cur;
+            c0 = (int64_t)(t - s_off[cur]) * kCh;
+        }
     };
     // pool rows of the wave's cells kCpw*wave .. kCpw*wave + kCpw - 1 of task k's chunk, as read
     // (always from inside the list), and whether each is a key: entries past the list end (or
@@ -245,7 +276,7 @@ decode_mma16_kernel(const SegParams p) {
     // head_dim 32*blk + 8*grp + 0..7
     auto load_q = [&](int pair, half8_t *q) __attribute__((always_inline)) {
         const int bb = pair / n_hgrp, hg = pair % n_hgrp;
-        const int r = col < R ? col : 0;
+        const int r = R0 + (col < RR ? col : 0);
         const int g = hg * kHW + head;
         const _Float16 *qrow = p.q + (int64_t)(r / p.gqa) * p.q_s1 + (int64_t)(g * p.gqa + r % p.gqa) * p.q_s2 +
                                (int64_t)bb * p.q_s3;
@@ -306,7 +337,7 @@ decode_mma16_kernel(const SegParams p) {
                 st.v[m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, vo + 16 * kTpc * m, 0, 0));
         }
         if (mthread) {
-            const _Float16 *mb = p.mask + p.pos0 + (int64_t)bb * p.m_s3 + (int64_t)(mrow / p.gqa) * p.m_s1;
+            const _Float16 *mb = p.mask + p.pos0 + (int64_t)bb * p.m_s3 + (int64_t)((R0 + mrow) / p.gqa) * p.m_s1;
             st.mk = __builtin_bit_cast(uint16_t, mb[min(c0 + mkey, n_cells - 1)]);
         }
         if constexpr (GD::kQStage) {
@@ -349,10 +380,15 @@ decode_mma16_kernel(const SegParams p) {
             write_partial(cur, mrun == -INFINITY ? -INFINITY : mrun * kLn2, S, oacc);
         }
     };
-    // pairs with no task in this workgroup get the empty partial up front
-    for (int pr = 0; pr < n_pairs; ++pr) {
-        const uint32_t lo = s_off[pr], hi = s_off[pr + 1];
-        if (!(lo < hi && n_t > 0 && lo < t_lo + n_t && hi > t_lo)) write_partial(pr, -INFINITY, 0.f, nullptr);
+    // pairs with no task in this workgroup get the empty partial up front (row-group form: an
+    // empty split)
+    if constexpr (RGM) {
+        if (n_t == 0) write_partial(rg_pair, -INFINITY, 0.f, nullptr);
+    } else {
+        for (int pr = 0; pr < n_pairs; ++pr) {
+            const uint32_t lo = s_off[pr], hi = s_off[pr + 1];
+            if (!(lo < hi && n_t > 0 && lo < t_lo + n_t && hi > t_lo)) write_partial(pr, -INFINITY, 0.f, nullptr);
+        }
     }
 
     // ---- one task from LDS stage `buf` (its metadata and, for a new pair, its Q^T were taken
@@ -394,7 +430,7 @@ decode_mma16_kernel(const SegParams p) {
         for (int u = 0; u < NU; ++u) {
             const int k0 = 16 * u + 4 * grp;  // the lane's first key in the chunk
             const int4 okv = *reinterpret_cast<const int4 *>(&s_ok[buf][k0]);
-            const uint2 mv = p.mask ? *reinterpret_cast<const uint2 *>(&s_mask[buf][min(col, R - 1)][k0]) : make_uint2(0, 0);
+            const uint2 mv = p.mask ? *reinterpret_cast<const uint2 *>(&s_mask[buf][min(col, RR - 1)][k0]) : make_uint2(0, 0);
             const half2_t m01 = __builtin_bit_cast(half2_t, mv.x), m23 = __builtin_bit_cast(half2_t, mv.y);
             const float mvals[4] = {(float)m01[0], (float)m01[1], (float)m23[0], (float)m23[1]};
             const int okk[4] = {okv.x, okv.y, okv.z, okv.w};
@@ -482,8 +518,13 @@ template <int D, int R, bool ROWS>
 hipError_t launch16(const SegParams &p, hipStream_t s, int *occupancy) {
     if (occupancy)
         return hipOccupancyMaxActiveBlocksPerMultiprocessor(occupancy, decode_mma16_kernel<D, R, ROWS>, kNT, 0);
-    // persistent: n_splits workgroups in all, each covering every pair
-    launch_seg(decode_mma16_kernel<D, R, ROWS>, dim3((unsigned)p.n_splits), dim3(kNT), s, p);
+    // persistent: n_splits workgroups in all, each covering every pair; row groups: one
+    // workgroup per (row group, split, head group, sequence)
+    int64_t blocks = p.n_splits;
+    if (R > kMaxR)
+        blocks *= (int64_t)((p.gqa * p.n_q + 15) / 16) * (p.n_head_kv / G16<D, ROWS>::HW) * p.n_seq;
+    if (blocks > ((int64_t)1 << 31) - 1) return hipErrorInvalidValue;
+    launch_seg(decode_mma16_kernel<D, R, ROWS>, dim3((unsigned)blocks), dim3(kNT), s, p);
     return hipGetLastError();
 }
 
@@ -499,7 +540,7 @@ hipError_t launch16_d(const SegParams &p, hipStream_t s, int *occupancy) {
         case 6: return rows ? launch16<D, 6, true>(p, s, occupancy) : launch16<D, 6, false>(p, s, occupancy);
         case 7: return rows ? launch16<D, 7, true>(p, s, occupancy) : launch16<D, 7, false>(p, s, occupancy);
         case 8: return rows ? launch16<D, 8, true>(p, s, occupancy) : launch16<D, 8, false>(p, s, occupancy);
-        default: return hipErrorInvalidValue;
+        default: return rows ? hipErrorInvalidValue : launch16<D, 16, false>(p, s, occupancy);  // row groups
     }
 }
 
@@ -531,8 +572,11 @@ int decode_mma16_heads(int d, int dv) {
 bool decode_mma16_ok(const SegParams &p) {
     const int R = p.gqa * p.n_q;
     const int hw = decode_mma16_heads(p.d, p.dv);
-    if (hw == 0 || p.cell_hw != hw || R < 1 || R > kMaxR || p.n_head_kv % hw != 0) return false;
-    if ((int64_t)p.n_seq * (p.n_head_kv / hw) > kMaxPairs) return false;
+    // more than 8 rows per KV head: row groups of 16 over a segment at the head dims other than
+    // 128 (where such calls are prefill, which has a kernel of its own)
+    const bool row_groups = R > kMaxR && !p.rows && p.d != kHeadDim;
+    if (hw == 0 || p.cell_hw != hw || R < 1 || (R > kMaxR && !row_groups) || p.n_head_kv % hw != 0) return false;
+    if (!row_groups && (int64_t)p.n_seq * (p.n_head_kv / hw) > kMaxPairs) return false;
     // row lists address the pool with 32-bit buffer offsets
     if (p.rows && (p.n_pool <= 0 || p.n_pool * p.k_s1 >= ((int64_t)1 << 31) || p.n_pool * p.v_s1 >= ((int64_t)1 << 31) ||
                    p.k_s1 >= (1 << 24) || p.v_s1 >= (1 << 24)))

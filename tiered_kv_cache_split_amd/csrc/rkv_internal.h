@@ -99,6 +99,9 @@ bool decode_mma16_ok(const SegParams &p);
 // and the cells of one of its tasks (chunks) at head dim d over a segment or a row list.
 int decode_mma16_heads(int d, int dv);
 int decode_mma16_chunk(int d, bool rows);
+// Workgroups per (split, head group, sequence) of a non-persistent cell-major launch for p: its
+// blocks of row groups.
+int cell_row_groups(const SegParams &p, int k_type, int v_type);
 // Whether the decode kernel for p is the persistent one: n_splits workgroups then take equal
 // contiguous runs of the 16-cell chunks of all (sequence, head group) pairs, numbered
 // pair-major, and cells_per_split is unused.

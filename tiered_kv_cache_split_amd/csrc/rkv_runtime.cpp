@@ -355,7 +355,7 @@ int use_cell_kernel(const Seg &sg, const SegParams &p, int k_type, int v_type) {
 // Split-K plan of one device segment: cells per split and number of splits.  The vector
 // kernel walks 64-cell chunks; the MFMA kernel walks key tiles of prefill_keys_per_iter().
 void seg_plan(const rkv_ctx *ctx, int64_t n_cells, const SegParams &p, bool mfma, int cell_occupancy, bool persistent,
-              int64_t &cps, int &n_splits) {
+              int row_groups, int64_t &cps, int &n_splits) {
     if (mfma) {
         const int kpi = prefill_keys_per_iter();
         const int64_t q_tiles = ((int64_t)p.gqa * p.n_q + prefill_rows_per_block() - 1) / prefill_rows_per_block();
@@ -380,7 +380,7 @@ void seg_plan(const rkv_ctx *ctx, int64_t n_cells, const SegParams &p, bool mfma
     } else if (p.cell_hw > 0) {
         // cell-major kernel: one wave of resident workgroups over (split, head group, sequence,
         // row group of 16), at least 256 cells per split
-        const int64_t groups = (int64_t)p.n_seq * (p.n_head_kv / p.cell_hw) * decode_mma_row_groups(p);
+        const int64_t groups = (int64_t)p.n_seq * (p.n_head_kv / p.cell_hw) * row_groups;
         const int64_t slots = (int64_t)std::max(1, cell_occupancy) * ctx->n_cu;
         int64_t want = ctx->splits_override > 0 ? ctx->splits_override : std::max<int64_t>(1, slots / groups);
         want = std::max<int64_t>(1, std::min(want, std::max<int64_t>(1, n_cells / 256)));
@@ -406,8 +406,8 @@ SegPlan plan_segment(const rkv_ctx *ctx, const SegParams &base, const Seg &sg, b
     p.cell_hw = mfma ? 0 : use_cell_kernel(sg, p, k_type, v_type);
     SegPlan pl{p.cell_hw, 0, 0};
     const int occ = p.cell_hw > 0 ? cell_blocks_per_cu(p, k_type, v_type) : 1;
-    seg_plan(ctx, sg.n_cells, p, mfma, occ, p.cell_hw > 0 && decode_kernel_persistent(p, k_type, v_type), pl.cps,
-             pl.n_splits);
+    seg_plan(ctx, sg.n_cells, p, mfma, occ, p.cell_hw > 0 && decode_kernel_persistent(p, k_type, v_type),
+             p.cell_hw > 0 ? cell_row_groups(p, k_type, v_type) : 1, pl.cps, pl.n_splits);
     return pl;
 }
 
