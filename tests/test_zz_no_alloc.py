@@ -25,7 +25,7 @@ def run_both(w, run, mask=None):
         md = rkv.mask_desc(mt)
     outs = []
     for which in ("ctx", "noalloc"):
-        o = torch.full((n_q, n_head, 128), float("nan"), dtype=torch.float32, device="cuda")
+        o = torch.full((n_q, n_head, w["dv"]), float("nan"), dtype=torch.float32, device="cuda")
         lse = torch.full((n_q, n_head), float("nan"), dtype=torch.float32, device="cuda")
         kd, vd = rkv.kv_desc(k, w["k_type"]), rkv.kv_desc(v, w["v_type"])
         if which == "ctx":
@@ -71,4 +71,25 @@ def test_noalloc_fewer_splits_when_the_array_is_full():
     Oref, Lref = oracle_decode(w)
     assert_close(N, M, Oref, Lref, what="noalloc capped splits")
     assert_close(O, L, Oref, Lref, what="decode")
+    run.ctx.close()
+
+
+@pytest.mark.parametrize("d,types", [(256, "f16"), (576, "f16"), (64, "q8q4")])
+def test_noalloc_other_head_dims_two_calls(d, types):
+    """Head dims other than 128 run on their own matrix-core kernels; the entry point plans
+    them the same way.  Two calls in a row, the second over fewer cells.  The static array
+    may hold fewer partial slots than the context plans here, so the two entry points are
+    compared to the fp64 oracle's tolerance rather than bit for bit."""
+    run = Runner()
+    kt = dict(k_type=gen.TYPE_F16, v_type=gen.TYPE_F16) if types == "f16" else \
+        dict(k_type=gen.TYPE_Q8_0, v_type=gen.TYPE_Q4_0)
+    dv = 512 if d == 576 else d
+    for n_kv in (6000, 1500):
+        w = gen.make_workload(1, d=d, dv=dv, n_head=32, n_head_kv=8, n_kv=n_kv, wc=n_kv, **kt)
+        step(f"noalloc {types} d {d} 32/8 heads n_kv {n_kv}")
+        (O, L), (N, M) = run_both(w, run)
+        Oref, Lref = oracle_decode(w)
+        assert_close(N, M, Oref, Lref, what=f"noalloc d {d} n_kv {n_kv}")
+        assert_close(O, L, Oref, Lref, what=f"decode d {d} n_kv {n_kv}")
+        assert_close(N, M, O.astype(np.float64), L.astype(np.float64), what=f"noalloc vs decode d {d}")
     run.ctx.close()
