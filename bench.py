@@ -404,8 +404,9 @@ def measure(args, num):
                            "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4),
                            "traffic": traffic_from_profiles("prefill_seg_q8q4_nq512_nkv106496", "prefill")
                            if w["d"] == 128 and args.kv_types == "own" else None,
-                           "kernel": (DECODE_KERNELS.get(stats.get("kernel_variant"), "segment kernel")
-                                      if w["d"] != 128 else "prefill_seg_kernel") + " (all segments of a step)",
+                           "kernel": ("prefill_seg_kernel" if stats.get("kernel_variant") == 1 else
+                                      DECODE_KERNELS.get(stats.get("kernel_variant"), "segment kernel"))
+                           + " (all segments of a step)",
                            "kernel_ms_per_step": round(kern_total_ms, 4)}
     else:
         name = {2: "decode_seg_q8q4_nkv131072", 4: "decode_seg_rows_f16_pool65536"}.get(num, "")

@@ -25,8 +25,9 @@
  * at 64; 8, 4 or 2 at 128; 4, 2 or 1 at 256; 1 at 512 and 576), with n_q * gqa <= 8 at 128 and
  * any number of rows at the other head dims; binary16 K and V at head_dim == dv in {64, 128,
  * 256, 512} in groups of 8, 8, 4 and 2 KV heads, and at 576 / 512 one head at a time, with
- * n_q * gqa <= 8 at 128 and any number of rows at the other head dims (row groups of 16).  Prefill at 128 runs on
- * the matrix-core prefill kernel; everything else on the vector kernels; rkv_lse_merge takes
+ * n_q * gqa <= 8 at 128 and any number of rows at the other head dims (row groups of 16).  Prefill at 128, and
+ * at 64 with more than 8 rows per KV head, runs on the matrix-core prefill kernel; everything
+ * else on the vector kernels; rkv_lse_merge takes
  * dv 64, 128, 256 or 512; Q in F16;
  * K in F16 or Q8_0; V in F16 or Q4_0.  Q8_0 is a 34-byte block (binary16 scale d, 32
  * int8 codes q; value d*q).  Q4_0 is an 18-byte block (binary16 scale d, 16 bytes; byte
@@ -245,12 +246,13 @@ int rkv_attn_decode_noalloc(const rkv_tensor *q, const rkv_tensor *k, const rkv_
  * tail streaming op serves a multi-token chunk, with the mask sliced at the global key
  * position, a per-tile flash attention and an LSE per tile for the combine; patch 0102,
  * commit message: 106k-token prefills through lifted tail tiles).  The same arguments as
- * rkv_attn_decode for any n_q, computed at head dim 128 with MFMA f16 tiles: q8_0 K enters
- * the matrix cores as the exact two-part binary16 sum hi + lo = d*q, q4_0 V as the exact
- * binary16 integers n - 8 with the block scales folded into the softmax weights; the other
- * head dims run on the decode kernels (the q8_0 / q4_0 and binary16 matrix-core kernels for
- * any n_q * gqa, in row groups of 16, when the KV heads form their groups; else the vector
- * kernel in groups of 8 rows).  The tail is always computed on the GPU
+ * rkv_attn_decode for any n_q, computed at head dim 128 (and at head dim 64 when n_q * gqa
+ * > 8) with MFMA f16 tiles: q8_0 K enters the matrix cores as the exact two-part binary16 sum
+ * hi + lo = d*q, q4_0 V as the exact binary16 integers n - 8 with the block scales folded
+ * into the softmax weights; the other head dims, and 64 with up to 8 rows per KV head, run on
+ * the decode kernels (the q8_0 / q4_0 and binary16 matrix-core kernels for any n_q * gqa, in
+ * row groups of 16, when the KV heads form their groups; else the vector kernel in groups of
+ * 8 rows).  The tail is always computed on the GPU
  * (RKV_TAIL_HOST applies to decode only).  q_pos0 >= 0 makes it
  * causal: query i sits at absolute position q_pos0 + i and sees keys at positions
  * <= q_pos0 + i (in addition to the mask); q_pos0 == -1 uses the mask alone. */

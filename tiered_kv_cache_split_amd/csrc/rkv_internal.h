@@ -107,6 +107,8 @@ int cell_row_groups(const SegParams &p, int k_type, int v_type);
 // pair-major, and cells_per_split is unused.
 bool decode_kernel_persistent(const SegParams &p, int k_type, int v_type);
 hipError_t launch_decode_mma16(const SegParams &p, hipStream_t s, int *occupancy);
+// The matrix-core prefill kernel takes dk = dv = 128 or 64.
+bool prefill_head_dims_ok(int d, int dv);
 hipError_t launch_prefill_segment(const SegParams &p, int k_type, int v_type, hipStream_t s);
 // Blocks the prefill kernel uses per (q tile, KV head) along the key axis.
 int prefill_rows_per_block();

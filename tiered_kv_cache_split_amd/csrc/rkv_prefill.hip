@@ -41,26 +41,28 @@ constexpr int kThreadsP = 64 * kWavesP;
 constexpr int kGroupT = kThreadsP / 2;  // threads per wave group
 constexpr int kBM = 32 * kWavesP;       // query rows per workgroup
 constexpr int kBN = 64;                 // keys per tile
-constexpr int kKP = 272;                // LDS bytes per K row: 128 binary16 + 16 (conflict-free 16-byte reads)
-constexpr int kVP = 320;                // LDS bytes per V row: 128 binary16 + 64 (conflict-free transposing reads)
+// LDS bytes per K row: D binary16 + 16 (16 rows of a 16-byte read fall on distinct banks)
+template <int D> constexpr int k_pitch() { return 2 * D + 16; }
+// LDS bytes per V row: D binary16 + 64 (the transposing reads' rows spread over the banks)
+template <int D> constexpr int v_pitch() { return 2 * D + 64; }
 constexpr int kPD = 4;                  // P.V steps whose operand reads run ahead of the current one
 constexpr int kKD = 4;                  // Q.K steps likewise
 constexpr float kLog2eP = 1.4426950408889634f;
 constexpr float kLn2P = 0.6931471805599453f;
 
-template <int T> constexpr int row_bytes_of() { return T == T_F16 ? 256 : (T == T_Q8_0 ? 136 : 72); }
-// 32-bit words a thread fetches for its quarter row (one block of 32 values, or 64 bytes of
+template <int D, int T> constexpr int row_bytes_of() { return T == T_F16 ? 2 * D : (T == T_Q8_0 ? 34 : 18) * (D / 32); }
+// 32-bit words a thread fetches for its part of a row (one block of 32 values, or 64 bytes of
 // binary16): a q8_0 block is 34 bytes from an even offset (9 words cover it), a q4_0 block 18
 // bytes (5 words)
 template <int T> constexpr int raw_words() { return T == T_F16 ? 16 : (T == T_Q8_0 ? 9 : 5); }
 
 // LDS layout (bytes): two K buffers (binary16 hi rows, for q8_0 also the lo rows), then two V
 // buffers (binary16 rows, for q4_0 followed by d_V as [block][key slot]).
-template <int KT, int VT> struct Lds {
-    static constexpr int kKhalf = kBN * kKP;
+template <int D, int KT, int VT> struct Lds {
+    static constexpr int kKhalf = kBN * k_pitch<D>();
     static constexpr int kKbuf = kKhalf * (KT == T_Q8_0 ? 2 : 1);
-    static constexpr int kVdat = kBN * kVP;
-    static constexpr int kVbuf = kVdat + (VT == T_Q4_0 ? 4 * kBN * 2 : 0);
+    static constexpr int kVdat = kBN * v_pitch<D>();
+    static constexpr int kVbuf = kVdat + (VT == T_Q4_0 ? (D / 32) * kBN * 2 : 0);
     static constexpr int kV0 = 2 * kKbuf;
     static constexpr int kSize = 2 * kKbuf + 2 * kVbuf;
 };
@@ -86,8 +88,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint8_t *base,
     return __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, range, 0x00020000);
 }
 
-// Fetch the thread's quarter row of tile key `key`, part `qq` (0..3): the block's bytes from
-// its word-aligned start (q8_0 / q4_0 blocks start 0 or 2 bytes into a word).
+// Fetch the thread's part (32 values) of a tile key's row: the block's bytes from its
+// word-aligned start (q8_0 / q4_0 blocks start 0 or 2 bytes into a word).
 template <int T>
 __device__ __forceinline__ void fetch_part(uint32_t (&w)[16], __amdgpu_buffer_rsrc_t rs, int off) {
     if constexpr (T == T_F16) {
@@ -108,7 +110,7 @@ __device__ __forceinline__ void fetch_part(uint32_t (&w)[16], __amdgpu_buffer_rs
     }
 }
 
-// K quarter row -> LDS: binary16 copy, or a q8_0 block as exact hi / lo binary16 rows.
+// K row part -> LDS: binary16 copy, or a q8_0 block as exact hi / lo binary16 rows.
 // `odd`: the block starts 2 bytes into its first word (its scale is that word's high half).
 template <int KT>
 __device__ __forceinline__ void decode_k_part(const uint32_t (&w)[16], bool odd, uint8_t *khi, uint8_t *klo) {
@@ -136,7 +138,7 @@ __device__ __forceinline__ void decode_k_part(const uint32_t (&w)[16], bool odd,
     }
 }
 
-// V quarter row -> LDS: binary16 copy, or a q4_0 block as the exact integers n - 8 (binary16)
+// V row part -> LDS: binary16 copy, or a q4_0 block as the exact integers n - 8 (binary16)
 // plus its scale at the key's P.V slot of the block's d_V row.
 template <int VT>
 __device__ __forceinline__ void decode_v_part(const uint32_t (&w)[16], bool odd, uint8_t *vrow, uint16_t *dv_slot) {
@@ -157,11 +159,17 @@ __device__ __forceinline__ void decode_v_part(const uint32_t (&w)[16], bool odd,
     }
 }
 
-// CAP: the logit soft-cap is on (a separate instantiation, so the plain path carries none of it)
-template <int KT, int VT, bool CAP>
+// D: head dim of Q, K and V (128 or 64).  CAP: the logit soft-cap is on (a separate
+// instantiation, so the plain path carries none of it)
+template <int D, int KT, int VT, bool CAP>
 __global__ void __launch_bounds__(kThreadsP) __attribute__((amdgpu_waves_per_eu(2, 2)))
 prefill_seg_kernel(const SegParams p, int q_tiles, int n_tasks) {
-    using L = Lds<KT, VT>;
+    using L = Lds<D, KT, VT>;
+    constexpr int kKP = k_pitch<D>(), kVP = v_pitch<D>();
+    constexpr int NP = D / 32;          // 32-value parts (blocks) of a row; also P.V output tiles
+    constexpr int NQK = D / 8;          // Q.K MFMA steps per tile: D/16 k-steps x 2 key halves
+    constexpr int NPV = 4 * NP;         // P.V MFMA steps per tile: 4 key steps x NP output tiles
+    constexpr int PS = 2 + D;           // partial row stride (M, S, D values)
     constexpr int RW = raw_words<KT>() > raw_words<VT>() ? raw_words<KT>() : raw_words<VT>();
     static_assert(RW <= 16, "raw words");
     __shared__ __attribute__((aligned(16))) uint8_t smem[L::kSize];
@@ -204,12 +212,12 @@ prefill_seg_kernel(const SegParams p, int q_tiles, int n_tasks) {
     const int wave_i_first = wrow0 / p.gqa;  // smallest query index of the wave's rows
 
     // Q^T fragments: lane holds row rho, head_dim 16*ks + 8*hh + 0..7
-    half8_t qf[8];
+    half8_t qf[D / 16];
     {
         const uint32_t *qp = reinterpret_cast<const uint32_t *>(
             p.q + (int64_t)qi * p.q_s1 + (int64_t)(g * p.gqa + qr) * p.q_s2 + (int64_t)b * p.q_s3 + 8 * hh);
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
+        for (int ks = 0; ks < D / 16; ++ks) {
             uint4 v = make_uint4(0, 0, 0, 0);
             if (row_ok) v = make_uint4(qp[8 * ks], qp[8 * ks + 1], qp[8 * ks + 2], qp[8 * ks + 3]);
             qf[ks] = __builtin_bit_cast(half8_t, v);
@@ -218,9 +226,11 @@ prefill_seg_kernel(const SegParams p, int q_tiles, int n_tasks) {
     // Q is complete before any tile load is issued, so no wait inside the loop covers it
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 
-    // ---- raw fetch of this thread's quarter row (group 0: K, group 1: V): key gt / 4, part gt % 4
+    // ---- raw fetch of this thread's row part (group 0: K, group 1: V): key gt / NP, part
+    // gt % NP; at D = 64 half of each group's threads have no part
     const int gt = tid & (kGroupT - 1);
-    const int fkey = gt >> 2, fq = gt & 3;
+    const int fkey = gt / NP, fq = gt % NP;
+    const bool fact = kBN * NP == kGroupT || gt < kBN * NP;
     const bool fodd = (fq & 1) != 0;  // q8_0 / q4_0 blocks 1 and 3 start 2 bytes into a word
     const uint8_t *kbase = p.k + (int64_t)g * p.k_s2;
     const uint8_t *vbase = p.v + (int64_t)g * p.v_s2;
@@ -229,9 +239,9 @@ prefill_seg_kernel(const SegParams p, int q_tiles, int n_tasks) {
 
     const float c = p.scale_log2;
     float m_used = -INFINITY, l_sum = 0.f;
-    f16x_t oacc[4];
+    f16x_t oacc[NP];
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) oacc[dt] = f16x_t{};
+    for (int dt = 0; dt < NP; ++dt) oacc[dt] = f16x_t{};
     f16x_t sacc[2];
     half8_t pf[4];
 #pragma unroll
@@ -251,7 +261,7 @@ prefill_seg_kernel(const SegParams p, int q_tiles, int n_tasks) {
             const uint8_t *dv0 = vb + L::kVdat + 16 * hh;
             half8_t av[kPD + 1], dv[kPD + 1];
             auto ld = [&](int n) __attribute__((always_inline)) {
-                const int s = n >> 2, dt = n & 3;
+                const int s = n / NP, dt = n % NP;
                 const uint8_t *va = va0 + 16 * s * kVP + 64 * dt;
                 const short4_t t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4_t *)va);
                 const short4_t t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -262,16 +272,16 @@ prefill_seg_kernel(const SegParams p, int q_tiles, int n_tasks) {
 #pragma unroll
             for (int n = 0; n < kPD; ++n) ld(n);
 #pragma unroll
-            for (int n = 0; n < 16; ++n) {
-                if (n + kPD < 16) ld(n + kPD);
-                const half8_t wv = (VT == T_Q4_0) ? pf[n >> 2] * dv[n % (kPD + 1)] : pf[n >> 2];
-                oacc[n & 3] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[n % (kPD + 1)], wv, oacc[n & 3], 0, 0, 0);
+            for (int n = 0; n < NPV; ++n) {
+                if (n + kPD < NPV) ld(n + kPD);
+                const half8_t wv = (VT == T_Q4_0) ? pf[n / NP] * dv[n % (kPD + 1)] : pf[n / NP];
+                oacc[n % NP] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[n % (kPD + 1)], wv, oacc[n % NP], 0, 0, 0);
             }
             constexpr int kRd = VT == T_Q4_0 ? 3 : 2;  // LDS reads per step
             __builtin_amdgcn_sched_group_barrier(0x100, kPD * kRd, 0);
 #pragma unroll
-            for (int n = 0; n < 16; ++n) {
-                if (n + kPD < 16) __builtin_amdgcn_sched_group_barrier(0x100, kRd, 0);
+            for (int n = 0; n < NPV; ++n) {
+                if (n + kPD < NPV) __builtin_amdgcn_sched_group_barrier(0x100, kRd, 0);
                 if constexpr (VT == T_Q4_0) __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             }
@@ -291,8 +301,8 @@ prefill_seg_kernel(const SegParams p, int q_tiles, int n_tasks) {
 #pragma unroll
             for (int n = 0; n < kKD; ++n) ld(n);
 #pragma unroll
-            for (int n = 0; n < 16; ++n) {
-                if (n + kKD < 16) ld(n + kKD);
+            for (int n = 0; n < NQK; ++n) {
+                if (n + kKD < NQK) ld(n + kKD);
                 const int ks = n >> 1, kt = n & 1;
                 sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ak[n % (kKD + 1)][0], qf[ks], sacc[kt], 0, 0, 0);
                 if constexpr (KT == T_Q8_0)
@@ -300,8 +310,8 @@ prefill_seg_kernel(const SegParams p, int q_tiles, int n_tasks) {
             }
             __builtin_amdgcn_sched_group_barrier(0x100, kKD * kParts, 0);
 #pragma unroll
-            for (int n = 0; n < 16; ++n) {
-                if (n + kKD < 16) __builtin_amdgcn_sched_group_barrier(0x100, kParts, 0);
+            for (int n = 0; n < NQK; ++n) {
+                if (n + kKD < NQK) __builtin_amdgcn_sched_group_barrier(0x100, kParts, 0);
                 __builtin_amdgcn_sched_group_barrier(0x008, kParts, 0);
             }
         }
@@ -373,7 +383,7 @@ prefill_seg_kernel(const SegParams p, int q_tiles, int n_tasks) {
             const float alpha = need ? __builtin_amdgcn_exp2f(m_used - mnew) : 1.0f;
             l_sum *= alpha;
 #pragma unroll
-            for (int dt = 0; dt < 4; ++dt)
+            for (int dt = 0; dt < NP; ++dt)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
             m_used = mnew;
@@ -405,12 +415,14 @@ prefill_seg_kernel(const SegParams p, int q_tiles, int n_tasks) {
         auto fetch = [&](uint32_t (&w)[16], int it) __attribute__((always_inline)) {
             const int64_t c0 = c_begin + (int64_t)kBN * it;
             const int64_t nv = it < n_it ? min((int64_t)kBN, p.n_cells - c0) : 0;
+            if (!fact) return;
             if constexpr (G0)
-                fetch_part<KT>(w, tile_rsrc(kbase + c0 * p.k_s1, p.k_s1, nv, row_bytes_of<KT>()), koff);
+                fetch_part<KT>(w, tile_rsrc(kbase + c0 * p.k_s1, p.k_s1, nv, row_bytes_of<D, KT>()), koff);
             else
-                fetch_part<VT>(w, tile_rsrc(vbase + c0 * p.v_s1, p.v_s1, nv, row_bytes_of<VT>()), voff);
+                fetch_part<VT>(w, tile_rsrc(vbase + c0 * p.v_s1, p.v_s1, nv, row_bytes_of<D, VT>()), voff);
         };
         auto decode = [&](const uint32_t (&w)[16], int it) __attribute__((always_inline)) {
+            if (!fact) return;
             if constexpr (G0) {
                 uint8_t *kb = smem + (it & 1) * L::kKbuf;
                 decode_k_part<KT>(w, fodd, kb + fkey * kKP + 64 * fq, kb + L::kKhalf + fkey * kKP + 64 * fq);
@@ -469,17 +481,17 @@ prefill_seg_kernel(const SegParams p, int q_tiles, int n_tasks) {
     else
         body(std::integral_constant<bool, false>{});
 
-    // ---- partial of the lane's row: lane holds head_dim 32dt + 8(i/4) + 4hh + i%4
+    // ---- partial of the lane's row: lane holds head dim 32dt + 8(i/4) + 4hh + i%4
     const float l_tot = lane_pair_sum(l_sum);
     if (row_ok) {
         const int64_t r_out = (int64_t)(g * p.gqa + qr) + (int64_t)p.n_head * (qi + (int64_t)p.n_q * b);
-        float *out = p.partials + ((int64_t)(p.slot0 + split) * p.n_rows + r_out) * kPartialStride;
+        float *out = p.partials + ((int64_t)(p.slot0 + split) * p.n_rows + r_out) * PS;
         if (hh == 0) {
             const float M = m_used == -INFINITY ? -INFINITY : m_used * kLn2P;
             *reinterpret_cast<float2 *>(out) = make_float2(M, l_tot);
         }
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
+        for (int dt = 0; dt < NP; ++dt) {
 #pragma unroll
             for (int a = 0; a < 4; ++a) {
                 float *o = out + 2 + 32 * dt + 8 * a + 4 * hh;
@@ -490,7 +502,7 @@ prefill_seg_kernel(const SegParams p, int q_tiles, int n_tasks) {
     }
 }
 
-template <int KT, int VT>
+template <int D, int KT, int VT>
 hipError_t launch_t(const SegParams &p, hipStream_t s) {
     const int q_tiles = (p.gqa * p.n_q + kBM - 1) / kBM;
     const int64_t n_tasks = (int64_t)p.n_splits * q_tiles * p.n_head_kv * p.n_seq;
@@ -498,10 +510,19 @@ hipError_t launch_t(const SegParams &p, hipStream_t s) {
     if (n_tasks > ((int64_t)1 << 30)) return hipErrorInvalidValue;
     const int64_t per = (n_tasks + 7) / 8;
     if (p.cap_l2 != 0.f)
-        launch_seg(prefill_seg_kernel<KT, VT, true>, dim3((unsigned)(8 * per)), dim3(kThreadsP), s, p, q_tiles, (int)n_tasks);
+        launch_seg(prefill_seg_kernel<D, KT, VT, true>, dim3((unsigned)(8 * per)), dim3(kThreadsP), s, p, q_tiles, (int)n_tasks);
     else
-        launch_seg(prefill_seg_kernel<KT, VT, false>, dim3((unsigned)(8 * per)), dim3(kThreadsP), s, p, q_tiles, (int)n_tasks);
+        launch_seg(prefill_seg_kernel<D, KT, VT, false>, dim3((unsigned)(8 * per)), dim3(kThreadsP), s, p, q_tiles, (int)n_tasks);
     return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const SegParams &p, int k_type, int v_type, hipStream_t s) {
+    if (k_type == T_Q8_0 && v_type == T_Q4_0) return launch_t<D, T_Q8_0, T_Q4_0>(p, s);
+    if (k_type == T_F16 && v_type == T_F16) return launch_t<D, T_F16, T_F16>(p, s);
+    if (k_type == T_Q8_0 && v_type == T_F16) return launch_t<D, T_Q8_0, T_F16>(p, s);
+    if (k_type == T_F16 && v_type == T_Q4_0) return launch_t<D, T_F16, T_Q4_0>(p, s);
+    return hipErrorNotSupported;
 }
 
 }  // namespace
@@ -510,15 +531,13 @@ int prefill_rows_per_block() { return kBM; }
 int prefill_keys_per_iter() { return kBN; }
 int prefill_blocks_per_cu() { return 1; }
 
+bool prefill_head_dims_ok(int d, int dv) { return d == dv && (d == kHeadDim || d == 64); }
+
 hipError_t launch_prefill_segment(const SegParams &p, int k_type, int v_type, hipStream_t s) {
-    if (p.rows) return hipErrorNotSupported;
+    if (p.rows || !prefill_head_dims_ok(p.d, p.dv)) return hipErrorNotSupported;
     // 64 rows of a tile are addressed with 32-bit offsets from the tile's first row
     if (p.k_s1 * kBN >= ((int64_t)1 << 31) || p.v_s1 * kBN >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
-    if (k_type == T_Q8_0 && v_type == T_Q4_0) return launch_t<T_Q8_0, T_Q4_0>(p, s);
-    if (k_type == T_F16 && v_type == T_F16) return launch_t<T_F16, T_F16>(p, s);
-    if (k_type == T_Q8_0 && v_type == T_F16) return launch_t<T_Q8_0, T_F16>(p, s);
-    if (k_type == T_F16 && v_type == T_Q4_0) return launch_t<T_F16, T_Q4_0>(p, s);
-    return hipErrorNotSupported;
+    return p.d == 64 ? launch_d<64>(p, k_type, v_type, s) : launch_d<kHeadDim>(p, k_type, v_type, s);
 }
 
 }  // namespace rkv

@@ -514,9 +514,9 @@ int attn_window_tail(rkv_ctx *ctx, const rkv_tensor *q, const rkv_tensor *k_win,
                      int64_t q_pos0, bool mfma, float *o, float *lse, hipStream_t stream,
                      float *ext_partials = nullptr, int64_t ext_cap = 0, bool prefill = false) {
     if (!ctx) return fail(RKV_ERR_ARG, "ctx is NULL");
-    // dk = dv in 64, 128, 256, 512 and the pair dk = 576 / dv = 512 (head dim 128 prefill on the
-    // matrix-core kernel, everything else on the vector kernels)
-    const bool any_d = !mfma;
+    // dk = dv in 64, 128, 256, 512 and the pair dk = 576 / dv = 512 (prefill at head dims 128
+    // and 64 on the matrix-core prefill kernel, everything else on the decode kernels)
+    const bool any_d = !mfma || (q && q->ne[0] != kHeadDim);
     int st = check_q(q, false, any_d);
     if (st) return st;
     if (wc < 0) return fail(RKV_ERR_ARG, "wc < 0");
@@ -561,6 +561,8 @@ int attn_window_tail(rkv_ctx *ctx, const rkv_tensor *q, const rkv_tensor *k_win,
     if (!head_dims_supported(d, dv))
         return fail(RKV_ERR_UNSUPPORTED, "head dims dk=%d, dv=%d not supported (dk = dv in 64, 128, 256, 512, or 576/512)",
                     d, dv);
+    if (mfma && !prefill_head_dims_ok(d, dv))
+        return fail(RKV_ERR_UNSUPPORTED, "the prefill kernel takes dk = dv = 128 or 64 (got %d / %d)", d, dv);
     const int64_t ps = 2 + dv;  // partial row stride
     // the head-dim-128 decode kernels take up to 8 rows per KV head; the kernel for other head
     // dims takes any number in row groups of 8
@@ -1233,10 +1235,17 @@ int rkv_attn_decode(rkv_ctx *ctx, const rkv_tensor *q, const rkv_tensor *k_win, 
 int rkv_attn_prefill(rkv_ctx *ctx, const rkv_tensor *q, const rkv_tensor *k_win, const rkv_tensor *v_win,
                      const rkv_tensor *k_tail, const rkv_tensor *v_tail, const rkv_tensor *mask, int64_t wc,
                      int64_t tile_kv, float scale, int64_t q_pos0, float *o, float *lse, void *stream) {
-    // head dim 128 runs on the matrix-core prefill kernel; the other head dims on the decode
-    // kernels (matrix-core where they take the types and head groups, else the vector kernel),
-    // which take the causal rule and the mask alike
-    const bool mfma = !q || q->ne[0] == kHeadDim;
+    // head dim 128 runs on the matrix-core prefill kernel, and so does head dim 64 with more
+    // than 8 rows per KV head; the rest on the decode kernels (matrix-core where they take the
+    // types and head groups, else the vector kernel), which take the causal rule and the mask
+    // alike
+    bool mfma = !q || q->ne[0] == kHeadDim;
+    if (q && q->ne[0] == 64) {
+        const rkv_tensor *kr = k_win ? k_win : k_tail;
+        const rkv_tensor *vr = v_win ? v_win : v_tail;
+        mfma = kr && vr && kr->ne[2] > 0 && q->ne[2] % kr->ne[2] == 0 && vr->ne[0] == 64 &&
+               (q->ne[2] / kr->ne[2]) * q->ne[1] > kMaxRowsVec;
+    }
     return attn_window_tail(ctx, q, k_win, v_win, k_tail, v_tail, mask, wc, tile_kv, scale, q_pos0, mfma, o, lse,
                             static_cast<hipStream_t>(stream), nullptr, 0, true);
 }
