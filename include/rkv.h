@@ -19,8 +19,7 @@
  * strides, nb[0] is the element (or quant block) size.  Rows of head_dim values must be
  * contiguous (nb[0] == type size).  Supported head dims (patch 0070, fattn.cu: the streaming
  * op's supported shapes): head_dim == dv in {64, 128, 256, 512}, and head_dim 576 for Q and
- * K with dv 512 for V, on every attention entry point but rkv_attn_partial (head_dim 128
- * only) and on the host tail partial.  Decode
+ * K with dv 512 for V, on every attention entry point and the host tail partial.  Decode
  * over cell-major caches runs on the matrix-core kernels: q8_0 K / q4_0 V at head_dim == dv in
  * {64, 128, 256, 512} and at 576 / 512 when the KV heads form groups the kernel takes (8 or 4
  * at 64; 8, 4 or 2 at 128; 4, 2 or 1 at 256; 1 at 512 and 576), with n_q * gqa <= 8 at 128 and
@@ -281,11 +280,12 @@ int rkv_attn_rows(rkv_ctx *ctx, const rkv_tensor *q, const rkv_tensor *k_pool,
                   const rkv_tensor *mask, float scale, float *o, float *lse, void *stream);
 
 /* One segment's partial over device-resident K/V (the per-segment step of the method):
- * writes (M, S, VKQ) for every output row into `partial` float32 [n_rows][2 + 128].  Head
- * dim 128 only (other head dims: RKV_ERR_UNSUPPORTED).
+ * writes (M, S, VKQ) for every output row (row = query * n_head + head) into `partial`
+ * float32 [n_rows][2 + dv], at every supported head-dim pair.
  * kv_pos0 is the global position of the segment's first cell (mask column offset and
- * causal position); q_pos0 as in rkv_attn_prefill (-1 = mask only).  Chooses the vector
- * kernel when n_q * gqa <= 8, the MFMA kernel otherwise. */
+ * causal position); q_pos0 as in rkv_attn_prefill (-1 = mask only).  Chooses the decode
+ * kernels when n_q * gqa <= 8 and at head dims 256, 512 and 576 / 512, the MFMA prefill
+ * kernel otherwise (head dims 128 and 64).  An empty segment writes (-inf, 0, 0...). */
 int rkv_attn_partial(rkv_ctx *ctx, const rkv_tensor *q, const rkv_tensor *k,
                      const rkv_tensor *v, const rkv_tensor *mask, int64_t kv_pos0,
                      int64_t q_pos0, float scale, float *partial, void *stream);

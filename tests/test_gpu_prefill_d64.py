@@ -9,7 +9,7 @@ import pytest
 
 import oracle
 import rkv_inputs as gen
-from rkv_testutil import Runner, assert_close, dev, oracle_decode, step
+from rkv_testutil import Runner, assert_close, oracle_decode, step
 
 pytestmark = pytest.mark.gpu
 
@@ -202,18 +202,3 @@ def test_random_prefill_d64(run, seed):
     Oref, Lref = causal_ref(w, q_pos0=q_pos0, mask=mask, softcap=cap)
     assert_close(O, L, Oref, Lref, what=f"random prefill d64 {seed}")
 
-
-def test_partial_entry_refuses_head_dim_64(run):
-    """rkv_attn_partial takes head dim 128 only; at 64 it refuses before any launch."""
-    import torch
-    import tiered_kv_cache_split_amd as rkv
-    w = chunk(n_kv=1664, n_q=32, wc=1664, tile=512)
-    step("attn_partial at head dim 64 refused")
-    qd = dev(w["q"])
-    kd, vd = dev(w["k"]), dev(w["v"])
-    part = torch.empty((32 * w["n_head"], 2 + D), dtype=torch.float32, device="cuda")
-    with pytest.raises(rkv.RkvError) as e:
-        run.ctx.attn_partial(rkv.q_desc(qd), rkv.kv_desc(kd, w["k_type"]), rkv.kv_desc(vd, w["v_type"]), None, 0,
-                             -1, w["scale"], part)
-    assert e.value.status == rkv.RKV_ERR_UNSUPPORTED
-    torch.cuda.synchronize()

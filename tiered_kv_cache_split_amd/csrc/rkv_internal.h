@@ -124,11 +124,12 @@ struct MergeRange {
 hipError_t launch_merge(const float *partials, int n_seg, int64_t n_rows, float *o, float *lse,
                         float *partial_out, hipStream_t s, const MergeRange *range = nullptr);
 // The same merge for partial rows of 2 + dv floats (dv = 64, 128, 256, 512), up to 1024
-// segments: up to four segments per thread over 16-value parts of each row.
+// segments: up to four segments per thread over 16-value parts of each row.  With
+// partial_out the merged (M, S, VKQ) rows go there instead of o / lse.
 hipError_t launch_merge_parts(const float *partials, int n_seg, int64_t n_rows, int dv, float *o, float *lse,
-                              hipStream_t s);
-// Writes (M=-inf, S=0, VKQ=0) for n_rows rows into partial slot 0.
-hipError_t launch_empty_partials(float *partials, int64_t n_rows, hipStream_t s);
+                              hipStream_t s, float *partial_out = nullptr);
+// Writes (M=-inf, S=0, VKQ=0) for n_rows rows of 2 + dv floats into partial slot 0.
+hipError_t launch_empty_partials(float *partials, int64_t n_rows, hipStream_t s, int dv = kHeadDim);
 // Row-list extents in kRowExtentParts pieces per sequence: the maximum of
 // extent[b * kRowExtentParts + 0 .. kRowExtentParts - 1] is 1 + the last index j < n_kv with
 // rows[j + rows_s*b] >= 0, or 0 (n_seq sequences)

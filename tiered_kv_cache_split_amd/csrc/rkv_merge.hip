@@ -268,9 +268,10 @@ __global__ void __launch_bounds__(64 * kMergeRowsPerBlock) merge_rows_kernel(con
     if (lse && lane == 0) lse[row] = ok ? M + logf(S) : -INFINITY;
 }
 
-__global__ void __launch_bounds__(128) empty_partials_kernel(float *__restrict__ part) {
-    float *q = part + (int64_t)blockIdx.x * kPartialStride;
-    q[2 + threadIdx.x] = 0.f;
+// one row per workgroup: (M, S) = (-inf, 0) and dv zeros, for rows of 2 + dv floats
+__global__ void __launch_bounds__(128) empty_partials_kernel(float *__restrict__ part, int dv) {
+    float *q = part + (int64_t)blockIdx.x * (2 + dv);
+    for (int j = threadIdx.x; j < dv; j += blockDim.x) q[2 + j] = 0.f;
     if (threadIdx.x == 0) {
         q[0] = -INFINITY;
         q[1] = 0.f;
@@ -302,37 +303,39 @@ hipError_t launch_merge(const float *partials, int n_seg, int64_t n_rows, float 
 }
 
 template <int D>
-void launch_parts_d(const float *partials, int n_seg, int64_t n_rows, float *o, float *lse, hipStream_t s) {
+void launch_parts_d(const float *partials, int n_seg, int64_t n_rows, float *o, float *lse, float *pout,
+                    hipStream_t s) {
     const dim3 grid((unsigned)n_rows, (unsigned)(D / kMergePartDim));
     const RowRange rr{};
     if (n_seg <= kMergePartThreads)
         hipLaunchKernelGGL((merge_parts_kernel<D, 1>), grid, dim3(kMergePartThreads), 0, s, partials, n_seg, n_rows, o,
-                           lse, nullptr, rr);
+                           lse, pout, rr);
     else
         hipLaunchKernelGGL((merge_parts_kernel<D, kMergePartMaxNs>), grid, dim3(kMergePartThreads), 0, s, partials,
-                           n_seg, n_rows, o, lse, nullptr, rr);
+                           n_seg, n_rows, o, lse, pout, rr);
 }
 
 hipError_t launch_merge_parts(const float *partials, int n_seg, int64_t n_rows, int dv, float *o, float *lse,
-                              hipStream_t s) {
+                              hipStream_t s, float *partial_out) {
     if (n_rows <= 0) return hipSuccess;
     if (n_seg > kMergePartMaxNs * kMergePartThreads || n_rows > ((int64_t)1 << 31) - 1) return hipErrorInvalidValue;
     if (dv == 64)
-        launch_parts_d<64>(partials, n_seg, n_rows, o, lse, s);
+        launch_parts_d<64>(partials, n_seg, n_rows, o, lse, partial_out, s);
     else if (dv == 128)
-        launch_parts_d<128>(partials, n_seg, n_rows, o, lse, s);
+        launch_parts_d<128>(partials, n_seg, n_rows, o, lse, partial_out, s);
     else if (dv == 256)
-        launch_parts_d<256>(partials, n_seg, n_rows, o, lse, s);
+        launch_parts_d<256>(partials, n_seg, n_rows, o, lse, partial_out, s);
     else if (dv == 512)
-        launch_parts_d<512>(partials, n_seg, n_rows, o, lse, s);
+        launch_parts_d<512>(partials, n_seg, n_rows, o, lse, partial_out, s);
     else
         return hipErrorNotSupported;
     return hipGetLastError();
 }
 
-hipError_t launch_empty_partials(float *partials, int64_t n_rows, hipStream_t s) {
+hipError_t launch_empty_partials(float *partials, int64_t n_rows, hipStream_t s, int dv) {
     if (n_rows <= 0) return hipSuccess;
-    hipLaunchKernelGGL(empty_partials_kernel, dim3((unsigned)n_rows), dim3(kHeadDim), 0, s, partials);
+    if (dv <= 0) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(empty_partials_kernel, dim3((unsigned)n_rows), dim3(128), 0, s, partials, dv);
     return hipGetLastError();
 }
 

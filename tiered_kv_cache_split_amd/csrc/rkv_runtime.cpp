@@ -1363,16 +1363,22 @@ int rkv_attn_partial(rkv_ctx *ctx, const rkv_tensor *q, const rkv_tensor *k, con
                      void *stream_) {
     hipStream_t stream = static_cast<hipStream_t>(stream_);
     if (!ctx) return fail(RKV_ERR_ARG, "ctx is NULL");
-    int st = check_q(q, false);
+    int st = check_q(q, false, true);
     if (st) return st;
-    if ((st = check_kv(k, "k", true)) || (st = check_kv(v, "v", false))) return st;
+    if ((st = check_kv(k, "k", true, true)) || (st = check_kv(v, "v", false, true))) return st;
     if (k->ne[1] != v->ne[1] || k->ne[2] != v->ne[2]) return fail(RKV_ERR_ARG, "k and v disagree in shape");
+    const int d = (int)q->ne[0], dv = (int)v->ne[0];
+    if (k->ne[0] != d) return fail(RKV_ERR_ARG, "K head dim must equal Q's");
+    if (!head_dims_supported(d, dv))
+        return fail(RKV_ERR_UNSUPPORTED, "head dims dk=%d, dv=%d not supported (dk = dv in 64, 128, 256, 512, or 576/512)",
+                    d, dv);
     if (kv_pos0 < 0 || q_pos0 < -1) return fail(RKV_ERR_ARG, "bad positions");
     if (!std::isfinite(scale)) return fail(RKV_ERR_ARG, "scale is not finite");
     const int64_t n_head = q->ne[2], n_q = q->ne[1], n_head_kv = k->ne[2];
     if (n_head % n_head_kv != 0) return fail(RKV_ERR_ARG, "n_head %% n_head_kv != 0");
     const int64_t gqa = n_head / n_head_kv;
-    const bool mfma = gqa * n_q > kMaxRowsVec;
+    // the prefill kernel (head dims 128 and 64) above 8 rows per KV head, else the decode kernels
+    const bool mfma = gqa * n_q > kMaxRowsVec && prefill_head_dims_ok(d, dv);
     if ((st = check_mask(mask, kv_pos0 + k->ne[1], n_q, 1))) return st;
     if (k->ne[1] > 0 && ((st = check_device_ptr(k->data, "k")) || (st = check_device_ptr(v->data, "v")))) return st;
     if ((st = check_device_ptr(partial, "partial"))) return st;
@@ -1389,10 +1395,14 @@ int rkv_attn_partial(rkv_ctx *ctx, const rkv_tensor *q, const rkv_tensor *k, con
     p.scale_log2 = scale * 1.4426950408889634f;
     fill_softcap(p, ctx, scale);
     p.n_rows = n_head * n_q;
+    p.d = d;
+    p.dv = dv;
     const Seg sg{static_cast<const uint8_t *>(k->data), static_cast<const uint8_t *>(v->data), k->nb[1], k->nb[2],
                  v->nb[1], v->nb[2], k->ne[1], kv_pos0};
     const int slots = plan_segment(ctx, p, sg, mfma, k->type, v->type).n_splits;
-    if ((st = ensure_partials(ctx, (int64_t)slots * p.n_rows * kPartialStride, stream))) return st;
+    if (dv != kHeadDim && slots > 1024)
+        return fail(RKV_ERR_UNSUPPORTED, "%d partial slots: the merge into one partial takes up to 1024 at dv %d", slots, dv);
+    if ((st = ensure_partials(ctx, (int64_t)slots * p.n_rows * (2 + dv), stream))) return st;
     p.partials = ctx->partials;
     ctx->stats = rkv_stats{};
     ctx->stats.kernel_variant = mfma ? RKV_KERNEL_PREFILL_MFMA : RKV_KERNEL_DECODE_HEAD;
@@ -1400,12 +1410,13 @@ int rkv_attn_partial(rkv_ctx *ctx, const rkv_tensor *q, const rkv_tensor *k, con
     if (k->ne[1] > 0) {
         if ((st = run_segment(ctx, p, sg, mfma, k->type, v->type, slot, stream))) return st;
     } else {
-        hipError_t e0 = launch_empty_partials(ctx->partials, p.n_rows, stream);
+        hipError_t e0 = launch_empty_partials(ctx->partials, p.n_rows, stream, dv);
         if (e0 != hipSuccess) return hip_fail(e0, "empty partial");
         slot = 1;
     }
     ctx->stats.n_partials = slot;
-    hipError_t e = launch_merge(ctx->partials, slot, p.n_rows, nullptr, nullptr, partial, stream);
+    hipError_t e = dv == kHeadDim ? launch_merge(ctx->partials, slot, p.n_rows, nullptr, nullptr, partial, stream)
+                                  : launch_merge_parts(ctx->partials, slot, p.n_rows, dv, nullptr, nullptr, stream, partial);
     if (e != hipSuccess) return hip_fail(e, "merge launch");
     return RKV_OK;
 }
